@@ -1,0 +1,181 @@
+"""MiniMax Sparse Attention (MSA) hot path for AMD MI355X (gfx950).
+
+Thin PyTorch binding over the C ABI of libmsa.so (include/msa.h): it checks
+tensor shapes and dtypes, allocates outputs and workspaces with torch, and
+passes raw device pointers plus torch's current HIP stream.  Every step of
+the computation runs in the library's HIP kernels; there is no fallback.
+
+Layouts: q/out [B, S, Hq, D] bf16; k, v [B, G, S, D] bf16; q_idx, k_idx
+[B, G, S, 64] int8; block_keys [B, G, nb, 64] int8; sel [B, G, S, top_k]
+int32 (ascending, -1 padded).  Decode: q [B, Hq, D], q_idx [B, G, 64],
+k_cache / v_cache [B, G, L, D], block_keys [B, G, nb, 64].
+"""
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import MSA_OP_DECODE, MSA_OP_INDEX, MSA_OP_POOL, MSA_OP_PREFILL, MsaDims  # noqa: F401
+
+__all__ = [
+    "MsaError", "make_dims", "msa_workspace_bytes", "msa_pool_block_keys", "msa_index_select",
+    "msa_prefill", "msa_decode", "MSA_OP_POOL", "MSA_OP_INDEX", "MSA_OP_PREFILL", "MSA_OP_DECODE",
+]
+
+
+class MsaError(RuntimeError):
+    def __init__(self, code, where):
+        super().__init__(f"{where}: {_lib.status_string(code)} ({code})")
+        self.code = code
+
+
+def _check(code, where):
+    if code != _lib.MSA_OK:
+        raise MsaError(code, where)
+
+
+def make_dims(batch, seq_len, n_q_heads, n_kv_heads, block_size, top_k, head_dim=128, idx_dim=64,
+              softmax_scale=0.0) -> MsaDims:
+    return MsaDims(batch, seq_len, n_q_heads, n_kv_heads, head_dim, idx_dim, block_size, top_k,
+                   float(softmax_scale))
+
+
+def msa_workspace_bytes(op, dims: MsaDims):
+    """(min_bytes, full_bytes) of workspace for an operation."""
+    lo, hi = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check(_lib.load().msa_workspace_bytes(op, ctypes.byref(dims), ctypes.byref(lo), ctypes.byref(hi)),
+           "msa_workspace_bytes")
+    return lo.value, hi.value
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, dtype, ndim, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _workspace(op, dims, device, workspace):
+    lo, hi = msa_workspace_bytes(op, dims)
+    if lo == 0:
+        return None, 0
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, 1, device)
+        return workspace, workspace.numel()
+    size = hi
+    if op == MSA_OP_PREFILL:
+        free, _ = torch.cuda.mem_get_info(device)
+        budget = int(free * 0.8)
+        if size > budget:
+            size = max(lo, budget)
+    return torch.empty(size, dtype=torch.uint8, device=device), size
+
+
+def msa_pool_block_keys(k_idx: torch.Tensor, block_size: int, block_keys=None) -> torch.Tensor:
+    """Block summary keys [B, G, nb, 64] (floor-mean of each block's index keys)."""
+    _need(k_idx, "k_idx", torch.int8, 4)
+    B, G, S, di = k_idx.shape
+    nb = -(-S // block_size)
+    if block_keys is None:
+        block_keys = torch.empty((B, G, nb, di), dtype=torch.int8, device=k_idx.device)
+    _need(block_keys, "block_keys", torch.int8, 4, k_idx.device)
+    dims = make_dims(B, S, G, G, block_size, 1, idx_dim=di)
+    _check(_lib.load().msa_pool_block_keys(ctypes.byref(dims), _ptr(k_idx), _ptr(block_keys),
+                                           _stream(k_idx.device)), "msa_pool_block_keys")
+    return block_keys
+
+
+def msa_index_select(q_idx: torch.Tensor, k_idx: torch.Tensor, block_size: int, top_k: int):
+    """Index branch: (block_keys [B, G, nb, 64] int8, sel [B, G, S, top_k] int32)."""
+    _need(q_idx, "q_idx", torch.int8, 4)
+    _need(k_idx, "k_idx", torch.int8, 4, q_idx.device)
+    if q_idx.shape != k_idx.shape:
+        raise ValueError("q_idx and k_idx must have the same shape")
+    B, G, S, di = q_idx.shape
+    nb = -(-S // block_size)
+    dev = q_idx.device
+    block_keys = torch.empty((B, G, nb, di), dtype=torch.int8, device=dev)
+    sel = torch.empty((B, G, S, top_k), dtype=torch.int32, device=dev)
+    dims = make_dims(B, S, G, G, block_size, top_k, idx_dim=di)
+    ws, ws_bytes = _workspace(MSA_OP_INDEX, dims, dev, None)
+    _check(_lib.load().msa_index_select(ctypes.byref(dims), _ptr(q_idx), _ptr(k_idx), _ptr(block_keys),
+                                        _ptr(sel), _ptr(ws), ws_bytes, _stream(dev)), "msa_index_select")
+    return block_keys, sel
+
+
+def msa_prefill(q, k, v, q_idx, k_idx, block_size: int, top_k: int, softmax_scale: float = 0.0,
+                out=None, sel=None, return_sel: bool = False, workspace=None):
+    """MSA prefill -> out [B, S, Hq, D] bf16 (and sel when return_sel)."""
+    _need(q, "q", torch.bfloat16, 4)
+    dev = q.device
+    _need(k, "k", torch.bfloat16, 4, dev)
+    _need(v, "v", torch.bfloat16, 4, dev)
+    _need(q_idx, "q_idx", torch.int8, 4, dev)
+    _need(k_idx, "k_idx", torch.int8, 4, dev)
+    B, S, Hq, D = q.shape
+    G = k.shape[1]
+    if k.shape != (B, G, S, D) or v.shape != k.shape:
+        raise ValueError(f"k/v must be [B, G, S, D] = {(B, G, S, D)}")
+    if q_idx.shape[:3] != (B, G, S) or k_idx.shape != q_idx.shape:
+        raise ValueError("q_idx/k_idx must be [B, G, S, di]")
+    dims = make_dims(B, S, Hq, G, block_size, top_k, head_dim=D, idx_dim=q_idx.shape[3],
+                     softmax_scale=softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16, 4, dev)
+    if sel is None and return_sel:
+        sel = torch.empty((B, G, S, top_k), dtype=torch.int32, device=dev)
+    if sel is not None:
+        _need(sel, "sel", torch.int32, 4, dev)
+    ws, ws_bytes = _workspace(MSA_OP_PREFILL, dims, dev, workspace)
+    _check(_lib.load().msa_prefill(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(q_idx), _ptr(k_idx),
+                                   _ptr(out), _ptr(sel), _ptr(ws), ws_bytes, _stream(dev)), "msa_prefill")
+    return (out, sel) if return_sel else out
+
+
+def msa_decode(q, q_idx, k_cache, v_cache, block_keys, block_size: int, top_k: int,
+               softmax_scale: float = 0.0, out=None, sel=None, return_sel: bool = False, workspace=None):
+    """One decode step at position L - 1 -> out [B, Hq, D] bf16."""
+    _need(q, "q", torch.bfloat16, 3)
+    dev = q.device
+    _need(q_idx, "q_idx", torch.int8, 3, dev)
+    _need(k_cache, "k_cache", torch.bfloat16, 4, dev)
+    _need(v_cache, "v_cache", torch.bfloat16, 4, dev)
+    _need(block_keys, "block_keys", torch.int8, 4, dev)
+    B, Hq, D = q.shape
+    _, G, L, _ = k_cache.shape
+    nb = -(-L // block_size)
+    if k_cache.shape != (B, G, L, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache/v_cache must be [B, G, L, D]")
+    if q_idx.shape[:2] != (B, G) or block_keys.shape != (B, G, nb, q_idx.shape[2]):
+        raise ValueError("q_idx must be [B, G, di] and block_keys [B, G, nb, di]")
+    dims = make_dims(B, L, Hq, G, block_size, top_k, head_dim=D, idx_dim=q_idx.shape[2],
+                     softmax_scale=softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16, 3, dev)
+    if sel is None and return_sel:
+        sel = torch.empty((B, G, top_k), dtype=torch.int32, device=dev)
+    if sel is not None:
+        _need(sel, "sel", torch.int32, 3, dev)
+    ws, ws_bytes = _workspace(MSA_OP_DECODE, dims, dev, workspace)
+    _check(_lib.load().msa_decode(ctypes.byref(dims), _ptr(q), _ptr(q_idx), _ptr(k_cache), _ptr(v_cache),
+                                  _ptr(block_keys), _ptr(out), _ptr(sel), _ptr(ws), ws_bytes, _stream(dev)),
+           "msa_decode")
+    return (out, sel) if return_sel else out

@@ -1,0 +1,240 @@
+// MSA index branch: block-summary pooling and the per-(query, group) top-k.
+//
+// The index branch is a cheap scorer over KV blocks whose best k blocks are
+// kept independently for every GQA group ("深度解析 MiniMax-M3：稀疏注意力机制、
+// 基准测试与 API 集成指南", section "架构核心：MoE 与 MSA 的深度融合", item 1), and
+// its top-k needs no exponentials (wiki.500nian.com digest of "MiniMax M3
+// Review: 1M Tokens, 15X Faster AI Agents", flowchart node "exp-free Top-k").
+// The scorer used here: int8 summaries = floor-mean of each block's int8
+// index keys, score = exact int32 dot product, candidates = blocks strictly
+// before the query's block, ties to the lower block index, own block added.
+
+#include "msa_device.h"
+#include "msa_kernels.h"
+
+#include <limits.h>
+
+namespace msa {
+namespace {
+
+// ---------------------------------------------------------------------------
+// Pooling: one wave per (unit, block).  Lane (row, col) = (lane / 16, lane %
+// 16) sums dword `col` (4 index dims) of tokens row, row + 4, ...; the four
+// rows are folded with lane shuffles.  HBM-bound streaming read.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void pool_kernel(const int8_t* __restrict__ k_idx,
+                                                   int8_t* __restrict__ block_keys, int units,
+                                                   int S, int bs, int nb) {
+  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wid >= units * nb) return;
+  const int lane = threadIdx.x & 63;
+  const int u = wid / nb;
+  const int j = wid - u * nb;
+  const int t0 = j * bs;
+  const int n = min(bs, S - t0);
+  const uint32_t* base = reinterpret_cast<const uint32_t*>(k_idx + ((size_t)u * S + t0) * kIdxDim);
+  const int col = lane & 15;
+  const int row = lane >> 4;
+  int s0 = 0, s1 = 0, s2 = 0, s3 = 0;
+#pragma unroll 8
+  for (int tt = row; tt < n; tt += 4) {
+    const uint32_t w = __builtin_nontemporal_load(base + tt * 16 + col);
+    s0 += sx8(w, 0);
+    s1 += sx8(w, 1);
+    s2 += sx8(w, 2);
+    s3 += sx8(w, 3);
+  }
+  s0 += __shfl_xor(s0, 16);
+  s1 += __shfl_xor(s1, 16);
+  s2 += __shfl_xor(s2, 16);
+  s3 += __shfl_xor(s3, 16);
+  s0 += __shfl_xor(s0, 32);
+  s1 += __shfl_xor(s1, 32);
+  s2 += __shfl_xor(s2, 32);
+  s3 += __shfl_xor(s3, 32);
+  if (row == 0) {
+    const uint32_t packed = (uint32_t)(floor_div(s0, n) & 0xff) |
+                            ((uint32_t)(floor_div(s1, n) & 0xff) << 8) |
+                            ((uint32_t)(floor_div(s2, n) & 0xff) << 16) |
+                            ((uint32_t)(floor_div(s3, n) & 0xff) << 24);
+    reinterpret_cast<uint32_t*>(block_keys + ((size_t)u * nb + j) * kIdxDim)[col] = packed;
+  }
+}
+
+// Ascending bitonic sort of N (a power of two) register values.
+template <int N>
+__device__ __forceinline__ void bitonic_sort(int (&x)[N]) {
+#pragma unroll
+  for (int k = 2; k <= N; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const int l = i ^ j;
+        if (l > i) {
+          const int a = x[i], b = x[l];
+          const bool up = (i & k) == 0;
+          x[i] = up ? min(a, b) : max(a, b);
+          x[l] = up ? max(a, b) : min(a, b);
+        }
+      }
+    }
+  }
+}
+
+template <int N>
+struct NextPow2 {
+  static constexpr int v = N <= 1 ? 1 : N <= 2 ? 2 : N <= 4 ? 4 : N <= 8 ? 8 : N <= 16 ? 16 : 32;
+};
+
+// ---------------------------------------------------------------------------
+// Scores + top-k: one lane per query token, 256 consecutive tokens of one
+// (batch, group) unit per workgroup.  Summaries of the candidate blocks are
+// staged through LDS in chunks and read as wave-wide broadcasts; each lane
+// scores every candidate with 16 v_dot4 and keeps a sorted register list of
+// its best KCAP (score desc, index asc).  Candidates arrive in ascending
+// block order, so a candidate enters the list only when its score beats the
+// list's last score strictly: an equal score belongs to a lower index already
+// in the list.  KCAP >= top_k - 1; the best top_k - 1 are taken from it.
+// ---------------------------------------------------------------------------
+template <int KCAP>
+__global__ __launch_bounds__(256) void index_topk_kernel(const int8_t* __restrict__ q_idx,
+                                                         const int8_t* __restrict__ block_keys,
+                                                         int32_t* __restrict__ sel,
+                                                         int32_t* __restrict__ counts, int S,
+                                                         int nb, int bs_log2, int top_k) {
+  constexpr int CH = 256;  // summaries per LDS chunk (16 KiB)
+  __shared__ i32x4_t sk[CH * 4];
+
+  const int u = blockIdx.y;
+  const int t0 = blockIdx.x * 256;
+  const int t = t0 + (int)threadIdx.x;
+  const bool live = t < S;
+  const int tc = live ? t : S - 1;
+  const int c = tc >> bs_log2;  // own block = number of candidates
+  const int c_last = min(S - 1, t0 + 255) >> bs_log2;
+  const int kp = top_k - 1;
+
+  const i32x4_t* qp = reinterpret_cast<const i32x4_t*>(q_idx + ((size_t)u * S + tc) * kIdxDim);
+  const i32x4_t q0 = qp[0], q1 = qp[1], q2 = qp[2], q3 = qp[3];
+
+  int Ls[KCAP], Li[KCAP];
+#pragma unroll
+  for (int i = 0; i < KCAP; ++i) {
+    Ls[i] = INT_MIN;
+    Li[i] = -1;
+  }
+
+  const i32x4_t* kb = reinterpret_cast<const i32x4_t*>(block_keys + (size_t)u * nb * kIdxDim);
+  const int n_cand = kp > 0 ? c_last : 0;
+  for (int base = 0; base < n_cand; base += CH) {
+    const int n = min(CH, n_cand - base);
+    __syncthreads();
+    for (int i = threadIdx.x; i < n * 4; i += 256) sk[i] = kb[base * 4 + i];
+    __syncthreads();
+    for (int jj = 0; jj < n; ++jj) {
+      const i32x4_t a0 = sk[4 * jj + 0], a1 = sk[4 * jj + 1];
+      const i32x4_t a2 = sk[4 * jj + 2], a3 = sk[4 * jj + 3];
+      int sa = 0, sb = 0;
+      sa = sdot4(q0.x, a0.x, sa);
+      sb = sdot4(q0.y, a0.y, sb);
+      sa = sdot4(q0.z, a0.z, sa);
+      sb = sdot4(q0.w, a0.w, sb);
+      sa = sdot4(q1.x, a1.x, sa);
+      sb = sdot4(q1.y, a1.y, sb);
+      sa = sdot4(q1.z, a1.z, sa);
+      sb = sdot4(q1.w, a1.w, sb);
+      sa = sdot4(q2.x, a2.x, sa);
+      sb = sdot4(q2.y, a2.y, sb);
+      sa = sdot4(q2.z, a2.z, sa);
+      sb = sdot4(q2.w, a2.w, sb);
+      sa = sdot4(q3.x, a3.x, sa);
+      sb = sdot4(q3.y, a3.y, sb);
+      sa = sdot4(q3.z, a3.z, sa);
+      sb = sdot4(q3.w, a3.w, sb);
+      const int s = sa + sb;
+      const int j = base + jj;
+      if (j < c && s > Ls[KCAP - 1]) {
+        // insert after every entry whose score is >= s (they all have a
+        // lower block index), shifting the rest down by one
+#pragma unroll
+        for (int i = KCAP - 1; i >= 0; --i) {
+          const bool keep = Ls[i] >= s;
+          const bool prev_keep = (i == 0) ? true : (Ls[i - 1] >= s);
+          const int ns = keep ? Ls[i] : (prev_keep ? s : Ls[i > 0 ? i - 1 : 0]);
+          const int ni = keep ? Li[i] : (prev_keep ? j : Li[i > 0 ? i - 1 : 0]);
+          Ls[i] = ns;
+          Li[i] = ni;
+        }
+      }
+    }
+  }
+
+  // best min(top_k - 1, c) candidates, ascending, then the own block
+  const int n_valid = min(kp, c);
+  constexpr int NP = NextPow2<KCAP>::v;
+  int x[NP];
+#pragma unroll
+  for (int i = 0; i < NP; ++i) x[i] = (i < KCAP && i < n_valid) ? Li[i < KCAP ? i : 0] : INT_MAX;
+  bitonic_sort<NP>(x);
+  if (!live) return;
+  int32_t* out = sel + ((size_t)u * S + t) * top_k;
+#pragma unroll
+  for (int i = 0; i <= KCAP; ++i) {
+    if (i < top_k) {
+      const int xv = (i < NP) ? x[i < NP ? i : 0] : INT_MAX;
+      out[i] = (i < n_valid) ? xv : (i == n_valid ? c : -1);
+    }
+  }
+  if (counts != nullptr) {
+    int32_t* cnt = counts + (size_t)u * nb;
+#pragma unroll
+    for (int i = 0; i < KCAP; ++i) {
+      if (i < n_valid) __hip_atomic_fetch_add(cnt + x[i], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* __restrict__ p, int32_t value, size_t n) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = value;
+}
+
+}  // namespace
+
+hipError_t launch_pool(const int8_t* k_idx, int8_t* block_keys, int units, int S, int bs,
+                       hipStream_t st) {
+  const int nb = (S + bs - 1) / bs;
+  const long waves = (long)units * nb;
+  const unsigned grid = (unsigned)((waves + 3) / 4);
+  hipLaunchKernelGGL(pool_kernel, dim3(grid), dim3(256), 0, st, k_idx, block_keys, units, S, bs, nb);
+  return hipGetLastError();
+}
+
+hipError_t launch_index_topk(const int8_t* q_idx, const int8_t* block_keys, int32_t* sel,
+                             int32_t* counts, int units, int S, int bs, int top_k, hipStream_t st) {
+  const int nb = (S + bs - 1) / bs;
+  int bs_log2 = 0;
+  while ((1 << bs_log2) < bs) ++bs_log2;
+  const dim3 grid((S + 255) / 256, units);
+  const int kp = top_k - 1;
+  if (kp <= 1)
+    hipLaunchKernelGGL(index_topk_kernel<1>, grid, dim3(256), 0, st, q_idx, block_keys, sel, counts, S, nb, bs_log2, top_k);
+  else if (kp <= 3)
+    hipLaunchKernelGGL(index_topk_kernel<3>, grid, dim3(256), 0, st, q_idx, block_keys, sel, counts, S, nb, bs_log2, top_k);
+  else if (kp <= 7)
+    hipLaunchKernelGGL(index_topk_kernel<7>, grid, dim3(256), 0, st, q_idx, block_keys, sel, counts, S, nb, bs_log2, top_k);
+  else if (kp <= 15)
+    hipLaunchKernelGGL(index_topk_kernel<15>, grid, dim3(256), 0, st, q_idx, block_keys, sel, counts, S, nb, bs_log2, top_k);
+  else
+    hipLaunchKernelGGL(index_topk_kernel<31>, grid, dim3(256), 0, st, q_idx, block_keys, sel, counts, S, nb, bs_log2, top_k);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_i32(int32_t* p, int32_t value, size_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, value, n);
+  return hipGetLastError();
+}
+
+}  // namespace msa

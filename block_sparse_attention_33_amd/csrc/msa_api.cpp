@@ -1,0 +1,323 @@
+// C ABI of the MSA hot path: argument checks, workspace planning and the
+// launch sequence of each entry point.  Everything here runs on the host;
+// argument checks and workspace sizes touch no HIP API, so they work (and
+// are tested) on machines without a GPU.
+
+#include "../../include/msa.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "msa_kernels.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kDecodeChunk = 128;     // candidate blocks per decode index wave (up to 512)
+constexpr int kDecodeMaxChunk = 512;
+constexpr int kDecodeMaxMergeKeys = 4096;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool pow2_in(int x, int lo, int hi) { return x >= lo && x <= hi && (x & (x - 1)) == 0; }
+
+struct Dims {
+  long B, S, Hq, G, r, D, di, bs, nb, k, kp, U;
+  float scale;
+};
+
+// Shape checks shared by every entry point.
+int check_dims(const msa_dims* d, Dims* o) {
+  if (d == nullptr) return MSA_ERR_INVALID_ARG;
+  if (d->batch <= 0 || d->seq_len <= 0 || d->n_q_heads <= 0 || d->n_kv_heads <= 0 ||
+      d->head_dim <= 0 || d->idx_dim <= 0 || d->block_size <= 0 || d->top_k <= 0)
+    return MSA_ERR_INVALID_ARG;
+  if (d->n_q_heads % d->n_kv_heads != 0) return MSA_ERR_INVALID_ARG;
+  if (!(d->softmax_scale == d->softmax_scale) || isinf(d->softmax_scale)) return MSA_ERR_INVALID_ARG;
+  const int r = d->n_q_heads / d->n_kv_heads;
+  if (d->head_dim != 128 || d->idx_dim != 64) return MSA_ERR_UNSUPPORTED;
+  if (d->block_size != 32 && d->block_size != 64 && d->block_size != 128) return MSA_ERR_UNSUPPORTED;
+  if (d->top_k > 32) return MSA_ERR_UNSUPPORTED;
+  if (!pow2_in(r, 1, 16)) return MSA_ERR_UNSUPPORTED;
+  if (d->seq_len >= (1 << 26)) return MSA_ERR_UNSUPPORTED;
+  const long units = (long)d->batch * d->n_kv_heads;
+  if (units * (long)d->seq_len * d->top_k >= (1L << 31)) return MSA_ERR_UNSUPPORTED;
+  if (units * (long)d->seq_len * d->n_q_heads / d->n_kv_heads >= (1L << 40)) return MSA_ERR_UNSUPPORTED;
+  o->B = d->batch;
+  o->S = d->seq_len;
+  o->Hq = d->n_q_heads;
+  o->G = d->n_kv_heads;
+  o->r = r;
+  o->D = d->head_dim;
+  o->di = d->idx_dim;
+  o->bs = d->block_size;
+  o->nb = (o->S + o->bs - 1) / o->bs;
+  o->k = d->top_k;
+  o->kp = d->top_k - 1;
+  o->U = units;
+  o->scale = d->softmax_scale > 0.f ? d->softmax_scale : 1.0f / sqrtf((float)d->head_dim);
+  return MSA_OK;
+}
+
+// ---- prefill workspace: fixed part + partials for `units_per_pass` units
+struct PrefillLayout {
+  size_t block_keys, sel, counts, fill, row_ptr, item_ptr, entries, items, part_o, part_lse, total;
+  long max_items_per_unit, tokens_per_item;
+};
+
+PrefillLayout prefill_layout(const Dims& d, long units_per_pass) {
+  PrefillLayout L{};
+  L.tokens_per_item = msa::kItemRows / d.r;
+  L.max_items_per_unit = (d.S * d.kp + L.tokens_per_item - 1) / L.tokens_per_item + d.nb;
+  const long nblk = d.U * d.nb;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align_up(bytes);
+    return at;
+  };
+  L.block_keys = take((size_t)nblk * d.di);
+  L.sel = take((size_t)d.U * d.S * d.k * 4);
+  L.counts = take((size_t)nblk * 4);
+  L.fill = take((size_t)nblk * 4);
+  L.row_ptr = take((size_t)(nblk + 1) * 4);
+  L.item_ptr = take((size_t)(nblk + 1) * 4);
+  L.entries = take((size_t)d.U * d.S * d.kp * 4);
+  L.items = take((size_t)(d.U * L.max_items_per_unit + 1) * 8);
+  L.part_o = take((size_t)units_per_pass * d.S * d.kp * d.r * d.D * 2);
+  L.part_lse = take((size_t)units_per_pass * d.S * d.kp * d.r * 4);
+  L.total = off;
+  return L;
+}
+
+struct DecodeLayout {
+  size_t chunk_best, part_o, part_ml, counters, sel, total;
+  int n_chunks, chunk;
+};
+
+int decode_layout(const Dims& d, DecodeLayout* L) {
+  const long n_cand = d.nb - 1;
+  int n_chunks = (int)std::max(1L, (n_cand + kDecodeChunk - 1) / kDecodeChunk);
+  int chunk = kDecodeChunk;
+  if (d.kp > 0 && (long)n_chunks * d.kp > kDecodeMaxMergeKeys) {
+    n_chunks = (int)(kDecodeMaxMergeKeys / d.kp);
+    chunk = (int)((n_cand + n_chunks - 1) / n_chunks);
+    chunk = (chunk + 63) / 64 * 64;
+    if (chunk > kDecodeMaxChunk) return MSA_ERR_UNSUPPORTED;
+    n_chunks = (int)std::max(1L, (n_cand + chunk - 1) / chunk);
+  }
+  L->n_chunks = n_chunks;
+  L->chunk = chunk;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align_up(bytes);
+    return at;
+  };
+  L->chunk_best = take((size_t)d.U * n_chunks * d.kp * 8);
+  L->part_o = take((size_t)d.U * d.k * d.r * d.D * 4);
+  L->part_ml = take((size_t)d.U * d.k * d.r * 2 * 4);
+  L->counters = take((size_t)d.U * 4);
+  L->sel = take((size_t)d.U * d.k * 4);
+  L->total = off;
+  return MSA_OK;
+}
+
+int check_ws(const void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return MSA_OK;
+  if (ws == nullptr || ws_bytes < need) return MSA_ERR_WORKSPACE;
+  if (((uintptr_t)ws) % kAlign != 0) return MSA_ERR_WORKSPACE;
+  return MSA_OK;
+}
+
+#define MSA_LAUNCH(call)                      \
+  do {                                        \
+    if ((call) != hipSuccess) return MSA_ERR_HIP; \
+  } while (0)
+
+int bs_log2_of(long bs) {
+  int l = 0;
+  while ((1L << l) < bs) ++l;
+  return l;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* msa_status_string(int status) {
+  switch (status) {
+    case MSA_OK:
+      return "MSA_OK";
+    case MSA_ERR_INVALID_ARG:
+      return "MSA_ERR_INVALID_ARG: null pointer, non-positive size or inconsistent shape";
+    case MSA_ERR_UNSUPPORTED:
+      return "MSA_ERR_UNSUPPORTED: shape outside the supported limits";
+    case MSA_ERR_WORKSPACE:
+      return "MSA_ERR_WORKSPACE: workspace missing, too small or not 256-byte aligned";
+    case MSA_ERR_HIP:
+      return "MSA_ERR_HIP: a HIP runtime call or kernel launch failed";
+    default:
+      return "unknown MSA status";
+  }
+}
+
+int msa_version(void) { return 10000; }
+
+int msa_workspace_bytes(int op, const msa_dims* dims, size_t* min_bytes, size_t* full_bytes) {
+  Dims d;
+  int st = check_dims(dims, &d);
+  if (st != MSA_OK) return st;
+  size_t lo = 0, hi = 0;
+  switch (op) {
+    case MSA_OP_POOL:
+    case MSA_OP_INDEX:
+      break;
+    case MSA_OP_PREFILL:
+      lo = prefill_layout(d, 1).total;
+      hi = prefill_layout(d, d.U).total;
+      break;
+    case MSA_OP_DECODE: {
+      DecodeLayout L;
+      st = decode_layout(d, &L);
+      if (st != MSA_OK) return st;
+      lo = hi = L.total;
+      break;
+    }
+    default:
+      return MSA_ERR_INVALID_ARG;
+  }
+  if (min_bytes) *min_bytes = lo;
+  if (full_bytes) *full_bytes = hi;
+  return MSA_OK;
+}
+
+int msa_pool_block_keys(const msa_dims* dims, const int8_t* k_idx, int8_t* block_keys, void* stream) {
+  Dims d;
+  int st = check_dims(dims, &d);
+  if (st != MSA_OK) return st;
+  if (k_idx == nullptr || block_keys == nullptr) return MSA_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  MSA_LAUNCH(msa::launch_pool(k_idx, block_keys, (int)d.U, (int)d.S, (int)d.bs, s));
+  return MSA_OK;
+}
+
+int msa_index_select(const msa_dims* dims, const int8_t* q_idx, const int8_t* k_idx, int8_t* block_keys,
+                     int32_t* sel, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  Dims d;
+  int st = check_dims(dims, &d);
+  if (st != MSA_OK) return st;
+  if (q_idx == nullptr || k_idx == nullptr || block_keys == nullptr || sel == nullptr) return MSA_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  MSA_LAUNCH(msa::launch_pool(k_idx, block_keys, (int)d.U, (int)d.S, (int)d.bs, s));
+  MSA_LAUNCH(msa::launch_index_topk(q_idx, block_keys, sel, nullptr, (int)d.U, (int)d.S, (int)d.bs, (int)d.k, s));
+  return MSA_OK;
+}
+
+int msa_prefill(const msa_dims* dims, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                const int8_t* q_idx, const int8_t* k_idx, uint16_t* out, int32_t* sel, void* ws,
+                size_t ws_bytes, void* stream) {
+  Dims d;
+  int st = check_dims(dims, &d);
+  if (st != MSA_OK) return st;
+  if (!q || !k || !v || !q_idx || !k_idx || !out) return MSA_ERR_INVALID_ARG;
+  const PrefillLayout one = prefill_layout(d, 1);
+  st = check_ws(ws, ws_bytes, one.total);
+  if (st != MSA_OK) return st;
+  // as many (batch, group) units per pass as the workspace holds
+  const size_t per_unit = prefill_layout(d, 2).total - one.total;
+  long upp = 1;
+  if (per_unit > 0) upp = std::min<long>(d.U, 1 + (long)((ws_bytes - one.total) / per_unit));
+  else upp = d.U;
+  PrefillLayout L = prefill_layout(d, upp);
+  while (L.total > ws_bytes && upp > 1) L = prefill_layout(d, --upp);
+
+  char* base = static_cast<char*>(ws);
+  int8_t* bkeys = reinterpret_cast<int8_t*>(base + L.block_keys);
+  int32_t* sel_use = sel ? sel : reinterpret_cast<int32_t*>(base + L.sel);
+  int32_t* counts = reinterpret_cast<int32_t*>(base + L.counts);
+  int32_t* fill = reinterpret_cast<int32_t*>(base + L.fill);
+  int32_t* row_ptr = reinterpret_cast<int32_t*>(base + L.row_ptr);
+  int32_t* item_ptr = reinterpret_cast<int32_t*>(base + L.item_ptr);
+  uint32_t* entries = reinterpret_cast<uint32_t*>(base + L.entries);
+  int2* items = reinterpret_cast<int2*>(base + L.items);
+  uint16_t* part_o = reinterpret_cast<uint16_t*>(base + L.part_o);
+  float* part_lse = reinterpret_cast<float*>(base + L.part_lse);
+
+  hipStream_t s = (hipStream_t)stream;
+  const int U = (int)d.U, S = (int)d.S, bs = (int)d.bs, nb = (int)d.nb, K = (int)d.k;
+  const int nblk = U * nb;
+  MSA_LAUNCH(msa::launch_pool(k_idx, bkeys, U, S, bs, s));
+  if (d.kp > 0) MSA_LAUNCH(msa::launch_fill_i32(counts, 0, (size_t)nblk, s));
+  if (d.kp > 0) MSA_LAUNCH(msa::launch_fill_i32(fill, 0, (size_t)nblk, s));
+  MSA_LAUNCH(msa::launch_index_topk(q_idx, bkeys, sel_use, d.kp > 0 ? counts : nullptr, U, S, bs, K, s));
+  if (d.kp > 0) {
+    MSA_LAUNCH(msa::launch_scan(counts, row_ptr, item_ptr, nblk, (int)L.tokens_per_item, s));
+    MSA_LAUNCH(msa::launch_build_items(row_ptr, item_ptr, items, nblk, (int)L.tokens_per_item, s));
+    MSA_LAUNCH(msa::launch_scatter(sel_use, row_ptr, fill, entries, U, S, bs, K, nb, s));
+  }
+  msa::PrefillShape sh;
+  sh.B = (int)d.B;
+  sh.S = S;
+  sh.Hq = (int)d.Hq;
+  sh.G = (int)d.G;
+  sh.r = (int)d.r;
+  sh.bs = bs;
+  sh.bs_log2 = bs_log2_of(bs);
+  sh.nb = nb;
+  sh.top_k = K;
+  sh.scale_log2 = d.scale * 1.4426950408889634f;
+  for (long u0 = 0; u0 < d.U; u0 += upp) {
+    const long u1 = std::min<long>(d.U, u0 + upp);
+    if (d.kp > 0) {
+      const long max_items = (u1 - u0) * L.max_items_per_unit;
+      MSA_LAUNCH(msa::launch_main_offdiag(sh, q, k, v, row_ptr, item_ptr, items, entries, part_o, part_lse,
+                                          (int)u0, (int)u1, (int)max_items, s));
+    }
+    MSA_LAUNCH(msa::launch_diag_merge(sh, q, k, v, part_o, part_lse, out, (int)u0, (int)u1, s));
+  }
+  return MSA_OK;
+}
+
+int msa_decode(const msa_dims* dims, const uint16_t* q, const int8_t* q_idx, const uint16_t* k_cache,
+               const uint16_t* v_cache, const int8_t* block_keys, uint16_t* out, int32_t* sel, void* ws,
+               size_t ws_bytes, void* stream) {
+  Dims d;
+  int st = check_dims(dims, &d);
+  if (st != MSA_OK) return st;
+  if (!q || !q_idx || !k_cache || !v_cache || !block_keys || !out) return MSA_ERR_INVALID_ARG;
+  DecodeLayout L;
+  st = decode_layout(d, &L);
+  if (st != MSA_OK) return st;
+  st = check_ws(ws, ws_bytes, L.total);
+  if (st != MSA_OK) return st;
+  char* base = static_cast<char*>(ws);
+  msa::DecodeShape sh;
+  sh.B = (int)d.B;
+  sh.L = (int)d.S;
+  sh.Hq = (int)d.Hq;
+  sh.G = (int)d.G;
+  sh.r = (int)d.r;
+  sh.bs = (int)d.bs;
+  sh.nb = (int)d.nb;
+  sh.top_k = (int)d.k;
+  sh.n_chunks = L.n_chunks;
+  sh.chunk = L.chunk;
+  sh.scale_log2 = d.scale * 1.4426950408889634f;
+  int64_t* chunk_best = reinterpret_cast<int64_t*>(base + L.chunk_best);
+  float* part_o = reinterpret_cast<float*>(base + L.part_o);
+  float* part_ml = reinterpret_cast<float*>(base + L.part_ml);
+  int32_t* counters = reinterpret_cast<int32_t*>(base + L.counters);
+  hipStream_t s = (hipStream_t)stream;
+  MSA_LAUNCH(msa::launch_decode_index(sh, q_idx, block_keys, chunk_best, counters, s));
+  MSA_LAUNCH(msa::launch_decode_attend(sh, q, k_cache, v_cache, chunk_best, sel, part_o, part_ml, counters, out, s));
+  return MSA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,146 @@
+/*
+ * msa.h -- C ABI of the MiniMax Sparse Attention (MSA) hot path for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * MSA is grouped-query attention (GQA) split into two branches.  An index
+ * branch ranks the key/value blocks that precede a query and lets every GQA
+ * group keep its own top-k set; a main branch runs exact softmax attention
+ * over the kept blocks only ("深度解析 MiniMax-M3：稀疏注意力机制、基准测试与
+ * API 集成指南", section "架构核心：MoE 与 MSA 的深度融合", items 1 and 2; the
+ * wiki.500nian.com digest of "MiniMax M3 Review: 1M Tokens, 15X Faster AI
+ * Agents", flowchart nodes "Index Branch" and "Main Branch").  The ranking is
+ * exponent-free: integer scores are compared directly (same flowchart, node
+ * "exp-free Top-k").  The pages give no formula for the index branch; this
+ * library fixes it as follows:
+ *
+ *   summary key of block j  s_j = floor( sum_{t in block j} k_idx[t] / n_j )
+ *                                  (int8, floor toward -inf, n_j = tokens in j)
+ *   score of block j        q_idx[t] . s_j   (exact int32 dot product)
+ *   candidates of query t   blocks 0 .. b_t - 1, b_t = floor(t / block_size)
+ *   selection               the best top_k - 1 candidates by score, ties to the
+ *                           lower block index (all of them if fewer exist),
+ *                           plus the own block b_t, listed ascending and padded
+ *                           with -1 to top_k entries
+ *   attention               one softmax over every key of the selected blocks
+ *                           at a position <= t, scale softmax_scale
+ *
+ * Query head h belongs to group g = h / (n_q_heads / n_kv_heads).
+ *
+ * Layouts (row-major, contiguous, element types as named):
+ *   q, out       [B, S, Hq, D]    bf16 bits (uint16_t)
+ *   k, v         [B, G, S, D]     bf16 bits, G = n_kv_heads
+ *   q_idx, k_idx [B, G, S, di]    int8
+ *   block_keys   [B, G, nb, di]   int8, nb = ceil(S / block_size)
+ *   sel          [B, G, S, top_k] int32
+ *   decode: q/out [B, Hq, D], q_idx [B, G, di], k_cache/v_cache [B, G, L, D],
+ *           block_keys [B, G, nb, di], sel [B, G, top_k]; the query sits at
+ *           position L - 1 and its own key/value are already in the cache.
+ *
+ * Ownership: every tensor pointer is a device pointer owned by the caller.
+ * The library allocates no device memory: scratch space comes from the
+ * caller's workspace (size from msa_workspace_bytes), which must be 256-byte
+ * aligned.  The library keeps no state between calls.
+ *
+ * Streams: each call validates its arguments on the host, enqueues its
+ * kernels on `stream` (a hipStream_t; NULL = the default stream) and returns
+ * without synchronising.  Results are valid once the stream has reached
+ * them.  Calls that share a workspace must be ordered on one stream.
+ *
+ * Errors: every entry point returns MSA_OK (0) or a negative status; invalid
+ * arguments are rejected before anything is enqueued.  No exception or abort
+ * crosses the ABI.
+ *
+ * Limits: head_dim 128, idx_dim 64, block_size 32, 64 or 128, 1 <= top_k <=
+ * 32, n_q_heads = r * n_kv_heads with r in {1, 2, 4, 8, 16}, S < 2^26 and
+ * B * G * S * top_k < 2^31; decode needs ceil((nb - 1) / 512) * (top_k - 1)
+ * <= 4096.  Anything else returns MSA_ERR_UNSUPPORTED.
+ */
+#ifndef MSA_H
+#define MSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define MSA_OK 0
+#define MSA_ERR_INVALID_ARG (-1)  /* null pointer, non-positive size, bad ratio */
+#define MSA_ERR_UNSUPPORTED (-2)  /* valid but outside the supported limits */
+#define MSA_ERR_WORKSPACE (-3)    /* workspace missing, too small or misaligned */
+#define MSA_ERR_HIP (-4)          /* a HIP runtime call or launch failed */
+
+/* Operations, for msa_workspace_bytes. */
+#define MSA_OP_POOL 0
+#define MSA_OP_INDEX 1
+#define MSA_OP_PREFILL 2
+#define MSA_OP_DECODE 3
+
+typedef struct msa_dims {
+  int32_t batch;        /* B */
+  int32_t seq_len;      /* S for prefill/index/pool, cache length L for decode */
+  int32_t n_q_heads;    /* Hq */
+  int32_t n_kv_heads;   /* G, the number of GQA groups (one KV head each) */
+  int32_t head_dim;     /* D, must be 128 */
+  int32_t idx_dim;      /* di, width of the int8 index vectors, must be 64 */
+  int32_t block_size;   /* tokens per KV block: 32, 64 or 128 */
+  int32_t top_k;        /* blocks kept per (query, group), own block included */
+  float softmax_scale;  /* <= 0 selects 1 / sqrt(head_dim) */
+} msa_dims;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* msa_status_string(int status);
+
+/* ABI version: major * 10000 + minor * 100 + patch. */
+int msa_version(void);
+
+/* Workspace sizes in bytes for `op` at `dims`.
+ * *min_bytes: the least workspace the call accepts.  *full_bytes: the size at
+ * which the call runs in one pass (MSA_OP_PREFILL processes the (batch,
+ * group) units in as few passes as the workspace allows; every size between
+ * the two works).  Either output pointer may be NULL. */
+int msa_workspace_bytes(int op, const msa_dims* dims, size_t* min_bytes, size_t* full_bytes);
+
+/* Index branch, pooling step: block summary keys.
+ * k_idx [B, G, S, di] int8 -> block_keys [B, G, nb, di] int8.
+ * Needs no workspace. */
+int msa_pool_block_keys(const msa_dims* dims, const int8_t* k_idx, int8_t* block_keys,
+                        void* stream);
+
+/* Index branch: pooling, scores and per-(query, group) top-k.
+ * q_idx, k_idx [B, G, S, di] int8 -> block_keys [B, G, nb, di] int8 and
+ * sel [B, G, S, top_k] int32 (both outputs required).
+ * ws/ws_bytes: workspace of at least msa_workspace_bytes(MSA_OP_INDEX) bytes
+ * (may be NULL/0 when that is 0). */
+int msa_index_select(const msa_dims* dims, const int8_t* q_idx, const int8_t* k_idx,
+                     int8_t* block_keys, int32_t* sel, void* ws, size_t ws_bytes, void* stream);
+
+/* Whole MSA prefill: index branch, then the main branch over the selected
+ * blocks.  q [B, S, Hq, D], k, v [B, G, S, D] bf16; q_idx, k_idx [B, G, S, di]
+ * int8 -> out [B, S, Hq, D] bf16 (round to nearest even).  sel [B, G, S,
+ * top_k] int32 receives the selection when non-NULL.  The main branch reads
+ * each selected key/value block once per batch of the queries that picked
+ * it and merges the per-block partial results of a query in log-sum-exp
+ * form.  ws/ws_bytes: at least the minimum of msa_workspace_bytes(
+ * MSA_OP_PREFILL). */
+int msa_prefill(const msa_dims* dims, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                const int8_t* q_idx, const int8_t* k_idx, uint16_t* out, int32_t* sel, void* ws,
+                size_t ws_bytes, void* stream);
+
+/* One decode step per sequence: the query at position L - 1 of each of the B
+ * caches.  q [B, Hq, D] bf16, q_idx [B, G, di] int8, k_cache, v_cache
+ * [B, G, L, D] bf16, block_keys [B, G, nb, di] int8 (summaries of the cache's
+ * index keys, e.g. from msa_pool_block_keys) -> out [B, Hq, D] bf16; sel
+ * [B, G, top_k] int32 when non-NULL.  ws/ws_bytes: at least
+ * msa_workspace_bytes(MSA_OP_DECODE). */
+int msa_decode(const msa_dims* dims, const uint16_t* q, const int8_t* q_idx,
+               const uint16_t* k_cache, const uint16_t* v_cache, const int8_t* block_keys,
+               uint16_t* out, int32_t* sel, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H */

@@ -1,0 +1,149 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/msa.h declares, rejects bad arguments with the
+documented status before touching the GPU, and sizes workspaces by the
+documented layout."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_sparse_attention_33_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from block_sparse_attention_33_amd import build
+        build.build()
+    return _lib.load()
+
+
+def _declared():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(msa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ["msa_index_select", "msa_prefill", "msa_decode", "msa_workspace_bytes",
+              "msa_pool_block_keys", "msa_status_string", "msa_version"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert set(_declared()) == set(_lib.SIGNATURES), "binding signatures out of sync with msa.h"
+
+
+def test_status_strings(lib):
+    for code, prefix in [(0, "MSA_OK"), (-1, "MSA_ERR_INVALID_ARG"), (-2, "MSA_ERR_UNSUPPORTED"),
+                         (-3, "MSA_ERR_WORKSPACE"), (-4, "MSA_ERR_HIP")]:
+        assert lib.msa_status_string(code).decode().startswith(prefix)
+    assert lib.msa_status_string(12345).decode() == "unknown MSA status"
+    assert lib.msa_version() == 10000
+
+
+def D(**kw):
+    base = dict(batch=1, seq_len=4096, n_q_heads=64, n_kv_heads=8, head_dim=128, idx_dim=64,
+                block_size=128, top_k=16, softmax_scale=0.0)
+    base.update(kw)
+    return _lib.MsaDims(**base)
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation
+
+
+def _ws(lib, op, dims):
+    lo, hi = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    st = lib.msa_workspace_bytes(op, ctypes.byref(dims), ctypes.byref(lo), ctypes.byref(hi))
+    return st, lo.value, hi.value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), -1), (dict(seq_len=-5), -1), (dict(n_q_heads=63), -1), (dict(top_k=0), -1),
+    (dict(softmax_scale=float("nan")), -1), (dict(softmax_scale=float("inf")), -1),
+    (dict(head_dim=64), -2), (dict(idx_dim=32), -2), (dict(block_size=96), -2),
+    (dict(block_size=256), -2), (dict(top_k=33), -2), (dict(n_q_heads=24), -2),
+    (dict(n_q_heads=256), -2), (dict(seq_len=1 << 26), -2),
+    (dict(batch=64, seq_len=1 << 20), -2),
+])
+def test_dims_validation(lib, kw, code):
+    dims = D(**kw)
+    st, _, _ = _ws(lib, _lib.MSA_OP_PREFILL, dims)
+    assert st == code
+    out = lib.msa_prefill(ctypes.byref(dims), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None)
+    assert out == code
+
+
+def test_null_pointers(lib):
+    dims = D()
+    assert lib.msa_prefill(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None) == -1
+    for i in range(6):
+        args = [FAKE] * 6
+        args[i] = None
+        assert lib.msa_prefill(ctypes.byref(dims), *args, None, FAKE, 1 << 40, None) == -1
+    assert lib.msa_index_select(ctypes.byref(dims), FAKE, FAKE, FAKE, None, None, 0, None) == -1
+    assert lib.msa_pool_block_keys(ctypes.byref(dims), None, FAKE, None) == -1
+    for i in range(6):
+        args = [FAKE] * 6
+        args[i] = None
+        assert lib.msa_decode(ctypes.byref(dims), *args, None, FAKE, 1 << 40, None) == -1
+
+
+def test_workspace_errors(lib):
+    dims = D()
+    st, lo, hi = _ws(lib, _lib.MSA_OP_PREFILL, dims)
+    assert st == 0 and 0 < lo <= hi
+    assert lib.msa_prefill(ctypes.byref(dims), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, lo, None) == -3
+    assert lib.msa_prefill(ctypes.byref(dims), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, lo - 1,
+                           None) == -3
+    misaligned = ctypes.c_void_p(0x1000 + 64)
+    assert lib.msa_prefill(ctypes.byref(dims), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, misaligned, hi,
+                           None) == -3
+    st, dlo, dhi = _ws(lib, _lib.MSA_OP_DECODE, dims)
+    assert st == 0 and dlo == dhi > 0
+    assert lib.msa_decode(ctypes.byref(dims), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, dlo - 1,
+                          None) == -3
+    assert lib.msa_workspace_bytes(99, ctypes.byref(dims), None, None) == -1
+
+
+def _a(x):
+    return (x + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("B,S,Hq,G,bs,k", [(1, 32768, 64, 8, 128, 16), (1, 2048, 8, 1, 64, 8),
+                                           (2, 1000, 8, 2, 32, 5), (1, 777, 16, 1, 128, 1)])
+def test_prefill_workspace_layout(lib, B, S, Hq, G, bs, k):
+    """The documented layout: fixed part + one bf16 partial (r x 128) and one
+    fp32 log-sum-exp (r) per (token, kept earlier block) per unit in a pass."""
+    dims = D(batch=B, seq_len=S, n_q_heads=Hq, n_kv_heads=G, block_size=bs, top_k=k)
+    st, lo, hi = _ws(lib, _lib.MSA_OP_PREFILL, dims)
+    assert st == 0
+    U, r, kp = B * G, Hq // G, k - 1
+    nb = -(-S // bs)
+    tpi = 256 // r
+    items = U * ((S * kp + tpi - 1) // tpi + nb) + 1
+    fixed = (_a(U * nb * 64) + _a(U * S * k * 4) + 2 * _a(U * nb * 4) + 2 * _a((U * nb + 1) * 4)
+             + _a(U * S * kp * 4) + _a(items * 8))
+    part = lambda n: _a(n * S * kp * r * 128 * 2) + _a(n * S * kp * r * 4)  # noqa: E731
+    assert lo == fixed + part(1)
+    assert hi == fixed + part(U)
+
+
+def test_decode_workspace_layout(lib):
+    dims = D(batch=16, seq_len=262144)
+    st, lo, hi = _ws(lib, _lib.MSA_OP_DECODE, dims)
+    U, k, r = 16 * 8, 16, 8
+    n_chunks = -(-(2048 - 1) // 128)
+    exp = _a(U * n_chunks * (k - 1) * 8) + _a(U * k * r * 128 * 4) + _a(U * k * r * 2 * 4) + _a(U * 4) + _a(U * k * 4)
+    assert st == 0 and lo == hi == exp
+    # huge caches need larger chunks; beyond the merge capacity the call is unsupported
+    st, _, _ = _ws(lib, _lib.MSA_OP_DECODE, D(batch=1, seq_len=(1 << 26) - 1, n_kv_heads=8, top_k=32))
+    assert st == -2
+    assert _ws(lib, _lib.MSA_OP_INDEX, dims)[1:] == (0, 0)
