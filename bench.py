@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""Benchmark of the MSA hot path on one MI355X.
+
+One step = one whole hot path: msa_prefill on the 32K-token prefill workload
+(batch 1, 64 query / 8 KV heads, head dim 128, blocks of 128, top_k 16:
+pooling, index top-k, inversion, off-diagonal main branch, own block +
+merge) followed by one msa_decode on the decode workload (16 sequences over
+262144-token caches, same heads).  Inputs are seeded synthetic tensors
+already resident in HBM.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import subprocess
+import sys
+import tempfile
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+CPU_SAMPLE_ROWS = 6144      # oracle rows timed on the host (about 15-20 s, one thread)
+
+
+def _prefill_counts(w):
+    """Algorithmic work of one prefill: attended keys per query head and the
+    off-diagonal (query row, kept earlier block) pairs."""
+    import numpy as np
+    t = np.arange(w.seq_len, dtype=np.int64)
+    own = t // w.block_size
+    kept = np.minimum(w.top_k - 1, own)
+    keys = kept * w.block_size + (t % w.block_size) + 1
+    per_head_keys = int(keys.sum()) * w.batch          # summed over queries, per query head
+    offdiag_pairs = int(kept.sum()) * w.batch * w.n_q_heads
+    return per_head_keys, offdiag_pairs
+
+
+def _decode_bytes(w):
+    B, Hq, G, D, bs, k = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size, w.top_k
+    nb = -(-w.seq_len // bs)
+    q = B * Hq * D * 2
+    q_idx = B * G * w.idx_dim
+    summaries = B * G * nb * w.idx_dim
+    kv = B * G * min(k, nb) * bs * D * 2 * 2
+    out = B * Hq * D * 2
+    return q + q_idx + summaries + kv + out
+
+
+def _kernel_hash():
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "block_sparse_attention_33_amd", "csrc", "main_branch.hip"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _measured_traffic():
+    """Per-launch HBM bytes of the off-diagonal kernel from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "main_offdiag_prefill_32k_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256_16") != _kernel_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline_worker(npz_path):
+    """Runs in a child process with one BLAS/OpenMP thread: the oracle on the
+    sampled rows.  Prints a JSON line with the time."""
+    import numpy as np
+    from oracle import msa_oracle as O
+    d = np.load(npz_path)
+    rows = d["rows"]
+    bs, top_k = int(d["bs"]), int(d["top_k"])
+    t0 = time.perf_counter()
+    summ = O.pool_block_keys(d["k_idx"], bs)
+    sel = O.select_blocks(d["q_idx"], summ, bs, top_k, rows)
+    O.attention_rows(d["q_rows"], d["k"], d["v"], sel, rows, bs)
+    dt = time.perf_counter() - t0
+    print(json.dumps({"seconds": dt, "rows": int(len(rows))}))
+
+
+def cpu_baseline(inp, w, n_rows):
+    import numpy as np
+    import torch
+    from synth import sample_rows
+    rows = sample_rows(w.seq_len, n_rows, 12345)
+    rt = torch.as_tensor(rows, device=inp["q"].device)
+    with tempfile.TemporaryDirectory() as td:
+        path = os.path.join(td, "cpu_baseline.npz")
+        np.savez(path, rows=rows, bs=w.block_size, top_k=w.top_k,
+                 q_rows=inp["q"][:, rt].float().cpu().numpy(), k=inp["k"].float().cpu().numpy(),
+                 v=inp["v"].float().cpu().numpy(), q_idx=inp["q_idx"].cpu().numpy(),
+                 k_idx=inp["k_idx"].cpu().numpy())
+        env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1",
+                   NUMEXPR_NUM_THREADS="1", HIP_VISIBLE_DEVICES="", CUDA_VISIBLE_DEVICES="")
+        res = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-baseline-worker", path],
+                             env=env, capture_output=True, text=True, timeout=600)
+    if res.returncode != 0:
+        raise RuntimeError(f"cpu baseline worker failed:\n{res.stderr}")
+    rec = json.loads(res.stdout.strip().splitlines()[-1])
+    return {
+        "value": rec["rows"] / rec["seconds"],
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"{rec['rows']} seeded query positions of the 32K prefill (all 8 groups, 64 heads): "
+                   f"pooling of all blocks + selection + attention, {rec['seconds']:.1f} s, one thread"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-baseline-worker", default=None, help=argparse.SUPPRESS)
+    args = ap.parse_args()
+    if args.cpu_baseline_worker:
+        cpu_baseline_worker(args.cpu_baseline_worker)
+        return 0
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the MSA path here runs on a single MI355X).", file=sys.stderr)
+        return 2
+
+    import torch
+    import block_sparse_attention_33_amd as msa
+    from synth import decode_inputs, get_workload, prefill_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wp = get_workload("prefill_32k")
+    wd = get_workload("decode_b16_256k")
+    print(f"[bench] generating inputs", file=sys.stderr, flush=True)
+    pin = prefill_inputs(wp, seed=0, device=dev)
+    din = decode_inputs(wd, seed=0, device=dev)
+    block_keys = msa.msa_pool_block_keys(din["k_idx_cache"], wd.block_size)
+    del din["k_idx_cache"]
+    out = torch.empty_like(pin["q"])
+    dout = torch.empty_like(din["q"])
+    pdims = msa.make_dims(wp.batch, wp.seq_len, wp.n_q_heads, wp.n_kv_heads, wp.block_size, wp.top_k)
+    ddims = msa.make_dims(wd.batch, wd.seq_len, wd.n_q_heads, wd.n_kv_heads, wd.block_size, wd.top_k)
+    pws = torch.empty(msa.msa_workspace_bytes(msa.MSA_OP_PREFILL, pdims)[1], dtype=torch.uint8, device=dev)
+    dws = torch.empty(msa.msa_workspace_bytes(msa.MSA_OP_DECODE, ddims)[1], dtype=torch.uint8, device=dev)
+
+    def prefill():
+        msa.msa_prefill(pin["q"], pin["k"], pin["v"], pin["q_idx"], pin["k_idx"], wp.block_size, wp.top_k,
+                        out=out, workspace=pws)
+
+    def decode():
+        msa.msa_decode(din["q"], din["q_idx"], din["k_cache"], din["v_cache"], block_keys, wd.block_size,
+                       wd.top_k, out=dout, workspace=dws)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        prefill()
+        decode()
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    msa.profile_read()              # drop anything recorded before
+    msa.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record()
+        prefill()
+        ev[i][1].record()
+        decode()
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    msa.profile_enable(False)
+    kt = msa.profile_read()
+    pre_ms = sorted(a.elapsed_time(b) for a, b, _ in ev)
+    dec_ms = sorted(b.elapsed_time(c) for _, b, c in ev)
+    pre_med = pre_ms[len(pre_ms) // 2]
+    dec_med = dec_ms[len(dec_ms) // 2]
+    ms_per_step = wall * 1e3 / args.steps
+
+    per_head_keys, offdiag_pairs = _prefill_counts(wp)
+    D = wp.head_dim
+    flop_alg = 4.0 * D * wp.n_q_heads * per_head_keys
+    tokens = wp.batch * wp.seq_len
+    offdiag_flop = 4.0 * D * wp.block_size * offdiag_pairs
+    n_off, off_ms = kt.get("main_offdiag", (0, 0.0))
+    off_avg_ms = off_ms / max(1, n_off)
+    off_tflops = offdiag_flop / (off_avg_ms * 1e-3) / 1e12 if off_avg_ms > 0 else None
+    # bytes the KV-outer design moves per off-diagonal row pair: gathered Q
+    # row (256 B) + bf16 partial (256 B) + fp32 log-sum-exp (4 B)
+    off_design_bytes = offdiag_pairs * (2 * D + 2 * D + 4)
+    dbytes = _decode_bytes(wd)
+    traffic = _measured_traffic()
+
+    kernels = {k: {"launches": n, "avg_ms": round(ms / max(1, n), 4)} for k, (n, ms) in sorted(kt.items())}
+    rec = {
+        "metric": "MSA prefill tokens/s (32K prefill); decode tokens/s and HBM GB/s in 'decode'",
+        "value": round(tokens / (pre_med * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "prefill_32k + decode_b16_256k", "batch": wp.batch, "seq_len": wp.seq_len,
+                   "n_q_heads": wp.n_q_heads, "n_kv_heads": wp.n_kv_heads, "head_dim": D,
+                   "block_size": wp.block_size, "top_k": wp.top_k, "decode_batch": wd.batch,
+                   "decode_cache_len": wd.seq_len, "parallelism": "none (1 GPU)"},
+        "prefill": {
+            "ms": round(pre_med, 4),
+            "tokens_per_s": round(tokens / (pre_med * 1e-3), 1),
+            "tflops_alg": round(flop_alg / (pre_med * 1e-3) / 1e12, 2),
+            "frac_bf16_peak": round(flop_alg / (pre_med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "flop_alg": flop_alg,
+        },
+        "decode": {
+            "us": round(dec_med * 1e3, 2),
+            "tokens_per_s": round(wd.batch / (dec_med * 1e-3), 1),
+            "hbm_gbs_alg": round(dbytes / (dec_med * 1e-3) / 1e9, 1),
+            "frac_hbm_peak": round(dbytes / (dec_med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "bytes_alg": dbytes,
+        },
+        "roofline": {
+            "kernel": "main_offdiag (KV-outer off-diagonal blocks)",
+            "bound": "mfma",
+            "achieved": round(off_tflops, 2) if off_tflops else None,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(off_tflops / PEAK_BF16_TFLOPS, 4) if off_tflops else None,
+            "traffic": traffic,
+            "avg_launch_ms": round(off_avg_ms, 4),
+            "flop_per_launch": offdiag_flop,
+            "design_bytes_per_launch": off_design_bytes,
+            "design_hbm_gbs": round(off_design_bytes / (off_avg_ms * 1e-3) / 1e9, 1) if off_avg_ms else None,
+        },
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        print(f"[bench] cpu baseline ({CPU_SAMPLE_ROWS} rows)", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(pin, wp, CPU_SAMPLE_ROWS)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -18,7 +18,7 @@ from . import _lib
 from ._lib import MSA_OP_DECODE, MSA_OP_INDEX, MSA_OP_POOL, MSA_OP_PREFILL, MsaDims  # noqa: F401
 
 __all__ = [
-    "MsaError", "make_dims", "msa_workspace_bytes", "msa_pool_block_keys", "msa_index_select",
+    "MsaError", "make_dims", "profile_enable", "profile_read", "msa_workspace_bytes", "msa_pool_block_keys", "msa_index_select",
     "msa_prefill", "msa_decode", "MSA_OP_POOL", "MSA_OP_INDEX", "MSA_OP_PREFILL", "MSA_OP_DECODE",
 ]
 
@@ -46,6 +46,20 @@ def msa_workspace_bytes(op, dims: MsaDims):
     _check(_lib.load().msa_workspace_bytes(op, ctypes.byref(dims), ctypes.byref(lo), ctypes.byref(hi)),
            "msa_workspace_bytes")
     return lo.value, hi.value
+
+
+def profile_enable(on: bool = True):
+    """Record every launch of the library's kernels with HIP events."""
+    _check(_lib.load().msa_profile_enable(1 if on else 0), "msa_profile_enable")
+
+
+def profile_read():
+    """{kernel name: (launches, total_ms)} recorded since the last read
+    (waits for the recorded launches)."""
+    arr = (_lib.MsaKernelTime * 64)()
+    n = ctypes.c_int(0)
+    _check(_lib.load().msa_profile_read(arr, 64, ctypes.byref(n)), "msa_profile_read")
+    return {arr[i].name.decode(): (arr[i].launches, arr[i].total_ms) for i in range(min(n.value, 64))}
 
 
 def _ptr(t):

@@ -30,6 +30,10 @@ class MsaDims(ctypes.Structure):
     ]
 
 
+class MsaKernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_int32), ("total_ms", ctypes.c_float)]
+
+
 _P = ctypes.c_void_p
 _DIMS = ctypes.POINTER(MsaDims)
 _SIZE_P = ctypes.POINTER(ctypes.c_size_t)
@@ -43,6 +47,9 @@ SIGNATURES = {
     "msa_index_select": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "msa_prefill": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "msa_decode": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "msa_profile_enable": (ctypes.c_int, [ctypes.c_int]),
+    "msa_profile_read": (ctypes.c_int, [ctypes.POINTER(MsaKernelTime), ctypes.c_int,
+                                        ctypes.POINTER(ctypes.c_int)]),
 }
 
 _lib = None

@@ -11,6 +11,9 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
+#include <string.h>
+#include <vector>
 
 #include "msa_kernels.h"
 
@@ -134,9 +137,53 @@ int check_ws(const void* ws, size_t ws_bytes, size_t need) {
   return MSA_OK;
 }
 
-#define MSA_LAUNCH(call)                      \
-  do {                                        \
-    if ((call) != hipSuccess) return MSA_ERR_HIP; \
+// ---- optional kernel timing (msa_profile_enable / msa_profile_read)
+struct ProfRec {
+  const char* name;
+  hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof_recs;
+std::vector<hipEvent_t> g_prof_pool;
+
+hipEvent_t prof_event() {
+  if (!g_prof_pool.empty()) {
+    hipEvent_t e = g_prof_pool.back();
+    g_prof_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Brackets one launch with events when timing is enabled.
+class ProfScope {
+ public:
+  ProfScope(const char* name, hipStream_t s) : name_(name), s_(s) {
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    if (!g_prof_on) return;
+    a_ = prof_event();
+    if (a_ && hipEventRecord(a_, s_) != hipSuccess) a_ = nullptr;
+  }
+  ~ProfScope() {
+    if (!a_) return;
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    hipEvent_t b = prof_event();
+    if (b && hipEventRecord(b, s_) == hipSuccess) g_prof_recs.push_back({name_, a_, b});
+  }
+
+ private:
+  const char* name_;
+  hipStream_t s_;
+  hipEvent_t a_ = nullptr;
+};
+
+#define MSA_LAUNCH_NAMED(name, stream, call)       \
+  do {                                             \
+    ProfScope prof_scope_(name, stream);           \
+    if ((call) != hipSuccess) return MSA_ERR_HIP;  \
   } while (0)
 
 int bs_log2_of(long bs) {
@@ -202,7 +249,7 @@ int msa_pool_block_keys(const msa_dims* dims, const int8_t* k_idx, int8_t* block
   if (st != MSA_OK) return st;
   if (k_idx == nullptr || block_keys == nullptr) return MSA_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
-  MSA_LAUNCH(msa::launch_pool(k_idx, block_keys, (int)d.U, (int)d.S, (int)d.bs, s));
+  MSA_LAUNCH_NAMED("pool", s, msa::launch_pool(k_idx, block_keys, (int)d.U, (int)d.S, (int)d.bs, s));
   return MSA_OK;
 }
 
@@ -215,8 +262,8 @@ int msa_index_select(const msa_dims* dims, const int8_t* q_idx, const int8_t* k_
   if (st != MSA_OK) return st;
   if (q_idx == nullptr || k_idx == nullptr || block_keys == nullptr || sel == nullptr) return MSA_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
-  MSA_LAUNCH(msa::launch_pool(k_idx, block_keys, (int)d.U, (int)d.S, (int)d.bs, s));
-  MSA_LAUNCH(msa::launch_index_topk(q_idx, block_keys, sel, nullptr, (int)d.U, (int)d.S, (int)d.bs, (int)d.k, s));
+  MSA_LAUNCH_NAMED("pool", s, msa::launch_pool(k_idx, block_keys, (int)d.U, (int)d.S, (int)d.bs, s));
+  MSA_LAUNCH_NAMED("index_topk", s, msa::launch_index_topk(q_idx, block_keys, sel, nullptr, (int)d.U, (int)d.S, (int)d.bs, (int)d.k, s));
   return MSA_OK;
 }
 
@@ -253,14 +300,14 @@ int msa_prefill(const msa_dims* dims, const uint16_t* q, const uint16_t* k, cons
   hipStream_t s = (hipStream_t)stream;
   const int U = (int)d.U, S = (int)d.S, bs = (int)d.bs, nb = (int)d.nb, K = (int)d.k;
   const int nblk = U * nb;
-  MSA_LAUNCH(msa::launch_pool(k_idx, bkeys, U, S, bs, s));
-  if (d.kp > 0) MSA_LAUNCH(msa::launch_fill_i32(counts, 0, (size_t)nblk, s));
-  if (d.kp > 0) MSA_LAUNCH(msa::launch_fill_i32(fill, 0, (size_t)nblk, s));
-  MSA_LAUNCH(msa::launch_index_topk(q_idx, bkeys, sel_use, d.kp > 0 ? counts : nullptr, U, S, bs, K, s));
+  MSA_LAUNCH_NAMED("pool", s, msa::launch_pool(k_idx, bkeys, U, S, bs, s));
+  if (d.kp > 0) MSA_LAUNCH_NAMED("fill", s, msa::launch_fill_i32(counts, 0, (size_t)nblk, s));
+  if (d.kp > 0) MSA_LAUNCH_NAMED("fill", s, msa::launch_fill_i32(fill, 0, (size_t)nblk, s));
+  MSA_LAUNCH_NAMED("index_topk", s, msa::launch_index_topk(q_idx, bkeys, sel_use, d.kp > 0 ? counts : nullptr, U, S, bs, K, s));
   if (d.kp > 0) {
-    MSA_LAUNCH(msa::launch_scan(counts, row_ptr, item_ptr, nblk, (int)L.tokens_per_item, s));
-    MSA_LAUNCH(msa::launch_build_items(row_ptr, item_ptr, items, nblk, (int)L.tokens_per_item, s));
-    MSA_LAUNCH(msa::launch_scatter(sel_use, row_ptr, fill, entries, U, S, bs, K, nb, s));
+    MSA_LAUNCH_NAMED("scan", s, msa::launch_scan(counts, row_ptr, item_ptr, nblk, (int)L.tokens_per_item, s));
+    MSA_LAUNCH_NAMED("build_items", s, msa::launch_build_items(row_ptr, item_ptr, items, nblk, (int)L.tokens_per_item, s));
+    MSA_LAUNCH_NAMED("scatter", s, msa::launch_scatter(sel_use, row_ptr, fill, entries, U, S, bs, K, nb, s));
   }
   msa::PrefillShape sh;
   sh.B = (int)d.B;
@@ -277,10 +324,10 @@ int msa_prefill(const msa_dims* dims, const uint16_t* q, const uint16_t* k, cons
     const long u1 = std::min<long>(d.U, u0 + upp);
     if (d.kp > 0) {
       const long max_items = (u1 - u0) * L.max_items_per_unit;
-      MSA_LAUNCH(msa::launch_main_offdiag(sh, q, k, v, row_ptr, item_ptr, items, entries, part_o, part_lse,
+      MSA_LAUNCH_NAMED("main_offdiag", s, msa::launch_main_offdiag(sh, q, k, v, row_ptr, item_ptr, items, entries, part_o, part_lse,
                                           (int)u0, (int)u1, (int)max_items, s));
     }
-    MSA_LAUNCH(msa::launch_diag_merge(sh, q, k, v, part_o, part_lse, out, (int)u0, (int)u1, s));
+    MSA_LAUNCH_NAMED("diag_merge", s, msa::launch_diag_merge(sh, q, k, v, part_o, part_lse, out, (int)u0, (int)u1, s));
   }
   return MSA_OK;
 }
@@ -315,9 +362,50 @@ int msa_decode(const msa_dims* dims, const uint16_t* q, const int8_t* q_idx, con
   float* part_ml = reinterpret_cast<float*>(base + L.part_ml);
   int32_t* counters = reinterpret_cast<int32_t*>(base + L.counters);
   hipStream_t s = (hipStream_t)stream;
-  MSA_LAUNCH(msa::launch_decode_index(sh, q_idx, block_keys, chunk_best, counters, s));
-  MSA_LAUNCH(msa::launch_decode_attend(sh, q, k_cache, v_cache, chunk_best, sel, part_o, part_ml, counters, out, s));
+  MSA_LAUNCH_NAMED("decode_index", s, msa::launch_decode_index(sh, q_idx, block_keys, chunk_best, counters, s));
+  MSA_LAUNCH_NAMED("decode_attend", s, msa::launch_decode_attend(sh, q, k_cache, v_cache, chunk_best, sel, part_o, part_ml, counters, out, s));
   return MSA_OK;
+}
+
+int msa_profile_enable(int on) {
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  g_prof_on = on != 0;
+  return MSA_OK;
+}
+
+int msa_profile_read(msa_kernel_time* out, int max_entries, int* n_out) {
+  if (max_entries < 0 || (max_entries > 0 && out == nullptr)) return MSA_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  struct Agg {
+    const char* name;
+    int n;
+    double ms;
+  };
+  std::vector<Agg> agg;
+  int status = MSA_OK;
+  for (const ProfRec& r : g_prof_recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess)
+      status = MSA_ERR_HIP;
+    auto it = std::find_if(agg.begin(), agg.end(), [&](const Agg& a) { return strcmp(a.name, r.name) == 0; });
+    if (it == agg.end()) agg.push_back({r.name, 1, ms});
+    else {
+      it->n += 1;
+      it->ms += ms;
+    }
+    g_prof_pool.push_back(r.a);
+    g_prof_pool.push_back(r.b);
+  }
+  g_prof_recs.clear();
+  const int n = (int)agg.size();
+  for (int i = 0; i < n && i < max_entries; ++i) {
+    memset(out[i].name, 0, sizeof(out[i].name));
+    strncpy(out[i].name, agg[i].name, sizeof(out[i].name) - 1);
+    out[i].launches = agg[i].n;
+    out[i].total_ms = (float)agg[i].ms;
+  }
+  if (n_out) *n_out = n;
+  return status;
 }
 
 }  // extern "C"

@@ -39,7 +39,8 @@
  * Ownership: every tensor pointer is a device pointer owned by the caller.
  * The library allocates no device memory: scratch space comes from the
  * caller's workspace (size from msa_workspace_bytes), which must be 256-byte
- * aligned.  The library keeps no state between calls.
+ * aligned.  The library keeps no state between calls, apart from the
+ * optional kernel-timing record (msa_profile_enable / msa_profile_read).
  *
  * Streams: each call validates its arguments on the host, enqueues its
  * kernels on `stream` (a hipStream_t; NULL = the default stream) and returns
@@ -138,6 +139,23 @@ int msa_prefill(const msa_dims* dims, const uint16_t* q, const uint16_t* k, cons
 int msa_decode(const msa_dims* dims, const uint16_t* q, const int8_t* q_idx,
                const uint16_t* k_cache, const uint16_t* v_cache, const int8_t* block_keys,
                uint16_t* out, int32_t* sel, void* ws, size_t ws_bytes, void* stream);
+
+/* Optional per-kernel timing.  While enabled (on != 0), every kernel the
+ * entry points enqueue is bracketed by two HIP events on the same stream and
+ * recorded under its kernel name; disabled by default.  Returns MSA_OK, or
+ * MSA_ERR_HIP if events cannot be created. */
+int msa_profile_enable(int on);
+
+typedef struct msa_kernel_time {
+  char name[32];      /* kernel name, e.g. "main_offdiag" */
+  int32_t launches;   /* launches recorded since the last read */
+  float total_ms;     /* summed event-to-event duration of those launches */
+} msa_kernel_time;
+
+/* Waits for every recorded launch to finish, writes one aggregate per kernel
+ * name into out[0 .. max_entries) (*n_out = number of names), and clears
+ * the record.  out may be NULL when max_entries is 0. */
+int msa_profile_read(msa_kernel_time* out, int max_entries, int* n_out);
 
 #ifdef __cplusplus
 }

@@ -14,6 +14,20 @@ def host_f32(t: torch.Tensor) -> np.ndarray:
     return t.detach().to("cpu").float().numpy()
 
 
+class HostBf16:
+    """A host copy of a bf16 tensor that hands out float32 numpy slices, so
+    the oracle can gather rows of a large cache without a full fp32 copy."""
+
+    def __init__(self, t: torch.Tensor):
+        self.t = t.detach().to("cpu")
+        self.shape = tuple(self.t.shape)
+
+    def __getitem__(self, idx):
+        idx = tuple(torch.as_tensor(i) if isinstance(i, np.ndarray) else i for i in idx) \
+            if isinstance(idx, tuple) else idx
+        return self.t[idx].float().numpy()
+
+
 def host_i8(t: torch.Tensor) -> np.ndarray:
     return t.detach().to("cpu").numpy()
 
@@ -38,8 +52,8 @@ def oracle_prefill_rows(inp, w, rows, block_size=None, top_k=None):
     bs = block_size or w.block_size
     k = top_k or w.top_k
     q_rows = host_f32(inp["q"][:, torch.as_tensor(rows, device=inp["q"].device)])
-    kk = host_f32(inp["k"])
-    vv = host_f32(inp["v"])
+    kk = HostBf16(inp["k"])
+    vv = HostBf16(inp["v"])
     qi = host_i8(inp["q_idx"])
     ki = host_i8(inp["k_idx"])
     summ = O.pool_block_keys(ki, bs)

@@ -15,7 +15,7 @@ import torch
 import block_sparse_attention_33_amd as msa
 from oracle import msa_oracle as O
 from synth import decode_inputs, get_workload, prefill_inputs, sample_rows
-from tests.helpers import compare_out, host_f32, host_i8, oracle_prefill_rows
+from tests.helpers import HostBf16, compare_out, host_f32, host_i8, oracle_prefill_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -207,7 +207,7 @@ def test_prefill_32k_selection_all_rows():
         key = sc * (1 << 20) - j
         key = np.where(j < own[:, None], key, np.iinfo(np.int64).min)
         m = np.minimum(kp, own)                                          # kept per row
-        srt = -np.sort(-key, axis=1)                                     # descending
+        srt = np.sort(key, axis=1)[:, ::-1]                                     # descending
         thr = srt[np.arange(S), np.maximum(m - 1, 0)]
         expect = (key >= thr[:, None]) & (j < own[:, None]) & (m[:, None] > 0)
         got = np.zeros((S, nb), bool)
@@ -238,8 +238,8 @@ def _decode_case(w, L, B, seed, n_check_units=None):
     torch.cuda.synchronize()
     summ = O.pool_block_keys(host_i8(inp["k_idx_cache"]), w.block_size)
     assert np.array_equal(host_i8(bk), summ)
-    osel, oout = O.decode(host_f32(inp["q"]), host_i8(inp["q_idx"]), host_f32(inp["k_cache"]),
-                          host_f32(inp["v_cache"]), summ, w.block_size, w.top_k)
+    osel, oout = O.decode(host_f32(inp["q"]), host_i8(inp["q_idx"]), HostBf16(inp["k_cache"]),
+                          HostBf16(inp["v_cache"]), summ, w.block_size, w.top_k)
     assert np.array_equal(host_i8(sel).astype(np.int32), osel)
     compare_out(out, oout, f"decode L={L}")
 
