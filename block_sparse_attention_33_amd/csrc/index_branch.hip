@@ -100,8 +100,7 @@ struct NextPow2 {
 template <int KCAP>
 __global__ __launch_bounds__(256) void index_topk_kernel(const int8_t* __restrict__ q_idx,
                                                          const int8_t* __restrict__ block_keys,
-                                                         int32_t* __restrict__ sel,
-                                                         int32_t* __restrict__ counts, int S,
+                                                         int32_t* __restrict__ sel, int S,
                                                          int nb, int bs_log2, int top_k) {
   constexpr int CH = 256;  // summaries per LDS chunk (16 KiB)
   __shared__ i32x4_t sk[CH * 4];
@@ -186,13 +185,6 @@ __global__ __launch_bounds__(256) void index_topk_kernel(const int8_t* __restric
       out[i] = (i < n_valid) ? xv : (i == n_valid ? c : -1);
     }
   }
-  if (counts != nullptr) {
-    int32_t* cnt = counts + (size_t)u * nb;
-#pragma unroll
-    for (int i = 0; i < KCAP; ++i) {
-      if (i < n_valid) __hip_atomic_fetch_add(cnt + x[i], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
 }
 
 __global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* __restrict__ p, int32_t value, size_t n) {
@@ -211,23 +203,23 @@ hipError_t launch_pool(const int8_t* k_idx, int8_t* block_keys, int units, int S
   return hipGetLastError();
 }
 
-hipError_t launch_index_topk(const int8_t* q_idx, const int8_t* block_keys, int32_t* sel,
-                             int32_t* counts, int units, int S, int bs, int top_k, hipStream_t st) {
+hipError_t launch_index_topk(const int8_t* q_idx, const int8_t* block_keys, int32_t* sel, int units,
+                             int S, int bs, int top_k, hipStream_t st) {
   const int nb = (S + bs - 1) / bs;
   int bs_log2 = 0;
   while ((1 << bs_log2) < bs) ++bs_log2;
   const dim3 grid((S + 255) / 256, units);
   const int kp = top_k - 1;
   if (kp <= 1)
-    hipLaunchKernelGGL(index_topk_kernel<1>, grid, dim3(256), 0, st, q_idx, block_keys, sel, counts, S, nb, bs_log2, top_k);
+    hipLaunchKernelGGL(index_topk_kernel<1>, grid, dim3(256), 0, st, q_idx, block_keys, sel, S, nb, bs_log2, top_k);
   else if (kp <= 3)
-    hipLaunchKernelGGL(index_topk_kernel<3>, grid, dim3(256), 0, st, q_idx, block_keys, sel, counts, S, nb, bs_log2, top_k);
+    hipLaunchKernelGGL(index_topk_kernel<3>, grid, dim3(256), 0, st, q_idx, block_keys, sel, S, nb, bs_log2, top_k);
   else if (kp <= 7)
-    hipLaunchKernelGGL(index_topk_kernel<7>, grid, dim3(256), 0, st, q_idx, block_keys, sel, counts, S, nb, bs_log2, top_k);
+    hipLaunchKernelGGL(index_topk_kernel<7>, grid, dim3(256), 0, st, q_idx, block_keys, sel, S, nb, bs_log2, top_k);
   else if (kp <= 15)
-    hipLaunchKernelGGL(index_topk_kernel<15>, grid, dim3(256), 0, st, q_idx, block_keys, sel, counts, S, nb, bs_log2, top_k);
+    hipLaunchKernelGGL(index_topk_kernel<15>, grid, dim3(256), 0, st, q_idx, block_keys, sel, S, nb, bs_log2, top_k);
   else
-    hipLaunchKernelGGL(index_topk_kernel<31>, grid, dim3(256), 0, st, q_idx, block_keys, sel, counts, S, nb, bs_log2, top_k);
+    hipLaunchKernelGGL(index_topk_kernel<31>, grid, dim3(256), 0, st, q_idx, block_keys, sel, S, nb, bs_log2, top_k);
   return hipGetLastError();
 }
 

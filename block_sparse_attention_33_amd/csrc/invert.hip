@@ -5,15 +5,55 @@
 // them (yunpan.plus article on MiniMax M3, section "百万上下文，AI 怎么从奢侈品
 // 变日用品", the paragraph on the operator level: KV blocks moved to the outer
 // loop, each block read once with contiguous access, queries aggregated
-// inward).  Building that gather list is a histogram (counted by the top-k
-// kernel), an exclusive scan and a scatter: a CSR matrix whose rows are
-// (unit, block) and whose entries are (query token, selection slot).
+// inward).  Building that gather list is a counting sort: per-chunk block
+// histograms in LDS, an exclusive scan, and a scatter through LDS cursors
+// into a CSR matrix whose rows are (unit, block) and whose entries are
+// (query token, selection slot).  Device-wide atomics are avoided on
+// purpose: thousands of queries hit the same block counter.
 
 #include "msa_device.h"
 #include "msa_kernels.h"
 
 namespace msa {
 namespace {
+
+// Per-chunk histograms: one workgroup per (token chunk, unit) counts, in LDS,
+// how many of the chunk's queries kept each block before their own block,
+// and stores the counts as H[u][chunk][block].  LDS atomics only.
+__global__ __launch_bounds__(256) void chunk_hist_kernel(const int32_t* __restrict__ sel,
+                                                         int32_t* __restrict__ H, int S, int nb,
+                                                         int bs_log2, int top_k, int tpc, int n_chunks) {
+  extern __shared__ int32_t hist[];
+  const int c = blockIdx.x;
+  const int u = blockIdx.y;
+  for (int j = threadIdx.x; j < nb; j += 256) hist[j] = 0;
+  __syncthreads();
+  const int t0 = c * tpc;
+  const int t1 = min(S, t0 + tpc);
+  const int kp = top_k - 1;
+  for (int t = t0 + (int)threadIdx.x; t < t1; t += 256) {
+    const int nv = min(kp, t >> bs_log2);
+    const int32_t* srow = sel + ((size_t)u * S + t) * top_k;
+    for (int s = 0; s < nv; ++s) atomicAdd(&hist[srow[s]], 1);
+  }
+  __syncthreads();
+  int32_t* dst = H + ((size_t)u * n_chunks + c) * nb;
+  for (int j = threadIdx.x; j < nb; j += 256) dst[j] = hist[j];
+}
+
+// Per (unit, block): total over the chunks -> counts.
+__global__ __launch_bounds__(256) void chunk_total_kernel(const int32_t* __restrict__ H,
+                                                          int32_t* __restrict__ counts, int units, int nb,
+                                                          int n_chunks) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= units * nb) return;
+  const int u = i / nb;
+  const int j = i - u * nb;
+  const int32_t* src = H + (size_t)u * n_chunks * nb + j;
+  int total = 0;
+  for (int c = 0; c < n_chunks; ++c) total += src[(size_t)c * nb];
+  counts[i] = total;
+}
 
 // One workgroup: each thread scans a contiguous run of the counts, the run
 // totals are scanned in LDS, then every thread writes its exclusive offsets.
@@ -59,39 +99,79 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
   }
 }
 
-__global__ __launch_bounds__(256) void build_items_kernel(const int32_t* __restrict__ row_ptr,
-                                                          const int32_t* __restrict__ item_ptr,
-                                                          int2* __restrict__ items, int n, int tpi) {
+// Per (unit, block): turn the chunk counts into the chunks' first positions
+// in the block's list (in place), and write the block's work items
+// {block id, first entry}.
+__global__ __launch_bounds__(256) void offsets_items_kernel(int32_t* __restrict__ H,
+                                                            const int32_t* __restrict__ row_ptr,
+                                                            const int32_t* __restrict__ item_ptr,
+                                                            int2* __restrict__ items, int units, int nb,
+                                                            int n_chunks, int tpi) {
   const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
+  if (i >= units * nb) return;
+  const int u = i / nb;
+  const int j = i - u * nb;
+  int32_t* col = H + (size_t)u * n_chunks * nb + j;
+  int run = row_ptr[i];
+  for (int c = 0; c < n_chunks; ++c) {
+    const int x = col[(size_t)c * nb];
+    col[(size_t)c * nb] = run;
+    run += x;
+  }
   const int first = item_ptr[i];
   const int ni = item_ptr[i + 1] - first;
   for (int m = 0; m < ni; ++m) items[first + m] = make_int2(i, m * tpi);
 }
 
-// One thread per (unit, query token): every selected block before the
-// query's own block gets the entry (t << 5) | slot at a fresh position of
-// that block's list.  The order inside a list does not matter: each entry's
+// One workgroup per (token chunk, unit): the chunk's entries go to its
+// reserved stretch of each block's list; positions inside the stretch come
+// from LDS cursors.  The order inside a list does not matter: each entry's
 // result is written to its own (token, slot) place.
 __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ sel,
-                                                      const int32_t* __restrict__ row_ptr,
-                                                      int32_t* __restrict__ fill,
-                                                      uint32_t* __restrict__ entries, int units,
-                                                      int S, int bs_log2, int top_k, int nb) {
-  const long gid = (long)blockIdx.x * 256 + threadIdx.x;
-  if (gid >= (long)units * S) return;
-  const int u = (int)(gid / S);
-  const int t = (int)(gid - (long)u * S);
-  const int nv = min(top_k - 1, t >> bs_log2);
-  const int32_t* srow = sel + gid * top_k;
-  for (int s = 0; s < nv; ++s) {
-    const int blk = u * nb + srow[s];
-    const int pos = __hip_atomic_fetch_add(fill + blk, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    entries[row_ptr[blk] + pos] = ((uint32_t)t << 5) | (uint32_t)s;
+                                                      const int32_t* __restrict__ H,
+                                                      uint32_t* __restrict__ entries, int S, int nb,
+                                                      int bs_log2, int top_k, int tpc, int n_chunks) {
+  extern __shared__ int32_t cursor[];
+  const int c = blockIdx.x;
+  const int u = blockIdx.y;
+  const int32_t* src = H + ((size_t)u * n_chunks + c) * nb;
+  for (int j = threadIdx.x; j < nb; j += 256) cursor[j] = src[j];
+  __syncthreads();
+  const int t0 = c * tpc;
+  const int t1 = min(S, t0 + tpc);
+  const int kp = top_k - 1;
+  for (int t = t0 + (int)threadIdx.x; t < t1; t += 256) {
+    const int nv = min(kp, t >> bs_log2);
+    const int32_t* srow = sel + ((size_t)u * S + t) * top_k;
+    for (int s = 0; s < nv; ++s) {
+      const int pos = atomicAdd(&cursor[srow[s]], 1);
+      entries[pos] = ((uint32_t)t << 5) | (uint32_t)s;
+    }
   }
 }
 
 }  // namespace
+
+hipError_t launch_chunk_hist(const int32_t* sel, int32_t* H, int units, int S, int nb, int bs, int top_k,
+                             int tpc, int n_chunks, hipStream_t st) {
+  int bs_log2 = 0;
+  while ((1 << bs_log2) < bs) ++bs_log2;
+  const size_t lds = (size_t)nb * 4;
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_hist_kernel),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     kMaxInvertBlocks * 4);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(chunk_hist_kernel, dim3(n_chunks, units), dim3(256), lds, st, sel, H, S, nb, bs_log2, top_k,
+                     tpc, n_chunks);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_total(const int32_t* H, int32_t* counts, int units, int nb, int n_chunks,
+                              hipStream_t st) {
+  const int n = units * nb;
+  hipLaunchKernelGGL(chunk_total_kernel, dim3((n + 255) / 256), dim3(256), 0, st, H, counts, units, nb, n_chunks);
+  return hipGetLastError();
+}
 
 hipError_t launch_scan(const int32_t* counts, int32_t* row_ptr, int32_t* item_ptr, int n,
                        int tokens_per_item, hipStream_t st) {
@@ -99,21 +179,25 @@ hipError_t launch_scan(const int32_t* counts, int32_t* row_ptr, int32_t* item_pt
   return hipGetLastError();
 }
 
-hipError_t launch_build_items(const int32_t* row_ptr, const int32_t* item_ptr, int2* items, int n,
-                              int tokens_per_item, hipStream_t st) {
-  hipLaunchKernelGGL(build_items_kernel, dim3((n + 255) / 256), dim3(256), 0, st, row_ptr, item_ptr, items, n,
-                     tokens_per_item);
+hipError_t launch_offsets_items(int32_t* H, const int32_t* row_ptr, const int32_t* item_ptr, int2* items,
+                                int units, int nb, int n_chunks, int tokens_per_item, hipStream_t st) {
+  const int n = units * nb;
+  hipLaunchKernelGGL(offsets_items_kernel, dim3((n + 255) / 256), dim3(256), 0, st, H, row_ptr, item_ptr, items,
+                     units, nb, n_chunks, tokens_per_item);
   return hipGetLastError();
 }
 
-hipError_t launch_scatter(const int32_t* sel, const int32_t* row_ptr, int32_t* fill,
-                          uint32_t* entries, int units, int S, int bs, int top_k, int nb,
-                          hipStream_t st) {
+hipError_t launch_scatter(const int32_t* sel, const int32_t* H, uint32_t* entries, int units, int S, int nb,
+                          int bs, int top_k, int tpc, int n_chunks, hipStream_t st) {
   int bs_log2 = 0;
   while ((1 << bs_log2) < bs) ++bs_log2;
-  const long n = (long)units * S;
-  hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, sel, row_ptr, fill,
-                     entries, units, S, bs_log2, top_k, nb);
+  const size_t lds = (size_t)nb * 4;
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&scatter_kernel),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     kMaxInvertBlocks * 4);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(scatter_kernel, dim3(n_chunks, units), dim3(256), lds, st, sel, H, entries, S, nb, bs_log2,
+                     top_k, tpc, n_chunks);
   return hipGetLastError();
 }
 

@@ -20,9 +20,6 @@
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr int kDecodeChunk = 128;     // candidate blocks per decode index wave (up to 512)
-constexpr int kDecodeMaxChunk = 512;
-constexpr int kDecodeMaxMergeKeys = 4096;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -68,13 +65,26 @@ int check_dims(const msa_dims* d, Dims* o) {
 
 // ---- prefill workspace: fixed part + partials for `units_per_pass` units
 struct PrefillLayout {
-  size_t block_keys, sel, counts, fill, row_ptr, item_ptr, entries, items, part_o, part_lse, total;
-  long max_items_per_unit, tokens_per_item;
+  size_t block_keys, sel, counts, hist, row_ptr, item_ptr, entries, items, part_o, part_lse, total;
+  long max_items_per_unit, tokens_per_item, n_chunks, tokens_per_chunk;
 };
+
+// Token chunks of the inversion: enough workgroups, and at most ~4 M
+// per-chunk block counters.
+void plan_chunks(const Dims& d, long* n_chunks, long* tpc) {
+  const long by_tokens = (d.S + 255) / 256;
+  const long by_size = std::max(1L, (1L << 22) / (d.U * d.nb));
+  long n = std::max(1L, std::min(by_tokens, by_size));
+  long t = (d.S + n - 1) / n;
+  t = (t + 255) / 256 * 256;
+  *tpc = t;
+  *n_chunks = (d.S + t - 1) / t;
+}
 
 PrefillLayout prefill_layout(const Dims& d, long units_per_pass) {
   PrefillLayout L{};
   L.tokens_per_item = msa::kItemRows / d.r;
+  plan_chunks(d, &L.n_chunks, &L.tokens_per_chunk);
   L.max_items_per_unit = (d.S * d.kp + L.tokens_per_item - 1) / L.tokens_per_item + d.nb;
   const long nblk = d.U * d.nb;
   size_t off = 0;
@@ -86,7 +96,7 @@ PrefillLayout prefill_layout(const Dims& d, long units_per_pass) {
   L.block_keys = take((size_t)nblk * d.di);
   L.sel = take((size_t)d.U * d.S * d.k * 4);
   L.counts = take((size_t)nblk * 4);
-  L.fill = take((size_t)nblk * 4);
+  L.hist = take((size_t)d.U * L.n_chunks * d.nb * 4);
   L.row_ptr = take((size_t)(nblk + 1) * 4);
   L.item_ptr = take((size_t)(nblk + 1) * 4);
   L.entries = take((size_t)d.U * d.S * d.kp * 4);
@@ -98,33 +108,19 @@ PrefillLayout prefill_layout(const Dims& d, long units_per_pass) {
 }
 
 struct DecodeLayout {
-  size_t chunk_best, part_o, part_ml, counters, sel, total;
-  int n_chunks, chunk;
+  size_t part_o, part_ml, sel, total;
 };
 
 int decode_layout(const Dims& d, DecodeLayout* L) {
-  const long n_cand = d.nb - 1;
-  int n_chunks = (int)std::max(1L, (n_cand + kDecodeChunk - 1) / kDecodeChunk);
-  int chunk = kDecodeChunk;
-  if (d.kp > 0 && (long)n_chunks * d.kp > kDecodeMaxMergeKeys) {
-    n_chunks = (int)(kDecodeMaxMergeKeys / d.kp);
-    chunk = (int)((n_cand + n_chunks - 1) / n_chunks);
-    chunk = (chunk + 63) / 64 * 64;
-    if (chunk > kDecodeMaxChunk) return MSA_ERR_UNSUPPORTED;
-    n_chunks = (int)std::max(1L, (n_cand + chunk - 1) / chunk);
-  }
-  L->n_chunks = n_chunks;
-  L->chunk = chunk;
+  if (d.nb - 1 > msa::kDecodeMaxCandidates) return MSA_ERR_UNSUPPORTED;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
     off += align_up(bytes);
     return at;
   };
-  L->chunk_best = take((size_t)d.U * n_chunks * d.kp * 8);
   L->part_o = take((size_t)d.U * d.k * d.r * d.D * 4);
   L->part_ml = take((size_t)d.U * d.k * d.r * 2 * 4);
-  L->counters = take((size_t)d.U * 4);
   L->sel = take((size_t)d.U * d.k * 4);
   L->total = off;
   return MSA_OK;
@@ -225,6 +221,7 @@ int msa_workspace_bytes(int op, const msa_dims* dims, size_t* min_bytes, size_t*
     case MSA_OP_INDEX:
       break;
     case MSA_OP_PREFILL:
+      if (d.nb > msa::kMaxInvertBlocks) return MSA_ERR_UNSUPPORTED;
       lo = prefill_layout(d, 1).total;
       hi = prefill_layout(d, d.U).total;
       break;
@@ -263,7 +260,7 @@ int msa_index_select(const msa_dims* dims, const int8_t* q_idx, const int8_t* k_
   if (q_idx == nullptr || k_idx == nullptr || block_keys == nullptr || sel == nullptr) return MSA_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
   MSA_LAUNCH_NAMED("pool", s, msa::launch_pool(k_idx, block_keys, (int)d.U, (int)d.S, (int)d.bs, s));
-  MSA_LAUNCH_NAMED("index_topk", s, msa::launch_index_topk(q_idx, block_keys, sel, nullptr, (int)d.U, (int)d.S, (int)d.bs, (int)d.k, s));
+  MSA_LAUNCH_NAMED("index_topk", s, msa::launch_index_topk(q_idx, block_keys, sel, (int)d.U, (int)d.S, (int)d.bs, (int)d.k, s));
   return MSA_OK;
 }
 
@@ -274,6 +271,7 @@ int msa_prefill(const msa_dims* dims, const uint16_t* q, const uint16_t* k, cons
   int st = check_dims(dims, &d);
   if (st != MSA_OK) return st;
   if (!q || !k || !v || !q_idx || !k_idx || !out) return MSA_ERR_INVALID_ARG;
+  if (d.nb > msa::kMaxInvertBlocks) return MSA_ERR_UNSUPPORTED;
   const PrefillLayout one = prefill_layout(d, 1);
   st = check_ws(ws, ws_bytes, one.total);
   if (st != MSA_OK) return st;
@@ -289,7 +287,7 @@ int msa_prefill(const msa_dims* dims, const uint16_t* q, const uint16_t* k, cons
   int8_t* bkeys = reinterpret_cast<int8_t*>(base + L.block_keys);
   int32_t* sel_use = sel ? sel : reinterpret_cast<int32_t*>(base + L.sel);
   int32_t* counts = reinterpret_cast<int32_t*>(base + L.counts);
-  int32_t* fill = reinterpret_cast<int32_t*>(base + L.fill);
+  int32_t* hist = reinterpret_cast<int32_t*>(base + L.hist);
   int32_t* row_ptr = reinterpret_cast<int32_t*>(base + L.row_ptr);
   int32_t* item_ptr = reinterpret_cast<int32_t*>(base + L.item_ptr);
   uint32_t* entries = reinterpret_cast<uint32_t*>(base + L.entries);
@@ -301,13 +299,14 @@ int msa_prefill(const msa_dims* dims, const uint16_t* q, const uint16_t* k, cons
   const int U = (int)d.U, S = (int)d.S, bs = (int)d.bs, nb = (int)d.nb, K = (int)d.k;
   const int nblk = U * nb;
   MSA_LAUNCH_NAMED("pool", s, msa::launch_pool(k_idx, bkeys, U, S, bs, s));
-  if (d.kp > 0) MSA_LAUNCH_NAMED("fill", s, msa::launch_fill_i32(counts, 0, (size_t)nblk, s));
-  if (d.kp > 0) MSA_LAUNCH_NAMED("fill", s, msa::launch_fill_i32(fill, 0, (size_t)nblk, s));
-  MSA_LAUNCH_NAMED("index_topk", s, msa::launch_index_topk(q_idx, bkeys, sel_use, d.kp > 0 ? counts : nullptr, U, S, bs, K, s));
+  MSA_LAUNCH_NAMED("index_topk", s, msa::launch_index_topk(q_idx, bkeys, sel_use, U, S, bs, K, s));
   if (d.kp > 0) {
-    MSA_LAUNCH_NAMED("scan", s, msa::launch_scan(counts, row_ptr, item_ptr, nblk, (int)L.tokens_per_item, s));
-    MSA_LAUNCH_NAMED("build_items", s, msa::launch_build_items(row_ptr, item_ptr, items, nblk, (int)L.tokens_per_item, s));
-    MSA_LAUNCH_NAMED("scatter", s, msa::launch_scatter(sel_use, row_ptr, fill, entries, U, S, bs, K, nb, s));
+    const int nch = (int)L.n_chunks, tpc = (int)L.tokens_per_chunk, tpi = (int)L.tokens_per_item;
+    MSA_LAUNCH_NAMED("chunk_hist", s, msa::launch_chunk_hist(sel_use, hist, U, S, nb, bs, K, tpc, nch, s));
+    MSA_LAUNCH_NAMED("chunk_total", s, msa::launch_chunk_total(hist, counts, U, nb, nch, s));
+    MSA_LAUNCH_NAMED("scan", s, msa::launch_scan(counts, row_ptr, item_ptr, nblk, tpi, s));
+    MSA_LAUNCH_NAMED("offsets_items", s, msa::launch_offsets_items(hist, row_ptr, item_ptr, items, U, nb, nch, tpi, s));
+    MSA_LAUNCH_NAMED("scatter", s, msa::launch_scatter(sel_use, hist, entries, U, S, nb, bs, K, tpc, nch, s));
   }
   msa::PrefillShape sh;
   sh.B = (int)d.B;
@@ -354,16 +353,14 @@ int msa_decode(const msa_dims* dims, const uint16_t* q, const int8_t* q_idx, con
   sh.bs = (int)d.bs;
   sh.nb = (int)d.nb;
   sh.top_k = (int)d.k;
-  sh.n_chunks = L.n_chunks;
-  sh.chunk = L.chunk;
   sh.scale_log2 = d.scale * 1.4426950408889634f;
-  int64_t* chunk_best = reinterpret_cast<int64_t*>(base + L.chunk_best);
   float* part_o = reinterpret_cast<float*>(base + L.part_o);
   float* part_ml = reinterpret_cast<float*>(base + L.part_ml);
-  int32_t* counters = reinterpret_cast<int32_t*>(base + L.counters);
+  int32_t* sel_use = sel ? sel : reinterpret_cast<int32_t*>(base + L.sel);
   hipStream_t s = (hipStream_t)stream;
-  MSA_LAUNCH_NAMED("decode_index", s, msa::launch_decode_index(sh, q_idx, block_keys, chunk_best, counters, s));
-  MSA_LAUNCH_NAMED("decode_attend", s, msa::launch_decode_attend(sh, q, k_cache, v_cache, chunk_best, sel, part_o, part_ml, counters, out, s));
+  MSA_LAUNCH_NAMED("decode_index", s, msa::launch_decode_index(sh, q_idx, block_keys, sel_use, s));
+  MSA_LAUNCH_NAMED("decode_attend", s, msa::launch_decode_attend(sh, q, k_cache, v_cache, sel_use, part_o, part_ml, s));
+  MSA_LAUNCH_NAMED("decode_merge", s, msa::launch_decode_merge(sh, part_o, part_ml, out, s));
   return MSA_OK;
 }
 

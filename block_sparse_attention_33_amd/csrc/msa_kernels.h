@@ -22,26 +22,33 @@ struct PrefillShape {
 hipError_t launch_pool(const int8_t* k_idx, int8_t* block_keys, int units, int S, int bs,
                        hipStream_t st);
 
-// Scores + per-(query, group) top-k.  counts (nullable) [U, nb] receives,
-// for every query, +1 on each selected block before the query's own block.
-hipError_t launch_index_topk(const int8_t* q_idx, const int8_t* block_keys, int32_t* sel,
-                             int32_t* counts, int units, int S, int bs, int top_k, hipStream_t st);
+// Scores + per-(query, group) top-k -> sel [U, S, top_k].
+hipError_t launch_index_topk(const int8_t* q_idx, const int8_t* block_keys, int32_t* sel, int units,
+                             int S, int bs, int top_k, hipStream_t st);
 
 hipError_t launch_fill_i32(int32_t* p, int32_t value, size_t n, hipStream_t st);
 
-// Query -> block inversion.
-//   scan:    counts [n] -> row_ptr [n + 1], item_ptr [n + 1] (exclusive, int32),
-//            items of a block = ceil(count / tokens_per_item)
-//   items:   item list {block id, first entry} for every block
-//   scatter: entries[row_ptr[blk] + pos] = (t << 5) | slot for every
-//            selected off-diagonal block of every query
+// Query -> block inversion (no global atomics).  Queries are cut into
+// n_chunks chunks of tpc tokens; H [U, n_chunks, nb] int32 holds per-chunk
+// block counts, then (in place) each chunk's first position in a block list.
+//   chunk_hist:    sel -> H (counts of kept blocks before the own block)
+//   chunk_total:   H -> counts [U * nb]
+//   scan:          counts -> row_ptr [n + 1], item_ptr [n + 1] (exclusive),
+//                  items of a block = ceil(count / tokens_per_item)
+//   offsets_items: H -> chunk offsets (in place); item list {block id, first entry}
+//   scatter:       entries[...] = (t << 5) | slot for every kept block before
+//                  the query's own block
+constexpr int kMaxInvertBlocks = 36864;  // nb limit: LDS histogram of nb int32
+hipError_t launch_chunk_hist(const int32_t* sel, int32_t* H, int units, int S, int nb, int bs, int top_k,
+                             int tpc, int n_chunks, hipStream_t st);
+hipError_t launch_chunk_total(const int32_t* H, int32_t* counts, int units, int nb, int n_chunks,
+                              hipStream_t st);
 hipError_t launch_scan(const int32_t* counts, int32_t* row_ptr, int32_t* item_ptr, int n,
                        int tokens_per_item, hipStream_t st);
-hipError_t launch_build_items(const int32_t* row_ptr, const int32_t* item_ptr, int2* items, int n,
-                              int tokens_per_item, hipStream_t st);
-hipError_t launch_scatter(const int32_t* sel, const int32_t* row_ptr, int32_t* fill,
-                          uint32_t* entries, int units, int S, int bs, int top_k, int nb,
-                          hipStream_t st);
+hipError_t launch_offsets_items(int32_t* H, const int32_t* row_ptr, const int32_t* item_ptr, int2* items,
+                                int units, int nb, int n_chunks, int tokens_per_item, hipStream_t st);
+hipError_t launch_scatter(const int32_t* sel, const int32_t* H, uint32_t* entries, int units, int S, int nb,
+                          int bs, int top_k, int tpc, int n_chunks, hipStream_t st);
 
 // Main branch, off-diagonal blocks: one work item = one KV block and up to
 // kItemRows query rows that selected it; writes normalised bf16 partials and
@@ -59,14 +66,17 @@ hipError_t launch_diag_merge(const PrefillShape& sh, const uint16_t* q, const ui
 
 // Decode.
 struct DecodeShape {
-  int B, L, Hq, G, r, bs, nb, top_k, n_chunks, chunk;
+  int B, L, Hq, G, r, bs, nb, top_k;
   float scale_log2;
 };
+constexpr int kDecodeCandPerThread = 32;  // candidates per thread of the index workgroup
+constexpr int kDecodeMaxCandidates = 256 * kDecodeCandPerThread;
 hipError_t launch_decode_index(const DecodeShape& sh, const int8_t* q_idx, const int8_t* block_keys,
-                               int64_t* chunk_best, int32_t* counters, hipStream_t st);
+                               int32_t* sel_out, hipStream_t st);
 hipError_t launch_decode_attend(const DecodeShape& sh, const uint16_t* q, const uint16_t* k_cache,
-                                const uint16_t* v_cache, const int64_t* chunk_best, int32_t* sel,
-                                float* part_o, float* part_ml, int32_t* counters, uint16_t* out,
+                                const uint16_t* v_cache, const int32_t* sel, float* part_o, float* part_ml,
                                 hipStream_t st);
+hipError_t launch_decode_merge(const DecodeShape& sh, const float* part_o, const float* part_ml, uint16_t* out,
+                               hipStream_t st);
 
 }  // namespace msa

@@ -53,8 +53,8 @@
  *
  * Limits: head_dim 128, idx_dim 64, block_size 32, 64 or 128, 1 <= top_k <=
  * 32, n_q_heads = r * n_kv_heads with r in {1, 2, 4, 8, 16}, S < 2^26 and
- * B * G * S * top_k < 2^31; decode needs ceil((nb - 1) / 512) * (top_k - 1)
- * <= 4096.  Anything else returns MSA_ERR_UNSUPPORTED.
+ * B * G * S * top_k < 2^31; prefill needs nb <= 36864 and decode
+ * nb <= 8193.  Anything else returns MSA_ERR_UNSUPPORTED.
  */
 #ifndef MSA_H
 #define MSA_H

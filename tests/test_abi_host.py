@@ -117,8 +117,18 @@ def _a(x):
     return (x + 255) // 256 * 256
 
 
+def _chunks(U, S, nb):
+    """Token chunks of the inversion: n = min(ceil(S / 256), max(1, 2^22 // (U nb)))
+    chunks of a multiple of 256 tokens."""
+    n = max(1, min(-(-S // 256), max(1, (1 << 22) // (U * nb))))
+    t = -(-S // n)
+    t = -(-t // 256) * 256
+    return -(-S // t), t
+
+
 @pytest.mark.parametrize("B,S,Hq,G,bs,k", [(1, 32768, 64, 8, 128, 16), (1, 2048, 8, 1, 64, 8),
-                                           (2, 1000, 8, 2, 32, 5), (1, 777, 16, 1, 128, 1)])
+                                           (2, 1000, 8, 2, 32, 5), (1, 777, 16, 1, 128, 1),
+                                           (1, 1048576, 64, 8, 128, 16)])
 def test_prefill_workspace_layout(lib, B, S, Hq, G, bs, k):
     """The documented layout: fixed part + one bf16 partial (r x 128) and one
     fp32 log-sum-exp (r) per (token, kept earlier block) per unit in a pass."""
@@ -129,21 +139,28 @@ def test_prefill_workspace_layout(lib, B, S, Hq, G, bs, k):
     nb = -(-S // bs)
     tpi = 256 // r
     items = U * ((S * kp + tpi - 1) // tpi + nb) + 1
-    fixed = (_a(U * nb * 64) + _a(U * S * k * 4) + 2 * _a(U * nb * 4) + 2 * _a((U * nb + 1) * 4)
-             + _a(U * S * kp * 4) + _a(items * 8))
+    n_chunks, _ = _chunks(U, S, nb)
+    fixed = (_a(U * nb * 64) + _a(U * S * k * 4) + _a(U * nb * 4) + _a(U * n_chunks * nb * 4)
+             + 2 * _a((U * nb + 1) * 4) + _a(U * S * kp * 4) + _a(items * 8))
     part = lambda n: _a(n * S * kp * r * 128 * 2) + _a(n * S * kp * r * 4)  # noqa: E731
     assert lo == fixed + part(1)
     assert hi == fixed + part(U)
+
+
+def test_prefill_block_limit(lib):
+    assert _ws(lib, _lib.MSA_OP_PREFILL, D(seq_len=36864 * 32, block_size=32, top_k=2, n_kv_heads=1,
+                                           n_q_heads=1))[0] == 0
+    assert _ws(lib, _lib.MSA_OP_PREFILL, D(seq_len=36864 * 32 + 1, block_size=32, top_k=2, n_kv_heads=1,
+                                           n_q_heads=1))[0] == -2
 
 
 def test_decode_workspace_layout(lib):
     dims = D(batch=16, seq_len=262144)
     st, lo, hi = _ws(lib, _lib.MSA_OP_DECODE, dims)
     U, k, r = 16 * 8, 16, 8
-    n_chunks = -(-(2048 - 1) // 128)
-    exp = _a(U * n_chunks * (k - 1) * 8) + _a(U * k * r * 128 * 4) + _a(U * k * r * 2 * 4) + _a(U * 4) + _a(U * k * 4)
+    exp = _a(U * k * r * 128 * 4) + _a(U * k * r * 2 * 4) + _a(U * k * 4)
     assert st == 0 and lo == hi == exp
-    # huge caches need larger chunks; beyond the merge capacity the call is unsupported
-    st, _, _ = _ws(lib, _lib.MSA_OP_DECODE, D(batch=1, seq_len=(1 << 26) - 1, n_kv_heads=8, top_k=32))
-    assert st == -2
+    # at most 8192 candidate blocks before the own block
+    assert _ws(lib, _lib.MSA_OP_DECODE, D(batch=1, seq_len=8193 * 128))[0] == 0
+    assert _ws(lib, _lib.MSA_OP_DECODE, D(batch=1, seq_len=8193 * 128 + 1))[0] == -2
     assert _ws(lib, _lib.MSA_OP_INDEX, dims)[1:] == (0, 0)
