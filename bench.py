@@ -3,8 +3,8 @@
 
 One step = one whole hot path: msa_prefill on the 32K-token prefill workload
 (batch 1, 64 query / 8 KV heads, head dim 128, blocks of 128, top_k 16:
-pooling, index top-k, inversion, off-diagonal main branch, own block +
-merge) followed by one msa_decode on the decode workload (16 sequences over
+pooling, index top-k, query->block inversion, KV-outer attention over every
+kept block, partial merge) followed by one msa_decode on the decode workload (16 sequences over
 262144-token caches, same heads).  Inputs are seeded synthetic tensors
 already resident in HBM.  Prints one JSON line.
 
@@ -28,16 +28,18 @@ CPU_SAMPLE_ROWS = 6144      # oracle rows timed on the host (about 15-20 s, one 
 
 
 def _prefill_counts(w):
-    """Algorithmic work of one prefill: attended keys per query head and the
-    off-diagonal (query row, kept earlier block) pairs."""
+    """Algorithmic work of one prefill: attended keys summed over queries
+    (per query head) and the (query row, kept block) pairs, own block
+    included."""
     import numpy as np
     t = np.arange(w.seq_len, dtype=np.int64)
     own = t // w.block_size
     kept = np.minimum(w.top_k - 1, own)
     keys = kept * w.block_size + (t % w.block_size) + 1
-    per_head_keys = int(keys.sum()) * w.batch          # summed over queries, per query head
-    offdiag_pairs = int(kept.sum()) * w.batch * w.n_q_heads
-    return per_head_keys, offdiag_pairs
+    per_head_keys = int(keys.sum()) * w.batch
+    pairs = int((kept + 1).sum()) * w.batch * w.n_q_heads
+    rows_merged = int((own > 0).sum()) * w.batch * w.n_q_heads   # rows with partials to merge
+    return per_head_keys, pairs, rows_merged
 
 
 def _decode_bytes(w):
@@ -51,7 +53,9 @@ def _decode_bytes(w):
     return q + q_idx + summaries + kv + out
 
 
-def _kernel_hash():
+def kernel_source_hash():
+    """Hash of the main-branch kernel source; counter summaries are valid only
+    for the source they were taken on."""
     h = hashlib.sha256()
     with open(os.path.join(ROOT, "block_sparse_attention_33_amd", "csrc", "main_branch.hip"), "rb") as f:
         h.update(f.read())
@@ -59,22 +63,49 @@ def _kernel_hash():
 
 
 def _measured_traffic():
-    """Per-launch HBM bytes of the off-diagonal kernel from the committed
-    rocprofv3 counter summary, if it was taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", "main_offdiag_prefill_32k_traffic.json")
+    """HBM bytes per launch of the attention kernel from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary (already scaled by the copy
+    kernel calibration), if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "attend_prefill_32k_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_sha256_16") != _kernel_hash():
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
     return rec.get("bytes_per_launch")
+
+
+def pmc_run():
+    """Workload for counter runs under rocprofv3 --pmc: two 32K prefills,
+    then a 1 GiB device copy whose bytes are known (the calibration of the
+    FETCH_SIZE / WRITE_SIZE counters)."""
+    import torch
+    import block_sparse_attention_33_amd as msa
+    from synth import get_workload, prefill_inputs
+    dev = torch.device("cuda:0")
+    w = get_workload("prefill_32k")
+    inp = prefill_inputs(w, seed=0, device=dev)
+    ws = torch.empty(msa.msa_workspace_bytes(
+        msa.MSA_OP_PREFILL, msa.make_dims(w.batch, w.seq_len, w.n_q_heads, w.n_kv_heads, w.block_size,
+                                           w.top_k))[1], dtype=torch.uint8, device=dev)
+    for _ in range(2):
+        msa.msa_prefill(inp["q"], inp["k"], inp["v"], inp["q_idx"], inp["k_idx"], w.block_size, w.top_k,
+                        workspace=ws)
+    src = torch.ones(2**30 // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"pmc_run": "done", "copy_bytes_each_way": 2**30,
+                      "kernel_source_sha256_16": kernel_source_hash()}))
 
 
 def cpu_baseline_worker(npz_path):
     """Runs in a child process with one BLAS/OpenMP thread: the oracle on the
     sampled rows.  Prints a JSON line with the time."""
     import numpy as np
+    if hasattr(os, "sched_setaffinity"):
+        os.sched_setaffinity(0, {min(os.sched_getaffinity(0))})
     from oracle import msa_oracle as O
     d = np.load(npz_path)
     rows = d["rows"]
@@ -123,9 +154,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-baseline-worker", default=None, help=argparse.SUPPRESS)
+    ap.add_argument("--pmc-run", action="store_true",
+                    help="run the counter-collection workload instead of the benchmark")
     args = ap.parse_args()
     if args.cpu_baseline_worker:
         cpu_baseline_worker(args.cpu_baseline_worker)
+        return 0
+    if args.pmc_run:
+        pmc_run()
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -188,23 +224,29 @@ def main():
     dec_med = dec_ms[len(dec_ms) // 2]
     ms_per_step = wall * 1e3 / args.steps
 
-    per_head_keys, offdiag_pairs = _prefill_counts(wp)
+    per_head_keys, pairs, rows_merged = _prefill_counts(wp)
     D = wp.head_dim
     flop_alg = 4.0 * D * wp.n_q_heads * per_head_keys
     tokens = wp.batch * wp.seq_len
-    offdiag_flop = 4.0 * D * wp.block_size * offdiag_pairs
-    n_off, off_ms = kt.get("main_offdiag", (0, 0.0))
-    off_avg_ms = off_ms / max(1, n_off)
-    off_tflops = offdiag_flop / (off_avg_ms * 1e-3) / 1e12 if off_avg_ms > 0 else None
-    # bytes the KV-outer design moves per off-diagonal row pair: gathered Q
-    # row (256 B) + bf16 partial (256 B) + fp32 log-sum-exp (4 B)
-    off_design_bytes = offdiag_pairs * (2 * D + 2 * D + 4)
+    # dominant kernel: the attention kernel (all selected blocks of every
+    # query); per step it may run in several launches (passes)
+    n_att, att_ms = kt.get("attend", (0, 0.0))
+    att_ms_step = att_ms / args.steps
+    att_launch_ms = att_ms / max(1, n_att)
+    launches_per_step = max(1, n_att // args.steps)
+    att_tflops = flop_alg / (att_ms_step * 1e-3) / 1e12 if att_ms_step > 0 else None
+    # bytes the KV-outer design moves: per (query row, kept block) pair a
+    # gathered Q row (256 B) and a bf16 partial + fp32 log-sum-exp (260 B)
+    att_design_bytes = pairs * (2 * D + 2 * D + 4)
+    n_mrg, mrg_ms = kt.get("merge", (0, 0.0))
+    mrg_ms_step = mrg_ms / args.steps
+    mrg_design_bytes = (pairs - (tokens * wp.n_q_heads - rows_merged)) * (2 * D + 4) + rows_merged * 2 * D
     dbytes = _decode_bytes(wd)
     traffic = _measured_traffic()
 
     kernels = {k: {"launches": n, "avg_ms": round(ms / max(1, n), 4)} for k, (n, ms) in sorted(kt.items())}
     rec = {
-        "metric": "MSA prefill tokens/s (32K prefill); decode tokens/s and HBM GB/s in 'decode'",
+        "metric": "MSA prefill tokens/s + TFLOP/s (% bf16 MFMA peak); decode tokens/s, HBM GB/s",
         "value": round(tokens / (pre_med * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -235,17 +277,23 @@ def main():
             "bytes_alg": dbytes,
         },
         "roofline": {
-            "kernel": "main_offdiag (KV-outer off-diagonal blocks)",
+            "kernel": "attend (KV-outer block attention, all kept blocks)",
             "bound": "mfma",
-            "achieved": round(off_tflops, 2) if off_tflops else None,
+            "achieved": round(att_tflops, 2) if att_tflops else None,
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
-            "frac": round(off_tflops / PEAK_BF16_TFLOPS, 4) if off_tflops else None,
+            "frac": round(att_tflops / PEAK_BF16_TFLOPS, 4) if att_tflops else None,
             "traffic": traffic,
-            "avg_launch_ms": round(off_avg_ms, 4),
-            "flop_per_launch": offdiag_flop,
-            "design_bytes_per_launch": off_design_bytes,
-            "design_hbm_gbs": round(off_design_bytes / (off_avg_ms * 1e-3) / 1e9, 1) if off_avg_ms else None,
+            "avg_launch_ms": round(att_launch_ms, 4),
+            "launches_per_step": launches_per_step,
+            "flop_per_launch": flop_alg / launches_per_step,
+            "design_bytes_per_step": att_design_bytes,
+            "design_hbm_gbs": round(att_design_bytes / (att_ms_step * 1e-3) / 1e9, 1) if att_ms_step else None,
+        },
+        "merge_kernel": {
+            "ms": round(mrg_ms_step, 4),
+            "design_bytes": mrg_design_bytes,
+            "hbm_gbs": round(mrg_design_bytes / (mrg_ms_step * 1e-3) / 1e9, 1) if mrg_ms_step else None,
         },
         "kernels": kernels,
     }

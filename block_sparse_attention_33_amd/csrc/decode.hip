@@ -61,14 +61,14 @@ __device__ __forceinline__ void wave_topk_regs(int64_t (&k)[NK], int kp, int64_t
 }
 
 // ---------------------------------------------------------------------------
-// Index: one workgroup (256 threads) per unit.  Thread i scores candidates
-// i, i + 256, ... (up to kDecodeCandPerThread of them), every wave keeps its
-// best kp, and wave 0 picks the best kp of the 4 x kp survivors.
+// Index: one workgroup (1024 threads) per unit.  Thread i scores candidates
+// i, i + 1024, ... (up to kDecodeCandPerThread of them), each of the 16
+// waves keeps its best kp, and wave 0 picks the best kp of the survivors.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void decode_index_kernel(const int8_t* __restrict__ q_idx,
-                                                           const int8_t* __restrict__ block_keys,
-                                                           int32_t* __restrict__ sel_ws, DecodeShape sh) {
-  __shared__ int64_t wbest[4][32];
+__global__ __launch_bounds__(1024) void decode_index_kernel(const int8_t* __restrict__ q_idx,
+                                                            const int8_t* __restrict__ block_keys,
+                                                            int32_t* __restrict__ sel_out, DecodeShape sh) {
+  __shared__ int64_t wbest[16][32];
   __shared__ int64_t best[32];
   const int u = blockIdx.x;
   const int tid = threadIdx.x;
@@ -82,43 +82,47 @@ __global__ __launch_bounds__(256) void decode_index_kernel(const int8_t* __restr
   int64_t keys[kDecodeCandPerThread];
 #pragma unroll
   for (int m = 0; m < kDecodeCandPerThread; ++m) {
-    const int j = tid + 256 * m;
+    const int j = tid + 1024 * m;
     int64_t key = kNoKey;
-    if (j < own) {
-      const i32x4_t* sp = reinterpret_cast<const i32x4_t*>(kb + (size_t)j * kIdxDim);
+    if (1024 * m < own) {  // uniform: the loads below are unconditional within it
+      const i32x4_t* sp = reinterpret_cast<const i32x4_t*>(kb + (size_t)min(j, own - 1) * kIdxDim);
       const i32x4_t a0 = sp[0], a1 = sp[1], a2 = sp[2], a3 = sp[3];
       int s = 0;
       s = sdot4(q0.x, a0.x, s); s = sdot4(q0.y, a0.y, s); s = sdot4(q0.z, a0.z, s); s = sdot4(q0.w, a0.w, s);
       s = sdot4(q1.x, a1.x, s); s = sdot4(q1.y, a1.y, s); s = sdot4(q1.z, a1.z, s); s = sdot4(q1.w, a1.w, s);
       s = sdot4(q2.x, a2.x, s); s = sdot4(q2.y, a2.y, s); s = sdot4(q2.z, a2.z, s); s = sdot4(q2.w, a2.w, s);
       s = sdot4(q3.x, a3.x, s); s = sdot4(q3.y, a3.y, s); s = sdot4(q3.z, a3.z, s); s = sdot4(q3.w, a3.w, s);
-      key = rank_key(s, j);
+      key = j < own ? rank_key(s, j) : kNoKey;
     }
     keys[m] = key;
   }
   wave_topk_regs(keys, kp, wbest[w]);
   __syncthreads();
-  if (w == 0) {
-    int64_t k2[2];
-    k2[0] = (tid < 4 * kp) ? wbest[tid / kp][tid % kp] : kNoKey;
-    k2[1] = (tid + 64 < 4 * kp) ? wbest[(tid + 64) / kp][(tid + 64) % kp] : kNoKey;
-    wave_topk_regs(k2, kp, best);
+  if (w == 0 && kp > 0) {
+    int64_t k8[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int i = tid + 64 * m;
+      k8[m] = (i < 16 * kp) ? wbest[i / kp][i % kp] : kNoKey;
+    }
+    wave_topk_regs(k8, kp, best);
   }
   __syncthreads();
   if (tid == 0) {
     // ascending block order of the kept candidates, then the own block
     const int n_valid = min(kp, own);
-    int32_t* out = sel_ws + (size_t)u * sh.top_k;
+    int32_t* out = sel_out + (size_t)u * sh.top_k;
+    int x[32];
     for (int i = 0; i < n_valid; ++i) {
       const int y = key_block(best[i]);
       int m = i - 1;
-      while (m >= 0 && out[m] > y) {
-        out[m + 1] = out[m];
+      while (m >= 0 && x[m] > y) {
+        x[m + 1] = x[m];
         --m;
       }
-      out[m + 1] = y;
+      x[m + 1] = y;
     }
-    for (int i = n_valid; i < sh.top_k; ++i) out[i] = (i == n_valid) ? own : -1;
+    for (int i = 0; i < sh.top_k; ++i) out[i] = i < n_valid ? x[i] : (i == n_valid ? own : -1);
   }
 }
 
@@ -126,16 +130,19 @@ __global__ __launch_bounds__(256) void decode_index_kernel(const int8_t* __restr
 // Attend: one workgroup (4 waves) per (slot, unit); wave w takes keys
 // 32 w .. 32 w + 31 of the slot's block (blocks of 32 or 64 keys leave waves
 // idle).  S^T = K Q^T on 32x32x16 MFMA with the query heads as columns
-// (r <= 16 of the 32 used); O^T = V^T P^T likewise, the V^T fragments
-// gathered with 16-bit loads.  Partial = (o unnormalised, max m, sum l) per
-// head, base 2.
+// (r <= 16 of the 32 used), K fragments straight from HBM; O^T = V^T P^T
+// likewise, V staged through LDS transposed (head dim major).  Partial =
+// (o unnormalised, max m, sum l) per head, base 2.
 // ---------------------------------------------------------------------------
+constexpr int kDecVtStride = 2 * 128 + 8;  // bytes per head-dim row of V^T
+
 __global__ __launch_bounds__(256) void decode_attend_kernel(const uint16_t* __restrict__ q,
                                                             const uint16_t* __restrict__ k_cache,
                                                             const uint16_t* __restrict__ v_cache,
-                                                            const int32_t* __restrict__ sel_ws,
+                                                            const int32_t* __restrict__ sel,
                                                             float* __restrict__ part_o,
                                                             float* __restrict__ part_ml, DecodeShape sh) {
+  __shared__ __align__(16) char vt[kHeadDim * kDecVtStride];
   __shared__ float red_m[4][32];
   __shared__ float red_l[4][32];
   __shared__ float red_o[4][16][kHeadDim];
@@ -153,7 +160,7 @@ __global__ __launch_bounds__(256) void decode_attend_kernel(const uint16_t* __re
   float* po = part_o + ((size_t)u * sh.top_k + slot) * r * kHeadDim;
   float* pml = part_ml + ((size_t)u * sh.top_k + slot) * r * 2;
 
-  const int j = sel_ws[(size_t)u * sh.top_k + slot];
+  const int j = sel[(size_t)u * sh.top_k + slot];
   if (j < 0) {
     if (tid < r) {
       pml[2 * tid] = -__builtin_inff();
@@ -166,6 +173,17 @@ __global__ __launch_bounds__(256) void decode_attend_kernel(const uint16_t* __re
   const int kbase = 32 * w;                // this wave's first key
   const bool wave_live = kbase < nk;
 
+  // V: thread takes key pairs (2p, 2p + 1) x 8 head dims, 16-byte loads
+  const uint16_t* vblk = v_cache + ((size_t)u * sh.L + key0) * kHeadDim;
+  u32x4_t va[4], vb[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int qid = tid + 256 * m;
+    const int p = qid & 63, c = qid >> 6;
+    const int k0 = min(2 * p, nk - 1), k1 = min(2 * p + 1, nk - 1);
+    va[m] = *reinterpret_cast<const u32x4_t*>(vblk + (size_t)k0 * kHeadDim + 8 * c);
+    vb[m] = *reinterpret_cast<const u32x4_t*>(vblk + (size_t)k1 * kHeadDim + 8 * c);
+  }
   // K fragments (A) straight from HBM; Q^T (B) for columns < r
   u32x4_t kf[8], qf[8];
   const int key = kbase + col;
@@ -177,22 +195,17 @@ __global__ __launch_bounds__(256) void decode_attend_kernel(const uint16_t* __re
     qf[ks] = *reinterpret_cast<const u32x4_t*>(qrow + 16 * ks + 8 * hf);
     if (col >= r) qf[ks] = u32x4_t{0u, 0u, 0u, 0u};
   }
-  // V^T fragments: d = 32 dt + col, keys kbase + 16 h2 + 4 hf + {0..3} and + 8
-  uint32_t vf[4][2][4];
-  const uint16_t* vblk = v_cache + ((size_t)u * sh.L + key0) * kHeadDim;
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
+  for (int m = 0; m < 4; ++m) {
+    const int qid = tid + 256 * m;
+    const int p = qid & 63, c = qid >> 6;
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // dword e holds keys (k0, k0 + 1): e < 2 -> the first run of 4, else the second
-        const int k0 = kbase + 16 * h2 + 4 * hf + (e < 2 ? 2 * e : 8 + 2 * (e - 2));
-        const int ka = min(k0, nk - 1), kb2 = min(k0 + 1, nk - 1);
-        const uint32_t lo = vblk[(size_t)ka * kHeadDim + 32 * dt + col];
-        const uint32_t hi = vblk[(size_t)kb2 * kHeadDim + 32 * dt + col];
-        vf[dt][h2][e] = lo | (hi << 16);
-      }
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t lo = va[m][e], hi = vb[m][e];
+      *reinterpret_cast<uint32_t*>(vt + (8 * c + 2 * e) * kDecVtStride + 4 * p) = (lo & 0xffffu) | (hi << 16);
+      *reinterpret_cast<uint32_t*>(vt + (8 * c + 2 * e + 1) * kDecVtStride + 4 * p) = (lo >> 16) | (hi & 0xffff0000u);
+    }
+  }
 
   // scores S^T (32 keys x 32 heads) of this wave, base 2
   f32x16_t s = f32x16_t{};
@@ -208,7 +221,7 @@ __global__ __launch_bounds__(256) void decode_attend_kernel(const uint16_t* __re
   }
   mx = wave_max_pair(mx);
   if (hf == 0) red_m[w][col] = mx;
-  __syncthreads();
+  __syncthreads();  // also publishes V^T
   const float m = fmaxf(fmaxf(red_m[0][col], red_m[1][col]), fmaxf(red_m[2][col], red_m[3][col]));
   float sum = 0.f;
   u32x4_t pk[2];
@@ -234,8 +247,10 @@ __global__ __launch_bounds__(256) void decode_attend_kernel(const uint16_t* __re
     o[dt] = f32x16_t{};
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
-      const u32x4_t a = u32x4_t{vf[dt][h2][0], vf[dt][h2][1], vf[dt][h2][2], vf[dt][h2][3]};
-      o[dt] = mfma32x32x16(a, pk[h2], o[dt]);
+      const char* pv = vt + (32 * dt + col) * kDecVtStride + 2 * (kbase + 16 * h2 + 4 * hf);
+      const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(pv);
+      const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(pv + 16);
+      o[dt] = mfma32x32x16(u32x4_t{lo.x, lo.y, hi.x, hi.y}, pk[h2], o[dt]);
     }
   }
   // sum the four waves' O^T in LDS (columns < r only)
@@ -256,51 +271,63 @@ __global__ __launch_bounds__(256) void decode_attend_kernel(const uint16_t* __re
   }
 }
 
-// One workgroup per unit: out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
-__global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restrict__ part_o,
+// One workgroup per (unit, head), thread = head dim:
+// out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
+__global__ __launch_bounds__(128) void decode_merge_kernel(const float* __restrict__ part_o,
                                                            const float* __restrict__ part_ml,
                                                            uint16_t* __restrict__ out, DecodeShape sh) {
   const int u = blockIdx.x;
+  const int h = blockIdx.y;
+  const int d = threadIdx.x;
   const int b = u / sh.G;
   const int g = u - b * sh.G;
   const int r = sh.r;
   const float* pml = part_ml + (size_t)u * sh.top_k * r * 2;
   const float* po = part_o + (size_t)u * sh.top_k * r * kHeadDim;
-  for (int i = threadIdx.x; i < r * kHeadDim; i += 256) {
-    const int h = i / kHeadDim;
-    float M = -__builtin_inff();
-    for (int s = 0; s < sh.top_k; ++s) M = fmaxf(M, pml[(s * r + h) * 2]);
-    float W = 0.f, acc = 0.f;
-    for (int s = 0; s < sh.top_k; ++s) {
-      const float ms = pml[(s * r + h) * 2];
-      if (ms == -__builtin_inff()) continue;
-      const float wgt = fast_exp2(ms - M);
-      W += wgt * pml[(s * r + h) * 2 + 1];
-      acc += wgt * po[(size_t)(s * r) * kHeadDim + i];
+  float ms[32], ls[32], os[32];
+#pragma unroll
+  for (int s = 0; s < 32; ++s) {
+    if (s < sh.top_k) {
+      ms[s] = pml[(s * r + h) * 2];
+      ls[s] = pml[(s * r + h) * 2 + 1];
+      os[s] = po[(size_t)(s * r + h) * kHeadDim + d];
     }
-    out[((size_t)b * sh.Hq + g * r) * kHeadDim + i] = to_bf16(acc / W);
   }
+  float M = -__builtin_inff();
+#pragma unroll
+  for (int s = 0; s < 32; ++s)
+    if (s < sh.top_k) M = fmaxf(M, ms[s]);
+  float W = 0.f, acc = 0.f;
+#pragma unroll
+  for (int s = 0; s < 32; ++s) {
+    if (s < sh.top_k && ms[s] != -__builtin_inff()) {
+      const float wgt = fast_exp2(ms[s] - M);
+      W = fmaf(wgt, ls[s], W);
+      acc = fmaf(wgt, os[s], acc);
+    }
+  }
+  out[((size_t)b * sh.Hq + g * r + h) * kHeadDim + d] = to_bf16(acc / W);
 }
 
 }  // namespace
 
 hipError_t launch_decode_index(const DecodeShape& sh, const int8_t* q_idx, const int8_t* block_keys,
-                               int32_t* sel_ws, hipStream_t st) {
-  hipLaunchKernelGGL(decode_index_kernel, dim3(sh.B * sh.G), dim3(256), 0, st, q_idx, block_keys, sel_ws, sh);
+                               int32_t* sel_out, hipStream_t st) {
+  hipLaunchKernelGGL(decode_index_kernel, dim3(sh.B * sh.G), dim3(1024), 0, st, q_idx, block_keys, sel_out, sh);
   return hipGetLastError();
 }
 
 hipError_t launch_decode_attend(const DecodeShape& sh, const uint16_t* q, const uint16_t* k_cache,
-                                const uint16_t* v_cache, const int32_t* sel_ws, float* part_o, float* part_ml,
+                                const uint16_t* v_cache, const int32_t* sel, float* part_o, float* part_ml,
                                 hipStream_t st) {
   hipLaunchKernelGGL(decode_attend_kernel, dim3(sh.top_k, sh.B * sh.G), dim3(256), 0, st, q, k_cache, v_cache,
-                     sel_ws, part_o, part_ml, sh);
+                     sel, part_o, part_ml, sh);
   return hipGetLastError();
 }
 
 hipError_t launch_decode_merge(const DecodeShape& sh, const float* part_o, const float* part_ml, uint16_t* out,
                                hipStream_t st) {
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(sh.B * sh.G), dim3(256), 0, st, part_o, part_ml, out, sh);
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(sh.B * sh.G, sh.r), dim3(128), 0, st, part_o, part_ml, out, sh);
   return hipGetLastError();
 }
 

@@ -18,40 +18,50 @@ namespace msa {
 namespace {
 
 // Per-chunk histograms: one workgroup per (token chunk, unit) counts, in LDS,
-// how many of the chunk's queries kept each block before their own block,
+// how many of the chunk's queries kept each block (the own block included),
 // and stores the counts as H[u][chunk][block].  LDS atomics only.
+__device__ __forceinline__ void chunk_tokens(const ChunkPlan& cp, int c, int S, int* t0, int* t1) {
+  const int rng = c / cp.m;
+  const int i = c - rng * cp.m;
+  *t0 = rng * cp.T + i * cp.tpc;
+  *t1 = min(min(S, (rng + 1) * cp.T), *t0 + cp.tpc);
+}
+
 __global__ __launch_bounds__(256) void chunk_hist_kernel(const int32_t* __restrict__ sel,
                                                          int32_t* __restrict__ H, int S, int nb,
-                                                         int bs_log2, int top_k, int tpc, int n_chunks) {
+                                                         int bs_log2, int top_k, ChunkPlan cp) {
   extern __shared__ int32_t hist[];
   const int c = blockIdx.x;
   const int u = blockIdx.y;
+  const int n_chunks = cp.n_chunks;
   for (int j = threadIdx.x; j < nb; j += 256) hist[j] = 0;
   __syncthreads();
-  const int t0 = c * tpc;
-  const int t1 = min(S, t0 + tpc);
+  int t0, t1;
+  chunk_tokens(cp, c, S, &t0, &t1);
   const int kp = top_k - 1;
   for (int t = t0 + (int)threadIdx.x; t < t1; t += 256) {
-    const int nv = min(kp, t >> bs_log2);
+    const int nv = min(kp, t >> bs_log2);  // slot nv holds the own block
     const int32_t* srow = sel + ((size_t)u * S + t) * top_k;
-    for (int s = 0; s < nv; ++s) atomicAdd(&hist[srow[s]], 1);
+    for (int s = 0; s <= nv; ++s) atomicAdd(&hist[srow[s]], 1);
   }
   __syncthreads();
   int32_t* dst = H + ((size_t)u * n_chunks + c) * nb;
   for (int j = threadIdx.x; j < nb; j += 256) dst[j] = hist[j];
 }
 
-// Per (unit, block): total over the chunks -> counts.
+// Per row (unit, range, block): total over the range's chunks -> counts.
 __global__ __launch_bounds__(256) void chunk_total_kernel(const int32_t* __restrict__ H,
                                                           int32_t* __restrict__ counts, int units, int nb,
-                                                          int n_chunks) {
+                                                          ChunkPlan cp) {
   const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= units * nb) return;
-  const int u = i / nb;
-  const int j = i - u * nb;
-  const int32_t* src = H + (size_t)u * n_chunks * nb + j;
+  if (i >= units * cp.n_ranges * nb) return;
+  const int u = i / (cp.n_ranges * nb);
+  const int rem = i - u * cp.n_ranges * nb;
+  const int rng = rem / nb;
+  const int j = rem - rng * nb;
+  const int32_t* src = H + ((size_t)u * cp.n_chunks + (size_t)rng * cp.m) * nb + j;
   int total = 0;
-  for (int c = 0; c < n_chunks; ++c) total += src[(size_t)c * nb];
+  for (int c = 0; c < cp.m; ++c) total += src[(size_t)c * nb];
   counts[i] = total;
 }
 
@@ -99,21 +109,23 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
   }
 }
 
-// Per (unit, block): turn the chunk counts into the chunks' first positions
-// in the block's list (in place), and write the block's work items
-// {block id, first entry}.
+// Per row (unit, range, block): turn the range's chunk counts into the
+// chunks' first positions in the row's list (in place), and write the row's
+// work items {row id, first entry}.
 __global__ __launch_bounds__(256) void offsets_items_kernel(int32_t* __restrict__ H,
                                                             const int32_t* __restrict__ row_ptr,
                                                             const int32_t* __restrict__ item_ptr,
                                                             int2* __restrict__ items, int units, int nb,
-                                                            int n_chunks, int tpi) {
+                                                            ChunkPlan cp, int tpi) {
   const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= units * nb) return;
-  const int u = i / nb;
-  const int j = i - u * nb;
-  int32_t* col = H + (size_t)u * n_chunks * nb + j;
+  if (i >= units * cp.n_ranges * nb) return;
+  const int u = i / (cp.n_ranges * nb);
+  const int rem = i - u * cp.n_ranges * nb;
+  const int rng = rem / nb;
+  const int j = rem - rng * nb;
+  int32_t* col = H + ((size_t)u * cp.n_chunks + (size_t)rng * cp.m) * nb + j;
   int run = row_ptr[i];
-  for (int c = 0; c < n_chunks; ++c) {
+  for (int c = 0; c < cp.m; ++c) {
     const int x = col[(size_t)c * nb];
     col[(size_t)c * nb] = run;
     run += x;
@@ -130,20 +142,20 @@ __global__ __launch_bounds__(256) void offsets_items_kernel(int32_t* __restrict_
 __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ sel,
                                                       const int32_t* __restrict__ H,
                                                       uint32_t* __restrict__ entries, int S, int nb,
-                                                      int bs_log2, int top_k, int tpc, int n_chunks) {
+                                                      int bs_log2, int top_k, ChunkPlan cp) {
   extern __shared__ int32_t cursor[];
   const int c = blockIdx.x;
   const int u = blockIdx.y;
-  const int32_t* src = H + ((size_t)u * n_chunks + c) * nb;
+  const int32_t* src = H + ((size_t)u * cp.n_chunks + c) * nb;
   for (int j = threadIdx.x; j < nb; j += 256) cursor[j] = src[j];
   __syncthreads();
-  const int t0 = c * tpc;
-  const int t1 = min(S, t0 + tpc);
+  int t0, t1;
+  chunk_tokens(cp, c, S, &t0, &t1);
   const int kp = top_k - 1;
   for (int t = t0 + (int)threadIdx.x; t < t1; t += 256) {
-    const int nv = min(kp, t >> bs_log2);
+    const int nv = min(kp, t >> bs_log2);  // slot nv holds the own block
     const int32_t* srow = sel + ((size_t)u * S + t) * top_k;
-    for (int s = 0; s < nv; ++s) {
+    for (int s = 0; s <= nv; ++s) {
       const int pos = atomicAdd(&cursor[srow[s]], 1);
       entries[pos] = ((uint32_t)t << 5) | (uint32_t)s;
     }
@@ -153,7 +165,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
 }  // namespace
 
 hipError_t launch_chunk_hist(const int32_t* sel, int32_t* H, int units, int S, int nb, int bs, int top_k,
-                             int tpc, int n_chunks, hipStream_t st) {
+                             const ChunkPlan& cp, hipStream_t st) {
   int bs_log2 = 0;
   while ((1 << bs_log2) < bs) ++bs_log2;
   const size_t lds = (size_t)nb * 4;
@@ -161,15 +173,15 @@ hipError_t launch_chunk_hist(const int32_t* sel, int32_t* H, int units, int S, i
                                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                                      kMaxInvertBlocks * 4);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(chunk_hist_kernel, dim3(n_chunks, units), dim3(256), lds, st, sel, H, S, nb, bs_log2, top_k,
-                     tpc, n_chunks);
+  hipLaunchKernelGGL(chunk_hist_kernel, dim3(cp.n_chunks, units), dim3(256), lds, st, sel, H, S, nb, bs_log2,
+                     top_k, cp);
   return hipGetLastError();
 }
 
-hipError_t launch_chunk_total(const int32_t* H, int32_t* counts, int units, int nb, int n_chunks,
+hipError_t launch_chunk_total(const int32_t* H, int32_t* counts, int units, int nb, const ChunkPlan& cp,
                               hipStream_t st) {
-  const int n = units * nb;
-  hipLaunchKernelGGL(chunk_total_kernel, dim3((n + 255) / 256), dim3(256), 0, st, H, counts, units, nb, n_chunks);
+  const int n = units * cp.n_ranges * nb;
+  hipLaunchKernelGGL(chunk_total_kernel, dim3((n + 255) / 256), dim3(256), 0, st, H, counts, units, nb, cp);
   return hipGetLastError();
 }
 
@@ -180,15 +192,15 @@ hipError_t launch_scan(const int32_t* counts, int32_t* row_ptr, int32_t* item_pt
 }
 
 hipError_t launch_offsets_items(int32_t* H, const int32_t* row_ptr, const int32_t* item_ptr, int2* items,
-                                int units, int nb, int n_chunks, int tokens_per_item, hipStream_t st) {
-  const int n = units * nb;
+                                int units, int nb, const ChunkPlan& cp, int tokens_per_item, hipStream_t st) {
+  const int n = units * cp.n_ranges * nb;
   hipLaunchKernelGGL(offsets_items_kernel, dim3((n + 255) / 256), dim3(256), 0, st, H, row_ptr, item_ptr, items,
-                     units, nb, n_chunks, tokens_per_item);
+                     units, nb, cp, tokens_per_item);
   return hipGetLastError();
 }
 
 hipError_t launch_scatter(const int32_t* sel, const int32_t* H, uint32_t* entries, int units, int S, int nb,
-                          int bs, int top_k, int tpc, int n_chunks, hipStream_t st) {
+                          int bs, int top_k, const ChunkPlan& cp, hipStream_t st) {
   int bs_log2 = 0;
   while ((1 << bs_log2) < bs) ++bs_log2;
   const size_t lds = (size_t)nb * 4;
@@ -196,8 +208,8 @@ hipError_t launch_scatter(const int32_t* sel, const int32_t* H, uint32_t* entrie
                                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                                      kMaxInvertBlocks * 4);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(scatter_kernel, dim3(n_chunks, units), dim3(256), lds, st, sel, H, entries, S, nb, bs_log2,
-                     top_k, tpc, n_chunks);
+  hipLaunchKernelGGL(scatter_kernel, dim3(cp.n_chunks, units), dim3(256), lds, st, sel, H, entries, S, nb, bs_log2,
+                     top_k, cp);
   return hipGetLastError();
 }
 

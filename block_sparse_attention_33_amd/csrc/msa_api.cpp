@@ -63,46 +63,83 @@ int check_dims(const msa_dims* d, Dims* o) {
   return MSA_OK;
 }
 
-// ---- prefill workspace: fixed part + partials for `units_per_pass` units
-struct PrefillLayout {
-  size_t block_keys, sel, counts, hist, row_ptr, item_ptr, entries, items, part_o, part_lse, total;
-  long max_items_per_unit, tokens_per_item, n_chunks, tokens_per_chunk;
+// ---- prefill planning
+//
+// The main branch runs in passes.  When the partials of one (unit, query
+// range) pass fit kPassPartialBudget and a range still gathers enough queries
+// per KV block, each unit is split into query ranges of T tokens so that the
+// partials written by the off-diagonal kernel are read back by the merge
+// kernel while they still sit in the 256 MB memory-side cache.  Otherwise a
+// unit is one range (T >= S) and a pass takes as many units as the
+// workspace holds.
+constexpr size_t kPassPartialBudget = 128ull << 20;
+// Measured on MI355X at 32K tokens: ranged passes leave about one work item
+// per CU per pass, and the passes' load imbalance costs more than the cache
+// residency of the partials saves, so one pass over all units is used.
+constexpr bool kUseQueryRanges = false;
+constexpr long kMaxRows = 1L << 22;      // CSR rows (unit, range, block)
+constexpr long kMaxChunkCounters = 1L << 22;
+
+struct PrefillPlan {
+  long T, n_ranges, m, tpc, n_chunks, rows, tokens_per_item, max_items_per_range;
+  bool ranged;
 };
 
-// Token chunks of the inversion: enough workgroups, and at most ~4 M
-// per-chunk block counters.
-void plan_chunks(const Dims& d, long* n_chunks, long* tpc) {
-  const long by_tokens = (d.S + 255) / 256;
-  const long by_size = std::max(1L, (1L << 22) / (d.U * d.nb));
-  long n = std::max(1L, std::min(by_tokens, by_size));
-  long t = (d.S + n - 1) / n;
-  t = (t + 255) / 256 * 256;
-  *tpc = t;
-  *n_chunks = (d.S + t - 1) / t;
+PrefillPlan plan_prefill(const Dims& d) {
+  PrefillPlan p{};
+  p.tokens_per_item = msa::kItemChunks * msa::kItemRows / d.r;
+  const long S256 = (d.S + 255) / 256 * 256;
+  p.ranged = false;
+  p.T = S256;
+  {
+    const long per_tok = d.k * d.r * (2 * d.D + 4);
+    const long t_mall = (long)(kPassPartialBudget / per_tok) / 256 * 256;
+    // about 32 queries per (range, block) row at the far end of the sequence
+    const long t_reuse = (32 * d.nb / d.k + 255) / 256 * 256;
+    if (kUseQueryRanges && t_mall >= 256 && t_mall >= t_reuse && t_mall < d.S &&
+        d.U * ((d.S + t_mall - 1) / t_mall) * d.nb <= kMaxRows) {
+      p.ranged = true;
+      p.T = t_mall;
+    }
+  }
+  p.n_ranges = (d.S + p.T - 1) / p.T;
+  p.rows = d.U * p.n_ranges * d.nb;
+  // chunks per range: tokens multiple of 256, bounded number of counters
+  const long by_tokens = p.T / 256;
+  const long by_size = std::max(1L, kMaxChunkCounters / (d.U * p.n_ranges * d.nb));
+  p.m = std::max(1L, std::min(by_tokens, by_size));
+  p.tpc = (p.T / 256 + p.m - 1) / p.m * 256;
+  p.m = (p.T + p.tpc - 1) / p.tpc;
+  p.n_chunks = p.n_ranges * p.m;
+  const long range_tok = std::min(p.T, d.S);
+  p.max_items_per_range = (range_tok * d.k + p.tokens_per_item - 1) / p.tokens_per_item + d.nb;
+  return p;
 }
 
-PrefillLayout prefill_layout(const Dims& d, long units_per_pass) {
+struct PrefillLayout {
+  size_t block_keys, sel, counts, hist, row_ptr, item_ptr, entries, items, part_o, part_lse, total;
+};
+
+// Workspace: fixed part + partials of `units_per_pass` units of pass_tokens.
+PrefillLayout prefill_layout(const Dims& d, const PrefillPlan& p, long units_per_pass) {
   PrefillLayout L{};
-  L.tokens_per_item = msa::kItemRows / d.r;
-  plan_chunks(d, &L.n_chunks, &L.tokens_per_chunk);
-  L.max_items_per_unit = (d.S * d.kp + L.tokens_per_item - 1) / L.tokens_per_item + d.nb;
-  const long nblk = d.U * d.nb;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
     off += align_up(bytes);
     return at;
   };
-  L.block_keys = take((size_t)nblk * d.di);
+  const long pass_tokens = std::min(p.T, d.S);
+  L.block_keys = take((size_t)d.U * d.nb * d.di);
   L.sel = take((size_t)d.U * d.S * d.k * 4);
-  L.counts = take((size_t)nblk * 4);
-  L.hist = take((size_t)d.U * L.n_chunks * d.nb * 4);
-  L.row_ptr = take((size_t)(nblk + 1) * 4);
-  L.item_ptr = take((size_t)(nblk + 1) * 4);
-  L.entries = take((size_t)d.U * d.S * d.kp * 4);
-  L.items = take((size_t)(d.U * L.max_items_per_unit + 1) * 8);
-  L.part_o = take((size_t)units_per_pass * d.S * d.kp * d.r * d.D * 2);
-  L.part_lse = take((size_t)units_per_pass * d.S * d.kp * d.r * 4);
+  L.counts = take((size_t)p.rows * 4);
+  L.hist = take((size_t)d.U * p.n_chunks * d.nb * 4);
+  L.row_ptr = take((size_t)(p.rows + 1) * 4);
+  L.item_ptr = take((size_t)(p.rows + 1) * 4);
+  L.entries = take((size_t)d.U * d.S * d.k * 4);
+  L.items = take((size_t)(d.U * p.n_ranges * p.max_items_per_range + 1) * 8);
+  L.part_o = take((size_t)units_per_pass * pass_tokens * d.k * d.r * d.D * 2);
+  L.part_lse = take((size_t)units_per_pass * pass_tokens * d.k * d.r * 4);
   L.total = off;
   return L;
 }
@@ -220,11 +257,13 @@ int msa_workspace_bytes(int op, const msa_dims* dims, size_t* min_bytes, size_t*
     case MSA_OP_POOL:
     case MSA_OP_INDEX:
       break;
-    case MSA_OP_PREFILL:
+    case MSA_OP_PREFILL: {
       if (d.nb > msa::kMaxInvertBlocks) return MSA_ERR_UNSUPPORTED;
-      lo = prefill_layout(d, 1).total;
-      hi = prefill_layout(d, d.U).total;
+      const PrefillPlan p = plan_prefill(d);
+      lo = prefill_layout(d, p, 1).total;
+      hi = p.ranged ? lo : prefill_layout(d, p, d.U).total;
       break;
+    }
     case MSA_OP_DECODE: {
       DecodeLayout L;
       st = decode_layout(d, &L);
@@ -272,16 +311,18 @@ int msa_prefill(const msa_dims* dims, const uint16_t* q, const uint16_t* k, cons
   if (st != MSA_OK) return st;
   if (!q || !k || !v || !q_idx || !k_idx || !out) return MSA_ERR_INVALID_ARG;
   if (d.nb > msa::kMaxInvertBlocks) return MSA_ERR_UNSUPPORTED;
-  const PrefillLayout one = prefill_layout(d, 1);
+  const PrefillPlan P = plan_prefill(d);
+  const PrefillLayout one = prefill_layout(d, P, 1);
   st = check_ws(ws, ws_bytes, one.total);
   if (st != MSA_OK) return st;
-  // as many (batch, group) units per pass as the workspace holds
-  const size_t per_unit = prefill_layout(d, 2).total - one.total;
+  // unranged: as many (batch, group) units per pass as the workspace holds
   long upp = 1;
-  if (per_unit > 0) upp = std::min<long>(d.U, 1 + (long)((ws_bytes - one.total) / per_unit));
-  else upp = d.U;
-  PrefillLayout L = prefill_layout(d, upp);
-  while (L.total > ws_bytes && upp > 1) L = prefill_layout(d, --upp);
+  if (!P.ranged) {
+    const size_t per_unit = prefill_layout(d, P, 2).total - one.total;
+    upp = per_unit > 0 ? std::min<long>(d.U, 1 + (long)((ws_bytes - one.total) / per_unit)) : d.U;
+  }
+  PrefillLayout L = prefill_layout(d, P, upp);
+  while (L.total > ws_bytes && upp > 1) L = prefill_layout(d, P, --upp);
 
   char* base = static_cast<char*>(ws);
   int8_t* bkeys = reinterpret_cast<int8_t*>(base + L.block_keys);
@@ -297,17 +338,20 @@ int msa_prefill(const msa_dims* dims, const uint16_t* q, const uint16_t* k, cons
 
   hipStream_t s = (hipStream_t)stream;
   const int U = (int)d.U, S = (int)d.S, bs = (int)d.bs, nb = (int)d.nb, K = (int)d.k;
-  const int nblk = U * nb;
+  msa::ChunkPlan cp;
+  cp.T = (int)P.T;
+  cp.m = (int)P.m;
+  cp.tpc = (int)P.tpc;
+  cp.n_chunks = (int)P.n_chunks;
+  cp.n_ranges = (int)P.n_ranges;
+  const int tpi = (int)P.tokens_per_item;
   MSA_LAUNCH_NAMED("pool", s, msa::launch_pool(k_idx, bkeys, U, S, bs, s));
   MSA_LAUNCH_NAMED("index_topk", s, msa::launch_index_topk(q_idx, bkeys, sel_use, U, S, bs, K, s));
-  if (d.kp > 0) {
-    const int nch = (int)L.n_chunks, tpc = (int)L.tokens_per_chunk, tpi = (int)L.tokens_per_item;
-    MSA_LAUNCH_NAMED("chunk_hist", s, msa::launch_chunk_hist(sel_use, hist, U, S, nb, bs, K, tpc, nch, s));
-    MSA_LAUNCH_NAMED("chunk_total", s, msa::launch_chunk_total(hist, counts, U, nb, nch, s));
-    MSA_LAUNCH_NAMED("scan", s, msa::launch_scan(counts, row_ptr, item_ptr, nblk, tpi, s));
-    MSA_LAUNCH_NAMED("offsets_items", s, msa::launch_offsets_items(hist, row_ptr, item_ptr, items, U, nb, nch, tpi, s));
-    MSA_LAUNCH_NAMED("scatter", s, msa::launch_scatter(sel_use, hist, entries, U, S, nb, bs, K, tpc, nch, s));
-  }
+  MSA_LAUNCH_NAMED("chunk_hist", s, msa::launch_chunk_hist(sel_use, hist, U, S, nb, bs, K, cp, s));
+  MSA_LAUNCH_NAMED("chunk_total", s, msa::launch_chunk_total(hist, counts, U, nb, cp, s));
+  MSA_LAUNCH_NAMED("scan", s, msa::launch_scan(counts, row_ptr, item_ptr, (int)P.rows, tpi, s));
+  MSA_LAUNCH_NAMED("offsets_items", s, msa::launch_offsets_items(hist, row_ptr, item_ptr, items, U, nb, cp, tpi, s));
+  MSA_LAUNCH_NAMED("scatter", s, msa::launch_scatter(sel_use, hist, entries, U, S, nb, bs, K, cp, s));
   msa::PrefillShape sh;
   sh.B = (int)d.B;
   sh.S = S;
@@ -318,15 +362,37 @@ int msa_prefill(const msa_dims* dims, const uint16_t* q, const uint16_t* k, cons
   sh.bs_log2 = bs_log2_of(bs);
   sh.nb = nb;
   sh.top_k = K;
+  sh.n_ranges = (int)P.n_ranges;
+  sh.range_tokens = (int)P.T;
   sh.scale_log2 = d.scale * 1.4426950408889634f;
-  for (long u0 = 0; u0 < d.U; u0 += upp) {
-    const long u1 = std::min<long>(d.U, u0 + upp);
-    if (d.kp > 0) {
-      const long max_items = (u1 - u0) * L.max_items_per_unit;
-      MSA_LAUNCH_NAMED("main_offdiag", s, msa::launch_main_offdiag(sh, q, k, v, row_ptr, item_ptr, items, entries, part_o, part_lse,
-                                          (int)u0, (int)u1, (int)max_items, s));
+  const int pass_tokens = (int)std::min(P.T, d.S);
+  auto run_pass = [&](long u0, long u1, long rng) -> int {
+    msa::PassInfo ps;
+    ps.u0 = (int)u0;
+    ps.u1 = (int)u1;
+    ps.rng = (int)rng;
+    ps.t0 = (int)(rng * P.T);
+    ps.t1 = (int)std::min<long>(d.S, (rng + 1) * P.T);
+    ps.pass_tokens = pass_tokens;
+    ps.row_begin = (int)((u0 * P.n_ranges + rng) * nb);
+    ps.row_end = (int)(((u1 - 1) * P.n_ranges + rng + 1) * nb);
+    const long max_items = (u1 - u0) * P.max_items_per_range;
+    MSA_LAUNCH_NAMED("attend", s, msa::launch_attend(sh, ps, q, k, v, row_ptr, item_ptr, items, entries, part_o,
+                                                     part_lse, out, (int)max_items, s));
+    MSA_LAUNCH_NAMED("merge", s, msa::launch_merge(sh, ps, part_o, part_lse, out, s));
+    return MSA_OK;
+  };
+  if (P.ranged) {
+    for (long u = 0; u < d.U; ++u)
+      for (long rng = 0; rng < P.n_ranges; ++rng) {
+        st = run_pass(u, u + 1, rng);
+        if (st != MSA_OK) return st;
+      }
+  } else {
+    for (long u0 = 0; u0 < d.U; u0 += upp) {
+      st = run_pass(u0, std::min<long>(d.U, u0 + upp), 0);
+      if (st != MSA_OK) return st;
     }
-    MSA_LAUNCH_NAMED("diag_merge", s, msa::launch_diag_merge(sh, q, k, v, part_o, part_lse, out, (int)u0, (int)u1, s));
   }
   return MSA_OK;
 }

@@ -15,7 +15,17 @@ constexpr int kItemRows = 256;
 
 struct PrefillShape {
   int B, S, Hq, G, r, bs, bs_log2, nb, top_k;
+  int n_ranges;      // query ranges per unit: CSR rows are (unit, range, block)
+  int range_tokens;  // tokens per query range
   float scale_log2;  // softmax scale * log2(e)
+};
+
+// One pass of the main branch: units [u0, u1) x query range `rng` (always
+// range 0 when a unit has a single range).  Partials of the pass are indexed
+// ((u - u0) * pass_tokens + (t - t0)) * (top_k - 1) + slot.
+struct PassInfo {
+  int u0, u1, rng, t0, t1, pass_tokens;
+  int row_begin, row_end;  // CSR rows of the pass
 };
 
 // Block summary keys: k_idx [U, S, 64] -> block_keys [U, nb, 64].
@@ -28,49 +38,54 @@ hipError_t launch_index_topk(const int8_t* q_idx, const int8_t* block_keys, int3
 
 hipError_t launch_fill_i32(int32_t* p, int32_t value, size_t n, hipStream_t st);
 
-// Query -> block inversion (no global atomics).  Queries are cut into
-// n_chunks chunks of tpc tokens; H [U, n_chunks, nb] int32 holds per-chunk
-// block counts, then (in place) each chunk's first position in a block list.
-//   chunk_hist:    sel -> H (counts of kept blocks before the own block)
-//   chunk_total:   H -> counts [U * nb]
+// Query -> block inversion (no global atomics).  Each query range of T
+// tokens is cut into m chunks of tpc tokens (n_chunks = n_ranges * m per
+// unit); H [U, n_chunks, nb] int32 holds per-chunk block counts, then (in
+// place) each chunk's first position in its (unit, range, block) list.
+//   chunk_hist:    sel -> H (counts of kept blocks, the own block included)
+//   chunk_total:   H -> counts [U * n_ranges * nb]
 //   scan:          counts -> row_ptr [n + 1], item_ptr [n + 1] (exclusive),
-//                  items of a block = ceil(count / tokens_per_item)
-//   offsets_items: H -> chunk offsets (in place); item list {block id, first entry}
-//   scatter:       entries[...] = (t << 5) | slot for every kept block before
-//                  the query's own block
+//                  items of a row = ceil(count / tokens_per_item)
+//   offsets_items: H -> chunk offsets (in place); item list {row id, first entry}
+//   scatter:       entries[...] = (t << 5) | slot for every kept block (the
+//                  own block sits at slot min(top_k - 1, t / block_size))
 constexpr int kMaxInvertBlocks = 36864;  // nb limit: LDS histogram of nb int32
+struct ChunkPlan {
+  int T, m, tpc, n_chunks, n_ranges;
+};
 hipError_t launch_chunk_hist(const int32_t* sel, int32_t* H, int units, int S, int nb, int bs, int top_k,
-                             int tpc, int n_chunks, hipStream_t st);
-hipError_t launch_chunk_total(const int32_t* H, int32_t* counts, int units, int nb, int n_chunks,
+                             const ChunkPlan& cp, hipStream_t st);
+hipError_t launch_chunk_total(const int32_t* H, int32_t* counts, int units, int nb, const ChunkPlan& cp,
                               hipStream_t st);
 hipError_t launch_scan(const int32_t* counts, int32_t* row_ptr, int32_t* item_ptr, int n,
                        int tokens_per_item, hipStream_t st);
 hipError_t launch_offsets_items(int32_t* H, const int32_t* row_ptr, const int32_t* item_ptr, int2* items,
-                                int units, int nb, int n_chunks, int tokens_per_item, hipStream_t st);
+                                int units, int nb, const ChunkPlan& cp, int tokens_per_item, hipStream_t st);
 hipError_t launch_scatter(const int32_t* sel, const int32_t* H, uint32_t* entries, int units, int S, int nb,
-                          int bs, int top_k, int tpc, int n_chunks, hipStream_t st);
+                          int bs, int top_k, const ChunkPlan& cp, hipStream_t st);
 
-// Main branch, off-diagonal blocks: one work item = one KV block and up to
-// kItemRows query rows that selected it; writes normalised bf16 partials and
-// their base-2 log-sum-exp.  Items [item_ptr[u0 * nb], item_ptr[u1 * nb]).
-hipError_t launch_main_offdiag(const PrefillShape& sh, const uint16_t* q, const uint16_t* k,
-                               const uint16_t* v, const int32_t* row_ptr, const int32_t* item_ptr,
-                               const int2* items, const uint32_t* entries, uint16_t* part_o,
-                               float* part_lse, int u0, int u1, int max_items, hipStream_t st);
+// Main branch: one work item = one KV block of a (unit, range) row and up to
+// 4 chunks of kItemRows gathered query rows (the query's own block
+// included); writes normalised bf16 partials + base-2 log-sum-exp per
+// (token, selection slot, head), or the final output for rows of block 0.
+// Items [item_ptr[row_begin], item_ptr[row_end]).
+constexpr int kItemChunks = 4;
+hipError_t launch_attend(const PrefillShape& sh, const PassInfo& pass, const uint16_t* q, const uint16_t* k,
+                         const uint16_t* v, const int32_t* row_ptr, const int32_t* item_ptr, const int2* items,
+                         const uint32_t* entries, uint16_t* part_o, float* part_lse, uint16_t* out,
+                         int max_items, hipStream_t st);
 
-// Main branch, own (diagonal) block of every query + merge of the partials
-// -> out, for units [u0, u1).
-hipError_t launch_diag_merge(const PrefillShape& sh, const uint16_t* q, const uint16_t* k,
-                             const uint16_t* v, const uint16_t* part_o, const float* part_lse,
-                             uint16_t* out, int u0, int u1, hipStream_t st);
+// Merge of every partial of the pass's query rows (blocks >= 1) -> out.
+hipError_t launch_merge(const PrefillShape& sh, const PassInfo& pass, const uint16_t* part_o,
+                        const float* part_lse, uint16_t* out, hipStream_t st);
 
 // Decode.
 struct DecodeShape {
   int B, L, Hq, G, r, bs, nb, top_k;
   float scale_log2;
 };
-constexpr int kDecodeCandPerThread = 32;  // candidates per thread of the index workgroup
-constexpr int kDecodeMaxCandidates = 256 * kDecodeCandPerThread;
+constexpr int kDecodeCandPerThread = 8;  // candidates per thread of the 1024-thread index workgroup
+constexpr int kDecodeMaxCandidates = 1024 * kDecodeCandPerThread;
 hipError_t launch_decode_index(const DecodeShape& sh, const int8_t* q_idx, const int8_t* block_keys,
                                int32_t* sel_out, hipStream_t st);
 hipError_t launch_decode_attend(const DecodeShape& sh, const uint16_t* q, const uint16_t* k_cache,
