@@ -236,11 +236,11 @@ def main():
     launches_per_step = max(1, n_att // args.steps)
     att_tflops = flop_alg / (att_ms_step * 1e-3) / 1e12 if att_ms_step > 0 else None
     # bytes the KV-outer design moves: per (query row, kept block) pair a
-    # gathered Q row (256 B) and a bf16 partial + fp32 log-sum-exp (260 B)
-    att_design_bytes = pairs * (2 * D + 2 * D + 4)
+    # gathered Q row (256 B) and a bf16 partial + fp32 (max, sum) (264 B)
+    att_design_bytes = pairs * (2 * D + 2 * D + 8)
     n_mrg, mrg_ms = kt.get("merge", (0, 0.0))
     mrg_ms_step = mrg_ms / args.steps
-    mrg_design_bytes = (pairs - (tokens * wp.n_q_heads - rows_merged)) * (2 * D + 4) + rows_merged * 2 * D
+    mrg_design_bytes = (pairs - (tokens * wp.n_q_heads - rows_merged)) * (2 * D + 8) + rows_merged * 2 * D
     dbytes = _decode_bytes(wd)
     traffic = _measured_traffic()
 

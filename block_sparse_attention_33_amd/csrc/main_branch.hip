@@ -9,17 +9,19 @@
 // node "KV-outer gather Q").
 //
 //   attend_kernel  one work item = one KV block j of one (batch, group) unit
-//                  and up to 4 chunks of the query rows (tokens x heads) whose
-//                  selection holds j, the query's own block included.  K_j
-//                  and V_j^T go through LDS once per item; four waves take 64
-//                  gathered query rows of every chunk, two workgroups share a
-//                  CU so one's gathers overlap the other's MFMAs.  Every row
-//                  leaves a normalised bf16 partial and its base-2
-//                  log-sum-exp at its selection slot; rows whose own block is
-//                  block 0 (they attend nothing else) are written to the
-//                  output directly.  Chunks holding a query's own block apply
-//                  the causal mask and split P into two bf16 terms, so P.V
-//                  keeps ~16 mantissa bits for the first tokens of a sequence,
+//                  and up to 4 chunks of 256 query rows (tokens x heads) whose
+//                  selection holds j, the query's own block included.  The
+//                  kernel is persistent: one workgroup of four waves per CU
+//                  walks its items, K_j and V_j^T go through one of two LDS
+//                  buffers while the next item's block is staged into the
+//                  other, and each wave loads the 64 gathered query rows of
+//                  its next chunk during the current one.  Every row leaves an
+//                  unnormalised bf16 partial and its (max, sum) in base-2
+//                  units at its selection slot; rows with no other partial
+//                  (own block 0, or top_k = 1) are written to the output
+//                  directly.  Chunks holding a query's own block apply the
+//                  causal mask and split P into two bf16 terms, so P.V keeps
+//                  ~16 mantissa bits for the first tokens of a sequence,
 //                  which see only a few keys.
 //   merge_kernel   log-sum-exp merge of a query row's partials -> out.
 //
@@ -33,6 +35,8 @@
 //
 // Partial rows hold their 128 values lane-half-major: position
 // 64 * hf + 16 * dt + i is head dim 32 * dt + 8 * (i / 4) + 4 * hf + i % 4.
+
+#include <algorithm>
 
 #include "msa_device.h"
 #include "msa_kernels.h"
@@ -51,36 +55,60 @@ struct Tile {
   static constexpr int kLdsBytes = kKBytes + kVtBytes;
 };
 
-// Copy K rows [0, n_keys) of a block into LDS (zero beyond n_keys) and V
-// transposed (head dim major), with NT threads.
+// A K/V block staged in registers on its way to LDS: NT threads, K as
+// 16-byte pieces of key rows, V as pairs of key rows (2p, 2p + 1) x 8 head
+// dims so that V^T can be written as dwords holding two keys.
 template <int BS, int NT>
-__device__ __forceinline__ void load_kv_lds(const uint16_t* __restrict__ kblk,
-                                            const uint16_t* __restrict__ vblk, int n_keys,
-                                            char* __restrict__ lds) {
-  using T = Tile<BS>;
+struct KvStage {
+  static constexpr int kK = BS * 16 / NT;
+  static constexpr int kV = BS * 8 / NT;
+  u32x4_t k[kK];
+  u32x4_t va[kV], vb[kV];
+};
+
+// Issue the loads of a block (rows beyond n_keys are clamped to a valid row
+// and zeroed when written, so every load is unconditional and in flight at
+// once).
+template <int BS, int NT>
+__device__ __forceinline__ void load_kv_regs(const uint16_t* __restrict__ kblk, const uint16_t* __restrict__ vblk,
+                                             int n_keys, KvStage<BS, NT>& st) {
   const int tid = threadIdx.x;
-  // K: 16-byte chunks, 16 per key row
 #pragma unroll
-  for (int m = 0; m < BS * 16 / NT; ++m) {
+  for (int m = 0; m < KvStage<BS, NT>::kK; ++m) {
     const int qid = tid + NT * m;
-    const int key = qid >> 4;
-    const int c = qid & 15;
-    // unconditional (clamped) loads, so that all of them are in flight at once
-    u32x4_t val = *reinterpret_cast<const u32x4_t*>(kblk + min(key, n_keys - 1) * kHeadDim + c * 8);
-    if (key >= n_keys) val = u32x4_t{0u, 0u, 0u, 0u};
-    *reinterpret_cast<u32x4_t*>(lds + key * kKStride + c * 16) = val;
+    st.k[m] = *reinterpret_cast<const u32x4_t*>(kblk + min(qid >> 4, n_keys - 1) * kHeadDim + (qid & 15) * 8);
   }
-  // V^T: a thread takes keys (2p, 2p + 1) x 8 head dims and writes 8 dwords
-  char* vt = lds + T::kKBytes;
 #pragma unroll
-  for (int m = 0; m < BS * 8 / NT; ++m) {
+  for (int m = 0; m < KvStage<BS, NT>::kV; ++m) {
     const int qid = tid + NT * m;
     const int p = qid % (BS / 2);
     const int c = qid / (BS / 2);
-    u32x4_t a = *reinterpret_cast<const u32x4_t*>(vblk + min(2 * p, n_keys - 1) * kHeadDim + c * 8);
-    u32x4_t b = *reinterpret_cast<const u32x4_t*>(vblk + min(2 * p + 1, n_keys - 1) * kHeadDim + c * 8);
-    if (2 * p >= n_keys) a = u32x4_t{0u, 0u, 0u, 0u};
-    if (2 * p + 1 >= n_keys) b = u32x4_t{0u, 0u, 0u, 0u};
+    st.va[m] = *reinterpret_cast<const u32x4_t*>(vblk + min(2 * p, n_keys - 1) * kHeadDim + c * 8);
+    st.vb[m] = *reinterpret_cast<const u32x4_t*>(vblk + min(2 * p + 1, n_keys - 1) * kHeadDim + c * 8);
+  }
+}
+
+// Write a staged block to LDS: K key-major (rows of kKStride bytes), V
+// transposed (head dim major, rows of kVtStride bytes).
+template <int BS, int NT>
+__device__ __forceinline__ void store_kv_lds(const KvStage<BS, NT>& st, int n_keys, char* __restrict__ lds) {
+  using T = Tile<BS>;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int m = 0; m < KvStage<BS, NT>::kK; ++m) {
+    const int qid = tid + NT * m;
+    const int key = qid >> 4;
+    const u32x4_t val = key < n_keys ? st.k[m] : u32x4_t{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4_t*>(lds + key * kKStride + (qid & 15) * 16) = val;
+  }
+  char* vt = lds + T::kKBytes;
+#pragma unroll
+  for (int m = 0; m < KvStage<BS, NT>::kV; ++m) {
+    const int qid = tid + NT * m;
+    const int p = qid % (BS / 2);
+    const int c = qid / (BS / 2);
+    const u32x4_t a = 2 * p < n_keys ? st.va[m] : u32x4_t{0u, 0u, 0u, 0u};
+    const u32x4_t b = 2 * p + 1 < n_keys ? st.vb[m] : u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const uint32_t lo = (e == 0) ? a.x : (e == 1) ? a.y : (e == 2) ? a.z : a.w;
@@ -117,217 +145,335 @@ __device__ __forceinline__ u32x4_t vt_frag(const char* lds, int dt, int kt, int 
   return r;
 }
 
-// One column tile's rows: rows whose own block is block 0 attend nothing else
-// and are written to the output; every other row leaves its partial (lane-
-// half-major bf16) and base-2 log-sum-exp at (token, slot, head).
-__device__ __forceinline__ void store_rows(const f32x16_t (&o)[4], float m2, float l, bool live, int tok,
-                                           int slot, int head, int hf, int b, int g, int K, size_t pass_row0,
-                                           const PrefillShape& sh, uint16_t* __restrict__ part_o,
-                                           float* __restrict__ part_lse, uint16_t* __restrict__ out) {
-  if (!live) return;
+// Final output of a row whose own block is block 0 (it attends nothing
+// else): o / l in bf16.
+__device__ __forceinline__ void store_final(const f32x16_t (&o)[4], float l, int tok, int head, int hf, int b,
+                                            int g, const PrefillShape& sh, uint16_t* __restrict__ out) {
   const float inv = 1.0f / l;
-  if ((tok >> sh.bs_log2) == 0) {
-    uint16_t* orow = out + (((size_t)b * sh.S + tok) * sh.Hq + g * sh.r + head) * kHeadDim;
+  uint16_t* orow = out + (((size_t)b * sh.S + tok) * sh.Hq + g * sh.r + head) * kHeadDim;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+  for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        u32x2_t wv;
-        wv.x = pack_bf16x2(o[dt][4 * q4 + 0] * inv, o[dt][4 * q4 + 1] * inv);
-        wv.y = pack_bf16x2(o[dt][4 * q4 + 2] * inv, o[dt][4 * q4 + 3] * inv);
-        *reinterpret_cast<u32x2_t*>(orow + 32 * dt + 8 * q4 + 4 * hf) = wv;
-      }
-    return;
-  }
-  const size_t pidx = ((pass_row0 + tok) * K + slot) * sh.r + head;
+    for (int q4 = 0; q4 < 4; ++q4) {
+      u32x2_t wv;
+      wv.x = pack_bf16x2(o[dt][4 * q4 + 0] * inv, o[dt][4 * q4 + 1] * inv);
+      wv.y = pack_bf16x2(o[dt][4 * q4 + 2] * inv, o[dt][4 * q4 + 3] * inv);
+      *reinterpret_cast<u32x2_t*>(orow + 32 * dt + 8 * q4 + 4 * hf) = wv;
+    }
+}
+
+// Partial of a row at (token, slot, head): the unnormalised sum
+// o = sum_s 2^(z_s - m2) v_s in bf16 (lane-half-major) and (m2, l) with
+// l = sum_s 2^(z_s - m2), z in base-2 units.
+__device__ __forceinline__ void store_partial(const f32x16_t (&o)[4], float m2, float l, int tok, int slot,
+                                              int head, int hf, int K, int r, size_t pass_row0,
+                                              uint16_t* __restrict__ part_o, float2* __restrict__ part_ml) {
+  const size_t pidx = ((pass_row0 + tok) * K + slot) * r + head;
   uint16_t* dst = part_o + pidx * kHeadDim + 64 * hf;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) {
     u32x4_t w0, w1;
-    w0.x = pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv);
-    w0.y = pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv);
-    w0.z = pack_bf16x2(o[dt][4] * inv, o[dt][5] * inv);
-    w0.w = pack_bf16x2(o[dt][6] * inv, o[dt][7] * inv);
-    w1.x = pack_bf16x2(o[dt][8] * inv, o[dt][9] * inv);
-    w1.y = pack_bf16x2(o[dt][10] * inv, o[dt][11] * inv);
-    w1.z = pack_bf16x2(o[dt][12] * inv, o[dt][13] * inv);
-    w1.w = pack_bf16x2(o[dt][14] * inv, o[dt][15] * inv);
+    w0.x = pack_bf16x2(o[dt][0], o[dt][1]);
+    w0.y = pack_bf16x2(o[dt][2], o[dt][3]);
+    w0.z = pack_bf16x2(o[dt][4], o[dt][5]);
+    w0.w = pack_bf16x2(o[dt][6], o[dt][7]);
+    w1.x = pack_bf16x2(o[dt][8], o[dt][9]);
+    w1.y = pack_bf16x2(o[dt][10], o[dt][11]);
+    w1.z = pack_bf16x2(o[dt][12], o[dt][13]);
+    w1.w = pack_bf16x2(o[dt][14], o[dt][15]);
     *reinterpret_cast<u32x4_t*>(dst + 16 * dt) = w0;
     *reinterpret_cast<u32x4_t*>(dst + 16 * dt + 8) = w1;
   }
-  if (hf == 0) part_lse[pidx] = m2 + fast_log2(l);
+  if (hf == 0) part_ml[pidx] = make_float2(m2, l);
 }
 
 // ---------------------------------------------------------------------------
-// Attention over one KV block for the gathered query rows of a work item.
+// Attention over the KV blocks of work items.  Persistent: one workgroup per
+// CU walks a static list of items; while it computes item i, the K/V block
+// of item i + 1 is loaded into registers and written to the second LDS
+// buffer, and every chunk's gathered query rows are loaded during the
+// previous chunk.
 // ---------------------------------------------------------------------------
+struct ItemDesc {
+  int e0, n_ent, j, u;  // first entry, entries, block, unit
+};
+
+__device__ __forceinline__ ItemDesc decode_item(const int2* __restrict__ items, const int32_t* __restrict__ row_ptr,
+                                                int idx, int n_ranges, int nb, int tpi) {
+  const int2 item = items[idx];
+  ItemDesc d;
+  d.u = item.x / (n_ranges * nb);
+  d.j = item.x % nb;
+  d.e0 = row_ptr[item.x] + item.y;
+  d.n_ent = min(tpi, row_ptr[item.x + 1] - d.e0);
+  return d;
+}
+
 template <int BS>
-__global__ __launch_bounds__(256, 2) void attend_kernel(
+__global__ __launch_bounds__(256, 1) void attend_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ item_ptr,
     const int2* __restrict__ items, const uint32_t* __restrict__ entries,
-    uint16_t* __restrict__ part_o, float* __restrict__ part_lse, uint16_t* __restrict__ out,
+    uint16_t* __restrict__ part_o, float2* __restrict__ part_ml, uint16_t* __restrict__ out,
     PrefillShape sh, PassInfo pass, int r_log2) {
   constexpr int KT = Tile<BS>::KT;
-  extern __shared__ __align__(16) char lds[];
+  extern __shared__ __align__(16) char lds[];  // two K/V buffers
 
-  // items of this pass, spread so that each XCD takes a contiguous range
+  // items of this pass, dealt round-robin: items are ordered by (unit,
+  // block), so the whole chip works on one unit's queries at a time and
+  // their gathered rows stay in the memory-side cache
   const int i_begin = item_ptr[pass.row_begin];
-  const int n_items = item_ptr[pass.row_end] - i_begin;
-  const int per_xcd = (n_items + 7) >> 3;
-  const int bid = blockIdx.x;
-  const int slot_in_xcd = bid >> 3;
-  const int it = (bid & 7) * per_xcd + slot_in_xcd;
-  if (slot_in_xcd >= per_xcd || it >= n_items) return;
-
-  const int2 item = items[i_begin + it];
-  const int bi = item.x;  // CSR row (unit, range, block)
-  const int u = bi / (sh.n_ranges * sh.nb);
-  const int j = bi % sh.nb;
-  const int e0 = row_ptr[bi] + item.y;
-  const int tpc = kItemRows >> r_log2;  // tokens per chunk
-  const int n_ent = min(kItemChunks * tpc, row_ptr[bi + 1] - e0);
-  const int n_chunks = (n_ent + tpc - 1) / tpc;
-  const int b = u / sh.G;
-  const int g = u - b * sh.G;
+  const int it_end = item_ptr[pass.row_end] - i_begin;
+  const int stride = gridDim.x;
+  int it = blockIdx.x;
+  if (it >= it_end) return;
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;  // rows 64 w .. 64 w + 63 of every chunk
   const int hf = lane >> 5;
   const int K = sh.top_k;
   const float c2 = sh.scale_log2;
-  const int key0 = j * BS;
-  const size_t pass_row0 = (size_t)(u - pass.u0) * pass.pass_tokens - pass.t0;
-  const uint16_t* qbase = q + ((size_t)b * sh.S * sh.Hq + g * sh.r) * kHeadDim;
+  const int tpc = kItemRows >> r_log2;  // tokens per chunk
+  const int tpi = kItemChunks * tpc;    // tokens per item
+  const size_t pass_row0 = (size_t)0 - pass.t0;
 
-  // entries of chunk c (clamped: always a valid entry, no branch)
-  auto entry_of = [&](int c, int ct) -> uint32_t {
-    const int tk = c * tpc + ((64 * w + 32 * ct + (lane & 31)) >> r_log2);
-    return entries[e0 + min(tk, n_ent - 1)];
+  auto q_base = [&](int u) -> const uint16_t* {
+    const int b = u / sh.G;
+    return q + ((size_t)b * sh.S * sh.Hq + (u - b * sh.G) * sh.r) * kHeadDim;
   };
-  uint32_t ent[2];
-#pragma unroll
-  for (int ct = 0; ct < 2; ++ct) ent[ct] = entry_of(0, ct);
-
-  const size_t kv_off = ((size_t)u * sh.S + (size_t)j * BS) * kHeadDim;
-  load_kv_lds<BS, 256>(k + kv_off, v + kv_off, min(BS, sh.S - j * BS), lds);
-  __syncthreads();
-
-  for (int c = 0; c < n_chunks; ++c) {
-    // keep the LDS fragment reads inside the loop (hoisted they would need
-    // far more registers than a wave has)
-    __asm__ volatile("" ::: "memory");
-    int tok[2], slot[2], head[2];
-    bool live[2];
-    u32x4_t qf[2][8];
+  // entry of column tile ct at chunk c of item d (clamped to the item)
+  auto entry_of = [&](const ItemDesc& d, int c, int ct) -> uint32_t {
+    const int tk = c * tpc + ((64 * w + 32 * ct + (lane & 31)) >> r_log2);
+    return entries[d.e0 + min(tk, d.n_ent - 1)];
+  };
+  auto load_q = [&](const uint16_t* qb, const uint32_t (&e)[2], u32x4_t (&qf)[2][8]) {
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
       const int qr = 64 * w + 32 * ct + (lane & 31);
-      live[ct] = c * tpc + (qr >> r_log2) < n_ent;
-      tok[ct] = (int)(ent[ct] >> 5);
-      slot[ct] = (int)(ent[ct] & 31u);
-      head[ct] = qr & (sh.r - 1);
-      load_q_frag(qbase + ((size_t)tok[ct] * sh.Hq + head[ct]) * kHeadDim, hf, qf[ct]);
+      load_q_frag(qb + ((size_t)(e[ct] >> 5) * sh.Hq + (qr & (sh.r - 1))) * kHeadDim, hf, qf[ct]);
     }
-    // the next chunk's entries are in flight during this chunk
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) ent[ct] = entry_of(c + 1, ct);
-    // waves whose rows are all past the item's end skip the math
-    const bool wave_live = c * tpc + ((64 * w) >> r_log2) < n_ent;
+  };
+  auto kv_src = [&](const ItemDesc& d, size_t* off) -> int {
+    *off = ((size_t)d.u * sh.S + (size_t)d.j * BS) * kHeadDim;
+    return min(BS, sh.S - d.j * BS);
+  };
 
-    if (wave_live) {
-    // S^T = K Q^T
-    f32x16_t s[KT][2];
+  ItemDesc cur = decode_item(items, row_ptr, i_begin + it, sh.n_ranges, sh.nb, tpi);
+  uint32_t ent[2];
+  u32x4_t qf[2][8];
+  const uint16_t* qb = q_base(cur.u);
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-      s[kt][0] = f32x16_t{};
-      s[kt][1] = f32x16_t{};
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const u32x4_t a = k_frag(lds, kt, ks, lane);
-        s[kt][0] = mfma32x32x16(a, qf[0][ks], s[kt][0]);
-        s[kt][1] = mfma32x32x16(a, qf[1][ks], s[kt][1]);
-      }
-    }
+  for (int ct = 0; ct < 2; ++ct) ent[ct] = entry_of(cur, 0, ct);
+  load_q(qb, ent, qf);
+  KvStage<BS, 256> kv;
+  {
+    size_t off;
+    const int nk = kv_src(cur, &off);
+    load_kv_regs<BS, 256>(k + off, v + off, nk, kv);
+    store_kv_lds<BS, 256>(kv, nk, lds);
+  }
+  __syncthreads();
 
-    // a chunk holding some query's own block: causal mask + two-term P
-    const bool own[2] = {(tok[0] >> sh.bs_log2) == j, (tok[1] >> sh.bs_log2) == j};
-    const bool diag = __any(own[0] || own[1]);
-    if (diag) {
+  int buf = 0;
+  while (true) {
+    const int it_next = it + stride;
+    const bool has_next = it_next < it_end;
+    const ItemDesc nxt = has_next ? decode_item(items, row_ptr, i_begin + it_next, sh.n_ranges, sh.nb, tpi) : cur;
+    size_t nxt_off;
+    const int nxt_keys = kv_src(nxt, &nxt_off);
+    if (has_next) load_kv_regs<BS, 256>(k + nxt_off, v + nxt_off, nxt_keys, kv);
+    const uint16_t* nxt_qb = q_base(nxt.u);
+    const char* kvl = lds + buf * Tile<BS>::kLdsBytes;
+    const int key0 = cur.j * BS;
+    const int b = cur.u / sh.G;
+    const int g = cur.u - b * sh.G;
+    const size_t row0 = (size_t)(cur.u - pass.u0) * pass.pass_tokens + pass_row0;
+    const int n_chunks = (cur.n_ent + tpc - 1) / tpc;
+
+    auto do_chunk = [&](const int c, const bool first) {
+      // keep the LDS fragment reads inside the loop (hoisted they would
+      // need far more registers than a wave has)
+      __asm__ volatile("" ::: "memory");
+      int tok[2], slot[2], head[2];
+      bool live[2];
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
-        // keys 0 .. tok - key0 are not after the query; the lane-half term of
-        // the key index moves to the right-hand side so that every compare
-        // is against a constant
-        const int lim = tok[ct] - key0 - 4 * hf;
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (32 * kt + c_row(i, 0) > lim) s[kt][ct][i] = -__builtin_inff();
+        const int qr = 64 * w + 32 * ct + (lane & 31);
+        live[ct] = c * tpc + (qr >> r_log2) < cur.n_ent;
+        tok[ct] = (int)(ent[ct] >> 5);
+        slot[ct] = (int)(ent[ct] & 31u);
+        head[ct] = qr & (sh.r - 1);
       }
-    }
-    float m2[2], sum[2];
+      // the position after this chunk: the item's next chunk, else the
+      // next item's first
+      const bool in_cur = c + 1 < n_chunks;
+      const bool more = in_cur || has_next;
+      uint32_t ent_nx[2];
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      float mx = -__builtin_inff();
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][ct][i]);
-      m2[ct] = wave_max_pair(mx) * c2;
-      sum[ct] = 0.f;
-    }
+      for (int ct = 0; ct < 2; ++ct) ent_nx[ct] = in_cur ? entry_of(cur, c + 1, ct) : entry_of(nxt, 0, ct);
+      const uint16_t* qb_nx = in_cur ? qb : nxt_qb;
+      // waves whose rows are all past the item's end skip the math
+      const bool wave_live = c * tpc + ((64 * w) >> r_log2) < cur.n_ent;
 
-    // O^T = V^T P^T one column tile at a time (32 accumulator registers
-    // less than both at once), then the tile's partials (or final values).
-    // A column whose own block this is gets P = hi + lo in bf16; the other
-    // columns add a zero low term and round exactly as outside such chunks.
+      if (wave_live) {
+        // S^T = K Q^T
+        f32x16_t s[KT][2];
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      f32x16_t o[4];
+        for (int kt = 0; kt < KT; ++kt) {
+          s[kt][0] = f32x16_t{};
+          s[kt][1] = f32x16_t{};
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16_t{};
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          uint32_t dh[4], dl[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float p0 = fast_exp2(fmaf(s[kt][ct][8 * h2 + 2 * e], c2, -m2[ct]));
-            const float p1 = fast_exp2(fmaf(s[kt][ct][8 * h2 + 2 * e + 1], c2, -m2[ct]));
-            dh[e] = pack_bf16x2(p0, p1);
-            if (diag) {
-              dl[e] = own[ct] ? pack_bf16x2(p0 - bf16_lo(dh[e]), p1 - bf16_hi(dh[e])) : 0u;
-              sum[ct] += (bf16_lo(dh[e]) + bf16_lo(dl[e])) + (bf16_hi(dh[e]) + bf16_hi(dl[e]));
-            } else {
-              sum[ct] += bf16_lo(dh[e]) + bf16_hi(dh[e]);  // normalise with the rounded weights
-            }
-          }
-          const u32x4_t ph = u32x4_t{dh[0], dh[1], dh[2], dh[3]};
-#pragma unroll
-          for (int dt = 0; dt < 4; ++dt) {
-            const u32x4_t a = vt_frag<BS>(lds, dt, kt, h2, lane);
-            o[dt] = mfma32x32x16(a, ph, o[dt]);
-            if (diag) o[dt] = mfma32x32x16(a, u32x4_t{dl[0], dl[1], dl[2], dl[3]}, o[dt]);
+          for (int ks = 0; ks < 8; ++ks) {
+            const u32x4_t a = k_frag(kvl, kt, ks, lane);
+            s[kt][0] = mfma32x32x16(a, qf[0][ks], s[kt][0]);
+            s[kt][1] = mfma32x32x16(a, qf[1][ks], s[kt][1]);
           }
         }
-      store_rows(o, m2[ct], wave_sum_pair(sum[ct]), live[ct], tok[ct], slot[ct], head[ct], hf, b, g, K,
-                 pass_row0, sh, part_o, part_lse, out);
-    }
-    }  // wave_live
+        // the next position's query rows load during this chunk's softmax and P.V
+        if (more) load_q(qb_nx, ent_nx, qf);
+
+        const bool own[2] = {(tok[0] >> sh.bs_log2) == cur.j, (tok[1] >> sh.bs_log2) == cur.j};
+        if (!__any(own[0] || own[1])) {
+          // ---- no query of this chunk owns the block: plain softmax
+          float m2[2], sum[2];
+          u32x4_t ph[KT][2][2];
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) {
+            float mx = -__builtin_inff();
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+              for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][ct][i]);
+            m2[ct] = wave_max_pair(mx) * c2;
+            sum[ct] = 0.f;
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+              for (int h2 = 0; h2 < 2; ++h2) {
+                uint32_t d[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const float p0 = fast_exp2(fmaf(s[kt][ct][8 * h2 + 2 * e], c2, -m2[ct]));
+                  const float p1 = fast_exp2(fmaf(s[kt][ct][8 * h2 + 2 * e + 1], c2, -m2[ct]));
+                  sum[ct] += p0 + p1;
+                  d[e] = pack_bf16x2(p0, p1);
+                }
+                ph[kt][ct][h2] = u32x4_t{d[0], d[1], d[2], d[3]};
+              }
+          }
+          // O^T = V^T P^T, one column tile at a time
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) {
+            __asm__ volatile("" ::: "memory");
+            f32x16_t o[4];
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16_t{};
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+              for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt)
+                  o[dt] = mfma32x32x16(vt_frag<BS>(kvl, dt, kt, h2, lane), ph[kt][ct][h2], o[dt]);
+            if (live[ct])
+              store_partial(o, m2[ct], wave_sum_pair(sum[ct]), tok[ct], slot[ct], head[ct], hf, K, sh.r, row0,
+                            part_o, part_ml);
+          }
+        } else {
+          // ---- some query owns the block: causal mask on the own columns,
+          // and P = hi + lo in bf16 there (~16 mantissa bits).  The other
+          // columns take a zero low term and come out bit-identical to the
+          // plain path.
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) {
+            // keys 0 .. tok - key0 are not after the query; the lane-half
+            // term of the key index moves to the right-hand side so that
+            // every compare is against a constant
+            const int lim = tok[ct] - key0 - 4 * hf;
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+              for (int i = 0; i < 16; ++i)
+                if (32 * kt + c_row(i, 0) > lim) s[kt][ct][i] = -__builtin_inff();
+          }
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) {
+            __asm__ volatile("" ::: "memory");
+            float mx = -__builtin_inff();
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+              for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][ct][i]);
+            const float m2 = wave_max_pair(mx) * c2;
+            const float lo_on = own[ct] ? 1.0f : 0.0f;  // arithmetic select: no divergent branch
+            float sum = 0.f;
+            f32x16_t o[4];
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16_t{};
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+              for (int h2 = 0; h2 < 2; ++h2) {
+                uint32_t dh[4], dl[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const float p0 = fast_exp2(fmaf(s[kt][ct][8 * h2 + 2 * e], c2, -m2));
+                  const float p1 = fast_exp2(fmaf(s[kt][ct][8 * h2 + 2 * e + 1], c2, -m2));
+                  sum += p0 + p1;
+                  dh[e] = pack_bf16x2(p0, p1);
+                  dl[e] = pack_bf16x2((p0 - bf16_lo(dh[e])) * lo_on, (p1 - bf16_hi(dh[e])) * lo_on);
+                }
+                const u32x4_t ph = u32x4_t{dh[0], dh[1], dh[2], dh[3]};
+                const u32x4_t pl = u32x4_t{dl[0], dl[1], dl[2], dl[3]};
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) {
+                  const u32x4_t a = vt_frag<BS>(kvl, dt, kt, h2, lane);
+                  o[dt] = mfma32x32x16(a, ph, o[dt]);
+                  o[dt] = mfma32x32x16(a, pl, o[dt]);
+                }
+              }
+            const float l = wave_sum_pair(sum);
+            if (live[ct]) {
+              // a row with no other partial (own block 0, or top_k = 1) is
+              // final here: one rounding to bf16, as for every other row
+              if ((tok[ct] >> sh.bs_log2) == 0 || K == 1)
+                store_final(o, l, tok[ct], head[ct], hf, b, g, sh, out);
+              else
+                store_partial(o, m2, l, tok[ct], slot[ct], head[ct], hf, K, sh.r, row0, part_o, part_ml);
+            }
+          }
+        }
+      } else if (more) {
+        load_q(qb_nx, ent_nx, qf);
+      }
+      // the next item's block goes to the other LDS buffer after the first
+      // chunk, when its loads have had a chunk's time to arrive
+      if (first && has_next) store_kv_lds<BS, 256>(kv, nxt_keys, lds + (buf ^ 1) * Tile<BS>::kLdsBytes);
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) ent[ct] = ent_nx[ct];
+      qb = qb_nx;
+    };
+    // the first chunk is a separate copy, so that the staged block's
+    // registers are free in the others
+    do_chunk(0, true);
+    for (int c = 1; c < n_chunks; ++c) do_chunk(c, false);
+    if (!has_next) break;
+    // the other buffer is complete and every wave is done with this one
+    __syncthreads();
+    buf ^= 1;
+    cur = nxt;
+    it = it_next;
   }
 }
 
 // ---------------------------------------------------------------------------
 // Merge: 16 threads per query row, 8 stored values (16 bytes) each.
-//   out = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M)
-// over the row's min(top_k - 1, own) + 1 partials.  Rows of block 0 were
-// finished by the attention kernel.
+//   out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,  M = max_s m_s
+// over the row's min(top_k - 1, own) + 1 partials.  Rows with a single
+// partial were finished by the attention kernel.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void merge_kernel(const uint16_t* __restrict__ part_o,
-                                                    const float* __restrict__ part_lse,
+                                                    const float2* __restrict__ part_ml,
                                                     uint16_t* __restrict__ out, PrefillShape sh, PassInfo pass,
                                                     int t_first, int r_log2) {
   const long gid = (long)blockIdx.x * 256 + threadIdx.x;
@@ -343,12 +489,14 @@ __global__ __launch_bounds__(256) void merge_kernel(const uint16_t* __restrict__
   const int n = min(K - 1, t >> sh.bs_log2) + 1;
   const size_t base = ((size_t)(u - pass.u0) * pass.pass_tokens + (t - pass.t0)) * K;
 
-  float lse[32];
+  float m[32], l[32];
   float M = -__builtin_inff();
 #pragma unroll
   for (int s = 0; s < 32; ++s) {
-    lse[s] = (s < n) ? part_lse[(base + s) * sh.r + h] : -__builtin_inff();
-    M = fmaxf(M, lse[s]);
+    const float2 ml = (s < n) ? part_ml[(base + s) * sh.r + h] : make_float2(-__builtin_inff(), 0.f);
+    m[s] = ml.x;
+    l[s] = ml.y;
+    M = fmaxf(M, m[s]);
   }
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float W = 0.f;
@@ -363,8 +511,8 @@ __global__ __launch_bounds__(256) void merge_kernel(const uint16_t* __restrict__
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       if (s0 + s < n) {
-        const float wgt = fast_exp2(lse[s0 + s] - M);
-        W += wgt;
+        const float wgt = fast_exp2(m[s0 + s] - M);
+        W = fmaf(wgt, l[s0 + s], W);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           acc[2 * e] = fmaf(wgt, bf16_lo(val[s][e]), acc[2 * e]);
@@ -391,18 +539,26 @@ __global__ __launch_bounds__(256) void merge_kernel(const uint16_t* __restrict__
 template <int BS>
 hipError_t launch_attend_bs(const PrefillShape& sh, const PassInfo& pass, const uint16_t* q, const uint16_t* k,
                             const uint16_t* v, const int32_t* row_ptr, const int32_t* item_ptr,
-                            const int2* items, const uint32_t* entries, uint16_t* part_o, float* part_lse,
+                            const int2* items, const uint32_t* entries, uint16_t* part_o, float2* part_ml,
                             uint16_t* out, int max_items, hipStream_t st) {
   int r_log2 = 0;
   while ((1 << r_log2) < sh.r) ++r_log2;
-  const unsigned grid = (unsigned)(((long)max_items + 7) / 8 * 8);
-  if (grid == 0) return hipSuccess;
+  // one workgroup per CU, never more workgroups than items
+  static int n_cu = 0;
+  if (n_cu == 0) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+  }
+  if (max_items <= 0) return hipSuccess;
+  const unsigned grid = (unsigned)std::max<long>(1, std::min<long>((long)n_cu, (long)max_items));
+  constexpr int lds_bytes = 2 * Tile<BS>::kLdsBytes;
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&attend_kernel<BS>),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                     Tile<BS>::kLdsBytes);
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(attend_kernel<BS>, dim3(grid), dim3(256), Tile<BS>::kLdsBytes, st, q, k, v, row_ptr,
-                     item_ptr, items, entries, part_o, part_lse, out, sh, pass, r_log2);
+  hipLaunchKernelGGL(attend_kernel<BS>, dim3(grid), dim3(256), lds_bytes, st, q, k, v, row_ptr, item_ptr, items,
+                     entries, part_o, part_ml, out, sh, pass, r_log2);
   return hipGetLastError();
 }
 
@@ -410,30 +566,31 @@ hipError_t launch_attend_bs(const PrefillShape& sh, const PassInfo& pass, const 
 
 hipError_t launch_attend(const PrefillShape& sh, const PassInfo& pass, const uint16_t* q, const uint16_t* k,
                          const uint16_t* v, const int32_t* row_ptr, const int32_t* item_ptr, const int2* items,
-                         const uint32_t* entries, uint16_t* part_o, float* part_lse, uint16_t* out,
+                         const uint32_t* entries, uint16_t* part_o, float2* part_ml, uint16_t* out,
                          int max_items, hipStream_t st) {
   switch (sh.bs) {
     case 32:
-      return launch_attend_bs<32>(sh, pass, q, k, v, row_ptr, item_ptr, items, entries, part_o, part_lse, out,
+      return launch_attend_bs<32>(sh, pass, q, k, v, row_ptr, item_ptr, items, entries, part_o, part_ml, out,
                                   max_items, st);
     case 64:
-      return launch_attend_bs<64>(sh, pass, q, k, v, row_ptr, item_ptr, items, entries, part_o, part_lse, out,
+      return launch_attend_bs<64>(sh, pass, q, k, v, row_ptr, item_ptr, items, entries, part_o, part_ml, out,
                                   max_items, st);
     default:
-      return launch_attend_bs<128>(sh, pass, q, k, v, row_ptr, item_ptr, items, entries, part_o, part_lse, out,
+      return launch_attend_bs<128>(sh, pass, q, k, v, row_ptr, item_ptr, items, entries, part_o, part_ml, out,
                                    max_items, st);
   }
 }
 
 hipError_t launch_merge(const PrefillShape& sh, const PassInfo& pass, const uint16_t* part_o,
-                        const float* part_lse, uint16_t* out, hipStream_t st) {
+                        const float2* part_ml, uint16_t* out, hipStream_t st) {
   int r_log2 = 0;
   while ((1 << r_log2) < sh.r) ++r_log2;
-  const int t_first = max(pass.t0, sh.bs);  // rows of block 0 are already final
-  if (t_first >= pass.t1) return hipSuccess;
+  // rows of block 0, and every row when top_k = 1, are already final
+  const int t_first = max(pass.t0, sh.bs);
+  if (t_first >= pass.t1 || sh.top_k == 1) return hipSuccess;
   const long threads = (long)(pass.t1 - t_first) * sh.r * 16;
   hipLaunchKernelGGL(merge_kernel, dim3((unsigned)((threads + 255) / 256), pass.u1 - pass.u0), dim3(256), 0, st,
-                     part_o, part_lse, out, sh, pass, t_first, r_log2);
+                     part_o, part_ml, out, sh, pass, t_first, r_log2);
   return hipGetLastError();
 }
 

@@ -92,7 +92,7 @@ PrefillPlan plan_prefill(const Dims& d) {
   p.ranged = false;
   p.T = S256;
   {
-    const long per_tok = d.k * d.r * (2 * d.D + 4);
+    const long per_tok = d.k * d.r * (2 * d.D + 8);
     const long t_mall = (long)(kPassPartialBudget / per_tok) / 256 * 256;
     // about 32 queries per (range, block) row at the far end of the sequence
     const long t_reuse = (32 * d.nb / d.k + 255) / 256 * 256;
@@ -117,7 +117,7 @@ PrefillPlan plan_prefill(const Dims& d) {
 }
 
 struct PrefillLayout {
-  size_t block_keys, sel, counts, hist, row_ptr, item_ptr, entries, items, part_o, part_lse, total;
+  size_t block_keys, sel, counts, hist, row_ptr, item_ptr, entries, items, part_o, part_ml, total;
 };
 
 // Workspace: fixed part + partials of `units_per_pass` units of pass_tokens.
@@ -139,7 +139,7 @@ PrefillLayout prefill_layout(const Dims& d, const PrefillPlan& p, long units_per
   L.entries = take((size_t)d.U * d.S * d.k * 4);
   L.items = take((size_t)(d.U * p.n_ranges * p.max_items_per_range + 1) * 8);
   L.part_o = take((size_t)units_per_pass * pass_tokens * d.k * d.r * d.D * 2);
-  L.part_lse = take((size_t)units_per_pass * pass_tokens * d.k * d.r * 4);
+  L.part_ml = take((size_t)units_per_pass * pass_tokens * d.k * d.r * 8);
   L.total = off;
   return L;
 }
@@ -334,7 +334,7 @@ int msa_prefill(const msa_dims* dims, const uint16_t* q, const uint16_t* k, cons
   uint32_t* entries = reinterpret_cast<uint32_t*>(base + L.entries);
   int2* items = reinterpret_cast<int2*>(base + L.items);
   uint16_t* part_o = reinterpret_cast<uint16_t*>(base + L.part_o);
-  float* part_lse = reinterpret_cast<float*>(base + L.part_lse);
+  float2* part_ml = reinterpret_cast<float2*>(base + L.part_ml);
 
   hipStream_t s = (hipStream_t)stream;
   const int U = (int)d.U, S = (int)d.S, bs = (int)d.bs, nb = (int)d.nb, K = (int)d.k;
@@ -378,8 +378,8 @@ int msa_prefill(const msa_dims* dims, const uint16_t* q, const uint16_t* k, cons
     ps.row_end = (int)(((u1 - 1) * P.n_ranges + rng + 1) * nb);
     const long max_items = (u1 - u0) * P.max_items_per_range;
     MSA_LAUNCH_NAMED("attend", s, msa::launch_attend(sh, ps, q, k, v, row_ptr, item_ptr, items, entries, part_o,
-                                                     part_lse, out, (int)max_items, s));
-    MSA_LAUNCH_NAMED("merge", s, msa::launch_merge(sh, ps, part_o, part_lse, out, s));
+                                                     part_ml, out, (int)max_items, s));
+    MSA_LAUNCH_NAMED("merge", s, msa::launch_merge(sh, ps, part_o, part_ml, out, s));
     return MSA_OK;
   };
   if (P.ranged) {

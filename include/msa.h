@@ -147,7 +147,7 @@ int msa_decode(const msa_dims* dims, const uint16_t* q, const int8_t* q_idx,
 int msa_profile_enable(int on);
 
 typedef struct msa_kernel_time {
-  char name[32];      /* kernel name, e.g. "main_offdiag" */
+  char name[32];      /* kernel name, e.g. "attend" */
   int32_t launches;   /* launches recorded since the last read */
   float total_ms;     /* summed event-to-event duration of those launches */
 } msa_kernel_time;

@@ -128,7 +128,7 @@ def _plan(U, S, nb, r, k):
     S256 = -(-S // 256) * 256
     T, ranged = S256, False
     if USE_QUERY_RANGES:
-        per_tok = k * r * (2 * 128 + 4)
+        per_tok = k * r * (2 * 128 + 8)
         t_mall = (128 * 2**20 // per_tok) // 256 * 256
         t_reuse = -(-(32 * nb // k) // 256) * 256
         if t_mall >= 256 and t_mall >= t_reuse and t_mall < S and U * (-(-S // t_mall)) * nb <= 1 << 22:
@@ -146,7 +146,7 @@ def _plan(U, S, nb, r, k):
     (1, 65536, 8, 1, 128, 1, False)])
 def test_prefill_workspace_layout(lib, B, S, Hq, G, bs, k, ranged):
     """The documented layout: fixed part + one bf16 partial (r x 128) and one
-    fp32 log-sum-exp (r) per (token, kept earlier block) of a pass."""
+    fp32 (max, sum) pair (r) per (token, kept block) of a pass."""
     dims = D(batch=B, seq_len=S, n_q_heads=Hq, n_kv_heads=G, block_size=bs, top_k=k)
     st, lo, hi = _ws(lib, _lib.MSA_OP_PREFILL, dims)
     assert st == 0
@@ -160,7 +160,7 @@ def test_prefill_workspace_layout(lib, B, S, Hq, G, bs, k, ranged):
     items = U * n_ranges * ((range_tok * k + tpi - 1) // tpi + nb) + 1
     fixed = (_a(U * nb * 64) + _a(U * S * k * 4) + _a(rows * 4) + _a(U * n_chunks * nb * 4)
              + 2 * _a((rows + 1) * 4) + _a(U * S * k * 4) + _a(items * 8))
-    part = lambda n: _a(n * range_tok * k * r * 128 * 2) + _a(n * range_tok * k * r * 4)  # noqa: E731
+    part = lambda n: _a(n * range_tok * k * r * 128 * 2) + _a(n * range_tok * k * r * 8)  # noqa: E731
     assert lo == fixed + part(1)
     assert hi == (lo if ranged else fixed + part(U))
 
