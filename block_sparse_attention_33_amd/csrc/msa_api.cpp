@@ -148,6 +148,8 @@ struct DecodeLayout {
   size_t part_o, part_ml, sel, total;
 };
 
+// Decode workspace: fp32 partials and (max, sum) pairs, and the selection
+// when the caller passes no sel.
 int decode_layout(const Dims& d, DecodeLayout* L) {
   if (d.nb - 1 > msa::kDecodeMaxCandidates) return MSA_ERR_UNSUPPORTED;
   size_t off = 0;
@@ -157,7 +159,7 @@ int decode_layout(const Dims& d, DecodeLayout* L) {
     return at;
   };
   L->part_o = take((size_t)d.U * d.k * d.r * d.D * 4);
-  L->part_ml = take((size_t)d.U * d.k * d.r * 2 * 4);
+  L->part_ml = take((size_t)d.U * d.k * d.r * 8);
   L->sel = take((size_t)d.U * d.k * 4);
   L->total = off;
   return MSA_OK;
@@ -421,11 +423,12 @@ int msa_decode(const msa_dims* dims, const uint16_t* q, const int8_t* q_idx, con
   sh.top_k = (int)d.k;
   sh.scale_log2 = d.scale * 1.4426950408889634f;
   float* part_o = reinterpret_cast<float*>(base + L.part_o);
-  float* part_ml = reinterpret_cast<float*>(base + L.part_ml);
+  float2* part_ml = reinterpret_cast<float2*>(base + L.part_ml);
   int32_t* sel_use = sel ? sel : reinterpret_cast<int32_t*>(base + L.sel);
   hipStream_t s = (hipStream_t)stream;
   MSA_LAUNCH_NAMED("decode_index", s, msa::launch_decode_index(sh, q_idx, block_keys, sel_use, s));
-  MSA_LAUNCH_NAMED("decode_attend", s, msa::launch_decode_attend(sh, q, k_cache, v_cache, sel_use, part_o, part_ml, s));
+  MSA_LAUNCH_NAMED("decode_attend", s,
+                   msa::launch_decode_attend(sh, q, k_cache, v_cache, sel_use, part_o, part_ml, s));
   MSA_LAUNCH_NAMED("decode_merge", s, msa::launch_decode_merge(sh, part_o, part_ml, out, s));
   return MSA_OK;
 }
