@@ -24,6 +24,9 @@ COMMON = [
     "-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
     # keep the compiler from forming packed fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs (the softmax reads them with VALU
+    # instructions; in AGPRs every value would first be copied out)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     "-Wall", "-Wno-unused-function",
 ]

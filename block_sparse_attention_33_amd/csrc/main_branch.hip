@@ -17,9 +17,9 @@
 //                  other, and each wave loads the 64 gathered query rows of
 //                  its next chunk during the current one.  Every row leaves an
 //                  unnormalised bf16 partial and its (max, sum) in base-2
-//                  units at its selection slot; rows with no other partial
-//                  (own block 0, or top_k = 1) are written to the output
-//                  directly.  Chunks holding a query's own block apply the
+//                  units at its selection slot (a row with no other partial,
+//                  own block 0 or top_k = 1, leaves o / l with a sum of 1).
+//                  Chunks holding a query's own block apply the
 //                  causal mask and split P into two bf16 terms, so P.V keeps
 //                  ~16 mantissa bits for the first tokens of a sequence,
 //                  which see only a few keys.
@@ -72,7 +72,11 @@ struct KvStage {
 template <int BS, int NT>
 __device__ __forceinline__ void load_kv_regs(const uint16_t* __restrict__ kblk, const uint16_t* __restrict__ vblk,
                                              int n_keys, KvStage<BS, NT>& st) {
-  const int tid = threadIdx.x;
+  // the thread index is made opaque here so that the addresses below are
+  // recomputed at each use instead of being kept live (and spilled) across
+  // the whole item loop
+  int tid = threadIdx.x;
+  __asm__ volatile("" : "+v"(tid));
 #pragma unroll
   for (int m = 0; m < KvStage<BS, NT>::kK; ++m) {
     const int qid = tid + NT * m;
@@ -93,7 +97,8 @@ __device__ __forceinline__ void load_kv_regs(const uint16_t* __restrict__ kblk, 
 template <int BS, int NT>
 __device__ __forceinline__ void store_kv_lds(const KvStage<BS, NT>& st, int n_keys, char* __restrict__ lds) {
   using T = Tile<BS>;
-  const int tid = threadIdx.x;
+  int tid = threadIdx.x;  // opaque, as in load_kv_regs
+  __asm__ volatile("" : "+v"(tid));
 #pragma unroll
   for (int m = 0; m < KvStage<BS, NT>::kK; ++m) {
     const int qid = tid + NT * m;
@@ -145,54 +150,55 @@ __device__ __forceinline__ u32x4_t vt_frag(const char* lds, int dt, int kt, int 
   return r;
 }
 
-// Final output of a row whose own block is block 0 (it attends nothing
-// else): o / l in bf16.
-__device__ __forceinline__ void store_final(const f32x16_t (&o)[4], float l, int tok, int head, int hf, int b,
-                                            int g, const PrefillShape& sh, uint16_t* __restrict__ out) {
-  const float inv = 1.0f / l;
-  uint16_t* orow = out + (((size_t)b * sh.S + tok) * sh.Hq + g * sh.r + head) * kHeadDim;
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      u32x2_t wv;
-      wv.x = pack_bf16x2(o[dt][4 * q4 + 0] * inv, o[dt][4 * q4 + 1] * inv);
-      wv.y = pack_bf16x2(o[dt][4 * q4 + 2] * inv, o[dt][4 * q4 + 3] * inv);
-      *reinterpret_cast<u32x2_t*>(orow + 32 * dt + 8 * q4 + 4 * hf) = wv;
-    }
-}
-
-// Partial of a row at (token, slot, head): the unnormalised sum
-// o = sum_s 2^(z_s - m2) v_s in bf16 (lane-half-major) and (m2, l) with
-// l = sum_s 2^(z_s - m2), z in base-2 units.
-__device__ __forceinline__ void store_partial(const f32x16_t (&o)[4], float m2, float l, int tok, int slot,
-                                              int head, int hf, int K, int r, size_t pass_row0,
-                                              uint16_t* __restrict__ part_o, float2* __restrict__ part_ml) {
-  const size_t pidx = ((pass_row0 + tok) * K + slot) * r + head;
-  uint16_t* dst = part_o + pidx * kHeadDim + 64 * hf;
+// A column tile's results packed for storing: the row's 128 values as bf16,
+// lane-half-major (position 64 * hf + 16 * dt + i), 8 u32x4 per lane.
+__device__ __forceinline__ void pack_tile(const f32x16_t (&o)[4], float scale, u32x4_t (&pv)[8]) {
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) {
-    u32x4_t w0, w1;
-    w0.x = pack_bf16x2(o[dt][0], o[dt][1]);
-    w0.y = pack_bf16x2(o[dt][2], o[dt][3]);
-    w0.z = pack_bf16x2(o[dt][4], o[dt][5]);
-    w0.w = pack_bf16x2(o[dt][6], o[dt][7]);
-    w1.x = pack_bf16x2(o[dt][8], o[dt][9]);
-    w1.y = pack_bf16x2(o[dt][10], o[dt][11]);
-    w1.z = pack_bf16x2(o[dt][12], o[dt][13]);
-    w1.w = pack_bf16x2(o[dt][14], o[dt][15]);
-    *reinterpret_cast<u32x4_t*>(dst + 16 * dt) = w0;
-    *reinterpret_cast<u32x4_t*>(dst + 16 * dt + 8) = w1;
+    pv[2 * dt] = u32x4_t{pack_bf16x2(o[dt][0] * scale, o[dt][1] * scale), pack_bf16x2(o[dt][2] * scale, o[dt][3] * scale),
+                         pack_bf16x2(o[dt][4] * scale, o[dt][5] * scale), pack_bf16x2(o[dt][6] * scale, o[dt][7] * scale)};
+    pv[2 * dt + 1] =
+        u32x4_t{pack_bf16x2(o[dt][8] * scale, o[dt][9] * scale), pack_bf16x2(o[dt][10] * scale, o[dt][11] * scale),
+                pack_bf16x2(o[dt][12] * scale, o[dt][13] * scale), pack_bf16x2(o[dt][14] * scale, o[dt][15] * scale)};
   }
-  if (hf == 0) part_ml[pidx] = make_float2(m2, l);
+}
+
+// Without a scale: plain conversion.
+__device__ __forceinline__ void pack_tile(const f32x16_t (&o)[4], u32x4_t (&pv)[8]) {
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    pv[2 * dt] = u32x4_t{pack_bf16x2(o[dt][0], o[dt][1]), pack_bf16x2(o[dt][2], o[dt][3]),
+                         pack_bf16x2(o[dt][4], o[dt][5]), pack_bf16x2(o[dt][6], o[dt][7])};
+    pv[2 * dt + 1] = u32x4_t{pack_bf16x2(o[dt][8], o[dt][9]), pack_bf16x2(o[dt][10], o[dt][11]),
+                             pack_bf16x2(o[dt][12], o[dt][13]), pack_bf16x2(o[dt][14], o[dt][15])};
+  }
+}
+
+// Store a packed row of the partials at row pidx, lane half hf, with its
+// (max, sum).  Both lane halves store the (max, sum) pair (the same value),
+// so that every path issues the same memory operations.
+__device__ __forceinline__ void store_row(const u32x4_t (&pv)[8], float2 ml, size_t pidx, int hf,
+                                          uint16_t* __restrict__ part_o, float2* __restrict__ part_ml) {
+  uint16_t* dst = part_o + pidx * kHeadDim + 64 * hf;
+#pragma unroll
+  for (int m = 0; m < 8; ++m) *reinterpret_cast<u32x4_t*>(dst + 8 * m) = pv[m];
+  part_ml[pidx] = ml;
 }
 
 // ---------------------------------------------------------------------------
 // Attention over the KV blocks of work items.  Persistent: one workgroup per
 // CU walks a static list of items; while it computes item i, the K/V block
-// of item i + 1 is loaded into registers and written to the second LDS
-// buffer, and every chunk's gathered query rows are loaded during the
-// previous chunk.
+// of item i + 1 is staged into the second LDS buffer and the entries of item
+// i + 2 into a wave-private LDS ring.
+//
+// Per chunk c the order is: S^T = K Q^T (waits for the chunk's query rows,
+// loaded during chunk c - 1), the loads of the next position's query rows,
+// softmax and P.V, the stores of the chunk's partials.  Entries come from
+// the LDS ring, not from global memory, so no wait in the loop is on a load
+// issued after the previous chunk's stores (vector-memory operations
+// complete in order).  Loads and stores are issued the same way on every
+// path (rows past an item's end repeat its last entry and rewrite identical
+// values).
 // ---------------------------------------------------------------------------
 struct ItemDesc {
   int e0, n_ent, j, u;  // first entry, entries, block, unit
@@ -214,10 +220,9 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ item_ptr,
     const int2* __restrict__ items, const uint32_t* __restrict__ entries,
-    uint16_t* __restrict__ part_o, float2* __restrict__ part_ml, uint16_t* __restrict__ out,
-    PrefillShape sh, PassInfo pass, int r_log2) {
+    uint16_t* __restrict__ part_o, float2* __restrict__ part_ml, PrefillShape sh, PassInfo pass, int r_log2) {
   constexpr int KT = Tile<BS>::KT;
-  extern __shared__ __align__(16) char lds[];  // two K/V buffers
+  extern __shared__ __align__(16) char lds[];  // two K/V buffers, then the entry rings
 
   // items of this pass, dealt round-robin: items are ordered by (unit,
   // block), so the whole chip works on one unit's queries at a time and
@@ -235,16 +240,36 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(
   const float c2 = sh.scale_log2;
   const int tpc = kItemRows >> r_log2;  // tokens per chunk
   const int tpi = kItemChunks * tpc;    // tokens per item
+  const int epw = 64 >> r_log2;         // tokens of one wave in one chunk
+  const int ring = kItemChunks * epw;   // a wave's entries of one item
+  uint32_t* ering = reinterpret_cast<uint32_t*>(lds + 2 * Tile<BS>::kLdsBytes) + w * 3 * ring;
   const size_t pass_row0 = (size_t)0 - pass.t0;
 
+  auto decode_at = [&](int idx) -> ItemDesc {
+    return decode_item(items, row_ptr, i_begin + min(idx, it_end - 1), sh.n_ranges, sh.nb, tpi);
+  };
+  auto n_chunks_of = [&](const ItemDesc& d) -> int { return (d.n_ent + tpc - 1) / tpc; };
   auto q_base = [&](int u) -> const uint16_t* {
     const int b = u / sh.G;
     return q + ((size_t)b * sh.S * sh.Hq + (u - b * sh.G) * sh.r) * kHeadDim;
   };
-  // entry of column tile ct at chunk c of item d (clamped to the item)
-  auto entry_of = [&](const ItemDesc& d, int c, int ct) -> uint32_t {
-    const int tk = c * tpc + ((64 * w + 32 * ct + (lane & 31)) >> r_log2);
-    return entries[d.e0 + min(tk, d.n_ent - 1)];
+  // this wave's entries of item d: ring position jj = c * epw + i holds
+  // the entry of token c * tpc + (64 w >> r_log2) + i (clamped to the item)
+  auto load_ents = [&](const ItemDesc& d, uint32_t (&e)[4]) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int jj = min(lane + 64 * m, ring - 1);
+      const int tk = (jj / epw) * tpc + ((64 * w) >> r_log2) + jj % epw;
+      e[m] = entries[d.e0 + min(tk, d.n_ent - 1)];
+    }
+  };
+  auto store_ents = [&](int slot, const uint32_t (&e)[4]) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      if (lane + 64 * m < ring) ering[slot * ring + lane + 64 * m] = e[m];
+  };
+  auto ent_at = [&](int slot, int c, int ct) -> uint32_t {
+    return ering[slot * ring + c * epw + ((32 * ct + (lane & 31)) >> r_log2)];
   };
   auto load_q = [&](const uint16_t* qb, const uint32_t (&e)[2], u32x4_t (&qf)[2][8]) {
 #pragma unroll
@@ -258,13 +283,25 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(
     return min(BS, sh.S - d.j * BS);
   };
 
-  ItemDesc cur = decode_item(items, row_ptr, i_begin + it, sh.n_ranges, sh.nb, tpi);
-  uint32_t ent[2];
+  // ---- prologue: entries of the first two items, the first block, the
+  // first chunk's query rows
+  ItemDesc cur = decode_at(it);
+  ItemDesc nxt = decode_at(it + stride);
+  ItemDesc nxt2 = decode_at(it + 2 * stride);
+  int qn = 0;  // sequence number of the current item (entry ring slot qn % 3)
+  {
+    uint32_t e0r[4], e1r[4];
+    load_ents(cur, e0r);
+    load_ents(nxt, e1r);
+    store_ents(0, e0r);
+    store_ents(1, e1r);
+  }
   u32x4_t qf[2][8];
   const uint16_t* qb = q_base(cur.u);
-#pragma unroll
-  for (int ct = 0; ct < 2; ++ct) ent[ct] = entry_of(cur, 0, ct);
-  load_q(qb, ent, qf);
+  {
+    uint32_t e[2] = {ent_at(0, 0, 0), ent_at(0, 0, 1)};
+    load_q(qb, e, qf);
+  }
   KvStage<BS, 256> kv;
   {
     size_t off;
@@ -276,201 +313,205 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(
 
   int buf = 0;
   while (true) {
-    const int it_next = it + stride;
-    const bool has_next = it_next < it_end;
-    const ItemDesc nxt = has_next ? decode_item(items, row_ptr, i_begin + it_next, sh.n_ranges, sh.nb, tpi) : cur;
+    const bool has_next = it + stride < it_end;
+    // the next item's block and the entries of the item after it
     size_t nxt_off;
     const int nxt_keys = kv_src(nxt, &nxt_off);
-    if (has_next) load_kv_regs<BS, 256>(k + nxt_off, v + nxt_off, nxt_keys, kv);
+    load_kv_regs<BS, 256>(k + nxt_off, v + nxt_off, nxt_keys, kv);
+    uint32_t e2r[4];
+    load_ents(nxt2, e2r);
     const uint16_t* nxt_qb = q_base(nxt.u);
-    const char* kvl = lds + buf * Tile<BS>::kLdsBytes;
     const int key0 = cur.j * BS;
-    const int b = cur.u / sh.G;
-    const int g = cur.u - b * sh.G;
     const size_t row0 = (size_t)(cur.u - pass.u0) * pass.pass_tokens + pass_row0;
-    const int n_chunks = (cur.n_ent + tpc - 1) / tpc;
+    const int n_chunks = n_chunks_of(cur);
+    const int slot_cur = qn % 3;
+    const int slot_nxt = (qn + 1) % 3;
 
-    auto do_chunk = [&](const int c, const bool first) {
-      // keep the LDS fragment reads inside the loop (hoisted they would
-      // need far more registers than a wave has)
-      __asm__ volatile("" ::: "memory");
+    for (int c = 0; c < n_chunks; ++c) {
+      const bool first = c == 0;
+      // the block's LDS offset is made opaque per chunk, so that the
+      // fragment reads stay inside the loop (hoisted they would need far
+      // more registers than a wave has)
+      int kvo = buf * Tile<BS>::kLdsBytes;
+      __asm__ volatile("" : "+v"(kvo));
+      const char* kvl = lds + kvo;
       int tok[2], slot[2], head[2];
-      bool live[2];
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
-        const int qr = 64 * w + 32 * ct + (lane & 31);
-        live[ct] = c * tpc + (qr >> r_log2) < cur.n_ent;
-        tok[ct] = (int)(ent[ct] >> 5);
-        slot[ct] = (int)(ent[ct] & 31u);
-        head[ct] = qr & (sh.r - 1);
+        const uint32_t e = ent_at(slot_cur, c, ct);
+        tok[ct] = (int)(e >> 5);
+        slot[ct] = (int)(e & 31u);
+        head[ct] = (64 * w + 32 * ct + (lane & 31)) & (sh.r - 1);
       }
       // the position after this chunk: the item's next chunk, else the
-      // next item's first
+      // next item's first (or, at the very end, a repeat of this one)
       const bool in_cur = c + 1 < n_chunks;
-      const bool more = in_cur || has_next;
       uint32_t ent_nx[2];
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) ent_nx[ct] = in_cur ? entry_of(cur, c + 1, ct) : entry_of(nxt, 0, ct);
-      const uint16_t* qb_nx = in_cur ? qb : nxt_qb;
-      // waves whose rows are all past the item's end skip the math
-      const bool wave_live = c * tpc + ((64 * w) >> r_log2) < cur.n_ent;
+      for (int ct = 0; ct < 2; ++ct)
+        ent_nx[ct] = in_cur ? ent_at(slot_cur, c + 1, ct) : ent_at(has_next ? slot_nxt : slot_cur, has_next ? 0 : c, ct);
+      const uint16_t* qb_nx = (in_cur || !has_next) ? qb : nxt_qb;
 
-      if (wave_live) {
-        // S^T = K Q^T
-        f32x16_t s[KT][2];
+      // S^T = K Q^T
+      f32x16_t s[KT][2];
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
-          s[kt][0] = f32x16_t{};
-          s[kt][1] = f32x16_t{};
+      for (int kt = 0; kt < KT; ++kt) {
+        s[kt][0] = f32x16_t{};
+        s[kt][1] = f32x16_t{};
 #pragma unroll
-          for (int ks = 0; ks < 8; ++ks) {
-            const u32x4_t a = k_frag(kvl, kt, ks, lane);
-            s[kt][0] = mfma32x32x16(a, qf[0][ks], s[kt][0]);
-            s[kt][1] = mfma32x32x16(a, qf[1][ks], s[kt][1]);
-          }
+        for (int ks = 0; ks < 8; ++ks) {
+          const u32x4_t a = k_frag(kvl, kt, ks, lane);
+          s[kt][0] = mfma32x32x16(a, qf[0][ks], s[kt][0]);
+          s[kt][1] = mfma32x32x16(a, qf[1][ks], s[kt][1]);
         }
-        // the next position's query rows load during this chunk's softmax and P.V
-        if (more) load_q(qb_nx, ent_nx, qf);
-
-        const bool own[2] = {(tok[0] >> sh.bs_log2) == cur.j, (tok[1] >> sh.bs_log2) == cur.j};
-        if (!__any(own[0] || own[1])) {
-          // ---- no query of this chunk owns the block: plain softmax
-          float m2[2], sum[2];
-          u32x4_t ph[KT][2][2];
-#pragma unroll
-          for (int ct = 0; ct < 2; ++ct) {
-            float mx = -__builtin_inff();
-#pragma unroll
-            for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-              for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][ct][i]);
-            m2[ct] = wave_max_pair(mx) * c2;
-            sum[ct] = 0.f;
-#pragma unroll
-            for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-              for (int h2 = 0; h2 < 2; ++h2) {
-                uint32_t d[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                  const float p0 = fast_exp2(fmaf(s[kt][ct][8 * h2 + 2 * e], c2, -m2[ct]));
-                  const float p1 = fast_exp2(fmaf(s[kt][ct][8 * h2 + 2 * e + 1], c2, -m2[ct]));
-                  sum[ct] += p0 + p1;
-                  d[e] = pack_bf16x2(p0, p1);
-                }
-                ph[kt][ct][h2] = u32x4_t{d[0], d[1], d[2], d[3]};
-              }
-          }
-          // O^T = V^T P^T, one column tile at a time
-#pragma unroll
-          for (int ct = 0; ct < 2; ++ct) {
-            __asm__ volatile("" ::: "memory");
-            f32x16_t o[4];
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16_t{};
-#pragma unroll
-            for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-              for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-                for (int dt = 0; dt < 4; ++dt)
-                  o[dt] = mfma32x32x16(vt_frag<BS>(kvl, dt, kt, h2, lane), ph[kt][ct][h2], o[dt]);
-            if (live[ct])
-              store_partial(o, m2[ct], wave_sum_pair(sum[ct]), tok[ct], slot[ct], head[ct], hf, K, sh.r, row0,
-                            part_o, part_ml);
-          }
-        } else {
-          // ---- some query owns the block: causal mask on the own columns,
-          // and P = hi + lo in bf16 there (~16 mantissa bits).  The other
-          // columns take a zero low term and come out bit-identical to the
-          // plain path.
-#pragma unroll
-          for (int ct = 0; ct < 2; ++ct) {
-            // keys 0 .. tok - key0 are not after the query; the lane-half
-            // term of the key index moves to the right-hand side so that
-            // every compare is against a constant
-            const int lim = tok[ct] - key0 - 4 * hf;
-#pragma unroll
-            for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-              for (int i = 0; i < 16; ++i)
-                if (32 * kt + c_row(i, 0) > lim) s[kt][ct][i] = -__builtin_inff();
-          }
-#pragma unroll
-          for (int ct = 0; ct < 2; ++ct) {
-            __asm__ volatile("" ::: "memory");
-            float mx = -__builtin_inff();
-#pragma unroll
-            for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-              for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][ct][i]);
-            const float m2 = wave_max_pair(mx) * c2;
-            const float lo_on = own[ct] ? 1.0f : 0.0f;  // arithmetic select: no divergent branch
-            float sum = 0.f;
-            f32x16_t o[4];
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16_t{};
-#pragma unroll
-            for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-              for (int h2 = 0; h2 < 2; ++h2) {
-                uint32_t dh[4], dl[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                  const float p0 = fast_exp2(fmaf(s[kt][ct][8 * h2 + 2 * e], c2, -m2));
-                  const float p1 = fast_exp2(fmaf(s[kt][ct][8 * h2 + 2 * e + 1], c2, -m2));
-                  sum += p0 + p1;
-                  dh[e] = pack_bf16x2(p0, p1);
-                  dl[e] = pack_bf16x2((p0 - bf16_lo(dh[e])) * lo_on, (p1 - bf16_hi(dh[e])) * lo_on);
-                }
-                const u32x4_t ph = u32x4_t{dh[0], dh[1], dh[2], dh[3]};
-                const u32x4_t pl = u32x4_t{dl[0], dl[1], dl[2], dl[3]};
-#pragma unroll
-                for (int dt = 0; dt < 4; ++dt) {
-                  const u32x4_t a = vt_frag<BS>(kvl, dt, kt, h2, lane);
-                  o[dt] = mfma32x32x16(a, ph, o[dt]);
-                  o[dt] = mfma32x32x16(a, pl, o[dt]);
-                }
-              }
-            const float l = wave_sum_pair(sum);
-            if (live[ct]) {
-              // a row with no other partial (own block 0, or top_k = 1) is
-              // final here: one rounding to bf16, as for every other row
-              if ((tok[ct] >> sh.bs_log2) == 0 || K == 1)
-                store_final(o, l, tok[ct], head[ct], hf, b, g, sh, out);
-              else
-                store_partial(o, m2, l, tok[ct], slot[ct], head[ct], hf, K, sh.r, row0, part_o, part_ml);
-            }
-          }
-        }
-      } else if (more) {
-        load_q(qb_nx, ent_nx, qf);
       }
       // the next item's block goes to the other LDS buffer after the first
-      // chunk, when its loads have had a chunk's time to arrive
-      if (first && has_next) store_kv_lds<BS, 256>(kv, nxt_keys, lds + (buf ^ 1) * Tile<BS>::kLdsBytes);
+      // chunk's S^T (its loads were issued at the start of the item, after
+      // everything this wait also covers); the entries of the item after it
+      // go to the ring
+      if (first) {
+        if (has_next) store_kv_lds<BS, 256>(kv, nxt_keys, lds + (buf ^ 1) * Tile<BS>::kLdsBytes);
+        store_ents((qn + 2) % 3, e2r);
+      }
+      load_q(qb_nx, ent_nx, qf);
+
+      size_t pidx[2];
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) ent[ct] = ent_nx[ct];
+      for (int ct = 0; ct < 2; ++ct) pidx[ct] = ((row0 + tok[ct]) * K + slot[ct]) * sh.r + head[ct];
+      const bool own[2] = {(tok[0] >> sh.bs_log2) == cur.j, (tok[1] >> sh.bs_log2) == cur.j};
+      if (!__any(own[0] || own[1])) {
+        // ---- no query of this chunk owns the block: plain softmax
+        float m2[2], sum[2];
+        u32x4_t ph[KT][2][2];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          float mx = -__builtin_inff();
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][ct][i]);
+          m2[ct] = wave_max_pair(mx) * c2;
+          sum[ct] = 0.f;
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+              uint32_t d[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float p0 = fast_exp2(fmaf(s[kt][ct][8 * h2 + 2 * e], c2, -m2[ct]));
+                const float p1 = fast_exp2(fmaf(s[kt][ct][8 * h2 + 2 * e + 1], c2, -m2[ct]));
+                sum[ct] += p0 + p1;
+                d[e] = pack_bf16x2(p0, p1);
+              }
+              ph[kt][ct][h2] = u32x4_t{d[0], d[1], d[2], d[3]};
+            }
+        }
+        // O^T = V^T P^T, one column tile at a time; V^T is read again for
+        // the second tile (kept from the first it would take 128 registers)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          int vo = kvo;
+          __asm__ volatile("" : "+v"(vo));
+          const char* kvt = lds + vo;
+          f32x16_t o[4];
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16_t{};
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+              for (int dt = 0; dt < 4; ++dt)
+                o[dt] = mfma32x32x16(vt_frag<BS>(kvt, dt, kt, h2, lane), ph[kt][ct][h2], o[dt]);
+          u32x4_t pv1[8];
+          pack_tile(o, pv1);
+          store_row(pv1, make_float2(m2[ct], wave_sum_pair(sum[ct])), pidx[ct], hf, part_o, part_ml);
+        }
+      } else {
+        // ---- some query owns the block: causal mask on the own columns,
+        // and P = hi + lo in bf16 there (~16 mantissa bits).  The other
+        // columns take a zero low term and come out bit-identical to the
+        // plain path.
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          // keys 0 .. tok - key0 are not after the query; the lane-half
+          // term of the key index moves to the right-hand side so that
+          // every compare is against a constant
+          const int lim = tok[ct] - key0 - 4 * hf;
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              if (32 * kt + c_row(i, 0) > lim) s[kt][ct][i] = -__builtin_inff();
+        }
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          int vo = kvo;
+          __asm__ volatile("" : "+v"(vo));
+          const char* kvt = lds + vo;
+          float mx = -__builtin_inff();
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][ct][i]);
+          const float m2 = wave_max_pair(mx) * c2;
+          const float lo_on = own[ct] ? 1.0f : 0.0f;  // arithmetic select: no divergent branch
+          float sum = 0.f;
+          f32x16_t o[4];
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16_t{};
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+              uint32_t dh[4], dl[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float p0 = fast_exp2(fmaf(s[kt][ct][8 * h2 + 2 * e], c2, -m2));
+                const float p1 = fast_exp2(fmaf(s[kt][ct][8 * h2 + 2 * e + 1], c2, -m2));
+                sum += p0 + p1;
+                dh[e] = pack_bf16x2(p0, p1);
+                dl[e] = pack_bf16x2((p0 - bf16_lo(dh[e])) * lo_on, (p1 - bf16_hi(dh[e])) * lo_on);
+              }
+              const u32x4_t ph = u32x4_t{dh[0], dh[1], dh[2], dh[3]};
+              const u32x4_t pl = u32x4_t{dl[0], dl[1], dl[2], dl[3]};
+#pragma unroll
+              for (int dt = 0; dt < 4; ++dt) {
+                const u32x4_t a = vt_frag<BS>(kvt, dt, kt, h2, lane);
+                o[dt] = mfma32x32x16(a, ph, o[dt]);
+                o[dt] = mfma32x32x16(a, pl, o[dt]);
+              }
+            }
+          const float l = wave_sum_pair(sum);
+          // a row with no other partial (own block 0, or top_k = 1) stores
+          // o / l with a sum of 1: the merge then reproduces it exactly, so
+          // the row is rounded to bf16 once, as every other row
+          const bool single = (tok[ct] >> sh.bs_log2) == 0 || K == 1;
+          u32x4_t pv1[8];
+          pack_tile(o, single ? 1.0f / l : 1.0f, pv1);
+          store_row(pv1, make_float2(m2, single ? 1.0f : l), pidx[ct], hf, part_o, part_ml);
+        }
+      }
       qb = qb_nx;
-    };
-    // the first chunk is a separate copy, so that the staged block's
-    // registers are free in the others
-    do_chunk(0, true);
-    for (int c = 1; c < n_chunks; ++c) do_chunk(c, false);
+    }
     if (!has_next) break;
     // the other buffer is complete and every wave is done with this one
     __syncthreads();
     buf ^= 1;
+    it += stride;
+    ++qn;
     cur = nxt;
-    it = it_next;
+    nxt = nxt2;
+    nxt2 = decode_at(it + 2 * stride);
   }
 }
 
 // ---------------------------------------------------------------------------
 // Merge: 16 threads per query row, 8 stored values (16 bytes) each.
 //   out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,  M = max_s m_s
-// over the row's min(top_k - 1, own) + 1 partials.  Rows with a single
-// partial were finished by the attention kernel.
+// over the row's min(top_k - 1, own) + 1 partials (a row with a single
+// partial holds o / l with a sum of 1, which the merge reproduces exactly).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void merge_kernel(const uint16_t* __restrict__ part_o,
                                                     const float2* __restrict__ part_ml,
@@ -540,7 +581,7 @@ template <int BS>
 hipError_t launch_attend_bs(const PrefillShape& sh, const PassInfo& pass, const uint16_t* q, const uint16_t* k,
                             const uint16_t* v, const int32_t* row_ptr, const int32_t* item_ptr,
                             const int2* items, const uint32_t* entries, uint16_t* part_o, float2* part_ml,
-                            uint16_t* out, int max_items, hipStream_t st) {
+                            int max_items, hipStream_t st) {
   int r_log2 = 0;
   while ((1 << r_log2) < sh.r) ++r_log2;
   // one workgroup per CU, never more workgroups than items
@@ -553,12 +594,14 @@ hipError_t launch_attend_bs(const PrefillShape& sh, const PassInfo& pass, const 
   }
   if (max_items <= 0) return hipSuccess;
   const unsigned grid = (unsigned)std::max<long>(1, std::min<long>((long)n_cu, (long)max_items));
-  constexpr int lds_bytes = 2 * Tile<BS>::kLdsBytes;
+  // two K/V buffers and, per wave, a ring of three items' entries
+  const int lds_bytes = 2 * Tile<BS>::kLdsBytes + 4 * 3 * kItemChunks * (64 >> r_log2) * 4;
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&attend_kernel<BS>),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     2 * Tile<BS>::kLdsBytes + 4 * 3 * kItemChunks * 64 * 4);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(attend_kernel<BS>, dim3(grid), dim3(256), lds_bytes, st, q, k, v, row_ptr, item_ptr, items,
-                     entries, part_o, part_ml, out, sh, pass, r_log2);
+                     entries, part_o, part_ml, sh, pass, r_log2);
   return hipGetLastError();
 }
 
@@ -566,18 +609,17 @@ hipError_t launch_attend_bs(const PrefillShape& sh, const PassInfo& pass, const 
 
 hipError_t launch_attend(const PrefillShape& sh, const PassInfo& pass, const uint16_t* q, const uint16_t* k,
                          const uint16_t* v, const int32_t* row_ptr, const int32_t* item_ptr, const int2* items,
-                         const uint32_t* entries, uint16_t* part_o, float2* part_ml, uint16_t* out,
-                         int max_items, hipStream_t st) {
+                         const uint32_t* entries, uint16_t* part_o, float2* part_ml, int max_items, hipStream_t st) {
   switch (sh.bs) {
     case 32:
-      return launch_attend_bs<32>(sh, pass, q, k, v, row_ptr, item_ptr, items, entries, part_o, part_ml, out,
-                                  max_items, st);
+      return launch_attend_bs<32>(sh, pass, q, k, v, row_ptr, item_ptr, items, entries, part_o, part_ml, max_items,
+                                  st);
     case 64:
-      return launch_attend_bs<64>(sh, pass, q, k, v, row_ptr, item_ptr, items, entries, part_o, part_ml, out,
-                                  max_items, st);
+      return launch_attend_bs<64>(sh, pass, q, k, v, row_ptr, item_ptr, items, entries, part_o, part_ml, max_items,
+                                  st);
     default:
-      return launch_attend_bs<128>(sh, pass, q, k, v, row_ptr, item_ptr, items, entries, part_o, part_ml, out,
-                                   max_items, st);
+      return launch_attend_bs<128>(sh, pass, q, k, v, row_ptr, item_ptr, items, entries, part_o, part_ml, max_items,
+                                   st);
   }
 }
 
@@ -585,9 +627,8 @@ hipError_t launch_merge(const PrefillShape& sh, const PassInfo& pass, const uint
                         const float2* part_ml, uint16_t* out, hipStream_t st) {
   int r_log2 = 0;
   while ((1 << r_log2) < sh.r) ++r_log2;
-  // rows of block 0, and every row when top_k = 1, are already final
-  const int t_first = max(pass.t0, sh.bs);
-  if (t_first >= pass.t1 || sh.top_k == 1) return hipSuccess;
+  const int t_first = pass.t0;
+  if (t_first >= pass.t1) return hipSuccess;
   const long threads = (long)(pass.t1 - t_first) * sh.r * 16;
   hipLaunchKernelGGL(merge_kernel, dim3((unsigned)((threads + 255) / 256), pass.u1 - pass.u0), dim3(256), 0, st,
                      part_o, part_ml, out, sh, pass, t_first, r_log2);

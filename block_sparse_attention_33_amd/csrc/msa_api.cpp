@@ -380,7 +380,7 @@ int msa_prefill(const msa_dims* dims, const uint16_t* q, const uint16_t* k, cons
     ps.row_end = (int)(((u1 - 1) * P.n_ranges + rng + 1) * nb);
     const long max_items = (u1 - u0) * P.max_items_per_range;
     MSA_LAUNCH_NAMED("attend", s, msa::launch_attend(sh, ps, q, k, v, row_ptr, item_ptr, items, entries, part_o,
-                                                     part_ml, out, (int)max_items, s));
+                                                     part_ml, (int)max_items, s));
     MSA_LAUNCH_NAMED("merge", s, msa::launch_merge(sh, ps, part_o, part_ml, out, s));
     return MSA_OK;
   };

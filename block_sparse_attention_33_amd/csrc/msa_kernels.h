@@ -67,16 +67,15 @@ hipError_t launch_scatter(const int32_t* sel, const int32_t* H, uint32_t* entrie
 // Main branch: one work item = one KV block of a (unit, range) row and up to
 // 4 chunks of kItemRows gathered query rows (the query's own block
 // included); writes unnormalised bf16 partials + (running max, sum) in base-2
-// units per (token, selection slot, head), or the final output for rows of
-// block 0.
-// Items [item_ptr[row_begin], item_ptr[row_end]).
+// units per (token, selection slot, head).  A row with a single partial
+// stores it normalised with a sum of 1.  Items [item_ptr[row_begin],
+// item_ptr[row_end]).
 constexpr int kItemChunks = 4;
 hipError_t launch_attend(const PrefillShape& sh, const PassInfo& pass, const uint16_t* q, const uint16_t* k,
                          const uint16_t* v, const int32_t* row_ptr, const int32_t* item_ptr, const int2* items,
-                         const uint32_t* entries, uint16_t* part_o, float2* part_ml, uint16_t* out,
-                         int max_items, hipStream_t st);
+                         const uint32_t* entries, uint16_t* part_o, float2* part_ml, int max_items, hipStream_t st);
 
-// Merge of every partial of the pass's query rows (blocks >= 1) -> out.
+// Merge of every partial of the pass's query rows -> out.
 hipError_t launch_merge(const PrefillShape& sh, const PassInfo& pass, const uint16_t* part_o,
                         const float2* part_ml, uint16_t* out, hipStream_t st);
 
