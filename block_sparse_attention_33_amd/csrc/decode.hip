@@ -7,15 +7,12 @@
 // reports the decode speed-up).  The work is bound by HBM reads: the block
 // summaries (nb x 64 B per group) and the selected K/V blocks.
 //
-//   decode_index_kernel   one workgroup per unit: scores every candidate
-//                         block, keeps the best top_k - 1 and writes the
-//                         sorted selection (own block last).
-//   decode_attend_kernel  one workgroup per (selected slot, unit): runs the
-//                         r query heads of the group against the slot's
-//                         block on bf16 MFMA (split-KV), leaving an
-//                         unnormalised fp32 partial and its base-2 (max, sum)
-//                         per head.
-//   decode_merge_kernel   one workgroup per unit: log-sum-exp merge -> out.
+//   decode_kernel  one workgroup per (batch, group): scores every candidate
+//                  block, keeps the best top_k - 1 plus the own block, and
+//                  runs the r query heads of the group over the kept blocks
+//                  with an online softmax (split over two groups of waves,
+//                  merged at the end).  Nothing but the selection and the
+//                  output leaves the workgroup.
 //
 // Ranking keys are 64-bit: (score << 32) | (0xffffffff - block), so a larger
 // key is a higher score or, at equal score, a lower block index.
@@ -82,246 +79,409 @@ __device__ __forceinline__ int64_t wave_topk(int64_t (&k)[NK], int kp) {
   return mine;
 }
 
-// ---------------------------------------------------------------------------
-// Index: one workgroup (16 waves) per unit.  Thread i scores candidates
-// i, i + 1024, ... (NK of them); each wave keeps its best kp, wave 0 picks
-// the best kp of the 16 lists, ranks them by block index and writes the
-// selection: the kept blocks ascending, the own block, then -1.
-// ---------------------------------------------------------------------------
+// The best kp keys (keys unique; kNoKey = none) held by one wave, NK per
+// lane, by rank counting: each lane's maximum is ranked among the 64 lane
+// maxima, the kp-th largest of them (T0) bounds the kp-th largest key from
+// below, the keys >= T0 (at most kp * NK, from the kp lanes whose maximum
+// is >= T0) are gathered in LDS and ranked exactly.  Writes the best kp,
+// descending, to out[0 .. kp) (kNoKey where fewer exist).
+// ws: this wave's LDS scratch of 64 + 64 * NK keys.
 template <int NK>
-__global__ __launch_bounds__(1024) void decode_index_kernel(const int8_t* __restrict__ q_idx,
-                                                            const int8_t* __restrict__ block_keys,
-                                                            int32_t* __restrict__ sel_out, DecodeShape sh) {
-  __shared__ int64_t wbest[16][32];
-  const int u = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int w = tid >> 6;
-  const int lane = tid & 63;
-  const int K = sh.top_k;
-  const int kp = K - 1;
-  const int own = sh.nb - 1;  // candidates are blocks 0 .. own - 1
-  const i32x4_t* qp = reinterpret_cast<const i32x4_t*>(q_idx + (size_t)u * kIdxDim);
-  const i32x4_t q0 = qp[0], q1 = qp[1], q2 = qp[2], q3 = qp[3];
-  const int8_t* kb = block_keys + (size_t)u * sh.nb * kIdxDim;
-
-  if (kp > 0) {
-    int64_t keys[NK];
+__device__ __forceinline__ void wave_topk_rank(const int64_t (&k)[NK], int kp, int64_t* ws, int64_t* out) {
+  const int lane = threadIdx.x & 63;
+  int64_t* lmx = ws;
+  int64_t* cand = ws + 64;
+  int64_t lm = k[0];
 #pragma unroll
-    for (int m = 0; m < NK; ++m) {
-      const int j = tid + 1024 * m;
-      int64_t key = kNoKey;
-      if (1024 * m < own) {  // uniform: the loads below are unconditional within it
-        const i32x4_t* sp = reinterpret_cast<const i32x4_t*>(kb + (size_t)min(j, own - 1) * kIdxDim);
-        const i32x4_t a0 = sp[0], a1 = sp[1], a2 = sp[2], a3 = sp[3];
-        int s = 0;
-        s = sdot4(q0.x, a0.x, s); s = sdot4(q0.y, a0.y, s); s = sdot4(q0.z, a0.z, s); s = sdot4(q0.w, a0.w, s);
-        s = sdot4(q1.x, a1.x, s); s = sdot4(q1.y, a1.y, s); s = sdot4(q1.z, a1.z, s); s = sdot4(q1.w, a1.w, s);
-        s = sdot4(q2.x, a2.x, s); s = sdot4(q2.y, a2.y, s); s = sdot4(q2.z, a2.z, s); s = sdot4(q2.w, a2.w, s);
-        s = sdot4(q3.x, a3.x, s); s = sdot4(q3.y, a3.y, s); s = sdot4(q3.z, a3.z, s); s = sdot4(q3.w, a3.w, s);
-        key = j < own ? rank_key(s, j) : kNoKey;
-      }
-      keys[m] = key;
-    }
-    const int64_t mine = wave_topk(keys, kp);
-    if (lane < kp) wbest[w][lane] = mine;
+  for (int i = 1; i < NK; ++i) lm = max_i64(lm, k[i]);
+  lmx[lane] = lm;
+  wave_lds_sync();
+  int rank = 0;
+#pragma unroll 16
+  for (int i = 0; i < 64; ++i) rank += lmx[i] > lm ? 1 : 0;
+  const uint64_t at = __ballot(lm != kNoKey && rank == kp - 1);
+  int64_t t0 = kNoKey;
+  if (at != 0) {
+    const int src = __builtin_ctzll(at);
+    const int lo = __builtin_amdgcn_readlane((int)(uint32_t)(uint64_t)lm, src);
+    const int hi = __builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)lm >> 32), src);
+    t0 = (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint64_t)(uint32_t)lo);
   }
-  __syncthreads();
-  if (w == 0) {
-    // the best kp of the 16 waves' lists (16 kp <= 496 keys, up to 8 a lane)
-    int64_t k8[8];
+  int nc = 0;
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const int i = lane + 64 * m;
-      k8[m] = (i < 16 * kp) ? wbest[i / kp][i % kp] : kNoKey;
-    }
-    const int64_t mine = wave_topk(k8, kp);
-    const int n_valid = min(kp, own);
-    const int blk = lane < n_valid ? key_block(mine) : INT_MAX;
-    int rank = 0;
-    for (int m = 0; m < n_valid; ++m) rank += __builtin_amdgcn_readlane(blk, m) < blk ? 1 : 0;
-    int32_t* out = sel_out + (size_t)u * K;
-    if (lane < n_valid) out[rank] = blk;
-    if (lane == n_valid) out[n_valid] = own;
-    if (lane > n_valid && lane < K) out[lane] = -1;
+  for (int m = 0; m < NK; ++m) {
+    const bool c = k[m] != kNoKey && k[m] >= t0;
+    const uint64_t bal = __ballot(c);
+    const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+    if (c) cand[nc + below] = k[m];
+    nc += __popcll(bal);
   }
+  wave_lds_sync();
+  for (int base = 0; base < nc; base += 64) {
+    const int i = base + lane;
+    const int64_t x = i < nc ? cand[i] : kNoKey;
+    int rk = 0;
+#pragma unroll 8
+    for (int jj = 0; jj < nc; ++jj) rk += cand[jj] > x ? 1 : 0;
+    if (i < nc && rk < kp) out[rk] = x;
+  }
+  if (lane >= nc && lane < kp) out[lane] = kNoKey;
+  wave_lds_sync();
 }
 
 // ---------------------------------------------------------------------------
-// Attend: one workgroup (4 waves) per (slot, unit) of the selection.
-//   S^T = K Q^T: wave w takes keys 32 w .. 32 w + 31 on 32x32x16 MFMA with
-//   the query heads as columns (r <= 16 of the 32 used), K straight from HBM.
-//   P = 2^(S - m) goes to LDS as bf16 [head][key]; V goes to LDS transposed.
-//   O^T = V^T P^T: wave w takes head dims 32 w .. 32 w + 31 over all keys.
+// Fused decode: one workgroup (8 waves) per (sequence, group) unit.
+//
+//   selection  thread i scores candidates i, i + 512, ... (NK of them), each
+//              wave keeps its best kp, wave 0 picks the best kp of the 8
+//              lists and ranks them by block index: slot s of the selection
+//              is the s-th smallest, the own block follows them, later slots
+//              are empty (-1).
+//   attention  two groups of 4 waves take the even and the odd slots; per
+//              slot a group runs S^T = K Q^T on 32x32x16 MFMA (wave w: keys
+//              32 w .. 32 w + 31, the r query heads as columns, K straight
+//              from HBM), P = 2^(S - m) goes to LDS as bf16 [head][key], V
+//              to LDS transposed, and O^T = V^T P^T (wave w: head dims
+//              32 w .. 32 w + 31) is added to the group's running
+//              online-softmax state.  A group's next slot loads while the
+//              current one is computed.
+//   merge      the two groups' states are combined in LDS and written as
+//              bf16, or, when a unit's slots are shared by n_split
+//              workgroups (slot s goes to workgroup s % n_split), written as
+//              the workgroup's (max, sum, unnormalised o) for
+//              decode_merge_kernel.
 // ---------------------------------------------------------------------------
 constexpr int kRowStride = 2 * 128 + 16;  // bytes per 128-key row of V^T and P^T in LDS
 
-__global__ __launch_bounds__(256) void decode_attend_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
-    const int32_t* __restrict__ sel, float* __restrict__ part_o, float2* __restrict__ part_ml, DecodeShape sh) {
-  __shared__ __align__(16) char vt[kHeadDim * kRowStride];
-  __shared__ __align__(16) char pt[32 * kRowStride];
-  __shared__ float red_m[4][32];
-  __shared__ float red_l[4][32];
+// One slot's block in registers: K fragments of this lane's key row and V
+// key pairs (2p, 2p + 1) x 8 head dims.
+struct DecBlock {
+  u32x4_t kf[8];
+  u32x4_t va[4], vb[4];
+};
 
-  const int slot = blockIdx.x;
-  const int u = blockIdx.y;
+// Loads of block j (a valid block index) for group thread gt, wave-in-group wg.
+__device__ __forceinline__ void dec_load_block(const DecodeShape& sh, const uint16_t* __restrict__ k_cache,
+                                               const uint16_t* __restrict__ v_cache, int u, int j, int gt, int wg,
+                                               int lane, DecBlock& blk) {
+  const int key0 = j * sh.bs;
+  const int nk = min(sh.bs, sh.L - key0);
+  const int col = lane & 31, hf = lane >> 5;
+  const uint16_t* krow = k_cache + ((size_t)u * sh.L + key0 + min(32 * wg + col, nk - 1)) * kHeadDim;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) blk.kf[ks] = *reinterpret_cast<const u32x4_t*>(krow + 16 * ks + 8 * hf);
+  const uint16_t* vblk = v_cache + ((size_t)u * sh.L + key0) * kHeadDim;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int qid = gt + 256 * m;
+    const int pp = qid & 63, c = qid >> 6;
+    blk.va[m] = *reinterpret_cast<const u32x4_t*>(vblk + (size_t)min(2 * pp, nk - 1) * kHeadDim + 8 * c);
+    blk.vb[m] = *reinterpret_cast<const u32x4_t*>(vblk + (size_t)min(2 * pp + 1, nk - 1) * kHeadDim + 8 * c);
+  }
+}
+
+// Running online-softmax state of a group: this lane's column (head) and its
+// wave's 32 head dims.
+struct DecState {
+  f32x16_t o;
+  float m, l;  // base-2 running max and sum of the column
+};
+
+// One slot (block j, or an empty slot when j < 0) added to the group's state.
+// Starts and ends with a workgroup barrier-free region: the caller places
+// the barriers that order the LDS buffers between slots.
+__device__ __forceinline__ void dec_slot(const DecodeShape& sh, const DecBlock& blk, int j, const u32x4_t (&qf)[8],
+                                         char* __restrict__ vt, char* __restrict__ pt, float (*red_m)[32],
+                                         float (*red_l)[32], int gt, int wg, int lane, DecState& st) {
+  const int col = lane & 31, hf = lane >> 5;
+  const bool qcol = col < sh.r;
+  const int nk = j < 0 ? 0 : min(sh.bs, sh.L - j * sh.bs);  // valid keys (0: empty slot)
+  const int kbase = 32 * wg;
+  // V^T in LDS, natural key order (zero beyond the block's keys)
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int qid = gt + 256 * m;
+    const int pp = qid & 63, c = qid >> 6;
+    const u32x4_t a = 2 * pp < nk ? blk.va[m] : u32x4_t{0u, 0u, 0u, 0u};
+    const u32x4_t bb = 2 * pp + 1 < nk ? blk.vb[m] : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t lo = a[e], hi = bb[e];
+      *reinterpret_cast<uint32_t*>(vt + (8 * c + 2 * e) * kRowStride + 4 * pp) = (lo & 0xffffu) | (hi << 16);
+      *reinterpret_cast<uint32_t*>(vt + (8 * c + 2 * e + 1) * kRowStride + 4 * pp) = (lo >> 16) | (hi & 0xffff0000u);
+    }
+  }
+  // scores S^T (32 keys x 32 heads) of this wave, base 2
+  f32x16_t s = f32x16_t{};
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) s = mfma32x32x16(blk.kf[ks], qf[ks], s);
+  const float c2 = sh.scale_log2;
+  float mx = -__builtin_inff();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    s[i] = kbase + c_row(i, hf) < nk ? s[i] * c2 : -__builtin_inff();
+    mx = fmaxf(mx, s[i]);
+  }
+  mx = wave_max_pair(mx);
+  if (hf == 0) red_m[wg][col] = mx;
+  __syncthreads();
+  const float m_blk = fmaxf(fmaxf(red_m[0][col], red_m[1][col]), fmaxf(red_m[2][col], red_m[3][col]));
+  const float m_new = fmaxf(st.m, m_blk);
+  const float m_use = m_new == -__builtin_inff() ? 0.f : m_new;  // nothing seen yet: every p is 0
+  const float alpha = fast_exp2(st.m - m_use);                   // 0 while the state is empty
+  float sum = 0.f;
+  // this lane's P^T row (its head): keys kbase + 8 q4 + 4 hf + 0..3
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    const float p0 = fast_exp2(s[4 * q4 + 0] - m_use);
+    const float p1 = fast_exp2(s[4 * q4 + 1] - m_use);
+    const float p2 = fast_exp2(s[4 * q4 + 2] - m_use);
+    const float p3 = fast_exp2(s[4 * q4 + 3] - m_use);
+    sum += (p0 + p1) + (p2 + p3);
+    u32x2_t pv;
+    pv.x = pack_bf16x2(p0, p1);
+    pv.y = pack_bf16x2(p2, p3);
+    if (qcol) *reinterpret_cast<u32x2_t*>(pt + col * kRowStride + 2 * (kbase + 8 * q4 + 4 * hf)) = pv;
+  }
+  sum = wave_sum_pair(sum);
+  if (hf == 0) red_l[wg][col] = sum;
+  __syncthreads();
+  // O^T: head dims 32 wg .. 32 wg + 31 x 32 heads over the block's keys
+  f32x16_t o = f32x16_t{};
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    const u32x4_t a = *reinterpret_cast<const u32x4_t*>(vt + (32 * wg + col) * kRowStride + 2 * (16 * kk + 8 * hf));
+    // columns >= r read some head's row: their results are not used
+    const u32x4_t bq = *reinterpret_cast<const u32x4_t*>(pt + (col & 15) * kRowStride + 2 * (16 * kk + 8 * hf));
+    o = mfma32x32x16(a, bq, o);
+  }
+  const float l_blk = red_l[0][col] + red_l[1][col] + red_l[2][col] + red_l[3][col];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) st.o[i] = fmaf(st.o[i], alpha, o[i]);
+  st.l = fmaf(st.l, alpha, l_blk);
+  st.m = m_new;
+}
+
+template <int NK>
+__global__ __launch_bounds__(512, 1) void decode_kernel(const uint16_t* __restrict__ q,
+                                                        const int8_t* __restrict__ q_idx,
+                                                        const uint16_t* __restrict__ k_cache,
+                                                        const uint16_t* __restrict__ v_cache,
+                                                        const int8_t* __restrict__ block_keys,
+                                                        int32_t* __restrict__ sel_out, uint16_t* __restrict__ out,
+                                                     float* __restrict__ state,
+                                                        DecodeShape sh) {
+  __shared__ __align__(16) char vt[2][kHeadDim * kRowStride];
+  __shared__ __align__(16) char pt[2][16 * kRowStride];  // P^T rows of the r <= 16 heads
+  __shared__ int64_t wbest[8 * 32];                // the waves' best kp, list w at w * kp
+  __shared__ int64_t wscr[8][64 + 64 * NK];         // per-wave top-k scratch
+  __shared__ int sorted[33];
+  __shared__ float red_m[2][4][32];
+  __shared__ float red_l[2][4][32];
+  __shared__ float xo[16][kHeadDim];  // the odd-slot group's state for the final merge
+  __shared__ float xml[16][2];
+
+  const int u = blockIdx.x;
+  const int part = blockIdx.y;  // this workgroup's share of the slots
+  const int n_split = gridDim.y;
   const int b = u / sh.G;
   const int g = u - b * sh.G;
   const int tid = threadIdx.x;
   const int w = tid >> 6;
   const int lane = tid & 63;
   const int hf = lane >> 5;
-  const int col = lane & 31;  // query head of this lane's column
+  const int col = lane & 31;
+  const int gp = w >> 2;     // group: even (0) or odd (1) slots
+  const int wg = w & 3;      // wave within the group
+  const int gt = tid & 255;  // thread within the group
   const int r = sh.r;
   const int K = sh.top_k;
+  const int kp = K - 1;
+  const int own = sh.nb - 1;  // candidates are blocks 0 .. own - 1
 
-  const int j = sel[(size_t)u * K + slot];
-  float* po = part_o + ((size_t)u * K + slot) * r * kHeadDim;
-  float2* pml = part_ml + ((size_t)u * K + slot) * r;
-
-  if (j < 0) {
-    if (tid < r) pml[tid] = make_float2(-__builtin_inff(), 0.f);
-  } else {
-    const int key0 = j * sh.bs;
-    const int nk = min(sh.bs, sh.L - key0);  // valid keys of the block
-    const int kbase = 32 * w;                // this wave's first key
-
-    // V: thread takes key pairs (2p, 2p + 1) x 8 head dims (16-byte loads)
-    const uint16_t* vblk = v_cache + ((size_t)u * sh.L + key0) * kHeadDim;
-    u32x4_t va[4], vb[4];
+  // ---- selection
+  if (kp > 0) {
+    const i32x4_t* qp = reinterpret_cast<const i32x4_t*>(q_idx + (size_t)u * kIdxDim);
+    const i32x4_t q0 = qp[0], q1 = qp[1], q2 = qp[2], q3 = qp[3];
+    const int8_t* kb = block_keys + (size_t)u * sh.nb * kIdxDim;
+    int64_t keys[NK];
+#pragma unroll
+    for (int m = 0; m < NK; ++m) {
+      const int j = tid + 512 * m;
+      int64_t key = kNoKey;
+      if (512 * m < own) {  // uniform: the loads below are unconditional within it
+        const i32x4_t* sp = reinterpret_cast<const i32x4_t*>(kb + (size_t)min(j, own - 1) * kIdxDim);
+        const i32x4_t a0 = sp[0], a1 = sp[1], a2 = sp[2], a3 = sp[3];
+        int sc = 0;
+        sc = sdot4(q0.x, a0.x, sc); sc = sdot4(q0.y, a0.y, sc); sc = sdot4(q0.z, a0.z, sc); sc = sdot4(q0.w, a0.w, sc);
+        sc = sdot4(q1.x, a1.x, sc); sc = sdot4(q1.y, a1.y, sc); sc = sdot4(q1.z, a1.z, sc); sc = sdot4(q1.w, a1.w, sc);
+        sc = sdot4(q2.x, a2.x, sc); sc = sdot4(q2.y, a2.y, sc); sc = sdot4(q2.z, a2.z, sc); sc = sdot4(q2.w, a2.w, sc);
+        sc = sdot4(q3.x, a3.x, sc); sc = sdot4(q3.y, a3.y, sc); sc = sdot4(q3.z, a3.z, sc); sc = sdot4(q3.w, a3.w, sc);
+        key = j < own ? rank_key(sc, j) : kNoKey;
+      }
+      keys[m] = key;
+    }
+    wave_topk_rank(keys, kp, wscr[w], wbest + w * kp);
+  }
+  __syncthreads();
+  if (w == 0) {
+    // the best kp of the 8 waves' lists (8 kp <= 248 keys, up to 4 a lane),
+    // by rank, then ranked by block index among themselves
+    const int n2 = 8 * kp;
+    int64_t x[4];
+    int rk[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      const int qid = tid + 256 * m;
-      const int pp = qid & 63, c = qid >> 6;
-      va[m] = *reinterpret_cast<const u32x4_t*>(vblk + (size_t)min(2 * pp, nk - 1) * kHeadDim + 8 * c);
-      vb[m] = *reinterpret_cast<const u32x4_t*>(vblk + (size_t)min(2 * pp + 1, nk - 1) * kHeadDim + 8 * c);
+      x[m] = lane + 64 * m < n2 ? wbest[lane + 64 * m] : kNoKey;
+      rk[m] = 0;
     }
-    // K fragments (A) straight from HBM; Q^T (B) for columns < r
-    u32x4_t kf[8], qf[8];
-    const uint16_t* krow = k_cache + ((size_t)u * sh.L + key0 + min(kbase + col, nk - 1)) * kHeadDim;
+#pragma unroll 8
+    for (int jj = 0; jj < n2; ++jj) {
+      const int64_t y = wbest[jj];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) rk[m] += y > x[m] ? 1 : 0;
+    }
+    int* kept = reinterpret_cast<int*>(wscr[0]);  // the kept blocks, by rank
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      if (x[m] != kNoKey && rk[m] < kp) kept[rk[m]] = key_block(x[m]);
+    const int n_valid = min(kp, own);  // valid keys that exist
+    wave_lds_sync();
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      if (x[m] != kNoKey && rk[m] < kp) {
+        const int blk = key_block(x[m]);
+        int pos = 0;
+#pragma unroll 8
+        for (int i = 0; i < n_valid; ++i) pos += kept[i] < blk ? 1 : 0;
+        sorted[pos] = blk;
+      }
+    }
+    if (lane == n_valid) sorted[n_valid] = own;
+    if (lane > n_valid && lane <= 32) sorted[lane] = -1;
+  }
+  __syncthreads();
+  if (part == 0 && tid < K) sel_out[(size_t)u * K + tid] = sorted[tid];
+
+  // ---- attention: group gp takes slots gp, gp + 2, ...; a group's next
+  // slot loads while the current one is computed (two register sets, so
+  // that no load result is moved between registers)
+  u32x4_t qf[8];
+  {
     const uint16_t* qrow = q + ((size_t)b * sh.Hq + g * r + min(col, r - 1)) * kHeadDim;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      kf[ks] = *reinterpret_cast<const u32x4_t*>(krow + 16 * ks + 8 * hf);
       qf[ks] = *reinterpret_cast<const u32x4_t*>(qrow + 16 * ks + 8 * hf);
-    }
-    const bool qcol = col < r;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-      if (!qcol) qf[ks] = u32x4_t{0u, 0u, 0u, 0u};
-    // V^T in LDS, natural key order (zero beyond the block's keys)
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int qid = tid + 256 * m;
-      const int pp = qid & 63, c = qid >> 6;
-      const u32x4_t a = 2 * pp < nk ? va[m] : u32x4_t{0u, 0u, 0u, 0u};
-      const u32x4_t bb = 2 * pp + 1 < nk ? vb[m] : u32x4_t{0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t lo = a[e], hi = bb[e];
-        *reinterpret_cast<uint32_t*>(vt + (8 * c + 2 * e) * kRowStride + 4 * pp) = (lo & 0xffffu) | (hi << 16);
-        *reinterpret_cast<uint32_t*>(vt + (8 * c + 2 * e + 1) * kRowStride + 4 * pp) =
-            (lo >> 16) | (hi & 0xffff0000u);
-      }
-    }
-
-    // scores S^T (32 keys x 32 heads) of this wave, base 2
-    f32x16_t s = f32x16_t{};
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) s = mfma32x32x16(kf[ks], qf[ks], s);
-    const float c2 = sh.scale_log2;
-    float mx = -__builtin_inff();
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      s[i] = kbase + c_row(i, hf) < nk ? s[i] * c2 : -__builtin_inff();
-      mx = fmaxf(mx, s[i]);
-    }
-    mx = wave_max_pair(mx);
-    if (hf == 0) red_m[w][col] = mx;
-    __syncthreads();
-    const float m = fmaxf(fmaxf(red_m[0][col], red_m[1][col]), fmaxf(red_m[2][col], red_m[3][col]));
-    float sum = 0.f;
-    // this lane's P^T row (its head): keys kbase + 8 q4 + 4 hf + 0..3
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const float p0 = fast_exp2(s[4 * q4 + 0] - m);
-      const float p1 = fast_exp2(s[4 * q4 + 1] - m);
-      const float p2 = fast_exp2(s[4 * q4 + 2] - m);
-      const float p3 = fast_exp2(s[4 * q4 + 3] - m);
-      sum += (p0 + p1) + (p2 + p3);
-      u32x2_t pv;
-      pv.x = pack_bf16x2(p0, p1);
-      pv.y = pack_bf16x2(p2, p3);
-      *reinterpret_cast<u32x2_t*>(pt + col * kRowStride + 2 * (kbase + 8 * q4 + 4 * hf)) = pv;
-    }
-    sum = wave_sum_pair(sum);
-    if (hf == 0) red_l[w][col] = sum;
-    __syncthreads();
-
-    // O^T: head dims 32 w .. 32 w + 31 x 32 heads over the block's keys
-    f32x16_t o = f32x16_t{};
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const u32x4_t a =
-          *reinterpret_cast<const u32x4_t*>(vt + (32 * w + col) * kRowStride + 2 * (16 * kk + 8 * hf));
-      const u32x4_t bq = *reinterpret_cast<const u32x4_t*>(pt + col * kRowStride + 2 * (16 * kk + 8 * hf));
-      o = mfma32x32x16(a, bq, o);
-    }
-    if (qcol) {
-      float* orow = po + (size_t)col * kHeadDim + 32 * w + 4 * hf;
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        *reinterpret_cast<f32x4_t*>(orow + 8 * q4) = f32x4_t{o[4 * q4], o[4 * q4 + 1], o[4 * q4 + 2], o[4 * q4 + 3]};
-      if (w == 0 && hf == 0)
-        pml[col] = make_float2(m, red_l[0][col] + red_l[1][col] + red_l[2][col] + red_l[3][col]);
+      if (col >= r) qf[ks] = u32x4_t{0u, 0u, 0u, 0u};
     }
   }
+  DecState st;
+  st.o = f32x16_t{};
+  st.m = -__builtin_inff();
+  st.l = 0.f;
+  // the group's round rd is slot gp + 2 rd; the loads of an empty slot go to
+  // the own block (valid memory, then ignored)
+  auto slot_block = [&](int rd) -> int {
+    const int s2 = (2 * rd + gp) * n_split + part;
+    return s2 < K ? sorted[s2] : -1;
+  };
+  auto load_round = [&](int rd, DecBlock& blk) {
+    const int j = slot_block(rd);
+    dec_load_block(sh, k_cache, v_cache, u, j >= 0 ? j : own, gt, wg, lane, blk);
+  };
+  const int per_wg = 2 * n_split;
+  const int n_rounds = (K + per_wg - 1) / per_wg;  // the same for both groups (barriers)
+  DecBlock A, B;
+  load_round(0, A);
+  for (int rd = 0; rd < n_rounds; rd += 2) {
+    load_round(rd + 1, B);
+    if (rd > 0) __syncthreads();  // the previous slot's LDS reads are done
+    dec_slot(sh, A, slot_block(rd), qf, vt[gp], pt[gp], red_m[gp], red_l[gp], gt, wg, lane, st);
+    if (rd + 1 >= n_rounds) break;
+    load_round(rd + 2, A);
+    __syncthreads();
+    dec_slot(sh, B, slot_block(rd + 1), qf, vt[gp], pt[gp], red_m[gp], red_l[gp], gt, wg, lane, st);
+  }
 
+  // ---- merge of the two groups' states -> out = o / l
+  if (gp == 1 && col < r) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) xo[col][32 * wg + c_row(i, hf)] = st.o[i];
+    if (wg == 0 && hf == 0) {
+      xml[col][0] = st.m;
+      xml[col][1] = st.l;
+    }
+  }
+  __syncthreads();
+  if (gp == 0 && col < r && n_split > 1) {
+    // this workgroup's state (max, sum, unnormalised o) for the merge kernel
+    const float m1 = xml[col][0], l1 = xml[col][1];
+    const float M = fmaxf(st.m, m1);
+    const float Mu = M == -__builtin_inff() ? 0.f : M;  // no key seen yet: all weights 0
+    const float w0 = fast_exp2(st.m - Mu), w1 = fast_exp2(m1 - Mu);
+    float* srow = state + (((size_t)u * n_split + part) * r + col) * (kHeadDim + 2);
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      f32x4_t v4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * q4 + e;
+        v4[e] = fmaf(st.o[i], w0, xo[col][32 * wg + c_row(i, hf)] * w1);
+      }
+      *reinterpret_cast<f32x4_t*>(srow + 32 * wg + 8 * q4 + 4 * hf) = v4;
+    }
+    if (wg == 0 && hf == 0) {
+      srow[kHeadDim] = M;
+      srow[kHeadDim + 1] = fmaf(st.l, w0, l1 * w1);
+    }
+  } else if (gp == 0 && col < r) {
+    const float m1 = xml[col][0], l1 = xml[col][1];
+    const float M = fmaxf(st.m, m1);  // finite: the own block is always kept
+    const float w0 = fast_exp2(st.m - M), w1 = fast_exp2(m1 - M);
+    const float inv = 1.0f / fmaf(st.l, w0, l1 * w1);
+    uint16_t* orow = out + ((size_t)b * sh.Hq + g * r + col) * kHeadDim;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      float v4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * q4 + e;
+        v4[e] = fmaf(st.o[i], w0, xo[col][32 * wg + c_row(i, hf)] * w1) * inv;
+      }
+      u32x2_t wv;
+      wv.x = pack_bf16x2(v4[0], v4[1]);
+      wv.y = pack_bf16x2(v4[2], v4[3]);
+      *reinterpret_cast<u32x2_t*>(orow + 32 * wg + 8 * q4 + 4 * hf) = wv;
+    }
+  }
 }
 
-// ---------------------------------------------------------------------------
-// Merge: one workgroup per unit, a thread per (head, 4 head dims):
-//   out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s  over the unit's slots.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restrict__ part_o,
-                                                           const float2* __restrict__ part_ml,
-                                                           uint16_t* __restrict__ out, DecodeShape sh) {
+// Merge of a unit's n_split workgroup states: one workgroup per unit, a
+// thread per (head, 4 head dims): out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.
+__global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restrict__ state,
+                                                           uint16_t* __restrict__ out, DecodeShape sh,
+                                                           int n_split) {
   const int u = blockIdx.x;
   const int b = u / sh.G;
   const int g = u - b * sh.G;
   const int r = sh.r;
-  const int K = sh.top_k;
-  const float2* ml = part_ml + (size_t)u * K * r;
-  const float* pou = part_o + (size_t)u * K * r * kHeadDim;
   for (int it = threadIdx.x; it < r * 32; it += 256) {
     const int h = it >> 5;
     const int d0 = (it & 31) * 4;
-    // every load of the row is issued before any is used
-    float2 v[32];
-    f32x4_t ov[32];
-#pragma unroll
-    for (int s2 = 0; s2 < 32; ++s2) {
-      if (s2 < K) {  // uniform
-        v[s2] = ml[s2 * r + h];
-        ov[s2] = *reinterpret_cast<const f32x4_t*>(pou + ((size_t)s2 * r + h) * kHeadDim + d0);
-      }
-    }
     float M = -__builtin_inff();
-#pragma unroll
-    for (int s2 = 0; s2 < 32; ++s2)
-      if (s2 < K) M = fmaxf(M, v[s2].x);
+    for (int p = 0; p < n_split; ++p)
+      M = fmaxf(M, state[(((size_t)u * n_split + p) * r + h) * (kHeadDim + 2) + kHeadDim]);
     float W = 0.f;
     f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < n_split; ++p) {
+      const float* srow = state + (((size_t)u * n_split + p) * r + h) * (kHeadDim + 2);
+      const float m = srow[kHeadDim];
+      if (m == -__builtin_inff()) continue;  // a share with no kept block
+      const float wgt = fast_exp2(m - M);
+      W = fmaf(wgt, srow[kHeadDim + 1], W);
+      const f32x4_t o4 = *reinterpret_cast<const f32x4_t*>(srow + d0);
 #pragma unroll
-    for (int s2 = 0; s2 < 32; ++s2) {
-      if (s2 < K) {
-        // an empty slot (max = -inf) wrote no partial: its values are skipped
-        const bool used = v[s2].x != -__builtin_inff();
-        const float wgt = used ? fast_exp2(v[s2].x - M) : 0.f;
-        W = fmaf(wgt, used ? v[s2].y : 0.f, W);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] = fmaf(wgt, used ? ov[s2][e] : 0.f, acc[e]);
-      }
+      for (int e = 0; e < 4; ++e) acc[e] = fmaf(wgt, o4[e], acc[e]);
     }
     const float inv = 1.0f / W;
     u32x2_t wv;
@@ -333,30 +493,26 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
 
 }  // namespace
 
-hipError_t launch_decode_index(const DecodeShape& sh, const int8_t* q_idx, const int8_t* block_keys,
-                               int32_t* sel_out, hipStream_t st) {
+hipError_t launch_decode(const DecodeShape& sh, const uint16_t* q, const int8_t* q_idx, const uint16_t* k_cache,
+                         const uint16_t* v_cache, const int8_t* block_keys, int32_t* sel_out, uint16_t* out,
+                         float* state, int n_split, hipStream_t st) {
   const int own = sh.nb - 1;
-  const dim3 grid(sh.B * sh.G), block(1024);
-  if (own <= 2 * 1024)
-    hipLaunchKernelGGL(decode_index_kernel<2>, grid, block, 0, st, q_idx, block_keys, sel_out, sh);
-  else if (own <= 4 * 1024)
-    hipLaunchKernelGGL(decode_index_kernel<4>, grid, block, 0, st, q_idx, block_keys, sel_out, sh);
+  const dim3 grid(sh.B * sh.G, n_split), block(512);
+  if (own <= 4 * 512)
+    hipLaunchKernelGGL(decode_kernel<4>, grid, block, 0, st, q, q_idx, k_cache, v_cache, block_keys, sel_out, out,
+                       state, sh);
+  else if (own <= 8 * 512)
+    hipLaunchKernelGGL(decode_kernel<8>, grid, block, 0, st, q, q_idx, k_cache, v_cache, block_keys, sel_out, out,
+                       state, sh);
   else
-    hipLaunchKernelGGL(decode_index_kernel<8>, grid, block, 0, st, q_idx, block_keys, sel_out, sh);
+    hipLaunchKernelGGL(decode_kernel<16>, grid, block, 0, st, q, q_idx, k_cache, v_cache, block_keys, sel_out, out,
+                       state, sh);
   return hipGetLastError();
 }
 
-hipError_t launch_decode_attend(const DecodeShape& sh, const uint16_t* q, const uint16_t* k_cache,
-                                const uint16_t* v_cache, const int32_t* sel, float* part_o, float2* part_ml,
-                                hipStream_t st) {
-  hipLaunchKernelGGL(decode_attend_kernel, dim3(sh.top_k, sh.B * sh.G), dim3(256), 0, st, q, k_cache, v_cache, sel,
-                     part_o, part_ml, sh);
-  return hipGetLastError();
-}
-
-hipError_t launch_decode_merge(const DecodeShape& sh, const float* part_o, const float2* part_ml, uint16_t* out,
+hipError_t launch_decode_merge(const DecodeShape& sh, const float* state, int n_split, uint16_t* out,
                                hipStream_t st) {
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(sh.B * sh.G), dim3(256), 0, st, part_o, part_ml, out, sh);
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(sh.B * sh.G), dim3(256), 0, st, state, out, sh, n_split);
   return hipGetLastError();
 }
 

@@ -144,12 +144,16 @@ PrefillLayout prefill_layout(const Dims& d, const PrefillPlan& p, long units_per
   return L;
 }
 
+// A unit's kept blocks are shared by two workgroups (so that the whole chip
+// streams the blocks) unless there are fewer than four of them.
+int decode_split(const Dims& d) { return d.k >= 4 ? 2 : 1; }
+
 struct DecodeLayout {
-  size_t part_o, part_ml, sel, total;
+  size_t sel, state, total;
 };
 
-// Decode workspace: fp32 partials and (max, sum) pairs, and the selection
-// when the caller passes no sel.
+// Decode workspace: the selection (when the caller passes no sel) and the
+// workgroups' states (max, sum, unnormalised o per head).
 int decode_layout(const Dims& d, DecodeLayout* L) {
   if (d.nb - 1 > msa::kDecodeMaxCandidates) return MSA_ERR_UNSUPPORTED;
   size_t off = 0;
@@ -158,9 +162,8 @@ int decode_layout(const Dims& d, DecodeLayout* L) {
     off += align_up(bytes);
     return at;
   };
-  L->part_o = take((size_t)d.U * d.k * d.r * d.D * 4);
-  L->part_ml = take((size_t)d.U * d.k * d.r * 8);
   L->sel = take((size_t)d.U * d.k * 4);
+  L->state = take((size_t)d.U * decode_split(d) * d.r * (d.D + 2) * 4);
   L->total = off;
   return MSA_OK;
 }
@@ -422,14 +425,13 @@ int msa_decode(const msa_dims* dims, const uint16_t* q, const int8_t* q_idx, con
   sh.nb = (int)d.nb;
   sh.top_k = (int)d.k;
   sh.scale_log2 = d.scale * 1.4426950408889634f;
-  float* part_o = reinterpret_cast<float*>(base + L.part_o);
-  float2* part_ml = reinterpret_cast<float2*>(base + L.part_ml);
   int32_t* sel_use = sel ? sel : reinterpret_cast<int32_t*>(base + L.sel);
   hipStream_t s = (hipStream_t)stream;
-  MSA_LAUNCH_NAMED("decode_index", s, msa::launch_decode_index(sh, q_idx, block_keys, sel_use, s));
-  MSA_LAUNCH_NAMED("decode_attend", s,
-                   msa::launch_decode_attend(sh, q, k_cache, v_cache, sel_use, part_o, part_ml, s));
-  MSA_LAUNCH_NAMED("decode_merge", s, msa::launch_decode_merge(sh, part_o, part_ml, out, s));
+  float* state = reinterpret_cast<float*>(base + L.state);
+  const int n_split = decode_split(d);
+  MSA_LAUNCH_NAMED("decode", s,
+                   msa::launch_decode(sh, q, q_idx, k_cache, v_cache, block_keys, sel_use, out, state, n_split, s));
+  if (n_split > 1) MSA_LAUNCH_NAMED("decode_merge", s, msa::launch_decode_merge(sh, state, n_split, out, s));
   return MSA_OK;
 }
 

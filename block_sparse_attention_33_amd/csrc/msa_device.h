@@ -52,6 +52,14 @@ __device__ __forceinline__ float wave_max_pair(float x) {  // max with lane ^ 32
 }
 __device__ __forceinline__ float wave_sum_pair(float x) { return x + __shfl_xor(x, 32); }
 
+// Orders a wave's LDS writes before other lanes' later reads of them (and
+// those reads before later writes): lanes exchanging data through LDS.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Sign-extend the four int8 lanes of a dword.
 __device__ __forceinline__ int sx8(uint32_t w, int byte) { return ((int)(w << (24 - 8 * byte))) >> 24; }
 

@@ -84,18 +84,16 @@ struct DecodeShape {
   int B, L, Hq, G, r, bs, nb, top_k;
   float scale_log2;
 };
-constexpr int kDecodeMaxCandidates = 8 * 1024;  // 1024 threads x 8 candidates
-// Scores + per-(sequence, group) top-k -> sel [U, top_k] (ascending, own
-// block last, -1 padding).
-hipError_t launch_decode_index(const DecodeShape& sh, const int8_t* q_idx, const int8_t* block_keys,
-                               int32_t* sel_out, hipStream_t st);
-// Split-KV attention -> part_o [U, top_k, r, 128] fp32 and part_ml
-// [U, top_k, r] (base-2 max, sum).
-hipError_t launch_decode_attend(const DecodeShape& sh, const uint16_t* q, const uint16_t* k_cache,
-                                const uint16_t* v_cache, const int32_t* sel, float* part_o, float2* part_ml,
-                                hipStream_t st);
-// Merge of a unit's partials -> out.
-hipError_t launch_decode_merge(const DecodeShape& sh, const float* part_o, const float2* part_ml, uint16_t* out,
+constexpr int kDecodeMaxCandidates = 16 * 512;  // 512 threads x 16 candidates
+// Selection (-> sel [U, top_k]: ascending, own block last, -1 padding) and
+// attention over the kept blocks.  n_split workgroups share a unit's slots;
+// with n_split = 1 the kernel writes out [B, Hq, 128], otherwise each
+// workgroup writes its state [U, n_split, r, 128 + 2] (o, max, sum) and
+// launch_decode_merge combines them into out.
+hipError_t launch_decode(const DecodeShape& sh, const uint16_t* q, const int8_t* q_idx, const uint16_t* k_cache,
+                         const uint16_t* v_cache, const int8_t* block_keys, int32_t* sel_out, uint16_t* out,
+                         float* state, int n_split, hipStream_t st);
+hipError_t launch_decode_merge(const DecodeShape& sh, const float* state, int n_split, uint16_t* out,
                                hipStream_t st);
 
 }  // namespace msa

@@ -176,7 +176,9 @@ def test_decode_workspace_layout(lib):
     dims = D(batch=16, seq_len=262144)
     st, lo, hi = _ws(lib, _lib.MSA_OP_DECODE, dims)
     U, k, r = 16 * 8, 16, 8
-    exp = _a(U * k * r * 128 * 4) + _a(U * k * r * 8) + _a(U * k * 4)
+    # the selection (when the caller passes no sel), then two workgroup
+    # states per unit: r x (128 + 2) fp32
+    exp = _a(U * k * 4) + _a(U * 2 * r * 130 * 4)
     assert st == 0 and lo == hi == exp
     # at most 8192 candidate blocks before the own block
     assert _ws(lib, _lib.MSA_OP_DECODE, D(batch=1, seq_len=8193 * 128))[0] == 0
