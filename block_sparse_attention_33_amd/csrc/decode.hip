@@ -34,49 +34,12 @@ __device__ __forceinline__ int key_block(int64_t key) { return (int)(0xffffffffu
 
 __device__ __forceinline__ int64_t max_i64(int64_t a, int64_t b) { return a > b ? a : b; }
 
-// x combined with its DPP-moved copy (lanes the pattern does not reach keep x).
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ int64_t dpp_max_i64(int64_t x) {
-  const int lo = (int)(uint32_t)(uint64_t)x;
-  const int hi = (int)(uint32_t)((uint64_t)x >> 32);
-  const int mlo = __builtin_amdgcn_update_dpp(lo, lo, CTRL, ROW_MASK, 0xf, false);
-  const int mhi = __builtin_amdgcn_update_dpp(hi, hi, CTRL, ROW_MASK, 0xf, false);
-  const int64_t y = (int64_t)(((uint64_t)(uint32_t)mhi << 32) | (uint64_t)(uint32_t)mlo);
-  return max_i64(x, y);
-}
-
-// Maximum over the wave, returned in every lane: DPP steps within rows of 16
-// lanes, row broadcasts towards lane 63, then a read of lane 63.
-__device__ __forceinline__ int64_t wave_max_i64(int64_t x) {
-  x = dpp_max_i64<0xb1, 0xf>(x);   // quad_perm [1,0,3,2]
-  x = dpp_max_i64<0x4e, 0xf>(x);   // quad_perm [2,3,0,1]
-  x = dpp_max_i64<0x141, 0xf>(x);  // row_half_mirror
-  x = dpp_max_i64<0x140, 0xf>(x);  // row_mirror
-  x = dpp_max_i64<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
-  x = dpp_max_i64<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
-  const int lo = __builtin_amdgcn_readlane((int)(uint32_t)(uint64_t)x, 63);
-  const int hi = __builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)x >> 32), 63);
-  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint64_t)(uint32_t)lo);
-}
-
-// The best `kp` keys held by one wave (NK per lane), extracted one at a time
-// (keys are unique).  Winner `it` is returned in lane `it` (kNoKey if there
-// are fewer keys); the other lanes return kNoKey.
-template <int NK>
-__device__ __forceinline__ int64_t wave_topk(int64_t (&k)[NK], int kp) {
-  const int lane = threadIdx.x & 63;
-  int64_t mine = kNoKey;
-  for (int it = 0; it < kp; ++it) {
-    int64_t best = k[0];
-#pragma unroll
-    for (int i = 1; i < NK; ++i) best = max_i64(best, k[i]);
-    const int64_t w = wave_max_i64(best);
-#pragma unroll
-    for (int i = 0; i < NK; ++i)
-      if (k[i] == w) k[i] = kNoKey;
-    if (lane == it) mine = w;
-  }
-  return mine;
+// x plus the value of lane (lane ^ 1), then of lane (lane ^ 2): the sum over
+// the lane's quad, in every lane of the quad
+__device__ __forceinline__ int quad_sum(int x) {
+  x += __builtin_amdgcn_mov_dpp(x, 0xb1, 0xf, 0xf, false);  // quad_perm [1,0,3,2]
+  x += __builtin_amdgcn_mov_dpp(x, 0x4e, 0xf, 0xf, false);  // quad_perm [2,3,0,1]
+  return x;
 }
 
 // The best kp keys (keys unique; kNoKey = none) held by one wave, NK per
@@ -157,7 +120,7 @@ constexpr int kRowStride = 2 * 128 + 16;  // bytes per 128-key row of V^T and P^
 // key pairs (2p, 2p + 1) x 8 head dims.
 struct DecBlock {
   u32x4_t kf[8];
-  u32x4_t va[4], vb[4];
+  u32x4_t vv[8];  // V rows 8 o + i (i = 0..7), head dims 8 c .. 8 c + 7 (o, c of the thread)
 };
 
 // Loads of block j (a valid block index) for group thread gt, wave-in-group wg.
@@ -170,14 +133,14 @@ __device__ __forceinline__ void dec_load_block(const DecodeShape& sh, const uint
   const uint16_t* krow = k_cache + ((size_t)u * sh.L + key0 + min(32 * wg + col, nk - 1)) * kHeadDim;
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) blk.kf[ks] = *reinterpret_cast<const u32x4_t*>(krow + 16 * ks + 8 * hf);
-  const uint16_t* vblk = v_cache + ((size_t)u * sh.L + key0) * kHeadDim;
+  // V: thread gt takes keys 8 o .. 8 o + 7 (o = gt / 16) and head dims
+  // 8 c .. 8 c + 7 (c = gt % 16): every load instruction of a wave reads
+  // four whole 256-byte rows
+  const uint16_t* vblk = v_cache + ((size_t)u * sh.L + key0) * kHeadDim + 8 * (gt & 15);
+  const int o8 = 8 * (gt >> 4);
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int qid = gt + 256 * m;
-    const int pp = qid & 63, c = qid >> 6;
-    blk.va[m] = *reinterpret_cast<const u32x4_t*>(vblk + (size_t)min(2 * pp, nk - 1) * kHeadDim + 8 * c);
-    blk.vb[m] = *reinterpret_cast<const u32x4_t*>(vblk + (size_t)min(2 * pp + 1, nk - 1) * kHeadDim + 8 * c);
-  }
+  for (int i = 0; i < 8; ++i)
+    blk.vv[i] = *reinterpret_cast<const u32x4_t*>(vblk + (size_t)min(o8 + i, nk - 1) * kHeadDim);
 }
 
 // Running online-softmax state of a group: this lane's column (head) and its
@@ -190,31 +153,37 @@ struct DecState {
 // One slot (block j, or an empty slot when j < 0) added to the group's state.
 // Starts and ends with a workgroup barrier-free region: the caller places
 // the barriers that order the LDS buffers between slots.
-__device__ __forceinline__ void dec_slot(const DecodeShape& sh, const DecBlock& blk, int j, const u32x4_t (&qf)[8],
+__device__ __forceinline__ void dec_slot(const DecodeShape& sh, const DecBlock& blk, int j, const char* __restrict__ qs,
                                          char* __restrict__ vt, char* __restrict__ pt, float (*red_m)[32],
                                          float (*red_l)[32], int gt, int wg, int lane, DecState& st) {
   const int col = lane & 31, hf = lane >> 5;
   const bool qcol = col < sh.r;
   const int nk = j < 0 ? 0 : min(sh.bs, sh.L - j * sh.bs);  // valid keys (0: empty slot)
   const int kbase = 32 * wg;
-  // V^T in LDS, natural key order (zero beyond the block's keys)
+  // V^T in LDS: the thread's 8 x 8 tile is transposed in registers and row
+  // d = 8 c + e gets keys 8 o .. 8 o + 7 as one 16-byte write, in 16-byte
+  // column (o ^ (d >> 4)) so that the writes and the P.V reads are free of
+  // bank conflicts.  Keys past the block's end hold a copy of its last
+  // (finite) row; their P is 0.
+  {
+    const int o = gt >> 4, c = gt & 15;
+    const u32x4_t (&x)[8] = blk.vv;
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int qid = gt + 256 * m;
-    const int pp = qid & 63, c = qid >> 6;
-    const u32x4_t a = 2 * pp < nk ? blk.va[m] : u32x4_t{0u, 0u, 0u, 0u};
-    const u32x4_t bb = 2 * pp + 1 < nk ? blk.vb[m] : u32x4_t{0u, 0u, 0u, 0u};
+    for (int e = 0; e < 8; ++e) {
+      u32x4_t t;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t lo = a[e], hi = bb[e];
-      *reinterpret_cast<uint32_t*>(vt + (8 * c + 2 * e) * kRowStride + 4 * pp) = (lo & 0xffffu) | (hi << 16);
-      *reinterpret_cast<uint32_t*>(vt + (8 * c + 2 * e + 1) * kRowStride + 4 * pp) = (lo >> 16) | (hi & 0xffff0000u);
+      for (int kk = 0; kk < 4; ++kk) {
+        const uint32_t lo = x[2 * kk][e >> 1], hi = x[2 * kk + 1][e >> 1];
+        t[kk] = (e & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+      }
+      *reinterpret_cast<u32x4_t*>(vt + (8 * c + e) * kRowStride + 16 * (o ^ (c >> 1))) = t;
     }
   }
   // scores S^T (32 keys x 32 heads) of this wave, base 2
   f32x16_t s = f32x16_t{};
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) s = mfma32x32x16(blk.kf[ks], qf[ks], s);
+  for (int ks = 0; ks < 8; ++ks)
+    s = mfma32x32x16(blk.kf[ks], *reinterpret_cast<const u32x4_t*>(qs + col * kRowStride + 2 * (16 * ks + 8 * hf)), s);
   const float c2 = sh.scale_log2;
   float mx = -__builtin_inff();
 #pragma unroll
@@ -250,7 +219,8 @@ __device__ __forceinline__ void dec_slot(const DecodeShape& sh, const DecBlock& 
   f32x16_t o = f32x16_t{};
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
-    const u32x4_t a = *reinterpret_cast<const u32x4_t*>(vt + (32 * wg + col) * kRowStride + 2 * (16 * kk + 8 * hf));
+    const int d = 32 * wg + col;
+    const u32x4_t a = *reinterpret_cast<const u32x4_t*>(vt + d * kRowStride + 16 * ((2 * kk + hf) ^ (d >> 4)));
     // columns >= r read some head's row: their results are not used
     const u32x4_t bq = *reinterpret_cast<const u32x4_t*>(pt + (col & 15) * kRowStride + 2 * (16 * kk + 8 * hf));
     o = mfma32x32x16(a, bq, o);
@@ -271,15 +241,23 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(const uint16_t* __restri
                                                         int32_t* __restrict__ sel_out, uint16_t* __restrict__ out,
                                                      float* __restrict__ state,
                                                         DecodeShape sh) {
-  __shared__ __align__(16) char vt[2][kHeadDim * kRowStride];
-  __shared__ __align__(16) char pt[2][16 * kRowStride];  // P^T rows of the r <= 16 heads
-  __shared__ int64_t wbest[8 * 32];                // the waves' best kp, list w at w * kp
-  __shared__ int64_t wscr[8][64 + 64 * NK];         // per-wave top-k scratch
+  // the groups' V^T and P^T (r <= 16 heads) buffers; during the selection
+  // they hold its scratch: the waves' best kp (list w at w * kp) and the
+  // per-wave top-k scratch
+  constexpr int kVt = kHeadDim * kRowStride, kPt = 16 * kRowStride;
+  constexpr int kScr = 64 + 64 * NK;
+  __shared__ __align__(16) char abuf[2 * kVt + 2 * kPt];
+  static_assert(8 * (8 * 32 + 8 * kScr) <= 2 * kVt + 2 * kPt, "selection scratch exceeds the attention buffers");
+  char (*vt)[kVt] = reinterpret_cast<char (*)[kVt]>(abuf);
+  char (*pt)[kPt] = reinterpret_cast<char (*)[kPt]>(abuf + 2 * kVt);
+  int64_t* wbest = reinterpret_cast<int64_t*>(abuf);
+  int64_t (*wscr)[kScr] = reinterpret_cast<int64_t (*)[kScr]>(abuf + 8 * 8 * 32);
   __shared__ int sorted[33];
   __shared__ float red_m[2][4][32];
   __shared__ float red_l[2][4][32];
   __shared__ float xo[16][kHeadDim];  // the odd-slot group's state for the final merge
   __shared__ float xml[16][2];
+  __shared__ __align__(16) char qs[32 * kRowStride];  // query rows (bf16), rows >= r zero
 
   const int u = blockIdx.x;
   const int part = blockIdx.y;  // this workgroup's share of the slots
@@ -298,83 +276,81 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(const uint16_t* __restri
   const int K = sh.top_k;
   const int kp = K - 1;
   const int own = sh.nb - 1;  // candidates are blocks 0 .. own - 1
+  // the unit's query rows in LDS (rows r .. 31 zero), read per slot
+  if (tid < 32 * 16) {
+    const int row = tid >> 4, ch = tid & 15;
+    u32x4_t v4 = u32x4_t{0u, 0u, 0u, 0u};
+    if (row < r) v4 = *reinterpret_cast<const u32x4_t*>(q + ((size_t)b * sh.Hq + g * r + row) * kHeadDim + 8 * ch);
+    *reinterpret_cast<u32x4_t*>(qs + row * kRowStride + 16 * ch) = v4;
+  }
 
   // ---- selection
   if (kp > 0) {
-    const i32x4_t* qp = reinterpret_cast<const i32x4_t*>(q_idx + (size_t)u * kIdxDim);
-    const i32x4_t q0 = qp[0], q1 = qp[1], q2 = qp[2], q3 = qp[3];
-    const int8_t* kb = block_keys + (size_t)u * sh.nb * kIdxDim;
+    // the 64-byte summary of candidate c is read as four 16-byte quarters by
+    // the four lanes of a quad (each wave load covers 16 whole summaries);
+    // thread tid takes quarter tid % 4 of candidates 128 i + tid / 4 and
+    // keeps the keys of i = 4 m + tid % 4 (candidates 512 m + 128 (tid % 4)
+    // + tid / 4), m < NK
+    const int qq = tid & 3;
+    const i32x4_t qv = reinterpret_cast<const i32x4_t*>(q_idx + (size_t)u * kIdxDim)[qq];
+    const int8_t* kb = block_keys + (size_t)u * sh.nb * kIdxDim + 16 * qq;
     int64_t keys[NK];
 #pragma unroll
-    for (int m = 0; m < NK; ++m) {
-      const int j = tid + 512 * m;
-      int64_t key = kNoKey;
-      if (512 * m < own) {  // uniform: the loads below are unconditional within it
-        const i32x4_t* sp = reinterpret_cast<const i32x4_t*>(kb + (size_t)min(j, own - 1) * kIdxDim);
-        const i32x4_t a0 = sp[0], a1 = sp[1], a2 = sp[2], a3 = sp[3];
+    for (int m = 0; m < NK; ++m) keys[m] = kNoKey;
+#pragma unroll
+    for (int i = 0; i < 4 * NK; ++i) {
+      if (128 * i < own) {  // uniform: the quad sums below run in whole quads
+        const int c = 128 * i + (tid >> 2);
+        const i32x4_t a = *reinterpret_cast<const i32x4_t*>(kb + (size_t)min(c, own - 1) * kIdxDim);
         int sc = 0;
-        sc = sdot4(q0.x, a0.x, sc); sc = sdot4(q0.y, a0.y, sc); sc = sdot4(q0.z, a0.z, sc); sc = sdot4(q0.w, a0.w, sc);
-        sc = sdot4(q1.x, a1.x, sc); sc = sdot4(q1.y, a1.y, sc); sc = sdot4(q1.z, a1.z, sc); sc = sdot4(q1.w, a1.w, sc);
-        sc = sdot4(q2.x, a2.x, sc); sc = sdot4(q2.y, a2.y, sc); sc = sdot4(q2.z, a2.z, sc); sc = sdot4(q2.w, a2.w, sc);
-        sc = sdot4(q3.x, a3.x, sc); sc = sdot4(q3.y, a3.y, sc); sc = sdot4(q3.z, a3.z, sc); sc = sdot4(q3.w, a3.w, sc);
-        key = j < own ? rank_key(sc, j) : kNoKey;
+        sc = sdot4(qv.x, a.x, sc);
+        sc = sdot4(qv.y, a.y, sc);
+        sc = sdot4(qv.z, a.z, sc);
+        sc = sdot4(qv.w, a.w, sc);
+        sc = quad_sum(sc);
+        if ((i & 3) == qq && c < own) keys[i >> 2] = rank_key(sc, c);
       }
-      keys[m] = key;
     }
     wave_topk_rank(keys, kp, wscr[w], wbest + w * kp);
   }
   __syncthreads();
-  if (w == 0) {
-    // the best kp of the 8 waves' lists (8 kp <= 248 keys, up to 4 a lane),
-    // by rank, then ranked by block index among themselves
+  // the best kp of the 8 waves' lists (n2 = 8 kp keys): key ci is ranked
+  // against the whole list by the four threads 4 ci .. 4 ci + 3, each over
+  // a quarter of it
+  int* kept = reinterpret_cast<int*>(wscr[0]);  // the kept blocks, by rank
+  const int n_valid = min(kp, own);             // valid keys that exist
+  {
     const int n2 = 8 * kp;
-    int64_t x[4];
-    int rk[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      x[m] = lane + 64 * m < n2 ? wbest[lane + 64 * m] : kNoKey;
-      rk[m] = 0;
+    const int qq = tid & 3;
+    const int per = (n2 + 3) >> 2;
+    const int j0 = qq * per, j1 = min(n2, j0 + per);
+    const int passes = (n2 + 127) >> 7;  // the same for every thread (quad sums)
+    for (int pz = 0; pz < passes; ++pz) {
+      const int ci = 128 * pz + (tid >> 2);
+      const int64_t x = ci < n2 ? wbest[ci] : kNoKey;
+      int rk = 0;
+#pragma unroll 4
+      for (int jj = j0; jj < j1; ++jj) rk += wbest[jj] > x ? 1 : 0;
+      rk = quad_sum(rk);
+      if (qq == 0 && x != kNoKey && rk < kp) kept[rk] = key_block(x);
     }
-#pragma unroll 8
-    for (int jj = 0; jj < n2; ++jj) {
-      const int64_t y = wbest[jj];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) rk[m] += y > x[m] ? 1 : 0;
-    }
-    int* kept = reinterpret_cast<int*>(wscr[0]);  // the kept blocks, by rank
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-      if (x[m] != kNoKey && rk[m] < kp) kept[rk[m]] = key_block(x[m]);
-    const int n_valid = min(kp, own);  // valid keys that exist
-    wave_lds_sync();
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      if (x[m] != kNoKey && rk[m] < kp) {
-        const int blk = key_block(x[m]);
-        int pos = 0;
-#pragma unroll 8
-        for (int i = 0; i < n_valid; ++i) pos += kept[i] < blk ? 1 : 0;
-        sorted[pos] = blk;
-      }
-    }
-    if (lane == n_valid) sorted[n_valid] = own;
-    if (lane > n_valid && lane <= 32) sorted[lane] = -1;
   }
+  __syncthreads();
+  // slot order: the kept blocks ascending, the own block, then empty (-1)
+  if (tid < n_valid) {
+    const int blk = kept[tid];
+    int pos = 0;
+    for (int i = 0; i < n_valid; ++i) pos += kept[i] < blk ? 1 : 0;
+    sorted[pos] = blk;
+  }
+  if (tid == n_valid) sorted[n_valid] = own;
+  if (tid > n_valid && tid <= 32) sorted[tid] = -1;
   __syncthreads();
   if (part == 0 && tid < K) sel_out[(size_t)u * K + tid] = sorted[tid];
 
   // ---- attention: group gp takes slots gp, gp + 2, ...; a group's next
   // slot loads while the current one is computed (two register sets, so
   // that no load result is moved between registers)
-  u32x4_t qf[8];
-  {
-    const uint16_t* qrow = q + ((size_t)b * sh.Hq + g * r + min(col, r - 1)) * kHeadDim;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      qf[ks] = *reinterpret_cast<const u32x4_t*>(qrow + 16 * ks + 8 * hf);
-      if (col >= r) qf[ks] = u32x4_t{0u, 0u, 0u, 0u};
-    }
-  }
   DecState st;
   st.o = f32x16_t{};
   st.m = -__builtin_inff();
@@ -396,11 +372,11 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(const uint16_t* __restri
   for (int rd = 0; rd < n_rounds; rd += 2) {
     load_round(rd + 1, B);
     if (rd > 0) __syncthreads();  // the previous slot's LDS reads are done
-    dec_slot(sh, A, slot_block(rd), qf, vt[gp], pt[gp], red_m[gp], red_l[gp], gt, wg, lane, st);
+    dec_slot(sh, A, slot_block(rd), qs, vt[gp], pt[gp], red_m[gp], red_l[gp], gt, wg, lane, st);
     if (rd + 1 >= n_rounds) break;
     load_round(rd + 2, A);
     __syncthreads();
-    dec_slot(sh, B, slot_block(rd + 1), qf, vt[gp], pt[gp], red_m[gp], red_l[gp], gt, wg, lane, st);
+    dec_slot(sh, B, slot_block(rd + 1), qs, vt[gp], pt[gp], red_m[gp], red_l[gp], gt, wg, lane, st);
   }
 
   // ---- merge of the two groups' states -> out = o / l
@@ -456,11 +432,11 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(const uint16_t* __restri
   }
 }
 
-// Merge of a unit's n_split workgroup states: one workgroup per unit, a
-// thread per (head, 4 head dims): out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.
+// Merge of a unit's two workgroup states: one workgroup per unit, a thread
+// per (head, 4 head dims): out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.
+// Every load is issued before the first use.
 __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restrict__ state,
-                                                           uint16_t* __restrict__ out, DecodeShape sh,
-                                                           int n_split) {
+                                                           uint16_t* __restrict__ out, DecodeShape sh) {
   const int u = blockIdx.x;
   const int b = u / sh.G;
   const int g = u - b * sh.G;
@@ -468,25 +444,23 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
   for (int it = threadIdx.x; it < r * 32; it += 256) {
     const int h = it >> 5;
     const int d0 = (it & 31) * 4;
-    float M = -__builtin_inff();
-    for (int p = 0; p < n_split; ++p)
-      M = fmaxf(M, state[(((size_t)u * n_split + p) * r + h) * (kHeadDim + 2) + kHeadDim]);
-    float W = 0.f;
-    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int p = 0; p < n_split; ++p) {
-      const float* srow = state + (((size_t)u * n_split + p) * r + h) * (kHeadDim + 2);
-      const float m = srow[kHeadDim];
-      if (m == -__builtin_inff()) continue;  // a share with no kept block
-      const float wgt = fast_exp2(m - M);
-      W = fmaf(wgt, srow[kHeadDim + 1], W);
-      const f32x4_t o4 = *reinterpret_cast<const f32x4_t*>(srow + d0);
+    const float* s0 = state + (((size_t)u * 2 + 0) * r + h) * (kHeadDim + 2);
+    const float* s1 = state + (((size_t)u * 2 + 1) * r + h) * (kHeadDim + 2);
+    const float m0 = s0[kHeadDim], l0 = s0[kHeadDim + 1];
+    const float m1 = s1[kHeadDim], l1 = s1[kHeadDim + 1];
+    const f32x4_t o0 = *reinterpret_cast<const f32x4_t*>(s0 + d0);
+    const f32x4_t o1 = *reinterpret_cast<const f32x4_t*>(s1 + d0);
+    // a share with no kept block has m = -inf, weight 0 (M is finite: the
+    // own block is always kept)
+    const float M = fmaxf(m0, m1);
+    const float w0 = fast_exp2(m0 - M), w1 = fast_exp2(m1 - M);
+    const float inv = 1.0f / fmaf(w0, l0, w1 * l1);
+    float v[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = fmaf(wgt, o4[e], acc[e]);
-    }
-    const float inv = 1.0f / W;
+    for (int e = 0; e < 4; ++e) v[e] = fmaf(w0, o0[e], w1 * o1[e]) * inv;
     u32x2_t wv;
-    wv.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-    wv.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+    wv.x = pack_bf16x2(v[0], v[1]);
+    wv.y = pack_bf16x2(v[2], v[3]);
     *reinterpret_cast<u32x2_t*>(out + ((size_t)b * sh.Hq + g * r + h) * kHeadDim + d0) = wv;
   }
 }
@@ -496,6 +470,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
 hipError_t launch_decode(const DecodeShape& sh, const uint16_t* q, const int8_t* q_idx, const uint16_t* k_cache,
                          const uint16_t* v_cache, const int8_t* block_keys, int32_t* sel_out, uint16_t* out,
                          float* state, int n_split, hipStream_t st) {
+  if (n_split < 1 || n_split > 2) return hipErrorInvalidValue;  // the merge combines two states
   const int own = sh.nb - 1;
   const dim3 grid(sh.B * sh.G, n_split), block(512);
   if (own <= 4 * 512)
@@ -512,7 +487,8 @@ hipError_t launch_decode(const DecodeShape& sh, const uint16_t* q, const int8_t*
 
 hipError_t launch_decode_merge(const DecodeShape& sh, const float* state, int n_split, uint16_t* out,
                                hipStream_t st) {
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(sh.B * sh.G), dim3(256), 0, st, state, out, sh, n_split);
+  if (n_split != 2) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(sh.B * sh.G), dim3(256), 0, st, state, out, sh);
   return hipGetLastError();
 }
 

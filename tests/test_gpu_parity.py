@@ -250,6 +250,9 @@ def _decode_case(w, L, B, seed, n_check_units=None):
     (100, 1, dict(block_size=128, top_k=4)),
     (5000, 2, dict(n_q_heads=16, n_kv_heads=1, block_size=32, top_k=32)),
     (3000, 2, dict(n_q_heads=8, n_kv_heads=8, top_k=1)),
+    # more than 2048 and more than 4096 candidate blocks (8 and 16 per thread)
+    (150000, 1, dict(n_q_heads=8, n_kv_heads=1, block_size=64, top_k=16)),
+    (300001, 1, dict(n_q_heads=8, n_kv_heads=1, block_size=64, top_k=20)),
 ])
 def test_decode_small(L, B, over):
     w = get_workload("decode_b16_256k", **over)
