@@ -78,11 +78,11 @@ def _measured_traffic():
 
 def pmc_run():
     """Workload for counter runs under rocprofv3 --pmc: two 32K prefills,
-    then a 1 GiB device copy whose bytes are known (the calibration of the
-    FETCH_SIZE / WRITE_SIZE counters)."""
+    two decodes of the decode workload, then a 1 GiB device copy whose bytes
+    are known (the calibration of the FETCH_SIZE / WRITE_SIZE counters)."""
     import torch
     import block_sparse_attention_33_amd as msa
-    from synth import get_workload, prefill_inputs
+    from synth import decode_inputs, get_workload, prefill_inputs
     dev = torch.device("cuda:0")
     w = get_workload("prefill_32k")
     inp = prefill_inputs(w, seed=0, device=dev)
@@ -92,12 +92,70 @@ def pmc_run():
     for _ in range(2):
         msa.msa_prefill(inp["q"], inp["k"], inp["v"], inp["q_idx"], inp["k_idx"], w.block_size, w.top_k,
                         workspace=ws)
+    del inp, ws
+    wd = get_workload("decode_b16_256k")
+    din = decode_inputs(wd, seed=0, device=dev)
+    bk = msa.msa_pool_block_keys(din["k_idx_cache"], wd.block_size)
+    del din["k_idx_cache"]
+    for _ in range(2):
+        msa.msa_decode(din["q"], din["q_idx"], din["k_cache"], din["v_cache"], bk, wd.block_size, wd.top_k)
+    del din, bk
     src = torch.ones(2**30 // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"pmc_run": "done", "copy_bytes_each_way": 2**30,
                       "kernel_source_sha256_16": kernel_source_hash()}))
+
+
+def pmc_summary(fetch_csv, write_csv, commands):
+    """Per-dispatch HBM traffic of the MSA kernels from two rocprofv3 --pmc
+    runs of --pmc-run (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each
+    scaled by what the counter reads for the 1 GiB copy at the end of the
+    run.  Writes the record that the benchmark line's roofline.traffic reads."""
+    import csv
+    import re
+
+    def per_kernel(path, counter):
+        got = {}
+        with open(path, newline="") as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] != counter:
+                    continue
+                name = row["Kernel_Name"]
+                m = re.search(r"msa::\(anonymous namespace\)::(\w+(?:<\d+>)?)", name)
+                key = m.group(1) if m else ("copy" if "copyBuffer" in name else None)
+                if key:
+                    got.setdefault(key, []).append(float(row["Counter_Value"]))
+        return got
+
+    fk, wk = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    copy_kib = 2**30 / 1024.0
+    fscale, wscale = copy_kib / fk["copy"][-1], copy_kib / wk["copy"][-1]
+    rec = {
+        "kernel": "attend_kernel<128>",
+        "workload": "prefill_32k (batch 1, seq 32768, 64q/8kv heads, head_dim 128, block 128, top_k 16); "
+                    "decode_b16_256k (16 x 262144-token caches, same heads)",
+        "kernel_source_sha256_16": kernel_source_hash(),
+        "commands": commands,
+        "calibration": {"kernel": "__amd_rocclr_copyBuffer, 1 GiB device copy",
+                        "fetch_kib_read": fk["copy"][-1], "write_kib_read": wk["copy"][-1],
+                        "bytes_each_way": 2**30, "fetch_scale": round(fscale, 5), "write_scale": round(wscale, 5)},
+        "note": "FETCH_SIZE counts L2 misses sent to the fabric (memory-side cache hits included); "
+                "values are per dispatch, scaled by the copy-kernel factors",
+    }
+    for k in sorted(set(fk) & set(wk)):
+        if k == "copy":
+            continue
+        fb = sum(fk[k]) / len(fk[k]) * 1024 * fscale
+        wb = sum(wk[k]) / len(wk[k]) * 1024 * wscale
+        rec[k] = {"dispatches": len(fk[k]), "fetch_kib_per_dispatch": fk[k], "write_kib_per_dispatch": wk[k],
+                  "fetch_bytes": round(fb), "write_bytes": round(wb), "bytes": round(fb + wb)}
+    rec["bytes_per_launch"] = rec["attend_kernel<128>"]["bytes"]
+    out = os.path.join(ROOT, "profiles", "attend_prefill_32k_traffic.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps({"written": out, "attend_bytes_per_launch": rec["bytes_per_launch"]}))
 
 
 def cpu_baseline_worker(npz_path):
@@ -156,7 +214,13 @@ def main():
     ap.add_argument("--cpu-baseline-worker", default=None, help=argparse.SUPPRESS)
     ap.add_argument("--pmc-run", action="store_true",
                     help="run the counter-collection workload instead of the benchmark")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the traffic record from the two counter runs' CSV files")
+    ap.add_argument("--pmc-commands", nargs="*", default=[], help=argparse.SUPPRESS)
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.pmc_commands)
+        return 0
     if args.cpu_baseline_worker:
         cpu_baseline_worker(args.cpu_baseline_worker)
         return 0
