@@ -85,8 +85,8 @@ __device__ __forceinline__ void load_kv_regs(const uint16_t* __restrict__ kblk, 
 #pragma unroll
   for (int m = 0; m < KvStage<BS, NT>::kV; ++m) {
     const int qid = tid + NT * m;
-    const int p = qid % (BS / 2);
-    const int c = qid / (BS / 2);
+    const int p = qid >> 4;  // 16 lanes read the two whole rows of key pair p
+    const int c = qid & 15;
     st.va[m] = *reinterpret_cast<const u32x4_t*>(vblk + min(2 * p, n_keys - 1) * kHeadDim + c * 8);
     st.vb[m] = *reinterpret_cast<const u32x4_t*>(vblk + min(2 * p + 1, n_keys - 1) * kHeadDim + c * 8);
   }
@@ -110,8 +110,8 @@ __device__ __forceinline__ void store_kv_lds(const KvStage<BS, NT>& st, int n_ke
 #pragma unroll
   for (int m = 0; m < KvStage<BS, NT>::kV; ++m) {
     const int qid = tid + NT * m;
-    const int p = qid % (BS / 2);
-    const int c = qid / (BS / 2);
+    const int p = qid >> 4;
+    const int c = qid & 15;
     const u32x4_t a = 2 * p < n_keys ? st.va[m] : u32x4_t{0u, 0u, 0u, 0u};
     const u32x4_t b = 2 * p + 1 < n_keys ? st.vb[m] : u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
