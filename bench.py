@@ -244,6 +244,13 @@ def main():
     pin = prefill_inputs(wp, seed=0, device=dev)
     din = decode_inputs(wd, seed=0, device=dev)
     block_keys = msa.msa_pool_block_keys(din["k_idx_cache"], wd.block_size)
+    # generation step (append + decode) at the same shape: the caches hold
+    # L - 1 tokens and each step appends token L - 1
+    L = wd.seq_len
+    gen_keys, gen_sums = msa.msa_decode_init(din["k_idx_cache"], L - 1, wd.block_size)
+    k_new = din["k_cache"][:, :, L - 1].contiguous()
+    v_new = din["v_cache"][:, :, L - 1].contiguous()
+    k_idx_new = din["k_idx_cache"][:, :, L - 1].contiguous()
     del din["k_idx_cache"]
     out = torch.empty_like(pin["q"])
     dout = torch.empty_like(din["q"])
@@ -299,6 +306,34 @@ def main():
     msa.profile_enable(False)
     dkt = msa.profile_read()
 
+    # generation step: append token L - 1 to the caches, refresh its block's
+    # summary, decode (outside the timed region; same events)
+    def gen_step():
+        msa.msa_decode_step(din["q"], din["q_idx"], k_new, v_new, k_idx_new, din["k_cache"], din["v_cache"],
+                            gen_sums, gen_keys, L, wd.block_size, wd.top_k, out=dout, workspace=dws)
+
+    for _ in range(3):
+        gen_step()
+    torch.cuda.synchronize()
+    gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in gev:
+        a.record()
+        gen_step()
+        b.record()
+    torch.cuda.synchronize()
+    gen_us = sorted(a.elapsed_time(b) * 1e3 for a, b in gev)
+    gen_med = gen_us[len(gen_us) // 2]
+    # the plain decode timed the same way (back to back, so the kept blocks
+    # may still sit in the memory-side cache, unlike in the step above where
+    # a prefill runs in between)
+    for a, b in gev:
+        a.record()
+        decode()
+        b.record()
+    torch.cuda.synchronize()
+    dwarm_us = sorted(a.elapsed_time(b) * 1e3 for a, b in gev)
+    dwarm_med = dwarm_us[len(dwarm_us) // 2]
+
     per_head_keys, pairs, rows_merged = _prefill_counts(wp)
     D = wp.head_dim
     flop_alg = 4.0 * D * wp.n_q_heads * per_head_keys
@@ -351,6 +386,14 @@ def main():
             "hbm_gbs_alg": round(dbytes / (dec_med * 1e-3) / 1e9, 1),
             "frac_hbm_peak": round(dbytes / (dec_med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "bytes_alg": dbytes,
+        },
+        "decode_step": {
+            "what": "append one token per sequence (K/V rows, running index-key sum, block summary) + decode",
+            "us": round(gen_med, 2),
+            "tokens_per_s": round(wd.batch / (gen_med * 1e-6), 1),
+            "frac_hbm_peak": round(dbytes / (gen_med * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "timing": "back-to-back calls",
+            "decode_only_back_to_back_us": round(dwarm_med, 2),
         },
         "roofline": {
             "kernel": "attend (KV-outer block attention, all kept blocks)",

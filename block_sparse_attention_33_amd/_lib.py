@@ -47,6 +47,9 @@ SIGNATURES = {
     "msa_index_select": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "msa_prefill": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "msa_decode": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "msa_decode_init": (ctypes.c_int, [_DIMS, ctypes.c_int32, _P, _P, _P, _P]),
+    "msa_decode_step": (ctypes.c_int, [_DIMS, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                       ctypes.c_size_t, _P]),
     "msa_profile_enable": (ctypes.c_int, [ctypes.c_int]),
     "msa_profile_read": (ctypes.c_int, [ctypes.POINTER(MsaKernelTime), ctypes.c_int,
                                         ctypes.POINTER(ctypes.c_int)]),

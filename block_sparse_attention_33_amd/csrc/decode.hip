@@ -130,13 +130,13 @@ __device__ __forceinline__ void dec_load_block(const DecodeShape& sh, const uint
   const int key0 = j * sh.bs;
   const int nk = min(sh.bs, sh.L - key0);
   const int col = lane & 31, hf = lane >> 5;
-  const uint16_t* krow = k_cache + ((size_t)u * sh.L + key0 + min(32 * wg + col, nk - 1)) * kHeadDim;
+  const uint16_t* krow = k_cache + ((size_t)u * sh.Lc + key0 + min(32 * wg + col, nk - 1)) * kHeadDim;
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) blk.kf[ks] = *reinterpret_cast<const u32x4_t*>(krow + 16 * ks + 8 * hf);
   // V: thread gt takes keys 8 o .. 8 o + 7 (o = gt / 16) and head dims
   // 8 c .. 8 c + 7 (c = gt % 16): every load instruction of a wave reads
   // four whole 256-byte rows
-  const uint16_t* vblk = v_cache + ((size_t)u * sh.L + key0) * kHeadDim + 8 * (gt & 15);
+  const uint16_t* vblk = v_cache + ((size_t)u * sh.Lc + key0) * kHeadDim + 8 * (gt & 15);
   const int o8 = 8 * (gt >> 4);
 #pragma unroll
   for (int i = 0; i < 8; ++i)
@@ -293,7 +293,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(const uint16_t* __restri
     // + tid / 4), m < NK
     const int qq = tid & 3;
     const i32x4_t qv = reinterpret_cast<const i32x4_t*>(q_idx + (size_t)u * kIdxDim)[qq];
-    const int8_t* kb = block_keys + (size_t)u * sh.nb * kIdxDim + 16 * qq;
+    const int8_t* kb = block_keys + (size_t)u * sh.nbc * kIdxDim + 16 * qq;
     int64_t keys[NK];
 #pragma unroll
     for (int m = 0; m < NK; ++m) keys[m] = kNoKey;
@@ -465,6 +465,32 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
   }
 }
 
+// Append of one token per (batch, group) unit at position pos: its K and V
+// rows go to the caches, its index key is added to the running int32 sums
+// of its block (which restart when pos opens a block) and the block's
+// summary becomes the floor-mean of the sums over the block's pos % bs + 1
+// tokens, so the summaries always equal the pooling of the cache prefix.
+__global__ __launch_bounds__(64) void append_kernel(const uint16_t* __restrict__ k_new,
+                                                    const uint16_t* __restrict__ v_new,
+                                                    const int8_t* __restrict__ k_idx_new,
+                                                    uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache,
+                                                    int32_t* __restrict__ open_sums,
+                                                    int8_t* __restrict__ block_keys, DecodeShape sh, int pos) {
+  const int u = blockIdx.x;
+  const int l = threadIdx.x;
+  const size_t row = ((size_t)u * sh.Lc + pos) * kHeadDim;
+  if (l < 16)
+    reinterpret_cast<u32x4_t*>(k_cache + row)[l] = reinterpret_cast<const u32x4_t*>(k_new + (size_t)u * kHeadDim)[l];
+  else if (l < 32)
+    reinterpret_cast<u32x4_t*>(v_cache + row)[l - 16] =
+        reinterpret_cast<const u32x4_t*>(v_new + (size_t)u * kHeadDim)[l - 16];
+  const int j = pos / sh.bs;
+  const int n = pos - j * sh.bs + 1;  // tokens of block j after the append
+  const int s = (n == 1 ? 0 : open_sums[(size_t)u * kIdxDim + l]) + (int)k_idx_new[(size_t)u * kIdxDim + l];
+  open_sums[(size_t)u * kIdxDim + l] = s;
+  block_keys[((size_t)u * sh.nbc + j) * kIdxDim + l] = (int8_t)floor_div(s, n);
+}
+
 }  // namespace
 
 hipError_t launch_decode(const DecodeShape& sh, const uint16_t* q, const int8_t* q_idx, const uint16_t* k_cache,
@@ -482,6 +508,14 @@ hipError_t launch_decode(const DecodeShape& sh, const uint16_t* q, const int8_t*
   else
     hipLaunchKernelGGL(decode_kernel<16>, grid, block, 0, st, q, q_idx, k_cache, v_cache, block_keys, sel_out, out,
                        state, sh);
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const DecodeShape& sh, const uint16_t* k_new, const uint16_t* v_new,
+                         const int8_t* k_idx_new, uint16_t* k_cache, uint16_t* v_cache, int32_t* open_sums,
+                         int8_t* block_keys, int pos, hipStream_t st) {
+  hipLaunchKernelGGL(append_kernel, dim3(sh.B * sh.G), dim3(64), 0, st, k_new, v_new, k_idx_new, k_cache, v_cache,
+                     open_sums, block_keys, sh, pos);
   return hipGetLastError();
 }
 

@@ -18,13 +18,18 @@ namespace msa {
 namespace {
 
 // ---------------------------------------------------------------------------
-// Pooling: one wave per (unit, block).  Lane (row, col) = (lane / 16, lane %
-// 16) sums dword `col` (4 index dims) of tokens row, row + 4, ...; the four
-// rows are folded with lane shuffles.  HBM-bound streaming read.
+// Pooling: one wave per (unit, block) of the first S tokens.  Lane (row, col)
+// = (lane / 16, lane % 16) sums dword `col` (4 index dims) of tokens row,
+// row + 4, ...; the four rows are folded with lane shuffles.  HBM-bound
+// streaming read.  k_idx rows of a unit are s_stride apart, summaries
+// nb_stride apart.  open_sums (optional): the int32 sums of the block the
+// next token goes to, tokens nb' * bs .. S - 1 with nb' = floor(S / bs)
+// (zero when S is a multiple of bs).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void pool_kernel(const int8_t* __restrict__ k_idx,
                                                    int8_t* __restrict__ block_keys, int units,
-                                                   int S, int bs, int nb) {
+                                                   int S, int bs, int nb, long s_stride, int nb_stride,
+                                                   int32_t* __restrict__ open_sums) {
   const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (wid >= units * nb) return;
   const int lane = threadIdx.x & 63;
@@ -32,7 +37,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const int8_t* __restrict__ k_
   const int j = wid - u * nb;
   const int t0 = j * bs;
   const int n = min(bs, S - t0);
-  const uint32_t* base = reinterpret_cast<const uint32_t*>(k_idx + ((size_t)u * S + t0) * kIdxDim);
+  const uint32_t* base = reinterpret_cast<const uint32_t*>(k_idx + ((size_t)u * s_stride + t0) * kIdxDim);
   const int col = lane & 15;
   const int row = lane >> 4;
   int s0 = 0, s1 = 0, s2 = 0, s3 = 0;
@@ -57,7 +62,16 @@ __global__ __launch_bounds__(256) void pool_kernel(const int8_t* __restrict__ k_
                             ((uint32_t)(floor_div(s1, n) & 0xff) << 8) |
                             ((uint32_t)(floor_div(s2, n) & 0xff) << 16) |
                             ((uint32_t)(floor_div(s3, n) & 0xff) << 24);
-    reinterpret_cast<uint32_t*>(block_keys + ((size_t)u * nb + j) * kIdxDim)[col] = packed;
+    reinterpret_cast<uint32_t*>(block_keys + ((size_t)u * nb_stride + j) * kIdxDim)[col] = packed;
+    if (open_sums != nullptr && j == nb - 1) {
+      const bool partial = n < bs;
+      i32x4_t v4;
+      v4.x = partial ? s0 : 0;
+      v4.y = partial ? s1 : 0;
+      v4.z = partial ? s2 : 0;
+      v4.w = partial ? s3 : 0;
+      reinterpret_cast<i32x4_t*>(open_sums + (size_t)u * kIdxDim)[col] = v4;
+    }
   }
 }
 
@@ -197,9 +211,16 @@ __global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* __restrict__ p, 
 hipError_t launch_pool(const int8_t* k_idx, int8_t* block_keys, int units, int S, int bs,
                        hipStream_t st) {
   const int nb = (S + bs - 1) / bs;
+  return launch_pool_strided(k_idx, block_keys, nullptr, units, S, S, nb, bs, st);
+}
+
+hipError_t launch_pool_strided(const int8_t* k_idx, int8_t* block_keys, int32_t* open_sums, int units, int S,
+                               long s_stride, int nb_stride, int bs, hipStream_t st) {
+  const int nb = (S + bs - 1) / bs;
   const long waves = (long)units * nb;
   const unsigned grid = (unsigned)((waves + 3) / 4);
-  hipLaunchKernelGGL(pool_kernel, dim3(grid), dim3(256), 0, st, k_idx, block_keys, units, S, bs, nb);
+  hipLaunchKernelGGL(pool_kernel, dim3(grid), dim3(256), 0, st, k_idx, block_keys, units, S, bs, nb, s_stride,
+                     nb_stride, open_sums);
   return hipGetLastError();
 }
 

@@ -230,6 +230,44 @@ int bs_log2_of(long bs) {
   return l;
 }
 
+
+msa::DecodeShape decode_shape(const Dims& d, long length) {
+  msa::DecodeShape sh;
+  sh.B = (int)d.B;
+  sh.L = (int)length;
+  sh.Hq = (int)d.Hq;
+  sh.G = (int)d.G;
+  sh.r = (int)d.r;
+  sh.bs = (int)d.bs;
+  sh.nb = (int)((length + d.bs - 1) / d.bs);
+  sh.top_k = (int)d.k;
+  sh.Lc = (int)d.S;
+  sh.nbc = (int)d.nb;
+  sh.scale_log2 = d.scale * 1.4426950408889634f;
+  return sh;
+}
+
+// Decode of the query at position length - 1 over caches with room for d.S
+// tokens per unit (arguments already checked).
+int run_decode(const Dims& d, long length, const uint16_t* q, const int8_t* q_idx, const uint16_t* k_cache,
+               const uint16_t* v_cache, const int8_t* block_keys, uint16_t* out, int32_t* sel, void* ws,
+               size_t ws_bytes, hipStream_t s) {
+  DecodeLayout L;
+  int st = decode_layout(d, &L);
+  if (st != MSA_OK) return st;
+  st = check_ws(ws, ws_bytes, L.total);
+  if (st != MSA_OK) return st;
+  char* base = static_cast<char*>(ws);
+  const msa::DecodeShape sh = decode_shape(d, length);
+  int32_t* sel_use = sel ? sel : reinterpret_cast<int32_t*>(base + L.sel);
+  float* state = reinterpret_cast<float*>(base + L.state);
+  const int n_split = decode_split(d);
+  MSA_LAUNCH_NAMED("decode", s,
+                   msa::launch_decode(sh, q, q_idx, k_cache, v_cache, block_keys, sel_use, out, state, n_split, s));
+  if (n_split > 1) MSA_LAUNCH_NAMED("decode_merge", s, msa::launch_decode_merge(sh, state, n_split, out, s));
+  return MSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -251,7 +289,7 @@ const char* msa_status_string(int status) {
   }
 }
 
-int msa_version(void) { return 10000; }
+int msa_version(void) { return 10100; }
 
 int msa_workspace_bytes(int op, const msa_dims* dims, size_t* min_bytes, size_t* full_bytes) {
   Dims d;
@@ -402,6 +440,7 @@ int msa_prefill(const msa_dims* dims, const uint16_t* q, const uint16_t* k, cons
   return MSA_OK;
 }
 
+
 int msa_decode(const msa_dims* dims, const uint16_t* q, const int8_t* q_idx, const uint16_t* k_cache,
                const uint16_t* v_cache, const int8_t* block_keys, uint16_t* out, int32_t* sel, void* ws,
                size_t ws_bytes, void* stream) {
@@ -409,30 +448,42 @@ int msa_decode(const msa_dims* dims, const uint16_t* q, const int8_t* q_idx, con
   int st = check_dims(dims, &d);
   if (st != MSA_OK) return st;
   if (!q || !q_idx || !k_cache || !v_cache || !block_keys || !out) return MSA_ERR_INVALID_ARG;
+  return run_decode(d, d.S, q, q_idx, k_cache, v_cache, block_keys, out, sel, ws, ws_bytes, (hipStream_t)stream);
+}
+
+int msa_decode_init(const msa_dims* dims, int32_t length, const int8_t* k_idx, int8_t* block_keys,
+                    int32_t* open_sums, void* stream) {
+  Dims d;
+  int st = check_dims(dims, &d);
+  if (st != MSA_OK) return st;
+  if (!k_idx || !block_keys || !open_sums || length < 0 || length > d.S) return MSA_ERR_INVALID_ARG;
+  if (length == 0) return MSA_OK;  // the first append opens block 0 and ignores open_sums
+  hipStream_t s = (hipStream_t)stream;
+  MSA_LAUNCH_NAMED("pool", s, msa::launch_pool_strided(k_idx, block_keys, open_sums, (int)d.U, (int)length, d.S,
+                                                       (int)d.nb, (int)d.bs, s));
+  return MSA_OK;
+}
+
+int msa_decode_step(const msa_dims* dims, int32_t length, const uint16_t* q, const int8_t* q_idx,
+                    const uint16_t* k_new, const uint16_t* v_new, const int8_t* k_idx_new, uint16_t* k_cache,
+                    uint16_t* v_cache, int32_t* open_sums, int8_t* block_keys, uint16_t* out, int32_t* sel,
+                    void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  int st = check_dims(dims, &d);
+  if (st != MSA_OK) return st;
+  if (!q || !q_idx || !k_new || !v_new || !k_idx_new || !k_cache || !v_cache || !open_sums || !block_keys || !out)
+    return MSA_ERR_INVALID_ARG;
+  if (length < 1 || length > d.S) return MSA_ERR_INVALID_ARG;
   DecodeLayout L;
   st = decode_layout(d, &L);
   if (st != MSA_OK) return st;
   st = check_ws(ws, ws_bytes, L.total);
   if (st != MSA_OK) return st;
-  char* base = static_cast<char*>(ws);
-  msa::DecodeShape sh;
-  sh.B = (int)d.B;
-  sh.L = (int)d.S;
-  sh.Hq = (int)d.Hq;
-  sh.G = (int)d.G;
-  sh.r = (int)d.r;
-  sh.bs = (int)d.bs;
-  sh.nb = (int)d.nb;
-  sh.top_k = (int)d.k;
-  sh.scale_log2 = d.scale * 1.4426950408889634f;
-  int32_t* sel_use = sel ? sel : reinterpret_cast<int32_t*>(base + L.sel);
   hipStream_t s = (hipStream_t)stream;
-  float* state = reinterpret_cast<float*>(base + L.state);
-  const int n_split = decode_split(d);
-  MSA_LAUNCH_NAMED("decode", s,
-                   msa::launch_decode(sh, q, q_idx, k_cache, v_cache, block_keys, sel_use, out, state, n_split, s));
-  if (n_split > 1) MSA_LAUNCH_NAMED("decode_merge", s, msa::launch_decode_merge(sh, state, n_split, out, s));
-  return MSA_OK;
+  const msa::DecodeShape sh = decode_shape(d, length);
+  MSA_LAUNCH_NAMED("append", s, msa::launch_append(sh, k_new, v_new, k_idx_new, k_cache, v_cache, open_sums,
+                                                   block_keys, (int)length - 1, s));
+  return run_decode(d, length, q, q_idx, k_cache, v_cache, block_keys, out, sel, ws, ws_bytes, s);
 }
 
 int msa_profile_enable(int on) {

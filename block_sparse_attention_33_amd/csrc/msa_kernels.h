@@ -31,6 +31,11 @@ struct PassInfo {
 // Block summary keys: k_idx [U, S, 64] -> block_keys [U, nb, 64].
 hipError_t launch_pool(const int8_t* k_idx, int8_t* block_keys, int units, int S, int bs,
                        hipStream_t st);
+// The same over the first S tokens of rows s_stride apart, summaries
+// nb_stride apart; open_sums [U, 64] (optional) receives the int32 sums of
+// the block the next token goes to (zero when S is a multiple of bs).
+hipError_t launch_pool_strided(const int8_t* k_idx, int8_t* block_keys, int32_t* open_sums, int units, int S,
+                               long s_stride, int nb_stride, int bs, hipStream_t st);
 
 // Scores + per-(query, group) top-k -> sel [U, S, top_k].
 hipError_t launch_index_topk(const int8_t* q_idx, const int8_t* block_keys, int32_t* sel, int units,
@@ -81,7 +86,8 @@ hipError_t launch_merge(const PrefillShape& sh, const PassInfo& pass, const uint
 
 // Decode.
 struct DecodeShape {
-  int B, L, Hq, G, r, bs, nb, top_k;
+  int B, L, Hq, G, r, bs, nb, top_k;  // L tokens in the caches, nb = ceil(L / bs)
+  int Lc, nbc;                        // cache rows and summary rows per unit (capacity)
   float scale_log2;
 };
 constexpr int kDecodeMaxCandidates = 16 * 512;  // 512 threads x 16 candidates
@@ -93,6 +99,11 @@ constexpr int kDecodeMaxCandidates = 16 * 512;  // 512 threads x 16 candidates
 hipError_t launch_decode(const DecodeShape& sh, const uint16_t* q, const int8_t* q_idx, const uint16_t* k_cache,
                          const uint16_t* v_cache, const int8_t* block_keys, int32_t* sel_out, uint16_t* out,
                          float* state, int n_split, hipStream_t st);
+// Append of token pos of every unit: k_new/v_new [U, 128] -> cache row pos,
+// k_idx_new [U, 64] -> open_sums [U, 64] and block_keys[u][pos / bs].
+hipError_t launch_append(const DecodeShape& sh, const uint16_t* k_new, const uint16_t* v_new,
+                         const int8_t* k_idx_new, uint16_t* k_cache, uint16_t* v_cache, int32_t* open_sums,
+                         int8_t* block_keys, int pos, hipStream_t st);
 hipError_t launch_decode_merge(const DecodeShape& sh, const float* state, int n_split, uint16_t* out,
                                hipStream_t st);
 

@@ -140,6 +140,43 @@ int msa_decode(const msa_dims* dims, const uint16_t* q, const int8_t* q_idx,
                const uint16_t* k_cache, const uint16_t* v_cache, const int8_t* block_keys,
                uint16_t* out, int32_t* sel, void* ws, size_t ws_bytes, void* stream);
 
+/* Generation with caches that grow by one token per step.  The decode
+ * pages describe the KV cache holding past keys and values so that each new
+ * token attends to them (wiki.500nian.com digest of "MiniMax M3 Review: 1M
+ * Tokens, 15X Faster AI Agents", paragraph on the quadratic wall and the KV
+ * cache); these two calls keep that cache and its block summaries current.
+ *
+ * Here dims->seq_len is the capacity C of the caches: k_cache/v_cache
+ * [B, G, C, D] bf16, block_keys [B, G, ceil(C / block_size), di] int8 and
+ * open_sums [B, G, di] int32, all caller-owned device memory.  open_sums
+ * holds the exact integer sum of the index keys already in the block the
+ * next token goes to, so that block's summary can be refreshed at every
+ * step without re-reading its tokens; the summaries always equal
+ * msa_pool_block_keys over the tokens present (a partial last block divides
+ * by its own token count).
+ *
+ * msa_decode_init: for caches that already hold `length` tokens (0 <= length
+ * <= C), k_idx [B, G, C, di] int8 their index keys (rows >= length are not
+ * read) -> block_keys of blocks 0 .. ceil(length / block_size) - 1 and
+ * open_sums (zero when length is a multiple of block_size).  Needs no
+ * workspace; length 0 enqueues nothing.
+ *
+ * msa_decode_step: one token per sequence at position pos = length - 1
+ * (1 <= length <= C): k_new, v_new [B, G, D] bf16 go to cache row pos,
+ * k_idx_new [B, G, di] int8 updates open_sums (restarted when pos opens a
+ * block) and block_keys[pos / block_size]; then the query q [B, Hq, D] /
+ * q_idx [B, G, di] at pos is decoded over the `length` cached tokens exactly
+ * as msa_decode does for L = length -> out [B, Hq, D], sel [B, G, top_k]
+ * when non-NULL.  ws/ws_bytes: at least msa_workspace_bytes(MSA_OP_DECODE)
+ * at dims.  A step with length L must follow the state left by init or by
+ * the step with length L - 1; the call itself cannot check this. */
+int msa_decode_init(const msa_dims* dims, int32_t length, const int8_t* k_idx, int8_t* block_keys,
+                    int32_t* open_sums, void* stream);
+int msa_decode_step(const msa_dims* dims, int32_t length, const uint16_t* q, const int8_t* q_idx,
+                    const uint16_t* k_new, const uint16_t* v_new, const int8_t* k_idx_new,
+                    uint16_t* k_cache, uint16_t* v_cache, int32_t* open_sums, int8_t* block_keys,
+                    uint16_t* out, int32_t* sel, void* ws, size_t ws_bytes, void* stream);
+
 /* Optional per-kernel timing.  While enabled (on != 0), every kernel the
  * entry points enqueue is bracketed by two HIP events on the same stream and
  * recorded under its kernel name; disabled by default.  Returns MSA_OK, or

@@ -31,7 +31,8 @@ def _declared():
 def test_header_declares_the_boundary():
     names = _declared()
     for n in ["msa_index_select", "msa_prefill", "msa_decode", "msa_workspace_bytes",
-              "msa_pool_block_keys", "msa_status_string", "msa_version"]:
+              "msa_pool_block_keys", "msa_status_string", "msa_version", "msa_decode_init",
+              "msa_decode_step"]:
         assert n in names
 
 
@@ -46,7 +47,7 @@ def test_status_strings(lib):
                          (-3, "MSA_ERR_WORKSPACE"), (-4, "MSA_ERR_HIP")]:
         assert lib.msa_status_string(code).decode().startswith(prefix)
     assert lib.msa_status_string(12345).decode() == "unknown MSA status"
-    assert lib.msa_version() == 10000
+    assert lib.msa_version() == 10100
 
 
 def D(**kw):
@@ -94,6 +95,29 @@ def test_null_pointers(lib):
         args = [FAKE] * 6
         args[i] = None
         assert lib.msa_decode(ctypes.byref(dims), *args, None, FAKE, 1 << 40, None) == -1
+
+
+def test_decode_step_validation(lib):
+    """The generation calls reject bad lengths and null pointers before any
+    launch (dims.seq_len is the cache capacity)."""
+    dims = D(batch=2, seq_len=1000)
+    st, lo, _ = _ws(lib, _lib.MSA_OP_DECODE, dims)
+    assert st == 0
+    for length in (0, -1, 1001):
+        assert lib.msa_decode_step(ctypes.byref(dims), length, *([FAKE] * 10), None, FAKE, lo, None) == -1
+    for i in range(10):
+        args = [FAKE] * 10
+        args[i] = None
+        assert lib.msa_decode_step(ctypes.byref(dims), 10, *args, None, FAKE, lo, None) == -1
+    assert lib.msa_decode_step(ctypes.byref(dims), 10, *([FAKE] * 10), None, FAKE, lo - 1, None) == -3
+    assert lib.msa_decode_step(ctypes.byref(D(head_dim=64)), 10, *([FAKE] * 10), None, FAKE, lo, None) == -2
+    for length in (-1, 1001):
+        assert lib.msa_decode_init(ctypes.byref(dims), length, FAKE, FAKE, FAKE, None) == -1
+    for i in range(3):
+        args = [FAKE] * 3
+        args[i] = None
+        assert lib.msa_decode_init(ctypes.byref(dims), 10, *args, None) == -1
+    assert lib.msa_decode_init(ctypes.byref(dims), 0, FAKE, FAKE, FAKE, None) == 0  # nothing to enqueue
 
 
 def test_workspace_errors(lib):

@@ -265,6 +265,51 @@ def test_decode_full_workload():
     _free()
 
 
+@pytest.mark.parametrize("bs,top_k,L0,steps", [(32, 6, 150, 120), (64, 4, 64, 70)])
+def test_decode_generation_steps(bs, top_k, L0, steps):
+    """Generation over caches of capacity C: msa_decode_init on L0 cached
+    tokens, then one msa_decode_step per new token, crossing block
+    boundaries.  Every step's selection and output match the oracle's decode
+    over the cache prefix with summaries pooled from all index keys so far;
+    the summaries match that pooling after every step, and the appended
+    cache rows are the new tokens."""
+    w = get_workload("decode_b16_256k", n_q_heads=8, n_kv_heads=2, block_size=bs, top_k=top_k)
+    B, C = 2, L0 + steps + 37
+    _say(f"[decode generation] bs={bs} k={top_k} L0={L0} steps={steps} C={C}")
+    truth = decode_inputs(w, seed=71 + bs, device=DEV, seq_len=C, batch=B)
+    tk, tv, tki = truth["k_cache"], truth["v_cache"], truth["k_idx_cache"]
+    hk, hv, hki = host_f32(tk), host_f32(tv), host_i8(tki)
+    kc, vc = tk.clone(), tv.clone()
+    kc[:, :, L0:] = 0
+    vc[:, :, L0:] = 0
+    kidx = tki.clone()
+    kidx[:, :, L0:] = 99  # rows past the cached tokens must not be read
+    bk, osum = msa.msa_decode_init(kidx, L0, bs)
+    torch.cuda.synchronize()
+    nb0 = -(-L0 // bs)
+    assert np.array_equal(host_i8(bk)[:, :, :nb0], O.pool_block_keys(hki[:, :, :L0], bs))
+    j0 = L0 // bs
+    exp_sum = hki[:, :, j0 * bs:L0].astype(np.int64).sum(axis=2)
+    assert np.array_equal(host_i8(osum).astype(np.int64), exp_sum)
+    for i in range(steps):
+        L = L0 + i + 1
+        pos = L - 1
+        qs = decode_inputs(w, seed=5000 + i, device=DEV, seq_len=1, batch=B)
+        out, sel = msa.msa_decode_step(qs["q"], qs["q_idx"], tk[:, :, pos].contiguous(), tv[:, :, pos].contiguous(),
+                                       tki[:, :, pos].contiguous(), kc, vc, osum, bk, L, bs, top_k,
+                                       return_sel=True)
+        torch.cuda.synchronize()
+        summ = O.pool_block_keys(hki[:, :, :L], bs)
+        assert np.array_equal(host_i8(bk)[:, :, :-(-L // bs)], summ), f"summaries after step L={L}"
+        osel, oout = O.decode(host_f32(qs["q"]), host_i8(qs["q_idx"]), hk[:, :, :L], hv[:, :, :L], summ, bs,
+                              top_k)
+        assert np.array_equal(host_i8(sel).astype(np.int32), osel), f"selection at L={L}"
+        compare_out(out, oout, f"decode step L={L}")
+    Lend = L0 + steps
+    assert torch.equal(kc[:, :, :Lend], tk[:, :, :Lend]) and torch.equal(vc[:, :, :Lend], tv[:, :, :Lend])
+    assert int(kc[:, :, Lend:].abs().sum()) == 0
+
+
 def test_decode_matches_last_prefill_row():
     w = get_workload("prefill_32k")
     S = 5000
