@@ -19,7 +19,7 @@ from ._lib import MSA_OP_DECODE, MSA_OP_INDEX, MSA_OP_POOL, MSA_OP_PREFILL, MsaD
 
 __all__ = [
     "MsaError", "make_dims", "profile_enable", "profile_read", "msa_workspace_bytes", "msa_pool_block_keys", "msa_index_select",
-    "msa_prefill", "msa_decode", "msa_decode_init", "msa_decode_step", "MSA_OP_POOL", "MSA_OP_INDEX", "MSA_OP_PREFILL", "MSA_OP_DECODE",
+    "msa_prefill", "msa_prefill_chunk", "msa_decode", "msa_decode_init", "msa_decode_step", "MSA_OP_POOL", "MSA_OP_INDEX", "MSA_OP_PREFILL", "MSA_OP_DECODE",
 ]
 
 
@@ -85,8 +85,8 @@ def _need(t, name, dtype, ndim, device=None):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
-def _workspace(op, dims, device, workspace):
-    lo, hi = msa_workspace_bytes(op, dims)
+def _workspace(op, dims, device, workspace, sizes=None):
+    lo, hi = sizes if sizes is not None else msa_workspace_bytes(op, dims)
     if lo == 0:
         return None, 0
     if workspace is not None:
@@ -263,4 +263,46 @@ def msa_decode_step(q, q_idx, k_new, v_new, k_idx_new, k_cache, v_cache, open_su
                                        _ptr(v_new), _ptr(k_idx_new), _ptr(k_cache), _ptr(v_cache),
                                        _ptr(open_sums), _ptr(block_keys), _ptr(out), _ptr(sel), _ptr(ws),
                                        ws_bytes, _stream(dev)), "msa_decode_step")
+    return (out, sel) if return_sel else out
+
+
+def msa_prefill_chunk(q, q_idx, k_cache, v_cache, k_idx, block_keys, start: int, block_size: int, top_k: int,
+                      softmax_scale: float = 0.0, out=None, sel=None, return_sel: bool = False, workspace=None):
+    """Prefill of the count = q.shape[1] queries at positions start .. start +
+    count - 1 against caches of capacity C that already hold tokens 0 ..
+    start + count - 1: k_cache/v_cache [B, G, C, D] bf16, k_idx [B, G, C, di]
+    int8; block_keys [B, G, ceil(C/bs), di] int8 holds the summaries of the
+    blocks before start / bs and receives those of the chunk's blocks.
+    q [B, count, Hq, D], q_idx [B, G, count, di] -> out [B, count, Hq, D]."""
+    _need(q, "q", torch.bfloat16, 4)
+    dev = q.device
+    _need(q_idx, "q_idx", torch.int8, 4, dev)
+    _need(k_cache, "k_cache", torch.bfloat16, 4, dev)
+    _need(v_cache, "v_cache", torch.bfloat16, 4, dev)
+    _need(k_idx, "k_idx", torch.int8, 4, dev)
+    _need(block_keys, "block_keys", torch.int8, 4, dev)
+    B, T, Hq, D = q.shape
+    _, G, C, _ = k_cache.shape
+    di = q_idx.shape[3]
+    if k_cache.shape != (B, G, C, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache/v_cache must be [B, G, C, D]")
+    if q_idx.shape != (B, G, T, di) or k_idx.shape != (B, G, C, di):
+        raise ValueError("q_idx must be [B, G, count, di] and k_idx [B, G, C, di]")
+    if block_keys.shape != (B, G, -(-C // block_size), di):
+        raise ValueError("block_keys must be [B, G, ceil(C/bs), di]")
+    dims = make_dims(B, C, Hq, G, block_size, top_k, head_dim=D, idx_dim=di, softmax_scale=softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16, 4, dev)
+    if sel is None and return_sel:
+        sel = torch.empty((B, G, T, top_k), dtype=torch.int32, device=dev)
+    if sel is not None:
+        _need(sel, "sel", torch.int32, 4, dev)
+    lo, hi = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check(_lib.load().msa_prefill_chunk_workspace_bytes(ctypes.byref(dims), int(T), ctypes.byref(lo),
+                                                         ctypes.byref(hi)), "msa_prefill_chunk_workspace_bytes")
+    ws, ws_bytes = _workspace(MSA_OP_PREFILL, dims, dev, workspace, sizes=(lo.value, hi.value))
+    _check(_lib.load().msa_prefill_chunk(ctypes.byref(dims), int(start), int(T), _ptr(q), _ptr(q_idx),
+                                         _ptr(k_cache), _ptr(v_cache), _ptr(k_idx), _ptr(block_keys), _ptr(out),
+                                         _ptr(sel), _ptr(ws), ws_bytes, _stream(dev)), "msa_prefill_chunk")
     return (out, sel) if return_sel else out

@@ -47,6 +47,9 @@ SIGNATURES = {
     "msa_index_select": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "msa_prefill": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "msa_decode": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "msa_prefill_chunk_workspace_bytes": (ctypes.c_int, [_DIMS, ctypes.c_int32, _SIZE_P, _SIZE_P]),
+    "msa_prefill_chunk": (ctypes.c_int, [_DIMS, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                         ctypes.c_size_t, _P]),
     "msa_decode_init": (ctypes.c_int, [_DIMS, ctypes.c_int32, _P, _P, _P, _P]),
     "msa_decode_step": (ctypes.c_int, [_DIMS, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                        ctypes.c_size_t, _P]),

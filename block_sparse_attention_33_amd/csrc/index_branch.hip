@@ -18,7 +18,7 @@ namespace msa {
 namespace {
 
 // ---------------------------------------------------------------------------
-// Pooling: one wave per (unit, block) of the first S tokens.  Lane (row, col)
+// Pooling: one wave per (unit, block j0 .. nb - 1) of the first S tokens.  Lane (row, col)
 // = (lane / 16, lane % 16) sums dword `col` (4 index dims) of tokens row,
 // row + 4, ...; the four rows are folded with lane shuffles.  HBM-bound
 // streaming read.  k_idx rows of a unit are s_stride apart, summaries
@@ -29,12 +29,13 @@ namespace {
 __global__ __launch_bounds__(256) void pool_kernel(const int8_t* __restrict__ k_idx,
                                                    int8_t* __restrict__ block_keys, int units,
                                                    int S, int bs, int nb, long s_stride, int nb_stride,
-                                                   int32_t* __restrict__ open_sums) {
+                                                   int32_t* __restrict__ open_sums, int j0) {
   const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (wid >= units * nb) return;
+  const int nbp = nb - j0;  // blocks pooled per unit
+  if (wid >= units * nbp) return;
   const int lane = threadIdx.x & 63;
-  const int u = wid / nb;
-  const int j = wid - u * nb;
+  const int u = wid / nbp;
+  const int j = j0 + (wid - u * nbp);
   const int t0 = j * bs;
   const int n = min(bs, S - t0);
   const uint32_t* base = reinterpret_cast<const uint32_t*>(k_idx + ((size_t)u * s_stride + t0) * kIdxDim);
@@ -110,12 +111,13 @@ struct NextPow2 {
 // block order, so a candidate enters the list only when its score beats the
 // list's last score strictly: an equal score belongs to a lower index already
 // in the list.  KCAP >= top_k - 1; the best top_k - 1 are taken from it.
+// Query row t (of S per unit) is the token at position pos0 + t.
 // ---------------------------------------------------------------------------
 template <int KCAP>
 __global__ __launch_bounds__(256) void index_topk_kernel(const int8_t* __restrict__ q_idx,
                                                          const int8_t* __restrict__ block_keys,
                                                          int32_t* __restrict__ sel, int S,
-                                                         int nb, int bs_log2, int top_k) {
+                                                         int nb_stride, int bs_log2, int top_k, int pos0) {
   constexpr int CH = 256;  // summaries per LDS chunk (16 KiB)
   __shared__ i32x4_t sk[CH * 4];
 
@@ -124,8 +126,8 @@ __global__ __launch_bounds__(256) void index_topk_kernel(const int8_t* __restric
   const int t = t0 + (int)threadIdx.x;
   const bool live = t < S;
   const int tc = live ? t : S - 1;
-  const int c = tc >> bs_log2;  // own block = number of candidates
-  const int c_last = min(S - 1, t0 + 255) >> bs_log2;
+  const int c = (pos0 + tc) >> bs_log2;  // own block = number of candidates
+  const int c_last = (pos0 + min(S - 1, t0 + 255)) >> bs_log2;
   const int kp = top_k - 1;
 
   const i32x4_t* qp = reinterpret_cast<const i32x4_t*>(q_idx + ((size_t)u * S + tc) * kIdxDim);
@@ -138,7 +140,7 @@ __global__ __launch_bounds__(256) void index_topk_kernel(const int8_t* __restric
     Li[i] = -1;
   }
 
-  const i32x4_t* kb = reinterpret_cast<const i32x4_t*>(block_keys + (size_t)u * nb * kIdxDim);
+  const i32x4_t* kb = reinterpret_cast<const i32x4_t*>(block_keys + (size_t)u * nb_stride * kIdxDim);
   const int n_cand = kp > 0 ? c_last : 0;
   for (int base = 0; base < n_cand; base += CH) {
     const int n = min(CH, n_cand - base);
@@ -211,36 +213,45 @@ __global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* __restrict__ p, 
 hipError_t launch_pool(const int8_t* k_idx, int8_t* block_keys, int units, int S, int bs,
                        hipStream_t st) {
   const int nb = (S + bs - 1) / bs;
-  return launch_pool_strided(k_idx, block_keys, nullptr, units, S, S, nb, bs, st);
+  return launch_pool_strided(k_idx, block_keys, nullptr, units, S, S, nb, bs, 0, st);
 }
 
 hipError_t launch_pool_strided(const int8_t* k_idx, int8_t* block_keys, int32_t* open_sums, int units, int S,
-                               long s_stride, int nb_stride, int bs, hipStream_t st) {
+                               long s_stride, int nb_stride, int bs, int j0, hipStream_t st) {
   const int nb = (S + bs - 1) / bs;
-  const long waves = (long)units * nb;
+  const long waves = (long)units * (nb - j0);
+  if (waves <= 0) return hipSuccess;
   const unsigned grid = (unsigned)((waves + 3) / 4);
   hipLaunchKernelGGL(pool_kernel, dim3(grid), dim3(256), 0, st, k_idx, block_keys, units, S, bs, nb, s_stride,
-                     nb_stride, open_sums);
+                     nb_stride, open_sums, j0);
   return hipGetLastError();
 }
 
 hipError_t launch_index_topk(const int8_t* q_idx, const int8_t* block_keys, int32_t* sel, int units,
                              int S, int bs, int top_k, hipStream_t st) {
-  const int nb = (S + bs - 1) / bs;
+  return launch_index_topk_at(q_idx, block_keys, sel, units, S, 0, (S + bs - 1) / bs, bs, top_k, st);
+}
+
+hipError_t launch_index_topk_at(const int8_t* q_idx, const int8_t* block_keys, int32_t* sel, int units, int S,
+                                int q0, int nb_stride, int bs, int top_k, hipStream_t st) {
   int bs_log2 = 0;
   while ((1 << bs_log2) < bs) ++bs_log2;
   const dim3 grid((S + 255) / 256, units);
   const int kp = top_k - 1;
+#define MSA_TOPK_LAUNCH(KC)                                                                                   \
+  hipLaunchKernelGGL(index_topk_kernel<KC>, grid, dim3(256), 0, st, q_idx, block_keys, sel, S, nb_stride, bs_log2, \
+                     top_k, q0)
   if (kp <= 1)
-    hipLaunchKernelGGL(index_topk_kernel<1>, grid, dim3(256), 0, st, q_idx, block_keys, sel, S, nb, bs_log2, top_k);
+    MSA_TOPK_LAUNCH(1);
   else if (kp <= 3)
-    hipLaunchKernelGGL(index_topk_kernel<3>, grid, dim3(256), 0, st, q_idx, block_keys, sel, S, nb, bs_log2, top_k);
+    MSA_TOPK_LAUNCH(3);
   else if (kp <= 7)
-    hipLaunchKernelGGL(index_topk_kernel<7>, grid, dim3(256), 0, st, q_idx, block_keys, sel, S, nb, bs_log2, top_k);
+    MSA_TOPK_LAUNCH(7);
   else if (kp <= 15)
-    hipLaunchKernelGGL(index_topk_kernel<15>, grid, dim3(256), 0, st, q_idx, block_keys, sel, S, nb, bs_log2, top_k);
+    MSA_TOPK_LAUNCH(15);
   else
-    hipLaunchKernelGGL(index_topk_kernel<31>, grid, dim3(256), 0, st, q_idx, block_keys, sel, S, nb, bs_log2, top_k);
+    MSA_TOPK_LAUNCH(31);
+#undef MSA_TOPK_LAUNCH
   return hipGetLastError();
 }
 

@@ -29,7 +29,7 @@ __device__ __forceinline__ void chunk_tokens(const ChunkPlan& cp, int c, int S, 
 
 __global__ __launch_bounds__(256) void chunk_hist_kernel(const int32_t* __restrict__ sel,
                                                          int32_t* __restrict__ H, int S, int nb,
-                                                         int bs_log2, int top_k, ChunkPlan cp) {
+                                                         int bs_log2, int top_k, ChunkPlan cp, int q0) {
   extern __shared__ int32_t hist[];
   const int c = blockIdx.x;
   const int u = blockIdx.y;
@@ -40,7 +40,7 @@ __global__ __launch_bounds__(256) void chunk_hist_kernel(const int32_t* __restri
   chunk_tokens(cp, c, S, &t0, &t1);
   const int kp = top_k - 1;
   for (int t = t0 + (int)threadIdx.x; t < t1; t += 256) {
-    const int nv = min(kp, t >> bs_log2);  // slot nv holds the own block
+    const int nv = min(kp, (q0 + t) >> bs_log2);  // slot nv holds the own block
     const int32_t* srow = sel + ((size_t)u * S + t) * top_k;
     for (int s = 0; s <= nv; ++s) atomicAdd(&hist[srow[s]], 1);
   }
@@ -142,7 +142,7 @@ __global__ __launch_bounds__(256) void offsets_items_kernel(int32_t* __restrict_
 __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ sel,
                                                       const int32_t* __restrict__ H,
                                                       uint32_t* __restrict__ entries, int S, int nb,
-                                                      int bs_log2, int top_k, ChunkPlan cp) {
+                                                      int bs_log2, int top_k, ChunkPlan cp, int q0) {
   extern __shared__ int32_t cursor[];
   const int c = blockIdx.x;
   const int u = blockIdx.y;
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
   chunk_tokens(cp, c, S, &t0, &t1);
   const int kp = top_k - 1;
   for (int t = t0 + (int)threadIdx.x; t < t1; t += 256) {
-    const int nv = min(kp, t >> bs_log2);  // slot nv holds the own block
+    const int nv = min(kp, (q0 + t) >> bs_log2);  // slot nv holds the own block
     const int32_t* srow = sel + ((size_t)u * S + t) * top_k;
     for (int s = 0; s <= nv; ++s) {
       const int pos = atomicAdd(&cursor[srow[s]], 1);
@@ -165,7 +165,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
 }  // namespace
 
 hipError_t launch_chunk_hist(const int32_t* sel, int32_t* H, int units, int S, int nb, int bs, int top_k,
-                             const ChunkPlan& cp, hipStream_t st) {
+                             const ChunkPlan& cp, int q0, hipStream_t st) {
   int bs_log2 = 0;
   while ((1 << bs_log2) < bs) ++bs_log2;
   const size_t lds = (size_t)nb * 4;
@@ -174,7 +174,7 @@ hipError_t launch_chunk_hist(const int32_t* sel, int32_t* H, int units, int S, i
                                                      kMaxInvertBlocks * 4);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(chunk_hist_kernel, dim3(cp.n_chunks, units), dim3(256), lds, st, sel, H, S, nb, bs_log2,
-                     top_k, cp);
+                     top_k, cp, q0);
   return hipGetLastError();
 }
 
@@ -200,7 +200,7 @@ hipError_t launch_offsets_items(int32_t* H, const int32_t* row_ptr, const int32_
 }
 
 hipError_t launch_scatter(const int32_t* sel, const int32_t* H, uint32_t* entries, int units, int S, int nb,
-                          int bs, int top_k, const ChunkPlan& cp, hipStream_t st) {
+                          int bs, int top_k, const ChunkPlan& cp, int q0, hipStream_t st) {
   int bs_log2 = 0;
   while ((1 << bs_log2) < bs) ++bs_log2;
   const size_t lds = (size_t)nb * 4;
@@ -209,7 +209,7 @@ hipError_t launch_scatter(const int32_t* sel, const int32_t* H, uint32_t* entrie
                                                      kMaxInvertBlocks * 4);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(scatter_kernel, dim3(cp.n_chunks, units), dim3(256), lds, st, sel, H, entries, S, nb, bs_log2,
-                     top_k, cp);
+                     top_k, cp, q0);
   return hipGetLastError();
 }
 

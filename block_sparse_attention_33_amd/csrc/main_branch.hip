@@ -279,8 +279,8 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(
     }
   };
   auto kv_src = [&](const ItemDesc& d, size_t* off) -> int {
-    *off = ((size_t)d.u * sh.S + (size_t)d.j * BS) * kHeadDim;
-    return min(BS, sh.S - d.j * BS);
+    *off = ((size_t)d.u * sh.kv_rows + (size_t)d.j * BS) * kHeadDim;
+    return min(BS, sh.q0 + sh.S - d.j * BS);
   };
 
   // ---- prologue: entries of the first two items, the first block, the
@@ -378,7 +378,7 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(
       size_t pidx[2];
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) pidx[ct] = ((row0 + tok[ct]) * K + slot[ct]) * sh.r + head[ct];
-      const bool own[2] = {(tok[0] >> sh.bs_log2) == cur.j, (tok[1] >> sh.bs_log2) == cur.j};
+      const bool own[2] = {((sh.q0 + tok[0]) >> sh.bs_log2) == cur.j, ((sh.q0 + tok[1]) >> sh.bs_log2) == cur.j};
       if (!__any(own[0] || own[1])) {
         // ---- no query of this chunk owns the block: plain softmax
         float m2[2], sum[2];
@@ -438,7 +438,7 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(
           // keys 0 .. tok - key0 are not after the query; the lane-half
           // term of the key index moves to the right-hand side so that
           // every compare is against a constant
-          const int lim = tok[ct] - key0 - 4 * hf;
+          const int lim = sh.q0 + tok[ct] - key0 - 4 * hf;
 #pragma unroll
           for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
@@ -487,7 +487,7 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(
           // a row with no other partial (own block 0, or top_k = 1) stores
           // o / l with a sum of 1: the merge then reproduces it exactly, so
           // the row is rounded to bf16 once, as every other row
-          const bool single = (tok[ct] >> sh.bs_log2) == 0 || K == 1;
+          const bool single = ((sh.q0 + tok[ct]) >> sh.bs_log2) == 0 || K == 1;
           u32x4_t pv1[8];
           pack_tile(o, single ? 1.0f / l : 1.0f, pv1);
           store_row(pv1, make_float2(m2, single ? 1.0f : l), pidx[ct], hf, part_o, part_ml);
@@ -527,7 +527,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const uint16_t* __restrict__
   const int b = u / sh.G;
   const int g = u - b * sh.G;
   const int K = sh.top_k;
-  const int n = min(K - 1, t >> sh.bs_log2) + 1;
+  const int n = min(K - 1, (sh.q0 + t) >> sh.bs_log2) + 1;
   const size_t base = ((size_t)(u - pass.u0) * pass.pass_tokens + (t - pass.t0)) * K;
 
   float m[32], l[32];

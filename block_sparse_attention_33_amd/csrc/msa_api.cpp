@@ -268,6 +268,121 @@ int run_decode(const Dims& d, long length, const uint16_t* q, const int8_t* q_id
   return MSA_OK;
 }
 
+// Dims of the query side of a prefill: n_q query rows per unit; nb stays
+// the block count of dc (all CSR rows a query of the sequence can reach).
+Dims chunk_dims(const Dims& dc, long n_q) {
+  Dims d = dc;
+  d.S = n_q;
+  return d;
+}
+
+// Prefill of the queries at positions q0 .. q0 + n_q - 1 of sequences whose
+// keys, values and index keys are rows 0 .. q0 + n_q - 1 of k, v and k_idx
+// (dc.S rows per unit; q0 = 0 and n_q = dc.S for a whole prefill).  q,
+// q_idx, out and sel hold the n_q query rows.  ext_keys: the caller's block
+// summaries (dc.nb rows per unit; blocks before q0 / bs already pooled), or
+// null to pool every block into the workspace.
+int run_prefill(const Dims& dc, long q0, long n_q, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                const int8_t* q_idx, const int8_t* k_idx, int8_t* ext_keys, uint16_t* out, int32_t* sel, void* ws,
+                size_t ws_bytes, hipStream_t s) {
+  const Dims d = chunk_dims(dc, n_q);
+  const PrefillPlan P = plan_prefill(d);
+  int st;
+  const PrefillLayout one = prefill_layout(d, P, 1);
+  st = check_ws(ws, ws_bytes, one.total);
+  if (st != MSA_OK) return st;
+  // unranged: as many (batch, group) units per pass as the workspace holds
+  long upp = 1;
+  if (!P.ranged) {
+    const size_t per_unit = prefill_layout(d, P, 2).total - one.total;
+    upp = per_unit > 0 ? std::min<long>(d.U, 1 + (long)((ws_bytes - one.total) / per_unit)) : d.U;
+  }
+  PrefillLayout L = prefill_layout(d, P, upp);
+  while (L.total > ws_bytes && upp > 1) L = prefill_layout(d, P, --upp);
+
+  char* base = static_cast<char*>(ws);
+  int8_t* bkeys = reinterpret_cast<int8_t*>(base + L.block_keys);
+  int32_t* sel_use = sel ? sel : reinterpret_cast<int32_t*>(base + L.sel);
+  int32_t* counts = reinterpret_cast<int32_t*>(base + L.counts);
+  int32_t* hist = reinterpret_cast<int32_t*>(base + L.hist);
+  int32_t* row_ptr = reinterpret_cast<int32_t*>(base + L.row_ptr);
+  int32_t* item_ptr = reinterpret_cast<int32_t*>(base + L.item_ptr);
+  uint32_t* entries = reinterpret_cast<uint32_t*>(base + L.entries);
+  int2* items = reinterpret_cast<int2*>(base + L.items);
+  uint16_t* part_o = reinterpret_cast<uint16_t*>(base + L.part_o);
+  float2* part_ml = reinterpret_cast<float2*>(base + L.part_ml);
+
+  const int U = (int)d.U, S = (int)d.S, bs = (int)d.bs, nb = (int)d.nb, K = (int)d.k;
+  msa::ChunkPlan cp;
+  cp.T = (int)P.T;
+  cp.m = (int)P.m;
+  cp.tpc = (int)P.tpc;
+  cp.n_chunks = (int)P.n_chunks;
+  cp.n_ranges = (int)P.n_ranges;
+  const int tpi = (int)P.tokens_per_item;
+  const int iq0 = (int)q0;
+  if (ext_keys != nullptr) {
+    // the blocks the new tokens fall in; earlier ones are the caller's
+    bkeys = ext_keys;
+    MSA_LAUNCH_NAMED("pool", s, msa::launch_pool_strided(k_idx, bkeys, nullptr, U, (int)(q0 + n_q), dc.S, nb, bs,
+                                                         (int)(q0 / bs), s));
+  } else {
+    MSA_LAUNCH_NAMED("pool", s, msa::launch_pool(k_idx, bkeys, U, S, bs, s));
+  }
+  MSA_LAUNCH_NAMED("index_topk", s, msa::launch_index_topk_at(q_idx, bkeys, sel_use, U, S, iq0, nb, bs, K, s));
+  MSA_LAUNCH_NAMED("chunk_hist", s, msa::launch_chunk_hist(sel_use, hist, U, S, nb, bs, K, cp, iq0, s));
+  MSA_LAUNCH_NAMED("chunk_total", s, msa::launch_chunk_total(hist, counts, U, nb, cp, s));
+  MSA_LAUNCH_NAMED("scan", s, msa::launch_scan(counts, row_ptr, item_ptr, (int)P.rows, tpi, s));
+  MSA_LAUNCH_NAMED("offsets_items", s, msa::launch_offsets_items(hist, row_ptr, item_ptr, items, U, nb, cp, tpi, s));
+  MSA_LAUNCH_NAMED("scatter", s, msa::launch_scatter(sel_use, hist, entries, U, S, nb, bs, K, cp, iq0, s));
+  msa::PrefillShape sh;
+  sh.B = (int)d.B;
+  sh.S = S;
+  sh.Hq = (int)d.Hq;
+  sh.G = (int)d.G;
+  sh.r = (int)d.r;
+  sh.bs = bs;
+  sh.bs_log2 = bs_log2_of(bs);
+  sh.nb = nb;
+  sh.top_k = K;
+  sh.n_ranges = (int)P.n_ranges;
+  sh.range_tokens = (int)P.T;
+  sh.scale_log2 = d.scale * 1.4426950408889634f;
+  sh.q0 = iq0;
+  sh.kv_rows = (int)dc.S;
+  const int pass_tokens = (int)std::min(P.T, d.S);
+  auto run_pass = [&](long u0, long u1, long rng) -> int {
+    msa::PassInfo ps;
+    ps.u0 = (int)u0;
+    ps.u1 = (int)u1;
+    ps.rng = (int)rng;
+    ps.t0 = (int)(rng * P.T);
+    ps.t1 = (int)std::min<long>(d.S, (rng + 1) * P.T);
+    ps.pass_tokens = pass_tokens;
+    ps.row_begin = (int)((u0 * P.n_ranges + rng) * nb);
+    ps.row_end = (int)(((u1 - 1) * P.n_ranges + rng + 1) * nb);
+    const long max_items = (u1 - u0) * P.max_items_per_range;
+    MSA_LAUNCH_NAMED("attend", s, msa::launch_attend(sh, ps, q, k, v, row_ptr, item_ptr, items, entries, part_o,
+                                                     part_ml, (int)max_items, s));
+    MSA_LAUNCH_NAMED("merge", s, msa::launch_merge(sh, ps, part_o, part_ml, out, s));
+    return MSA_OK;
+  };
+  if (P.ranged) {
+    for (long u = 0; u < d.U; ++u)
+      for (long rng = 0; rng < P.n_ranges; ++rng) {
+        st = run_pass(u, u + 1, rng);
+        if (st != MSA_OK) return st;
+      }
+  } else {
+    for (long u0 = 0; u0 < d.U; u0 += upp) {
+      st = run_pass(u0, std::min<long>(d.U, u0 + upp), 0);
+      if (st != MSA_OK) return st;
+    }
+  }
+  return MSA_OK;
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -354,92 +469,36 @@ int msa_prefill(const msa_dims* dims, const uint16_t* q, const uint16_t* k, cons
   if (st != MSA_OK) return st;
   if (!q || !k || !v || !q_idx || !k_idx || !out) return MSA_ERR_INVALID_ARG;
   if (d.nb > msa::kMaxInvertBlocks) return MSA_ERR_UNSUPPORTED;
-  const PrefillPlan P = plan_prefill(d);
-  const PrefillLayout one = prefill_layout(d, P, 1);
-  st = check_ws(ws, ws_bytes, one.total);
+  return run_prefill(d, 0, d.S, q, k, v, q_idx, k_idx, nullptr, out, sel, ws, ws_bytes, (hipStream_t)stream);
+}
+
+int msa_prefill_chunk_workspace_bytes(const msa_dims* dims, int32_t count, size_t* min_bytes, size_t* full_bytes) {
+  Dims d;
+  int st = check_dims(dims, &d);
   if (st != MSA_OK) return st;
-  // unranged: as many (batch, group) units per pass as the workspace holds
-  long upp = 1;
-  if (!P.ranged) {
-    const size_t per_unit = prefill_layout(d, P, 2).total - one.total;
-    upp = per_unit > 0 ? std::min<long>(d.U, 1 + (long)((ws_bytes - one.total) / per_unit)) : d.U;
-  }
-  PrefillLayout L = prefill_layout(d, P, upp);
-  while (L.total > ws_bytes && upp > 1) L = prefill_layout(d, P, --upp);
-
-  char* base = static_cast<char*>(ws);
-  int8_t* bkeys = reinterpret_cast<int8_t*>(base + L.block_keys);
-  int32_t* sel_use = sel ? sel : reinterpret_cast<int32_t*>(base + L.sel);
-  int32_t* counts = reinterpret_cast<int32_t*>(base + L.counts);
-  int32_t* hist = reinterpret_cast<int32_t*>(base + L.hist);
-  int32_t* row_ptr = reinterpret_cast<int32_t*>(base + L.row_ptr);
-  int32_t* item_ptr = reinterpret_cast<int32_t*>(base + L.item_ptr);
-  uint32_t* entries = reinterpret_cast<uint32_t*>(base + L.entries);
-  int2* items = reinterpret_cast<int2*>(base + L.items);
-  uint16_t* part_o = reinterpret_cast<uint16_t*>(base + L.part_o);
-  float2* part_ml = reinterpret_cast<float2*>(base + L.part_ml);
-
-  hipStream_t s = (hipStream_t)stream;
-  const int U = (int)d.U, S = (int)d.S, bs = (int)d.bs, nb = (int)d.nb, K = (int)d.k;
-  msa::ChunkPlan cp;
-  cp.T = (int)P.T;
-  cp.m = (int)P.m;
-  cp.tpc = (int)P.tpc;
-  cp.n_chunks = (int)P.n_chunks;
-  cp.n_ranges = (int)P.n_ranges;
-  const int tpi = (int)P.tokens_per_item;
-  MSA_LAUNCH_NAMED("pool", s, msa::launch_pool(k_idx, bkeys, U, S, bs, s));
-  MSA_LAUNCH_NAMED("index_topk", s, msa::launch_index_topk(q_idx, bkeys, sel_use, U, S, bs, K, s));
-  MSA_LAUNCH_NAMED("chunk_hist", s, msa::launch_chunk_hist(sel_use, hist, U, S, nb, bs, K, cp, s));
-  MSA_LAUNCH_NAMED("chunk_total", s, msa::launch_chunk_total(hist, counts, U, nb, cp, s));
-  MSA_LAUNCH_NAMED("scan", s, msa::launch_scan(counts, row_ptr, item_ptr, (int)P.rows, tpi, s));
-  MSA_LAUNCH_NAMED("offsets_items", s, msa::launch_offsets_items(hist, row_ptr, item_ptr, items, U, nb, cp, tpi, s));
-  MSA_LAUNCH_NAMED("scatter", s, msa::launch_scatter(sel_use, hist, entries, U, S, nb, bs, K, cp, s));
-  msa::PrefillShape sh;
-  sh.B = (int)d.B;
-  sh.S = S;
-  sh.Hq = (int)d.Hq;
-  sh.G = (int)d.G;
-  sh.r = (int)d.r;
-  sh.bs = bs;
-  sh.bs_log2 = bs_log2_of(bs);
-  sh.nb = nb;
-  sh.top_k = K;
-  sh.n_ranges = (int)P.n_ranges;
-  sh.range_tokens = (int)P.T;
-  sh.scale_log2 = d.scale * 1.4426950408889634f;
-  const int pass_tokens = (int)std::min(P.T, d.S);
-  auto run_pass = [&](long u0, long u1, long rng) -> int {
-    msa::PassInfo ps;
-    ps.u0 = (int)u0;
-    ps.u1 = (int)u1;
-    ps.rng = (int)rng;
-    ps.t0 = (int)(rng * P.T);
-    ps.t1 = (int)std::min<long>(d.S, (rng + 1) * P.T);
-    ps.pass_tokens = pass_tokens;
-    ps.row_begin = (int)((u0 * P.n_ranges + rng) * nb);
-    ps.row_end = (int)(((u1 - 1) * P.n_ranges + rng + 1) * nb);
-    const long max_items = (u1 - u0) * P.max_items_per_range;
-    MSA_LAUNCH_NAMED("attend", s, msa::launch_attend(sh, ps, q, k, v, row_ptr, item_ptr, items, entries, part_o,
-                                                     part_ml, (int)max_items, s));
-    MSA_LAUNCH_NAMED("merge", s, msa::launch_merge(sh, ps, part_o, part_ml, out, s));
-    return MSA_OK;
-  };
-  if (P.ranged) {
-    for (long u = 0; u < d.U; ++u)
-      for (long rng = 0; rng < P.n_ranges; ++rng) {
-        st = run_pass(u, u + 1, rng);
-        if (st != MSA_OK) return st;
-      }
-  } else {
-    for (long u0 = 0; u0 < d.U; u0 += upp) {
-      st = run_pass(u0, std::min<long>(d.U, u0 + upp), 0);
-      if (st != MSA_OK) return st;
-    }
-  }
+  if (count < 1 || count > d.S) return MSA_ERR_INVALID_ARG;
+  if (d.nb > msa::kMaxInvertBlocks) return MSA_ERR_UNSUPPORTED;
+  const Dims dq = chunk_dims(d, count);
+  const PrefillPlan p = plan_prefill(dq);
+  const size_t lo = prefill_layout(dq, p, 1).total;
+  const size_t hi = p.ranged ? lo : prefill_layout(dq, p, dq.U).total;
+  if (min_bytes) *min_bytes = lo;
+  if (full_bytes) *full_bytes = hi;
   return MSA_OK;
 }
 
+int msa_prefill_chunk(const msa_dims* dims, int32_t start, int32_t count, const uint16_t* q, const int8_t* q_idx,
+                      const uint16_t* k_cache, const uint16_t* v_cache, const int8_t* k_idx, int8_t* block_keys,
+                      uint16_t* out, int32_t* sel, void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  int st = check_dims(dims, &d);
+  if (st != MSA_OK) return st;
+  if (!q || !q_idx || !k_cache || !v_cache || !k_idx || !block_keys || !out) return MSA_ERR_INVALID_ARG;
+  if (start < 0 || count < 1 || (long)start + count > d.S) return MSA_ERR_INVALID_ARG;
+  if (d.nb > msa::kMaxInvertBlocks) return MSA_ERR_UNSUPPORTED;
+  return run_prefill(d, start, count, q, k_cache, v_cache, q_idx, k_idx, block_keys, out, sel, ws, ws_bytes,
+                     (hipStream_t)stream);
+}
 
 int msa_decode(const msa_dims* dims, const uint16_t* q, const int8_t* q_idx, const uint16_t* k_cache,
                const uint16_t* v_cache, const int8_t* block_keys, uint16_t* out, int32_t* sel, void* ws,
@@ -460,7 +519,7 @@ int msa_decode_init(const msa_dims* dims, int32_t length, const int8_t* k_idx, i
   if (length == 0) return MSA_OK;  // the first append opens block 0 and ignores open_sums
   hipStream_t s = (hipStream_t)stream;
   MSA_LAUNCH_NAMED("pool", s, msa::launch_pool_strided(k_idx, block_keys, open_sums, (int)d.U, (int)length, d.S,
-                                                       (int)d.nb, (int)d.bs, s));
+                                                       (int)d.nb, (int)d.bs, 0, s));
   return MSA_OK;
 }
 

@@ -14,7 +14,9 @@ namespace msa {
 constexpr int kItemRows = 256;
 
 struct PrefillShape {
-  int B, S, Hq, G, r, bs, bs_log2, nb, top_k;
+  int B, S, Hq, G, r, bs, bs_log2, nb, top_k;  // S: query rows per unit, nb: CSR blocks per unit
+  int q0;            // position of query row 0 (queries are tokens q0 .. q0 + S - 1)
+  int kv_rows;       // K/V rows per unit (stride); keys present: q0 + S
   int n_ranges;      // query ranges per unit: CSR rows are (unit, range, block)
   int range_tokens;  // tokens per query range
   float scale_log2;  // softmax scale * log2(e)
@@ -32,14 +34,19 @@ struct PassInfo {
 hipError_t launch_pool(const int8_t* k_idx, int8_t* block_keys, int units, int S, int bs,
                        hipStream_t st);
 // The same over the first S tokens of rows s_stride apart, summaries
-// nb_stride apart; open_sums [U, 64] (optional) receives the int32 sums of
-// the block the next token goes to (zero when S is a multiple of bs).
+// nb_stride apart, blocks j0 .. ceil(S / bs) - 1 only; open_sums [U, 64]
+// (optional) receives the int32 sums of the block the next token goes to
+// (zero when S is a multiple of bs).
 hipError_t launch_pool_strided(const int8_t* k_idx, int8_t* block_keys, int32_t* open_sums, int units, int S,
-                               long s_stride, int nb_stride, int bs, hipStream_t st);
+                               long s_stride, int nb_stride, int bs, int j0, hipStream_t st);
 
 // Scores + per-(query, group) top-k -> sel [U, S, top_k].
 hipError_t launch_index_topk(const int8_t* q_idx, const int8_t* block_keys, int32_t* sel, int units,
                              int S, int bs, int top_k, hipStream_t st);
+// The same for queries at positions q0 .. q0 + S - 1 (rows 0 .. S - 1 of
+// q_idx and sel), summaries nb_stride rows apart per unit.
+hipError_t launch_index_topk_at(const int8_t* q_idx, const int8_t* block_keys, int32_t* sel, int units, int S,
+                                int q0, int nb_stride, int bs, int top_k, hipStream_t st);
 
 hipError_t launch_fill_i32(int32_t* p, int32_t value, size_t n, hipStream_t st);
 
@@ -58,8 +65,9 @@ constexpr int kMaxInvertBlocks = 36864;  // nb limit: LDS histogram of nb int32
 struct ChunkPlan {
   int T, m, tpc, n_chunks, n_ranges;
 };
+// (query rows are tokens q0 .. q0 + S - 1)
 hipError_t launch_chunk_hist(const int32_t* sel, int32_t* H, int units, int S, int nb, int bs, int top_k,
-                             const ChunkPlan& cp, hipStream_t st);
+                             const ChunkPlan& cp, int q0, hipStream_t st);
 hipError_t launch_chunk_total(const int32_t* H, int32_t* counts, int units, int nb, const ChunkPlan& cp,
                               hipStream_t st);
 hipError_t launch_scan(const int32_t* counts, int32_t* row_ptr, int32_t* item_ptr, int n,
@@ -67,7 +75,7 @@ hipError_t launch_scan(const int32_t* counts, int32_t* row_ptr, int32_t* item_pt
 hipError_t launch_offsets_items(int32_t* H, const int32_t* row_ptr, const int32_t* item_ptr, int2* items,
                                 int units, int nb, const ChunkPlan& cp, int tokens_per_item, hipStream_t st);
 hipError_t launch_scatter(const int32_t* sel, const int32_t* H, uint32_t* entries, int units, int S, int nb,
-                          int bs, int top_k, const ChunkPlan& cp, hipStream_t st);
+                          int bs, int top_k, const ChunkPlan& cp, int q0, hipStream_t st);
 
 // Main branch: one work item = one KV block of a (unit, range) row and up to
 // 4 chunks of kItemRows gathered query rows (the query's own block

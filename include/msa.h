@@ -130,6 +130,28 @@ int msa_prefill(const msa_dims* dims, const uint16_t* q, const uint16_t* k, cons
                 const int8_t* q_idx, const int8_t* k_idx, uint16_t* out, int32_t* sel, void* ws,
                 size_t ws_bytes, void* stream);
 
+/* Chunked prefill against a cache.  Here dims->seq_len is the capacity C
+ * of the caches: k_cache/v_cache [B, G, C, D] bf16 and k_idx [B, G, C, di]
+ * int8 already hold the tokens 0 .. start + count - 1 (the caller writes
+ * the chunk's rows before the call); block_keys [B, G, ceil(C/block_size),
+ * di] int8 holds the summaries of the blocks before start / block_size
+ * (from earlier chunks or msa_decode_init) and receives those of the
+ * blocks the chunk's tokens fall in.  The count queries at positions
+ * start .. start + count - 1, q [B, count, Hq, D] bf16 and q_idx [B, G,
+ * count, di] int8, give out [B, count, Hq, D] bf16 and sel [B, G, count,
+ * top_k] int32 when non-NULL: the rows msa_prefill gives for those
+ * positions of the whole sequence (the pages use MSA for 1M-token prompts,
+ * which a chunked prefill bounds in memory: "深度解析 MiniMax-M3：
+ * 稀疏注意力机制、基准测试与 API 集成指南", section "技术细节").
+ * 0 <= start, 1 <= count, start + count <= C.  ws/ws_bytes: at least the
+ * minimum of msa_prefill_chunk_workspace_bytes(dims, count). */
+int msa_prefill_chunk_workspace_bytes(const msa_dims* dims, int32_t count, size_t* min_bytes,
+                                      size_t* full_bytes);
+int msa_prefill_chunk(const msa_dims* dims, int32_t start, int32_t count, const uint16_t* q,
+                      const int8_t* q_idx, const uint16_t* k_cache, const uint16_t* v_cache,
+                      const int8_t* k_idx, int8_t* block_keys, uint16_t* out, int32_t* sel, void* ws,
+                      size_t ws_bytes, void* stream);
+
 /* One decode step per sequence: the query at position L - 1 of each of the B
  * caches.  q [B, Hq, D] bf16, q_idx [B, G, di] int8, k_cache, v_cache
  * [B, G, L, D] bf16, block_keys [B, G, nb, di] int8 (summaries of the cache's

@@ -32,7 +32,7 @@ def test_header_declares_the_boundary():
     names = _declared()
     for n in ["msa_index_select", "msa_prefill", "msa_decode", "msa_workspace_bytes",
               "msa_pool_block_keys", "msa_status_string", "msa_version", "msa_decode_init",
-              "msa_decode_step"]:
+              "msa_decode_step", "msa_prefill_chunk", "msa_prefill_chunk_workspace_bytes"]:
         assert n in names
 
 
@@ -118,6 +118,30 @@ def test_decode_step_validation(lib):
         args[i] = None
         assert lib.msa_decode_init(ctypes.byref(dims), 10, *args, None) == -1
     assert lib.msa_decode_init(ctypes.byref(dims), 0, FAKE, FAKE, FAKE, None) == 0  # nothing to enqueue
+
+
+def test_prefill_chunk_validation(lib):
+    """Chunked prefill: start/count must lie inside the capacity; null
+    pointers and short workspaces are rejected before any launch."""
+    dims = D(batch=1, seq_len=4096)
+    lo, hi = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert lib.msa_prefill_chunk_workspace_bytes(ctypes.byref(dims), 1024, ctypes.byref(lo), ctypes.byref(hi)) == 0
+    assert 0 < lo.value <= hi.value
+    for count in (0, -3, 4097):
+        assert lib.msa_prefill_chunk_workspace_bytes(ctypes.byref(dims), count, None, None) == -1
+    # the workspace of a chunk grows with the chunk, not with the capacity's tokens
+    lo2 = ctypes.c_size_t(0)
+    assert lib.msa_prefill_chunk_workspace_bytes(ctypes.byref(dims), 2048, ctypes.byref(lo2), None) == 0
+    assert lo2.value > lo.value
+    for start, count in ((-1, 10), (0, 0), (4000, 97), (4096, 1)):
+        assert lib.msa_prefill_chunk(ctypes.byref(dims), start, count, *([FAKE] * 7), None, FAKE, hi.value,
+                                     None) == -1
+    for i in range(7):
+        args = [FAKE] * 7
+        args[i] = None
+        assert lib.msa_prefill_chunk(ctypes.byref(dims), 0, 1024, *args, None, FAKE, hi.value, None) == -1
+    assert lib.msa_prefill_chunk(ctypes.byref(dims), 0, 1024, *([FAKE] * 7), None, FAKE, lo.value - 1,
+                                 None) == -3
 
 
 def test_workspace_errors(lib):

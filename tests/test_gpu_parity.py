@@ -227,6 +227,71 @@ def test_prefill_1m_sampled():
     _full_prefill_case("prefill_1m", 96, seed=41, ws_cap_gb=70)
 
 
+# ------------------------------------------------------------------ chunked prefill
+
+def _chunked(inp, bs, k, bounds, C):
+    """Run msa_prefill_chunk over the chunks [bounds[i], bounds[i + 1]) of
+    a sequence held in caches of capacity C; returns (out, sel) of all rows."""
+    B, S, Hq, D = inp["q"].shape
+    G = inp["k"].shape[1]
+    kc = torch.zeros((B, G, C, D), dtype=torch.bfloat16, device=DEV)
+    vc = torch.zeros_like(kc)
+    kic = torch.full((B, G, C, inp["k_idx"].shape[3]), 77, dtype=torch.int8, device=DEV)
+    bk = torch.zeros((B, G, -(-C // bs), inp["k_idx"].shape[3]), dtype=torch.int8, device=DEV)
+    outs, sels = [], []
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        # the chunk's keys, values and index keys enter the caches first
+        kc[:, :, a:b] = inp["k"][:, :, a:b]
+        vc[:, :, a:b] = inp["v"][:, :, a:b]
+        kic[:, :, a:b] = inp["k_idx"][:, :, a:b]
+        o, sl = msa.msa_prefill_chunk(inp["q"][:, a:b].contiguous(), inp["q_idx"][:, :, a:b].contiguous(), kc, vc,
+                                      kic, bk, a, bs, k, return_sel=True)
+        outs.append(o)
+        sels.append(sl)
+    torch.cuda.synchronize()
+    return torch.cat(outs, dim=1), torch.cat(sels, dim=2)
+
+
+CHUNKED = [
+    # name, workload overrides, S, chunk bounds, capacity
+    ("ragged_gqa4", dict(n_q_heads=8, n_kv_heads=2, block_size=64, top_k=5), 1000, [0, 300, 301, 700, 1000], 1100),
+    ("bs128_r8", dict(n_q_heads=16, n_kv_heads=2, block_size=128, top_k=6), 2048, [0, 512, 1024, 1536, 2048], 2048),
+    ("bs32_k32", dict(n_q_heads=4, n_kv_heads=2, block_size=32, top_k=32), 1500, [0, 40, 1023, 1500], 1600),
+]
+
+
+@pytest.mark.parametrize("name,over,S,bounds,C", CHUNKED, ids=[c[0] for c in CHUNKED])
+def test_prefill_chunked_all_rows(name, over, S, bounds, C):
+    """A sequence prefilled in chunks against the cache gives, row by row,
+    the whole prefill's selection and output (bit for bit), which match the
+    oracle."""
+    w = get_workload("tiny_2k", **over)
+    _say(f"[prefill chunked] {name} S={S} chunks={bounds} C={C}")
+    inp = prefill_inputs(w, seed=23, device="cpu", seq_len=S)
+    dinp = {kk: vv.to(DEV) for kk, vv in inp.items()}
+    cout, csel = _chunked(dinp, w.block_size, w.top_k, bounds, C)
+    out, sel = _run_prefill(dinp, w.block_size, w.top_k)
+    assert torch.equal(csel, sel), f"{name}: chunked selection differs from the whole prefill"
+    assert torch.equal(cout, out), f"{name}: chunked output differs from the whole prefill"
+    summ, osel, oout = oracle_prefill_rows(inp, w, np.arange(S))
+    assert np.array_equal(host_i8(csel).astype(np.int32), osel)
+    compare_out(cout, oout, name)
+
+
+def test_prefill_chunked_32k_equals_whole():
+    """The 32K workload in four chunks of 8192 queries: bit-identical to the
+    whole prefill."""
+    w = get_workload("prefill_32k")
+    _say("[prefill chunked] 32K in 4 chunks")
+    inp = prefill_inputs(w, seed=29, device=DEV)
+    out, sel = _run_prefill(inp, w.block_size, w.top_k)
+    cout, csel = _chunked(inp, w.block_size, w.top_k, [0, 8192, 16384, 24576, 32768], w.seq_len)
+    assert torch.equal(csel, sel)
+    assert torch.equal(cout, out)
+    del inp, out, sel, cout, csel
+    _free()
+
+
 # ------------------------------------------------------------------ decode
 
 def _decode_case(w, L, B, seed, n_check_units=None):
