@@ -117,7 +117,8 @@ template <int KCAP>
 __global__ __launch_bounds__(256) void index_topk_kernel(const int8_t* __restrict__ q_idx,
                                                          const int8_t* __restrict__ block_keys,
                                                          int32_t* __restrict__ sel, int S,
-                                                         int nb_stride, int bs_log2, int top_k, int pos0) {
+                                                         int nb_stride, int bs_log2, int top_k, int pos0,
+                                                         int q_stride, int sel_stride) {
   constexpr int CH = 256;  // summaries per LDS chunk (16 KiB)
   __shared__ i32x4_t sk[CH * 4];
 
@@ -130,7 +131,7 @@ __global__ __launch_bounds__(256) void index_topk_kernel(const int8_t* __restric
   const int c_last = (pos0 + min(S - 1, t0 + 255)) >> bs_log2;
   const int kp = top_k - 1;
 
-  const i32x4_t* qp = reinterpret_cast<const i32x4_t*>(q_idx + ((size_t)u * S + tc) * kIdxDim);
+  const i32x4_t* qp = reinterpret_cast<const i32x4_t*>(q_idx + ((size_t)u * q_stride + tc) * kIdxDim);
   const i32x4_t q0 = qp[0], q1 = qp[1], q2 = qp[2], q3 = qp[3];
 
   int Ls[KCAP], Li[KCAP];
@@ -193,7 +194,7 @@ __global__ __launch_bounds__(256) void index_topk_kernel(const int8_t* __restric
   for (int i = 0; i < NP; ++i) x[i] = (i < KCAP && i < n_valid) ? Li[i < KCAP ? i : 0] : INT_MAX;
   bitonic_sort<NP>(x);
   if (!live) return;
-  int32_t* out = sel + ((size_t)u * S + t) * top_k;
+  int32_t* out = sel + ((size_t)u * sel_stride + t) * top_k;
 #pragma unroll
   for (int i = 0; i <= KCAP; ++i) {
     if (i < top_k) {
@@ -229,18 +230,19 @@ hipError_t launch_pool_strided(const int8_t* k_idx, int8_t* block_keys, int32_t*
 
 hipError_t launch_index_topk(const int8_t* q_idx, const int8_t* block_keys, int32_t* sel, int units,
                              int S, int bs, int top_k, hipStream_t st) {
-  return launch_index_topk_at(q_idx, block_keys, sel, units, S, 0, (S + bs - 1) / bs, bs, top_k, st);
+  return launch_index_topk_at(q_idx, block_keys, sel, units, S, 0, S, S, (S + bs - 1) / bs, bs, top_k, st);
 }
 
 hipError_t launch_index_topk_at(const int8_t* q_idx, const int8_t* block_keys, int32_t* sel, int units, int S,
-                                int q0, int nb_stride, int bs, int top_k, hipStream_t st) {
+                                int q0, int q_stride, int sel_stride, int nb_stride, int bs, int top_k,
+                                hipStream_t st) {
   int bs_log2 = 0;
   while ((1 << bs_log2) < bs) ++bs_log2;
   const dim3 grid((S + 255) / 256, units);
   const int kp = top_k - 1;
 #define MSA_TOPK_LAUNCH(KC)                                                                                   \
   hipLaunchKernelGGL(index_topk_kernel<KC>, grid, dim3(256), 0, st, q_idx, block_keys, sel, S, nb_stride, bs_log2, \
-                     top_k, q0)
+                     top_k, q0, q_stride, sel_stride)
   if (kp <= 1)
     MSA_TOPK_LAUNCH(1);
   else if (kp <= 3)

@@ -41,7 +41,7 @@ __global__ __launch_bounds__(256) void chunk_hist_kernel(const int32_t* __restri
   const int kp = top_k - 1;
   for (int t = t0 + (int)threadIdx.x; t < t1; t += 256) {
     const int nv = min(kp, (q0 + t) >> bs_log2);  // slot nv holds the own block
-    const int32_t* srow = sel + ((size_t)u * S + t) * top_k;
+    const int32_t* srow = sel + ((size_t)u * cp.q_stride + t) * top_k;
     for (int s = 0; s <= nv; ++s) atomicAdd(&hist[srow[s]], 1);
   }
   __syncthreads();
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
   const int kp = top_k - 1;
   for (int t = t0 + (int)threadIdx.x; t < t1; t += 256) {
     const int nv = min(kp, (q0 + t) >> bs_log2);  // slot nv holds the own block
-    const int32_t* srow = sel + ((size_t)u * S + t) * top_k;
+    const int32_t* srow = sel + ((size_t)u * cp.q_stride + t) * top_k;
     for (int s = 0; s <= nv; ++s) {
       const int pos = atomicAdd(&cursor[srow[s]], 1);
       entries[pos] = ((uint32_t)t << 5) | (uint32_t)s;

@@ -251,7 +251,7 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(
   auto n_chunks_of = [&](const ItemDesc& d) -> int { return (d.n_ent + tpc - 1) / tpc; };
   auto q_base = [&](int u) -> const uint16_t* {
     const int b = u / sh.G;
-    return q + ((size_t)b * sh.S * sh.Hq + (u - b * sh.G) * sh.r) * kHeadDim;
+    return q + ((size_t)b * sh.q_stride * sh.Hq + (u - b * sh.G) * sh.r) * kHeadDim;
   };
   // this wave's entries of item d: ring position jj = c * epw + i holds
   // the entry of token c * tpc + (64 w >> r_log2) + i (clamped to the item)
@@ -567,7 +567,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const uint16_t* __restrict__
   const int p0 = 8 * c16;
   const int hfp = p0 >> 6, dt = (p0 >> 4) & 3, i0 = p0 & 15;
   const int d0 = 32 * dt + 8 * (i0 >> 2) + 4 * hfp;
-  uint16_t* orow = out + (((size_t)b * sh.S + t) * sh.Hq + g * sh.r + h) * kHeadDim;
+  uint16_t* orow = out + (((size_t)b * sh.q_stride + t) * sh.Hq + g * sh.r + h) * kHeadDim;
   u32x2_t w0, w1;
   w0.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
   w0.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);

@@ -16,6 +16,7 @@ constexpr int kItemRows = 256;
 struct PrefillShape {
   int B, S, Hq, G, r, bs, bs_log2, nb, top_k;  // S: query rows per unit, nb: CSR blocks per unit
   int q0;            // position of query row 0 (queries are tokens q0 .. q0 + S - 1)
+  int q_stride;      // rows per unit (batch) of q and out: S, or more for a slice of longer tensors
   int kv_rows;       // K/V rows per unit (stride); keys present: q0 + S
   int n_ranges;      // query ranges per unit: CSR rows are (unit, range, block)
   int range_tokens;  // tokens per query range
@@ -44,9 +45,11 @@ hipError_t launch_pool_strided(const int8_t* k_idx, int8_t* block_keys, int32_t*
 hipError_t launch_index_topk(const int8_t* q_idx, const int8_t* block_keys, int32_t* sel, int units,
                              int S, int bs, int top_k, hipStream_t st);
 // The same for queries at positions q0 .. q0 + S - 1 (rows 0 .. S - 1 of
-// q_idx and sel), summaries nb_stride rows apart per unit.
+// q_idx and sel, q_stride and sel_stride rows apart per unit), summaries
+// nb_stride rows apart per unit.
 hipError_t launch_index_topk_at(const int8_t* q_idx, const int8_t* block_keys, int32_t* sel, int units, int S,
-                                int q0, int nb_stride, int bs, int top_k, hipStream_t st);
+                                int q0, int q_stride, int sel_stride, int nb_stride, int bs, int top_k,
+                                hipStream_t st);
 
 hipError_t launch_fill_i32(int32_t* p, int32_t value, size_t n, hipStream_t st);
 
@@ -64,6 +67,7 @@ hipError_t launch_fill_i32(int32_t* p, int32_t value, size_t n, hipStream_t st);
 constexpr int kMaxInvertBlocks = 36864;  // nb limit: LDS histogram of nb int32
 struct ChunkPlan {
   int T, m, tpc, n_chunks, n_ranges;
+  int q_stride;  // rows per unit of sel
 };
 // (query rows are tokens q0 .. q0 + S - 1)
 hipError_t launch_chunk_hist(const int32_t* sel, int32_t* H, int units, int S, int nb, int bs, int top_k,

@@ -166,6 +166,7 @@ def _a(x):
 
 
 USE_QUERY_RANGES = False   # the library's current choice (one pass over all units)
+QUERY_CHUNK = 16384        # a longer prefill runs in query chunks of this many tokens
 
 
 def _plan(U, S, nb, r, k):
@@ -194,12 +195,15 @@ def _plan(U, S, nb, r, k):
     (1, 65536, 8, 1, 128, 1, False)])
 def test_prefill_workspace_layout(lib, B, S, Hq, G, bs, k, ranged):
     """The documented layout: fixed part + one bf16 partial (r x 128) and one
-    fp32 (max, sum) pair (r) per (token, kept block) of a pass."""
+    fp32 (max, sum) pair (r) per (token, kept block) of a pass; the
+    token-sized parts cover one query chunk, the block-sized parts the whole
+    sequence."""
     dims = D(batch=B, seq_len=S, n_q_heads=Hq, n_kv_heads=G, block_size=bs, top_k=k)
     st, lo, hi = _ws(lib, _lib.MSA_OP_PREFILL, dims)
     assert st == 0
     U, r = B * G, Hq // G
     nb = -(-S // bs)
+    S = min(S, QUERY_CHUNK)
     tpi = 4 * 256 // r          # up to 4 chunks of 256 query rows per work item
     T, is_ranged, n_ranges, n_chunks = _plan(U, S, nb, r, k)
     assert is_ranged == ranged
