@@ -24,6 +24,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+D_HEAD = 128
 CPU_SAMPLE_ROWS = 6144      # oracle rows timed on the host (about 15-20 s, one thread)
 
 
@@ -365,6 +366,36 @@ def main():
     ch_ms = sorted(a.elapsed_time(b) for a, b in cev)[2]
     del cq, cqi, couts, cws
 
+    # short sequence, top_k covering every block (4096 tokens, top_k 32 =
+    # nb): msa_prefill takes the dense causal kernel; the chunked entry point
+    # runs the sparse path on the same data
+    ws_ = get_workload("prefill_32k", top_k=32)
+    Ss = 4096
+    sin = prefill_inputs(ws_, seed=1, device=dev, seq_len=Ss)
+    sout = torch.empty_like(sin["q"])
+    skeys = torch.empty((1, ws_.n_kv_heads, Ss // ws_.block_size, 64), dtype=torch.int8, device=dev)
+    sdims = msa.make_dims(1, Ss, ws_.n_q_heads, ws_.n_kv_heads, ws_.block_size, ws_.top_k)
+    sws = torch.empty(_chunk_ws_bytes(msa, sdims, Ss), dtype=torch.uint8, device=dev)
+    short_runs = {
+        "dense": lambda: msa.msa_prefill(sin["q"], sin["k"], sin["v"], sin["q_idx"], sin["k_idx"], ws_.block_size,
+                                         ws_.top_k, out=sout),
+        "sparse_path": lambda: msa.msa_prefill_chunk(sin["q"], sin["q_idx"], sin["k"], sin["v"], sin["k_idx"], skeys,
+                                                     0, ws_.block_size, ws_.top_k, out=sout, workspace=sws),
+    }
+    short_ms = {}
+    for name_, fn in short_runs.items():
+        fn()
+        torch.cuda.synchronize()
+        sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+        for a, b in sev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        short_ms[name_] = sorted(a.elapsed_time(b) for a, b in sev)[2]
+    short_flop = 4.0 * D_HEAD * ws_.n_q_heads * Ss * (Ss + 1) / 2
+    del sin, sout, sws
+
     # the plain decode timed the same way (back to back, so the kept blocks
     # may still sit in the memory-side cache, unlike in the step above where
     # a prefill runs in between)
@@ -434,6 +465,13 @@ def main():
             "ms": round(ch_ms, 4),
             "tokens_per_s": round(tokens / (ch_ms * 1e-3), 1),
             "tflops_alg": round(flop_alg / (ch_ms * 1e-3) / 1e12, 2),
+        },
+        "prefill_short_dense": {
+            "what": "4096 tokens, top_k 32 = every block: dense causal kernel vs the sparse path on the same data",
+            "dense_ms": round(short_ms["dense"], 4),
+            "sparse_path_ms": round(short_ms["sparse_path"], 4),
+            "dense_tflops": round(short_flop / (short_ms["dense"] * 1e-3) / 1e12, 2),
+            "dense_frac_bf16_peak": round(short_flop / (short_ms["dense"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         },
         "decode_step": {
             "what": "append one token per sequence (K/V rows, running index-key sum, block summary) + decode",

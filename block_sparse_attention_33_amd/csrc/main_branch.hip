@@ -605,6 +605,169 @@ hipError_t launch_attend_bs(const PrefillShape& sh, const PassInfo& pass, const 
   return hipGetLastError();
 }
 
+
+// ---------------------------------------------------------------------------
+// Dense causal attention, for a prefill whose top_k covers every block (the
+// selection then keeps all earlier blocks and the own block, and MSA is
+// plain causal GQA attention): one workgroup per tile of 256 query rows
+// (256 / r tokens x the r heads of a group) of one unit, the longest tiles
+// first.  The KV blocks 0 .. (last token of the tile) / BS stream through two
+// LDS buffers (the next block's loads in flight while one is computed); per
+// block S^T = K Q^T, an online softmax in base 2 and O^T += V^T P^T, with
+// the causal mask and the two-term P (hi + lo in bf16) on the blocks that
+// hold a tile token, as in the sparse kernel.  O is written once, no
+// partials.
+// ---------------------------------------------------------------------------
+template <int BS>
+__global__ __launch_bounds__(256, 1) void dense_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                       const uint16_t* __restrict__ v, uint16_t* __restrict__ out,
+                                                       PrefillShape sh, int r_log2) {
+  constexpr int KT = Tile<BS>::KT;
+  extern __shared__ __align__(16) char lds[];  // two K/V buffers
+  const int tpt = kItemRows >> r_log2;          // tokens per tile
+  const int n_tiles = (sh.S + tpt - 1) / tpt;
+  const int tile = n_tiles - 1 - (int)blockIdx.x;
+  const int u = blockIdx.y;
+  const int b = u / sh.G;
+  const int g = u - b * sh.G;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int hf = lane >> 5;
+  const float c2 = sh.scale_log2;
+  const int t0 = tile * tpt;
+  const int last_tok = min(sh.S, t0 + tpt) - 1;
+  const int j_last = last_tok >> sh.bs_log2;
+  const int j_mask = t0 >> sh.bs_log2;  // blocks from here on hold keys after some tile token
+
+  int tok[2], head[2];
+  u32x4_t qf[2][8];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const int qr = 64 * w + 32 * ct + (lane & 31);
+    tok[ct] = t0 + (qr >> r_log2);
+    head[ct] = qr & (sh.r - 1);
+    const int tc = min(tok[ct], sh.S - 1);
+    load_q_frag(q + (((size_t)b * sh.q_stride + tc) * sh.Hq + g * sh.r + head[ct]) * kHeadDim, hf, qf[ct]);
+  }
+  float m[2] = {-__builtin_inff(), -__builtin_inff()};
+  float l[2] = {0.f, 0.f};
+  f32x16_t o[2][4];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) o[ct][dt] = f32x16_t{};
+
+  auto kv_off = [&](int j) -> size_t { return ((size_t)u * sh.kv_rows + (size_t)j * BS) * kHeadDim; };
+  auto kv_keys = [&](int j) -> int { return min(BS, sh.S - j * BS); };
+  KvStage<BS, 256> kv;
+  load_kv_regs<BS, 256>(k + kv_off(0), v + kv_off(0), kv_keys(0), kv);
+  store_kv_lds<BS, 256>(kv, kv_keys(0), lds);
+  __syncthreads();
+
+  for (int j = 0; j <= j_last; ++j) {
+    const bool more = j < j_last;
+    if (more) load_kv_regs<BS, 256>(k + kv_off(j + 1), v + kv_off(j + 1), kv_keys(j + 1), kv);
+    int kvo = (j & 1) * Tile<BS>::kLdsBytes;
+    __asm__ volatile("" : "+v"(kvo));
+    const bool masked = j >= j_mask;
+    const float lo_on = masked ? 1.0f : 0.0f;
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      // S^T = K Q^T of this column tile (K is read again for the second
+      // tile: both at once would need 64 more registers)
+      int ko = kvo;
+      __asm__ volatile("" : "+v"(ko));
+      const char* kvl = lds + ko;
+      f32x16_t s[KT];
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        s[kt] = f32x16_t{};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) s[kt] = mfma32x32x16(k_frag(kvl, kt, ks, lane), qf[ct][ks], s[kt]);
+      }
+      if (masked) {
+        const int lim = tok[ct] - j * BS - 4 * hf;
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (32 * kt + c_row(i, 0) > lim) s[kt][i] = -__builtin_inff();
+      }
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
+      // finite from block 0 on: key 0 is visible to every token
+      const float m_new = fmaxf(m[ct], wave_max_pair(mx) * c2);
+      const float alpha = fast_exp2(m[ct] - m_new);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[ct][dt][i] *= alpha;
+      int vo = kvo;
+      __asm__ volatile("" : "+v"(vo));
+      const char* kvt = lds + vo;
+      float sum = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          uint32_t dh[4], dl[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float p0 = fast_exp2(fmaf(s[kt][8 * h2 + 2 * e], c2, -m_new));
+            const float p1 = fast_exp2(fmaf(s[kt][8 * h2 + 2 * e + 1], c2, -m_new));
+            sum += p0 + p1;
+            dh[e] = pack_bf16x2(p0, p1);
+            dl[e] = pack_bf16x2((p0 - bf16_lo(dh[e])) * lo_on, (p1 - bf16_hi(dh[e])) * lo_on);
+          }
+          const u32x4_t ph = u32x4_t{dh[0], dh[1], dh[2], dh[3]};
+          const u32x4_t pl = u32x4_t{dl[0], dl[1], dl[2], dl[3]};
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) {
+            const u32x4_t a = vt_frag<BS>(kvt, dt, kt, h2, lane);
+            o[ct][dt] = mfma32x32x16(a, ph, o[ct][dt]);
+            if (masked) o[ct][dt] = mfma32x32x16(a, pl, o[ct][dt]);
+          }
+        }
+      l[ct] = fmaf(l[ct], alpha, wave_sum_pair(sum));
+      m[ct] = m_new;
+    }
+    // the next block into the other buffer (released by the barrier that
+    // ended block j - 1), its loads having had this block's work to arrive
+    if (more) store_kv_lds<BS, 256>(kv, kv_keys(j + 1), lds + ((j + 1) & 1) * Tile<BS>::kLdsBytes);
+    __syncthreads();
+  }
+
+  // O = o / l, head dims 32 dt + 8 q4 + 4 hf + 0..3 of this lane's row
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    if (tok[ct] >= sh.S) continue;
+    const float inv = 1.0f / l[ct];
+    uint16_t* orow = out + (((size_t)b * sh.q_stride + tok[ct]) * sh.Hq + g * sh.r + head[ct]) * kHeadDim;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        u32x2_t wv;
+        wv.x = pack_bf16x2(o[ct][dt][4 * q4 + 0] * inv, o[ct][dt][4 * q4 + 1] * inv);
+        wv.y = pack_bf16x2(o[ct][dt][4 * q4 + 2] * inv, o[ct][dt][4 * q4 + 3] * inv);
+        *reinterpret_cast<u32x2_t*>(orow + 32 * dt + 8 * q4 + 4 * hf) = wv;
+      }
+  }
+}
+
+// sel of a dense prefill: every block up to the own one, ascending, then -1.
+__global__ __launch_bounds__(256) void dense_sel_kernel(int32_t* __restrict__ sel, int units, int S, int bs_log2,
+                                                        int top_k) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long)units * S * top_k) return;
+  const int s = (int)(i % top_k);
+  const int t = (int)((i / top_k) % S);
+  sel[i] = s <= (t >> bs_log2) ? s : -1;
+}
+
 }  // namespace
 
 hipError_t launch_attend(const PrefillShape& sh, const PassInfo& pass, const uint16_t* q, const uint16_t* k,
@@ -632,6 +795,39 @@ hipError_t launch_merge(const PrefillShape& sh, const PassInfo& pass, const uint
   const long threads = (long)(pass.t1 - t_first) * sh.r * 16;
   hipLaunchKernelGGL(merge_kernel, dim3((unsigned)((threads + 255) / 256), pass.u1 - pass.u0), dim3(256), 0, st,
                      part_o, part_ml, out, sh, pass, t_first, r_log2);
+  return hipGetLastError();
+}
+
+
+hipError_t launch_dense(const PrefillShape& sh, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                        uint16_t* out, int32_t* sel, hipStream_t st) {
+  int r_log2 = 0;
+  while ((1 << r_log2) < sh.r) ++r_log2;
+  const int tpt = kItemRows >> r_log2;
+  const dim3 grid((unsigned)((sh.S + tpt - 1) / tpt), (unsigned)(sh.B * sh.G));
+  switch (sh.bs) {
+#define MSA_DENSE_LAUNCH(BS_)                                                                                 \
+  {                                                                                                           \
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&dense_kernel<BS_>),     \
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize,           \
+                                                       2 * Tile<BS_>::kLdsBytes);                             \
+    if (attr != hipSuccess) return attr;                                                                      \
+    hipLaunchKernelGGL(dense_kernel<BS_>, grid, dim3(256), 2 * Tile<BS_>::kLdsBytes, st, q, k, v, out, sh, r_log2); \
+    break;                                                                                                    \
+  }
+    case 32:
+      MSA_DENSE_LAUNCH(32)
+    case 64:
+      MSA_DENSE_LAUNCH(64)
+    default:
+      MSA_DENSE_LAUNCH(128)
+#undef MSA_DENSE_LAUNCH
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || sel == nullptr) return e;
+  const long n = (long)sh.B * sh.G * sh.S * sh.top_k;
+  hipLaunchKernelGGL(dense_sel_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, sel, sh.B * sh.G, sh.S,
+                     sh.bs_log2, sh.top_k);
   return hipGetLastError();
 }
 

@@ -25,6 +25,8 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool pow2_in(int x, int lo, int hi) { return x >= lo && x <= hi && (x & (x - 1)) == 0; }
 
+constexpr long kMaxSparseTopK = 32;  // selection slots of the sparse paths (5 bits in a CSR entry)
+
 struct Dims {
   long B, S, Hq, G, r, D, di, bs, nb, k, kp, U;
   float scale;
@@ -41,7 +43,10 @@ int check_dims(const msa_dims* d, Dims* o) {
   const int r = d->n_q_heads / d->n_kv_heads;
   if (d->head_dim != 128 || d->idx_dim != 64) return MSA_ERR_UNSUPPORTED;
   if (d->block_size != 32 && d->block_size != 64 && d->block_size != 128) return MSA_ERR_UNSUPPORTED;
-  if (d->top_k > 32) return MSA_ERR_UNSUPPORTED;
+  // more than 32 kept blocks only where they are all the blocks (a dense
+  // prefill); the sparse paths keep at most 32 (checked by each of them)
+  if (d->top_k > kMaxSparseTopK && d->top_k < ((long)d->seq_len + d->block_size - 1) / d->block_size)
+    return MSA_ERR_UNSUPPORTED;
   if (!pow2_in(r, 1, 16)) return MSA_ERR_UNSUPPORTED;
   if (d->seq_len >= (1 << 26)) return MSA_ERR_UNSUPPORTED;
   const long units = (long)d->batch * d->n_kv_heads;
@@ -427,10 +432,13 @@ int msa_workspace_bytes(int op, const msa_dims* dims, size_t* min_bytes, size_t*
   size_t lo = 0, hi = 0;
   switch (op) {
     case MSA_OP_POOL:
+      break;
     case MSA_OP_INDEX:
+      if (d.k > kMaxSparseTopK) return MSA_ERR_UNSUPPORTED;
       break;
     case MSA_OP_PREFILL: {
       if (d.nb > msa::kMaxInvertBlocks) return MSA_ERR_UNSUPPORTED;
+      if (d.k >= d.nb) break;  // dense causal attention needs no workspace
       const Dims dq = chunk_dims(d, std::min(d.S, prefill_query_chunk(d)));
       const PrefillPlan p = plan_prefill(dq);
       lo = prefill_layout(dq, p, 1).total;
@@ -438,6 +446,7 @@ int msa_workspace_bytes(int op, const msa_dims* dims, size_t* min_bytes, size_t*
       break;
     }
     case MSA_OP_DECODE: {
+      if (d.k > kMaxSparseTopK) return MSA_ERR_UNSUPPORTED;
       DecodeLayout L;
       st = decode_layout(d, &L);
       if (st != MSA_OK) return st;
@@ -469,6 +478,7 @@ int msa_index_select(const msa_dims* dims, const int8_t* q_idx, const int8_t* k_
   Dims d;
   int st = check_dims(dims, &d);
   if (st != MSA_OK) return st;
+  if (d.k > kMaxSparseTopK) return MSA_ERR_UNSUPPORTED;
   if (q_idx == nullptr || k_idx == nullptr || block_keys == nullptr || sel == nullptr) return MSA_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
   MSA_LAUNCH_NAMED("pool", s, msa::launch_pool(k_idx, block_keys, (int)d.U, (int)d.S, (int)d.bs, s));
@@ -485,6 +495,26 @@ int msa_prefill(const msa_dims* dims, const uint16_t* q, const uint16_t* k, cons
   if (!q || !k || !v || !q_idx || !k_idx || !out) return MSA_ERR_INVALID_ARG;
   if (d.nb > msa::kMaxInvertBlocks) return MSA_ERR_UNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
+  if (d.k >= d.nb) {
+    // top_k covers every block: each query keeps all earlier blocks and its
+    // own, which is plain causal attention (no index branch, no partials)
+    msa::PrefillShape sh{};
+    sh.B = (int)d.B;
+    sh.S = (int)d.S;
+    sh.Hq = (int)d.Hq;
+    sh.G = (int)d.G;
+    sh.r = (int)d.r;
+    sh.bs = (int)d.bs;
+    sh.bs_log2 = bs_log2_of(d.bs);
+    sh.nb = (int)d.nb;
+    sh.top_k = (int)d.k;
+    sh.q0 = 0;
+    sh.q_stride = (int)d.S;
+    sh.kv_rows = (int)d.S;
+    sh.scale_log2 = d.scale * 1.4426950408889634f;
+    MSA_LAUNCH_NAMED("dense", s, msa::launch_dense(sh, q, k, v, out, sel, s));
+    return MSA_OK;
+  }
   const long T = prefill_query_chunk(d);
   if (T >= d.S) return run_prefill(d, 0, d.S, d.S, q, k, v, q_idx, k_idx, nullptr, out, sel, ws, ws_bytes, s);
   // query chunks of T tokens; the summaries persist in the workspace's first
@@ -503,6 +533,7 @@ int msa_prefill_chunk_workspace_bytes(const msa_dims* dims, int32_t count, size_
   Dims d;
   int st = check_dims(dims, &d);
   if (st != MSA_OK) return st;
+  if (d.k > kMaxSparseTopK) return MSA_ERR_UNSUPPORTED;
   if (count < 1 || count > d.S) return MSA_ERR_INVALID_ARG;
   if (d.nb > msa::kMaxInvertBlocks) return MSA_ERR_UNSUPPORTED;
   const Dims dq = chunk_dims(d, count);
@@ -520,6 +551,7 @@ int msa_prefill_chunk(const msa_dims* dims, int32_t start, int32_t count, const 
   Dims d;
   int st = check_dims(dims, &d);
   if (st != MSA_OK) return st;
+  if (d.k > kMaxSparseTopK) return MSA_ERR_UNSUPPORTED;
   if (!q || !q_idx || !k_cache || !v_cache || !k_idx || !block_keys || !out) return MSA_ERR_INVALID_ARG;
   if (start < 0 || count < 1 || (long)start + count > d.S) return MSA_ERR_INVALID_ARG;
   if (d.nb > msa::kMaxInvertBlocks) return MSA_ERR_UNSUPPORTED;
@@ -533,6 +565,7 @@ int msa_decode(const msa_dims* dims, const uint16_t* q, const int8_t* q_idx, con
   Dims d;
   int st = check_dims(dims, &d);
   if (st != MSA_OK) return st;
+  if (d.k > kMaxSparseTopK) return MSA_ERR_UNSUPPORTED;
   if (!q || !q_idx || !k_cache || !v_cache || !block_keys || !out) return MSA_ERR_INVALID_ARG;
   return run_decode(d, d.S, q, q_idx, k_cache, v_cache, block_keys, out, sel, ws, ws_bytes, (hipStream_t)stream);
 }
@@ -542,6 +575,7 @@ int msa_decode_init(const msa_dims* dims, int32_t length, const int8_t* k_idx, i
   Dims d;
   int st = check_dims(dims, &d);
   if (st != MSA_OK) return st;
+  if (d.k > kMaxSparseTopK) return MSA_ERR_UNSUPPORTED;
   if (!k_idx || !block_keys || !open_sums || length < 0 || length > d.S) return MSA_ERR_INVALID_ARG;
   if (length == 0) return MSA_OK;  // the first append opens block 0 and ignores open_sums
   hipStream_t s = (hipStream_t)stream;
@@ -557,6 +591,7 @@ int msa_decode_step(const msa_dims* dims, int32_t length, const uint16_t* q, con
   Dims d;
   int st = check_dims(dims, &d);
   if (st != MSA_OK) return st;
+  if (d.k > kMaxSparseTopK) return MSA_ERR_UNSUPPORTED;
   if (!q || !q_idx || !k_new || !v_new || !k_idx_new || !k_cache || !v_cache || !open_sums || !block_keys || !out)
     return MSA_ERR_INVALID_ARG;
   if (length < 1 || length > d.S) return MSA_ERR_INVALID_ARG;

@@ -52,9 +52,17 @@
  * crosses the ABI.
  *
  * Limits: head_dim 128, idx_dim 64, block_size 32, 64 or 128, 1 <= top_k <=
- * 32, n_q_heads = r * n_kv_heads with r in {1, 2, 4, 8, 16}, S < 2^26 and
- * B * G * S * top_k < 2^31; prefill needs nb <= 36864 and decode
- * nb <= 8193.  Anything else returns MSA_ERR_UNSUPPORTED.
+ * 32 (msa_prefill also takes any top_k >= nb), n_q_heads = r * n_kv_heads
+ * with r in {1, 2, 4, 8, 16}, S < 2^26 and B * G * S * top_k < 2^31; prefill
+ * needs nb <= 36864 and decode nb <= 8193.  Anything else returns
+ * MSA_ERR_UNSUPPORTED.
+ *
+ * When top_k >= nb every query keeps all earlier blocks and its own, so
+ * msa_prefill computes plain causal GQA attention with a dense kernel (no
+ * index branch, no partials, no workspace); one page names short sequences
+ * as the case where the selection does not pay and standard attention is
+ * used instead (devpress.csdn.net article on MiniMax M3, section "M3的技术局限
+ * 与改进方向", first limitation).
  */
 #ifndef MSA_H
 #define MSA_H

@@ -70,7 +70,7 @@ def _ws(lib, op, dims):
     (dict(batch=0), -1), (dict(seq_len=-5), -1), (dict(n_q_heads=63), -1), (dict(top_k=0), -1),
     (dict(softmax_scale=float("nan")), -1), (dict(softmax_scale=float("inf")), -1),
     (dict(head_dim=64), -2), (dict(idx_dim=32), -2), (dict(block_size=96), -2),
-    (dict(block_size=256), -2), (dict(top_k=33), -2), (dict(n_q_heads=24), -2),
+    (dict(block_size=256), -2), (dict(top_k=33, seq_len=8192), -2), (dict(n_q_heads=24), -2),
     (dict(n_q_heads=256), -2), (dict(seq_len=1 << 26), -2),
     (dict(batch=64, seq_len=1 << 20), -2),
 ])
@@ -80,6 +80,18 @@ def test_dims_validation(lib, kw, code):
     assert st == code
     out = lib.msa_prefill(ctypes.byref(dims), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None)
     assert out == code
+
+
+def test_dense_top_k(lib):
+    """top_k >= nb: a dense prefill with no workspace, any top_k; the sparse
+    entry points still keep at most 32 blocks."""
+    dims = D(seq_len=8192, top_k=64)  # nb = 64
+    assert _ws(lib, _lib.MSA_OP_PREFILL, dims) == (0, 0, 0)
+    for op in (_lib.MSA_OP_INDEX, _lib.MSA_OP_DECODE):
+        assert _ws(lib, op, dims)[0] == -2
+    assert lib.msa_decode(ctypes.byref(dims), *([FAKE] * 6), None, FAKE, 1 << 30, None) == -2
+    assert lib.msa_prefill_chunk(ctypes.byref(dims), 0, 10, *([FAKE] * 7), None, FAKE, 1 << 30, None) == -2
+    assert _ws(lib, _lib.MSA_OP_PREFILL, D(seq_len=4096, top_k=16))[1] > 0  # nb = 32 > 16: sparse
 
 
 def test_null_pointers(lib):

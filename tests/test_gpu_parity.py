@@ -227,6 +227,54 @@ def test_prefill_1m_sampled():
     _full_prefill_case("prefill_1m", 96, seed=41, ws_cap_gb=70)
 
 
+# ------------------------------------------------------------------ dense fallback (top_k >= nb)
+
+DENSE = [
+    # name, workload overrides, S
+    ("r1_bs32_tiles_span_blocks", dict(n_q_heads=2, n_kv_heads=2, block_size=32, top_k=32), 700),
+    ("r16_bs128", dict(n_q_heads=16, n_kv_heads=1, block_size=128, top_k=8), 1000),
+    ("r8_bs64_exact", dict(n_q_heads=16, n_kv_heads=2, block_size=64, top_k=16), 1024),
+]
+
+
+@pytest.mark.parametrize("name,over,S", DENSE, ids=[c[0] for c in DENSE])
+def test_prefill_dense_all_rows(name, over, S):
+    """top_k >= nb runs the dense causal kernel: every row against the
+    oracle, the selection (every block up to the own one) bit for bit, and
+    the output within tolerance of the sparse path (run through the chunked
+    entry point, which always takes it)."""
+    w = get_workload("tiny_2k", **over)
+    assert w.top_k >= -(-S // w.block_size)
+    _say(f"[prefill dense] {name} S={S} {w}")
+    inp = prefill_inputs(w, seed=31, device="cpu", seq_len=S)
+    dinp = {kk: vv.to(DEV) for kk, vv in inp.items()}
+    out, sel = _run_prefill(dinp, w.block_size, w.top_k)
+    summ, osel, oout = oracle_prefill_rows(inp, w, np.arange(S))
+    assert np.array_equal(host_i8(sel).astype(np.int32), osel)
+    compare_out(out, oout, name)
+    sout, ssel = _chunked(dinp, w.block_size, w.top_k, [0, S], S)
+    assert torch.equal(ssel, sel)
+    d = (sout.float() - out.float()).abs()
+    assert float(d.max()) <= 1e-2 and float(d.mean()) <= 1e-3
+
+
+def test_prefill_dense_8k_sampled():
+    """A short sequence at the 32K workload's heads: 8192 tokens with
+    top_k 64 = nb (dense); 256 sampled rows against the oracle."""
+    w = get_workload("prefill_32k", top_k=64)
+    S = 8192
+    _say(f"[prefill dense] S={S} k=64")
+    inp = prefill_inputs(w, seed=37, device=DEV, seq_len=S)
+    out, sel = _run_prefill(inp, w.block_size, w.top_k)
+    rows = sample_rows(S, 256, seed=37)
+    summ, osel, oout = oracle_prefill_rows(inp, w, rows)
+    rt = torch.as_tensor(rows, device=DEV)
+    assert np.array_equal(host_i8(sel[:, :, rt]).astype(np.int32), osel)
+    compare_out(out[:, rt], oout, "dense 8K")
+    del inp, out, sel
+    _free()
+
+
 # ------------------------------------------------------------------ chunked prefill
 
 def _chunked(inp, bs, k, bounds, C):
