@@ -618,11 +618,14 @@ hipError_t launch_attend_bs(const PrefillShape& sh, const PassInfo& pass, const 
 // hold a tile token, as in the sparse kernel.  O is written once, no
 // partials.
 // ---------------------------------------------------------------------------
-template <int BS>
-__global__ __launch_bounds__(256, 1) void dense_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                                                       const uint16_t* __restrict__ v, uint16_t* __restrict__ out,
-                                                       PrefillShape sh, int r_log2) {
+template <int BS, int NCT>
+__global__ __launch_bounds__(512 / NCT, 1) void dense_kernel(const uint16_t* __restrict__ q,
+                                                             const uint16_t* __restrict__ k,
+                                                             const uint16_t* __restrict__ v,
+                                                             uint16_t* __restrict__ out, PrefillShape sh, int r_log2) {
+  // NCT column tiles of 32 rows per wave, 8 / NCT waves per tile of 256 rows
   constexpr int KT = Tile<BS>::KT;
+  constexpr int NT = 512 / NCT;
   extern __shared__ __align__(16) char lds[];  // two K/V buffers
   const int tpt = kItemRows >> r_log2;          // tokens per tile
   const int n_tiles = (sh.S + tpt - 1) / tpt;
@@ -639,40 +642,44 @@ __global__ __launch_bounds__(256, 1) void dense_kernel(const uint16_t* __restric
   const int j_last = last_tok >> sh.bs_log2;
   const int j_mask = t0 >> sh.bs_log2;  // blocks from here on hold keys after some tile token
 
-  int tok[2], head[2];
-  u32x4_t qf[2][8];
+  int tok[NCT], head[NCT];
+  u32x4_t qf[NCT][8];
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
-    const int qr = 64 * w + 32 * ct + (lane & 31);
+  for (int ct = 0; ct < NCT; ++ct) {
+    const int qr = 32 * (NCT * w + ct) + (lane & 31);
     tok[ct] = t0 + (qr >> r_log2);
     head[ct] = qr & (sh.r - 1);
     const int tc = min(tok[ct], sh.S - 1);
     load_q_frag(q + (((size_t)b * sh.q_stride + tc) * sh.Hq + g * sh.r + head[ct]) * kHeadDim, hf, qf[ct]);
   }
-  float m[2] = {-__builtin_inff(), -__builtin_inff()};
-  float l[2] = {0.f, 0.f};
-  f32x16_t o[2][4];
+  float m[NCT], l[NCT];
+  f32x16_t o[NCT][4];
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct)
+  for (int ct = 0; ct < NCT; ++ct) {
+    m[ct] = -__builtin_inff();
+    l[ct] = 0.f;
+  }
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) o[ct][dt] = f32x16_t{};
 
   auto kv_off = [&](int j) -> size_t { return ((size_t)u * sh.kv_rows + (size_t)j * BS) * kHeadDim; };
   auto kv_keys = [&](int j) -> int { return min(BS, sh.S - j * BS); };
-  KvStage<BS, 256> kv;
-  load_kv_regs<BS, 256>(k + kv_off(0), v + kv_off(0), kv_keys(0), kv);
-  store_kv_lds<BS, 256>(kv, kv_keys(0), lds);
+  KvStage<BS, NT> kv;
+  load_kv_regs<BS, NT>(k + kv_off(0), v + kv_off(0), kv_keys(0), kv);
+  store_kv_lds<BS, NT>(kv, kv_keys(0), lds);
   __syncthreads();
 
   for (int j = 0; j <= j_last; ++j) {
     const bool more = j < j_last;
-    if (more) load_kv_regs<BS, 256>(k + kv_off(j + 1), v + kv_off(j + 1), kv_keys(j + 1), kv);
+    if (more) load_kv_regs<BS, NT>(k + kv_off(j + 1), v + kv_off(j + 1), kv_keys(j + 1), kv);
     int kvo = (j & 1) * Tile<BS>::kLdsBytes;
     __asm__ volatile("" : "+v"(kvo));
     const bool masked = j >= j_mask;
     const float lo_on = masked ? 1.0f : 0.0f;
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
+    for (int ct = 0; ct < NCT; ++ct) {
       // S^T = K Q^T of this column tile (K is read again for the second
       // tile: both at once would need 64 more registers)
       int ko = kvo;
@@ -736,13 +743,13 @@ __global__ __launch_bounds__(256, 1) void dense_kernel(const uint16_t* __restric
     }
     // the next block into the other buffer (released by the barrier that
     // ended block j - 1), its loads having had this block's work to arrive
-    if (more) store_kv_lds<BS, 256>(kv, kv_keys(j + 1), lds + ((j + 1) & 1) * Tile<BS>::kLdsBytes);
+    if (more) store_kv_lds<BS, NT>(kv, kv_keys(j + 1), lds + ((j + 1) & 1) * Tile<BS>::kLdsBytes);
     __syncthreads();
   }
 
   // O = o / l, head dims 32 dt + 8 q4 + 4 hf + 0..3 of this lane's row
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
+  for (int ct = 0; ct < NCT; ++ct) {
     if (tok[ct] >= sh.S) continue;
     const float inv = 1.0f / l[ct];
     uint16_t* orow = out + (((size_t)b * sh.q_stride + tok[ct]) * sh.Hq + g * sh.r + head[ct]) * kHeadDim;
@@ -806,21 +813,24 @@ hipError_t launch_dense(const PrefillShape& sh, const uint16_t* q, const uint16_
   const int tpt = kItemRows >> r_log2;
   const dim3 grid((unsigned)((sh.S + tpt - 1) / tpt), (unsigned)(sh.B * sh.G));
   switch (sh.bs) {
-#define MSA_DENSE_LAUNCH(BS_)                                                                                 \
+#define MSA_DENSE_LAUNCH(BS_, NCT_)                                                                          \
   {                                                                                                           \
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&dense_kernel<BS_>),     \
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&dense_kernel<BS_, NCT_>), \
                                                        hipFuncAttributeMaxDynamicSharedMemorySize,           \
                                                        2 * Tile<BS_>::kLdsBytes);                             \
     if (attr != hipSuccess) return attr;                                                                      \
-    hipLaunchKernelGGL(dense_kernel<BS_>, grid, dim3(256), 2 * Tile<BS_>::kLdsBytes, st, q, k, v, out, sh, r_log2); \
+    hipLaunchKernelGGL((dense_kernel<BS_, NCT_>), grid, dim3(512 / NCT_), 2 * Tile<BS_>::kLdsBytes, st, q, k, v, \
+                       out, sh, r_log2);                                                                      \
     break;                                                                                                    \
   }
+    // one column tile per wave (8 waves) where a block gives every thread
+    // a piece of V to stage, two (4 waves) for 32-key blocks
     case 32:
-      MSA_DENSE_LAUNCH(32)
+      MSA_DENSE_LAUNCH(32, 2)
     case 64:
-      MSA_DENSE_LAUNCH(64)
+      MSA_DENSE_LAUNCH(64, 1)
     default:
-      MSA_DENSE_LAUNCH(128)
+      MSA_DENSE_LAUNCH(128, 1)
 #undef MSA_DENSE_LAUNCH
   }
   hipError_t e = hipGetLastError();
