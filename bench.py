@@ -229,6 +229,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--core-only", action="store_true",
+                    help="time the step only: no chunked, short-sequence or generation-step extras")
     ap.add_argument("--cpu-baseline-worker", default=None, help=argparse.SUPPRESS)
     ap.add_argument("--pmc-run", action="store_true",
                     help="run the counter-collection workload instead of the benchmark")
@@ -324,88 +326,94 @@ def main():
     msa.profile_enable(False)
     dkt = msa.profile_read()
 
-    # generation step: append token L - 1 to the caches, refresh its block's
-    # summary, decode (outside the timed region; same events)
-    def gen_step():
-        msa.msa_decode_step(din["q"], din["q_idx"], k_new, v_new, k_idx_new, din["k_cache"], din["v_cache"],
-                            gen_sums, gen_keys, L, wd.block_size, wd.top_k, out=dout, workspace=dws)
+    # further measurements outside the timed step (left out by --core-only,
+    # e.g. under a profiler, so that each kernel's launches are those of the
+    # step alone)
+    gen_med = ch_ms = dwarm_med = None
+    short_ms, short_flop = {}, None
+    if not args.core_only:
+        # generation step: append token L - 1 to the caches, refresh its block's
+        # summary, decode (outside the timed region; same events)
+        def gen_step():
+            msa.msa_decode_step(din["q"], din["q_idx"], k_new, v_new, k_idx_new, din["k_cache"], din["v_cache"],
+                                gen_sums, gen_keys, L, wd.block_size, wd.top_k, out=dout, workspace=dws)
 
-    for _ in range(3):
-        gen_step()
-    torch.cuda.synchronize()
-    gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for a, b in gev:
-        a.record()
-        gen_step()
-        b.record()
-    torch.cuda.synchronize()
-    gen_us = sorted(a.elapsed_time(b) * 1e3 for a, b in gev)
-    gen_med = gen_us[len(gen_us) // 2]
-    # chunked prefill of the same 32K workload: four chunks of 8192 queries
-    # against the cache (the K/V tensors serve as caches of capacity S)
-    bounds = [0, 8192, 16384, 24576, wp.seq_len]
-    cq = [pin["q"][:, a:b].contiguous() for a, b in zip(bounds[:-1], bounds[1:])]
-    cqi = [pin["q_idx"][:, :, a:b].contiguous() for a, b in zip(bounds[:-1], bounds[1:])]
-    couts = [torch.empty_like(x) for x in cq]
-    ckeys = torch.empty_like(block_keys_prefill_shape(pin, wp))
-    cws = torch.empty(_chunk_ws_bytes(msa, pdims, 8192), dtype=torch.uint8, device=dev)
-
-    def chunked():
-        for i, a in enumerate(bounds[:-1]):
-            msa.msa_prefill_chunk(cq[i], cqi[i], pin["k"], pin["v"], pin["k_idx"], ckeys, a, wp.block_size,
-                                  wp.top_k, out=couts[i], workspace=cws)
-
-    chunked()
-    torch.cuda.synchronize()
-    cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
-    for a, b in cev:
-        a.record()
-        chunked()
-        b.record()
-    torch.cuda.synchronize()
-    ch_ms = sorted(a.elapsed_time(b) for a, b in cev)[2]
-    del cq, cqi, couts, cws
-
-    # short sequence, top_k covering every block (4096 tokens, top_k 32 =
-    # nb): msa_prefill takes the dense causal kernel; the chunked entry point
-    # runs the sparse path on the same data
-    ws_ = get_workload("prefill_32k", top_k=32)
-    Ss = 4096
-    sin = prefill_inputs(ws_, seed=1, device=dev, seq_len=Ss)
-    sout = torch.empty_like(sin["q"])
-    skeys = torch.empty((1, ws_.n_kv_heads, Ss // ws_.block_size, 64), dtype=torch.int8, device=dev)
-    sdims = msa.make_dims(1, Ss, ws_.n_q_heads, ws_.n_kv_heads, ws_.block_size, ws_.top_k)
-    sws = torch.empty(_chunk_ws_bytes(msa, sdims, Ss), dtype=torch.uint8, device=dev)
-    short_runs = {
-        "dense": lambda: msa.msa_prefill(sin["q"], sin["k"], sin["v"], sin["q_idx"], sin["k_idx"], ws_.block_size,
-                                         ws_.top_k, out=sout),
-        "sparse_path": lambda: msa.msa_prefill_chunk(sin["q"], sin["q_idx"], sin["k"], sin["v"], sin["k_idx"], skeys,
-                                                     0, ws_.block_size, ws_.top_k, out=sout, workspace=sws),
-    }
-    short_ms = {}
-    for name_, fn in short_runs.items():
-        fn()
+        for _ in range(3):
+            gen_step()
         torch.cuda.synchronize()
-        sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
-        for a, b in sev:
+        gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for a, b in gev:
             a.record()
-            fn()
+            gen_step()
             b.record()
         torch.cuda.synchronize()
-        short_ms[name_] = sorted(a.elapsed_time(b) for a, b in sev)[2]
-    short_flop = 4.0 * D_HEAD * ws_.n_q_heads * Ss * (Ss + 1) / 2
-    del sin, sout, sws
+        gen_us = sorted(a.elapsed_time(b) * 1e3 for a, b in gev)
+        gen_med = gen_us[len(gen_us) // 2]
+        # chunked prefill of the same 32K workload: four chunks of 8192 queries
+        # against the cache (the K/V tensors serve as caches of capacity S)
+        bounds = [0, 8192, 16384, 24576, wp.seq_len]
+        cq = [pin["q"][:, a:b].contiguous() for a, b in zip(bounds[:-1], bounds[1:])]
+        cqi = [pin["q_idx"][:, :, a:b].contiguous() for a, b in zip(bounds[:-1], bounds[1:])]
+        couts = [torch.empty_like(x) for x in cq]
+        ckeys = torch.empty_like(block_keys_prefill_shape(pin, wp))
+        cws = torch.empty(_chunk_ws_bytes(msa, pdims, 8192), dtype=torch.uint8, device=dev)
 
-    # the plain decode timed the same way (back to back, so the kept blocks
-    # may still sit in the memory-side cache, unlike in the step above where
-    # a prefill runs in between)
-    for a, b in gev:
-        a.record()
-        decode()
-        b.record()
-    torch.cuda.synchronize()
-    dwarm_us = sorted(a.elapsed_time(b) * 1e3 for a, b in gev)
-    dwarm_med = dwarm_us[len(dwarm_us) // 2]
+        def chunked():
+            for i, a in enumerate(bounds[:-1]):
+                msa.msa_prefill_chunk(cq[i], cqi[i], pin["k"], pin["v"], pin["k_idx"], ckeys, a, wp.block_size,
+                                      wp.top_k, out=couts[i], workspace=cws)
+
+        chunked()
+        torch.cuda.synchronize()
+        cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+        for a, b in cev:
+            a.record()
+            chunked()
+            b.record()
+        torch.cuda.synchronize()
+        ch_ms = sorted(a.elapsed_time(b) for a, b in cev)[2]
+        del cq, cqi, couts, cws
+
+        # short sequence, top_k covering every block (4096 tokens, top_k 32 =
+        # nb): msa_prefill takes the dense causal kernel; the chunked entry point
+        # runs the sparse path on the same data
+        ws_ = get_workload("prefill_32k", top_k=32)
+        Ss = 4096
+        sin = prefill_inputs(ws_, seed=1, device=dev, seq_len=Ss)
+        sout = torch.empty_like(sin["q"])
+        skeys = torch.empty((1, ws_.n_kv_heads, Ss // ws_.block_size, 64), dtype=torch.int8, device=dev)
+        sdims = msa.make_dims(1, Ss, ws_.n_q_heads, ws_.n_kv_heads, ws_.block_size, ws_.top_k)
+        sws = torch.empty(_chunk_ws_bytes(msa, sdims, Ss), dtype=torch.uint8, device=dev)
+        short_runs = {
+            "dense": lambda: msa.msa_prefill(sin["q"], sin["k"], sin["v"], sin["q_idx"], sin["k_idx"], ws_.block_size,
+                                             ws_.top_k, out=sout),
+            "sparse_path": lambda: msa.msa_prefill_chunk(sin["q"], sin["q_idx"], sin["k"], sin["v"], sin["k_idx"], skeys,
+                                                         0, ws_.block_size, ws_.top_k, out=sout, workspace=sws),
+        }
+        short_ms = {}
+        for name_, fn in short_runs.items():
+            fn()
+            torch.cuda.synchronize()
+            sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+            for a, b in sev:
+                a.record()
+                fn()
+                b.record()
+            torch.cuda.synchronize()
+            short_ms[name_] = sorted(a.elapsed_time(b) for a, b in sev)[2]
+        short_flop = 4.0 * D_HEAD * ws_.n_q_heads * Ss * (Ss + 1) / 2
+        del sin, sout, sws
+
+        # the plain decode timed the same way (back to back, so the kept blocks
+        # may still sit in the memory-side cache, unlike in the step above where
+        # a prefill runs in between)
+        for a, b in gev:
+            a.record()
+            decode()
+            b.record()
+        torch.cuda.synchronize()
+        dwarm_us = sorted(a.elapsed_time(b) * 1e3 for a, b in gev)
+        dwarm_med = dwarm_us[len(dwarm_us) // 2]
 
     per_head_keys, pairs, rows_merged = _prefill_counts(wp)
     D = wp.head_dim
@@ -460,20 +468,20 @@ def main():
             "frac_hbm_peak": round(dbytes / (dec_med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "bytes_alg": dbytes,
         },
-        "prefill_chunked": {
+        "prefill_chunked": None if ch_ms is None else {
             "what": "the same 32K prefill as four chunks of 8192 queries against the cache",
             "ms": round(ch_ms, 4),
             "tokens_per_s": round(tokens / (ch_ms * 1e-3), 1),
             "tflops_alg": round(flop_alg / (ch_ms * 1e-3) / 1e12, 2),
         },
-        "prefill_short_dense": {
+        "prefill_short_dense": None if not short_ms else {
             "what": "4096 tokens, top_k 32 = every block: dense causal kernel vs the sparse path on the same data",
             "dense_ms": round(short_ms["dense"], 4),
             "sparse_path_ms": round(short_ms["sparse_path"], 4),
             "dense_tflops": round(short_flop / (short_ms["dense"] * 1e-3) / 1e12, 2),
             "dense_frac_bf16_peak": round(short_flop / (short_ms["dense"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         },
-        "decode_step": {
+        "decode_step": None if gen_med is None else {
             "what": "append one token per sequence (K/V rows, running index-key sum, block summary) + decode",
             "us": round(gen_med, 2),
             "tokens_per_s": round(wd.batch / (gen_med * 1e-6), 1),
