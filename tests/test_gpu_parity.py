@@ -300,11 +300,34 @@ def _chunked(inp, bs, k, bounds, C):
     return torch.cat(outs, dim=1), torch.cat(sels, dim=2)
 
 
+def test_prefill_query_chunks_batch2():
+    """A prefill longer than one query chunk (16384 tokens) with two
+    sequences: the chunks slice rows of batch-strided tensors.  Sampled rows
+    of both sequences against the oracle, and every row against the same
+    sequences prefilled through msa_prefill_chunk in other chunks."""
+    w = get_workload("tiny_2k", batch=2, n_q_heads=4, n_kv_heads=2, block_size=64, top_k=6)
+    S = 20000
+    _say(f"[prefill query chunks] B=2 S={S} {w}")
+    inp = prefill_inputs(w, seed=43, device=DEV, seq_len=S)
+    out, sel = _run_prefill(inp, w.block_size, w.top_k)
+    rows = sample_rows(S, 192, seed=43)
+    rt = torch.as_tensor(rows, device=DEV)
+    _, osel, oout = oracle_prefill_rows(inp, w, rows)
+    assert np.array_equal(host_i8(sel[:, :, rt]).astype(np.int32), osel)
+    compare_out(out[:, rt], oout, "query chunks B=2")
+    cout, csel = _chunked(inp, w.block_size, w.top_k, [0, 7000, 16384, 16385, S], S)
+    assert torch.equal(csel, sel)
+    assert torch.equal(cout, out)
+    del inp, out, sel, cout, csel
+    _free()
+
+
 CHUNKED = [
     # name, workload overrides, S, chunk bounds, capacity
     ("ragged_gqa4", dict(n_q_heads=8, n_kv_heads=2, block_size=64, top_k=5), 1000, [0, 300, 301, 700, 1000], 1100),
     ("bs128_r8", dict(n_q_heads=16, n_kv_heads=2, block_size=128, top_k=6), 2048, [0, 512, 1024, 1536, 2048], 2048),
     ("bs32_k32", dict(n_q_heads=4, n_kv_heads=2, block_size=32, top_k=32), 1500, [0, 40, 1023, 1500], 1600),
+    ("batch3", dict(batch=3, n_q_heads=8, n_kv_heads=2, block_size=64, top_k=4), 900, [0, 450, 900], 1000),
 ]
 
 
