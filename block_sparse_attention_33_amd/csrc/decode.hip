@@ -7,12 +7,15 @@
 // reports the decode speed-up).  The work is bound by HBM reads: the block
 // summaries (nb x 64 B per group) and the selected K/V blocks.
 //
-//   decode_kernel  one workgroup per (batch, group): scores every candidate
-//                  block, keeps the best top_k - 1 plus the own block, and
-//                  runs the r query heads of the group over the kept blocks
-//                  with an online softmax (split over two groups of waves,
-//                  merged at the end).  Nothing but the selection and the
-//                  output leaves the workgroup.
+//   decode_kernel  two workgroups per (batch, group): each scores every
+//                  candidate block, keeps the best top_k - 1 plus the own
+//                  block, and runs the r query heads of the group over its
+//                  share of the kept blocks with an online softmax (split
+//                  over two groups of waves, merged at the end); with one
+//                  workgroup per unit it writes the output directly.
+//   decode_merge_kernel  combines the two workgroups' states of a unit.
+//   append_kernel  one new token per unit into the caches, its index key
+//                  into the running sums and the summary of its block.
 //
 // Ranking keys are 64-bit: (score << 32) | (0xffffffff - block), so a larger
 // key is a higher score or, at equal score, a lower block index.
@@ -95,19 +98,23 @@ __device__ __forceinline__ void wave_topk_rank(const int64_t (&k)[NK], int kp, i
 // ---------------------------------------------------------------------------
 // Fused decode: one workgroup (8 waves) per (sequence, group) unit.
 //
-//   selection  thread i scores candidates i, i + 512, ... (NK of them), each
-//              wave keeps its best kp, wave 0 picks the best kp of the 8
-//              lists and ranks them by block index: slot s of the selection
-//              is the s-th smallest, the own block follows them, later slots
-//              are empty (-1).
-//   attention  two groups of 4 waves take the even and the odd slots; per
-//              slot a group runs S^T = K Q^T on 32x32x16 MFMA (wave w: keys
-//              32 w .. 32 w + 31, the r query heads as columns, K straight
-//              from HBM), P = 2^(S - m) goes to LDS as bf16 [head][key], V
-//              to LDS transposed, and O^T = V^T P^T (wave w: head dims
-//              32 w .. 32 w + 31) is added to the group's running
-//              online-softmax state.  A group's next slot loads while the
-//              current one is computed.
+//   selection  the four lanes of a quad read the four 16-byte quarters of
+//              one candidate's summary (a wave load covers 16 whole
+//              summaries) and sum their partial dot products; each thread
+//              keeps NK candidates, each wave ranks its keys down to its
+//              best kp, all eight waves rank the 8 kp survivors (four
+//              threads per key) and the kept blocks are sorted by block
+//              index: slot s of the selection is the s-th smallest, the own
+//              block follows them, later slots are empty (-1).
+//   attention  two groups of 4 waves take the even and the odd slots of
+//              the workgroup's share; per slot a group runs S^T = K Q^T on
+//              32x32x16 MFMA (wave w: keys 32 w .. 32 w + 31, the r query
+//              heads as columns, K straight from HBM, Q from LDS),
+//              P = 2^(S - m) goes to LDS as bf16 [head][key], V (loaded as
+//              whole rows) is transposed in registers into LDS, and
+//              O^T = V^T P^T (wave w: head dims 32 w .. 32 w + 31) is added
+//              to the group's running online-softmax state.  A group's next
+//              slot loads while the current one is computed.
 //   merge      the two groups' states are combined in LDS and written as
 //              bf16, or, when a unit's slots are shared by n_split
 //              workgroups (slot s goes to workgroup s % n_split), written as
@@ -116,8 +123,8 @@ __device__ __forceinline__ void wave_topk_rank(const int64_t (&k)[NK], int kp, i
 // ---------------------------------------------------------------------------
 constexpr int kRowStride = 2 * 128 + 16;  // bytes per 128-key row of V^T and P^T in LDS
 
-// One slot's block in registers: K fragments of this lane's key row and V
-// key pairs (2p, 2p + 1) x 8 head dims.
+// One slot's block in registers: K fragments of this lane's key row and an
+// 8 x 8 tile of V.
 struct DecBlock {
   u32x4_t kf[8];
   u32x4_t vv[8];  // V rows 8 o + i (i = 0..7), head dims 8 c .. 8 c + 7 (o, c of the thread)

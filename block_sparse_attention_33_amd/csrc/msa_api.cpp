@@ -70,54 +70,34 @@ int check_dims(const msa_dims* d, Dims* o) {
 
 // ---- prefill planning
 //
-// The main branch runs in passes.  When the partials of one (unit, query
-// range) pass fit kPassPartialBudget and a range still gathers enough queries
-// per KV block, each unit is split into query ranges of T tokens so that the
-// partials written by the off-diagonal kernel are read back by the merge
-// kernel while they still sit in the 256 MB memory-side cache.  Otherwise a
-// unit is one range (T >= S) and a pass takes as many units as the
-// workspace holds.
-constexpr size_t kPassPartialBudget = 128ull << 20;
-// Measured on MI355X at 32K tokens: ranged passes leave about one work item
-// per CU per pass, and the passes' load imbalance costs more than the cache
-// residency of the partials saves, so one pass over all units is used.
-constexpr bool kUseQueryRanges = false;
-constexpr long kMaxRows = 1L << 22;      // CSR rows (unit, range, block)
+// A long prefill runs in query chunks (kPrefillQueryChunk); within a chunk
+// the main branch runs in passes of as many (batch, group) units as the
+// workspace holds partials for (all of them at the full workspace size).
+// The CSR rows are (unit, block): one query range per unit.  (The kernels
+// also take (unit, range, block) rows, several ranges per unit; that split,
+// one unit's range per pass, measured slower on MI355X than query chunks
+// over all units, so it is not planned here.)
 constexpr long kMaxChunkCounters = 1L << 22;
 
 struct PrefillPlan {
   long T, n_ranges, m, tpc, n_chunks, rows, tokens_per_item, max_items_per_range;
-  bool ranged;
 };
 
 PrefillPlan plan_prefill(const Dims& d) {
   PrefillPlan p{};
   p.tokens_per_item = msa::kItemChunks * msa::kItemRows / d.r;
-  const long S256 = (d.S + 255) / 256 * 256;
-  p.ranged = false;
-  p.T = S256;
-  {
-    const long per_tok = d.k * d.r * (2 * d.D + 8);
-    const long t_mall = (long)(kPassPartialBudget / per_tok) / 256 * 256;
-    // about 32 queries per (range, block) row at the far end of the sequence
-    const long t_reuse = (32 * d.nb / d.k + 255) / 256 * 256;
-    if (kUseQueryRanges && t_mall >= 256 && t_mall >= t_reuse && t_mall < d.S &&
-        d.U * ((d.S + t_mall - 1) / t_mall) * d.nb <= kMaxRows) {
-      p.ranged = true;
-      p.T = t_mall;
-    }
-  }
-  p.n_ranges = (d.S + p.T - 1) / p.T;
-  p.rows = d.U * p.n_ranges * d.nb;
-  // chunks per range: tokens multiple of 256, bounded number of counters
+  p.T = (d.S + 255) / 256 * 256;
+  p.n_ranges = 1;
+  p.rows = d.U * d.nb;
+  // token chunks of the inversion's histograms: multiples of 256 tokens, a
+  // bounded number of counters
   const long by_tokens = p.T / 256;
-  const long by_size = std::max(1L, kMaxChunkCounters / (d.U * p.n_ranges * d.nb));
+  const long by_size = std::max(1L, kMaxChunkCounters / (d.U * d.nb));
   p.m = std::max(1L, std::min(by_tokens, by_size));
   p.tpc = (p.T / 256 + p.m - 1) / p.m * 256;
   p.m = (p.T + p.tpc - 1) / p.tpc;
-  p.n_chunks = p.n_ranges * p.m;
-  const long range_tok = std::min(p.T, d.S);
-  p.max_items_per_range = (range_tok * d.k + p.tokens_per_item - 1) / p.tokens_per_item + d.nb;
+  p.n_chunks = p.m;
+  p.max_items_per_range = (d.S * d.k + p.tokens_per_item - 1) / p.tokens_per_item + d.nb;
   return p;
 }
 
@@ -134,7 +114,7 @@ PrefillLayout prefill_layout(const Dims& d, const PrefillPlan& p, long units_per
     off += align_up(bytes);
     return at;
   };
-  const long pass_tokens = std::min(p.T, d.S);
+  const long pass_tokens = d.S;
   L.block_keys = take((size_t)d.U * d.nb * d.di);
   L.sel = take((size_t)d.U * d.S * d.k * 4);
   L.counts = take((size_t)p.rows * 4);
@@ -306,12 +286,9 @@ int run_prefill(const Dims& dc, long q0, long n_q, long q_stride, const uint16_t
   const PrefillLayout one = prefill_layout(d, P, 1);
   st = check_ws(ws, ws_bytes, one.total);
   if (st != MSA_OK) return st;
-  // unranged: as many (batch, group) units per pass as the workspace holds
-  long upp = 1;
-  if (!P.ranged) {
-    const size_t per_unit = prefill_layout(d, P, 2).total - one.total;
-    upp = per_unit > 0 ? std::min<long>(d.U, 1 + (long)((ws_bytes - one.total) / per_unit)) : d.U;
-  }
+  // as many (batch, group) units per pass as the workspace holds
+  const size_t per_unit = prefill_layout(d, P, 2).total - one.total;
+  long upp = per_unit > 0 ? std::min<long>(d.U, 1 + (long)((ws_bytes - one.total) / per_unit)) : d.U;
   PrefillLayout L = prefill_layout(d, P, upp);
   while (L.total > ws_bytes && upp > 1) L = prefill_layout(d, P, --upp);
 
@@ -369,34 +346,25 @@ int run_prefill(const Dims& dc, long q0, long n_q, long q_stride, const uint16_t
   sh.q0 = iq0;
   sh.q_stride = (int)q_stride;
   sh.kv_rows = (int)dc.S;
-  const int pass_tokens = (int)std::min(P.T, d.S);
-  auto run_pass = [&](long u0, long u1, long rng) -> int {
+  auto run_pass = [&](long u0, long u1) -> int {
     msa::PassInfo ps;
     ps.u0 = (int)u0;
     ps.u1 = (int)u1;
-    ps.rng = (int)rng;
-    ps.t0 = (int)(rng * P.T);
-    ps.t1 = (int)std::min<long>(d.S, (rng + 1) * P.T);
-    ps.pass_tokens = pass_tokens;
-    ps.row_begin = (int)((u0 * P.n_ranges + rng) * nb);
-    ps.row_end = (int)(((u1 - 1) * P.n_ranges + rng + 1) * nb);
+    ps.rng = 0;
+    ps.t0 = 0;
+    ps.t1 = S;
+    ps.pass_tokens = S;
+    ps.row_begin = (int)(u0 * nb);
+    ps.row_end = (int)(u1 * nb);
     const long max_items = (u1 - u0) * P.max_items_per_range;
     MSA_LAUNCH_NAMED("attend", s, msa::launch_attend(sh, ps, q, k, v, row_ptr, item_ptr, items, entries, part_o,
                                                      part_ml, (int)max_items, s));
     MSA_LAUNCH_NAMED("merge", s, msa::launch_merge(sh, ps, part_o, part_ml, out, s));
     return MSA_OK;
   };
-  if (P.ranged) {
-    for (long u = 0; u < d.U; ++u)
-      for (long rng = 0; rng < P.n_ranges; ++rng) {
-        st = run_pass(u, u + 1, rng);
-        if (st != MSA_OK) return st;
-      }
-  } else {
-    for (long u0 = 0; u0 < d.U; u0 += upp) {
-      st = run_pass(u0, std::min<long>(d.U, u0 + upp), 0);
-      if (st != MSA_OK) return st;
-    }
+  for (long u0 = 0; u0 < d.U; u0 += upp) {
+    st = run_pass(u0, std::min<long>(d.U, u0 + upp));
+    if (st != MSA_OK) return st;
   }
   return MSA_OK;
 }
@@ -442,7 +410,7 @@ int msa_workspace_bytes(int op, const msa_dims* dims, size_t* min_bytes, size_t*
       const Dims dq = chunk_dims(d, std::min(d.S, prefill_query_chunk(d)));
       const PrefillPlan p = plan_prefill(dq);
       lo = prefill_layout(dq, p, 1).total;
-      hi = p.ranged ? lo : prefill_layout(dq, p, dq.U).total;
+      hi = prefill_layout(dq, p, dq.U).total;
       break;
     }
     case MSA_OP_DECODE: {
@@ -539,7 +507,7 @@ int msa_prefill_chunk_workspace_bytes(const msa_dims* dims, int32_t count, size_
   const Dims dq = chunk_dims(d, count);
   const PrefillPlan p = plan_prefill(dq);
   const size_t lo = prefill_layout(dq, p, 1).total;
-  const size_t hi = p.ranged ? lo : prefill_layout(dq, p, dq.U).total;
+  const size_t hi = prefill_layout(dq, p, dq.U).total;
   if (min_bytes) *min_bytes = lo;
   if (full_bytes) *full_bytes = hi;
   return MSA_OK;

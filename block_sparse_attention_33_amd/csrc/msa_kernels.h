@@ -25,7 +25,7 @@ struct PrefillShape {
 
 // One pass of the main branch: units [u0, u1) x query range `rng` (always
 // range 0 when a unit has a single range).  Partials of the pass are indexed
-// ((u - u0) * pass_tokens + (t - t0)) * (top_k - 1) + slot.
+// ((u - u0) * pass_tokens + (t - t0)) * top_k + slot.
 struct PassInfo {
   int u0, u1, rng, t0, t1, pass_tokens;
   int row_begin, row_end;  // CSR rows of the pass

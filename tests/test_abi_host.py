@@ -177,35 +177,24 @@ def _a(x):
     return (x + 255) // 256 * 256
 
 
-USE_QUERY_RANGES = False   # the library's current choice (one pass over all units)
 QUERY_CHUNK = 16384        # a longer prefill runs in query chunks of this many tokens
 
 
-def _plan(U, S, nb, r, k):
-    """The documented prefill plan: with query ranges enabled, ranges of T
-    tokens per (batch, group) unit when one range's partials (one per kept
-    block, own block included) fit 128 MiB and a range still gathers ~32
-    queries per KV block; chunks of a multiple of 256 tokens."""
-    S256 = -(-S // 256) * 256
-    T, ranged = S256, False
-    if USE_QUERY_RANGES:
-        per_tok = k * r * (2 * 128 + 8)
-        t_mall = (128 * 2**20 // per_tok) // 256 * 256
-        t_reuse = -(-(32 * nb // k) // 256) * 256
-        if t_mall >= 256 and t_mall >= t_reuse and t_mall < S and U * (-(-S // t_mall)) * nb <= 1 << 22:
-            T, ranged = t_mall, True
-    n_ranges = -(-S // T)
-    m = max(1, min(T // 256, max(1, (1 << 22) // (U * n_ranges * nb))))
+def _plan(U, S, nb):
+    """The documented prefill plan: one query range per unit, histogram
+    chunks of a multiple of 256 tokens, at most 2^22 counters."""
+    T = -(-S // 256) * 256
+    m = max(1, min(T // 256, max(1, (1 << 22) // (U * nb))))
     tpc = -(-(T // 256) // m) * 256
     m = -(-T // tpc)
-    return T, ranged, n_ranges, n_ranges * m
+    return m
 
 
-@pytest.mark.parametrize("B,S,Hq,G,bs,k,ranged", [
-    (1, 32768, 64, 8, 128, 16, False), (1, 2048, 8, 1, 64, 8, False), (2, 1000, 8, 2, 32, 5, False),
-    (1, 777, 16, 1, 128, 1, False), (1, 1048576, 64, 8, 128, 16, False), (1, 131072, 64, 8, 128, 16, False),
-    (1, 65536, 8, 1, 128, 1, False)])
-def test_prefill_workspace_layout(lib, B, S, Hq, G, bs, k, ranged):
+@pytest.mark.parametrize("B,S,Hq,G,bs,k", [
+    (1, 32768, 64, 8, 128, 16), (1, 2048, 8, 1, 64, 8), (2, 1000, 8, 2, 32, 5),
+    (1, 777, 16, 1, 128, 1), (1, 1048576, 64, 8, 128, 16), (1, 131072, 64, 8, 128, 16),
+    (1, 65536, 8, 1, 128, 1)])
+def test_prefill_workspace_layout(lib, B, S, Hq, G, bs, k):
     """The documented layout: fixed part + one bf16 partial (r x 128) and one
     fp32 (max, sum) pair (r) per (token, kept block) of a pass; the
     token-sized parts cover one query chunk, the block-sized parts the whole
@@ -217,16 +206,14 @@ def test_prefill_workspace_layout(lib, B, S, Hq, G, bs, k, ranged):
     nb = -(-S // bs)
     S = min(S, QUERY_CHUNK)
     tpi = 4 * 256 // r          # up to 4 chunks of 256 query rows per work item
-    T, is_ranged, n_ranges, n_chunks = _plan(U, S, nb, r, k)
-    assert is_ranged == ranged
-    rows = U * n_ranges * nb
-    range_tok = min(T, S)
-    items = U * n_ranges * ((range_tok * k + tpi - 1) // tpi + nb) + 1
+    n_chunks = _plan(U, S, nb)
+    rows = U * nb
+    items = U * ((S * k + tpi - 1) // tpi + nb) + 1
     fixed = (_a(U * nb * 64) + _a(U * S * k * 4) + _a(rows * 4) + _a(U * n_chunks * nb * 4)
              + 2 * _a((rows + 1) * 4) + _a(U * S * k * 4) + _a(items * 8))
-    part = lambda n: _a(n * range_tok * k * r * 128 * 2) + _a(n * range_tok * k * r * 8)  # noqa: E731
+    part = lambda n: _a(n * S * k * r * 128 * 2) + _a(n * S * k * r * 8)  # noqa: E731
     assert lo == fixed + part(1)
-    assert hi == (lo if ranged else fixed + part(U))
+    assert hi == fixed + part(U)
 
 
 def test_prefill_block_limit(lib):

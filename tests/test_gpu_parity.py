@@ -178,7 +178,7 @@ def _full_prefill_case(name, n_rows, seed, ws_cap_gb=None):
 
 
 def test_prefill_32k_sampled():
-    _full_prefill_case("prefill_32k", 384, seed=21)
+    _full_prefill_case("prefill_32k", 256, seed=21)
 
 
 def test_prefill_32k_selection_all_rows():
@@ -260,13 +260,13 @@ def test_prefill_dense_all_rows(name, over, S):
 
 def test_prefill_dense_8k_sampled():
     """A short sequence at the 32K workload's heads: 8192 tokens with
-    top_k 64 = nb (dense); 256 sampled rows against the oracle."""
+    top_k 64 = nb (dense); 128 sampled rows against the oracle."""
     w = get_workload("prefill_32k", top_k=64)
     S = 8192
     _say(f"[prefill dense] S={S} k=64")
     inp = prefill_inputs(w, seed=37, device=DEV, seq_len=S)
     out, sel = _run_prefill(inp, w.block_size, w.top_k)
-    rows = sample_rows(S, 256, seed=37)
+    rows = sample_rows(S, 128, seed=37)
     summ, osel, oout = oracle_prefill_rows(inp, w, rows)
     rt = torch.as_tensor(rows, device=DEV)
     assert np.array_equal(host_i8(sel[:, :, rt]).astype(np.int32), osel)
@@ -325,7 +325,7 @@ def test_prefill_query_chunks_batch2():
 CHUNKED = [
     # name, workload overrides, S, chunk bounds, capacity
     ("ragged_gqa4", dict(n_q_heads=8, n_kv_heads=2, block_size=64, top_k=5), 1000, [0, 300, 301, 700, 1000], 1100),
-    ("bs128_r8", dict(n_q_heads=16, n_kv_heads=2, block_size=128, top_k=6), 2048, [0, 512, 1024, 1536, 2048], 2048),
+    ("bs128_r8", dict(n_q_heads=16, n_kv_heads=2, block_size=128, top_k=6), 1536, [0, 512, 1024, 1536], 1536),
     ("bs32_k32", dict(n_q_heads=4, n_kv_heads=2, block_size=32, top_k=32), 1500, [0, 40, 1023, 1500], 1600),
     ("batch3", dict(batch=3, n_q_heads=8, n_kv_heads=2, block_size=64, top_k=4), 900, [0, 450, 900], 1000),
 ]
