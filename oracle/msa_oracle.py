@@ -184,6 +184,102 @@ def decode(q, q_idx, k_cache, v_cache, summaries, block_size: int, top_k: int, s
 
 
 # --------------------------------------------------------------------------
+# main branch, training: log-sum-exp and gradients with the selection fixed
+# --------------------------------------------------------------------------
+#
+# The pages report ablations of trained MSA models and a training cost
+# (wiki.500nian.com digest of "MiniMax M3 Review", the ablation paragraph;
+# devpress.csdn.net article, section "M3的技术局限与改进方向", third
+# limitation) but print no backward formula.  The reading here: the index
+# branch is integer arithmetic and carries no gradient, so the selection is a
+# constant of the backward pass, and the gradients are those of the forward
+# definition above -- one softmax over the attended keys -- by the chain rule.
+
+def lse_rows(q_rows, k, v, sel, rows, block_size: int, scale=None) -> np.ndarray:
+    """Natural log-sum-exp of the scaled scores q.k * scale over the keys a
+    query row attends to: [B, len(rows), Hq] float64."""
+    B, R, Hq, D = q_rows.shape
+    G, S = k.shape[1], k.shape[2]
+    r = Hq // G
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    out = np.empty((B, R, Hq), dtype=np.float64)
+    for b in range(B):
+        for i, t in enumerate(np.asarray(rows)):
+            for g in range(G):
+                keys = selected_keys(sel[b, g, i], int(t), block_size, S)
+                z = (q_rows[b, i, g * r:(g + 1) * r].astype(np.float64) @ k[b, g, keys].astype(np.float64).T) * scale
+                zm = z.max(axis=1, keepdims=True)
+                out[b, i, g * r:(g + 1) * r] = (zm + np.log(np.exp(z - zm).sum(axis=1, keepdims=True)))[:, 0]
+    return out
+
+
+def _query_grads(qh, ks, vs, doh, scale):
+    """Gradients of sum(do * o) for o = softmax(qh ks^T * scale) vs, for the r
+    query heads of one token over its m attended keys.
+
+    qh, doh: [r, D]; ks, vs: [m, D].  With w the softmax weights [r, m]:
+      dv = w^T do;  dw = do vs^T;  dz = w * (dw - rowsum(w * dw));
+      dq = scale dz ks;  dk = scale dz^T qh.
+    """
+    z = (qh @ ks.T) * scale
+    z = z - z.max(axis=1, keepdims=True)
+    w = np.exp(z)
+    w = w / w.sum(axis=1, keepdims=True)
+    dw = doh @ vs.T
+    dz = w * (dw - (w * dw).sum(axis=1, keepdims=True))
+    return scale * (dz @ ks), scale * (dz.T @ qh), w.T @ doh
+
+
+def backward(q, k, v, dout, sel, block_size: int, scale=None, rows=None, kv_blocks=None):
+    """Gradients of sum(dout * O) with respect to q, k and v, O being the
+    main-branch output of every query row and the selection sel
+    [B, G, S, top_k] held fixed.
+
+    q, dout: [B, S, Hq, D]; k, v: [B, G, S, D] (fp32 or fp64 holding the bf16
+    inputs).  Returns float64 (dq [B, len(rows), Hq, D] for the query rows
+    `rows` (default all), dk, dv [B, G, len(kv_blocks), block_size, D] for
+    the key blocks `kv_blocks` (default all blocks, then reshaped to
+    [B, G, S, D])).  dk and dv of a block sum the contributions of every
+    query whose selection holds it.
+    """
+    B, S, Hq, D = q.shape
+    G = k.shape[1]
+    r = Hq // G
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    nb = -(-S // block_size)
+    all_blocks = kv_blocks is None
+    blocks = np.arange(nb) if all_blocks else np.asarray(kv_blocks)
+    rows = np.arange(S) if rows is None else np.asarray(rows)
+    row_pos = {int(t): i for i, t in enumerate(rows)}
+    blk_pos = {int(j): i for i, j in enumerate(blocks)}
+    dq = np.zeros((B, len(rows), Hq, D), dtype=np.float64)
+    dkb = np.zeros((B, G, len(blocks), block_size, D), dtype=np.float64)
+    dvb = np.zeros_like(dkb)
+    for b in range(B):
+        for g in range(G):
+            hs = slice(g * r, (g + 1) * r)
+            for t in range(S):
+                kept = [int(j) for j in sel[b, g, t] if j >= 0]
+                if t not in row_pos and not any(j in blk_pos for j in kept):
+                    continue
+                keys = selected_keys(sel[b, g, t], t, block_size, S)
+                gq, gk, gv = _query_grads(q[b, t, hs].astype(np.float64), k[b, g, keys].astype(np.float64),
+                                          v[b, g, keys].astype(np.float64), dout[b, t, hs].astype(np.float64),
+                                          scale)
+                if t in row_pos:
+                    dq[b, row_pos[t], hs] = gq
+                for i, key in enumerate(keys):
+                    j = int(key) // block_size
+                    if j in blk_pos:
+                        dkb[b, g, blk_pos[j], int(key) % block_size] += gk[i]
+                        dvb[b, g, blk_pos[j], int(key) % block_size] += gv[i]
+    if all_blocks:
+        dkb = dkb.reshape(B, G, nb * block_size, D)[:, :, :S]
+        dvb = dvb.reshape(B, G, nb * block_size, D)[:, :, :S]
+    return dq, dkb, dvb
+
+
+# --------------------------------------------------------------------------
 # output rounding used by the comparison
 # --------------------------------------------------------------------------
 

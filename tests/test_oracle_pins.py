@@ -285,6 +285,142 @@ def test_decode_equals_last_prefill_row():
     np.testing.assert_allclose(dout, out[:, 0], rtol=0, atol=1e-13)
 
 
+# ---------------------------------------------------------------- backward
+
+def _sel_mask(sel, S, bs):
+    """Attend mask [G, S, S] implied by a selection (built here, not by the
+    oracle): keys of the kept blocks that are not after the query."""
+    G = sel.shape[1]
+    mask = torch.zeros(G, S, S, dtype=torch.bool)
+    for g in range(G):
+        for t in range(S):
+            for j in sel[0, g, t]:
+                if j >= 0:
+                    mask[g, t, j * bs:(j + 1) * bs] = True
+    return mask & torch.ones(S, S, dtype=torch.bool).tril()
+
+
+def _autograd_grads(q, k, v, dout, mask):
+    """dq, dk, dv of sum(dout * attention) by torch autograd in fp64 (B = 1),
+    attention written as softmax of masked scores times v, per group."""
+    S, Hq, D = q.shape[1:]
+    G = k.shape[1]
+    r = Hq // G
+    q = q.clone().requires_grad_(True)
+    k = k.clone().requires_grad_(True)
+    v = v.clone().requires_grad_(True)
+    outs = []
+    for g in range(G):
+        z = torch.einsum("shd,kd->hsk", q[0, :, g * r:(g + 1) * r], k[0, g]) / math.sqrt(D)
+        z = z.masked_fill(~mask[g][None], float("-inf"))
+        outs.append(torch.einsum("hsk,kd->shd", torch.softmax(z, dim=-1), v[0, g]))
+    o = torch.cat(outs, dim=1)[None]
+    (o * dout).sum().backward()
+    return q.grad.numpy(), k.grad.numpy(), v.grad.numpy()
+
+
+def _bwd_case(seed, S, bs, G, r, D, top_k, di=8):
+    q, k, v = _rand_attention_inputs(seed, 1, S, G * r, G, D)
+    dout = torch.randn(1, S, G * r, D, generator=torch.Generator().manual_seed(seed + 1), dtype=torch.float64)
+    rng = _rng(seed)
+    q_idx = rng.integers(-64, 64, size=(1, G, S, di), dtype=np.int8)
+    k_idx = rng.integers(-64, 64, size=(1, G, S, di), dtype=np.int8)
+    _, sel, _ = O.prefill(q.numpy(), k.numpy(), v.numpy(), q_idx, k_idx, bs, top_k)
+    return q, k, v, dout, sel
+
+
+def test_backward_equals_dense_sdpa_autograd_when_all_blocks_selected():
+    """With every earlier block kept the gradients are those of dense causal
+    GQA attention: torch's own attention, differentiated by autograd."""
+    S, bs, G, r, D = 40, 8, 2, 2, 16
+    q, k, v, dout, sel = _bwd_case(31, S, bs, G, r, D, top_k=5)
+    dq, dk, dv = O.backward(q.numpy(), k.numpy(), v.numpy(), dout.numpy(), sel, bs)
+    qq, kk, vv = (x.clone().requires_grad_(True) for x in (q, k, v))
+    o = torch.nn.functional.scaled_dot_product_attention(
+        qq.permute(0, 2, 1, 3), kk.repeat_interleave(r, dim=1), vv.repeat_interleave(r, dim=1), is_causal=True)
+    (o.permute(0, 2, 1, 3) * dout).sum().backward()
+    np.testing.assert_allclose(dq, qq.grad.numpy(), rtol=0, atol=1e-10)
+    np.testing.assert_allclose(dk, kk.grad.numpy(), rtol=0, atol=1e-10)
+    np.testing.assert_allclose(dv, vv.grad.numpy(), rtol=0, atol=1e-10)
+
+
+@pytest.mark.parametrize("S,bs,G,r,top_k", [(96, 8, 2, 4, 4), (61, 16, 1, 8, 2), (50, 8, 2, 1, 1)])
+def test_backward_sparse_matches_masked_autograd(S, bs, G, r, top_k):
+    q, k, v, dout, sel = _bwd_case(S + top_k, S, bs, G, r, 16, top_k)
+    dq, dk, dv = O.backward(q.numpy(), k.numpy(), v.numpy(), dout.numpy(), sel, bs)
+    rq, rk, rv = _autograd_grads(q, k, v, dout, _sel_mask(sel, S, bs))
+    np.testing.assert_allclose(dq, rq, rtol=0, atol=1e-10)
+    np.testing.assert_allclose(dk, rk, rtol=0, atol=1e-10)
+    np.testing.assert_allclose(dv, rv, rtol=0, atol=1e-10)
+
+
+def test_backward_finite_differences():
+    """Central differences of sum(dout * O) through the oracle's own forward,
+    on every input element of a tiny case."""
+    S, bs, G, r, D, top_k = 12, 4, 1, 2, 4, 2
+    q, k, v, dout, sel = _bwd_case(7, S, bs, G, r, D, top_k)
+    q, k, v, dout = (x.numpy() for x in (q, k, v, dout))
+    dq, dk, dv = O.backward(q, k, v, dout, sel, bs)
+
+    def loss(qx, kx, vx):
+        return float((O.attention_rows(qx, kx, vx, sel, np.arange(S), bs) * dout).sum())
+
+    h = 1e-6
+    for which, x, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = [q, k, v]
+            args_m = [q, k, v]
+            pos = "qkv".index(which)
+            args_p[pos], args_m[pos] = xp, xm
+            num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        np.testing.assert_allclose(grad, num, rtol=0, atol=1e-7)
+
+
+def test_backward_sums_over_keys():
+    """Closed forms: the softmax weights of a row sum to 1, so the dv rows of
+    a group sum to the dout rows of its heads; the score gradients of a row
+    sum to 0, so the dk rows of a group sum to 0."""
+    S, bs, G, r, D, top_k = 80, 8, 2, 4, 8, 3
+    q, k, v, dout, sel = _bwd_case(17, S, bs, G, r, D, top_k)
+    _, dk, dv = O.backward(q.numpy(), k.numpy(), v.numpy(), dout.numpy(), sel, bs)
+    d = dout.numpy()
+    for g in range(G):
+        np.testing.assert_allclose(dv[0, g].sum(axis=0), d[0, :, g * r:(g + 1) * r].sum(axis=(0, 1)), atol=1e-10)
+        np.testing.assert_allclose(dk[0, g].sum(axis=0), 0.0, atol=1e-10)
+
+
+def test_backward_rows_and_blocks_subsets():
+    """Restricting the rows or the key blocks returns the same values."""
+    S, bs, G, r, D, top_k = 72, 8, 2, 2, 8, 3
+    q, k, v, dout, sel = _bwd_case(23, S, bs, G, r, D, top_k)
+    q, k, v, dout = (x.numpy() for x in (q, k, v, dout))
+    dq, dk, dv = O.backward(q, k, v, dout, sel, bs)
+    rows, blocks = [0, 9, 40, 71], [0, 4, 8]
+    sq, sk, sv = O.backward(q, k, v, dout, sel, bs, rows=rows, kv_blocks=blocks)
+    np.testing.assert_array_equal(sq, dq[:, rows])
+    for i, j in enumerate(blocks):
+        np.testing.assert_allclose(sk[:, :, i], dk[:, :, j * bs:(j + 1) * bs], rtol=0, atol=1e-14)
+        np.testing.assert_allclose(sv[:, :, i], dv[:, :, j * bs:(j + 1) * bs], rtol=0, atol=1e-14)
+
+
+def test_lse_against_torch_logsumexp():
+    S, bs, G, r, D, top_k = 64, 8, 2, 2, 16, 3
+    q, k, v, dout, sel = _bwd_case(41, S, bs, G, r, D, top_k)
+    lse = O.lse_rows(q.numpy(), k.numpy(), v.numpy(), sel, np.arange(S), bs)
+    mask = _sel_mask(sel, S, bs)
+    for g in range(G):
+        z = torch.einsum("shd,kd->hsk", q[0, :, g * r:(g + 1) * r], k[0, g]) / math.sqrt(D)
+        ref = torch.logsumexp(z.masked_fill(~mask[g][None], float("-inf")), dim=-1).T.numpy()
+        np.testing.assert_allclose(lse[0, :, g * r:(g + 1) * r], ref, rtol=0, atol=1e-12)
+    # the first query sees only key 0
+    np.testing.assert_allclose(lse[0, 0], [q[0, 0, h].dot(k[0, h // r, 0]).item() / math.sqrt(D) for h in range(G * r)],
+                               atol=1e-12)
+
+
 # ---------------------------------------------------------------- bf16 rounding
 
 def test_round_to_bf16_matches_torch_on_fp32_values():
