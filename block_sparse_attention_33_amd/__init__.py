@@ -15,11 +15,11 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import MSA_OP_DECODE, MSA_OP_INDEX, MSA_OP_POOL, MSA_OP_PREFILL, MsaDims  # noqa: F401
+from ._lib import MSA_OP_BACKWARD, MSA_OP_DECODE, MSA_OP_INDEX, MSA_OP_POOL, MSA_OP_PREFILL, MsaDims  # noqa: F401
 
 __all__ = [
     "MsaError", "make_dims", "profile_enable", "profile_read", "msa_workspace_bytes", "msa_pool_block_keys", "msa_index_select",
-    "msa_prefill", "msa_prefill_chunk", "msa_decode", "msa_decode_init", "msa_decode_step", "MSA_OP_POOL", "MSA_OP_INDEX", "MSA_OP_PREFILL", "MSA_OP_DECODE",
+    "msa_prefill", "msa_prefill_lse", "msa_prefill_backward", "msa_prefill_chunk", "msa_decode", "msa_decode_init", "msa_decode_step", "MSA_OP_POOL", "MSA_OP_INDEX", "MSA_OP_PREFILL", "MSA_OP_DECODE", "MSA_OP_BACKWARD",
 ]
 
 
@@ -161,6 +161,65 @@ def msa_prefill(q, k, v, q_idx, k_idx, block_size: int, top_k: int, softmax_scal
     _check(_lib.load().msa_prefill(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(q_idx), _ptr(k_idx),
                                    _ptr(out), _ptr(sel), _ptr(ws), ws_bytes, _stream(dev)), "msa_prefill")
     return (out, sel) if return_sel else out
+
+
+def msa_prefill_lse(q, k, v, q_idx, k_idx, block_size: int, top_k: int, softmax_scale: float = 0.0,
+                    workspace=None):
+    """Prefill for training -> (out [B, S, Hq, D] bf16, sel [B, G, S, top_k]
+    int32, lse [B, S, Hq] fp32: natural log-sum-exp of each row's scaled
+    scores)."""
+    _need(q, "q", torch.bfloat16, 4)
+    dev = q.device
+    _need(k, "k", torch.bfloat16, 4, dev)
+    _need(v, "v", torch.bfloat16, 4, dev)
+    _need(q_idx, "q_idx", torch.int8, 4, dev)
+    _need(k_idx, "k_idx", torch.int8, 4, dev)
+    B, S, Hq, D = q.shape
+    G = k.shape[1]
+    if k.shape != (B, G, S, D) or v.shape != k.shape:
+        raise ValueError(f"k/v must be [B, G, S, D] = {(B, G, S, D)}")
+    if q_idx.shape[:3] != (B, G, S) or k_idx.shape != q_idx.shape:
+        raise ValueError("q_idx/k_idx must be [B, G, S, di]")
+    dims = make_dims(B, S, Hq, G, block_size, top_k, head_dim=D, idx_dim=q_idx.shape[3],
+                     softmax_scale=softmax_scale)
+    out = torch.empty_like(q)
+    sel = torch.empty((B, G, S, top_k), dtype=torch.int32, device=dev)
+    lse = torch.empty((B, S, Hq), dtype=torch.float32, device=dev)
+    ws, ws_bytes = _workspace(MSA_OP_PREFILL, dims, dev, workspace)
+    _check(_lib.load().msa_prefill_lse(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(q_idx), _ptr(k_idx),
+                                       _ptr(out), _ptr(sel), _ptr(lse), _ptr(ws), ws_bytes, _stream(dev)),
+           "msa_prefill_lse")
+    return out, sel, lse
+
+
+def msa_prefill_backward(q, k, v, out, dout, lse, sel, block_size: int, softmax_scale: float = 0.0,
+                         workspace=None):
+    """Gradients of the main branch with the selection fixed -> (dq [B, S, Hq, D],
+    dk [B, G, S, D], dv [B, G, S, D]) bf16, from the forward's out, lse and sel."""
+    _need(q, "q", torch.bfloat16, 4)
+    dev = q.device
+    B, S, Hq, D = q.shape
+    _need(k, "k", torch.bfloat16, 4, dev)
+    _need(v, "v", torch.bfloat16, 4, dev)
+    _need(out, "out", torch.bfloat16, 4, dev)
+    _need(dout, "dout", torch.bfloat16, 4, dev)
+    _need(lse, "lse", torch.float32, 3, dev)
+    _need(sel, "sel", torch.int32, 4, dev)
+    G = k.shape[1]
+    top_k = sel.shape[3]
+    if k.shape != (B, G, S, D) or v.shape != k.shape:
+        raise ValueError(f"k/v must be [B, G, S, D] = {(B, G, S, D)}")
+    if out.shape != q.shape or dout.shape != q.shape or lse.shape != (B, S, Hq) or sel.shape[:3] != (B, G, S):
+        raise ValueError("out/dout must be [B, S, Hq, D], lse [B, S, Hq], sel [B, G, S, top_k]")
+    dims = make_dims(B, S, Hq, G, block_size, top_k, head_dim=D, softmax_scale=softmax_scale)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    ws, ws_bytes = _workspace(MSA_OP_BACKWARD, dims, dev, workspace)
+    _check(_lib.load().msa_prefill_backward(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout),
+                                            _ptr(lse), _ptr(sel), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws_bytes,
+                                            _stream(dev)), "msa_prefill_backward")
+    return dq, dk, dv
 
 
 def msa_decode(q, q_idx, k_cache, v_cache, block_keys, block_size: int, top_k: int,

@@ -14,6 +14,7 @@ MSA_OP_POOL = 0
 MSA_OP_INDEX = 1
 MSA_OP_PREFILL = 2
 MSA_OP_DECODE = 3
+MSA_OP_BACKWARD = 4
 
 
 class MsaDims(ctypes.Structure):
@@ -47,6 +48,9 @@ SIGNATURES = {
     "msa_index_select": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "msa_prefill": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "msa_decode": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "msa_prefill_lse": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "msa_prefill_backward": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                                            _P]),
     "msa_prefill_chunk_workspace_bytes": (ctypes.c_int, [_DIMS, ctypes.c_int32, _SIZE_P, _SIZE_P]),
     "msa_prefill_chunk": (ctypes.c_int, [_DIMS, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                          ctypes.c_size_t, _P]),

@@ -1,0 +1,459 @@
+// MSA main branch, backward: gradients of the attention output with respect
+// to q, k and v, the block selection held fixed.
+//
+// The index branch is integer arithmetic and carries no gradient; the pages
+// report trained MSA models (wiki.500nian.com digest of "MiniMax M3 Review",
+// the ablation paragraph; devpress.csdn.net article, section
+// "M3的技术局限与改进方向", third limitation, on the training cost) but print no
+// backward, so this is the chain rule of the forward -- one softmax over the
+// attended keys of the kept blocks -- with P rebuilt from the forward's
+// log-sum-exp.  The loop order is the forward's: the KV block outside, the
+// query rows that selected it gathered inward (yunpan.plus article on
+// MiniMax M3, the paragraph on the operator level), which is also the order
+// that lets dK and dV of a block stay in registers until the block is done.
+//
+//   bwd_delta_kernel  delta[row] = sum_d dO[row][d] O[row][d] in fp32.
+//   bwd_kv_kernel     one workgroup per CSR row (unit, KV block j), the
+//                     block's keys split over BS / 32 waves of 32 keys (K and
+//                     V rows of a wave's keys held in registers; dK^T and
+//                     dV^T accumulated there over every gathered row).  Per
+//                     chunk of 32 gathered query rows (tokens x heads of the
+//                     group), staged in LDS as rows and as transposes:
+//                       S = Q K^T, P = exp2(S c2 - lse2) (0 past the query),
+//                       dP = dO V^T, dS = P (dP - delta),
+//                       dV^T += dO^T P, dK^T += Q^T dS;
+//                     dS then goes through LDS and every wave forms
+//                     dQ^T = K^T dS^T for its share of the head dims, stored
+//                     as one bf16 partial per (query row, selection slot).
+//   bwd_dq_kernel     dq = scale * sum of a query row's partials.
+//
+// MFMA shapes (v_mfma_f32_32x32x16_bf16, wave64): an operand element e of a
+// lane in half hf of the contraction over query rows stands for row
+// 16 h2 + 8 (e / 4) + 4 hf + e % 4 of k-step h2 -- the rows that the S / dP
+// accumulators hold in their elements 8 h2 .. 8 h2 + 7 -- so P and dS feed
+// the next products straight from registers, and the Q^T / dO^T reads pick
+// the same rows.
+
+#include "msa_device.h"
+#include "msa_kernels.h"
+
+namespace msa {
+namespace {
+
+constexpr int kChunkRows = 32;                       // gathered query rows per chunk
+constexpr int kNatStride = 2 * kHeadDim + 16;        // bytes per row of Q / dO in LDS
+constexpr int kTrStride = 2 * kChunkRows + 8;        // bytes per head-dim row of Q^T / dO^T
+
+template <int BS>
+struct BwdLds {
+  static constexpr int kKtStride = 2 * BS + 16;  // bytes per head-dim row of K^T
+  static constexpr int kDsStride = 2 * BS + 16;  // bytes per query row of dS
+  static constexpr int kQn = 0;
+  static constexpr int kDn = kQn + kChunkRows * kNatStride;
+  static constexpr int kQt = kDn + kChunkRows * kNatStride;
+  static constexpr int kDt = kQt + kHeadDim * kTrStride;
+  static constexpr int kInfo = kDt + kHeadDim * kTrStride;  // lse2[32], delta[32], lim[32], entry[32]
+  static constexpr int kDs = kInfo + 4 * kChunkRows * 4;
+  static constexpr int kKt = kDs + kChunkRows * kDsStride;
+  static constexpr int kBytes = kKt + kHeadDim * kKtStride;
+};
+
+// One chunk's gathered rows on their way to LDS: NT threads, each holding
+// jobs (row pair p, head dims 8 c .. 8 c + 7) of Q and dO, plus (threads
+// 0 .. 31) one row's lse2, delta, visible-key limit and CSR entry.
+template <int NT>
+struct RowStage {
+  static constexpr int kJobs = 16 * 16 / NT;
+  u32x4_t qa[kJobs], qb[kJobs], da[kJobs], db[kJobs];
+  float lse2, delta;
+  int lim;
+  uint32_t ent;
+};
+
+// CSR entries of the rows a thread stages for chunk cc (clamped to the row's
+// last entry past its end).
+template <int NT>
+struct RowEnts {
+  uint32_t e[RowStage<NT>::kJobs][2];
+  uint32_t info;
+};
+
+__device__ __forceinline__ u32x4_t tr_frag(const char* base, int d, int h2, int hf) {
+  const char* p = base + d * kTrStride + 2 * (16 * h2 + 4 * hf);
+  const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(p);
+  const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(p + 16);
+  return u32x4_t{lo.x, lo.y, hi.x, hi.y};
+}
+
+template <int BS>
+__global__ __launch_bounds__(2 * BS, 1) void bwd_kv_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
+    const int32_t* __restrict__ row_ptr, const uint32_t* __restrict__ entries, uint16_t* __restrict__ dk,
+    uint16_t* __restrict__ dv, uint16_t* __restrict__ part_dq, BwdShape sh) {
+  constexpr int NW = BS / 32;
+  constexpr int NT = 64 * NW;
+  constexpr int DT = 4 / NW;  // head-dim tiles of dQ per wave
+  using L = BwdLds<BS>;
+  using Stage = RowStage<NT>;
+  extern __shared__ __align__(16) char lds[];
+
+  // blocks in ascending order, the units of one block side by side: early
+  // blocks are kept by more queries, so the longest rows start first
+  const int u = blockIdx.x % sh.U;
+  const int j = blockIdx.x / sh.U;
+  const int b = u / sh.G;
+  const int g = u - b * sh.G;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int hf = lane >> 5;
+  const int crow = u * sh.nb + j;
+  const int e0 = row_ptr[crow];
+  const int n = row_ptr[crow + 1] - e0;
+  const int n_keys = min(BS, sh.S - j * BS);
+  const int tpc = kChunkRows >> sh.r_log2;  // tokens per chunk
+  const int n_chunks = (n + tpc - 1) / tpc;
+  const float c2 = sh.scale_log2;
+  const size_t kv_base = ((size_t)u * sh.S + (size_t)j * BS) * kHeadDim;
+
+  // ---- the wave's K and V rows (B operands: key = lane % 32, head dims
+  // 16 ks + 8 hf .. + 7), K^T of the whole block into LDS
+  u32x4_t kb[8], vb[8];
+  {
+    const int key = min(32 * w + (lane & 31), n_keys - 1);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      kb[ks] = *reinterpret_cast<const u32x4_t*>(k + kv_base + (size_t)key * kHeadDim + 16 * ks + 8 * hf);
+      vb[ks] = *reinterpret_cast<const u32x4_t*>(v + kv_base + (size_t)key * kHeadDim + 16 * ks + 8 * hf);
+    }
+    constexpr int kKJobs = 8 * BS / NT;  // (key pair, 8 head dims) jobs per thread
+#pragma unroll
+    for (int m = 0; m < kKJobs; ++m) {
+      const int qid = tid + NT * m;
+      const int p = qid >> 4;
+      const int c = qid & 15;
+      const u32x4_t a =
+          *reinterpret_cast<const u32x4_t*>(k + kv_base + (size_t)min(2 * p, n_keys - 1) * kHeadDim + 8 * c);
+      const u32x4_t bb =
+          *reinterpret_cast<const u32x4_t*>(k + kv_base + (size_t)min(2 * p + 1, n_keys - 1) * kHeadDim + 8 * c);
+      char* kt = lds + L::kKt;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        *reinterpret_cast<uint32_t*>(kt + (8 * c + 2 * e) * L::kKtStride + 4 * p) = (a[e] & 0xffffu) | (bb[e] << 16);
+        *reinterpret_cast<uint32_t*>(kt + (8 * c + 2 * e + 1) * L::kKtStride + 4 * p) =
+            (a[e] >> 16) | (bb[e] & 0xffff0000u);
+      }
+    }
+  }
+
+  f32x16_t dkt[4], dvt[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    dkt[dt] = f32x16_t{};
+    dvt[dt] = f32x16_t{};
+  }
+
+  // entries of chunk cc for this thread's rows
+  auto load_ents = [&](int cc, RowEnts<NT>& re) {
+#pragma unroll
+    for (int m = 0; m < Stage::kJobs; ++m) {
+      const int p = (tid + NT * m) >> 4;
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int tk = cc * tpc + ((2 * p + x) >> sh.r_log2);
+        re.e[m][x] = entries[e0 + min(tk, n - 1)];
+      }
+    }
+    re.info = entries[e0 + min(cc * tpc + ((tid & 31) >> sh.r_log2), n - 1)];
+  };
+  auto row_ptr_q = [&](const uint16_t* base, uint32_t ent, int rho) -> const uint16_t* {
+    const int t = (int)(ent >> 5);
+    return base + (((size_t)b * sh.S + t) * sh.Hq + g * sh.r + (rho & (sh.r - 1))) * kHeadDim;
+  };
+  auto load_rows = [&](int cc, const RowEnts<NT>& re, Stage& st) {
+#pragma unroll
+    for (int m = 0; m < Stage::kJobs; ++m) {
+      const int qid = tid + NT * m;
+      const int p = qid >> 4;
+      const int c = qid & 15;
+      st.qa[m] = *reinterpret_cast<const u32x4_t*>(row_ptr_q(q, re.e[m][0], 2 * p) + 8 * c);
+      st.qb[m] = *reinterpret_cast<const u32x4_t*>(row_ptr_q(q, re.e[m][1], 2 * p + 1) + 8 * c);
+      st.da[m] = *reinterpret_cast<const u32x4_t*>(row_ptr_q(dout, re.e[m][0], 2 * p) + 8 * c);
+      st.db[m] = *reinterpret_cast<const u32x4_t*>(row_ptr_q(dout, re.e[m][1], 2 * p + 1) + 8 * c);
+    }
+    // row info: threads 0 .. 31, row = tid (other threads load a copy)
+    const int rho = tid & 31;
+    const int tk = cc * tpc + (rho >> sh.r_log2);
+    const bool valid = tk < n;
+    const int t = (int)(re.info >> 5);
+    const size_t ri = ((size_t)b * sh.S + t) * sh.Hq + g * sh.r + (rho & (sh.r - 1));
+    const float l2 = lse[ri] * kLog2e;
+    st.lse2 = valid ? l2 : __builtin_inff();
+    st.delta = delta[ri];
+    st.lim = t - j * BS;
+    st.ent = valid ? re.info : 0xffffffffu;
+  };
+  auto store_rows = [&](const Stage& st) {
+#pragma unroll
+    for (int m = 0; m < Stage::kJobs; ++m) {
+      const int qid = tid + NT * m;
+      const int p = qid >> 4;
+      const int c = qid & 15;
+      *reinterpret_cast<u32x4_t*>(lds + L::kQn + (2 * p) * kNatStride + 16 * c) = st.qa[m];
+      *reinterpret_cast<u32x4_t*>(lds + L::kQn + (2 * p + 1) * kNatStride + 16 * c) = st.qb[m];
+      *reinterpret_cast<u32x4_t*>(lds + L::kDn + (2 * p) * kNatStride + 16 * c) = st.da[m];
+      *reinterpret_cast<u32x4_t*>(lds + L::kDn + (2 * p + 1) * kNatStride + 16 * c) = st.db[m];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        char* qt = lds + L::kQt;
+        char* dt = lds + L::kDt;
+        *reinterpret_cast<uint32_t*>(qt + (8 * c + 2 * e) * kTrStride + 4 * p) =
+            (st.qa[m][e] & 0xffffu) | (st.qb[m][e] << 16);
+        *reinterpret_cast<uint32_t*>(qt + (8 * c + 2 * e + 1) * kTrStride + 4 * p) =
+            (st.qa[m][e] >> 16) | (st.qb[m][e] & 0xffff0000u);
+        *reinterpret_cast<uint32_t*>(dt + (8 * c + 2 * e) * kTrStride + 4 * p) =
+            (st.da[m][e] & 0xffffu) | (st.db[m][e] << 16);
+        *reinterpret_cast<uint32_t*>(dt + (8 * c + 2 * e + 1) * kTrStride + 4 * p) =
+            (st.da[m][e] >> 16) | (st.db[m][e] & 0xffff0000u);
+      }
+    }
+    if (tid < kChunkRows) {
+      reinterpret_cast<float*>(lds + L::kInfo)[tid] = st.lse2;
+      reinterpret_cast<float*>(lds + L::kInfo + 128)[tid] = st.delta;
+      reinterpret_cast<int*>(lds + L::kInfo + 256)[tid] = st.lim;
+      reinterpret_cast<uint32_t*>(lds + L::kInfo + 384)[tid] = st.ent;
+    }
+  };
+
+  RowEnts<NT> ent_next, ent_after;
+  Stage stage;
+  if (n_chunks > 0) {
+    load_ents(0, ent_next);
+    load_rows(0, ent_next, stage);
+    load_ents(1, ent_next);
+    store_rows(stage);
+  }
+  __syncthreads();
+
+  const int key = 32 * w + (lane & 31);  // this lane's key within the block (S / dP columns)
+  for (int c = 0; c < n_chunks; ++c) {
+    const bool more = c + 1 < n_chunks;
+    if (more) {
+      load_ents(c + 2, ent_after);
+      load_rows(c + 1, ent_next, stage);
+    }
+    // ---- S = Q K^T and dP = dO V^T for the wave's 32 keys
+    f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const u32x4_t aq = *reinterpret_cast<const u32x4_t*>(lds + L::kQn + (lane & 31) * kNatStride + 32 * ks + 16 * hf);
+      const u32x4_t ad = *reinterpret_cast<const u32x4_t*>(lds + L::kDn + (lane & 31) * kNatStride + 32 * ks + 16 * hf);
+      s = mfma32x32x16(aq, kb[ks], s);
+      dp = mfma32x32x16(ad, vb[ks], dp);
+    }
+    // ---- P and dS; element i is query row c_row(i, hf), column = key
+    float pv[16], dsv[16];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int r0 = 8 * q4 + 4 * hf;
+      const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(lds + L::kInfo + 4 * r0);
+      const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(lds + L::kInfo + 128 + 4 * r0);
+      const i32x4_t m4 = *reinterpret_cast<const i32x4_t*>(lds + L::kInfo + 256 + 4 * r0);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int i = 4 * q4 + x;
+        const float p = key <= m4[x] ? fast_exp2(fmaf(s[i], c2, -l4[x])) : 0.f;
+        pv[i] = p;
+        dsv[i] = p * (dp[i] - d4[x]);
+      }
+    }
+    const uint32_t my_ent = reinterpret_cast<const uint32_t*>(lds + L::kInfo + 384)[lane & 31];
+    u32x4_t ph[2], dsh[2];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      ph[h2] = u32x4_t{pack_bf16x2(pv[8 * h2], pv[8 * h2 + 1]), pack_bf16x2(pv[8 * h2 + 2], pv[8 * h2 + 3]),
+                       pack_bf16x2(pv[8 * h2 + 4], pv[8 * h2 + 5]), pack_bf16x2(pv[8 * h2 + 6], pv[8 * h2 + 7])};
+      dsh[h2] = u32x4_t{pack_bf16x2(dsv[8 * h2], dsv[8 * h2 + 1]), pack_bf16x2(dsv[8 * h2 + 2], dsv[8 * h2 + 3]),
+                        pack_bf16x2(dsv[8 * h2 + 4], dsv[8 * h2 + 5]), pack_bf16x2(dsv[8 * h2 + 6], dsv[8 * h2 + 7])};
+    }
+    // ---- dV^T += dO^T P, dK^T += Q^T dS (head dims x the wave's keys)
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int d = 32 * dt + (lane & 31);
+        dvt[dt] = mfma32x32x16(tr_frag(lds + L::kDt, d, h2, hf), ph[h2], dvt[dt]);
+        dkt[dt] = mfma32x32x16(tr_frag(lds + L::kQt, d, h2, hf), dsh[h2], dkt[dt]);
+      }
+    // ---- dS (bf16, as used above) -> LDS, rows x keys
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t pair = dsh[h2][e];
+        const int i = 8 * h2 + 2 * e;
+        *reinterpret_cast<uint16_t*>(lds + L::kDs + c_row(i, hf) * L::kDsStride + 2 * key) = (uint16_t)(pair & 0xffffu);
+        *reinterpret_cast<uint16_t*>(lds + L::kDs + c_row(i + 1, hf) * L::kDsStride + 2 * key) = (uint16_t)(pair >> 16);
+      }
+    __syncthreads();
+    // the staged rows of the next chunk replace this one's (every read of
+    // them is above the barrier)
+    if (more) {
+      store_rows(stage);
+      ent_next = ent_after;
+    }
+    // ---- dQ^T = K^T dS^T for head-dim tiles DT w .. DT w + DT - 1
+#pragma unroll
+    for (int dd = 0; dd < DT; ++dd) {
+      const int dt = DT * w + dd;
+      f32x16_t acc = f32x16_t{};
+#pragma unroll
+      for (int ks = 0; ks < BS / 16; ++ks) {
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(lds + L::kKt + (32 * dt + (lane & 31)) * L::kKtStride +
+                                                            32 * ks + 16 * hf);
+        const u32x4_t bq =
+            *reinterpret_cast<const u32x4_t*>(lds + L::kDs + (lane & 31) * L::kDsStride + 32 * ks + 16 * hf);
+        acc = mfma32x32x16(a, bq, acc);
+      }
+      if (my_ent != 0xffffffffu) {
+        const int t = (int)(my_ent >> 5);
+        const int slot = (int)(my_ent & 31u);
+        uint16_t* dst = part_dq + ((((size_t)u * sh.S + t) * sh.top_k + slot) * sh.r + ((lane & 31) & (sh.r - 1))) *
+                                      kHeadDim + 32 * dt + 4 * hf;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          u32x2_t wv;
+          wv.x = pack_bf16x2(acc[4 * q4], acc[4 * q4 + 1]);
+          wv.y = pack_bf16x2(acc[4 * q4 + 2], acc[4 * q4 + 3]);
+          *reinterpret_cast<u32x2_t*>(dst + 8 * q4) = wv;
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- dK = scale * dK^T^T, dV: this lane's key, head dims 32 dt + 8 q4 + 4 hf + 0..3
+  if (key < n_keys) {
+    uint16_t* dkr = dk + kv_base + (size_t)key * kHeadDim;
+    uint16_t* dvr = dv + kv_base + (size_t)key * kHeadDim;
+    const float sc = sh.scale;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = 32 * dt + 8 * q4 + 4 * hf;
+        u32x2_t a, bq;
+        a.x = pack_bf16x2(dkt[dt][4 * q4] * sc, dkt[dt][4 * q4 + 1] * sc);
+        a.y = pack_bf16x2(dkt[dt][4 * q4 + 2] * sc, dkt[dt][4 * q4 + 3] * sc);
+        bq.x = pack_bf16x2(dvt[dt][4 * q4], dvt[dt][4 * q4 + 1]);
+        bq.y = pack_bf16x2(dvt[dt][4 * q4 + 2], dvt[dt][4 * q4 + 3]);
+        *reinterpret_cast<u32x2_t*>(dkr + d0) = a;
+        *reinterpret_cast<u32x2_t*>(dvr + d0) = bq;
+      }
+  }
+}
+
+// delta of every row: 16 threads per row, 8 head dims each.
+__global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restrict__ out,
+                                                        const uint16_t* __restrict__ dout,
+                                                        float* __restrict__ delta, long rows) {
+  const long gid = (long)blockIdx.x * 256 + threadIdx.x;
+  const long row = gid >> 4;
+  const int c16 = (int)(gid & 15);
+  // a row's 16 threads are all in range or all out of it
+  if (row >= rows) return;
+  const u32x4_t o = *reinterpret_cast<const u32x4_t*>(out + row * kHeadDim + 8 * c16);
+  const u32x4_t d = *reinterpret_cast<const u32x4_t*>(dout + row * kHeadDim + 8 * c16);
+  float acc = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    acc = fmaf(bf16_lo(o[e]), bf16_lo(d[e]), acc);
+    acc = fmaf(bf16_hi(o[e]), bf16_hi(d[e]), acc);
+  }
+#pragma unroll
+  for (int x = 1; x < 16; x <<= 1) acc += __shfl_xor(acc, x);
+  if (c16 == 0) delta[row] = acc;
+}
+
+// dq of every row: 16 threads per (token, head), 8 head dims each, summing
+// the row's min(top_k - 1, own block) + 1 partials.
+__global__ __launch_bounds__(256) void bwd_dq_kernel(const uint16_t* __restrict__ part_dq, uint16_t* __restrict__ dq,
+                                                     BwdShape sh) {
+  const long gid = (long)blockIdx.x * 256 + threadIdx.x;
+  const int c16 = (int)(gid & 15);
+  const long qr = gid >> 4;
+  const int h = (int)(qr & (sh.r - 1));
+  const long t = qr >> sh.r_log2;
+  if (t >= sh.S) return;
+  const int u = blockIdx.y;
+  const int b = u / sh.G;
+  const int g = u - b * sh.G;
+  const int n = min(sh.top_k - 1, (int)(t >> sh.bs_log2)) + 1;
+  const uint16_t* src = part_dq + (((size_t)u * sh.S + t) * sh.top_k * sh.r + h) * kHeadDim + 8 * c16;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < n; s0 += 8) {
+    u32x4_t val[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      if (s0 + s < n) val[s] = *reinterpret_cast<const u32x4_t*>(src + (size_t)(s0 + s) * sh.r * kHeadDim);
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      if (s0 + s < n)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += bf16_lo(val[s][e]);
+          acc[2 * e + 1] += bf16_hi(val[s][e]);
+        }
+  }
+  const float sc = sh.scale;
+  u32x4_t wv = {pack_bf16x2(acc[0] * sc, acc[1] * sc), pack_bf16x2(acc[2] * sc, acc[3] * sc),
+                pack_bf16x2(acc[4] * sc, acc[5] * sc), pack_bf16x2(acc[6] * sc, acc[7] * sc)};
+  *reinterpret_cast<u32x4_t*>(dq + (((size_t)b * sh.S + t) * sh.Hq + g * sh.r + h) * kHeadDim + 8 * c16) = wv;
+}
+
+template <int BS>
+hipError_t launch_bwd_kv_bs(const BwdShape& sh, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                            const uint16_t* dout, const float* lse, const float* delta, const int32_t* row_ptr,
+                            const uint32_t* entries, uint16_t* dk, uint16_t* dv, uint16_t* part_dq,
+                            hipStream_t st) {
+  constexpr int bytes = BwdLds<BS>::kBytes;
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_kv_kernel<BS>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(bwd_kv_kernel<BS>, dim3((unsigned)(sh.U * sh.nb)), dim3(2 * BS), bytes, st, q, k, v, dout, lse,
+                     delta, row_ptr, entries, dk, dv, part_dq, sh);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_delta(const uint16_t* out, const uint16_t* dout, float* delta, long rows, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  const long threads = rows * 16;
+  hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, out, dout, delta,
+                     rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_kv(const BwdShape& sh, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                         const uint16_t* dout, const float* lse, const float* delta, const int32_t* row_ptr,
+                         const uint32_t* entries, uint16_t* dk, uint16_t* dv, uint16_t* part_dq, hipStream_t st) {
+  switch (sh.bs) {
+    case 32:
+      return launch_bwd_kv_bs<32>(sh, q, k, v, dout, lse, delta, row_ptr, entries, dk, dv, part_dq, st);
+    case 64:
+      return launch_bwd_kv_bs<64>(sh, q, k, v, dout, lse, delta, row_ptr, entries, dk, dv, part_dq, st);
+    default:
+      return launch_bwd_kv_bs<128>(sh, q, k, v, dout, lse, delta, row_ptr, entries, dk, dv, part_dq, st);
+  }
+}
+
+hipError_t launch_bwd_dq(const BwdShape& sh, const uint16_t* part_dq, uint16_t* dq, hipStream_t st) {
+  const long threads = (long)sh.S * sh.r * 16;
+  hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)((threads + 255) / 256), (unsigned)sh.U), dim3(256), 0, st, part_dq,
+                     dq, sh);
+  return hipGetLastError();
+}
+
+}  // namespace msa

@@ -488,9 +488,12 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(
           // o / l with a sum of 1: the merge then reproduces it exactly, so
           // the row is rounded to bf16 once, as every other row
           const bool single = ((sh.q0 + tok[ct]) >> sh.bs_log2) == 0 || K == 1;
+          // (its max then carries log2 l, so that the merge's log-sum-exp
+          // is the row's)
           u32x4_t pv1[8];
           pack_tile(o, single ? 1.0f / l : 1.0f, pv1);
-          store_row(pv1, make_float2(m2, single ? 1.0f : l), pidx[ct], hf, part_o, part_ml);
+          store_row(pv1, make_float2(single ? m2 + fast_log2(l) : m2, single ? 1.0f : l), pidx[ct], hf, part_o,
+                    part_ml);
         }
       }
       qb = qb_nx;
@@ -563,6 +566,8 @@ __global__ __launch_bounds__(256) void merge_kernel(const uint16_t* __restrict__
     }
   }
   const float inv = 1.0f / W;
+  if (sh.lse != nullptr && c16 == 0)
+    sh.lse[((size_t)b * sh.q_stride + t) * sh.Hq + g * sh.r + h] = (M + fast_log2(W)) * 0.6931471805599453f;
   // stored positions 8 * c16 .. + 7 = lane half hf, tile dt, i0 .. i0 + 7
   const int p0 = 8 * c16;
   const int hfp = p0 >> 6, dt = (p0 >> 4) & 3, i0 = p0 & 15;
@@ -752,6 +757,9 @@ __global__ __launch_bounds__(512 / NCT, 1) void dense_kernel(const uint16_t* __r
   for (int ct = 0; ct < NCT; ++ct) {
     if (tok[ct] >= sh.S) continue;
     const float inv = 1.0f / l[ct];
+    if (sh.lse != nullptr && hf == 0)
+      sh.lse[((size_t)b * sh.q_stride + tok[ct]) * sh.Hq + g * sh.r + head[ct]] =
+          (m[ct] + fast_log2(l[ct])) * 0.6931471805599453f;
     uint16_t* orow = out + (((size_t)b * sh.q_stride + tok[ct]) * sh.Hq + g * sh.r + head[ct]) * kHeadDim;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)

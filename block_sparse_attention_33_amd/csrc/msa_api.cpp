@@ -279,7 +279,7 @@ long prefill_query_chunk(const Dims& d) { return d.S > kPrefillQueryChunk ? kPre
 // null to pool every block into the workspace.
 int run_prefill(const Dims& dc, long q0, long n_q, long q_stride, const uint16_t* q, const uint16_t* k,
                 const uint16_t* v, const int8_t* q_idx, const int8_t* k_idx, int8_t* ext_keys, uint16_t* out,
-                int32_t* sel, void* ws, size_t ws_bytes, hipStream_t s) {
+                int32_t* sel, float* lse, void* ws, size_t ws_bytes, hipStream_t s) {
   const Dims d = chunk_dims(dc, n_q);
   const PrefillPlan P = plan_prefill(d);
   int st;
@@ -346,6 +346,7 @@ int run_prefill(const Dims& dc, long q0, long n_q, long q_stride, const uint16_t
   sh.q0 = iq0;
   sh.q_stride = (int)q_stride;
   sh.kv_rows = (int)dc.S;
+  sh.lse = lse;
   auto run_pass = [&](long u0, long u1) -> int {
     msa::PassInfo ps;
     ps.u0 = (int)u0;
@@ -370,6 +371,73 @@ int run_prefill(const Dims& dc, long q0, long n_q, long q_stride, const uint16_t
 }
 
 
+// Backward workspace: delta, the inversion of sel (as in a whole prefill)
+// and the bf16 dq partials of every (query row, selection slot).
+struct BackwardLayout {
+  size_t delta, counts, hist, row_ptr, item_ptr, entries, items, part_dq, total;
+};
+
+BackwardLayout backward_layout(const Dims& d, const PrefillPlan& p) {
+  BackwardLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align_up(bytes);
+    return at;
+  };
+  L.delta = take((size_t)d.B * d.S * d.Hq * 4);
+  L.counts = take((size_t)p.rows * 4);
+  L.hist = take((size_t)d.U * p.n_chunks * d.nb * 4);
+  L.row_ptr = take((size_t)(p.rows + 1) * 4);
+  L.item_ptr = take((size_t)(p.rows + 1) * 4);
+  L.entries = take((size_t)d.U * d.S * d.k * 4);
+  L.items = take((size_t)(d.U * p.n_ranges * p.max_items_per_range + 1) * 8);
+  L.part_dq = take((size_t)d.U * d.S * d.k * d.r * d.D * 2);
+  L.total = off;
+  return L;
+}
+
+// Whole prefill (msa_prefill, msa_prefill_lse), arguments checked.
+int prefill_impl(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v, const int8_t* q_idx,
+                 const int8_t* k_idx, uint16_t* out, int32_t* sel, float* lse, void* ws, size_t ws_bytes,
+                 hipStream_t s) {
+  if (d.nb > msa::kMaxInvertBlocks) return MSA_ERR_UNSUPPORTED;
+  if (d.k >= d.nb) {
+    // top_k covers every block: each query keeps all earlier blocks and its
+    // own, which is plain causal attention (no index branch, no partials)
+    msa::PrefillShape sh{};
+    sh.B = (int)d.B;
+    sh.S = (int)d.S;
+    sh.Hq = (int)d.Hq;
+    sh.G = (int)d.G;
+    sh.r = (int)d.r;
+    sh.bs = (int)d.bs;
+    sh.bs_log2 = bs_log2_of(d.bs);
+    sh.nb = (int)d.nb;
+    sh.top_k = (int)d.k;
+    sh.q0 = 0;
+    sh.q_stride = (int)d.S;
+    sh.kv_rows = (int)d.S;
+    sh.scale_log2 = d.scale * 1.4426950408889634f;
+    sh.lse = lse;
+    MSA_LAUNCH_NAMED("dense", s, msa::launch_dense(sh, q, k, v, out, sel, s));
+    return MSA_OK;
+  }
+  const long T = prefill_query_chunk(d);
+  if (T >= d.S) return run_prefill(d, 0, d.S, d.S, q, k, v, q_idx, k_idx, nullptr, out, sel, lse, ws, ws_bytes, s);
+  // query chunks of T tokens; the summaries persist in the workspace's first
+  // region (block_keys, which every layout places at offset 0)
+  int8_t* keys = static_cast<int8_t*>(ws);
+  for (long q0 = 0; q0 < d.S; q0 += T) {
+    const long n = std::min(T, d.S - q0);
+    const int st2 = run_prefill(d, q0, n, d.S, q + q0 * d.Hq * d.D, k, v, q_idx + q0 * d.di, k_idx, keys,
+                                out + q0 * d.Hq * d.D, sel ? sel + q0 * d.k : nullptr,
+                                lse ? lse + q0 * d.Hq : nullptr, ws, ws_bytes, s);
+    if (st2 != MSA_OK) return st2;
+  }
+  return MSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -391,7 +459,7 @@ const char* msa_status_string(int status) {
   }
 }
 
-int msa_version(void) { return 10100; }
+int msa_version(void) { return 10200; }
 
 int msa_workspace_bytes(int op, const msa_dims* dims, size_t* min_bytes, size_t* full_bytes) {
   Dims d;
@@ -411,6 +479,11 @@ int msa_workspace_bytes(int op, const msa_dims* dims, size_t* min_bytes, size_t*
       const PrefillPlan p = plan_prefill(dq);
       lo = prefill_layout(dq, p, 1).total;
       hi = prefill_layout(dq, p, dq.U).total;
+      break;
+    }
+    case MSA_OP_BACKWARD: {
+      if (d.k > kMaxSparseTopK || d.nb > msa::kMaxInvertBlocks) return MSA_ERR_UNSUPPORTED;
+      lo = hi = backward_layout(d, plan_prefill(d)).total;
       break;
     }
     case MSA_OP_DECODE: {
@@ -461,41 +534,76 @@ int msa_prefill(const msa_dims* dims, const uint16_t* q, const uint16_t* k, cons
   int st = check_dims(dims, &d);
   if (st != MSA_OK) return st;
   if (!q || !k || !v || !q_idx || !k_idx || !out) return MSA_ERR_INVALID_ARG;
+  return prefill_impl(d, q, k, v, q_idx, k_idx, out, sel, nullptr, ws, ws_bytes, (hipStream_t)stream);
+}
+
+int msa_prefill_lse(const msa_dims* dims, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                    const int8_t* q_idx, const int8_t* k_idx, uint16_t* out, int32_t* sel, float* lse, void* ws,
+                    size_t ws_bytes, void* stream) {
+  Dims d;
+  int st = check_dims(dims, &d);
+  if (st != MSA_OK) return st;
+  if (!q || !k || !v || !q_idx || !k_idx || !out || !lse) return MSA_ERR_INVALID_ARG;
+  return prefill_impl(d, q, k, v, q_idx, k_idx, out, sel, lse, ws, ws_bytes, (hipStream_t)stream);
+}
+
+int msa_prefill_backward(const msa_dims* dims, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                         const uint16_t* out, const uint16_t* dout, const float* lse, const int32_t* sel,
+                         uint16_t* dq, uint16_t* dk, uint16_t* dv, void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  int st = check_dims(dims, &d);
+  if (st != MSA_OK) return st;
+  if (d.k > kMaxSparseTopK) return MSA_ERR_UNSUPPORTED;
   if (d.nb > msa::kMaxInvertBlocks) return MSA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !out || !dout || !lse || !sel || !dq || !dk || !dv) return MSA_ERR_INVALID_ARG;
+  const PrefillPlan P = plan_prefill(d);
+  const BackwardLayout L = backward_layout(d, P);
+  st = check_ws(ws, ws_bytes, L.total);
+  if (st != MSA_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  if (d.k >= d.nb) {
-    // top_k covers every block: each query keeps all earlier blocks and its
-    // own, which is plain causal attention (no index branch, no partials)
-    msa::PrefillShape sh{};
-    sh.B = (int)d.B;
-    sh.S = (int)d.S;
-    sh.Hq = (int)d.Hq;
-    sh.G = (int)d.G;
-    sh.r = (int)d.r;
-    sh.bs = (int)d.bs;
-    sh.bs_log2 = bs_log2_of(d.bs);
-    sh.nb = (int)d.nb;
-    sh.top_k = (int)d.k;
-    sh.q0 = 0;
-    sh.q_stride = (int)d.S;
-    sh.kv_rows = (int)d.S;
-    sh.scale_log2 = d.scale * 1.4426950408889634f;
-    MSA_LAUNCH_NAMED("dense", s, msa::launch_dense(sh, q, k, v, out, sel, s));
-    return MSA_OK;
-  }
-  const long T = prefill_query_chunk(d);
-  if (T >= d.S) return run_prefill(d, 0, d.S, d.S, q, k, v, q_idx, k_idx, nullptr, out, sel, ws, ws_bytes, s);
-  // query chunks of T tokens; the summaries persist in the workspace's first
-  // region (block_keys, which every layout places at offset 0)
-  int8_t* keys = static_cast<int8_t*>(ws);
-  for (long q0 = 0; q0 < d.S; q0 += T) {
-    const long n = std::min(T, d.S - q0);
-    const int st2 = run_prefill(d, q0, n, d.S, q + q0 * d.Hq * d.D, k, v, q_idx + q0 * d.di, k_idx, keys,
-                                out + q0 * d.Hq * d.D, sel ? sel + q0 * d.k : nullptr, ws, ws_bytes, s);
-    if (st2 != MSA_OK) return st2;
-  }
+  char* base = static_cast<char*>(ws);
+  float* delta = reinterpret_cast<float*>(base + L.delta);
+  int32_t* counts = reinterpret_cast<int32_t*>(base + L.counts);
+  int32_t* hist = reinterpret_cast<int32_t*>(base + L.hist);
+  int32_t* row_ptr = reinterpret_cast<int32_t*>(base + L.row_ptr);
+  int32_t* item_ptr = reinterpret_cast<int32_t*>(base + L.item_ptr);
+  uint32_t* entries = reinterpret_cast<uint32_t*>(base + L.entries);
+  int2* items = reinterpret_cast<int2*>(base + L.items);
+  uint16_t* part_dq = reinterpret_cast<uint16_t*>(base + L.part_dq);
+  const int U = (int)d.U, S = (int)d.S, bs = (int)d.bs, nb = (int)d.nb, K = (int)d.k;
+  msa::ChunkPlan cp;
+  cp.T = (int)P.T;
+  cp.m = (int)P.m;
+  cp.tpc = (int)P.tpc;
+  cp.n_chunks = (int)P.n_chunks;
+  cp.n_ranges = (int)P.n_ranges;
+  cp.q_stride = S;
+  const int tpi = (int)P.tokens_per_item;
+  MSA_LAUNCH_NAMED("bwd_delta", s, msa::launch_bwd_delta(out, dout, delta, d.B * d.S * d.Hq, s));
+  MSA_LAUNCH_NAMED("chunk_hist", s, msa::launch_chunk_hist(sel, hist, U, S, nb, bs, K, cp, 0, s));
+  MSA_LAUNCH_NAMED("chunk_total", s, msa::launch_chunk_total(hist, counts, U, nb, cp, s));
+  MSA_LAUNCH_NAMED("scan", s, msa::launch_scan(counts, row_ptr, item_ptr, (int)P.rows, tpi, s));
+  MSA_LAUNCH_NAMED("offsets_items", s, msa::launch_offsets_items(hist, row_ptr, item_ptr, items, U, nb, cp, tpi, s));
+  MSA_LAUNCH_NAMED("scatter", s, msa::launch_scatter(sel, hist, entries, U, S, nb, bs, K, cp, 0, s));
+  msa::BwdShape sh;
+  sh.B = (int)d.B;
+  sh.S = S;
+  sh.Hq = (int)d.Hq;
+  sh.G = (int)d.G;
+  sh.r = (int)d.r;
+  sh.r_log2 = bs_log2_of(d.r);
+  sh.bs = bs;
+  sh.bs_log2 = bs_log2_of(bs);
+  sh.nb = nb;
+  sh.top_k = K;
+  sh.U = U;
+  sh.scale = d.scale;
+  sh.scale_log2 = d.scale * 1.4426950408889634f;
+  MSA_LAUNCH_NAMED("bwd_kv", s, msa::launch_bwd_kv(sh, q, k, v, dout, lse, delta, row_ptr, entries, dk, dv, part_dq, s));
+  MSA_LAUNCH_NAMED("bwd_dq", s, msa::launch_bwd_dq(sh, part_dq, dq, s));
   return MSA_OK;
 }
+
 
 int msa_prefill_chunk_workspace_bytes(const msa_dims* dims, int32_t count, size_t* min_bytes, size_t* full_bytes) {
   Dims d;
@@ -523,8 +631,8 @@ int msa_prefill_chunk(const msa_dims* dims, int32_t start, int32_t count, const 
   if (!q || !q_idx || !k_cache || !v_cache || !k_idx || !block_keys || !out) return MSA_ERR_INVALID_ARG;
   if (start < 0 || count < 1 || (long)start + count > d.S) return MSA_ERR_INVALID_ARG;
   if (d.nb > msa::kMaxInvertBlocks) return MSA_ERR_UNSUPPORTED;
-  return run_prefill(d, start, count, count, q, k_cache, v_cache, q_idx, k_idx, block_keys, out, sel, ws, ws_bytes,
-                     (hipStream_t)stream);
+  return run_prefill(d, start, count, count, q, k_cache, v_cache, q_idx, k_idx, block_keys, out, sel, nullptr, ws,
+                     ws_bytes, (hipStream_t)stream);
 }
 
 int msa_decode(const msa_dims* dims, const uint16_t* q, const int8_t* q_idx, const uint16_t* k_cache,

@@ -21,6 +21,7 @@ struct PrefillShape {
   int n_ranges;      // query ranges per unit: CSR rows are (unit, range, block)
   int range_tokens;  // tokens per query range
   float scale_log2;  // softmax scale * log2(e)
+  float* lse;        // [B, q_stride, Hq] natural log-sum-exp of each row's scores, or null
 };
 
 // One pass of the main branch: units [u0, u1) x query range `rng` (always
@@ -101,6 +102,23 @@ hipError_t launch_dense(const PrefillShape& sh, const uint16_t* q, const uint16_
 // Merge of every partial of the pass's query rows -> out.
 hipError_t launch_merge(const PrefillShape& sh, const PassInfo& pass, const uint16_t* part_o,
                         const float2* part_ml, uint16_t* out, hipStream_t st);
+
+// Backward of the main branch (selection fixed).
+struct BwdShape {
+  int B, S, Hq, G, r, r_log2, bs, bs_log2, nb, top_k, U;
+  float scale, scale_log2;
+};
+// delta[row] = sum_d dout[row][d] * out[row][d] (fp32) for rows of 128 dims.
+hipError_t launch_bwd_delta(const uint16_t* out, const uint16_t* dout, float* delta, long rows, hipStream_t st);
+// One workgroup per CSR row (unit, block), rows (u, j) with j-major order:
+// dk, dv [U, S, 128] of the block's keys and the bf16 dq partials
+// part_dq [U, S, top_k, r, 128] of every (query row, slot) of the row.
+// lse [B, S, Hq] natural log-sum-exp of the forward, delta as above.
+hipError_t launch_bwd_kv(const BwdShape& sh, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                         const uint16_t* dout, const float* lse, const float* delta, const int32_t* row_ptr,
+                         const uint32_t* entries, uint16_t* dk, uint16_t* dv, uint16_t* part_dq, hipStream_t st);
+// dq [B, S, Hq, 128] = scale * sum of each row's partials.
+hipError_t launch_bwd_dq(const BwdShape& sh, const uint16_t* part_dq, uint16_t* dq, hipStream_t st);
 
 // Decode.
 struct DecodeShape {

@@ -86,6 +86,7 @@ extern "C" {
 #define MSA_OP_INDEX 1
 #define MSA_OP_PREFILL 2
 #define MSA_OP_DECODE 3
+#define MSA_OP_BACKWARD 4
 
 typedef struct msa_dims {
   int32_t batch;        /* B */
@@ -137,6 +138,35 @@ int msa_index_select(const msa_dims* dims, const int8_t* q_idx, const int8_t* k_
 int msa_prefill(const msa_dims* dims, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                 const int8_t* q_idx, const int8_t* k_idx, uint16_t* out, int32_t* sel, void* ws,
                 size_t ws_bytes, void* stream);
+
+/* Whole prefill for training: msa_prefill, plus lse [B, S, Hq] fp32 (required),
+ * the natural log-sum-exp of each query row's scaled scores over the keys it
+ * attends to, log sum_key exp(softmax_scale * q . k) -- what the backward
+ * pass rebuilds the attention weights from.  Same workspace as msa_prefill. */
+int msa_prefill_lse(const msa_dims* dims, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                    const int8_t* q_idx, const int8_t* k_idx, uint16_t* out, int32_t* sel, float* lse,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of the main branch with the selection held fixed (the index
+ * branch is integer arithmetic and has no gradient).  The pages report
+ * trained MSA models and their training cost (wiki.500nian.com digest of
+ * "MiniMax M3 Review", the ablation paragraph; devpress.csdn.net article,
+ * section "M3的技术局限与改进方向", third limitation) without a backward
+ * formula; this is the chain rule of the forward's single softmax:
+ *   P = exp(scale q.k - lse) over the attended keys, dP = dout . v,
+ *   dS = P (dP - sum_d dout * out),
+ *   dq = scale dS k, dk = scale dS^T q, dv = P^T dout.
+ * Inputs: q, out, dout [B, S, Hq, D] bf16; k, v [B, G, S, D] bf16; lse
+ * [B, S, Hq] fp32 and sel [B, G, S, top_k] int32 exactly as msa_prefill_lse
+ * wrote them (sel must be a valid selection: ascending kept blocks, the own
+ * block included, -1 padding).  Outputs dq [B, S, Hq, D], dk, dv [B, G, S, D]
+ * bf16, every element written.  top_k <= 32.  ws/ws_bytes: at least
+ * msa_workspace_bytes(MSA_OP_BACKWARD) (it holds one bf16 partial of dq per
+ * (query row, kept block): B * Hq * S * top_k * D * 2 bytes and the
+ * inversion of sel). */
+int msa_prefill_backward(const msa_dims* dims, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                         const uint16_t* out, const uint16_t* dout, const float* lse, const int32_t* sel,
+                         uint16_t* dq, uint16_t* dk, uint16_t* dv, void* ws, size_t ws_bytes, void* stream);
 
 /* Chunked prefill against a cache.  Here dims->seq_len is the capacity C
  * of the caches: k_cache/v_cache [B, G, C, D] bf16 and k_idx [B, G, C, di]

@@ -230,7 +230,7 @@ def _query_grads(qh, ks, vs, doh, scale):
     return scale * (dz @ ks), scale * (dz.T @ qh), w.T @ doh
 
 
-def backward(q, k, v, dout, sel, block_size: int, scale=None, rows=None, kv_blocks=None):
+def backward(q, k, v, dout, sel, block_size: int, scale=None, rows=None, kv_blocks=None, groups=None):
     """Gradients of sum(dout * O) with respect to q, k and v, O being the
     main-branch output of every query row and the selection sel
     [B, G, S, top_k] held fixed.
@@ -240,7 +240,8 @@ def backward(q, k, v, dout, sel, block_size: int, scale=None, rows=None, kv_bloc
     `rows` (default all), dk, dv [B, G, len(kv_blocks), block_size, D] for
     the key blocks `kv_blocks` (default all blocks, then reshaped to
     [B, G, S, D])).  dk and dv of a block sum the contributions of every
-    query whose selection holds it.
+    query whose selection holds it.  `groups` (default all) limits the work
+    to those GQA groups; the other groups' entries stay zero.
     """
     B, S, Hq, D = q.shape
     G = k.shape[1]
@@ -256,7 +257,7 @@ def backward(q, k, v, dout, sel, block_size: int, scale=None, rows=None, kv_bloc
     dkb = np.zeros((B, G, len(blocks), block_size, D), dtype=np.float64)
     dvb = np.zeros_like(dkb)
     for b in range(B):
-        for g in range(G):
+        for g in (range(G) if groups is None else groups):
             hs = slice(g * r, (g + 1) * r)
             for t in range(S):
                 kept = [int(j) for j in sel[b, g, t] if j >= 0]

@@ -8,6 +8,7 @@ consume what it produces.
 from .configs import WORKLOADS, Workload, get_workload  # noqa: F401
 from .gen import (  # noqa: F401
     decode_inputs,
+    grad_output,
     prefill_inputs,
     sample_rows,
     seed_for,

@@ -84,6 +84,17 @@ def prefill_inputs(w: Workload, seed: int = 0, device="cpu", seq_len=None, batch
     return {"q": q, "k": k, "v": v, "q_idx": q_idx, "k_idx": k_idx}
 
 
+def grad_output(w: Workload, seed: int = 0, device="cpu", seq_len=None, batch=None):
+    """dout [B, S, Hq, D] bf16 ~ N(0, 1): the gradient arriving at the
+    attention output in a backward pass."""
+    B = batch if batch is not None else w.batch
+    S = seq_len if seq_len is not None else w.seq_len
+    dev = torch.device(device)
+    dout = torch.empty((B, S, w.n_q_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+    _fill_token_major(dout, "dout", seed, dev, "normal", 1)
+    return dout
+
+
 def hot_blocks(w: Workload, seed: int, b: int, g: int, n_blocks: int):
     """Indices of the planted hot blocks of (b, g) (sorted)."""
     n_hot = max(1, int(round(w.hot_fraction * n_blocks)))

@@ -32,7 +32,8 @@ def test_header_declares_the_boundary():
     names = _declared()
     for n in ["msa_index_select", "msa_prefill", "msa_decode", "msa_workspace_bytes",
               "msa_pool_block_keys", "msa_status_string", "msa_version", "msa_decode_init",
-              "msa_decode_step", "msa_prefill_chunk", "msa_prefill_chunk_workspace_bytes"]:
+              "msa_decode_step", "msa_prefill_chunk", "msa_prefill_chunk_workspace_bytes", "msa_prefill_lse",
+              "msa_prefill_backward"]:
         assert n in names
 
 
@@ -47,7 +48,7 @@ def test_status_strings(lib):
                          (-3, "MSA_ERR_WORKSPACE"), (-4, "MSA_ERR_HIP")]:
         assert lib.msa_status_string(code).decode().startswith(prefix)
     assert lib.msa_status_string(12345).decode() == "unknown MSA status"
-    assert lib.msa_version() == 10100
+    assert lib.msa_version() == 10200
 
 
 def D(**kw):
@@ -154,6 +155,31 @@ def test_prefill_chunk_validation(lib):
         assert lib.msa_prefill_chunk(ctypes.byref(dims), 0, 1024, *args, None, FAKE, hi.value, None) == -1
     assert lib.msa_prefill_chunk(ctypes.byref(dims), 0, 1024, *([FAKE] * 7), None, FAKE, lo.value - 1,
                                  None) == -3
+
+
+def test_backward_validation(lib):
+    """Training path: msa_prefill_lse needs its lse output; the backward
+    needs every tensor, a workspace of its documented size (one bf16 dq
+    partial per (query row, kept block) and head), and top_k <= 32."""
+    dims = D(batch=2, seq_len=3000, top_k=8)
+    for i in range(7):
+        args = [FAKE] * 7
+        args[i] = None
+        assert lib.msa_prefill_lse(ctypes.byref(dims), *args[:6], None, args[6], FAKE, 1 << 40, None) == -1
+    st, lo, hi = _ws(lib, _lib.MSA_OP_BACKWARD, dims)
+    assert st == 0 and lo == hi
+    part = 2 * 64 * 3000 * 8 * 128 * 2          # B * Hq * S * top_k * D * bf16
+    assert part < lo < part + 2 * 3000 * 64 * 4 + 40 * 2 * 8 * 3000 * 8 + (1 << 20)
+    for i in range(10):
+        args = [FAKE] * 10
+        args[i] = None
+        assert lib.msa_prefill_backward(ctypes.byref(dims), *args, FAKE, lo, None) == -1
+    assert lib.msa_prefill_backward(ctypes.byref(dims), *([FAKE] * 10), FAKE, lo - 1, None) == -3
+    assert lib.msa_prefill_backward(ctypes.byref(dims), *([FAKE] * 10), ctypes.c_void_p(0x1008), lo, None) == -3
+    assert lib.msa_prefill_backward(ctypes.byref(dims), *([FAKE] * 10), None, 0, None) == -3
+    big_k = D(seq_len=4096, top_k=64)            # dense forward, but no sparse backward
+    assert _ws(lib, _lib.MSA_OP_BACKWARD, big_k)[0] == -2
+    assert lib.msa_prefill_backward(ctypes.byref(big_k), *([FAKE] * 10), FAKE, 1 << 40, None) == -2
 
 
 def test_workspace_errors(lib):

@@ -1,0 +1,164 @@
+"""GPU parity of the training path: msa_prefill_lse (forward + log-sum-exp)
+and msa_prefill_backward (dq, dk, dv with the selection fixed) against the
+CPU oracle.
+
+The log-sum-exp is fp32 arithmetic on bf16 inputs: within 1e-3 of the
+oracle's fp64 value.  A gradient element is a bf16-rounded sum whose terms
+each pass through bf16 rounding (relative error <= 2^-9) two or three more
+times than the forward's do: P or dS as an MFMA operand, the per-block dq
+partial, and delta taken from the bf16 output.  So the error is a few 2^-9
+of the terms' magnitude, and the comparison is relative to the gradient's
+own scale, per tensor:
+  max |gpu - bf16(oracle)|  <= 1.5e-2 (about 8 * 2^-9) * max |oracle|
+  mean |gpu - bf16(oracle)| <= 5e-3 (about 2.5 * 2^-9) * mean |oracle|.
+"""
+import gc
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_33_amd as msa
+from oracle import msa_oracle as O
+from synth import get_workload, grad_output, prefill_inputs, sample_rows
+from tests.helpers import host_f32, host_i8
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+LSE_ABS = 1e-3
+GRAD_MAX_REL = 1.5e-2
+GRAD_MEAN_REL = 5e-3
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _free():
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def compare_grad(gpu_bf16, oracle_f64, what):
+    g = host_f32(gpu_bf16).astype(np.float64)
+    ref = O.round_to_bf16(oracle_f64)
+    assert g.shape == ref.shape, (g.shape, ref.shape)
+    assert np.isfinite(g).all(), f"{what}: non-finite GPU gradient"
+    d = np.abs(g - ref)
+    scale_max, scale_mean = float(np.abs(ref).max()), float(np.abs(ref).mean())
+    max_rel, mean_rel = float(d.max()) / scale_max, float(d.mean()) / scale_mean
+    _say(f"  {what}: max_rel={max_rel:.2e} mean_rel={mean_rel:.2e} (max|ref|={scale_max:.3g})")
+    assert max_rel <= GRAD_MAX_REL and mean_rel <= GRAD_MEAN_REL, (
+        f"{what}: max|err|/max|ref| = {max_rel:.3e} (<= {GRAD_MAX_REL}), mean|err|/mean|ref| = {mean_rel:.3e} "
+        f"(<= {GRAD_MEAN_REL}), worst at {np.unravel_index(int(d.argmax()), d.shape)}")
+
+
+def _forward_backward(inp, dout, bs, top_k):
+    out, sel, lse = msa.msa_prefill_lse(inp["q"], inp["k"], inp["v"], inp["q_idx"], inp["k_idx"], bs, top_k)
+    dq, dk, dv = msa.msa_prefill_backward(inp["q"], inp["k"], inp["v"], out, dout, lse, sel, bs)
+    torch.cuda.synchronize()
+    return out, sel, lse, dq, dk, dv
+
+
+# ------------------------------------------------------------------ small cases, every element
+
+SMALL = [
+    # name, workload overrides, seq_len
+    ("tiny_2k", {}, None),
+    ("ragged_gqa4_bs64", dict(n_q_heads=8, n_kv_heads=2, block_size=64, top_k=5), 1000),
+    ("batch2_r1_bs32", dict(batch=2, n_q_heads=2, n_kv_heads=2, block_size=32, top_k=4), 600),
+    ("r16_bs128", dict(n_q_heads=16, n_kv_heads=1, block_size=128, top_k=3), 777),
+    ("topk1_own_only", dict(n_q_heads=8, n_kv_heads=1, top_k=1), 700),
+    ("dense_sel_bs64", dict(n_q_heads=8, n_kv_heads=2, block_size=64, top_k=32), 1100),
+    ("single_block", dict(n_q_heads=8, n_kv_heads=1, block_size=128, top_k=4), 100),
+    ("r2_bs64_k2", dict(n_q_heads=4, n_kv_heads=2, block_size=64, top_k=2), 513),
+]
+
+
+@pytest.mark.parametrize("name,over,S", SMALL, ids=[c[0] for c in SMALL])
+def test_prefill_lse_small(name, over, S):
+    w = get_workload("tiny_2k", **over)
+    _say(f"[lse small] {name} S={S or w.seq_len}")
+    inp = prefill_inputs(w, seed=5, device="cpu", seq_len=S)
+    dinp = {k: v.to(DEV) for k, v in inp.items()}
+    out, sel, lse = msa.msa_prefill_lse(dinp["q"], dinp["k"], dinp["v"], dinp["q_idx"], dinp["k_idx"],
+                                        w.block_size, w.top_k)
+    ref_out = msa.msa_prefill(dinp["q"], dinp["k"], dinp["v"], dinp["q_idx"], dinp["k_idx"], w.block_size, w.top_k)
+    torch.cuda.synchronize()
+    # the log-sum-exp output changes nothing else
+    assert torch.equal(out, ref_out), f"{name}: msa_prefill_lse output differs from msa_prefill"
+    Sn = inp["q"].shape[1]
+    rows = np.arange(Sn)
+    summ = O.pool_block_keys(inp["k_idx"].numpy(), w.block_size)
+    osel = O.select_blocks(inp["q_idx"].numpy(), summ, w.block_size, w.top_k, rows)
+    assert np.array_equal(host_i8(sel).astype(np.int32), osel), f"{name}: selection differs"
+    olse = O.lse_rows(host_f32(inp["q"]), host_f32(inp["k"]), host_f32(inp["v"]), osel, rows, w.block_size)
+    err = np.abs(lse.cpu().numpy().astype(np.float64) - olse)
+    assert float(err.max()) <= LSE_ABS, f"{name}: lse max_abs={err.max():.3e}"
+
+
+@pytest.mark.parametrize("name,over,S", SMALL, ids=[c[0] for c in SMALL])
+def test_backward_small_all_elements(name, over, S):
+    w = get_workload("tiny_2k", **over)
+    _say(f"[backward small] {name} S={S or w.seq_len}")
+    inp = prefill_inputs(w, seed=9, device="cpu", seq_len=S)
+    dout = grad_output(w, seed=9, device="cpu", seq_len=S)
+    dinp = {k: v.to(DEV) for k, v in inp.items()}
+    _, sel, _, dq, dk, dv = _forward_backward(dinp, dout.to(DEV), w.block_size, w.top_k)
+    Sn = inp["q"].shape[1]
+    summ = O.pool_block_keys(inp["k_idx"].numpy(), w.block_size)
+    osel = O.select_blocks(inp["q_idx"].numpy(), summ, w.block_size, w.top_k)
+    assert np.array_equal(host_i8(sel).astype(np.int32), osel), f"{name}: selection differs"
+    rq, rk, rv = O.backward(host_f32(inp["q"]), host_f32(inp["k"]), host_f32(inp["v"]), host_f32(dout), osel,
+                            w.block_size)
+    assert rq.shape == (w.batch, Sn, w.n_q_heads, 128)
+    compare_grad(dq, rq, f"{name} dq")
+    compare_grad(dk, rk, f"{name} dk")
+    compare_grad(dv, rv, f"{name} dv")
+
+
+# ------------------------------------------------------------------ full size
+
+def test_backward_32k_sampled_and_sums():
+    """Prefill 32K (64 query heads, 8 groups, block 128, top_k 16): dq on
+    sampled rows and dk, dv on sampled blocks against the oracle; over every
+    key, the closed-form sums (dv rows of a group sum to its heads' dout
+    rows, dk rows sum to 0)."""
+    w = get_workload("prefill_32k")
+    S, bs = w.seq_len, w.block_size
+    _say(f"[backward full] prefill_32k S={S}")
+    inp = prefill_inputs(w, seed=33, device=DEV)
+    dout = grad_output(w, seed=33, device=DEV)
+    _, sel, _, dq, dk, dv = _forward_backward(inp, dout, bs, w.top_k)
+    gsel = host_i8(sel).astype(np.int32)
+    del sel
+    _free()
+    # sums over every key of each group (fp64 on the host)
+    gdv = host_f32(dv).astype(np.float64)
+    gdk = host_f32(dk).astype(np.float64)
+    dsum = host_f32(dout).astype(np.float64).reshape(w.batch, S, w.n_kv_heads, -1, 128).sum(axis=(1, 3))
+    np.testing.assert_allclose(gdv.sum(axis=2), dsum, rtol=0, atol=2e-3 * np.abs(gdv).sum(axis=2).max())
+    assert np.abs(gdk.sum(axis=2)).max() <= 2e-3 * np.abs(gdk).sum(axis=2).max()
+    # oracle on samples, with its own selection of every row
+    _say("[backward full] oracle selection of every row")
+    summ = O.pool_block_keys(host_i8(inp["k_idx"]), bs)
+    osel = O.select_blocks(host_i8(inp["q_idx"]), summ, bs, w.top_k)
+    assert np.array_equal(gsel, osel), "selection differs"
+    # fp32 host copies (exact): the oracle gathers thousands of key rows per query
+    hq, hk, hv, hd = host_f32(inp["q"]), host_f32(inp["k"]), host_f32(inp["v"]), host_f32(dout)
+    rows = sample_rows(S, 32, 33)
+    _say(f"[backward full] oracle dq on {len(rows)} rows")
+    rq, _, _ = O.backward(hq, hk, hv, hd, osel, bs, rows=rows, kv_blocks=[])
+    compare_grad(dq[:, torch.as_tensor(rows, device=DEV)], rq, "32k dq (sampled rows)")
+    # an early block (kept by ~6000 queries of its group), a middle one and
+    # the last one, each in one group
+    for j, g in ((5, 3), (140, 6), (255, 0)):
+        _say(f"[backward full] oracle dk, dv of block {j}, group {g}")
+        _, rk, rv = O.backward(hq, hk, hv, hd, osel, bs, rows=[], kv_blocks=[j], groups=[g])
+        compare_grad(dk[:, g, j * bs:(j + 1) * bs], rk[:, g, 0], f"32k dk block {j} group {g}")
+        compare_grad(dv[:, g, j * bs:(j + 1) * bs], rv[:, g, 0], f"32k dv block {j} group {g}")
+    del inp, dout, dq, dk, dv
+    _free()

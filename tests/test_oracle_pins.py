@@ -402,6 +402,10 @@ def test_backward_rows_and_blocks_subsets():
     rows, blocks = [0, 9, 40, 71], [0, 4, 8]
     sq, sk, sv = O.backward(q, k, v, dout, sel, bs, rows=rows, kv_blocks=blocks)
     np.testing.assert_array_equal(sq, dq[:, rows])
+    gq, gk, gv = O.backward(q, k, v, dout, sel, bs, rows=rows, kv_blocks=blocks, groups=[1])
+    np.testing.assert_array_equal(gq[:, :, r:], sq[:, :, r:])
+    np.testing.assert_array_equal(gk[:, 1], sk[:, 1])
+    assert not gq[:, :, :r].any() and not gk[:, 0].any() and not gv[:, 0].any()
     for i, j in enumerate(blocks):
         np.testing.assert_allclose(sk[:, :, i], dk[:, :, j * bs:(j + 1) * bs], rtol=0, atol=1e-14)
         np.testing.assert_allclose(sv[:, :, i], dv[:, :, j * bs:(j + 1) * bs], rtol=0, atol=1e-14)
