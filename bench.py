@@ -331,6 +331,7 @@ def main():
     # step alone)
     gen_med = ch_ms = dwarm_med = None
     short_ms, short_flop = {}, None
+    train_ms, bkt = {}, {}
     if not args.core_only:
         # generation step: append token L - 1 to the caches, refresh its block's
         # summary, decode (outside the timed region; same events)
@@ -403,6 +404,36 @@ def main():
             short_ms[name_] = sorted(a.elapsed_time(b) for a, b in sev)[2]
         short_flop = 4.0 * D_HEAD * ws_.n_q_heads * Ss * (Ss + 1) / 2
         del sin, sout, sws
+
+        # training step of the same 32K prefill: the forward with its
+        # log-sum-exp, then the backward (dq, dk, dv; selection fixed)
+        from synth import grad_output
+        bout, bsel, blse = msa.msa_prefill_lse(pin["q"], pin["k"], pin["v"], pin["q_idx"], pin["k_idx"],
+                                               wp.block_size, wp.top_k, workspace=pws)
+        bdout = grad_output(wp, seed=0, device=dev)
+        bws = torch.empty(msa.msa_workspace_bytes(msa.MSA_OP_BACKWARD, pdims)[1], dtype=torch.uint8, device=dev)
+        train_runs = {
+            "forward_lse": lambda: msa.msa_prefill_lse(pin["q"], pin["k"], pin["v"], pin["q_idx"], pin["k_idx"],
+                                                       wp.block_size, wp.top_k, workspace=pws),
+            "backward": lambda: msa.msa_prefill_backward(pin["q"], pin["k"], pin["v"], bout, bdout, blse, bsel,
+                                                         wp.block_size, workspace=bws),
+        }
+        for name_, fn in train_runs.items():
+            fn()
+            torch.cuda.synchronize()
+            msa.profile_read()
+            msa.profile_enable(name_ == "backward")
+            tev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+            for a, b in tev:
+                a.record()
+                fn()
+                b.record()
+            torch.cuda.synchronize()
+            msa.profile_enable(False)
+            train_ms[name_] = sorted(a.elapsed_time(b) for a, b in tev)[2]
+            if name_ == "backward":
+                bkt = msa.profile_read()
+        del bout, bsel, blse, bdout, bws
 
         # the plain decode timed the same way (back to back, so the kept blocks
         # may still sit in the memory-side cache, unlike in the step above where
@@ -480,6 +511,19 @@ def main():
             "sparse_path_ms": round(short_ms["sparse_path"], 4),
             "dense_tflops": round(short_flop / (short_ms["dense"] * 1e-3) / 1e12, 2),
             "dense_frac_bf16_peak": round(short_flop / (short_ms["dense"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        },
+        "training": None if not train_ms else {
+            "what": "the 32K prefill for training: forward with log-sum-exp, and the main-branch backward "
+                    "(dq, dk, dv; selection fixed)",
+            "forward_lse_ms": round(train_ms["forward_lse"], 4),
+            "backward_ms": round(train_ms["backward"], 4),
+            "backward_tflops_alg": round(2.5 * flop_alg / (train_ms["backward"] * 1e-3) / 1e12, 2),
+            "backward_frac_bf16_peak": round(2.5 * flop_alg / (train_ms["backward"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                                             4),
+            "backward_flop_alg": 2.5 * flop_alg,
+            "bwd_kv_tflops_alg": round(2.5 * flop_alg / (bkt["bwd_kv"][1] / bkt["bwd_kv"][0] * 1e-3) / 1e12, 2)
+            if "bwd_kv" in bkt else None,
+            "kernels": {k: {"launches": n, "avg_ms": round(ms / max(1, n), 4)} for k, (n, ms) in sorted(bkt.items())},
         },
         "decode_step": None if gen_med is None else {
             "what": "append one token per sequence (K/V rows, running index-key sum, block summary) + decode",

@@ -55,7 +55,8 @@ struct BwdLds {
   static constexpr int kInfo = kDt + kHeadDim * kTrStride;  // lse2[32], delta[32], lim[32], entry[32]
   static constexpr int kDs = kInfo + 4 * kChunkRows * 4;
   static constexpr int kKt = kDs + kChunkRows * kDsStride;
-  static constexpr int kBytes = kKt + kHeadDim * kKtStride;
+  static constexpr int kDq = kKt + kHeadDim * kKtStride;  // dq tile: rows x head dims (bf16)
+  static constexpr int kBytes = kDq + kChunkRows * kNatStride;
 };
 
 // One chunk's gathered rows on their way to LDS: NT threads, each holding
@@ -226,23 +227,32 @@ __global__ __launch_bounds__(2 * BS, 1) void bwd_kv_kernel(
     }
   };
 
-  RowEnts<NT> ent_next, ent_after;
+  // Pipeline per chunk c (one register stage, loads a full chunk ahead):
+  //   phase 1 on the LDS rows of chunk c; dS -> LDS        | barrier A
+  //   rows of chunk c + 1 (registers) -> LDS; loads of chunk c + 2
+  //   phase 2: dQ^T -> the LDS dq tile                     | barrier B
+  //   the dq tile -> part_dq, 16 bytes per thread
+  // Every wait on a load is on one issued before the previous chunk's
+  // stores (vector-memory operations complete in order), and loads and
+  // stores are issued the same way on every path: past the row's end they
+  // repeat its last entry, and their rows are masked (lse2 = +inf, no dq
+  // store).
+  constexpr int kCopyRows = kChunkRows * 16 / NT;  // dq tile rows each thread stores
+  RowEnts<NT> ent_next;
   Stage stage;
-  if (n_chunks > 0) {
+  const bool any = n_chunks > 0;
+  if (any) {
     load_ents(0, ent_next);
     load_rows(0, ent_next, stage);
-    load_ents(1, ent_next);
     store_rows(stage);
+    load_ents(1, ent_next);
+    load_rows(1, ent_next, stage);
+    load_ents(2, ent_next);
   }
   __syncthreads();
 
   const int key = 32 * w + (lane & 31);  // this lane's key within the block (S / dP columns)
   for (int c = 0; c < n_chunks; ++c) {
-    const bool more = c + 1 < n_chunks;
-    if (more) {
-      load_ents(c + 2, ent_after);
-      load_rows(c + 1, ent_next, stage);
-    }
     // ---- S = Q K^T and dP = dO V^T for the wave's 32 keys
     f32x16_t s = f32x16_t{}, dp = f32x16_t{};
 #pragma unroll
@@ -268,7 +278,11 @@ __global__ __launch_bounds__(2 * BS, 1) void bwd_kv_kernel(
         dsv[i] = p * (dp[i] - d4[x]);
       }
     }
-    const uint32_t my_ent = reinterpret_cast<const uint32_t*>(lds + L::kInfo + 384)[lane & 31];
+    // entries of the dq tile rows this thread stores after phase 2
+    uint32_t copy_ent[kCopyRows];
+#pragma unroll
+    for (int m = 0; m < kCopyRows; ++m)
+      copy_ent[m] = reinterpret_cast<const uint32_t*>(lds + L::kInfo + 384)[(tid >> 4) + (NT >> 4) * m];
     u32x4_t ph[2], dsh[2];
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
@@ -297,13 +311,13 @@ __global__ __launch_bounds__(2 * BS, 1) void bwd_kv_kernel(
         *reinterpret_cast<uint16_t*>(lds + L::kDs + c_row(i + 1, hf) * L::kDsStride + 2 * key) = (uint16_t)(pair >> 16);
       }
     __syncthreads();
-    // the staged rows of the next chunk replace this one's (every read of
-    // them is above the barrier)
-    if (more) {
-      store_rows(stage);
-      ent_next = ent_after;
-    }
-    // ---- dQ^T = K^T dS^T for head-dim tiles DT w .. DT w + DT - 1
+    // the rows of chunk c + 1 replace this chunk's (every read of them is
+    // above the barrier), then the loads of chunk c + 2
+    store_rows(stage);
+    load_rows(c + 2, ent_next, stage);
+    load_ents(c + 3, ent_next);
+    // ---- dQ^T = K^T dS^T for head-dim tiles DT w .. DT w + DT - 1, into
+    // the LDS dq tile (rows x head dims)
 #pragma unroll
     for (int dd = 0; dd < DT; ++dd) {
       const int dt = DT * w + dd;
@@ -316,21 +330,28 @@ __global__ __launch_bounds__(2 * BS, 1) void bwd_kv_kernel(
             *reinterpret_cast<const u32x4_t*>(lds + L::kDs + (lane & 31) * L::kDsStride + 32 * ks + 16 * hf);
         acc = mfma32x32x16(a, bq, acc);
       }
-      if (my_ent != 0xffffffffu) {
-        const int t = (int)(my_ent >> 5);
-        const int slot = (int)(my_ent & 31u);
-        uint16_t* dst = part_dq + ((((size_t)u * sh.S + t) * sh.top_k + slot) * sh.r + ((lane & 31) & (sh.r - 1))) *
-                                      kHeadDim + 32 * dt + 4 * hf;
+      char* dst = lds + L::kDq + (lane & 31) * kNatStride + 2 * (32 * dt + 4 * hf);
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          u32x2_t wv;
-          wv.x = pack_bf16x2(acc[4 * q4], acc[4 * q4 + 1]);
-          wv.y = pack_bf16x2(acc[4 * q4 + 2], acc[4 * q4 + 3]);
-          *reinterpret_cast<u32x2_t*>(dst + 8 * q4) = wv;
-        }
+      for (int q4 = 0; q4 < 4; ++q4) {
+        u32x2_t wv;
+        wv.x = pack_bf16x2(acc[4 * q4], acc[4 * q4 + 1]);
+        wv.y = pack_bf16x2(acc[4 * q4 + 2], acc[4 * q4 + 3]);
+        *reinterpret_cast<u32x2_t*>(dst + 16 * q4) = wv;
       }
     }
     __syncthreads();
+    // ---- the dq tile -> one bf16 partial per (row, slot): 16 threads per
+    // row, 16 bytes each
+#pragma unroll
+    for (int m = 0; m < kCopyRows; ++m) {
+      const int rho = (tid >> 4) + (NT >> 4) * m;
+      const u32x4_t val = *reinterpret_cast<const u32x4_t*>(lds + L::kDq + rho * kNatStride + 16 * (tid & 15));
+      const uint32_t e = copy_ent[m];
+      if (e != 0xffffffffu) {
+        const size_t pidx = (((size_t)u * sh.S + (e >> 5)) * sh.top_k + (e & 31u)) * sh.r + (rho & (sh.r - 1));
+        *reinterpret_cast<u32x4_t*>(part_dq + pidx * kHeadDim + 8 * (tid & 15)) = val;
+      }
+    }
   }
 
   // ---- dK = scale * dK^T^T, dV: this lane's key, head dims 32 dt + 8 q4 + 4 hf + 0..3
