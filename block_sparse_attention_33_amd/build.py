@@ -24,12 +24,17 @@ COMMON = [
     "-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
     # keep the compiler from forming packed fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # MFMA accumulators in VGPRs (the softmax reads them with VALU
-    # instructions; in AGPRs every value would first be copied out)
-    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     "-Wall", "-Wno-unused-function",
 ]
+
+# MFMA accumulators in VGPRs for the forward kernels (their softmax reads
+# every accumulator with VALU instructions; in AGPRs each value would first
+# be copied out).  The backward keeps its long-lived dK / dV accumulators in
+# AGPRs instead, which leaves the VGPRs to the K / V operands (measured 7 %
+# faster on MI355X).
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+PER_FILE = {"backward.hip": []}
 
 
 def _hipcc():
@@ -42,7 +47,7 @@ def _hipcc():
 def _compile(src):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     lang = ["-x", "hip"]
-    cmd = [_hipcc(), *lang, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *lang, *COMMON, *PER_FILE.get(src, VGPR_FORM), "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{res.stdout}\n{res.stderr}")

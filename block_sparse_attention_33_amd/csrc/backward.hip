@@ -17,8 +17,9 @@
 //                     block's keys split over BS / 32 waves of 32 keys (K and
 //                     V rows of a wave's keys held in registers; dK^T and
 //                     dV^T accumulated there over every gathered row).  Per
-//                     chunk of 32 gathered query rows (tokens x heads of the
-//                     group), staged in LDS as rows and as transposes:
+//                     chunk of 64 (128-key blocks) or 32 gathered query rows
+//                     (tokens x heads of the group), staged in LDS as rows
+//                     and as transposes:
 //                       S = Q K^T, P = exp2(S c2 - lse2) (0 past the query),
 //                       dP = dO V^T, dS = P (dP - delta),
 //                       dV^T += dO^T P, dK^T += Q^T dS;
@@ -27,12 +28,12 @@
 //                     as one bf16 partial per (query row, selection slot).
 //   bwd_dq_kernel     dq = scale * sum of a query row's partials.
 //
-// MFMA shapes (v_mfma_f32_32x32x16_bf16, wave64): an operand element e of a
-// lane in half hf of the contraction over query rows stands for row
-// 16 h2 + 8 (e / 4) + 4 hf + e % 4 of k-step h2 -- the rows that the S / dP
-// accumulators hold in their elements 8 h2 .. 8 h2 + 7 -- so P and dS feed
-// the next products straight from registers, and the Q^T / dO^T reads pick
-// the same rows.
+// MFMA shapes (v_mfma_f32_32x32x16_bf16, wave64): in the contraction over
+// query rows, operand element e of a lane in half hf stands for row
+// 32 rt + 16 h2 + 8 (e / 4) + 4 hf + e % 4 at k-step h2 of row tile rt -- the
+// rows that the S / dP accumulators of tile rt hold in their elements
+// 8 h2 .. 8 h2 + 7 -- so P and dS feed the next products straight from
+// registers, and the Q^T / dO^T reads pick the same rows.
 
 #include "msa_device.h"
 #include "msa_kernels.h"
@@ -40,19 +41,29 @@
 namespace msa {
 namespace {
 
-constexpr int kChunkRows = 32;                       // gathered query rows per chunk
-constexpr int kNatStride = 2 * kHeadDim + 16;        // bytes per row of Q / dO in LDS
-constexpr int kTrStride = 2 * kChunkRows + 8;        // bytes per head-dim row of Q^T / dO^T
+constexpr int kNatStride = 2 * kHeadDim + 16;  // bytes per row of Q / dO / the dq tile in LDS
+
+// Gathered query rows per chunk: 64 for 128-key blocks (half the barriers
+// and row bookkeeping per row; measured 6 % faster than 32 on MI355X), 32
+// for smaller blocks, whose waves hold more staged rows each.
+template <int BS>
+struct Chunk {
+  static constexpr int kRows = BS == 128 ? 64 : 32;
+  static constexpr int kRT = kRows / 32;           // 32-row tiles per chunk
+  static constexpr int kTrStride = 2 * kRows + 8;  // bytes per head-dim row of Q^T / dO^T
+};
 
 template <int BS>
 struct BwdLds {
+  static constexpr int kChunkRows = Chunk<BS>::kRows;
+  static constexpr int kTrStride = Chunk<BS>::kTrStride;
   static constexpr int kKtStride = 2 * BS + 16;  // bytes per head-dim row of K^T
   static constexpr int kDsStride = 2 * BS + 16;  // bytes per query row of dS
   static constexpr int kQn = 0;
   static constexpr int kDn = kQn + kChunkRows * kNatStride;
   static constexpr int kQt = kDn + kChunkRows * kNatStride;
   static constexpr int kDt = kQt + kHeadDim * kTrStride;
-  static constexpr int kInfo = kDt + kHeadDim * kTrStride;  // lse2[32], delta[32], lim[32], entry[32]
+  static constexpr int kInfo = kDt + kHeadDim * kTrStride;  // lse2, delta, lim, entry: kChunkRows each
   static constexpr int kDs = kInfo + 4 * kChunkRows * 4;
   static constexpr int kKt = kDs + kChunkRows * kDsStride;
   static constexpr int kDq = kKt + kHeadDim * kKtStride;  // dq tile: rows x head dims (bf16)
@@ -61,10 +72,13 @@ struct BwdLds {
 
 // One chunk's gathered rows on their way to LDS: NT threads, each holding
 // jobs (row pair p, head dims 8 c .. 8 c + 7) of Q and dO, plus (threads
-// 0 .. 31) one row's lse2, delta, visible-key limit and CSR entry.
-template <int NT>
+// 0 .. rows - 1) one row's lse2, delta, visible-key limit and CSR entry.
+// Job q is row pair (q % 16) + 16 (q / 256), dims 8 ((q / 16) % 16): the 32
+// lanes of an LDS write cycle then cover 16 row pairs of two head-dim rows
+// 8 apart, so the transposed writes hit 32 distinct banks.
+template <int NT, int CR>
 struct RowStage {
-  static constexpr int kJobs = 16 * 16 / NT;
+  static constexpr int kJobs = CR / 2 * 16 / NT;
   u32x4_t qa[kJobs], qb[kJobs], da[kJobs], db[kJobs];
   float lse2, delta;
   int lim;
@@ -73,14 +87,15 @@ struct RowStage {
 
 // CSR entries of the rows a thread stages for chunk cc (clamped to the row's
 // last entry past its end).
-template <int NT>
+template <int NT, int CR>
 struct RowEnts {
-  uint32_t e[RowStage<NT>::kJobs][2];
+  uint32_t e[RowStage<NT, CR>::kJobs][2];
   uint32_t info;
 };
 
-__device__ __forceinline__ u32x4_t tr_frag(const char* base, int d, int h2, int hf) {
-  const char* p = base + d * kTrStride + 2 * (16 * h2 + 4 * hf);
+template <int TRS>
+__device__ __forceinline__ u32x4_t tr_frag(const char* base, int d, int rt, int h2, int hf) {
+  const char* p = base + d * TRS + 2 * (32 * rt + 16 * h2 + 4 * hf);
   const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(p);
   const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(p + 16);
   return u32x4_t{lo.x, lo.y, hi.x, hi.y};
@@ -96,7 +111,11 @@ __global__ __launch_bounds__(2 * BS, 1) void bwd_kv_kernel(
   constexpr int NT = 64 * NW;
   constexpr int DT = 4 / NW;  // head-dim tiles of dQ per wave
   using L = BwdLds<BS>;
-  using Stage = RowStage<NT>;
+  constexpr int kChunkRows = Chunk<BS>::kRows;
+  constexpr int kRT = Chunk<BS>::kRT;
+  constexpr int kTrStride = Chunk<BS>::kTrStride;
+  using Stage = RowStage<NT, kChunkRows>;
+  using Ents = RowEnts<NT, kChunkRows>;
   extern __shared__ __align__(16) char lds[];
 
   // blocks in ascending order, the units of one block side by side: early
@@ -156,35 +175,35 @@ __global__ __launch_bounds__(2 * BS, 1) void bwd_kv_kernel(
   }
 
   // entries of chunk cc for this thread's rows
-  auto load_ents = [&](int cc, RowEnts<NT>& re) {
+  auto load_ents = [&](int cc, Ents& re) {
 #pragma unroll
     for (int m = 0; m < Stage::kJobs; ++m) {
-      const int p = (tid + NT * m) >> 4;
+      const int p = ((tid + NT * m) & 15) + 16 * ((tid + NT * m) >> 8);
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
         const int tk = cc * tpc + ((2 * p + x) >> sh.r_log2);
         re.e[m][x] = entries[e0 + min(tk, n - 1)];
       }
     }
-    re.info = entries[e0 + min(cc * tpc + ((tid & 31) >> sh.r_log2), n - 1)];
+    re.info = entries[e0 + min(cc * tpc + ((tid & (kChunkRows - 1)) >> sh.r_log2), n - 1)];
   };
   auto row_ptr_q = [&](const uint16_t* base, uint32_t ent, int rho) -> const uint16_t* {
     const int t = (int)(ent >> 5);
     return base + (((size_t)b * sh.S + t) * sh.Hq + g * sh.r + (rho & (sh.r - 1))) * kHeadDim;
   };
-  auto load_rows = [&](int cc, const RowEnts<NT>& re, Stage& st) {
+  auto load_rows = [&](int cc, const Ents& re, Stage& st) {
 #pragma unroll
     for (int m = 0; m < Stage::kJobs; ++m) {
       const int qid = tid + NT * m;
-      const int p = qid >> 4;
-      const int c = qid & 15;
+      const int p = (qid & 15) + 16 * (qid >> 8);
+      const int c = (qid >> 4) & 15;
       st.qa[m] = *reinterpret_cast<const u32x4_t*>(row_ptr_q(q, re.e[m][0], 2 * p) + 8 * c);
       st.qb[m] = *reinterpret_cast<const u32x4_t*>(row_ptr_q(q, re.e[m][1], 2 * p + 1) + 8 * c);
       st.da[m] = *reinterpret_cast<const u32x4_t*>(row_ptr_q(dout, re.e[m][0], 2 * p) + 8 * c);
       st.db[m] = *reinterpret_cast<const u32x4_t*>(row_ptr_q(dout, re.e[m][1], 2 * p + 1) + 8 * c);
     }
-    // row info: threads 0 .. 31, row = tid (other threads load a copy)
-    const int rho = tid & 31;
+    // row info: threads 0 .. kChunkRows - 1, row = tid (other threads load a copy)
+    const int rho = tid & (kChunkRows - 1);
     const int tk = cc * tpc + (rho >> sh.r_log2);
     const bool valid = tk < n;
     const int t = (int)(re.info >> 5);
@@ -199,8 +218,8 @@ __global__ __launch_bounds__(2 * BS, 1) void bwd_kv_kernel(
 #pragma unroll
     for (int m = 0; m < Stage::kJobs; ++m) {
       const int qid = tid + NT * m;
-      const int p = qid >> 4;
-      const int c = qid & 15;
+      const int p = (qid & 15) + 16 * (qid >> 8);
+      const int c = (qid >> 4) & 15;
       *reinterpret_cast<u32x4_t*>(lds + L::kQn + (2 * p) * kNatStride + 16 * c) = st.qa[m];
       *reinterpret_cast<u32x4_t*>(lds + L::kQn + (2 * p + 1) * kNatStride + 16 * c) = st.qb[m];
       *reinterpret_cast<u32x4_t*>(lds + L::kDn + (2 * p) * kNatStride + 16 * c) = st.da[m];
@@ -221,13 +240,14 @@ __global__ __launch_bounds__(2 * BS, 1) void bwd_kv_kernel(
     }
     if (tid < kChunkRows) {
       reinterpret_cast<float*>(lds + L::kInfo)[tid] = st.lse2;
-      reinterpret_cast<float*>(lds + L::kInfo + 128)[tid] = st.delta;
-      reinterpret_cast<int*>(lds + L::kInfo + 256)[tid] = st.lim;
-      reinterpret_cast<uint32_t*>(lds + L::kInfo + 384)[tid] = st.ent;
+      reinterpret_cast<float*>(lds + L::kInfo + 4 * kChunkRows)[tid] = st.delta;
+      reinterpret_cast<int*>(lds + L::kInfo + 8 * kChunkRows)[tid] = st.lim;
+      reinterpret_cast<uint32_t*>(lds + L::kInfo + 12 * kChunkRows)[tid] = st.ent;
     }
   };
 
-  // Pipeline per chunk c (one register stage, loads a full chunk ahead):
+  // Pipeline per chunk c (one register stage, loads a full chunk ahead; a
+  // second stage, loads two chunks ahead, measured no faster):
   //   phase 1 on the LDS rows of chunk c; dS -> LDS        | barrier A
   //   rows of chunk c + 1 (registers) -> LDS; loads of chunk c + 2
   //   phase 2: dQ^T -> the LDS dq tile                     | barrier B
@@ -238,7 +258,7 @@ __global__ __launch_bounds__(2 * BS, 1) void bwd_kv_kernel(
   // repeat its last entry, and their rows are masked (lse2 = +inf, no dq
   // store).
   constexpr int kCopyRows = kChunkRows * 16 / NT;  // dq tile rows each thread stores
-  RowEnts<NT> ent_next;
+  Ents ent_next;
   Stage stage;
   const bool any = n_chunks > 0;
   if (any) {
@@ -249,67 +269,84 @@ __global__ __launch_bounds__(2 * BS, 1) void bwd_kv_kernel(
     load_rows(1, ent_next, stage);
     load_ents(2, ent_next);
   }
+  // every load issued so far (the wave's K and V rows above all) is complete
+  // before the loop, so that no wait inside it is on them
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   const int key = 32 * w + (lane & 31);  // this lane's key within the block (S / dP columns)
   for (int c = 0; c < n_chunks; ++c) {
-    // ---- S = Q K^T and dP = dO V^T for the wave's 32 keys
-    f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+    // ---- S = Q K^T and dP = dO V^T for the wave's 32 keys, per row tile
+    f32x16_t s[kRT], dp[kRT];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const u32x4_t aq = *reinterpret_cast<const u32x4_t*>(lds + L::kQn + (lane & 31) * kNatStride + 32 * ks + 16 * hf);
-      const u32x4_t ad = *reinterpret_cast<const u32x4_t*>(lds + L::kDn + (lane & 31) * kNatStride + 32 * ks + 16 * hf);
-      s = mfma32x32x16(aq, kb[ks], s);
-      dp = mfma32x32x16(ad, vb[ks], dp);
+    for (int rt = 0; rt < kRT; ++rt) {
+      s[rt] = f32x16_t{};
+      dp[rt] = f32x16_t{};
+      const char* qrow = lds + L::kQn + (32 * rt + (lane & 31)) * kNatStride + 16 * hf;
+      const char* drow = lds + L::kDn + (32 * rt + (lane & 31)) * kNatStride + 16 * hf;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        s[rt] = mfma32x32x16(*reinterpret_cast<const u32x4_t*>(qrow + 32 * ks), kb[ks], s[rt]);
+        dp[rt] = mfma32x32x16(*reinterpret_cast<const u32x4_t*>(drow + 32 * ks), vb[ks], dp[rt]);
+      }
     }
-    // ---- P and dS; element i is query row c_row(i, hf), column = key
-    float pv[16], dsv[16];
+    // ---- P and dS; element i of tile rt is query row 32 rt + c_row(i, hf), column = key
+    u32x4_t ph[kRT][2], dsh[kRT][2];
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int r0 = 8 * q4 + 4 * hf;
-      const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(lds + L::kInfo + 4 * r0);
-      const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(lds + L::kInfo + 128 + 4 * r0);
-      const i32x4_t m4 = *reinterpret_cast<const i32x4_t*>(lds + L::kInfo + 256 + 4 * r0);
+    for (int rt = 0; rt < kRT; ++rt) {
+      float pv[16], dsv[16];
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const int i = 4 * q4 + x;
-        const float p = key <= m4[x] ? fast_exp2(fmaf(s[i], c2, -l4[x])) : 0.f;
-        pv[i] = p;
-        dsv[i] = p * (dp[i] - d4[x]);
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int r0 = 32 * rt + 8 * q4 + 4 * hf;
+        const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(lds + L::kInfo + 4 * r0);
+        const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(lds + L::kInfo + 4 * kChunkRows + 4 * r0);
+        const i32x4_t m4 = *reinterpret_cast<const i32x4_t*>(lds + L::kInfo + 8 * kChunkRows + 4 * r0);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int i = 4 * q4 + x;
+          const float p = key <= m4[x] ? fast_exp2(fmaf(s[rt][i], c2, -l4[x])) : 0.f;
+          pv[i] = p;
+          dsv[i] = p * (dp[rt][i] - d4[x]);
+        }
+      }
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        ph[rt][h2] = u32x4_t{pack_bf16x2(pv[8 * h2], pv[8 * h2 + 1]), pack_bf16x2(pv[8 * h2 + 2], pv[8 * h2 + 3]),
+                             pack_bf16x2(pv[8 * h2 + 4], pv[8 * h2 + 5]), pack_bf16x2(pv[8 * h2 + 6], pv[8 * h2 + 7])};
+        dsh[rt][h2] =
+            u32x4_t{pack_bf16x2(dsv[8 * h2], dsv[8 * h2 + 1]), pack_bf16x2(dsv[8 * h2 + 2], dsv[8 * h2 + 3]),
+                    pack_bf16x2(dsv[8 * h2 + 4], dsv[8 * h2 + 5]), pack_bf16x2(dsv[8 * h2 + 6], dsv[8 * h2 + 7])};
       }
     }
     // entries of the dq tile rows this thread stores after phase 2
     uint32_t copy_ent[kCopyRows];
 #pragma unroll
     for (int m = 0; m < kCopyRows; ++m)
-      copy_ent[m] = reinterpret_cast<const uint32_t*>(lds + L::kInfo + 384)[(tid >> 4) + (NT >> 4) * m];
-    u32x4_t ph[2], dsh[2];
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      ph[h2] = u32x4_t{pack_bf16x2(pv[8 * h2], pv[8 * h2 + 1]), pack_bf16x2(pv[8 * h2 + 2], pv[8 * h2 + 3]),
-                       pack_bf16x2(pv[8 * h2 + 4], pv[8 * h2 + 5]), pack_bf16x2(pv[8 * h2 + 6], pv[8 * h2 + 7])};
-      dsh[h2] = u32x4_t{pack_bf16x2(dsv[8 * h2], dsv[8 * h2 + 1]), pack_bf16x2(dsv[8 * h2 + 2], dsv[8 * h2 + 3]),
-                        pack_bf16x2(dsv[8 * h2 + 4], dsv[8 * h2 + 5]), pack_bf16x2(dsv[8 * h2 + 6], dsv[8 * h2 + 7])};
-    }
+      copy_ent[m] = reinterpret_cast<const uint32_t*>(lds + L::kInfo + 12 * kChunkRows)[(tid >> 4) + (NT >> 4) * m];
     // ---- dV^T += dO^T P, dK^T += Q^T dS (head dims x the wave's keys)
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const int d = 32 * dt + (lane & 31);
-        dvt[dt] = mfma32x32x16(tr_frag(lds + L::kDt, d, h2, hf), ph[h2], dvt[dt]);
-        dkt[dt] = mfma32x32x16(tr_frag(lds + L::kQt, d, h2, hf), dsh[h2], dkt[dt]);
-      }
+      for (int rt = 0; rt < kRT; ++rt)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int d = 32 * dt + (lane & 31);
+          dvt[dt] = mfma32x32x16(tr_frag<kTrStride>(lds + L::kDt, d, rt, h2, hf), ph[rt][h2], dvt[dt]);
+          dkt[dt] = mfma32x32x16(tr_frag<kTrStride>(lds + L::kQt, d, rt, h2, hf), dsh[rt][h2], dkt[dt]);
+        }
     // ---- dS (bf16, as used above) -> LDS, rows x keys
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
+    for (int rt = 0; rt < kRT; ++rt)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t pair = dsh[h2][e];
-        const int i = 8 * h2 + 2 * e;
-        *reinterpret_cast<uint16_t*>(lds + L::kDs + c_row(i, hf) * L::kDsStride + 2 * key) = (uint16_t)(pair & 0xffffu);
-        *reinterpret_cast<uint16_t*>(lds + L::kDs + c_row(i + 1, hf) * L::kDsStride + 2 * key) = (uint16_t)(pair >> 16);
-      }
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t pair = dsh[rt][h2][e];
+          const int i = 8 * h2 + 2 * e;
+          char* col = lds + L::kDs + 2 * key + 32 * rt * L::kDsStride;
+          *reinterpret_cast<uint16_t*>(col + c_row(i, hf) * L::kDsStride) = (uint16_t)(pair & 0xffffu);
+          *reinterpret_cast<uint16_t*>(col + c_row(i + 1, hf) * L::kDsStride) = (uint16_t)(pair >> 16);
+        }
     __syncthreads();
     // the rows of chunk c + 1 replace this chunk's (every read of them is
     // above the barrier), then the loads of chunk c + 2
@@ -321,22 +358,25 @@ __global__ __launch_bounds__(2 * BS, 1) void bwd_kv_kernel(
 #pragma unroll
     for (int dd = 0; dd < DT; ++dd) {
       const int dt = DT * w + dd;
-      f32x16_t acc = f32x16_t{};
 #pragma unroll
-      for (int ks = 0; ks < BS / 16; ++ks) {
-        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(lds + L::kKt + (32 * dt + (lane & 31)) * L::kKtStride +
-                                                            32 * ks + 16 * hf);
-        const u32x4_t bq =
-            *reinterpret_cast<const u32x4_t*>(lds + L::kDs + (lane & 31) * L::kDsStride + 32 * ks + 16 * hf);
-        acc = mfma32x32x16(a, bq, acc);
-      }
-      char* dst = lds + L::kDq + (lane & 31) * kNatStride + 2 * (32 * dt + 4 * hf);
+      for (int rt = 0; rt < kRT; ++rt) {
+        f32x16_t acc = f32x16_t{};
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        u32x2_t wv;
-        wv.x = pack_bf16x2(acc[4 * q4], acc[4 * q4 + 1]);
-        wv.y = pack_bf16x2(acc[4 * q4 + 2], acc[4 * q4 + 3]);
-        *reinterpret_cast<u32x2_t*>(dst + 16 * q4) = wv;
+        for (int ks = 0; ks < BS / 16; ++ks) {
+          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(lds + L::kKt + (32 * dt + (lane & 31)) * L::kKtStride +
+                                                              32 * ks + 16 * hf);
+          const u32x4_t bq = *reinterpret_cast<const u32x4_t*>(lds + L::kDs + (32 * rt + (lane & 31)) * L::kDsStride +
+                                                               32 * ks + 16 * hf);
+          acc = mfma32x32x16(a, bq, acc);
+        }
+        char* dst = lds + L::kDq + (32 * rt + (lane & 31)) * kNatStride + 2 * (32 * dt + 4 * hf);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          u32x2_t wv;
+          wv.x = pack_bf16x2(acc[4 * q4], acc[4 * q4 + 1]);
+          wv.y = pack_bf16x2(acc[4 * q4 + 2], acc[4 * q4 + 3]);
+          *reinterpret_cast<u32x2_t*>(dst + 16 * q4) = wv;
+        }
       }
     }
     __syncthreads();
