@@ -78,12 +78,13 @@ def _measured_traffic():
 
 
 def pmc_run():
-    """Workload for counter runs under rocprofv3 --pmc: two 32K prefills,
-    two decodes of the decode workload, then a 1 GiB device copy whose bytes
-    are known (the calibration of the FETCH_SIZE / WRITE_SIZE counters)."""
+    """Workload for counter runs under rocprofv3 --pmc: two 32K prefills, the
+    32K training forward and two backward calls, two decodes of the decode
+    workload, then a 1 GiB device copy whose bytes are known (the
+    calibration of the FETCH_SIZE / WRITE_SIZE counters)."""
     import torch
     import block_sparse_attention_33_amd as msa
-    from synth import decode_inputs, get_workload, prefill_inputs
+    from synth import decode_inputs, get_workload, grad_output, prefill_inputs
     dev = torch.device("cuda:0")
     w = get_workload("prefill_32k")
     inp = prefill_inputs(w, seed=0, device=dev)
@@ -93,7 +94,14 @@ def pmc_run():
     for _ in range(2):
         msa.msa_prefill(inp["q"], inp["k"], inp["v"], inp["q_idx"], inp["k_idx"], w.block_size, w.top_k,
                         workspace=ws)
-    del inp, ws
+    out, sel, lse = msa.msa_prefill_lse(inp["q"], inp["k"], inp["v"], inp["q_idx"], inp["k_idx"], w.block_size,
+                                        w.top_k, workspace=ws)
+    del ws
+    dout = grad_output(w, seed=0, device=dev)
+    for _ in range(2):
+        msa.msa_prefill_backward(inp["q"], inp["k"], inp["v"], out, dout, lse, sel, w.block_size)
+    torch.cuda.synchronize()
+    del inp, out, sel, lse, dout
     wd = get_workload("decode_b16_256k")
     din = decode_inputs(wd, seed=0, device=dev)
     bk = msa.msa_pool_block_keys(din["k_idx_cache"], wd.block_size)
@@ -223,6 +231,50 @@ def _chunk_ws_bytes(msa, dims, count):
     return hi.value
 
 
+def train_only(steps, warmup):
+    """The 32K prefill for training alone: forward with log-sum-exp, then the
+    backward, each timed over `steps` calls (for profiler runs)."""
+    import torch
+    import block_sparse_attention_33_amd as msa
+    from synth import get_workload, grad_output, prefill_inputs
+
+    dev = torch.device("cuda:0")
+    w = get_workload("prefill_32k")
+    pin = prefill_inputs(w, seed=0, device=dev)
+    dout = grad_output(w, seed=0, device=dev)
+    dims = msa.make_dims(w.batch, w.seq_len, w.n_q_heads, w.n_kv_heads, w.block_size, w.top_k)
+    pws = torch.empty(msa.msa_workspace_bytes(msa.MSA_OP_PREFILL, dims)[1], dtype=torch.uint8, device=dev)
+    bws = torch.empty(msa.msa_workspace_bytes(msa.MSA_OP_BACKWARD, dims)[1], dtype=torch.uint8, device=dev)
+
+    def fwd():
+        return msa.msa_prefill_lse(pin["q"], pin["k"], pin["v"], pin["q_idx"], pin["k_idx"], w.block_size, w.top_k,
+                                   workspace=pws)
+
+    out, sel, lse = fwd()
+
+    def bwd():
+        return msa.msa_prefill_backward(pin["q"], pin["k"], pin["v"], out, dout, lse, sel, w.block_size,
+                                        workspace=bws)
+
+    res = {}
+    for name, fn in (("forward_lse", fwd), ("backward", bwd)):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        res[name] = sorted(a.elapsed_time(b) for a, b in ev)[steps // 2]
+    per_head_keys, _, _ = _prefill_counts(w)
+    flop = 2.5 * 4.0 * w.head_dim * w.n_q_heads * per_head_keys
+    print(json.dumps({"workload": "prefill_32k training", "forward_lse_ms": round(res["forward_lse"], 4),
+                      "backward_ms": round(res["backward"], 4),
+                      "backward_tflops_alg": round(flop / (res["backward"] * 1e-3) / 1e12, 2)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -231,6 +283,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--core-only", action="store_true",
                     help="time the step only: no chunked, short-sequence or generation-step extras")
+    ap.add_argument("--train-only", action="store_true",
+                    help="time only the training forward (with log-sum-exp) and backward of the 32K prefill")
     ap.add_argument("--cpu-baseline-worker", default=None, help=argparse.SUPPRESS)
     ap.add_argument("--pmc-run", action="store_true",
                     help="run the counter-collection workload instead of the benchmark")
@@ -251,6 +305,9 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the MSA path here runs on a single MI355X).", file=sys.stderr)
         return 2
+    if args.train_only:
+        train_only(args.steps, args.warmup)
+        return 0
 
     import torch
     import block_sparse_attention_33_amd as msa
