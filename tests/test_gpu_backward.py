@@ -100,6 +100,31 @@ def test_prefill_lse_small(name, over, S):
     assert float(err.max()) <= LSE_ABS, f"{name}: lse max_abs={err.max():.3e}"
 
 
+def test_backward_custom_scale():
+    """A softmax scale other than 1/sqrt(D), passed to both calls."""
+    w = get_workload("tiny_2k", n_q_heads=8, n_kv_heads=2, block_size=64, top_k=4)
+    S, scale = 900, 0.05
+    _say(f"[backward scale] S={S} scale={scale}")
+    inp = prefill_inputs(w, seed=13, device="cpu", seq_len=S)
+    dout = grad_output(w, seed=13, device="cpu", seq_len=S)
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    out, sel, lse = msa.msa_prefill_lse(d["q"], d["k"], d["v"], d["q_idx"], d["k_idx"], w.block_size, w.top_k,
+                                        softmax_scale=scale)
+    dq, dk, dv = msa.msa_prefill_backward(d["q"], d["k"], d["v"], out, dout.to(DEV), lse, sel, w.block_size,
+                                          softmax_scale=scale)
+    torch.cuda.synchronize()
+    summ = O.pool_block_keys(inp["k_idx"].numpy(), w.block_size)
+    osel = O.select_blocks(inp["q_idx"].numpy(), summ, w.block_size, w.top_k)
+    assert np.array_equal(host_i8(sel).astype(np.int32), osel)
+    hq, hk, hv = host_f32(inp["q"]), host_f32(inp["k"]), host_f32(inp["v"])
+    olse = O.lse_rows(hq, hk, hv, osel, np.arange(S), w.block_size, scale=scale)
+    assert float(np.abs(lse.cpu().numpy() - olse).max()) <= LSE_ABS
+    rq, rk, rv = O.backward(hq, hk, hv, host_f32(dout), osel, w.block_size, scale=scale)
+    compare_grad(dq, rq, "scale dq")
+    compare_grad(dk, rk, "scale dk")
+    compare_grad(dv, rv, "scale dv")
+
+
 @pytest.mark.parametrize("name,over,S", SMALL, ids=[c[0] for c in SMALL])
 def test_backward_small_all_elements(name, over, S):
     w = get_workload("tiny_2k", **over)
@@ -160,5 +185,42 @@ def test_backward_32k_sampled_and_sums():
         _, rk, rv = O.backward(hq, hk, hv, hd, osel, bs, rows=[], kv_blocks=[j], groups=[g])
         compare_grad(dk[:, g, j * bs:(j + 1) * bs], rk[:, g, 0], f"32k dk block {j} group {g}")
         compare_grad(dv[:, g, j * bs:(j + 1) * bs], rv[:, g, 0], f"32k dv block {j} group {g}")
+    del inp, dout, dq, dk, dv
+    _free()
+
+
+def test_backward_structured_128k_sampled_and_sums():
+    """The structured 128K workload (hot blocks kept by most queries of their
+    group, so some CSR rows are very long): dq on sampled rows and dk, dv of
+    the last block against the oracle; the closed-form sums over every key."""
+    w = get_workload("structured_128k")
+    S, bs = w.seq_len, w.block_size
+    _say(f"[backward full] structured_128k S={S}")
+    inp = prefill_inputs(w, seed=41, device=DEV)
+    dout = grad_output(w, seed=41, device=DEV)
+    _, sel, _, dq, dk, dv = _forward_backward(inp, dout, bs, w.top_k)
+    gsel = host_i8(sel).astype(np.int32)
+    del sel
+    _free()
+    gdv = host_f32(dv).astype(np.float64)
+    gdk = host_f32(dk).astype(np.float64)
+    dsum = host_f32(dout).astype(np.float64).reshape(w.batch, S, w.n_kv_heads, -1, 128).sum(axis=(1, 3))
+    np.testing.assert_allclose(gdv.sum(axis=2), dsum, rtol=0, atol=2e-3 * np.abs(gdv).sum(axis=2).max())
+    assert np.abs(gdk.sum(axis=2)).max() <= 2e-3 * np.abs(gdk).sum(axis=2).max()
+    del gdv, gdk
+    _say("[backward full] oracle selection of every row")
+    summ = O.pool_block_keys(host_i8(inp["k_idx"]), bs)
+    osel = O.select_blocks(host_i8(inp["q_idx"]), summ, bs, w.top_k)
+    assert np.array_equal(gsel, osel), "selection differs"
+    hq, hk, hv, hd = host_f32(inp["q"]), host_f32(inp["k"]), host_f32(inp["v"]), host_f32(dout)
+    rows = sample_rows(S, 24, 41)
+    _say(f"[backward full] oracle dq on {len(rows)} rows")
+    rq, _, _ = O.backward(hq, hk, hv, hd, osel, bs, rows=rows, kv_blocks=[])
+    compare_grad(dq[:, torch.as_tensor(rows, device=DEV)], rq, "128k dq (sampled rows)")
+    j, g = S // bs - 1, 5
+    _say(f"[backward full] oracle dk, dv of block {j}, group {g}")
+    _, rk, rv = O.backward(hq, hk, hv, hd, osel, bs, rows=[], kv_blocks=[j], groups=[g])
+    compare_grad(dk[:, g, j * bs:(j + 1) * bs], rk[:, g, 0], f"128k dk block {j} group {g}")
+    compare_grad(dv[:, g, j * bs:(j + 1) * bs], rv[:, g, 0], f"128k dv block {j} group {g}")
     del inp, dout, dq, dk, dv
     _free()
