@@ -389,6 +389,7 @@ def main():
     gen_med = ch_ms = dwarm_med = None
     short_ms, short_flop = {}, None
     train_ms, bkt = {}, {}
+    other_cfg = {}
     if not args.core_only:
         # generation step: append token L - 1 to the caches, refresh its block's
         # summary, decode (outside the timed region; same events)
@@ -492,6 +493,38 @@ def main():
                 bkt = msa.profile_read()
         del bout, bsel, blse, bdout, bws
 
+        # the other prefill workloads, timed the same way (median of a few
+        # calls after one warm-up; the 2K one is launch-bound)
+        for name_, reps in (("tiny_2k", 10), ("structured_128k", 5), ("prefill_1m", 3)):
+            wc = get_workload(name_)
+            cin = prefill_inputs(wc, seed=0, device=dev)
+            cdims = msa.make_dims(wc.batch, wc.seq_len, wc.n_q_heads, wc.n_kv_heads, wc.block_size, wc.top_k)
+            cws = torch.empty(msa.msa_workspace_bytes(msa.MSA_OP_PREFILL, cdims)[1], dtype=torch.uint8, device=dev)
+            cout = torch.empty_like(cin["q"])
+
+            def fn():
+                msa.msa_prefill(cin["q"], cin["k"], cin["v"], cin["q_idx"], cin["k_idx"], wc.block_size, wc.top_k,
+                                out=cout, workspace=cws)
+
+            fn()
+            torch.cuda.synchronize()
+            pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+            for a, b in pev:
+                a.record()
+                fn()
+                b.record()
+            torch.cuda.synchronize()
+            cms = sorted(a.elapsed_time(b) for a, b in pev)[reps // 2]
+            cflop = 4.0 * wc.head_dim * wc.n_q_heads * _prefill_counts(wc)[0]
+            other_cfg[name_] = {"seq_len": wc.seq_len, "n_q_heads": wc.n_q_heads, "n_kv_heads": wc.n_kv_heads,
+                                "block_size": wc.block_size, "top_k": wc.top_k, "calls": reps,
+                                "ms": round(cms, 4), "tokens_per_s": round(wc.batch * wc.seq_len / (cms * 1e-3), 1),
+                                "tflops_alg": round(cflop / (cms * 1e-3) / 1e12, 2),
+                                "frac_bf16_peak": round(cflop / (cms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+            print(f"[bench] {name_}: {cms:.3f} ms", file=sys.stderr, flush=True)
+            del cin, cout, cws
+            torch.cuda.empty_cache()
+
         # the plain decode timed the same way (back to back, so the kept blocks
         # may still sit in the memory-side cache, unlike in the step above where
         # a prefill runs in between)
@@ -582,6 +615,7 @@ def main():
             if "bwd_kv" in bkt else None,
             "kernels": {k: {"launches": n, "avg_ms": round(ms / max(1, n), 4)} for k, (n, ms) in sorted(bkt.items())},
         },
+        "prefill_other_workloads": other_cfg or None,
         "decode_step": None if gen_med is None else {
             "what": "append one token per sequence (K/V rows, running index-key sum, block summary) + decode",
             "us": round(gen_med, 2),

@@ -70,7 +70,7 @@ int check_dims(const msa_dims* d, Dims* o) {
 
 // ---- prefill planning
 //
-// A long prefill runs in query chunks (kPrefillQueryChunk); within a chunk
+// A long prefill runs in query chunks (prefill_query_chunk); within a chunk
 // the main branch runs in passes of as many (batch, group) units as the
 // workspace holds partials for (all of them at the full workspace size).
 // The CSR rows are (unit, block): one query range per unit.  (The kernels
@@ -261,14 +261,25 @@ Dims chunk_dims(const Dims& dc, long n_q) {
   return d;
 }
 
-// A long prefill runs in query chunks of this many tokens: one chunk's
-// partials (about 280 MB for 64 query heads and top_k 16) then mostly stay
-// in the 256 MB memory-side cache until the merge reads them.  Measured on
-// MI355X: 3 % faster at 32K and 6 % at 128K than one pass; smaller chunks
-// lose more to the per-chunk launches and the shorter item lists.
+// A long prefill runs in query chunks.  Up to 128K tokens a chunk holds
+// 16384 queries: its partials (about 280 MB for 64 query heads and top_k 16)
+// then mostly stay in the 256 MB memory-side cache until the merge reads
+// them (measured on MI355X: 3 % faster at 32K and 6 % at 128K than one
+// pass, and at 128K faster than 32K or 64K chunks).  Every chunk reads the
+// K/V blocks its queries kept once, so when the blocks far outnumber a
+// chunk's queries (a 16K chunk of a 1M-token prefill keeps each block for
+// about 32 tokens) that re-reading dominates; beyond 128K tokens a chunk is
+// a quarter of the sequence (1M tokens: 251 ms against 328 ms with 16K
+// chunks, 260 ms with 128K and 257 ms with 512K).
 constexpr long kPrefillQueryChunk = 16384;
+constexpr long kShortPrefill = 131072;
 
-long prefill_query_chunk(const Dims& d) { return d.S > kPrefillQueryChunk ? kPrefillQueryChunk : d.S; }
+long prefill_query_chunk(const Dims& d) {
+  if (d.S <= kPrefillQueryChunk) return d.S;
+  if (d.S <= kShortPrefill) return kPrefillQueryChunk;
+  const long quarter = (d.S + 3) / 4;
+  return (quarter + kPrefillQueryChunk - 1) / kPrefillQueryChunk * kPrefillQueryChunk;
+}
 
 // Prefill of the queries at positions q0 .. q0 + n_q - 1 of sequences whose
 // keys, values and index keys are rows 0 .. q0 + n_q - 1 of k, v and k_idx

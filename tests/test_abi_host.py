@@ -203,7 +203,15 @@ def _a(x):
     return (x + 255) // 256 * 256
 
 
-QUERY_CHUNK = 16384        # a longer prefill runs in query chunks of this many tokens
+def _query_chunk(S):
+    """Tokens per query chunk of a prefill: the whole sequence up to 16384,
+    16384 up to 131072, a quarter of the sequence (a multiple of 16384)
+    beyond."""
+    if S <= 16384:
+        return S
+    if S <= 131072:
+        return 16384
+    return -(-(-(-S // 4)) // 16384) * 16384
 
 
 def _plan(U, S, nb):
@@ -219,7 +227,7 @@ def _plan(U, S, nb):
 @pytest.mark.parametrize("B,S,Hq,G,bs,k", [
     (1, 32768, 64, 8, 128, 16), (1, 2048, 8, 1, 64, 8), (2, 1000, 8, 2, 32, 5),
     (1, 777, 16, 1, 128, 1), (1, 1048576, 64, 8, 128, 16), (1, 131072, 64, 8, 128, 16),
-    (1, 65536, 8, 1, 128, 1)])
+    (1, 65536, 8, 1, 128, 1), (1, 200000, 8, 1, 128, 4)])
 def test_prefill_workspace_layout(lib, B, S, Hq, G, bs, k):
     """The documented layout: fixed part + one bf16 partial (r x 128) and one
     fp32 (max, sum) pair (r) per (token, kept block) of a pass; the
@@ -230,7 +238,7 @@ def test_prefill_workspace_layout(lib, B, S, Hq, G, bs, k):
     assert st == 0
     U, r = B * G, Hq // G
     nb = -(-S // bs)
-    S = min(S, QUERY_CHUNK)
+    S = _query_chunk(S)
     tpi = 4 * 256 // r          # up to 4 chunks of 256 query rows per work item
     n_chunks = _plan(U, S, nb)
     rows = U * nb
