@@ -51,6 +51,8 @@ SMALL = [
     ("topk_ge_nb_dense", dict(n_q_heads=8, n_kv_heads=2, block_size=64, top_k=32), 1100),
     ("single_block", dict(n_q_heads=8, n_kv_heads=1, block_size=128, top_k=4), 100),
     ("r2_bs64_k2", dict(n_q_heads=4, n_kv_heads=2, block_size=64, top_k=2), 513),
+    ("one_token", dict(n_q_heads=8, n_kv_heads=2, block_size=64, top_k=4), 1),
+    ("three_tokens_b3_r1", dict(batch=3, n_q_heads=2, n_kv_heads=2, block_size=32, top_k=2), 3),
 ]
 
 
