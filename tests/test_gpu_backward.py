@@ -6,11 +6,14 @@ The log-sum-exp is fp32 arithmetic on bf16 inputs: within 1e-3 of the
 oracle's fp64 value.  A gradient element is a bf16-rounded sum whose terms
 each pass through bf16 rounding (relative error <= 2^-9) two or three more
 times than the forward's do: P or dS as an MFMA operand, the per-block dq
-partial, and delta taken from the bf16 output.  So the error is a few 2^-9
-of the terms' magnitude, and the comparison is relative to the gradient's
-own scale, per tensor:
-  max |gpu - bf16(oracle)|  <= 1.5e-2 (about 8 * 2^-9) * max |oracle|
-  mean |gpu - bf16(oracle)| <= 5e-3 (about 2.5 * 2^-9) * mean |oracle|.
+partial, and delta taken from the bf16 output: at most about 3 * 2^-9 of
+the terms' magnitude.  dq and dk are sums of terms that cancel (the dS of a
+query row sum to zero), so relative to the result the error can be a small
+multiple of that; the comparison allows a factor of about two, relative to
+the gradient's own scale (floored at 1e-2, for gradients that are exactly
+zero, e.g. with a single attended key), per tensor:
+  max |gpu - bf16(oracle)|  <= 2e-2 * max |oracle|
+  mean |gpu - bf16(oracle)| <= 1e-2 * mean |oracle|.
 """
 import gc
 import sys
@@ -28,8 +31,8 @@ pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
 LSE_ABS = 1e-3
-GRAD_MAX_REL = 1.5e-2
-GRAD_MEAN_REL = 5e-3
+GRAD_MAX_REL = 2e-2
+GRAD_MEAN_REL = 1e-2
 GRAD_FLOOR = 1e-2
 
 
