@@ -438,7 +438,8 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restri
 }
 
 // dq of every row: 16 threads per (token, head), 8 head dims each, summing
-// the row's min(top_k - 1, own block) + 1 partials.
+// the row's min(top_k - 1, own block) + 1 partials (each read once, with a
+// non-temporal hint, as in the forward's merge).
 __global__ __launch_bounds__(256) void bwd_dq_kernel(const uint16_t* __restrict__ part_dq, uint16_t* __restrict__ dq,
                                                      BwdShape sh) {
   const long gid = (long)blockIdx.x * 256 + threadIdx.x;
@@ -457,7 +458,8 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const uint16_t* __restrict_
     u32x4_t val[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s)
-      if (s0 + s < n) val[s] = *reinterpret_cast<const u32x4_t*>(src + (size_t)(s0 + s) * sh.r * kHeadDim);
+      if (s0 + s < n)
+        val[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src + (size_t)(s0 + s) * sh.r * kHeadDim));
 #pragma unroll
     for (int s = 0; s < 8; ++s)
       if (s0 + s < n)
