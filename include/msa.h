@@ -52,7 +52,8 @@
  * crosses the ABI.
  *
  * Limits: head_dim 128, idx_dim 64, block_size 32, 64 or 128, 1 <= top_k <=
- * 32 (msa_prefill also takes any top_k >= nb), n_q_heads = r * n_kv_heads
+ * 32 (msa_prefill and msa_prefill_lse also take any top_k >= nb; the
+ * backward keeps top_k <= 32), n_q_heads = r * n_kv_heads
  * with r in {1, 2, 4, 8, 16}, S < 2^26 and B * G * S * top_k < 2^31; prefill
  * needs nb <= 36864 and decode nb <= 8193.  Anything else returns
  * MSA_ERR_UNSUPPORTED.
@@ -162,8 +163,10 @@ int msa_prefill_lse(const msa_dims* dims, const uint16_t* q, const uint16_t* k, 
  * block included, -1 padding).  Outputs dq [B, S, Hq, D], dk, dv [B, G, S, D]
  * bf16, every element written.  top_k <= 32.  ws/ws_bytes: at least
  * msa_workspace_bytes(MSA_OP_BACKWARD) (it holds one bf16 partial of dq per
- * (query row, kept block): B * Hq * S * top_k * D * 2 bytes and the
- * inversion of sel). */
+ * (query row, kept block): B * Hq * S * top_k * D * 2 bytes -- 8.6 GB at
+ * 32K tokens with 64 query heads and top_k 16 -- and the inversion of sel).
+ * The backward runs whole, not in query chunks: dk and dv of a block sum
+ * over every query. */
 int msa_prefill_backward(const msa_dims* dims, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                          const uint16_t* out, const uint16_t* dout, const float* lse, const int32_t* sel,
                          uint16_t* dq, uint16_t* dk, uint16_t* dv, void* ws, size_t ws_bytes, void* stream);
