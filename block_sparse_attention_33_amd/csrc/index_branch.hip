@@ -108,11 +108,38 @@ struct NextPow2 {
 // staged through LDS in chunks and read as wave-wide broadcasts; each lane
 // scores every candidate with 16 v_dot4 and keeps a sorted register list of
 // its best KCAP (score desc, index asc).  Candidates arrive in ascending
-// block order, so a candidate enters the list only when its score beats the
-// list's last score strictly: an equal score belongs to a lower index already
-// in the list.  KCAP >= top_k - 1; the best top_k - 1 are taken from it.
-// Query row t (of S per unit) is the token at position pos0 + t.
+// block order, so a candidate can enter the list only when its score beats
+// the list's last score strictly: an equal score belongs to a lower index
+// already in the list.  KCAP >= top_k - 1; the best top_k - 1 are taken
+// from it.  Query row t (of S per unit) is the token at position pos0 + t.
+//
+// The lanes of a wave hold different queries, so a sorted insertion run by
+// one lane costs the whole wave.  A candidate that beats the lane's
+// threshold (the list's last score when the list was last updated) is only
+// appended to a short per-lane LDS buffer; the buffers are merged into the
+// lists, in arrival order, when one of them fills and at the end.  A stale
+// (lower) threshold lets more candidates through, never fewer, and the
+// arrival order keeps the tie rule, so the lists are the same.
 // ---------------------------------------------------------------------------
+constexpr int kTopkBuf = 16;  // buffered candidates per lane
+
+template <int KCAP>
+__device__ __forceinline__ void topk_insert(int (&Ls)[KCAP], int (&Li)[KCAP], int s, int j) {
+  if (s > Ls[KCAP - 1]) {
+    // insert after every entry whose score is >= s (they all have a lower
+    // block index), shifting the rest down by one
+#pragma unroll
+    for (int i = KCAP - 1; i >= 0; --i) {
+      const bool keep = Ls[i] >= s;
+      const bool prev_keep = (i == 0) ? true : (Ls[i - 1] >= s);
+      const int ns = keep ? Ls[i] : (prev_keep ? s : Ls[i > 0 ? i - 1 : 0]);
+      const int ni = keep ? Li[i] : (prev_keep ? j : Li[i > 0 ? i - 1 : 0]);
+      Ls[i] = ns;
+      Li[i] = ni;
+    }
+  }
+}
+
 template <int KCAP>
 __global__ __launch_bounds__(256) void index_topk_kernel(const int8_t* __restrict__ q_idx,
                                                          const int8_t* __restrict__ block_keys,
@@ -121,6 +148,7 @@ __global__ __launch_bounds__(256) void index_topk_kernel(const int8_t* __restric
                                                          int q_stride, int sel_stride) {
   constexpr int CH = 256;  // summaries per LDS chunk (16 KiB)
   __shared__ i32x4_t sk[CH * 4];
+  __shared__ int2 buf[kTopkBuf][256];  // per lane: (score, block) waiting for the list
 
   const int u = blockIdx.y;
   const int t0 = blockIdx.x * 256;
@@ -140,6 +168,18 @@ __global__ __launch_bounds__(256) void index_topk_kernel(const int8_t* __restric
     Ls[i] = INT_MIN;
     Li[i] = -1;
   }
+  int thr = INT_MIN;  // Ls[KCAP - 1] as of the last merge
+  int nbuf = 0;
+  auto merge_buf = [&]() {
+    for (int i = 0; __any(i < nbuf); ++i) {
+      if (i < nbuf) {
+        const int2 e = buf[i][threadIdx.x];
+        topk_insert<KCAP>(Ls, Li, e.x, e.y);
+      }
+    }
+    nbuf = 0;
+    thr = Ls[KCAP - 1];
+  };
 
   const i32x4_t* kb = reinterpret_cast<const i32x4_t*>(block_keys + (size_t)u * nb_stride * kIdxDim);
   const int n_cand = kp > 0 ? c_last : 0;
@@ -170,21 +210,14 @@ __global__ __launch_bounds__(256) void index_topk_kernel(const int8_t* __restric
       sb = sdot4(q3.w, a3.w, sb);
       const int s = sa + sb;
       const int j = base + jj;
-      if (j < c && s > Ls[KCAP - 1]) {
-        // insert after every entry whose score is >= s (they all have a
-        // lower block index), shifting the rest down by one
-#pragma unroll
-        for (int i = KCAP - 1; i >= 0; --i) {
-          const bool keep = Ls[i] >= s;
-          const bool prev_keep = (i == 0) ? true : (Ls[i - 1] >= s);
-          const int ns = keep ? Ls[i] : (prev_keep ? s : Ls[i > 0 ? i - 1 : 0]);
-          const int ni = keep ? Li[i] : (prev_keep ? j : Li[i > 0 ? i - 1 : 0]);
-          Ls[i] = ns;
-          Li[i] = ni;
-        }
+      if (j < c && s > thr) {
+        buf[nbuf][threadIdx.x] = make_int2(s, j);
+        ++nbuf;
       }
+      if (__any(nbuf == kTopkBuf)) merge_buf();
     }
   }
+  merge_buf();
 
   // best min(top_k - 1, c) candidates, ascending, then the own block
   const int n_valid = min(kp, c);
