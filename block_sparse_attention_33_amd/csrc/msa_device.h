@@ -14,6 +14,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+typedef int32_t i32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kWave = 64;
 constexpr int kHeadDim = 128;

@@ -42,7 +42,10 @@ hipError_t launch_pool(const int8_t* k_idx, int8_t* block_keys, int units, int S
 hipError_t launch_pool_strided(const int8_t* k_idx, int8_t* block_keys, int32_t* open_sums, int units, int S,
                                long s_stride, int nb_stride, int bs, int j0, hipStream_t st);
 
-// Scores + per-(query, group) top-k -> sel [U, S, top_k].
+// Scores + per-(query, group) top-k -> sel [U, S, top_k].  Launches whose
+// queries rank at least kIndexMfmaMinBlocks blocks score on the matrix
+// cores, the others with dot4 instructions; the selections are the same.
+constexpr int kIndexMfmaMinBlocks = 512;
 hipError_t launch_index_topk(const int8_t* q_idx, const int8_t* block_keys, int32_t* sel, int units,
                              int S, int bs, int top_k, hipStream_t st);
 // The same for queries at positions q0 .. q0 + S - 1 (rows 0 .. S - 1 of

@@ -195,30 +195,55 @@ def test_prefill_32k_selection_all_rows():
     # kept set must be exactly the best top_k - 1 by (score desc, index asc)
     qi = host_i8(inp["q_idx"]).astype(np.int64)
     gsel = host_i8(sel).astype(np.int64)
-    S, bs, kp = w.seq_len, w.block_size, w.top_k - 1
+    S, bs = w.seq_len, w.block_size
     rows = sample_rows(S, 2048, 99)
     osel = O.select_blocks(host_i8(inp["q_idx"]), summ, bs, w.top_k, rows)
     assert np.array_equal(gsel[:, :, rows], osel)
-    # every row: with composite key = score * 2^20 - block (higher is better,
-    # ties to the lower block), the kept set is exactly the top min(kp, c)
+    _check_all_selections(gsel, qi, summ, S, bs, w.top_k)
+
+
+def _check_all_selections(gsel, qi, summ, S, bs, top_k):
+    """Every row: with composite key = score * 2^20 - block (higher is
+    better, ties to the lower block), the kept set is exactly the top
+    min(top_k - 1, own) of the earlier blocks, and the own block follows."""
+    kp = top_k - 1
     own = np.arange(S) // bs
     nb = summ.shape[2]
     j = np.arange(nb)[None, :]
-    for g in range(w.n_kv_heads):
+    for g in range(summ.shape[1]):
         sc = qi[0, g] @ summ[0, g].astype(np.int64).T                     # [S, nb]
         key = sc * (1 << 20) - j
         key = np.where(j < own[:, None], key, np.iinfo(np.int64).min)
-        m = np.minimum(kp, own)                                          # kept per row
-        srt = np.sort(key, axis=1)[:, ::-1]                                     # descending
+        m = np.minimum(kp, own)
+        srt = np.sort(key, axis=1)[:, ::-1]
         thr = srt[np.arange(S), np.maximum(m - 1, 0)]
         expect = (key >= thr[:, None]) & (j < own[:, None]) & (m[:, None] > 0)
         got = np.zeros((S, nb), bool)
         kept = gsel[0, g]
         rr, cc = np.nonzero(kept >= 0)
         got[rr, kept[rr, cc]] = True
-        got[np.arange(S), own] = False                                   # own block apart
+        got[np.arange(S), own] = False
         assert np.array_equal(got, expect), f"group {g}"
         assert (kept[np.arange(S), m] == own).all()
+
+
+def test_index_select_many_blocks_all_rows():
+    """40000 tokens in blocks of 32 (1250 blocks): the queries rank enough
+    blocks for the matrix-core scoring; every selection is checked, and
+    sampled rows against the oracle's selection."""
+    w = get_workload("tiny_2k", n_q_heads=4, n_kv_heads=2, block_size=32, top_k=12)
+    S = 40000
+    _say(f"[index many blocks] S={S} bs=32 k=12")
+    inp = prefill_inputs(w, seed=77, device=DEV, seq_len=S)
+    bk, sel = msa.msa_index_select(inp["q_idx"], inp["k_idx"], w.block_size, w.top_k)
+    torch.cuda.synchronize()
+    summ = O.pool_block_keys(host_i8(inp["k_idx"]), w.block_size)
+    assert np.array_equal(host_i8(bk), summ)
+    gsel = host_i8(sel).astype(np.int64)
+    rows = sample_rows(S, 512, 77)
+    osel = O.select_blocks(host_i8(inp["q_idx"]), summ, w.block_size, w.top_k, rows)
+    assert np.array_equal(gsel[:, :, rows], osel)
+    _check_all_selections(gsel, host_i8(inp["q_idx"]).astype(np.int64), summ, S, w.block_size, w.top_k)
 
 
 def test_structured_128k_sampled():
