@@ -227,14 +227,14 @@ def _check_all_selections(gsel, qi, summ, S, bs, top_k):
         assert (kept[np.arange(S), m] == own).all()
 
 
-def test_index_select_many_blocks_all_rows():
-    """40000 tokens in blocks of 32 (1250 blocks): the queries rank enough
-    blocks for the matrix-core scoring; every selection is checked, and
-    sampled rows against the oracle's selection."""
-    w = get_workload("tiny_2k", n_q_heads=4, n_kv_heads=2, block_size=32, top_k=12)
-    S = 40000
-    _say(f"[index many blocks] S={S} bs=32 k=12")
-    inp = prefill_inputs(w, seed=77, device=DEV, seq_len=S)
+@pytest.mark.parametrize("S,top_k,B", [(40000, 12, 1), (20000, 32, 1), (20000, 2, 2), (17000, 5, 1)])
+def test_index_select_many_blocks_all_rows(S, top_k, B):
+    """Thousands of tokens in blocks of 32 (531 to 1250 blocks): the queries
+    rank enough blocks for the matrix-core scoring; every selection is
+    checked, and sampled rows against the oracle's selection."""
+    w = get_workload("tiny_2k", batch=B, n_q_heads=4, n_kv_heads=2, block_size=32, top_k=top_k)
+    _say(f"[index many blocks] S={S} bs=32 k={top_k} B={B}")
+    inp = prefill_inputs(w, seed=77 + top_k, device=DEV, seq_len=S)
     bk, sel = msa.msa_index_select(inp["q_idx"], inp["k_idx"], w.block_size, w.top_k)
     torch.cuda.synchronize()
     summ = O.pool_block_keys(host_i8(inp["k_idx"]), w.block_size)
@@ -243,7 +243,9 @@ def test_index_select_many_blocks_all_rows():
     rows = sample_rows(S, 512, 77)
     osel = O.select_blocks(host_i8(inp["q_idx"]), summ, w.block_size, w.top_k, rows)
     assert np.array_equal(gsel[:, :, rows], osel)
-    _check_all_selections(gsel, host_i8(inp["q_idx"]).astype(np.int64), summ, S, w.block_size, w.top_k)
+    qi = host_i8(inp["q_idx"]).astype(np.int64)
+    for b in range(B):
+        _check_all_selections(gsel[b:b + 1], qi[b:b + 1], summ[b:b + 1], S, w.block_size, w.top_k)
 
 
 def test_structured_128k_sampled():
