@@ -126,6 +126,26 @@ def attend(q_rows: np.ndarray, k_sel: np.ndarray, v_sel: np.ndarray, scale: floa
     return w @ v_sel
 
 
+def partial_state(q_rows: np.ndarray, k_sel: np.ndarray, v_sel: np.ndarray, scale: float):
+    """Unnormalised softmax state of query rows [n, D] over a subset of their
+    keys [m, D]: (o = sum_s e^(z_s - m) v_s, m = max_s z_s, l = sum_s
+    e^(z_s - m)), z = q.k * scale."""
+    z = (q_rows @ k_sel.T) * scale
+    m = z.max(axis=1)
+    w = np.exp(z - m[:, None])
+    return w @ v_sel, m, w.sum(axis=1)
+
+
+def merge_states(states) -> np.ndarray:
+    """Log-sum-exp combination of the states of a partition of the attended
+    keys: O = sum_i e^(m_i - M) o_i / sum_i e^(m_i - M) l_i, M = max_i m_i.
+    Equals one softmax over all the keys (the identity the main branch's
+    per-block partials rely on)."""
+    M = np.max([m for _, m, _ in states], axis=0)
+    num = sum(np.exp(m - M)[:, None] * o for o, m, _ in states)
+    den = sum(np.exp(m - M) * l for _, m, l in states)
+    return num / den[:, None]
+
 def attention_rows(q_rows, k, v, sel, rows, block_size: int, scale=None) -> np.ndarray:
     """MSA main-branch output for the given query rows.
 

@@ -210,6 +210,28 @@ def test_attention_sparse_matches_masked_dense():
         np.testing.assert_allclose(out[:, :, g * r:(g + 1) * r], ref, rtol=0, atol=1e-10)
 
 
+def test_merge_of_any_partition_equals_one_softmax():
+    """Closed form: the log-sum-exp merge of the states of any partition of
+    the keys (per block, single keys, random groups) equals softmax attention
+    over all of them."""
+    rng = _rng(3)
+    q = rng.standard_normal((6, 16))
+    k = rng.standard_normal((40, 16))
+    v = rng.standard_normal((40, 16))
+    scale = 0.25
+    ref = O.attend(q, k, v, scale)
+    for parts in ([np.arange(40)], np.array_split(np.arange(40), 5), [np.array([i]) for i in range(40)],
+                  np.array_split(rng.permutation(40), 7)):
+        got = O.merge_states([O.partial_state(q, k[p], v[p], scale) for p in parts])
+        np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+    # a state scaled consistently (o, l by e^d, m by -d) merges to the same result
+    o, m, l = O.partial_state(q, k[:20], v[:20], scale)
+    d = 3.0
+    shifted = (o * np.exp(d), m - d, l * np.exp(d))
+    got = O.merge_states([shifted, O.partial_state(q, k[20:], v[20:], scale)])
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
 def test_attention_weights_sum_to_one():
     # with every value row equal to c the output must be c exactly (up to
     # rounding): the weights of every row sum to 1
