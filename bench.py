@@ -637,6 +637,14 @@ def main():
             "flop_per_launch": flop_alg / launches_per_step,
             "design_bytes_per_step": att_design_bytes,
             "design_hbm_gbs": round(att_design_bytes / (att_ms_step * 1e-3) / 1e9, 1) if att_ms_step else None,
+            # the same kernel against the HBM roof, with the bytes the KV-outer
+            # design moves (gathered Q rows and partials) and with the
+            # measured bytes: the design is bound by this traffic, the
+            # algorithm (each tensor once) by the MFMA roof above
+            "design_frac_hbm_peak": round(att_design_bytes / (att_ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+            if att_ms_step else None,
+            "measured_frac_hbm_peak": round(traffic / (att_launch_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+            if (traffic and att_launch_ms) else None,
         },
         "merge_kernel": {
             "ms": round(mrg_ms_step, 4),
