@@ -93,7 +93,7 @@ def _workspace(op, dims, device, workspace, sizes=None):
         _need(workspace, "workspace", torch.uint8, 1, device)
         return workspace, workspace.numel()
     size = hi
-    if op == MSA_OP_PREFILL:
+    if op in (MSA_OP_PREFILL, MSA_OP_BACKWARD):
         free, _ = torch.cuda.mem_get_info(device)
         budget = int(free * 0.8)
         if size > budget:

@@ -131,6 +131,8 @@ __global__ __launch_bounds__(2 * BS, 1) void bwd_kv_kernel(
   const int crow = u * sh.nb + j;
   const int e0 = row_ptr[crow];
   const int n = row_ptr[crow + 1] - e0;
+  // a pass whose queries did not keep the block adds nothing to its sums
+  if (n == 0 && sh.acc_k != nullptr) return;
   const int n_keys = min(BS, sh.S - j * BS);
   const int tpc = kChunkRows >> sh.r_log2;  // tokens per chunk
   const int n_chunks = (n + tpc - 1) / tpc;
@@ -188,7 +190,7 @@ __global__ __launch_bounds__(2 * BS, 1) void bwd_kv_kernel(
     re.info = entries[e0 + min(cc * tpc + ((tid & (kChunkRows - 1)) >> sh.r_log2), n - 1)];
   };
   auto row_ptr_q = [&](const uint16_t* base, uint32_t ent, int rho) -> const uint16_t* {
-    const int t = (int)(ent >> 5);
+    const int t = sh.q0 + (int)(ent >> 5);
     return base + (((size_t)b * sh.S + t) * sh.Hq + g * sh.r + (rho & (sh.r - 1))) * kHeadDim;
   };
   auto load_rows = [&](int cc, const Ents& re, Stage& st) {
@@ -206,7 +208,7 @@ __global__ __launch_bounds__(2 * BS, 1) void bwd_kv_kernel(
     const int rho = tid & (kChunkRows - 1);
     const int tk = cc * tpc + (rho >> sh.r_log2);
     const bool valid = tk < n;
-    const int t = (int)(re.info >> 5);
+    const int t = sh.q0 + (int)(re.info >> 5);
     const size_t ri = ((size_t)b * sh.S + t) * sh.Hq + g * sh.r + (rho & (sh.r - 1));
     const float l2 = lse[ri] * kLog2e;
     st.lse2 = valid ? l2 : __builtin_inff();
@@ -388,30 +390,51 @@ __global__ __launch_bounds__(2 * BS, 1) void bwd_kv_kernel(
       const u32x4_t val = *reinterpret_cast<const u32x4_t*>(lds + L::kDq + rho * kNatStride + 16 * (tid & 15));
       const uint32_t e = copy_ent[m];
       if (e != 0xffffffffu) {
-        const size_t pidx = (((size_t)u * sh.S + (e >> 5)) * sh.top_k + (e & 31u)) * sh.r + (rho & (sh.r - 1));
+        const size_t pidx = (((size_t)u * sh.n_q + (e >> 5)) * sh.top_k + (e & 31u)) * sh.r + (rho & (sh.r - 1));
         *reinterpret_cast<u32x4_t*>(part_dq + pidx * kHeadDim + 8 * (tid & 15)) = val;
       }
     }
   }
 
   // ---- dK = scale * dK^T^T, dV: this lane's key, head dims 32 dt + 8 q4 + 4 hf + 0..3
+  // (over several passes the unscaled fp32 sums are added to acc_k, acc_v)
   if (key < n_keys) {
-    uint16_t* dkr = dk + kv_base + (size_t)key * kHeadDim;
-    uint16_t* dvr = dv + kv_base + (size_t)key * kHeadDim;
-    const float sc = sh.scale;
+    if (sh.acc_k != nullptr) {
+      float* akr = sh.acc_k + kv_base + (size_t)key * kHeadDim;
+      float* avr = sh.acc_v + kv_base + (size_t)key * kHeadDim;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+      for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d0 = 32 * dt + 8 * q4 + 4 * hf;
-        u32x2_t a, bq;
-        a.x = pack_bf16x2(dkt[dt][4 * q4] * sc, dkt[dt][4 * q4 + 1] * sc);
-        a.y = pack_bf16x2(dkt[dt][4 * q4 + 2] * sc, dkt[dt][4 * q4 + 3] * sc);
-        bq.x = pack_bf16x2(dvt[dt][4 * q4], dvt[dt][4 * q4 + 1]);
-        bq.y = pack_bf16x2(dvt[dt][4 * q4 + 2], dvt[dt][4 * q4 + 3]);
-        *reinterpret_cast<u32x2_t*>(dkr + d0) = a;
-        *reinterpret_cast<u32x2_t*>(dvr + d0) = bq;
-      }
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d0 = 32 * dt + 8 * q4 + 4 * hf;
+          f32x4_t ka = *reinterpret_cast<const f32x4_t*>(akr + d0);
+          f32x4_t va = *reinterpret_cast<const f32x4_t*>(avr + d0);
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            ka[x] += dkt[dt][4 * q4 + x];
+            va[x] += dvt[dt][4 * q4 + x];
+          }
+          *reinterpret_cast<f32x4_t*>(akr + d0) = ka;
+          *reinterpret_cast<f32x4_t*>(avr + d0) = va;
+        }
+    } else {
+      uint16_t* dkr = dk + kv_base + (size_t)key * kHeadDim;
+      uint16_t* dvr = dv + kv_base + (size_t)key * kHeadDim;
+      const float sc = sh.scale;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d0 = 32 * dt + 8 * q4 + 4 * hf;
+          u32x2_t a, bq;
+          a.x = pack_bf16x2(dkt[dt][4 * q4] * sc, dkt[dt][4 * q4 + 1] * sc);
+          a.y = pack_bf16x2(dkt[dt][4 * q4 + 2] * sc, dkt[dt][4 * q4 + 3] * sc);
+          bq.x = pack_bf16x2(dvt[dt][4 * q4], dvt[dt][4 * q4 + 1]);
+          bq.y = pack_bf16x2(dvt[dt][4 * q4 + 2], dvt[dt][4 * q4 + 3]);
+          *reinterpret_cast<u32x2_t*>(dkr + d0) = a;
+          *reinterpret_cast<u32x2_t*>(dvr + d0) = bq;
+        }
+    }
   }
 }
 
@@ -446,13 +469,13 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const uint16_t* __restrict_
   const int c16 = (int)(gid & 15);
   const long qr = gid >> 4;
   const int h = (int)(qr & (sh.r - 1));
-  const long t = qr >> sh.r_log2;
-  if (t >= sh.S) return;
+  const long t = qr >> sh.r_log2;  // row of the pass (token q0 + t)
+  if (t >= sh.n_q) return;
   const int u = blockIdx.y;
   const int b = u / sh.G;
   const int g = u - b * sh.G;
-  const int n = min(sh.top_k - 1, (int)(t >> sh.bs_log2)) + 1;
-  const uint16_t* src = part_dq + (((size_t)u * sh.S + t) * sh.top_k * sh.r + h) * kHeadDim + 8 * c16;
+  const int n = min(sh.top_k - 1, (int)((sh.q0 + t) >> sh.bs_log2)) + 1;
+  const uint16_t* src = part_dq + (((size_t)u * sh.n_q + t) * sh.top_k * sh.r + h) * kHeadDim + 8 * c16;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < n; s0 += 8) {
     u32x4_t val[8];
@@ -472,7 +495,24 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const uint16_t* __restrict_
   const float sc = sh.scale;
   u32x4_t wv = {pack_bf16x2(acc[0] * sc, acc[1] * sc), pack_bf16x2(acc[2] * sc, acc[3] * sc),
                 pack_bf16x2(acc[4] * sc, acc[5] * sc), pack_bf16x2(acc[6] * sc, acc[7] * sc)};
-  *reinterpret_cast<u32x4_t*>(dq + (((size_t)b * sh.S + t) * sh.Hq + g * sh.r + h) * kHeadDim + 8 * c16) = wv;
+  *reinterpret_cast<u32x4_t*>(dq + (((size_t)b * sh.S + sh.q0 + t) * sh.Hq + g * sh.r + h) * kHeadDim + 8 * c16) = wv;
+}
+
+// dk, dv from the fp32 sums of several passes: 4 head dims per thread.
+__global__ __launch_bounds__(256) void bwd_acc_kernel(const float* __restrict__ acc_k,
+                                                      const float* __restrict__ acc_v, uint16_t* __restrict__ dk,
+                                                      uint16_t* __restrict__ dv, long quads, float scale) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= quads) return;
+  const f32x4_t a = reinterpret_cast<const f32x4_t*>(acc_k)[i];
+  const f32x4_t c = reinterpret_cast<const f32x4_t*>(acc_v)[i];
+  u32x2_t wk, wv;
+  wk.x = pack_bf16x2(a[0] * scale, a[1] * scale);
+  wk.y = pack_bf16x2(a[2] * scale, a[3] * scale);
+  wv.x = pack_bf16x2(c[0], c[1]);
+  wv.y = pack_bf16x2(c[2], c[3]);
+  reinterpret_cast<u32x2_t*>(dk)[i] = wk;
+  reinterpret_cast<u32x2_t*>(dv)[i] = wv;
 }
 
 template <int BS>
@@ -512,8 +552,15 @@ hipError_t launch_bwd_kv(const BwdShape& sh, const uint16_t* q, const uint16_t* 
   }
 }
 
+hipError_t launch_bwd_acc(const BwdShape& sh, uint16_t* dk, uint16_t* dv, hipStream_t st) {
+  const long quads = (long)sh.U * sh.S * kHeadDim / 4;
+  hipLaunchKernelGGL(bwd_acc_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, st, sh.acc_k, sh.acc_v, dk,
+                     dv, quads, sh.scale);
+  return hipGetLastError();
+}
+
 hipError_t launch_bwd_dq(const BwdShape& sh, const uint16_t* part_dq, uint16_t* dq, hipStream_t st) {
-  const long threads = (long)sh.S * sh.r * 16;
+  const long threads = (long)sh.n_q * sh.r * 16;
   hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)((threads + 255) / 256), (unsigned)sh.U), dim3(256), 0, st, part_dq,
                      dq, sh);
   return hipGetLastError();

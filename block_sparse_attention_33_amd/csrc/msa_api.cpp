@@ -382,13 +382,20 @@ int run_prefill(const Dims& dc, long q0, long n_q, long q_stride, const uint16_t
 }
 
 
-// Backward workspace: delta, the inversion of sel (as in a whole prefill)
-// and the bf16 dq partials of every (query row, selection slot).
+// Backward workspace: delta of every row, the inversion of sel for the
+// query rows of one pass (as in a prefill), one bf16 dq partial per (query
+// row of the pass, selection slot), and -- when the pass holds fewer rows
+// than the sequence -- fp32 sums of dK and dV over the passes.
 struct BackwardLayout {
-  size_t delta, counts, hist, row_ptr, item_ptr, entries, items, part_dq, total;
+  size_t delta, counts, hist, row_ptr, item_ptr, entries, items, part_dq, acc_k, acc_v, total;
 };
 
-BackwardLayout backward_layout(const Dims& d, const PrefillPlan& p) {
+constexpr long kBackwardPassGranule = 256;  // query rows of a pass: the whole sequence or a multiple of this
+
+BackwardLayout backward_layout(const Dims& d, long pass_rows) {
+  const Dims dc = chunk_dims(d, pass_rows);
+  const PrefillPlan p = plan_prefill(dc);
+  const bool passes = pass_rows < d.S;
   BackwardLayout L{};
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -401,11 +408,27 @@ BackwardLayout backward_layout(const Dims& d, const PrefillPlan& p) {
   L.hist = take((size_t)d.U * p.n_chunks * d.nb * 4);
   L.row_ptr = take((size_t)(p.rows + 1) * 4);
   L.item_ptr = take((size_t)(p.rows + 1) * 4);
-  L.entries = take((size_t)d.U * d.S * d.k * 4);
+  L.entries = take((size_t)d.U * pass_rows * d.k * 4);
   L.items = take((size_t)(d.U * p.n_ranges * p.max_items_per_range + 1) * 8);
-  L.part_dq = take((size_t)d.U * d.S * d.k * d.r * d.D * 2);
+  L.part_dq = take((size_t)d.U * pass_rows * d.k * d.r * d.D * 2);
+  L.acc_k = take(passes ? (size_t)d.U * d.S * d.D * 4 : 0);
+  L.acc_v = take(passes ? (size_t)d.U * d.S * d.D * 4 : 0);
   L.total = off;
   return L;
+}
+
+// Query rows per backward pass for a workspace of ws_bytes: the whole
+// sequence when the workspace holds it, else the largest multiple of the
+// granule that fits (0: not even one granule fits).
+long backward_pass_rows(const Dims& d, size_t ws_bytes) {
+  if (backward_layout(d, d.S).total <= ws_bytes) return d.S;
+  long lo = 0, hi = (d.S - 1) / kBackwardPassGranule;  // granules: hi * granule < S
+  while (lo < hi) {
+    const long mid = (lo + hi + 1) / 2;
+    if (backward_layout(d, mid * kBackwardPassGranule).total <= ws_bytes) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo * kBackwardPassGranule;
 }
 
 // Whole prefill (msa_prefill, msa_prefill_lse), arguments checked.
@@ -494,7 +517,8 @@ int msa_workspace_bytes(int op, const msa_dims* dims, size_t* min_bytes, size_t*
     }
     case MSA_OP_BACKWARD: {
       if (d.k > kMaxSparseTopK || d.nb > msa::kMaxInvertBlocks) return MSA_ERR_UNSUPPORTED;
-      lo = hi = backward_layout(d, plan_prefill(d)).total;
+      hi = backward_layout(d, d.S).total;
+      lo = d.S > kBackwardPassGranule ? std::min(hi, backward_layout(d, kBackwardPassGranule).total) : hi;
       break;
     }
     case MSA_OP_DECODE: {
@@ -567,8 +591,10 @@ int msa_prefill_backward(const msa_dims* dims, const uint16_t* q, const uint16_t
   if (d.k > kMaxSparseTopK) return MSA_ERR_UNSUPPORTED;
   if (d.nb > msa::kMaxInvertBlocks) return MSA_ERR_UNSUPPORTED;
   if (!q || !k || !v || !out || !dout || !lse || !sel || !dq || !dk || !dv) return MSA_ERR_INVALID_ARG;
-  const PrefillPlan P = plan_prefill(d);
-  const BackwardLayout L = backward_layout(d, P);
+  if (ws == nullptr || ((uintptr_t)ws) % kAlign != 0) return MSA_ERR_WORKSPACE;
+  const long T = backward_pass_rows(d, ws_bytes);
+  if (T == 0) return MSA_ERR_WORKSPACE;
+  const BackwardLayout L = backward_layout(d, T);
   st = check_ws(ws, ws_bytes, L.total);
   if (st != MSA_OK) return st;
   hipStream_t s = (hipStream_t)stream;
@@ -581,21 +607,8 @@ int msa_prefill_backward(const msa_dims* dims, const uint16_t* q, const uint16_t
   uint32_t* entries = reinterpret_cast<uint32_t*>(base + L.entries);
   int2* items = reinterpret_cast<int2*>(base + L.items);
   uint16_t* part_dq = reinterpret_cast<uint16_t*>(base + L.part_dq);
+  const bool passes = T < d.S;
   const int U = (int)d.U, S = (int)d.S, bs = (int)d.bs, nb = (int)d.nb, K = (int)d.k;
-  msa::ChunkPlan cp;
-  cp.T = (int)P.T;
-  cp.m = (int)P.m;
-  cp.tpc = (int)P.tpc;
-  cp.n_chunks = (int)P.n_chunks;
-  cp.n_ranges = (int)P.n_ranges;
-  cp.q_stride = S;
-  const int tpi = (int)P.tokens_per_item;
-  MSA_LAUNCH_NAMED("bwd_delta", s, msa::launch_bwd_delta(out, dout, delta, d.B * d.S * d.Hq, s));
-  MSA_LAUNCH_NAMED("chunk_hist", s, msa::launch_chunk_hist(sel, hist, U, S, nb, bs, K, cp, 0, s));
-  MSA_LAUNCH_NAMED("chunk_total", s, msa::launch_chunk_total(hist, counts, U, nb, cp, s));
-  MSA_LAUNCH_NAMED("scan", s, msa::launch_scan(counts, row_ptr, item_ptr, (int)P.rows, tpi, s));
-  MSA_LAUNCH_NAMED("offsets_items", s, msa::launch_offsets_items(hist, row_ptr, item_ptr, items, U, nb, cp, tpi, s));
-  MSA_LAUNCH_NAMED("scatter", s, msa::launch_scatter(sel, hist, entries, U, S, nb, bs, K, cp, 0, s));
   msa::BwdShape sh;
   sh.B = (int)d.B;
   sh.S = S;
@@ -610,8 +623,44 @@ int msa_prefill_backward(const msa_dims* dims, const uint16_t* q, const uint16_t
   sh.U = U;
   sh.scale = d.scale;
   sh.scale_log2 = d.scale * 1.4426950408889634f;
-  MSA_LAUNCH_NAMED("bwd_kv", s, msa::launch_bwd_kv(sh, q, k, v, dout, lse, delta, row_ptr, entries, dk, dv, part_dq, s));
-  MSA_LAUNCH_NAMED("bwd_dq", s, msa::launch_bwd_dq(sh, part_dq, dq, s));
+  sh.acc_k = passes ? reinterpret_cast<float*>(base + L.acc_k) : nullptr;
+  sh.acc_v = passes ? reinterpret_cast<float*>(base + L.acc_v) : nullptr;
+  MSA_LAUNCH_NAMED("bwd_delta", s, msa::launch_bwd_delta(out, dout, delta, d.B * d.S * d.Hq, s));
+  if (passes) {
+    // fp32 zeros: a fill kernel (no memset node, so the call can be captured)
+    const size_t n = (size_t)U * S * d.D;
+    MSA_LAUNCH_NAMED("fill", s, msa::launch_fill_i32(reinterpret_cast<int32_t*>(sh.acc_k), 0, n, s));
+    MSA_LAUNCH_NAMED("fill", s, msa::launch_fill_i32(reinterpret_cast<int32_t*>(sh.acc_v), 0, n, s));
+  }
+  // passes of T query rows: the rows' selections inverted into CSR rows
+  // (unit, block), then dK / dV of every kept block and the rows' dq
+  for (long q0 = 0; q0 < S; q0 += T) {
+    const long n_q = std::min(T, (long)S - q0);
+    const Dims dc = chunk_dims(d, n_q);
+    const PrefillPlan P = plan_prefill(dc);
+    msa::ChunkPlan cp;
+    cp.T = (int)P.T;
+    cp.m = (int)P.m;
+    cp.tpc = (int)P.tpc;
+    cp.n_chunks = (int)P.n_chunks;
+    cp.n_ranges = (int)P.n_ranges;
+    cp.q_stride = S;  // sel rows per unit
+    const int tpi = (int)P.tokens_per_item;
+    const int32_t* psel = sel + q0 * K;
+    const int iq0 = (int)q0, in_q = (int)n_q;
+    MSA_LAUNCH_NAMED("chunk_hist", s, msa::launch_chunk_hist(psel, hist, U, in_q, nb, bs, K, cp, iq0, s));
+    MSA_LAUNCH_NAMED("chunk_total", s, msa::launch_chunk_total(hist, counts, U, nb, cp, s));
+    MSA_LAUNCH_NAMED("scan", s, msa::launch_scan(counts, row_ptr, item_ptr, (int)P.rows, tpi, s));
+    MSA_LAUNCH_NAMED("offsets_items", s,
+                     msa::launch_offsets_items(hist, row_ptr, item_ptr, items, U, nb, cp, tpi, s));
+    MSA_LAUNCH_NAMED("scatter", s, msa::launch_scatter(psel, hist, entries, U, in_q, nb, bs, K, cp, iq0, s));
+    sh.q0 = iq0;
+    sh.n_q = in_q;
+    MSA_LAUNCH_NAMED("bwd_kv", s,
+                     msa::launch_bwd_kv(sh, q, k, v, dout, lse, delta, row_ptr, entries, dk, dv, part_dq, s));
+    MSA_LAUNCH_NAMED("bwd_dq", s, msa::launch_bwd_dq(sh, part_dq, dq, s));
+  }
+  if (passes) MSA_LAUNCH_NAMED("bwd_acc", s, msa::launch_bwd_acc(sh, dk, dv, s));
   return MSA_OK;
 }
 

@@ -110,18 +110,23 @@ hipError_t launch_merge(const PrefillShape& sh, const PassInfo& pass, const uint
 struct BwdShape {
   int B, S, Hq, G, r, r_log2, bs, bs_log2, nb, top_k, U;
   float scale, scale_log2;
+  int q0, n_q;           // this pass: query rows q0 .. q0 + n_q - 1 (CSR entries and dq partials relative to q0)
+  float *acc_k, *acc_v;  // [U, S, 128] fp32 sums of dK^T (unscaled) and dV^T over passes, or null: one pass, bf16 out
 };
 // delta[row] = sum_d dout[row][d] * out[row][d] (fp32) for rows of 128 dims.
 hipError_t launch_bwd_delta(const uint16_t* out, const uint16_t* dout, float* delta, long rows, hipStream_t st);
 // One workgroup per CSR row (unit, block), rows (u, j) with j-major order:
-// dk, dv [U, S, 128] of the block's keys and the bf16 dq partials
-// part_dq [U, S, top_k, r, 128] of every (query row, slot) of the row.
+// dk, dv [U, S, 128] of the block's keys (or their fp32 sums added to
+// acc_k, acc_v) and the bf16 dq partials part_dq [U, n_q, top_k, r, 128] of
+// every (query row, slot) of the row.
 // lse [B, S, Hq] natural log-sum-exp of the forward, delta as above.
 hipError_t launch_bwd_kv(const BwdShape& sh, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                          const uint16_t* dout, const float* lse, const float* delta, const int32_t* row_ptr,
                          const uint32_t* entries, uint16_t* dk, uint16_t* dv, uint16_t* part_dq, hipStream_t st);
-// dq [B, S, Hq, 128] = scale * sum of each row's partials.
+// dq [B, S, Hq, 128] of the pass's rows = scale * sum of each row's partials.
 hipError_t launch_bwd_dq(const BwdShape& sh, const uint16_t* part_dq, uint16_t* dq, hipStream_t st);
+// dk = bf16(scale * acc_k), dv = bf16(acc_v) after the last pass.
+hipError_t launch_bwd_acc(const BwdShape& sh, uint16_t* dk, uint16_t* dv, hipStream_t st);
 
 // Decode.
 struct DecodeShape {

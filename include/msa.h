@@ -161,12 +161,15 @@ int msa_prefill_lse(const msa_dims* dims, const uint16_t* q, const uint16_t* k, 
  * [B, S, Hq] fp32 and sel [B, G, S, top_k] int32 exactly as msa_prefill_lse
  * wrote them (sel must be a valid selection: ascending kept blocks, the own
  * block included, -1 padding).  Outputs dq [B, S, Hq, D], dk, dv [B, G, S, D]
- * bf16, every element written.  top_k <= 32.  ws/ws_bytes: at least
- * msa_workspace_bytes(MSA_OP_BACKWARD) (it holds one bf16 partial of dq per
- * (query row, kept block): B * Hq * S * top_k * D * 2 bytes -- 8.6 GB at
- * 32K tokens with 64 query heads and top_k 16 -- and the inversion of sel).
- * The backward runs whole, not in query chunks: dk and dv of a block sum
- * over every query. */
+ * bf16, every element written.  top_k <= 32.  ws/ws_bytes: between the
+ * minimum and full sizes of msa_workspace_bytes(MSA_OP_BACKWARD).  At the
+ * full size the call runs in one pass; the workspace then holds one bf16
+ * partial of dq per (query row, kept block), B * Hq * S * top_k * D * 2
+ * bytes (8.6 GB at 32K tokens with 64 query heads and top_k 16), and the
+ * inversion of sel.  A smaller workspace runs the query rows in passes of
+ * the largest multiple of 256 rows it holds, plus fp32 sums of dk and dv
+ * over the passes (2 * B * G * S * D * 4 bytes); dq is the same, dk and dv
+ * are rounded once from the fp32 sums. */
 int msa_prefill_backward(const msa_dims* dims, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                          const uint16_t* out, const uint16_t* dout, const float* lse, const int32_t* sel,
                          uint16_t* dq, uint16_t* dk, uint16_t* dv, void* ws, size_t ws_bytes, void* stream);

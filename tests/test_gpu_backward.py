@@ -234,3 +234,91 @@ def test_backward_structured_128k_sampled_and_sums():
     compare_grad(dv[:, g, j * bs:(j + 1) * bs], rv[:, g, 0], f"128k dv block {j} group {g}")
     del inp, dout, dq, dk, dv
     _free()
+
+
+# ------------------------------------------------------------------ query passes (bounded workspace)
+
+def _pass_workspace(w, S, frac):
+    """A workspace between the least one (passes of 256 query rows) and the
+    full one: frac 0 gives the least, 1 the full size."""
+    dims = msa.make_dims(w.batch, S, w.n_q_heads, w.n_kv_heads, w.block_size, w.top_k, head_dim=128)
+    lo, hi = msa.msa_workspace_bytes(msa.MSA_OP_BACKWARD, dims)
+    size = lo + int((hi - lo) * frac)
+    return torch.empty(size, dtype=torch.uint8, device=DEV), lo, hi
+
+
+def _close_to_one_pass(a, b, what):
+    """dk or dv from passes against the one-pass result: both round fp32 sums
+    of the same terms, added in another order, to bf16."""
+    x, y = a.float(), b.float()
+    d = (x - y).abs()
+    scale_max = max(float(y.abs().max()), GRAD_FLOOR)
+    scale_mean = max(float(y.abs().mean()), GRAD_FLOOR)
+    max_rel, mean_rel = float(d.max()) / scale_max, float(d.mean()) / scale_mean
+    _say(f"  {what} vs one pass: max_rel={max_rel:.2e} mean_rel={mean_rel:.2e}")
+    assert max_rel <= 2.0 ** -7 and mean_rel <= 2.0 ** -8, (what, max_rel, mean_rel)
+
+
+PASS_CASES = [
+    # name, workload overrides, seq_len, place of the workspace between least and full
+    ("tiny_2k_least", {}, None, 0.0),
+    ("tiny_2k_middle", {}, None, 0.4),
+    # (with one head per group and few kept blocks the fp32 sums outweigh the
+    # saved partials: the least workspace is then the full one)
+    ("batch2_r2_bs32_least", dict(batch=2, n_q_heads=4, n_kv_heads=2, block_size=32, top_k=8), 600, 0.0),
+    ("ragged_gqa4_bs64_least", dict(n_q_heads=8, n_kv_heads=2, block_size=64, top_k=5), 1000, 0.0),
+    ("r16_bs128_least", dict(n_q_heads=16, n_kv_heads=1, block_size=128, top_k=3), 777, 0.0),
+    ("dense_sel_bs64_least", dict(n_q_heads=8, n_kv_heads=2, block_size=64, top_k=32), 1100, 0.0),
+]
+
+
+@pytest.mark.parametrize("name,over,S", [c[:3] for c in PASS_CASES], ids=[c[0] for c in PASS_CASES])
+def test_backward_passes_small(name, over, S):
+    """A workspace smaller than the full one runs the query rows in passes:
+    dq equals the one-pass result bit for bit (each query's partials do not
+    depend on which rows share its pass), dk and dv agree with the one-pass
+    result to bf16 rounding and with the oracle to the gradient bar."""
+    frac = {c[0]: c[3] for c in PASS_CASES}[name]
+    w = get_workload("tiny_2k", **over)
+    Sn = S or w.seq_len
+    inp = prefill_inputs(w, seed=17, device="cpu", seq_len=S)
+    dout = grad_output(w, seed=17, device="cpu", seq_len=S)
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    ws, lo, hi = _pass_workspace(w, Sn, frac)
+    _say(f"[backward passes] {name} S={Sn} workspace={ws.numel()} (least {lo}, full {hi})")
+    assert lo < hi
+    out, sel, lse, dq1, dk1, dv1 = _forward_backward(d, dout.to(DEV), w.block_size, w.top_k)
+    dq, dk, dv = msa.msa_prefill_backward(d["q"], d["k"], d["v"], out, dout.to(DEV), lse, sel, w.block_size,
+                                          workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, dq1), f"{name}: dq from passes differs from one pass"
+    _close_to_one_pass(dk, dk1, f"{name} dk")
+    _close_to_one_pass(dv, dv1, f"{name} dv")
+    summ = O.pool_block_keys(inp["k_idx"].numpy(), w.block_size)
+    osel = O.select_blocks(inp["q_idx"].numpy(), summ, w.block_size, w.top_k)
+    assert np.array_equal(host_i8(sel).astype(np.int32), osel), f"{name}: selection differs"
+    rq, rk, rv = O.backward(host_f32(inp["q"]), host_f32(inp["k"]), host_f32(inp["v"]), host_f32(dout), osel,
+                            w.block_size)
+    compare_grad(dq, rq, f"{name} dq")
+    compare_grad(dk, rk, f"{name} dk")
+    compare_grad(dv, rv, f"{name} dv")
+
+
+def test_backward_passes_32k():
+    """Prefill 32K with a workspace of about an eighth of the full one
+    (passes of a few thousand query rows): dq equals the one-pass result,
+    dk and dv agree with it to bf16 rounding."""
+    w = get_workload("prefill_32k")
+    S, bs = w.seq_len, w.block_size
+    inp = prefill_inputs(w, seed=35, device=DEV)
+    dout = grad_output(w, seed=35, device=DEV)
+    out, sel, lse, dq1, dk1, dv1 = _forward_backward(inp, dout, bs, w.top_k)
+    ws, lo, hi = _pass_workspace(w, S, 0.125)
+    _say(f"[backward passes] prefill_32k workspace={ws.numel()} (least {lo}, full {hi})")
+    dq, dk, dv = msa.msa_prefill_backward(inp["q"], inp["k"], inp["v"], out, dout, lse, sel, bs, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, dq1), "32k: dq from passes differs from one pass"
+    _close_to_one_pass(dk, dk1, "32k dk")
+    _close_to_one_pass(dv, dv1, "32k dv")
+    del inp, dout, out, sel, lse, dq1, dk1, dv1, ws, dq, dk, dv
+    _free()
