@@ -269,8 +269,8 @@ def backward(q, k, v, dout, sel, block_size: int, scale=None, rows=None, kv_bloc
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     nb = -(-S // block_size)
     all_blocks = kv_blocks is None
-    blocks = np.arange(nb) if all_blocks else np.asarray(kv_blocks)
-    rows = np.arange(S) if rows is None else np.asarray(rows)
+    blocks = np.arange(nb) if all_blocks else np.asarray(kv_blocks, dtype=np.int64)
+    rows = np.arange(S) if rows is None else np.asarray(rows, dtype=np.int64)
     row_pos = {int(t): i for i, t in enumerate(rows)}
     blk_pos = {int(j): i for i, j in enumerate(blocks)}
     dq = np.zeros((B, len(rows), Hq, D), dtype=np.float64)
@@ -279,10 +279,12 @@ def backward(q, k, v, dout, sel, block_size: int, scale=None, rows=None, kv_bloc
     for b in range(B):
         for g in (range(G) if groups is None else groups):
             hs = slice(g * r, (g + 1) * r)
-            for t in range(S):
-                kept = [int(j) for j in sel[b, g, t] if j >= 0]
-                if t not in row_pos and not any(j in blk_pos for j in kept):
-                    continue
+            # the rows that matter: those asked for and those that kept one
+            # of the asked blocks (every other row contributes nothing)
+            visit = np.isin(sel[b, g], blocks).any(axis=1)
+            visit[rows] = True
+            for t in np.flatnonzero(visit):
+                t = int(t)
                 keys = selected_keys(sel[b, g, t], t, block_size, S)
                 gq, gk, gv = _query_grads(q[b, t, hs].astype(np.float64), k[b, g, keys].astype(np.float64),
                                           v[b, g, keys].astype(np.float64), dout[b, t, hs].astype(np.float64),
@@ -298,6 +300,32 @@ def backward(q, k, v, dout, sel, block_size: int, scale=None, rows=None, kv_bloc
         dkb = dkb.reshape(B, G, nb * block_size, D)[:, :, :S]
         dvb = dvb.reshape(B, G, nb * block_size, D)[:, :, :S]
     return dq, dkb, dvb
+
+
+def query_grad_rows(q_rows, k, v, dout_rows, sel, rows, block_size: int, scale=None):
+    """dq of the given query rows alone, for long sequences: a row's query
+    gradient depends only on its own q and dout and on the keys it attends
+    to, so no other row is visited.
+
+    q_rows, dout_rows: [B, len(rows), Hq, D]; k, v: [B, G, S, D] (any
+    indexable holding the bf16 inputs); sel: int32 [B, G, len(rows), top_k].
+    Returns float64 [B, len(rows), Hq, D], equal to backward(..., rows=rows)'s dq.
+    """
+    B, R, Hq, D = q_rows.shape
+    G, S = k.shape[1], k.shape[2]
+    r = Hq // G
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    dq = np.empty((B, R, Hq, D), dtype=np.float64)
+    for b in range(B):
+        for i, t in enumerate(np.asarray(rows)):
+            for g in range(G):
+                hs = slice(g * r, (g + 1) * r)
+                keys = selected_keys(sel[b, g, i], int(t), block_size, S)
+                dq[b, i, hs], _, _ = _query_grads(q_rows[b, i, hs].astype(np.float64),
+                                                  k[b, g, keys].astype(np.float64),
+                                                  v[b, g, keys].astype(np.float64),
+                                                  dout_rows[b, i, hs].astype(np.float64), scale)
+    return dq
 
 
 # --------------------------------------------------------------------------

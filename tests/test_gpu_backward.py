@@ -322,3 +322,90 @@ def test_backward_passes_32k():
     _close_to_one_pass(dv, dv1, "32k dv")
     del inp, dout, out, sel, lse, dq1, dk1, dv1, ws, dq, dk, dv
     _free()
+
+
+def test_backward_1m_passes_sampled_and_sums():
+    """Prefill 1M (64 query heads, 8 groups, block 128, top_k 16) forward and
+    backward; the backward's full workspace (about 275 GB) does not fit next
+    to the tensors, so it runs in query passes.  dq on sampled rows and dk, dv
+    of the last block of one group against the oracle; over every key, the
+    closed-form sums of dv and dk."""
+    from tests.helpers import HostBf16
+    w = get_workload("prefill_1m")
+    S, bs, K = w.seq_len, w.block_size, w.top_k
+    B, G, r = w.batch, w.n_kv_heads, w.n_q_heads // w.n_kv_heads
+    _say(f"[backward 1m] S={S}")
+    inp = prefill_inputs(w, seed=43, device=DEV)
+    dout = grad_output(w, seed=43, device=DEV)
+    out, sel, lse = msa.msa_prefill_lse(inp["q"], inp["k"], inp["v"], inp["q_idx"], inp["k_idx"], bs, K)
+    torch.cuda.synchronize()
+    _free()
+    dims = msa.make_dims(B, S, w.n_q_heads, G, bs, K)
+    lo, hi = msa.msa_workspace_bytes(msa.MSA_OP_BACKWARD, dims)
+    free, _ = torch.cuda.mem_get_info()
+    _say(f"[backward 1m] workspace least {lo / 2**30:.1f} GiB, full {hi / 2**30:.1f} GiB, free {free / 2**30:.1f} GiB")
+    assert hi > free, "the full workspace fits: the case would not run in passes"
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    dq, dk, dv = msa.msa_prefill_backward(inp["q"], inp["k"], inp["v"], out, dout, lse, sel, bs)
+    t1.record()
+    torch.cuda.synchronize()
+    _say(f"[backward 1m] backward {t0.elapsed_time(t1):.1f} ms")
+    del out, lse
+    _free()
+    # closed-form sums over every key (fp64 on the GPU, in slices of rows)
+    step = 1 << 16
+    sv = torch.zeros(B, G, 128, dtype=torch.float64, device=DEV)
+    sk = torch.zeros_like(sv)
+    av = torch.zeros_like(sv)
+    ak = torch.zeros_like(sv)
+    sd = torch.zeros_like(sv)
+    for s0 in range(0, S, step):
+        x = dv[:, :, s0:s0 + step].double()
+        sv += x.sum(2)
+        av += x.abs().sum(2)
+        x = dk[:, :, s0:s0 + step].double()
+        sk += x.sum(2)
+        ak += x.abs().sum(2)
+        n = min(step, S - s0)
+        sd += dout[:, s0:s0 + step].double().view(B, n, G, r, 128).sum((1, 3))
+    assert float((sv - sd).abs().max()) <= 2e-3 * float(av.max()), "dv rows do not sum to the dout rows"
+    assert float(sk.abs().max()) <= 2e-3 * float(ak.max()), "dk rows do not sum to zero"
+    # oracle: selection and dq of sampled rows
+    summ = O.pool_block_keys(host_i8(inp["k_idx"]), bs)
+    qi = host_i8(inp["q_idx"])
+    rows = sample_rows(S, 16, 43)
+    rows_t = torch.as_tensor(rows, device=DEV)
+    osel = O.select_blocks(qi, summ, bs, K, rows)
+    assert np.array_equal(host_i8(sel[:, :, rows_t]).astype(np.int32), osel), "selection differs on sampled rows"
+    kk, vv = HostBf16(inp["k"]), HostBf16(inp["v"])
+    _say(f"[backward 1m] oracle dq on {len(rows)} rows")
+    rq = O.query_grad_rows(host_f32(inp["q"][:, rows_t]), kk, vv, host_f32(dout[:, rows_t]), osel, rows, bs)
+    compare_grad(dq[:, rows_t], rq, "1m dq (sampled rows)")
+    # the last block: only the queries inside it can keep it (candidates are
+    # earlier blocks and the own one), so the oracle's selection of those
+    # rows is all it needs; the other rows keep nothing here
+    j, g = S // bs - 1, 3
+    tail = np.arange(j * bs, S)
+    sel_full = np.full((B, G, S, K), -1, dtype=np.int32)
+    sel_full[:, :, tail] = O.select_blocks(qi, summ, bs, K, tail)
+    tail_t = torch.as_tensor(tail, device=DEV)
+    gsel_tail = host_i8(sel[:, :, tail_t]).astype(np.int32)
+    assert np.array_equal(gsel_tail, sel_full[:, :, tail]), "selection differs on the last block's rows"
+
+    class Tail:
+        """Rows [j * bs, S) of a [B, S, Hq, D] tensor, indexed by absolute row."""
+        def __init__(self, t):
+            self.h = t[:, j * bs:].to("cpu")
+            self.shape = tuple(t.shape)
+
+        def __getitem__(self, idx):
+            b, t, hs = idx
+            return self.h[b, t - j * bs, hs].float().numpy()
+
+    _say(f"[backward 1m] oracle dk, dv of block {j}, group {g}")
+    _, rk, rv = O.backward(Tail(inp["q"]), kk, vv, Tail(dout), sel_full, bs, rows=[], kv_blocks=[j], groups=[g])
+    compare_grad(dk[:, g, j * bs:], rk[:, g, 0], f"1m dk block {j} group {g}")
+    compare_grad(dv[:, g, j * bs:], rv[:, g, 0], f"1m dv block {j} group {g}")
+    del inp, dout, sel, dq, dk, dv
+    _free()

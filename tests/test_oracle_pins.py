@@ -431,6 +431,26 @@ def test_backward_rows_and_blocks_subsets():
     for i, j in enumerate(blocks):
         np.testing.assert_allclose(sk[:, :, i], dk[:, :, j * bs:(j + 1) * bs], rtol=0, atol=1e-14)
         np.testing.assert_allclose(sv[:, :, i], dv[:, :, j * bs:(j + 1) * bs], rtol=0, atol=1e-14)
+    # no rows, or no blocks
+    eq, ek, ev = O.backward(q, k, v, dout, sel, bs, rows=[], kv_blocks=[4])
+    assert eq.shape == (1, 0, G * r, D)
+    np.testing.assert_allclose(ek[:, :, 0], dk[:, :, 32:40], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(ev[:, :, 0], dv[:, :, 32:40], rtol=0, atol=1e-14)
+    fq, fk, _ = O.backward(q, k, v, dout, sel, bs, rows=[3, 50], kv_blocks=[])
+    np.testing.assert_array_equal(fq, dq[:, [3, 50]])
+    assert fk.shape == (1, G, 0, bs, D)
+
+
+def test_query_grad_rows_matches_masked_autograd():
+    """dq of a few rows alone, from the rows' own selection, against autograd
+    of masked attention over every row."""
+    S, bs, G, r, D, top_k = 70, 8, 2, 3, 16, 3
+    q, k, v, dout, sel = _bwd_case(47, S, bs, G, r, D, top_k)
+    rq, _, _ = _autograd_grads(q, k, v, dout, _sel_mask(sel, S, bs))
+    rows = [0, 7, 8, 33, 69]
+    dq = O.query_grad_rows(q.numpy()[:, rows], k.numpy(), v.numpy(), dout.numpy()[:, rows], sel[:, :, rows], rows,
+                           bs)
+    np.testing.assert_allclose(dq, rq[:, rows], rtol=0, atol=1e-10)
 
 
 def test_lse_against_torch_logsumexp():
