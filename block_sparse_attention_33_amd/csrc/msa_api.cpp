@@ -81,6 +81,11 @@ constexpr long kMaxChunkCounters = 1L << 22;
 
 struct PrefillPlan {
   long T, n_ranges, m, tpc, n_chunks, rows, tokens_per_item, max_items_per_range;
+  // histogram chunks of a plan for at most this many queries: the rounding
+  // of tpc can give a shorter query range more chunks than a longer one
+  // (at 1M tokens, 62 for 253952 queries but 64 for 32768), so regions
+  // that serve several ranges are sized by this bound, not by n_chunks
+  long max_chunks;
 };
 
 PrefillPlan plan_prefill(const Dims& d) {
@@ -94,6 +99,7 @@ PrefillPlan plan_prefill(const Dims& d) {
   const long by_tokens = p.T / 256;
   const long by_size = std::max(1L, kMaxChunkCounters / (d.U * d.nb));
   p.m = std::max(1L, std::min(by_tokens, by_size));
+  p.max_chunks = p.m;  // n_chunks <= min(by_tokens, by_size), both monotone in S
   p.tpc = (p.T / 256 + p.m - 1) / p.m * 256;
   p.m = (p.T + p.tpc - 1) / p.tpc;
   p.n_chunks = p.m;
@@ -118,7 +124,7 @@ PrefillLayout prefill_layout(const Dims& d, const PrefillPlan& p, long units_per
   L.block_keys = take((size_t)d.U * d.nb * d.di);
   L.sel = take((size_t)d.U * d.S * d.k * 4);
   L.counts = take((size_t)p.rows * 4);
-  L.hist = take((size_t)d.U * p.n_chunks * d.nb * 4);
+  L.hist = take((size_t)d.U * p.max_chunks * d.nb * 4);
   L.row_ptr = take((size_t)(p.rows + 1) * 4);
   L.item_ptr = take((size_t)(p.rows + 1) * 4);
   L.entries = take((size_t)d.U * d.S * d.k * 4);
@@ -388,6 +394,7 @@ int run_prefill(const Dims& dc, long q0, long n_q, long q_stride, const uint16_t
 // than the sequence -- fp32 sums of dK and dV over the passes.
 struct BackwardLayout {
   size_t delta, counts, hist, row_ptr, item_ptr, entries, items, part_dq, acc_k, acc_v, total;
+  long max_chunks, max_items;  // the inversion regions' capacity, per unit
 };
 
 constexpr long kBackwardPassGranule = 256;  // query rows of a pass: the whole sequence or a multiple of this
@@ -405,7 +412,7 @@ BackwardLayout backward_layout(const Dims& d, long pass_rows) {
   };
   L.delta = take((size_t)d.B * d.S * d.Hq * 4);
   L.counts = take((size_t)p.rows * 4);
-  L.hist = take((size_t)d.U * p.n_chunks * d.nb * 4);
+  L.hist = take((size_t)d.U * p.max_chunks * d.nb * 4);  // every pass, the last and shortest too
   L.row_ptr = take((size_t)(p.rows + 1) * 4);
   L.item_ptr = take((size_t)(p.rows + 1) * 4);
   L.entries = take((size_t)d.U * pass_rows * d.k * 4);
@@ -414,6 +421,8 @@ BackwardLayout backward_layout(const Dims& d, long pass_rows) {
   L.acc_k = take(passes ? (size_t)d.U * d.S * d.D * 4 : 0);
   L.acc_v = take(passes ? (size_t)d.U * d.S * d.D * 4 : 0);
   L.total = off;
+  L.max_chunks = p.max_chunks;
+  L.max_items = p.max_items_per_range;
   return L;
 }
 
@@ -638,6 +647,10 @@ int msa_prefill_backward(const msa_dims* dims, const uint16_t* q, const uint16_t
     const long n_q = std::min(T, (long)S - q0);
     const Dims dc = chunk_dims(d, n_q);
     const PrefillPlan P = plan_prefill(dc);
+    // the pass's inversion must fit the regions sized for T rows (it does,
+    // by the bounds above; checked so that a mistake there is an error, not
+    // a write past a region)
+    if (P.n_chunks > L.max_chunks || P.max_items_per_range > L.max_items) return MSA_ERR_WORKSPACE;
     msa::ChunkPlan cp;
     cp.T = (int)P.T;
     cp.m = (int)P.m;

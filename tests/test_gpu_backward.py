@@ -351,7 +351,19 @@ def test_backward_1m_passes_sampled_and_sums():
     t1.record()
     torch.cuda.synchronize()
     _say(f"[backward 1m] backward {t0.elapsed_time(t1):.1f} ms")
-    del out, lse
+    # a quarter of the way from the least to the full workspace: five passes,
+    # the last one (32768 rows) planned with more histogram chunks than the
+    # first ones
+    ws = torch.empty(lo + (hi - lo) // 4, dtype=torch.uint8, device=DEV)
+    _say(f"[backward 1m] backward with a workspace of {ws.numel() / 2**30:.1f} GiB")
+    dq4, dk4, dv4 = msa.msa_prefill_backward(inp["q"], inp["k"], inp["v"], out, dout, lse, sel, bs, workspace=ws)
+    torch.cuda.synchronize()
+    del ws, out, lse
+    _free()
+    assert torch.equal(dq4, dq), "1m: dq differs between pass sizes"
+    _close_to_one_pass(dk4, dk, "1m dk (five passes vs two)")
+    _close_to_one_pass(dv4, dv, "1m dv (five passes vs two)")
+    del dq4, dk4, dv4
     _free()
     # closed-form sums over every key (fp64 on the GPU, in slices of rows)
     step = 1 << 16
