@@ -522,7 +522,45 @@ def main():
                                 "tflops_alg": round(cflop / (cms * 1e-3) / 1e12, 2),
                                 "frac_bf16_peak": round(cflop / (cms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
             print(f"[bench] {name_}: {cms:.3f} ms", file=sys.stderr, flush=True)
-            del cin, cout, cws
+            if name_ == "prefill_1m":
+                # its backward too: the full workspace (about 276 GB) does not
+                # fit beside the tensors, so it runs in query passes in what
+                # the binding allocates by default (80 % of the free memory)
+                cws = None
+                torch.cuda.empty_cache()
+                tout, tsel, tlse = msa.msa_prefill_lse(cin["q"], cin["k"], cin["v"], cin["q_idx"], cin["k_idx"],
+                                                       wc.block_size, wc.top_k)
+                tdout = grad_output(wc, seed=0, device=dev)
+                cout = None
+                torch.cuda.empty_cache()
+
+                def bfn():
+                    return msa.msa_prefill_backward(cin["q"], cin["k"], cin["v"], tout, tdout, tlse, tsel,
+                                                    wc.block_size, workspace=tws)
+
+                tlo, thi = msa.msa_workspace_bytes(msa.MSA_OP_BACKWARD, cdims)
+                tws = torch.empty(max(tlo, min(thi, int(torch.cuda.mem_get_info(dev)[0] * 0.8) - (20 << 30))),
+                                  dtype=torch.uint8, device=dev)
+                bfn()
+                torch.cuda.synchronize()
+                msa.profile_read()
+                msa.profile_enable(True)
+                bev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(2)]
+                for a, b in bev:
+                    a.record()
+                    bfn()
+                    b.record()
+                torch.cuda.synchronize()
+                msa.profile_enable(False)
+                bk1 = msa.profile_read()
+                bms = max(a.elapsed_time(b) for a, b in bev)
+                other_cfg[name_]["backward"] = {
+                    "workspace_gib": round(tws.numel() / 2**30, 1), "passes": bk1["bwd_kv"][0] // 2,
+                    "ms": round(bms, 2), "tflops_alg": round(2.5 * cflop / (bms * 1e-3) / 1e12, 2),
+                    "bwd_kv_ms": round(bk1["bwd_kv"][1] / 2, 2)}
+                print(f"[bench] {name_} backward: {bms:.1f} ms", file=sys.stderr, flush=True)
+                del tout, tsel, tlse, tdout, tws
+            cin = cout = cws = None
             torch.cuda.empty_cache()
 
         # the plain decode timed the same way (back to back, so the kept blocks
