@@ -324,47 +324,13 @@ def test_backward_passes_32k():
     _free()
 
 
-def test_backward_1m_passes_sampled_and_sums():
-    """Prefill 1M (64 query heads, 8 groups, block 128, top_k 16) forward and
-    backward; the backward's full workspace (about 275 GB) does not fit next
-    to the tensors, so it runs in query passes.  dq on sampled rows and dk, dv
-    of the last block of one group against the oracle; over every key, the
-    closed-form sums of dv and dk."""
+def _check_long_backward(w, inp, dout, sel, dq, dk, dv, seed, g, n_rows=16):
+    """Checks of a long backward: the closed-form sums over every key (fp64
+    on the GPU), dq of sampled rows and dk, dv of the last block of group g
+    against the oracle."""
     from tests.helpers import HostBf16
-    w = get_workload("prefill_1m")
     S, bs, K = w.seq_len, w.block_size, w.top_k
     B, G, r = w.batch, w.n_kv_heads, w.n_q_heads // w.n_kv_heads
-    _say(f"[backward 1m] S={S}")
-    inp = prefill_inputs(w, seed=43, device=DEV)
-    dout = grad_output(w, seed=43, device=DEV)
-    out, sel, lse = msa.msa_prefill_lse(inp["q"], inp["k"], inp["v"], inp["q_idx"], inp["k_idx"], bs, K)
-    torch.cuda.synchronize()
-    _free()
-    dims = msa.make_dims(B, S, w.n_q_heads, G, bs, K)
-    lo, hi = msa.msa_workspace_bytes(msa.MSA_OP_BACKWARD, dims)
-    free, _ = torch.cuda.mem_get_info()
-    _say(f"[backward 1m] workspace least {lo / 2**30:.1f} GiB, full {hi / 2**30:.1f} GiB, free {free / 2**30:.1f} GiB")
-    assert hi > free, "the full workspace fits: the case would not run in passes"
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record()
-    dq, dk, dv = msa.msa_prefill_backward(inp["q"], inp["k"], inp["v"], out, dout, lse, sel, bs)
-    t1.record()
-    torch.cuda.synchronize()
-    _say(f"[backward 1m] backward {t0.elapsed_time(t1):.1f} ms")
-    # a quarter of the way from the least to the full workspace: five passes,
-    # the last one (32768 rows) planned with more histogram chunks than the
-    # first ones
-    ws = torch.empty(lo + (hi - lo) // 4, dtype=torch.uint8, device=DEV)
-    _say(f"[backward 1m] backward with a workspace of {ws.numel() / 2**30:.1f} GiB")
-    dq4, dk4, dv4 = msa.msa_prefill_backward(inp["q"], inp["k"], inp["v"], out, dout, lse, sel, bs, workspace=ws)
-    torch.cuda.synchronize()
-    del ws, out, lse
-    _free()
-    assert torch.equal(dq4, dq), "1m: dq differs between pass sizes"
-    _close_to_one_pass(dk4, dk, "1m dk (five passes vs two)")
-    _close_to_one_pass(dv4, dv, "1m dv (five passes vs two)")
-    del dq4, dk4, dv4
-    _free()
     # closed-form sums over every key (fp64 on the GPU, in slices of rows)
     step = 1 << 16
     sv = torch.zeros(B, G, 128, dtype=torch.float64, device=DEV)
@@ -386,18 +352,18 @@ def test_backward_1m_passes_sampled_and_sums():
     # oracle: selection and dq of sampled rows
     summ = O.pool_block_keys(host_i8(inp["k_idx"]), bs)
     qi = host_i8(inp["q_idx"])
-    rows = sample_rows(S, 16, 43)
+    rows = sample_rows(S, n_rows, seed)
     rows_t = torch.as_tensor(rows, device=DEV)
     osel = O.select_blocks(qi, summ, bs, K, rows)
     assert np.array_equal(host_i8(sel[:, :, rows_t]).astype(np.int32), osel), "selection differs on sampled rows"
     kk, vv = HostBf16(inp["k"]), HostBf16(inp["v"])
-    _say(f"[backward 1m] oracle dq on {len(rows)} rows")
+    _say(f"[backward {S}] oracle dq on {len(rows)} rows")
     rq = O.query_grad_rows(host_f32(inp["q"][:, rows_t]), kk, vv, host_f32(dout[:, rows_t]), osel, rows, bs)
-    compare_grad(dq[:, rows_t], rq, "1m dq (sampled rows)")
+    compare_grad(dq[:, rows_t], rq, f"{S} dq (sampled rows)")
     # the last block: only the queries inside it can keep it (candidates are
     # earlier blocks and the own one), so the oracle's selection of those
     # rows is all it needs; the other rows keep nothing here
-    j, g = S // bs - 1, 3
+    j = (S - 1) // bs
     tail = np.arange(j * bs, S)
     sel_full = np.full((B, G, S, K), -1, dtype=np.int32)
     sel_full[:, :, tail] = O.select_blocks(qi, summ, bs, K, tail)
@@ -415,9 +381,85 @@ def test_backward_1m_passes_sampled_and_sums():
             b, t, hs = idx
             return self.h[b, t - j * bs, hs].float().numpy()
 
-    _say(f"[backward 1m] oracle dk, dv of block {j}, group {g}")
+    _say(f"[backward {S}] oracle dk, dv of block {j}, group {g}")
     _, rk, rv = O.backward(Tail(inp["q"]), kk, vv, Tail(dout), sel_full, bs, rows=[], kv_blocks=[j], groups=[g])
-    compare_grad(dk[:, g, j * bs:], rk[:, g, 0], f"1m dk block {j} group {g}")
-    compare_grad(dv[:, g, j * bs:], rv[:, g, 0], f"1m dv block {j} group {g}")
+    nt = S - j * bs  # keys of the (possibly ragged) last block
+    compare_grad(dk[:, g, j * bs:], rk[:, g, 0, :nt], f"{S} dk block {j} group {g}")
+    compare_grad(dv[:, g, j * bs:], rv[:, g, 0, :nt], f"{S} dv block {j} group {g}")
+
+
+def test_backward_1m_passes_sampled_and_sums():
+    """Prefill 1M (64 query heads, 8 groups, block 128, top_k 16) forward and
+    backward; the backward's full workspace (about 275 GB) does not fit next
+    to the tensors, so it runs in query passes.  dq on sampled rows and dk, dv
+    of the last block of one group against the oracle; over every key, the
+    closed-form sums of dv and dk."""
+    w = get_workload("prefill_1m")
+    S, bs, K = w.seq_len, w.block_size, w.top_k
+    B, G = w.batch, w.n_kv_heads
+    _say(f"[backward 1m] S={S}")
+    inp = prefill_inputs(w, seed=43, device=DEV)
+    dout = grad_output(w, seed=43, device=DEV)
+    out, sel, lse = msa.msa_prefill_lse(inp["q"], inp["k"], inp["v"], inp["q_idx"], inp["k_idx"], bs, K)
+    torch.cuda.synchronize()
+    _free()
+    dims = msa.make_dims(B, S, w.n_q_heads, G, bs, K)
+    lo, hi = msa.msa_workspace_bytes(msa.MSA_OP_BACKWARD, dims)
+    free, _ = torch.cuda.mem_get_info()
+    _say(f"[backward 1m] workspace least {lo / 2**30:.1f} GiB, full {hi / 2**30:.1f} GiB, free {free / 2**30:.1f} GiB")
+    assert hi > free, "the full workspace fits: the case would not run in passes"
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    dq, dk, dv = msa.msa_prefill_backward(inp["q"], inp["k"], inp["v"], out, dout, lse, sel, bs)
+    t1.record()
+    torch.cuda.synchronize()
+    _say(f"[backward 1m] backward, with its allocations: {t0.elapsed_time(t1):.1f} ms")
+    # a quarter of the way from the least to the full workspace: five passes,
+    # the last one (32768 rows) planned with more histogram chunks than the
+    # first ones
+    ws = torch.empty(lo + (hi - lo) // 4, dtype=torch.uint8, device=DEV)
+    _say(f"[backward 1m] backward with a workspace of {ws.numel() / 2**30:.1f} GiB")
+    dq4, dk4, dv4 = msa.msa_prefill_backward(inp["q"], inp["k"], inp["v"], out, dout, lse, sel, bs, workspace=ws)
+    torch.cuda.synchronize()
+    del ws, out, lse
+    _free()
+    assert torch.equal(dq4, dq), "1m: dq differs between pass sizes"
+    _close_to_one_pass(dk4, dk, "1m dk (five passes vs two)")
+    _close_to_one_pass(dv4, dv, "1m dv (five passes vs two)")
+    del dq4, dk4, dv4
+    _free()
+    _check_long_backward(w, inp, dout, sel, dq, dk, dv, seed=43, g=3)
+    del inp, dout, sel, dq, dk, dv
+    _free()
+
+
+def test_ragged_300k_forward_and_backward_passes():
+    """300000 tokens (last block 96 tokens; four query chunks, the last one
+    shorter): the forward on sampled rows, then the backward with a fifth of
+    the way from the least to the full workspace (passes, the last one
+    shorter), against the oracle."""
+    from tests.helpers import compare_out, oracle_prefill_rows
+    w = get_workload("prefill_1m", seq_len=300000)
+    S, bs, K = w.seq_len, w.block_size, w.top_k
+    _say(f"[ragged 300k] S={S}")
+    inp = prefill_inputs(w, seed=47, device=DEV)
+    dout = grad_output(w, seed=47, device=DEV)
+    out, sel, lse = msa.msa_prefill_lse(inp["q"], inp["k"], inp["v"], inp["q_idx"], inp["k_idx"], bs, K)
+    torch.cuda.synchronize()
+    _free()
+    rows = sample_rows(S, 48, 47)
+    rows[-1] = S - 1
+    rows_t = torch.as_tensor(rows, device=DEV)
+    _say(f"[ragged 300k] oracle forward on {len(rows)} rows")
+    _, osel, oout = oracle_prefill_rows(inp, w, rows)
+    assert np.array_equal(host_i8(sel[:, :, rows_t]).astype(np.int32), osel), "selection differs on sampled rows"
+    compare_out(out[:, rows_t], oout, "300k out (sampled rows)")
+    ws, lo, hi = _pass_workspace(w, S, 0.2)
+    _say(f"[ragged 300k] backward, workspace {ws.numel() / 2**30:.1f} GiB (least {lo / 2**30:.1f}, full {hi / 2**30:.1f})")
+    dq, dk, dv = msa.msa_prefill_backward(inp["q"], inp["k"], inp["v"], out, dout, lse, sel, bs, workspace=ws)
+    torch.cuda.synchronize()
+    del ws, out, lse
+    _free()
+    _check_long_backward(w, inp, dout, sel, dq, dk, dv, seed=47, g=5)
     del inp, dout, sel, dq, dk, dv
     _free()
