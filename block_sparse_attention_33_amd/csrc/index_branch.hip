@@ -337,12 +337,28 @@ __global__ __launch_bounds__(256) void index_topk_mfma_kernel(const int8_t* __re
 
   const long* kb8 = reinterpret_cast<const long*>(block_keys + (size_t)u * nb_stride * kIdxDim);
   const int n_cand = kp > 0 ? c_last : 0;
+  // the next chunk's summaries (8 bytes x 8 per thread) load while the
+  // current chunk is scored
+  long pre[CH * 8 / 256];
+  auto fetch = [&](int from) {
+    const int n = min(CH, n_cand - from);
+#pragma unroll
+    for (int m = 0; m < CH * 8 / 256; ++m) {
+      const int i = tid + 256 * m;
+      pre[m] = i < n * 8 ? kb8[(size_t)from * 8 + i] : 0;
+    }
+  };
+  if (n_cand > 0) fetch(0);
   for (int base = 0; base < n_cand; base += CH) {
     const int n = min(CH, n_cand - base);
     __syncthreads();
-    for (int i = tid; i < n * 8; i += 256)
-      *reinterpret_cast<long*>(sk + (i >> 3) * kSumStride + 8 * (i & 7)) = kb8[(size_t)base * 8 + i];
+#pragma unroll
+    for (int m = 0; m < CH * 8 / 256; ++m) {
+      const int i = tid + 256 * m;
+      *reinterpret_cast<long*>(sk + (i >> 3) * kSumStride + 8 * (i & 7)) = pre[m];
+    }
     __syncthreads();
+    if (base + CH < n_cand) fetch(base + CH);
     for (int tile = 0; tile < n; tile += 32) {
       // rows past the chunk's n hold stale summaries: their candidates are
       // >= c for every query of the workgroup and are skipped below
@@ -352,6 +368,12 @@ __global__ __launch_bounds__(256) void index_topk_mfma_kernel(const int8_t* __re
       for (int ks = 0; ks < 4; ++ks)
         acc = __builtin_amdgcn_mfma_i32_32x32x16_i8(*reinterpret_cast<const long*>(arow + 16 * ks), qb[ks], acc, 0,
                                                     0, 0);
+      // most tiles, once the lists have filled, hold no candidate above any
+      // lane's threshold: one test for the wave skips the 16 per-candidate ones
+      int best = INT_MIN;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) best = max(best, acc[i]);
+      if (!__any(best > thr)) continue;
       if (__any(nbuf > kTopkBufMfma - 16)) merge_buf();
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
