@@ -195,7 +195,10 @@ def msa_prefill_lse(q, k, v, q_idx, k_idx, block_size: int, top_k: int, softmax_
 def msa_prefill_backward(q, k, v, out, dout, lse, sel, block_size: int, softmax_scale: float = 0.0,
                          workspace=None):
     """Gradients of the main branch with the selection fixed -> (dq [B, S, Hq, D],
-    dk [B, G, S, D], dv [B, G, S, D]) bf16, from the forward's out, lse and sel."""
+    dk [B, G, S, D], dv [B, G, S, D]) bf16, from the forward's out, lse and sel.
+    Without a workspace, one of the full size is allocated when it fits in 80 %
+    of the free device memory, else the largest that does (the library then
+    runs the query rows in passes; at least the minimum size is needed)."""
     _need(q, "q", torch.bfloat16, 4)
     dev = q.device
     B, S, Hq, D = q.shape
