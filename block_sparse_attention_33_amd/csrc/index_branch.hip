@@ -292,9 +292,16 @@ __global__ __launch_bounds__(256) void index_topk_mfma_kernel(const int8_t* __re
                                                          int32_t* __restrict__ sel, int S,
                                                          int nb_stride, int bs_log2, int top_k, int pos0,
                                                          int q_stride, int sel_stride) {
-  constexpr int CH = 256;  // summaries per LDS chunk
+  // 128 summaries per LDS chunk and 4-byte buffer entries: 33 KiB of LDS,
+  // so four workgroups share a CU (the kernel waits on its MFMA results,
+  // LDS reads and wave-wide tests far more than it issues; measured on
+  // MI355X, 1M tokens: 23.4 ms with 66 KiB and two workgroups per CU,
+  // 16.5 ms with four)
+  constexpr int CH = 128;
   __shared__ __align__(16) char sk[CH * kSumStride];
-  __shared__ int2 buf[kTopkBufMfma][256];  // per lane: (score, block) waiting for the list
+  // per lane: score * 256 + (block - base), waiting for the list; |score| <=
+  // 64 * 128 * 128 = 2^20, so the packed entry fits 29 bits and a sign
+  __shared__ int buf[kTopkBufMfma][256];
 
   const int u = blockIdx.y;
   const int tid = threadIdx.x;
@@ -324,11 +331,12 @@ __global__ __launch_bounds__(256) void index_topk_mfma_kernel(const int8_t* __re
   }
   int thr = INT_MIN;  // Ls[KCAP - 1] as of the last merge
   int nbuf = 0;
+  int base = 0;  // first candidate of the current chunk (entries hold block - base)
   auto merge_buf = [&]() {
     for (int i = 0; __any(i < nbuf); ++i) {
       if (i < nbuf) {
-        const int2 e = buf[i][tid];
-        topk_insert<KCAP>(Ls, Li, e.x, e.y);
+        const int e = buf[i][tid];
+        topk_insert<KCAP>(Ls, Li, e >> 8, base + (e & 255));
       }
     }
     nbuf = 0;
@@ -349,7 +357,7 @@ __global__ __launch_bounds__(256) void index_topk_mfma_kernel(const int8_t* __re
     }
   };
   if (n_cand > 0) fetch(0);
-  for (int base = 0; base < n_cand; base += CH) {
+  for (base = 0; base < n_cand; base += CH) {
     const int n = min(CH, n_cand - base);
     __syncthreads();
 #pragma unroll
@@ -379,11 +387,12 @@ __global__ __launch_bounds__(256) void index_topk_mfma_kernel(const int8_t* __re
       for (int i = 0; i < 16; ++i) {
         const int j = base + tile + c_row(i, hf);
         if (j < c && acc[i] > thr) {
-          buf[nbuf][tid] = make_int2(acc[i], j);
+          buf[nbuf][tid] = acc[i] * 256 | (j - base);
           ++nbuf;
         }
       }
     }
+    merge_buf();  // entries hold block - base: the buffer empties with its chunk
   }
   merge_buf();
 
