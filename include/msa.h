@@ -110,8 +110,9 @@ int msa_version(void);
 /* Workspace sizes in bytes for `op` at `dims`.
  * *min_bytes: the least workspace the call accepts.  *full_bytes: the size at
  * which the call runs in one pass (MSA_OP_PREFILL processes the (batch,
- * group) units in as few passes as the workspace allows; every size between
- * the two works).  Either output pointer may be NULL. */
+ * group) units in as few passes as the workspace allows, MSA_OP_BACKWARD
+ * the query rows in passes of the largest multiple of 256 rows it holds;
+ * every size between the two works).  Either output pointer may be NULL. */
 int msa_workspace_bytes(int op, const msa_dims* dims, size_t* min_bytes, size_t* full_bytes);
 
 /* Index branch, pooling step: block summary keys.
