@@ -18,7 +18,7 @@ from . import _lib
 from ._lib import MSA_OP_BACKWARD, MSA_OP_DECODE, MSA_OP_INDEX, MSA_OP_POOL, MSA_OP_PREFILL, MsaDims  # noqa: F401
 
 __all__ = [
-    "MsaError", "make_dims", "profile_enable", "profile_read", "msa_workspace_bytes", "msa_pool_block_keys", "msa_index_select",
+    "MsaError", "make_dims", "profile_enable", "profile_read", "msa_workspace_bytes", "msa_backward_pass_rows", "msa_pool_block_keys", "msa_index_select",
     "msa_prefill", "msa_prefill_lse", "msa_prefill_backward", "msa_prefill_chunk", "msa_decode", "msa_decode_init", "msa_decode_step", "MSA_OP_POOL", "MSA_OP_INDEX", "MSA_OP_PREFILL", "MSA_OP_DECODE", "MSA_OP_BACKWARD",
 ]
 
@@ -51,6 +51,15 @@ def msa_workspace_bytes(op, dims: MsaDims):
 def profile_enable(on: bool = True):
     """Record every launch of the library's kernels with HIP events."""
     _check(_lib.load().msa_profile_enable(1 if on else 0), "msa_profile_enable")
+
+
+def msa_backward_pass_rows(dims: MsaDims, ws_bytes: int) -> int:
+    """Query rows per backward pass with a workspace of ws_bytes (seq_len:
+    one pass; 0: below the minimum)."""
+    rows = ctypes.c_int32(0)
+    _check(_lib.load().msa_backward_pass_rows(ctypes.byref(dims), ctypes.c_size_t(ws_bytes), ctypes.byref(rows)),
+           "msa_backward_pass_rows")
+    return rows.value
 
 
 def profile_read():

@@ -44,6 +44,7 @@ SIGNATURES = {
     "msa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "msa_version": (ctypes.c_int, []),
     "msa_workspace_bytes": (ctypes.c_int, [ctypes.c_int, _DIMS, _SIZE_P, _SIZE_P]),
+    "msa_backward_pass_rows": (ctypes.c_int, [_DIMS, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int32)]),
     "msa_pool_block_keys": (ctypes.c_int, [_DIMS, _P, _P, _P]),
     "msa_index_select": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "msa_prefill": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),

@@ -502,7 +502,17 @@ const char* msa_status_string(int status) {
   }
 }
 
-int msa_version(void) { return 10200; }
+int msa_version(void) { return 10300; }
+
+int msa_backward_pass_rows(const msa_dims* dims, size_t ws_bytes, int32_t* rows) {
+  Dims d;
+  int st = check_dims(dims, &d);
+  if (st != MSA_OK) return st;
+  if (d.k > kMaxSparseTopK || d.nb > msa::kMaxInvertBlocks) return MSA_ERR_UNSUPPORTED;
+  if (!rows) return MSA_ERR_INVALID_ARG;
+  *rows = (int32_t)backward_pass_rows(d, ws_bytes);
+  return MSA_OK;
+}
 
 int msa_workspace_bytes(int op, const msa_dims* dims, size_t* min_bytes, size_t* full_bytes) {
   Dims d;

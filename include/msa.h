@@ -115,6 +115,13 @@ int msa_version(void);
  * every size between the two works).  Either output pointer may be NULL. */
 int msa_workspace_bytes(int op, const msa_dims* dims, size_t* min_bytes, size_t* full_bytes);
 
+/* Query rows per pass of msa_prefill_backward with a workspace of ws_bytes
+ * (host only, nothing enqueued): *rows = seq_len when the full workspace
+ * fits (one pass), else the largest multiple of 256 rows that fits, or 0
+ * when ws_bytes is below the minimum (the backward then returns
+ * MSA_ERR_WORKSPACE).  The backward runs ceil(seq_len / *rows) passes. */
+int msa_backward_pass_rows(const msa_dims* dims, size_t ws_bytes, int32_t* rows);
+
 /* Index branch, pooling step: block summary keys.
  * k_idx [B, G, S, di] int8 -> block_keys [B, G, nb, di] int8.
  * Needs no workspace. */

@@ -48,7 +48,7 @@ def test_status_strings(lib):
                          (-3, "MSA_ERR_WORKSPACE"), (-4, "MSA_ERR_HIP")]:
         assert lib.msa_status_string(code).decode().startswith(prefix)
     assert lib.msa_status_string(12345).decode() == "unknown MSA status"
-    assert lib.msa_version() == 10200
+    assert lib.msa_version() == 10300
 
 
 def D(**kw):
@@ -175,6 +175,18 @@ def test_backward_validation(lib):
     acc = 2 * 2 * 8 * 3000 * 128 * 4
     part256 = 2 * 64 * 256 * 8 * 128 * 2
     assert acc + part256 < lo < acc + part256 + 2 * 3000 * 64 * 4 + (4 << 20)
+    # pass planning on the host: full -> one pass, least -> 256 rows, in
+    # between a multiple of 256 that grows with the workspace, below -> 0
+    rows = ctypes.c_int32(-1)
+    for size, want in ((hi, 3000), (lo, 256), (lo - 1, 0), (0, 0)):
+        assert lib.msa_backward_pass_rows(ctypes.byref(dims), size, ctypes.byref(rows)) == 0
+        assert rows.value == want, (size, rows.value, want)
+    prev = 256
+    for f in (0.2, 0.5, 0.9):
+        assert lib.msa_backward_pass_rows(ctypes.byref(dims), lo + int((hi - lo) * f), ctypes.byref(rows)) == 0
+        assert rows.value % 256 == 0 and prev <= rows.value < 3000, (f, rows.value)
+        prev = rows.value
+    assert lib.msa_backward_pass_rows(ctypes.byref(dims), hi, None) == -1
     # a sequence of at most 256 rows runs in one pass: min = full
     st, lo1, hi1 = _ws(lib, _lib.MSA_OP_BACKWARD, D(batch=1, seq_len=256, top_k=2))
     assert st == 0 and lo1 == hi1

@@ -418,7 +418,9 @@ def test_backward_1m_passes_sampled_and_sums():
     # the last one (32768 rows) planned with more histogram chunks than the
     # first ones
     ws = torch.empty(lo + (hi - lo) // 4, dtype=torch.uint8, device=DEV)
-    _say(f"[backward 1m] backward with a workspace of {ws.numel() / 2**30:.1f} GiB")
+    rows = msa.msa_backward_pass_rows(dims, ws.numel())
+    _say(f"[backward 1m] backward with a workspace of {ws.numel() / 2**30:.1f} GiB: passes of {rows} rows")
+    assert 0 < rows < S and rows % 256 == 0 and -(-S // rows) >= 4
     dq4, dk4, dv4 = msa.msa_prefill_backward(inp["q"], inp["k"], inp["v"], out, dout, lse, sel, bs, workspace=ws)
     torch.cuda.synchronize()
     del ws, out, lse
