@@ -521,8 +521,7 @@ hipError_t launch_bwd_kv_bs(const BwdShape& sh, const uint16_t* q, const uint16_
                             const uint32_t* entries, uint16_t* dk, uint16_t* dv, uint16_t* part_dq,
                             hipStream_t st) {
   constexpr int bytes = BwdLds<BS>::kBytes;
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_kv_kernel<BS>),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  const hipError_t attr = ensure_dynamic_lds(reinterpret_cast<const void*>(&bwd_kv_kernel<BS>), bytes);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(bwd_kv_kernel<BS>, dim3((unsigned)(sh.U * sh.nb)), dim3(2 * BS), bytes, st, q, k, v, dout, lse,
                      delta, row_ptr, entries, dk, dv, part_dq, sh);

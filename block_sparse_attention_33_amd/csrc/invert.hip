@@ -169,9 +169,8 @@ hipError_t launch_chunk_hist(const int32_t* sel, int32_t* H, int units, int S, i
   int bs_log2 = 0;
   while ((1 << bs_log2) < bs) ++bs_log2;
   const size_t lds = (size_t)nb * 4;
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_hist_kernel),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                     kMaxInvertBlocks * 4);
+  const hipError_t attr =
+      ensure_dynamic_lds(reinterpret_cast<const void*>(&chunk_hist_kernel), kMaxInvertBlocks * 4);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(chunk_hist_kernel, dim3(cp.n_chunks, units), dim3(256), lds, st, sel, H, S, nb, bs_log2,
                      top_k, cp, q0);
@@ -204,9 +203,7 @@ hipError_t launch_scatter(const int32_t* sel, const int32_t* H, uint32_t* entrie
   int bs_log2 = 0;
   while ((1 << bs_log2) < bs) ++bs_log2;
   const size_t lds = (size_t)nb * 4;
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&scatter_kernel),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                     kMaxInvertBlocks * 4);
+  const hipError_t attr = ensure_dynamic_lds(reinterpret_cast<const void*>(&scatter_kernel), kMaxInvertBlocks * 4);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(scatter_kernel, dim3(cp.n_chunks, units), dim3(256), lds, st, sel, H, entries, S, nb, bs_log2,
                      top_k, cp, q0);

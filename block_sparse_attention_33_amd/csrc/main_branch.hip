@@ -598,20 +598,15 @@ hipError_t launch_attend_bs(const PrefillShape& sh, const PassInfo& pass, const 
   int r_log2 = 0;
   while ((1 << r_log2) < sh.r) ++r_log2;
   // one workgroup per CU, never more workgroups than items
-  static int n_cu = 0;
-  if (n_cu == 0) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-  }
+  int n_cu = 0;
+  const hipError_t ce = current_cu_count(&n_cu);
+  if (ce != hipSuccess) return ce;
   if (max_items <= 0) return hipSuccess;
   const unsigned grid = (unsigned)std::max<long>(1, std::min<long>((long)n_cu, (long)max_items));
   // two K/V buffers and, per wave, a ring of three items' entries
   const int lds_bytes = 2 * Tile<BS>::kLdsBytes + 4 * 3 * kItemChunks * (64 >> r_log2) * 4;
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&attend_kernel<BS>),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                     2 * Tile<BS>::kLdsBytes + 4 * 3 * kItemChunks * 64 * 4);
+  const hipError_t attr = ensure_dynamic_lds(reinterpret_cast<const void*>(&attend_kernel<BS>),
+                                            2 * Tile<BS>::kLdsBytes + 4 * 3 * kItemChunks * 64 * 4);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(attend_kernel<BS>, dim3(grid), dim3(256), lds_bytes, st, q, k, v, row_ptr, item_ptr, items,
                      entries, part_o, part_ml, sh, pass, r_log2);
@@ -831,9 +826,8 @@ hipError_t launch_dense(const PrefillShape& sh, const uint16_t* q, const uint16_
   switch (sh.bs) {
 #define MSA_DENSE_LAUNCH(BS_, NCT_)                                                                          \
   {                                                                                                           \
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&dense_kernel<BS_, NCT_>), \
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize,           \
-                                                       2 * Tile<BS_>::kLdsBytes);                             \
+    const hipError_t attr = ensure_dynamic_lds(reinterpret_cast<const void*>(&dense_kernel<BS_, NCT_>),        \
+                                               2 * Tile<BS_>::kLdsBytes);                                     \
     if (attr != hipSuccess) return attr;                                                                      \
     hipLaunchKernelGGL((dense_kernel<BS_, NCT_>), grid, dim3(512 / NCT_), 2 * Tile<BS_>::kLdsBytes, st, q, k, v, \
                        out, sh, r_log2);                                                                      \

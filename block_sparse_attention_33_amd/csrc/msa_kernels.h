@@ -9,6 +9,12 @@
 
 namespace msa {
 
+// Compute units of the current device (queried once per device).
+hipError_t current_cu_count(int* n_cu);
+// Raises the dynamic-LDS limit of kernel `fn` on the current device to at
+// least `bytes` (once per device and kernel; thread-safe).
+hipError_t ensure_dynamic_lds(const void* fn, int bytes);
+
 // Tokens of one main-branch work item hold at most this many query rows
 // (tokens x heads of the group).
 constexpr int kItemRows = 256;
