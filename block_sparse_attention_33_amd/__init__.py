@@ -19,7 +19,7 @@ from ._lib import MSA_OP_BACKWARD, MSA_OP_DECODE, MSA_OP_INDEX, MSA_OP_POOL, MSA
 
 __all__ = [
     "MsaError", "make_dims", "profile_enable", "profile_read", "msa_workspace_bytes", "msa_backward_pass_rows", "msa_pool_block_keys", "msa_index_select",
-    "msa_prefill", "msa_prefill_lse", "msa_prefill_backward", "msa_prefill_chunk", "msa_decode", "msa_decode_init", "msa_decode_step", "MSA_OP_POOL", "MSA_OP_INDEX", "MSA_OP_PREFILL", "MSA_OP_DECODE", "MSA_OP_BACKWARD",
+    "msa_prefill", "msa_prefill_lse", "msa_prefill_backward", "msa_prefill_chunk", "msa_decode", "msa_decode_noalloc", "msa_decode_init", "msa_decode_step", "MSA_OP_POOL", "MSA_OP_INDEX", "MSA_OP_PREFILL", "MSA_OP_DECODE", "MSA_OP_BACKWARD",
 ]
 
 
@@ -264,6 +264,35 @@ def msa_decode(q, q_idx, k_cache, v_cache, block_keys, block_size: int, top_k: i
                                   _ptr(block_keys), _ptr(out), _ptr(sel), _ptr(ws), ws_bytes, _stream(dev)),
            "msa_decode")
     return (out, sel) if return_sel else out
+
+
+def msa_decode_noalloc(q, q_idx, k_cache, v_cache, block_keys, block_size: int, top_k: int, out,
+                       softmax_scale: float = 0.0, sel=None):
+    """msa_decode through the entry point that allocates nothing: the caller
+    passes the output (and optionally sel); the library's scratch is a fixed
+    per-device array.  Returns out (and sel when given)."""
+    _need(q, "q", torch.bfloat16, 3)
+    dev = q.device
+    _need(q_idx, "q_idx", torch.int8, 3, dev)
+    _need(k_cache, "k_cache", torch.bfloat16, 4, dev)
+    _need(v_cache, "v_cache", torch.bfloat16, 4, dev)
+    _need(block_keys, "block_keys", torch.int8, 4, dev)
+    _need(out, "out", torch.bfloat16, 3, dev)
+    B, Hq, D = q.shape
+    _, G, L, _ = k_cache.shape
+    nb = -(-L // block_size)
+    if k_cache.shape != (B, G, L, D) or v_cache.shape != k_cache.shape or out.shape != q.shape:
+        raise ValueError("k_cache/v_cache must be [B, G, L, D] and out shaped like q")
+    if q_idx.shape[:2] != (B, G) or block_keys.shape != (B, G, nb, q_idx.shape[2]):
+        raise ValueError("q_idx must be [B, G, di] and block_keys [B, G, nb, di]")
+    if sel is not None:
+        _need(sel, "sel", torch.int32, 3, dev)
+    dims = make_dims(B, L, Hq, G, block_size, top_k, head_dim=D, idx_dim=q_idx.shape[2],
+                     softmax_scale=softmax_scale)
+    _check(_lib.load().msa_decode_noalloc(ctypes.byref(dims), _ptr(q), _ptr(q_idx), _ptr(k_cache), _ptr(v_cache),
+                                          _ptr(block_keys), _ptr(out), _ptr(sel), _stream(dev)),
+           "msa_decode_noalloc")
+    return (out, sel) if sel is not None else out
 
 
 def _cache_dims(k_cache, block_size, top_k, n_q_heads, idx_dim, softmax_scale=0.0):

@@ -9,6 +9,8 @@ MSA_ERR_INVALID_ARG = -1
 MSA_ERR_UNSUPPORTED = -2
 MSA_ERR_WORKSPACE = -3
 MSA_ERR_HIP = -4
+MSA_ERR_SCRATCH = -5
+MSA_DECODE_SCRATCH_BYTES = 16 << 20
 
 MSA_OP_POOL = 0
 MSA_OP_INDEX = 1
@@ -49,6 +51,7 @@ SIGNATURES = {
     "msa_index_select": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "msa_prefill": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "msa_decode": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "msa_decode_noalloc": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P]),
     "msa_prefill_lse": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "msa_prefill_backward": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
                                             _P]),

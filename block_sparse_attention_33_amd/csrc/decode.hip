@@ -22,6 +22,9 @@
 
 #include <limits.h>
 
+#include <mutex>
+#include <vector>
+
 #include "msa_device.h"
 #include "msa_kernels.h"
 
@@ -498,7 +501,33 @@ __global__ __launch_bounds__(64) void append_kernel(const uint16_t* __restrict__
   block_keys[((size_t)u * sh.nbc + j) * kIdxDim + l] = (int8_t)floor_div(s, n);
 }
 
+// Scratch of the allocation-free decode entry point: one array per device,
+// held until the process ends.  Host code never passes `scratch` itself to
+// a kernel (on the host that name is a stand-in, not a device address); it
+// passes the address decode_scratch() looked up for the current device.
+static __device__ __align__(256) char scratch[kDecodeScratchBytes];
+
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;  // by device ordinal; null = not looked up yet
+
 }  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if ((int)g_scratch_ptr.size() <= dev) g_scratch_ptr.resize(dev + 1, nullptr);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_decode(const DecodeShape& sh, const uint16_t* q, const int8_t* q_idx, const uint16_t* k_cache,
                          const uint16_t* v_cache, const int8_t* block_keys, int32_t* sel_out, uint16_t* out,

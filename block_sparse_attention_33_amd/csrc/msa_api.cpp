@@ -25,6 +25,8 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool pow2_in(int x, int lo, int hi) { return x >= lo && x <= hi && (x & (x - 1)) == 0; }
 
+static_assert(MSA_DECODE_SCRATCH_BYTES == msa::kDecodeScratchBytes, "msa.h and the decode scratch disagree");
+
 constexpr long kMaxSparseTopK = 32;  // selection slots of the sparse paths (5 bits in a CSR entry)
 
 struct Dims {
@@ -497,12 +499,14 @@ const char* msa_status_string(int status) {
       return "MSA_ERR_WORKSPACE: workspace missing, too small or not 256-byte aligned";
     case MSA_ERR_HIP:
       return "MSA_ERR_HIP: a HIP runtime call or kernel launch failed";
+    case MSA_ERR_SCRATCH:
+      return "MSA_ERR_SCRATCH: the shape needs more than the library's fixed decode scratch (msa_decode_noalloc)";
     default:
       return "unknown MSA status";
   }
 }
 
-int msa_version(void) { return 10300; }
+int msa_version(void) { return 10400; }
 
 int msa_backward_pass_rows(const msa_dims* dims, size_t ws_bytes, int32_t* rows) {
   Dims d;
@@ -727,6 +731,27 @@ int msa_decode(const msa_dims* dims, const uint16_t* q, const int8_t* q_idx, con
   if (d.k > kMaxSparseTopK) return MSA_ERR_UNSUPPORTED;
   if (!q || !q_idx || !k_cache || !v_cache || !block_keys || !out) return MSA_ERR_INVALID_ARG;
   return run_decode(d, d.S, q, q_idx, k_cache, v_cache, block_keys, out, sel, ws, ws_bytes, (hipStream_t)stream);
+}
+
+int msa_decode_noalloc(const msa_dims* dims, const uint16_t* q, const int8_t* q_idx, const uint16_t* k_cache,
+                       const uint16_t* v_cache, const int8_t* block_keys, uint16_t* out, int32_t* sel,
+                       void* stream) {
+  Dims d;
+  int st = check_dims(dims, &d);
+  if (st != MSA_OK) return st;
+  if (d.k > kMaxSparseTopK) return MSA_ERR_UNSUPPORTED;
+  if (!q || !q_idx || !k_cache || !v_cache || !block_keys || !out) return MSA_ERR_INVALID_ARG;
+  DecodeLayout L;
+  st = decode_layout(d, &L);
+  if (st != MSA_OK) return st;
+  if (L.total > msa::kDecodeScratchBytes) return MSA_ERR_SCRATCH;
+  // the current device's copy of the fixed scratch (looked up once per
+  // device); no allocation, no memset: the decode kernels write every byte
+  // of the scratch they later read
+  void* scratch = nullptr;
+  if (msa::decode_scratch(&scratch) != hipSuccess) return MSA_ERR_HIP;
+  return run_decode(d, d.S, q, q_idx, k_cache, v_cache, block_keys, out, sel, scratch, msa::kDecodeScratchBytes,
+                    (hipStream_t)stream);
 }
 
 int msa_decode_init(const msa_dims* dims, int32_t length, const int8_t* k_idx, int8_t* block_keys,

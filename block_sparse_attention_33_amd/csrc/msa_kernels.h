@@ -152,6 +152,10 @@ constexpr int kDecodeMaxCandidates = 16 * 512;  // 512 threads x 16 candidates
 hipError_t launch_decode(const DecodeShape& sh, const uint16_t* q, const int8_t* q_idx, const uint16_t* k_cache,
                          const uint16_t* v_cache, const int8_t* block_keys, int32_t* sel_out, uint16_t* out,
                          float* state, int n_split, hipStream_t st);
+// Device address, on the current device, of the library's fixed decode
+// scratch (kDecodeScratchBytes, 256-byte aligned), looked up once per device.
+constexpr size_t kDecodeScratchBytes = 16u << 20;
+hipError_t decode_scratch(void** ptr);
 // Append of token pos of every unit: k_new/v_new [U, 128] -> cache row pos,
 // k_idx_new [U, 64] -> open_sums [U, 64] and block_keys[u][pos / bs].
 hipError_t launch_append(const DecodeShape& sh, const uint16_t* k_new, const uint16_t* v_new,

@@ -81,6 +81,7 @@ extern "C" {
 #define MSA_ERR_UNSUPPORTED (-2)  /* valid but outside the supported limits */
 #define MSA_ERR_WORKSPACE (-3)    /* workspace missing, too small or misaligned */
 #define MSA_ERR_HIP (-4)          /* a HIP runtime call or launch failed */
+#define MSA_ERR_SCRATCH (-5)      /* msa_decode_noalloc: shape needs more than the fixed scratch */
 
 /* Operations, for msa_workspace_bytes. */
 #define MSA_OP_POOL 0
@@ -213,6 +214,26 @@ int msa_prefill_chunk(const msa_dims* dims, int32_t start, int32_t count, const 
 int msa_decode(const msa_dims* dims, const uint16_t* q, const int8_t* q_idx,
                const uint16_t* k_cache, const uint16_t* v_cache, const int8_t* block_keys,
                uint16_t* out, int32_t* sel, void* ws, size_t ws_bytes, void* stream);
+
+/* msa_decode without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, results and kernels as msa_decode; the
+ * scratch msa_decode takes from the caller's workspace (the selection when
+ * sel is NULL and the per-workgroup softmax states) lives instead in one
+ * fixed array of MSA_DECODE_SCRATCH_BYTES per device, compiled into the
+ * library and held until the process ends.  The call allocates nothing: no
+ * hipMalloc, hipFree or allocating library routine.  Returns
+ * MSA_ERR_SCRATCH, before anything is enqueued, when the shape needs more
+ * than that (msa_workspace_bytes(MSA_OP_DECODE) tells the need; about 1.1 MB
+ * for 16 sequences x 8 groups x 8 heads).  Every call on one device shares
+ * its array: calls that overlap in time on one device (other streams or
+ * host threads) race and must be ordered by the caller; calls in one stream
+ * are ordered.  Each call writes all the scratch it later reads, so nothing
+ * carries over from an earlier call. */
+#define MSA_DECODE_SCRATCH_BYTES (16u << 20)
+int msa_decode_noalloc(const msa_dims* dims, const uint16_t* q, const int8_t* q_idx,
+                       const uint16_t* k_cache, const uint16_t* v_cache, const int8_t* block_keys,
+                       uint16_t* out, int32_t* sel, void* stream);
 
 /* Generation with caches that grow by one token per step.  The decode
  * pages describe the KV cache holding past keys and values so that each new

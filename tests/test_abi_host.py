@@ -45,10 +45,10 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_status_strings(lib):
     for code, prefix in [(0, "MSA_OK"), (-1, "MSA_ERR_INVALID_ARG"), (-2, "MSA_ERR_UNSUPPORTED"),
-                         (-3, "MSA_ERR_WORKSPACE"), (-4, "MSA_ERR_HIP")]:
+                         (-3, "MSA_ERR_WORKSPACE"), (-4, "MSA_ERR_HIP"), (-5, "MSA_ERR_SCRATCH")]:
         assert lib.msa_status_string(code).decode().startswith(prefix)
     assert lib.msa_status_string(12345).decode() == "unknown MSA status"
-    assert lib.msa_version() == 10300
+    assert lib.msa_version() == 10400
 
 
 def D(**kw):
@@ -289,3 +289,21 @@ def test_decode_workspace_layout(lib):
     assert _ws(lib, _lib.MSA_OP_DECODE, D(batch=1, seq_len=8193 * 128))[0] == 0
     assert _ws(lib, _lib.MSA_OP_DECODE, D(batch=1, seq_len=8193 * 128 + 1))[0] == -2
     assert _ws(lib, _lib.MSA_OP_INDEX, dims)[1:] == (0, 0)
+
+
+def test_decode_noalloc_validation(lib):
+    """The allocation-free decode rejects null pointers and shapes whose
+    scratch exceeds the library's fixed array before anything is enqueued."""
+    dims = D(batch=16, seq_len=262144)
+    for i in range(6):
+        args = [FAKE] * 6
+        args[i] = None
+        assert lib.msa_decode_noalloc(ctypes.byref(dims), *args, None, None) == -1
+    # the decode workload's scratch fits; 32768 units x 8 heads do not
+    st, lo, _ = _ws(lib, _lib.MSA_OP_DECODE, dims)
+    assert st == 0 and lo <= _lib.MSA_DECODE_SCRATCH_BYTES
+    big = D(batch=4096, seq_len=1000)
+    st, lo, _ = _ws(lib, _lib.MSA_OP_DECODE, big)
+    assert st == 0 and lo > _lib.MSA_DECODE_SCRATCH_BYTES
+    assert lib.msa_decode_noalloc(ctypes.byref(big), *([FAKE] * 6), None, None) == _lib.MSA_ERR_SCRATCH
+    assert lib.msa_decode_noalloc(ctypes.byref(D(top_k=33)), *([FAKE] * 6), None, None) == -2
