@@ -296,20 +296,47 @@ long prefill_query_chunk(const Dims& d) {
 // apart per batch / unit.  ext_keys: block summaries that persist across
 // calls (dc.nb rows per unit; blocks before q0 / bs already pooled), or
 // null to pool every block into the workspace.
-int run_prefill(const Dims& dc, long q0, long n_q, long q_stride, const uint16_t* q, const uint16_t* k,
-                const uint16_t* v, const int8_t* q_idx, const int8_t* k_idx, int8_t* ext_keys, uint16_t* out,
-                int32_t* sel, float* lse, void* ws, size_t ws_bytes, hipStream_t s) {
+// The plan of one query chunk (n_q rows of a prefill of dc) in a workspace
+// of ws_bytes: the inversion's plan, the workspace layout and the (batch,
+// group) units per pass -- as many as the workspace holds partials for.
+// Checks what the kernels rely on: every region inside the workspace, the
+// histogram chunks within their region, the persistent summaries at offset
+// 0 (query chunks of one prefill share them).
+struct ChunkRun {
+  PrefillPlan P;
+  PrefillLayout L;
+  long upp;
+};
+
+int plan_chunk(const Dims& dc, long n_q, size_t ws_bytes, ChunkRun* run) {
   const Dims d = chunk_dims(dc, n_q);
-  const PrefillPlan P = plan_prefill(d);
-  int st;
+  run->P = plan_prefill(d);
+  const PrefillPlan& P = run->P;
   const PrefillLayout one = prefill_layout(d, P, 1);
-  st = check_ws(ws, ws_bytes, one.total);
-  if (st != MSA_OK) return st;
-  // as many (batch, group) units per pass as the workspace holds
+  if (ws_bytes < one.total) return MSA_ERR_WORKSPACE;
   const size_t per_unit = prefill_layout(d, P, 2).total - one.total;
   long upp = per_unit > 0 ? std::min<long>(d.U, 1 + (long)((ws_bytes - one.total) / per_unit)) : d.U;
   PrefillLayout L = prefill_layout(d, P, upp);
   while (L.total > ws_bytes && upp > 1) L = prefill_layout(d, P, --upp);
+  if (L.total > ws_bytes || upp < 1) return MSA_ERR_WORKSPACE;
+  if (L.block_keys != 0 || P.n_chunks > P.max_chunks || P.m * P.tpc < P.T || P.T < n_q) return MSA_ERR_WORKSPACE;
+  run->L = L;
+  run->upp = upp;
+  return MSA_OK;
+}
+
+int run_prefill(const Dims& dc, long q0, long n_q, long q_stride, const uint16_t* q, const uint16_t* k,
+                const uint16_t* v, const int8_t* q_idx, const int8_t* k_idx, int8_t* ext_keys, uint16_t* out,
+                int32_t* sel, float* lse, void* ws, size_t ws_bytes, hipStream_t s) {
+  const Dims d = chunk_dims(dc, n_q);
+  int st = check_ws(ws, ws_bytes, 1);
+  if (st != MSA_OK) return st;
+  ChunkRun run;
+  st = plan_chunk(dc, n_q, ws_bytes, &run);
+  if (st != MSA_OK) return st;
+  const PrefillPlan& P = run.P;
+  const PrefillLayout& L = run.L;
+  const long upp = run.upp;
 
   char* base = static_cast<char*>(ws);
   int8_t* bkeys = reinterpret_cast<int8_t*>(base + L.block_keys);
@@ -442,6 +469,36 @@ long backward_pass_rows(const Dims& d, size_t ws_bytes) {
   return lo * kBackwardPassGranule;
 }
 
+// Plans of every query chunk of a whole sparse prefill in ws_bytes;
+// *launches (optional) = the attention launches (chunks x unit passes).
+int check_prefill_plans(const Dims& d, size_t ws_bytes, long* launches) {
+  const long T = prefill_query_chunk(d);
+  long n = 0;
+  for (long q0 = 0; q0 < d.S; q0 += T) {
+    ChunkRun run;
+    const int st = plan_chunk(d, std::min(T, d.S - q0), ws_bytes, &run);
+    if (st != MSA_OK) return st;
+    n += (d.U + run.upp - 1) / run.upp;
+  }
+  if (launches) *launches = n;
+  return MSA_OK;
+}
+
+// Plans of every query pass of a backward with passes of T rows against the
+// layout sized for T rows: the histogram chunks and work items of each pass
+// within their regions (a shorter last pass can plan more histogram chunks
+// than a full one: its chunk length rounds to whole 256-token granules).
+int check_backward_plans(const Dims& d, long T, const BackwardLayout& L) {
+  if (T < 1 || T > d.S) return MSA_ERR_WORKSPACE;
+  for (long q0 = 0; q0 < d.S; q0 += T) {
+    const long n_q = std::min(T, d.S - q0);
+    const PrefillPlan P = plan_prefill(chunk_dims(d, n_q));
+    if (P.n_chunks > L.max_chunks || P.max_items_per_range > L.max_items || P.m * P.tpc < P.T || P.T < n_q)
+      return MSA_ERR_WORKSPACE;
+  }
+  return MSA_OK;
+}
+
 // Whole prefill (msa_prefill, msa_prefill_lse), arguments checked.
 int prefill_impl(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v, const int8_t* q_idx,
                  const int8_t* k_idx, uint16_t* out, int32_t* sel, float* lse, void* ws, size_t ws_bytes,
@@ -469,6 +526,9 @@ int prefill_impl(const Dims& d, const uint16_t* q, const uint16_t* k, const uint
     return MSA_OK;
   }
   const long T = prefill_query_chunk(d);
+  // every chunk is planned and checked before anything is enqueued
+  int st = check_prefill_plans(d, ws_bytes, nullptr);
+  if (st != MSA_OK) return st;
   if (T >= d.S) return run_prefill(d, 0, d.S, d.S, q, k, v, q_idx, k_idx, nullptr, out, sel, lse, ws, ws_bytes, s);
   // query chunks of T tokens; the summaries persist in the workspace's first
   // region (block_keys, which every layout places at offset 0)
@@ -515,6 +575,35 @@ int msa_backward_pass_rows(const msa_dims* dims, size_t ws_bytes, int32_t* rows)
   if (d.k > kMaxSparseTopK || d.nb > msa::kMaxInvertBlocks) return MSA_ERR_UNSUPPORTED;
   if (!rows) return MSA_ERR_INVALID_ARG;
   *rows = (int32_t)backward_pass_rows(d, ws_bytes);
+  return MSA_OK;
+}
+
+int msa_plan_check(int op, const msa_dims* dims, size_t ws_bytes, int32_t* launches) {
+  Dims d;
+  int st = check_dims(dims, &d);
+  if (st != MSA_OK) return st;
+  if (d.nb > msa::kMaxInvertBlocks) return MSA_ERR_UNSUPPORTED;
+  long n = 0;
+  if (op == MSA_OP_PREFILL) {
+    if (d.k >= d.nb) {
+      n = 1;  // the dense kernel: no workspace, nothing to plan
+    } else {
+      st = check_prefill_plans(d, ws_bytes, &n);
+      if (st != MSA_OK) return st;
+    }
+  } else if (op == MSA_OP_BACKWARD) {
+    if (d.k > kMaxSparseTopK) return MSA_ERR_UNSUPPORTED;
+    const long T = backward_pass_rows(d, ws_bytes);
+    if (T == 0) return MSA_ERR_WORKSPACE;
+    const BackwardLayout L = backward_layout(d, T);
+    if (L.total > ws_bytes) return MSA_ERR_WORKSPACE;
+    st = check_backward_plans(d, T, L);
+    if (st != MSA_OK) return st;
+    n = (d.S + T - 1) / T;
+  } else {
+    return MSA_ERR_INVALID_ARG;
+  }
+  if (launches) *launches = (int32_t)n;
   return MSA_OK;
 }
 
@@ -620,6 +709,12 @@ int msa_prefill_backward(const msa_dims* dims, const uint16_t* q, const uint16_t
   const BackwardLayout L = backward_layout(d, T);
   st = check_ws(ws, ws_bytes, L.total);
   if (st != MSA_OK) return st;
+  // every pass's inversion must fit the regions sized for T rows (it does,
+  // by the bounds in backward_layout); checked for all passes before the
+  // first launch, so that a planning mistake is an error, not a write past
+  // a region
+  st = check_backward_plans(d, T, L);
+  if (st != MSA_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   char* base = static_cast<char*>(ws);
   float* delta = reinterpret_cast<float*>(base + L.delta);
@@ -661,10 +756,6 @@ int msa_prefill_backward(const msa_dims* dims, const uint16_t* q, const uint16_t
     const long n_q = std::min(T, (long)S - q0);
     const Dims dc = chunk_dims(d, n_q);
     const PrefillPlan P = plan_prefill(dc);
-    // the pass's inversion must fit the regions sized for T rows (it does,
-    // by the bounds above; checked so that a mistake there is an error, not
-    // a write past a region)
-    if (P.n_chunks > L.max_chunks || P.max_items_per_range > L.max_items) return MSA_ERR_WORKSPACE;
     msa::ChunkPlan cp;
     cp.T = (int)P.T;
     cp.m = (int)P.m;

@@ -123,6 +123,17 @@ int msa_workspace_bytes(int op, const msa_dims* dims, size_t* min_bytes, size_t*
  * MSA_ERR_WORKSPACE).  The backward runs ceil(seq_len / *rows) passes. */
 int msa_backward_pass_rows(const msa_dims* dims, size_t ws_bytes, int32_t* rows);
 
+/* Host-only check of the launch plan of msa_prefill (op MSA_OP_PREFILL) or
+ * msa_prefill_backward (op MSA_OP_BACKWARD) at dims with a workspace of
+ * ws_bytes; nothing is enqueued and no HIP call is made.  Returns MSA_OK
+ * when every query chunk / pass the call would run lays out inside the
+ * workspace and its inversion fits the regions reserved for it, with
+ * *launches (optional) = the attention launches (prefill: query chunks x
+ * unit passes; backward: query passes); MSA_ERR_WORKSPACE when ws_bytes is
+ * below the minimum.  The two entry points run this same check before their
+ * first launch. */
+int msa_plan_check(int op, const msa_dims* dims, size_t ws_bytes, int32_t* launches);
+
 /* Index branch, pooling step: block summary keys.
  * k_idx [B, G, S, di] int8 -> block_keys [B, G, nb, di] int8.
  * Needs no workspace. */

@@ -307,3 +307,79 @@ def test_decode_noalloc_validation(lib):
     assert st == 0 and lo > _lib.MSA_DECODE_SCRATCH_BYTES
     assert lib.msa_decode_noalloc(ctypes.byref(big), *([FAKE] * 6), None, None) == _lib.MSA_ERR_SCRATCH
     assert lib.msa_decode_noalloc(ctypes.byref(D(top_k=33)), *([FAKE] * 6), None, None) == -2
+
+
+def _plan_check(lib, op, dims, ws):
+    n = ctypes.c_int32(-1)
+    st = lib.msa_plan_check(op, ctypes.byref(dims), ctypes.c_size_t(int(ws)), ctypes.byref(n))
+    return st, n.value
+
+
+def _rows_per_pass(lib, dims, ws):
+    r = ctypes.c_int32(-1)
+    assert lib.msa_backward_pass_rows(ctypes.byref(dims), ctypes.c_size_t(int(ws)), ctypes.byref(r)) == 0
+    return r.value
+
+
+# up to the longest supported prefill: 36864 blocks of 128 tokens
+SWEEP_S = [1, 255, 256, 257, 4097, 32768, 300000, 1 << 20, 36864 * 128 - 5, 36864 * 128]
+
+
+@pytest.mark.parametrize("S", SWEEP_S)
+def test_plan_sweep_backward(lib, S):
+    """For every sequence length above and a spread of workspaces between the
+    backward's minimum and full size, every pass the call would run (the
+    shorter last one included) plans its inversion inside the regions sized
+    for the pass length; below the minimum the call is refused."""
+    dims = D(seq_len=S)
+    st, lo, hi = _ws(lib, _lib.MSA_OP_BACKWARD, dims)
+    assert st == 0 and 0 < lo <= hi
+    sizes = sorted({lo, hi, (lo + hi) // 2, lo + (hi - lo) // 7, lo + (hi - lo) // 64, lo + 12345,
+                    max(lo, hi - 1)} | {int(lo + (hi - lo) * f) for f in (0.01, 0.03, 0.1, 0.27, 0.5, 0.9)})
+    for ws in sizes:
+        st, passes = _plan_check(lib, _lib.MSA_OP_BACKWARD, dims, ws)
+        assert st == 0, (S, ws, st)
+        rows = _rows_per_pass(lib, dims, ws)
+        assert rows == S or (rows > 0 and rows % 256 == 0), (S, ws, rows)
+        assert passes == -(-S // rows), (S, ws, rows, passes)
+    if lo > 1:
+        assert _plan_check(lib, _lib.MSA_OP_BACKWARD, dims, lo - 1)[0] == -3
+
+
+@pytest.mark.parametrize("S", SWEEP_S)
+def test_plan_sweep_prefill(lib, S):
+    """Every query chunk of a prefill (the last, shorter one included) and
+    every unit pass fits the workspace, for workspaces from the minimum to the
+    full size; the summaries shared by the chunks sit at offset 0."""
+    dims = D(seq_len=S)
+    st, lo, hi = _ws(lib, _lib.MSA_OP_PREFILL, dims)
+    assert st == 0
+    if hi == 0:  # top_k >= nb: dense kernel, nothing planned
+        assert _plan_check(lib, _lib.MSA_OP_PREFILL, dims, 0) == (0, 1)
+        return
+    for ws in sorted({lo, hi, (lo + hi) // 2, lo + (hi - lo) // 5, lo + 1000, max(lo, hi - 1)}):
+        st, launches = _plan_check(lib, _lib.MSA_OP_PREFILL, dims, ws)
+        assert st == 0 and launches >= 1, (S, ws, st)
+    assert _plan_check(lib, _lib.MSA_OP_PREFILL, dims, hi)[1] == -(-S // max(1, min(S, _chunk_tokens(S))))
+    assert _plan_check(lib, _lib.MSA_OP_PREFILL, dims, lo - 1)[0] == -3
+
+
+def _chunk_tokens(S):
+    """Query tokens per chunk of a whole prefill, as the library documents it:
+    16384 up to 128K tokens, a quarter of the sequence (in whole 16384s) beyond."""
+    if S <= 16384:
+        return S
+    if S <= 131072:
+        return 16384
+    quarter = -(-S // 4)
+    return -(-quarter // 16384) * 16384
+
+
+def test_plan_check_arguments(lib):
+    # beyond 36864 blocks (here 2^26 - 1 tokens) neither call is supported
+    for op in (_lib.MSA_OP_PREFILL, _lib.MSA_OP_BACKWARD):
+        assert _plan_check(lib, op, D(seq_len=(1 << 26) - 1), 1 << 40)[0] == -2
+        assert _plan_check(lib, op, D(seq_len=36864 * 128 + 1), 1 << 40)[0] == -2
+    assert _plan_check(lib, 99, D(), 1 << 30)[0] == -1
+    assert _plan_check(lib, _lib.MSA_OP_PREFILL, D(head_dim=64), 1 << 30)[0] == -2
+    assert _plan_check(lib, _lib.MSA_OP_BACKWARD, D(), 0)[0] == -3
