@@ -25,7 +25,7 @@ import torch
 import block_sparse_attention_33_amd as msa
 from oracle import msa_oracle as O
 from synth import get_workload, grad_output, prefill_inputs, sample_rows
-from tests.helpers import host_f32, host_i8
+from tests.helpers import host_f32, host_i8, record
 
 pytestmark = pytest.mark.gpu
 
@@ -59,6 +59,9 @@ def compare_grad(gpu_bf16, oracle_f64, what):
     scale_mean = max(float(np.abs(ref).mean()), GRAD_FLOOR)
     max_rel, mean_rel = float(d.max()) / scale_max, float(d.mean()) / scale_mean
     _say(f"  {what}: max_rel={max_rel:.2e} mean_rel={mean_rel:.2e} (max|ref|={scale_max:.3g})")
+    record(what, {"elements": int(d.size), "grad_max_rel": max_rel, "grad_mean_rel": mean_rel,
+                  "max_abs_oracle": float(np.abs(ref).max()), "mean_abs_oracle": float(np.abs(ref).mean()),
+                  "bars": [GRAD_MAX_REL, GRAD_MEAN_REL]})
     assert max_rel <= GRAD_MAX_REL and mean_rel <= GRAD_MEAN_REL, (
         f"{what}: max|err|/max|ref| = {max_rel:.3e} (<= {GRAD_MAX_REL}), mean|err|/mean|ref| = {mean_rel:.3e} "
         f"(<= {GRAD_MEAN_REL}), worst at {np.unravel_index(int(d.argmax()), d.shape)}")
