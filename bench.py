@@ -1,22 +1,30 @@
 #!/usr/bin/env python3
 """Benchmark of the MSA hot path on one MI355X.
 
-One step = one whole hot path: msa_prefill on the 32K-token prefill workload
-(batch 1, 64 query / 8 KV heads, head dim 128, blocks of 128, top_k 16:
-pooling, index top-k, query->block inversion, KV-outer attention over every
-kept block, partial merge) followed by one msa_decode on the decode workload (16 sequences over
-262144-token caches, same heads).  Inputs are seeded synthetic tensors
-already resident in HBM.  Prints one JSON line.
+One step = one whole hot path over the two workloads it serves: msa_prefill
+on the 1M-token prefill (batch 1, 1048576 tokens, 64 query / 8 KV heads, head
+dim 128, blocks of 128, top_k 16: pooling, index top-k, query->block
+inversion, KV-outer attention over every kept block, partial merge, in four
+query chunks) followed by one msa_decode of 16 sequences over
+262144-token caches (same heads).  Inputs are seeded synthetic tensors
+already resident in HBM.  Prints one JSON line; its headline `value` is the
+1M prefill's tokens/s.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+Beside the step (unless --core-only): the other prefill workloads (2K, 32K,
+structured 128K), decode back to back and the generation step, the 32K
+prefill in chunks and its training forward/backward, the 1M backward, a
+short dense prefill; and (unless --no-cpu-baseline) the CPU oracle timed on
+every workload's rows -- all rows of the 2K and 32K prefills and of the
+decode, 4096 seeded rows of the 128K and 1M prefills -- with the parity of
+those rows against the GPU's.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--core-only]
 """
 import argparse
 import hashlib
 import json
 import os
-import subprocess
 import sys
-import tempfile
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -25,7 +33,14 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 D_HEAD = 128
-CPU_SAMPLE_ROWS = 6144      # oracle rows timed on the host (about 15-20 s, one thread)
+HEADLINE = "prefill_1m"
+DECODE = "decode_b16_256k"
+CPU_SAMPLE_ROWS = 4096      # oracle rows timed for the 128K and 1M prefills
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_prefill_1m_traffic.json")
+
+
+def _say(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
 
 
 def _prefill_counts(w):
@@ -43,6 +58,10 @@ def _prefill_counts(w):
     return per_head_keys, pairs, rows_merged
 
 
+def _flop_alg(w):
+    return 4.0 * w.head_dim * w.n_q_heads * _prefill_counts(w)[0]
+
+
 def _decode_bytes(w):
     B, Hq, G, D, bs, k = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size, w.top_k
     nb = -(-w.seq_len // bs)
@@ -55,7 +74,7 @@ def _decode_bytes(w):
 
 
 def kernel_source_hash():
-    """Hash of the main-branch kernel source; counter summaries are valid only
+    """Hash of the main-branch kernel source; counter records are valid only
     for the source they were taken on."""
     h = hashlib.sha256()
     with open(os.path.join(ROOT, "block_sparse_attention_33_amd", "csrc", "main_branch.hip"), "rb") as f:
@@ -64,45 +83,67 @@ def kernel_source_hash():
 
 
 def _measured_traffic():
-    """HBM bytes per launch of the attention kernel from the committed
-    rocprofv3 FETCH_SIZE / WRITE_SIZE summary (already scaled by the copy
+    """HBM bytes per launch of the 1M prefill's attention kernel from the
+    committed rocprofv3 FETCH_SIZE / WRITE_SIZE record (scaled by the copy
     kernel calibration), if it was taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", "attend_prefill_32k_traffic.json")
-    if not os.path.exists(path):
+    if not os.path.exists(TRAFFIC_FILE):
         return None
-    with open(path) as f:
+    with open(TRAFFIC_FILE) as f:
         rec = json.load(f)
     if rec.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
     return rec.get("bytes_per_launch")
 
 
+def _events(n):
+    import torch
+    return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+
+
+def _median_ms(fn, reps, warm=1):
+    import torch
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    ev = _events(reps)
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in ev)
+    return t[len(t) // 2]
+
+
+def _workspace(msa, op, w, dev, cap_bytes=None):
+    import torch
+    dims = msa.make_dims(w.batch, w.seq_len, w.n_q_heads, w.n_kv_heads, w.block_size, w.top_k)
+    lo, hi = msa.msa_workspace_bytes(op, dims)
+    size = hi if cap_bytes is None else max(lo, min(hi, cap_bytes))
+    return torch.empty(max(size, 256), dtype=torch.uint8, device=dev)
+
+
+# ------------------------------------------------------------------ counters
+
 def pmc_run():
-    """Workload for counter runs under rocprofv3 --pmc: two 32K prefills, the
-    32K training forward and two backward calls, two decodes of the decode
-    workload, then a 1 GiB device copy whose bytes are known (the
-    calibration of the FETCH_SIZE / WRITE_SIZE counters)."""
+    """Workload for counter runs under rocprofv3 --pmc: two 1M prefills, two
+    decodes of the decode workload, then a 1 GiB device copy whose bytes are
+    known (the calibration of the FETCH_SIZE / WRITE_SIZE counters)."""
     import torch
     import block_sparse_attention_33_amd as msa
-    from synth import decode_inputs, get_workload, grad_output, prefill_inputs
+    from synth import decode_inputs, get_workload, prefill_inputs
     dev = torch.device("cuda:0")
-    w = get_workload("prefill_32k")
+    w = get_workload(HEADLINE)
     inp = prefill_inputs(w, seed=0, device=dev)
-    ws = torch.empty(msa.msa_workspace_bytes(
-        msa.MSA_OP_PREFILL, msa.make_dims(w.batch, w.seq_len, w.n_q_heads, w.n_kv_heads, w.block_size,
-                                           w.top_k))[1], dtype=torch.uint8, device=dev)
+    ws = _workspace(msa, msa.MSA_OP_PREFILL, w, dev)
+    out = torch.empty_like(inp["q"])
     for _ in range(2):
-        msa.msa_prefill(inp["q"], inp["k"], inp["v"], inp["q_idx"], inp["k_idx"], w.block_size, w.top_k,
+        msa.msa_prefill(inp["q"], inp["k"], inp["v"], inp["q_idx"], inp["k_idx"], w.block_size, w.top_k, out=out,
                         workspace=ws)
-    out, sel, lse = msa.msa_prefill_lse(inp["q"], inp["k"], inp["v"], inp["q_idx"], inp["k_idx"], w.block_size,
-                                        w.top_k, workspace=ws)
-    del ws
-    dout = grad_output(w, seed=0, device=dev)
-    for _ in range(2):
-        msa.msa_prefill_backward(inp["q"], inp["k"], inp["v"], out, dout, lse, sel, w.block_size)
     torch.cuda.synchronize()
-    del inp, out, sel, lse, dout
-    wd = get_workload("decode_b16_256k")
+    del inp, ws, out
+    torch.cuda.empty_cache()
+    wd = get_workload(DECODE)
     din = decode_inputs(wd, seed=0, device=dev)
     bk = msa.msa_pool_block_keys(din["k_idx_cache"], wd.block_size)
     del din["k_idx_cache"]
@@ -132,7 +173,7 @@ def pmc_summary(fetch_csv, write_csv, commands):
                 if row["Counter_Name"] != counter:
                     continue
                 name = row["Kernel_Name"]
-                m = re.search(r"msa::\(anonymous namespace\)::(\w+(?:<\d+>)?)", name)
+                m = re.search(r"msa::\(anonymous namespace\)::(\w+(?:<[\d, ]+>)?)", name)
                 key = m.group(1) if m else ("copy" if "copyBuffer" in name else None)
                 if key:
                     got.setdefault(key, []).append(float(row["Counter_Value"]))
@@ -143,8 +184,8 @@ def pmc_summary(fetch_csv, write_csv, commands):
     fscale, wscale = copy_kib / fk["copy"][-1], copy_kib / wk["copy"][-1]
     rec = {
         "kernel": "attend_kernel<128>",
-        "workload": "prefill_32k (batch 1, seq 32768, 64q/8kv heads, head_dim 128, block 128, top_k 16); "
-                    "decode_b16_256k (16 x 262144-token caches, same heads)",
+        "workload": "prefill_1m (batch 1, seq 1048576, 64q/8kv heads, head_dim 128, block 128, top_k 16; four "
+                    "query chunks of 262144); decode_b16_256k (16 x 262144-token caches, same heads)",
         "kernel_source_sha256_16": kernel_source_hash(),
         "commands": commands,
         "calibration": {"kernel": "__amd_rocclr_copyBuffer, 1 GiB device copy",
@@ -161,75 +202,86 @@ def pmc_summary(fetch_csv, write_csv, commands):
         rec[k] = {"dispatches": len(fk[k]), "fetch_kib_per_dispatch": fk[k], "write_kib_per_dispatch": wk[k],
                   "fetch_bytes": round(fb), "write_bytes": round(wb), "bytes": round(fb + wb)}
     rec["bytes_per_launch"] = rec["attend_kernel<128>"]["bytes"]
-    out = os.path.join(ROOT, "profiles", "attend_prefill_32k_traffic.json")
-    with open(out, "w") as f:
+    with open(TRAFFIC_FILE, "w") as f:
         json.dump(rec, f, indent=1)
-    print(json.dumps({"written": out, "attend_bytes_per_launch": rec["bytes_per_launch"]}))
+    print(json.dumps({"written": TRAFFIC_FILE, "attend_bytes_per_launch": rec["bytes_per_launch"]}))
 
 
-def cpu_baseline_worker(npz_path):
-    """Runs in a child process with one BLAS/OpenMP thread: the oracle on the
-    sampled rows.  Prints a JSON line with the time."""
-    import numpy as np
-    if hasattr(os, "sched_setaffinity"):
-        os.sched_setaffinity(0, {min(os.sched_getaffinity(0))})
-    from oracle import msa_oracle as O
-    d = np.load(npz_path)
-    rows = d["rows"]
-    bs, top_k = int(d["bs"]), int(d["top_k"])
-    t0 = time.perf_counter()
-    summ = O.pool_block_keys(d["k_idx"], bs)
-    sel = O.select_blocks(d["q_idx"], summ, bs, top_k, rows)
-    O.attention_rows(d["q_rows"], d["k"], d["v"], sel, rows, bs)
-    dt = time.perf_counter() - t0
-    print(json.dumps({"seconds": dt, "rows": int(len(rows))}))
+# ------------------------------------------------------------------ CPU oracle baseline
+
+def _host_info():
+    try:
+        aff = sorted(os.sched_getaffinity(0))
+    except AttributeError:
+        aff = None
+    return {"cpu_count": os.cpu_count(), "affinity_cpus": len(aff) if aff is not None else None}
 
 
-def cpu_baseline(inp, w, n_rows):
+def cpu_baseline_prefill(name, inp, out, sel, rows):
+    """The oracle (over worker processes, one thread each) on `rows` of a
+    prefill workload whose GPU output and selection are given: its rows/s,
+    and the parity of those rows."""
     import numpy as np
     import torch
-    from synth import sample_rows
-    rows = sample_rows(w.seq_len, n_rows, 12345)
+    from oracle import pool
+    from synth import get_workload
+    w = get_workload(name)
     rt = torch.as_tensor(rows, device=inp["q"].device)
-    with tempfile.TemporaryDirectory() as td:
-        path = os.path.join(td, "cpu_baseline.npz")
-        np.savez(path, rows=rows, bs=w.block_size, top_k=w.top_k,
-                 q_rows=inp["q"][:, rt].float().cpu().numpy(), k=inp["k"].float().cpu().numpy(),
-                 v=inp["v"].float().cpu().numpy(), q_idx=inp["q_idx"].cpu().numpy(),
-                 k_idx=inp["k_idx"].cpu().numpy())
-        env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1",
-                   NUMEXPR_NUM_THREADS="1", HIP_VISIBLE_DEVICES="", CUDA_VISIBLE_DEVICES="")
-        res = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-baseline-worker", path],
-                             env=env, capture_output=True, text=True, timeout=600)
-    if res.returncode != 0:
-        raise RuntimeError(f"cpu baseline worker failed:\n{res.stderr}")
-    rec = json.loads(res.stdout.strip().splitlines()[-1])
+    bits = lambda t: t.detach().to("cpu").contiguous().view(torch.int16).numpy().view(np.uint16)  # noqa: E731
+    summ, osel, oout, st = pool.prefill_rows(bits(inp["q"][:, rt]), bits(inp["k"]), bits(inp["v"]),
+                                             inp["q_idx"].cpu().numpy(), inp["k_idx"].cpu().numpy(), rows,
+                                             w.block_size, w.top_k)
+    gsel = sel[:, :, rt].cpu().numpy()
+    g = out[:, rt].float().cpu().numpy().astype(np.float64)
+    d = np.abs(g - oout)
+    rel = d.mean(axis=-1) / np.maximum(np.abs(oout).mean(axis=-1), 1e-30)
     return {
-        "value": rec["rows"] / rec["seconds"],
-        "unit": "tokens/s",
-        "cores": 1,
-        "kind": "oracle",
-        "sample": (f"{rec['rows']} seeded query positions of the 32K prefill (all 8 groups, 64 heads): "
-                   f"pooling of all blocks + selection + attention, {rec['seconds']:.1f} s, one thread"),
+        "value": round(len(rows) / st["seconds"], 2), "unit": "tokens/s", "cores": st["workers"], "kind": "oracle",
+        "sample": (f"{len(rows)} {'seeded ' if len(rows) < w.seq_len else ''}query positions of {name} "
+                   f"(all {w.n_kv_heads} groups, {w.n_q_heads} heads): pooling of all blocks, selection and "
+                   f"attention, {st['seconds']:.1f} s over {st['workers']} one-thread worker processes "
+                   f"(input files and process start included)"),
+        "rows": len(rows), "seconds": st["seconds"], **_host_info(),
+        "parity": {"selection_bit_exact": bool(np.array_equal(gsel, osel)), "max_abs": float(d.max()),
+                   "mean_abs": float(d.mean()), "max_row_mean_rel": float(rel.max())},
     }
 
 
-def block_keys_prefill_shape(pin, w):
-    """An int8 tensor shaped like the prefill's block summaries [B, G, nb, 64]."""
+def cpu_baseline_decode(din, block_keys, out, sel, w):
+    """The oracle's decode of every (sequence, group) unit, in this process
+    (one thread), and the parity of the GPU's decode."""
+    import numpy as np
     import torch
-    B, G, S, di = pin["k_idx"].shape
-    return torch.empty((B, G, -(-S // w.block_size), di), dtype=torch.int8, device=pin["k_idx"].device)
+    from oracle import msa_oracle as O
+
+    class Bits:  # bf16 cache on the host, gathered rows widened to float32 exactly
+        def __init__(self, t):
+            self.b = t.detach().to("cpu").contiguous().view(torch.int16).numpy().view(np.uint16)
+            self.shape = self.b.shape
+
+        def __getitem__(self, idx):
+            return (np.asarray(self.b[idx]).astype(np.uint32) << 16).view(np.float32)
+
+    kc, vc = Bits(din["k_cache"]), Bits(din["v_cache"])
+    qf = din["q"].float().cpu().numpy()
+    qi = din["q_idx"].cpu().numpy()
+    summ = block_keys.cpu().numpy()
+    t0 = time.perf_counter()
+    osel, oout = O.decode(qf, qi, kc, vc, summ, w.block_size, w.top_k)
+    dt = time.perf_counter() - t0
+    ref = O.round_to_bf16(oout)
+    d = np.abs(out.float().cpu().numpy().astype(np.float64) - ref)
+    return {
+        "value": round(w.batch / dt, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+        "sample": (f"all {w.batch} sequences x {w.n_kv_heads} groups of {DECODE}: selection over the given "
+                   f"summaries and attention, {dt:.2f} s, one thread"),
+        "rows": w.batch, "seconds": round(dt, 3), **_host_info(),
+        "parity": {"selection_bit_exact": bool(np.array_equal(sel.cpu().numpy(), osel)), "max_abs": float(d.max()),
+                   "mean_abs": float(d.mean())},
+    }
 
 
-def _chunk_ws_bytes(msa, dims, count):
-    import ctypes
-    from block_sparse_attention_33_amd import _lib
-    hi = ctypes.c_size_t(0)
-    rc = _lib.load().msa_prefill_chunk_workspace_bytes(ctypes.byref(dims), count, None, ctypes.byref(hi))
-    if rc != 0:
-        raise RuntimeError(f"msa_prefill_chunk_workspace_bytes: {rc}")
-    return hi.value
-
+# ------------------------------------------------------------------ training-only run (profilers)
 
 def train_only(steps, warmup):
     """The 32K prefill for training alone: forward with log-sum-exp, then the
@@ -242,9 +294,8 @@ def train_only(steps, warmup):
     w = get_workload("prefill_32k")
     pin = prefill_inputs(w, seed=0, device=dev)
     dout = grad_output(w, seed=0, device=dev)
-    dims = msa.make_dims(w.batch, w.seq_len, w.n_q_heads, w.n_kv_heads, w.block_size, w.top_k)
-    pws = torch.empty(msa.msa_workspace_bytes(msa.MSA_OP_PREFILL, dims)[1], dtype=torch.uint8, device=dev)
-    bws = torch.empty(msa.msa_workspace_bytes(msa.MSA_OP_BACKWARD, dims)[1], dtype=torch.uint8, device=dev)
+    pws = _workspace(msa, msa.MSA_OP_PREFILL, w, dev)
+    bws = _workspace(msa, msa.MSA_OP_BACKWARD, w, dev)
 
     def fwd():
         return msa.msa_prefill_lse(pin["q"], pin["k"], pin["v"], pin["q_idx"], pin["k_idx"], w.block_size, w.top_k,
@@ -256,36 +307,200 @@ def train_only(steps, warmup):
         return msa.msa_prefill_backward(pin["q"], pin["k"], pin["v"], out, dout, lse, sel, w.block_size,
                                         workspace=bws)
 
-    res = {}
-    for name, fn in (("forward_lse", fwd), ("backward", bwd)):
-        for _ in range(warmup):
-            fn()
-        torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-        for a, b in ev:
-            a.record()
-            fn()
-            b.record()
-        torch.cuda.synchronize()
-        res[name] = sorted(a.elapsed_time(b) for a, b in ev)[steps // 2]
-    per_head_keys, _, _ = _prefill_counts(w)
-    flop = 2.5 * 4.0 * w.head_dim * w.n_q_heads * per_head_keys
+    res = {name: _median_ms(fn, steps, warmup) for name, fn in (("forward_lse", fwd), ("backward", bwd))}
+    flop = 2.5 * _flop_alg(w)
     print(json.dumps({"workload": "prefill_32k training", "forward_lse_ms": round(res["forward_lse"], 4),
                       "backward_ms": round(res["backward"], 4),
                       "backward_tflops_alg": round(flop / (res["backward"] * 1e-3) / 1e12, 2)}), flush=True)
 
 
+# ------------------------------------------------------------------ extras beside the step
+
+def other_prefills(msa, dev, cpu):
+    """The 2K, 32K and structured 128K prefills: median time of a few calls,
+    and (with cpu) the oracle on their rows with parity."""
+    import torch
+    from synth import get_workload, prefill_inputs, sample_rows
+    res, base = {}, {}
+    for name, reps in (("tiny_2k", 10), ("prefill_32k", 10), ("structured_128k", 5)):
+        w = get_workload(name)
+        inp = prefill_inputs(w, seed=0, device=dev)
+        ws = _workspace(msa, msa.MSA_OP_PREFILL, w, dev)
+        out = torch.empty_like(inp["q"])
+        sel = torch.empty((w.batch, w.n_kv_heads, w.seq_len, w.top_k), dtype=torch.int32, device=dev)
+
+        def fn():
+            msa.msa_prefill(inp["q"], inp["k"], inp["v"], inp["q_idx"], inp["k_idx"], w.block_size, w.top_k, out=out,
+                            sel=sel, workspace=ws)
+
+        ms = _median_ms(fn, reps)
+        flop = _flop_alg(w)
+        res[name] = {"seq_len": w.seq_len, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+                     "block_size": w.block_size, "top_k": w.top_k, "calls": reps, "ms": round(ms, 4),
+                     "tokens_per_s": round(w.batch * w.seq_len / (ms * 1e-3), 1),
+                     "tflops_alg": round(flop / (ms * 1e-3) / 1e12, 2),
+                     "frac_bf16_peak": round(flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        _say(f"{name}: {ms:.3f} ms")
+        if cpu:
+            rows = sample_rows(w.seq_len, w.seq_len if w.seq_len <= 32768 else CPU_SAMPLE_ROWS, 12345)
+            base[name] = cpu_baseline_prefill(name, inp, out, sel, rows)
+            _say(f"{name}: oracle {base[name]['value']} tokens/s, parity {base[name]['parity']}")
+        del inp, ws, out, sel
+        torch.cuda.empty_cache()
+    return res, base
+
+
+def decode_extras(msa, din, block_keys, wd, dws, dout, steps):
+    """Decode back to back (the kept blocks may still sit in the memory-side
+    cache) and the generation step (append + decode)."""
+    import torch
+    L = wd.seq_len
+    gen_keys, gen_sums = msa.msa_decode_init(din["k_idx_cache"], L - 1, wd.block_size)
+    k_new = din["k_cache"][:, :, L - 1].contiguous()
+    v_new = din["v_cache"][:, :, L - 1].contiguous()
+    k_idx_new = din["k_idx_cache"][:, :, L - 1].contiguous()
+
+    def decode():
+        msa.msa_decode(din["q"], din["q_idx"], din["k_cache"], din["v_cache"], block_keys, wd.block_size, wd.top_k,
+                       out=dout, workspace=dws)
+
+    def gen_step():
+        msa.msa_decode_step(din["q"], din["q_idx"], k_new, v_new, k_idx_new, din["k_cache"], din["v_cache"],
+                            gen_sums, gen_keys, L, wd.block_size, wd.top_k, out=dout, workspace=dws)
+
+    b2b = _median_ms(decode, steps, 3) * 1e3
+    gen = _median_ms(gen_step, steps, 3) * 1e3
+    dbytes = _decode_bytes(wd)
+    return {"decode_back_to_back_us": round(b2b, 2), "decode_back_to_back_frac_hbm_peak":
+            round(dbytes / (b2b * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "generation_step_us": round(gen, 2),
+            "generation_step_what": "append one token per sequence (K/V rows, running index-key sum, block "
+                                    "summary) + decode, back to back",
+            "generation_step_frac_hbm_peak": round(dbytes / (gen * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+
+
+def training_extras(msa, dev):
+    """The 32K prefill's training forward and backward, and the 1M backward in
+    query passes."""
+    import torch
+    from synth import get_workload, grad_output, prefill_inputs
+    res = {}
+    w = get_workload("prefill_32k")
+    pin = prefill_inputs(w, seed=0, device=dev)
+    pws = _workspace(msa, msa.MSA_OP_PREFILL, w, dev)
+    bws = _workspace(msa, msa.MSA_OP_BACKWARD, w, dev)
+    out, sel, lse = msa.msa_prefill_lse(pin["q"], pin["k"], pin["v"], pin["q_idx"], pin["k_idx"], w.block_size,
+                                        w.top_k, workspace=pws)
+    dout = grad_output(w, seed=0, device=dev)
+    fwd_ms = _median_ms(lambda: msa.msa_prefill_lse(pin["q"], pin["k"], pin["v"], pin["q_idx"], pin["k_idx"],
+                                                    w.block_size, w.top_k, workspace=pws), 5)
+    msa.profile_read()
+    msa.profile_enable(True)
+    bwd_ms = _median_ms(lambda: msa.msa_prefill_backward(pin["q"], pin["k"], pin["v"], out, dout, lse, sel,
+                                                         w.block_size, workspace=bws), 5)
+    msa.profile_enable(False)
+    bkt = msa.profile_read()
+    flop = 2.5 * _flop_alg(w)
+    res["prefill_32k"] = {
+        "forward_lse_ms": round(fwd_ms, 4), "backward_ms": round(bwd_ms, 4),
+        "backward_tflops_alg": round(flop / (bwd_ms * 1e-3) / 1e12, 2),
+        "backward_frac_bf16_peak": round(flop / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "backward_flop_alg": flop,
+        "kernels": {k: {"launches": n, "avg_ms": round(ms / max(1, n), 4)} for k, (n, ms) in sorted(bkt.items())}}
+    del pin, pws, bws, out, sel, lse, dout
+    torch.cuda.empty_cache()
+    # 1M backward: the full workspace (about 276 GB) does not fit beside the
+    # tensors, so it runs in query passes in 80 % of the free memory
+    w = get_workload(HEADLINE)
+    cin = prefill_inputs(w, seed=0, device=dev)
+    tout, tsel, tlse = msa.msa_prefill_lse(cin["q"], cin["k"], cin["v"], cin["q_idx"], cin["k_idx"], w.block_size,
+                                           w.top_k)
+    tdout = grad_output(w, seed=0, device=dev)
+    torch.cuda.empty_cache()
+    dims = msa.make_dims(w.batch, w.seq_len, w.n_q_heads, w.n_kv_heads, w.block_size, w.top_k)
+    tlo, thi = msa.msa_workspace_bytes(msa.MSA_OP_BACKWARD, dims)
+    tws = torch.empty(max(tlo, min(thi, int(torch.cuda.mem_get_info(dev)[0] * 0.8) - (20 << 30))),
+                      dtype=torch.uint8, device=dev)
+    msa.profile_read()
+    msa.profile_enable(True)
+    bms = _median_ms(lambda: msa.msa_prefill_backward(cin["q"], cin["k"], cin["v"], tout, tdout, tlse, tsel,
+                                                      w.block_size, workspace=tws), 2)
+    msa.profile_enable(False)
+    bk1 = msa.profile_read()
+    flop = 2.5 * _flop_alg(w)
+    rows = msa.msa_backward_pass_rows(dims, tws.numel())
+    res[HEADLINE] = {"workspace_gib": round(tws.numel() / 2**30, 1), "passes": -(-w.seq_len // rows),
+                     "backward_ms": round(bms, 2), "backward_tflops_alg": round(flop / (bms * 1e-3) / 1e12, 2),
+                     "backward_frac_bf16_peak": round(flop / (bms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "bwd_kv_ms_per_call": round(bk1["bwd_kv"][1] / 3, 2) if "bwd_kv" in bk1 else None}
+    _say(f"1M backward: {bms:.1f} ms")
+    del cin, tout, tsel, tlse, tdout, tws
+    torch.cuda.empty_cache()
+    return res
+
+
+def chunked_and_dense(msa, dev):
+    """The 32K prefill as four chunks of 8192 queries against the cache, and a
+    4096-token prefill with top_k = every block (dense kernel) beside the
+    sparse path on the same data."""
+    import torch
+    from synth import get_workload, prefill_inputs
+    res = {}
+    w = get_workload("prefill_32k")
+    pin = prefill_inputs(w, seed=0, device=dev)
+    bounds = [0, 8192, 16384, 24576, w.seq_len]
+    cq = [pin["q"][:, a:b].contiguous() for a, b in zip(bounds[:-1], bounds[1:])]
+    cqi = [pin["q_idx"][:, :, a:b].contiguous() for a, b in zip(bounds[:-1], bounds[1:])]
+    couts = [torch.empty_like(x) for x in cq]
+    ckeys = torch.empty((1, w.n_kv_heads, w.seq_len // w.block_size, 64), dtype=torch.int8, device=dev)
+    dims = msa.make_dims(w.batch, w.seq_len, w.n_q_heads, w.n_kv_heads, w.block_size, w.top_k)
+    cws = torch.empty(msa.msa_prefill_chunk_workspace_bytes(dims, 8192)[1], dtype=torch.uint8, device=dev)
+
+    def chunked():
+        for i, a in enumerate(bounds[:-1]):
+            msa.msa_prefill_chunk(cq[i], cqi[i], pin["k"], pin["v"], pin["k_idx"], ckeys, a, w.block_size, w.top_k,
+                                  out=couts[i], workspace=cws)
+
+    ms = _median_ms(chunked, 5)
+    res["prefill_32k_chunked"] = {"what": "the 32K prefill as four chunks of 8192 queries against the cache",
+                                  "ms": round(ms, 4), "tokens_per_s": round(w.seq_len / (ms * 1e-3), 1),
+                                  "tflops_alg": round(_flop_alg(w) / (ms * 1e-3) / 1e12, 2)}
+    del pin, cq, cqi, couts, cws
+    ws_ = get_workload("prefill_32k", top_k=32)
+    Ss = 4096
+    sin = prefill_inputs(ws_, seed=1, device=dev, seq_len=Ss)
+    sout = torch.empty_like(sin["q"])
+    skeys = torch.empty((1, ws_.n_kv_heads, Ss // ws_.block_size, 64), dtype=torch.int8, device=dev)
+    sdims = msa.make_dims(1, Ss, ws_.n_q_heads, ws_.n_kv_heads, ws_.block_size, ws_.top_k)
+    sws = torch.empty(msa.msa_prefill_chunk_workspace_bytes(sdims, Ss)[1], dtype=torch.uint8, device=dev)
+    dense_ms = _median_ms(lambda: msa.msa_prefill(sin["q"], sin["k"], sin["v"], sin["q_idx"], sin["k_idx"],
+                                                  ws_.block_size, ws_.top_k, out=sout), 5)
+    sparse_ms = _median_ms(lambda: msa.msa_prefill_chunk(sin["q"], sin["q_idx"], sin["k"], sin["v"], sin["k_idx"],
+                                                         skeys, 0, ws_.block_size, ws_.top_k, out=sout,
+                                                         workspace=sws), 5)
+    flop = 4.0 * D_HEAD * ws_.n_q_heads * Ss * (Ss + 1) / 2
+    res["prefill_short_dense"] = {
+        "what": "4096 tokens, top_k 32 = every block: dense causal kernel vs the sparse path on the same data",
+        "dense_ms": round(dense_ms, 4), "sparse_path_ms": round(sparse_ms, 4),
+        "dense_tflops": round(flop / (dense_ms * 1e-3) / 1e12, 2),
+        "dense_frac_bf16_peak": round(flop / (dense_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    del sin, sout, sws
+    torch.cuda.empty_cache()
+    return res
+
+
+# ------------------------------------------------------------------ main
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--core-only", action="store_true",
-                    help="time the step only: no chunked, short-sequence or generation-step extras")
+                    help="time the step only (no other workloads, extras or CPU baseline), e.g. under a profiler")
     ap.add_argument("--train-only", action="store_true",
                     help="time only the training forward (with log-sum-exp) and backward of the 32K prefill")
-    ap.add_argument("--cpu-baseline-worker", default=None, help=argparse.SUPPRESS)
     ap.add_argument("--pmc-run", action="store_true",
                     help="run the counter-collection workload instead of the benchmark")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -295,69 +510,60 @@ def main():
     if args.pmc_summary:
         pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.pmc_commands)
         return 0
-    if args.cpu_baseline_worker:
-        cpu_baseline_worker(args.cpu_baseline_worker)
-        return 0
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the MSA path here runs on a single MI355X; it would shard by GQA group, with no exchange).",
+              file=sys.stderr)
+        return 2
     if args.pmc_run:
         pmc_run()
         return 0
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the MSA path here runs on a single MI355X).", file=sys.stderr)
-        return 2
     if args.train_only:
         train_only(args.steps, args.warmup)
         return 0
 
     import torch
     import block_sparse_attention_33_amd as msa
-    from synth import decode_inputs, get_workload, prefill_inputs
+    from synth import decode_inputs, get_workload, prefill_inputs, sample_rows
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    wp = get_workload("prefill_32k")
-    wd = get_workload("decode_b16_256k")
-    print(f"[bench] generating inputs", file=sys.stderr, flush=True)
+    wp = get_workload(HEADLINE)
+    wd = get_workload(DECODE)
+    _say("generating inputs")
     pin = prefill_inputs(wp, seed=0, device=dev)
     din = decode_inputs(wd, seed=0, device=dev)
     block_keys = msa.msa_pool_block_keys(din["k_idx_cache"], wd.block_size)
-    # generation step (append + decode) at the same shape: the caches hold
-    # L - 1 tokens and each step appends token L - 1
-    L = wd.seq_len
-    gen_keys, gen_sums = msa.msa_decode_init(din["k_idx_cache"], L - 1, wd.block_size)
-    k_new = din["k_cache"][:, :, L - 1].contiguous()
-    v_new = din["v_cache"][:, :, L - 1].contiguous()
-    k_idx_new = din["k_idx_cache"][:, :, L - 1].contiguous()
-    del din["k_idx_cache"]
     out = torch.empty_like(pin["q"])
+    sel = torch.empty((wp.batch, wp.n_kv_heads, wp.seq_len, wp.top_k), dtype=torch.int32, device=dev)
     dout = torch.empty_like(din["q"])
-    pdims = msa.make_dims(wp.batch, wp.seq_len, wp.n_q_heads, wp.n_kv_heads, wp.block_size, wp.top_k)
-    ddims = msa.make_dims(wd.batch, wd.seq_len, wd.n_q_heads, wd.n_kv_heads, wd.block_size, wd.top_k)
-    pws = torch.empty(msa.msa_workspace_bytes(msa.MSA_OP_PREFILL, pdims)[1], dtype=torch.uint8, device=dev)
-    dws = torch.empty(msa.msa_workspace_bytes(msa.MSA_OP_DECODE, ddims)[1], dtype=torch.uint8, device=dev)
+    dsel = torch.empty((wd.batch, wd.n_kv_heads, wd.top_k), dtype=torch.int32, device=dev)
+    pws = _workspace(msa, msa.MSA_OP_PREFILL, wp, dev)
+    dws = _workspace(msa, msa.MSA_OP_DECODE, wd, dev)
 
     def prefill():
-        msa.msa_prefill(pin["q"], pin["k"], pin["v"], pin["q_idx"], pin["k_idx"], wp.block_size, wp.top_k,
-                        out=out, workspace=pws)
+        msa.msa_prefill(pin["q"], pin["k"], pin["v"], pin["q_idx"], pin["k_idx"], wp.block_size, wp.top_k, out=out,
+                        sel=sel, workspace=pws)
 
     def decode():
-        msa.msa_decode(din["q"], din["q_idx"], din["k_cache"], din["v_cache"], block_keys, wd.block_size,
-                       wd.top_k, out=dout, workspace=dws)
+        msa.msa_decode(din["q"], din["q_idx"], din["k_cache"], din["v_cache"], block_keys, wd.block_size, wd.top_k,
+                       out=dout, sel=dsel, workspace=dws)
 
-    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    _say(f"warmup {args.warmup}")
     for _ in range(args.warmup):
         prefill()
         decode()
     torch.cuda.synchronize()
 
+    # Timed region: the library's kernel timing (HIP events around each of its
+    # launches, on its stream) is on for the prefill (its launches are long;
+    # the events cost microseconds) and off for the decode, whose kernel
+    # breakdown comes from a separate pass below.
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    # Timed region: the library's kernel timing is on for the prefill (its
-    # kernels are long; the per-kernel events cost microseconds) and off for
-    # the ~0.1 ms decode call, whose kernel breakdown comes from a separate
-    # pass below.
-    msa.profile_read()              # drop anything recorded before
+    msa.profile_read()
     torch.cuda.synchronize()
+    _say(f"timing {args.steps} steps")
     t0 = time.perf_counter()
     for i in range(args.steps):
         ev[i][0].record()
@@ -375,7 +581,6 @@ def main():
     pre_med = pre_ms[len(pre_ms) // 2]
     dec_med = dec_ms[len(dec_ms) // 2]
     ms_per_step = wall * 1e3 / args.steps
-    # decode kernel breakdown (instrumented, outside the timed region)
     msa.profile_enable(True)
     for _ in range(args.steps):
         decode()
@@ -383,203 +588,12 @@ def main():
     msa.profile_enable(False)
     dkt = msa.profile_read()
 
-    # further measurements outside the timed step (left out by --core-only,
-    # e.g. under a profiler, so that each kernel's launches are those of the
-    # step alone)
-    gen_med = ch_ms = dwarm_med = None
-    short_ms, short_flop = {}, None
-    train_ms, bkt = {}, {}
-    other_cfg = {}
-    if not args.core_only:
-        # generation step: append token L - 1 to the caches, refresh its block's
-        # summary, decode (outside the timed region; same events)
-        def gen_step():
-            msa.msa_decode_step(din["q"], din["q_idx"], k_new, v_new, k_idx_new, din["k_cache"], din["v_cache"],
-                                gen_sums, gen_keys, L, wd.block_size, wd.top_k, out=dout, workspace=dws)
-
-        for _ in range(3):
-            gen_step()
-        torch.cuda.synchronize()
-        gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-        for a, b in gev:
-            a.record()
-            gen_step()
-            b.record()
-        torch.cuda.synchronize()
-        gen_us = sorted(a.elapsed_time(b) * 1e3 for a, b in gev)
-        gen_med = gen_us[len(gen_us) // 2]
-        # chunked prefill of the same 32K workload: four chunks of 8192 queries
-        # against the cache (the K/V tensors serve as caches of capacity S)
-        bounds = [0, 8192, 16384, 24576, wp.seq_len]
-        cq = [pin["q"][:, a:b].contiguous() for a, b in zip(bounds[:-1], bounds[1:])]
-        cqi = [pin["q_idx"][:, :, a:b].contiguous() for a, b in zip(bounds[:-1], bounds[1:])]
-        couts = [torch.empty_like(x) for x in cq]
-        ckeys = torch.empty_like(block_keys_prefill_shape(pin, wp))
-        cws = torch.empty(_chunk_ws_bytes(msa, pdims, 8192), dtype=torch.uint8, device=dev)
-
-        def chunked():
-            for i, a in enumerate(bounds[:-1]):
-                msa.msa_prefill_chunk(cq[i], cqi[i], pin["k"], pin["v"], pin["k_idx"], ckeys, a, wp.block_size,
-                                      wp.top_k, out=couts[i], workspace=cws)
-
-        chunked()
-        torch.cuda.synchronize()
-        cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
-        for a, b in cev:
-            a.record()
-            chunked()
-            b.record()
-        torch.cuda.synchronize()
-        ch_ms = sorted(a.elapsed_time(b) for a, b in cev)[2]
-        del cq, cqi, couts, cws
-
-        # short sequence, top_k covering every block (4096 tokens, top_k 32 =
-        # nb): msa_prefill takes the dense causal kernel; the chunked entry point
-        # runs the sparse path on the same data
-        ws_ = get_workload("prefill_32k", top_k=32)
-        Ss = 4096
-        sin = prefill_inputs(ws_, seed=1, device=dev, seq_len=Ss)
-        sout = torch.empty_like(sin["q"])
-        skeys = torch.empty((1, ws_.n_kv_heads, Ss // ws_.block_size, 64), dtype=torch.int8, device=dev)
-        sdims = msa.make_dims(1, Ss, ws_.n_q_heads, ws_.n_kv_heads, ws_.block_size, ws_.top_k)
-        sws = torch.empty(_chunk_ws_bytes(msa, sdims, Ss), dtype=torch.uint8, device=dev)
-        short_runs = {
-            "dense": lambda: msa.msa_prefill(sin["q"], sin["k"], sin["v"], sin["q_idx"], sin["k_idx"], ws_.block_size,
-                                             ws_.top_k, out=sout),
-            "sparse_path": lambda: msa.msa_prefill_chunk(sin["q"], sin["q_idx"], sin["k"], sin["v"], sin["k_idx"], skeys,
-                                                         0, ws_.block_size, ws_.top_k, out=sout, workspace=sws),
-        }
-        short_ms = {}
-        for name_, fn in short_runs.items():
-            fn()
-            torch.cuda.synchronize()
-            sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
-            for a, b in sev:
-                a.record()
-                fn()
-                b.record()
-            torch.cuda.synchronize()
-            short_ms[name_] = sorted(a.elapsed_time(b) for a, b in sev)[2]
-        short_flop = 4.0 * D_HEAD * ws_.n_q_heads * Ss * (Ss + 1) / 2
-        del sin, sout, sws
-
-        # training step of the same 32K prefill: the forward with its
-        # log-sum-exp, then the backward (dq, dk, dv; selection fixed)
-        from synth import grad_output
-        bout, bsel, blse = msa.msa_prefill_lse(pin["q"], pin["k"], pin["v"], pin["q_idx"], pin["k_idx"],
-                                               wp.block_size, wp.top_k, workspace=pws)
-        bdout = grad_output(wp, seed=0, device=dev)
-        bws = torch.empty(msa.msa_workspace_bytes(msa.MSA_OP_BACKWARD, pdims)[1], dtype=torch.uint8, device=dev)
-        train_runs = {
-            "forward_lse": lambda: msa.msa_prefill_lse(pin["q"], pin["k"], pin["v"], pin["q_idx"], pin["k_idx"],
-                                                       wp.block_size, wp.top_k, workspace=pws),
-            "backward": lambda: msa.msa_prefill_backward(pin["q"], pin["k"], pin["v"], bout, bdout, blse, bsel,
-                                                         wp.block_size, workspace=bws),
-        }
-        for name_, fn in train_runs.items():
-            fn()
-            torch.cuda.synchronize()
-            msa.profile_read()
-            msa.profile_enable(name_ == "backward")
-            tev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
-            for a, b in tev:
-                a.record()
-                fn()
-                b.record()
-            torch.cuda.synchronize()
-            msa.profile_enable(False)
-            train_ms[name_] = sorted(a.elapsed_time(b) for a, b in tev)[2]
-            if name_ == "backward":
-                bkt = msa.profile_read()
-        del bout, bsel, blse, bdout, bws
-
-        # the other prefill workloads, timed the same way (median of a few
-        # calls after one warm-up; the 2K one is launch-bound)
-        for name_, reps in (("tiny_2k", 10), ("structured_128k", 5), ("prefill_1m", 3)):
-            wc = get_workload(name_)
-            cin = prefill_inputs(wc, seed=0, device=dev)
-            cdims = msa.make_dims(wc.batch, wc.seq_len, wc.n_q_heads, wc.n_kv_heads, wc.block_size, wc.top_k)
-            cws = torch.empty(msa.msa_workspace_bytes(msa.MSA_OP_PREFILL, cdims)[1], dtype=torch.uint8, device=dev)
-            cout = torch.empty_like(cin["q"])
-
-            def fn():
-                msa.msa_prefill(cin["q"], cin["k"], cin["v"], cin["q_idx"], cin["k_idx"], wc.block_size, wc.top_k,
-                                out=cout, workspace=cws)
-
-            fn()
-            torch.cuda.synchronize()
-            pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-            for a, b in pev:
-                a.record()
-                fn()
-                b.record()
-            torch.cuda.synchronize()
-            cms = sorted(a.elapsed_time(b) for a, b in pev)[reps // 2]
-            cflop = 4.0 * wc.head_dim * wc.n_q_heads * _prefill_counts(wc)[0]
-            other_cfg[name_] = {"seq_len": wc.seq_len, "n_q_heads": wc.n_q_heads, "n_kv_heads": wc.n_kv_heads,
-                                "block_size": wc.block_size, "top_k": wc.top_k, "calls": reps,
-                                "ms": round(cms, 4), "tokens_per_s": round(wc.batch * wc.seq_len / (cms * 1e-3), 1),
-                                "tflops_alg": round(cflop / (cms * 1e-3) / 1e12, 2),
-                                "frac_bf16_peak": round(cflop / (cms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
-            print(f"[bench] {name_}: {cms:.3f} ms", file=sys.stderr, flush=True)
-            if name_ == "prefill_1m":
-                # its backward too: the full workspace (about 276 GB) does not
-                # fit beside the tensors, so it runs in query passes in what
-                # the binding allocates by default (80 % of the free memory)
-                cws = None
-                torch.cuda.empty_cache()
-                tout, tsel, tlse = msa.msa_prefill_lse(cin["q"], cin["k"], cin["v"], cin["q_idx"], cin["k_idx"],
-                                                       wc.block_size, wc.top_k)
-                tdout = grad_output(wc, seed=0, device=dev)
-                cout = None
-                torch.cuda.empty_cache()
-
-                def bfn():
-                    return msa.msa_prefill_backward(cin["q"], cin["k"], cin["v"], tout, tdout, tlse, tsel,
-                                                    wc.block_size, workspace=tws)
-
-                tlo, thi = msa.msa_workspace_bytes(msa.MSA_OP_BACKWARD, cdims)
-                tws = torch.empty(max(tlo, min(thi, int(torch.cuda.mem_get_info(dev)[0] * 0.8) - (20 << 30))),
-                                  dtype=torch.uint8, device=dev)
-                bfn()
-                torch.cuda.synchronize()
-                msa.profile_read()
-                msa.profile_enable(True)
-                bev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(2)]
-                for a, b in bev:
-                    a.record()
-                    bfn()
-                    b.record()
-                torch.cuda.synchronize()
-                msa.profile_enable(False)
-                bk1 = msa.profile_read()
-                bms = max(a.elapsed_time(b) for a, b in bev)
-                other_cfg[name_]["backward"] = {
-                    "workspace_gib": round(tws.numel() / 2**30, 1), "passes": bk1["bwd_kv"][0] // 2,
-                    "ms": round(bms, 2), "tflops_alg": round(2.5 * cflop / (bms * 1e-3) / 1e12, 2),
-                    "bwd_kv_ms": round(bk1["bwd_kv"][1] / 2, 2)}
-                print(f"[bench] {name_} backward: {bms:.1f} ms", file=sys.stderr, flush=True)
-                del tout, tsel, tlse, tdout, tws
-            cin = cout = cws = None
-            torch.cuda.empty_cache()
-
-        # the plain decode timed the same way (back to back, so the kept blocks
-        # may still sit in the memory-side cache, unlike in the step above where
-        # a prefill runs in between)
-        for a, b in gev:
-            a.record()
-            decode()
-            b.record()
-        torch.cuda.synchronize()
-        dwarm_us = sorted(a.elapsed_time(b) * 1e3 for a, b in gev)
-        dwarm_med = dwarm_us[len(dwarm_us) // 2]
-
     per_head_keys, pairs, rows_merged = _prefill_counts(wp)
     D = wp.head_dim
     flop_alg = 4.0 * D * wp.n_q_heads * per_head_keys
     tokens = wp.batch * wp.seq_len
-    # dominant kernel: the attention kernel (all selected blocks of every
-    # query); per step it may run in several launches (passes)
+    # dominant kernel: the attention kernel (all kept blocks of every query),
+    # one launch per query chunk
     n_att, att_ms = kt.get("attend", (0, 0.0))
     att_ms_step = att_ms / args.steps
     att_launch_ms = att_ms / max(1, n_att)
@@ -594,8 +608,6 @@ def main():
     dbytes = _decode_bytes(wd)
     traffic = _measured_traffic()
 
-    kernels = {k: {"launches": n, "avg_ms": round(ms / max(1, n), 4)}
-               for k, (n, ms) in sorted(list(kt.items()) + list(dkt.items()))}
     rec = {
         "metric": "MSA prefill tokens/s + TFLOP/s (% bf16 MFMA peak); decode tokens/s, HBM GB/s",
         "value": round(tokens / (pre_med * 1e-3), 1),
@@ -609,11 +621,12 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "prefill_32k + decode_b16_256k", "batch": wp.batch, "seq_len": wp.seq_len,
+        "config": {"workload": f"{HEADLINE} + {DECODE}", "batch": wp.batch, "seq_len": wp.seq_len,
                    "n_q_heads": wp.n_q_heads, "n_kv_heads": wp.n_kv_heads, "head_dim": D,
                    "block_size": wp.block_size, "top_k": wp.top_k, "decode_batch": wd.batch,
                    "decode_cache_len": wd.seq_len, "parallelism": "none (1 GPU)"},
         "prefill": {
+            "workload": HEADLINE,
             "ms": round(pre_med, 4),
             "tokens_per_s": round(tokens / (pre_med * 1e-3), 1),
             "tflops_alg": round(flop_alg / (pre_med * 1e-3) / 1e12, 2),
@@ -621,49 +634,17 @@ def main():
             "flop_alg": flop_alg,
         },
         "decode": {
+            "workload": DECODE,
             "us": round(dec_med * 1e3, 2),
             "tokens_per_s": round(wd.batch / (dec_med * 1e-3), 1),
             "hbm_gbs_alg": round(dbytes / (dec_med * 1e-3) / 1e9, 1),
             "frac_hbm_peak": round(dbytes / (dec_med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "bytes_alg": dbytes,
-        },
-        "prefill_chunked": None if ch_ms is None else {
-            "what": "the same 32K prefill as four chunks of 8192 queries against the cache",
-            "ms": round(ch_ms, 4),
-            "tokens_per_s": round(tokens / (ch_ms * 1e-3), 1),
-            "tflops_alg": round(flop_alg / (ch_ms * 1e-3) / 1e12, 2),
-        },
-        "prefill_short_dense": None if not short_ms else {
-            "what": "4096 tokens, top_k 32 = every block: dense causal kernel vs the sparse path on the same data",
-            "dense_ms": round(short_ms["dense"], 4),
-            "sparse_path_ms": round(short_ms["sparse_path"], 4),
-            "dense_tflops": round(short_flop / (short_ms["dense"] * 1e-3) / 1e12, 2),
-            "dense_frac_bf16_peak": round(short_flop / (short_ms["dense"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-        },
-        "training": None if not train_ms else {
-            "what": "the 32K prefill for training: forward with log-sum-exp, and the main-branch backward "
-                    "(dq, dk, dv; selection fixed)",
-            "forward_lse_ms": round(train_ms["forward_lse"], 4),
-            "backward_ms": round(train_ms["backward"], 4),
-            "backward_tflops_alg": round(2.5 * flop_alg / (train_ms["backward"] * 1e-3) / 1e12, 2),
-            "backward_frac_bf16_peak": round(2.5 * flop_alg / (train_ms["backward"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-                                             4),
-            "backward_flop_alg": 2.5 * flop_alg,
-            "bwd_kv_tflops_alg": round(2.5 * flop_alg / (bkt["bwd_kv"][1] / bkt["bwd_kv"][0] * 1e-3) / 1e12, 2)
-            if "bwd_kv" in bkt else None,
-            "kernels": {k: {"launches": n, "avg_ms": round(ms / max(1, n), 4)} for k, (n, ms) in sorted(bkt.items())},
-        },
-        "prefill_other_workloads": other_cfg or None,
-        "decode_step": None if gen_med is None else {
-            "what": "append one token per sequence (K/V rows, running index-key sum, block summary) + decode",
-            "us": round(gen_med, 2),
-            "tokens_per_s": round(wd.batch / (gen_med * 1e-6), 1),
-            "frac_hbm_peak": round(dbytes / (gen_med * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
-            "timing": "back-to-back calls",
-            "decode_only_back_to_back_us": round(dwarm_med, 2),
+            "timing": "right after the 1M prefill in the same stream",
         },
         "roofline": {
-            "kernel": "attend (KV-outer block attention, all kept blocks)",
+            "kernel": "attend_kernel<128> (KV-outer block attention, all kept blocks of one query chunk)",
+            "workload": HEADLINE,
             "bound": "mfma",
             "achieved": round(att_tflops, 2) if att_tflops else None,
             "peak": PEAK_BF16_TFLOPS,
@@ -685,17 +666,31 @@ def main():
             if (traffic and att_launch_ms) else None,
         },
         "merge_kernel": {
-            "ms": round(mrg_ms_step, 4),
+            "ms_per_step": round(mrg_ms_step, 4),
             "design_bytes": mrg_design_bytes,
             "hbm_gbs": round(mrg_design_bytes / (mrg_ms_step * 1e-3) / 1e9, 1) if mrg_ms_step else None,
         },
-        "kernels": kernels,
+        "kernels": {k: {"launches": n, "avg_ms": round(ms / max(1, n), 4)}
+                    for k, (n, ms) in sorted(list(kt.items()) + list(dkt.items()))},
     }
-    if not args.no_cpu_baseline:
-        print(f"[bench] cpu baseline ({CPU_SAMPLE_ROWS} rows)", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(pin, wp, CPU_SAMPLE_ROWS)
-    else:
-        rec["cpu_baseline"] = None
+    cpu = not (args.no_cpu_baseline or args.core_only)
+    baselines = {}
+    if cpu:
+        _say(f"cpu baseline: {HEADLINE} ({CPU_SAMPLE_ROWS} rows), {DECODE}")
+        rows = sample_rows(wp.seq_len, CPU_SAMPLE_ROWS, 12345)
+        baselines[HEADLINE] = cpu_baseline_prefill(HEADLINE, pin, out, sel, rows)
+        baselines[DECODE] = cpu_baseline_decode(din, block_keys, dout, dsel, wd)
+    if not args.core_only:
+        rec["decode"].update(decode_extras(msa, din, block_keys, wd, dws, dout, args.steps))
+    del pin, out, sel, pws, din, block_keys, dout, dsel, dws
+    torch.cuda.empty_cache()
+    if not args.core_only:
+        rec["prefill_other_workloads"], more = other_prefills(msa, dev, cpu)
+        baselines.update(more)
+        rec.update(chunked_and_dense(msa, dev))
+        rec["training"] = training_extras(msa, dev)
+    rec["cpu_baseline"] = baselines.get(HEADLINE)
+    rec["cpu_baselines"] = baselines or None
     print(json.dumps(rec), flush=True)
     return 0
 

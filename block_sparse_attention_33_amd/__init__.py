@@ -18,7 +18,8 @@ from . import _lib
 from ._lib import MSA_OP_BACKWARD, MSA_OP_DECODE, MSA_OP_INDEX, MSA_OP_POOL, MSA_OP_PREFILL, MsaDims  # noqa: F401
 
 __all__ = [
-    "MsaError", "make_dims", "profile_enable", "profile_read", "msa_workspace_bytes", "msa_backward_pass_rows", "msa_pool_block_keys", "msa_index_select",
+    "MsaError", "make_dims", "profile_enable", "profile_read", "msa_workspace_bytes", "msa_backward_pass_rows", "msa_prefill_chunk_workspace_bytes", "msa_plan_check",
+    "msa_pool_block_keys", "msa_index_select",
     "msa_prefill", "msa_prefill_lse", "msa_prefill_backward", "msa_prefill_chunk", "msa_decode", "msa_decode_noalloc", "msa_decode_init", "msa_decode_step", "MSA_OP_POOL", "MSA_OP_INDEX", "MSA_OP_PREFILL", "MSA_OP_DECODE", "MSA_OP_BACKWARD",
 ]
 
@@ -60,6 +61,23 @@ def msa_backward_pass_rows(dims: MsaDims, ws_bytes: int) -> int:
     _check(_lib.load().msa_backward_pass_rows(ctypes.byref(dims), ctypes.c_size_t(ws_bytes), ctypes.byref(rows)),
            "msa_backward_pass_rows")
     return rows.value
+
+
+def msa_prefill_chunk_workspace_bytes(dims: MsaDims, count: int):
+    """(minimum, full) workspace bytes of msa_prefill_chunk for count queries."""
+    lo, hi = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check(_lib.load().msa_prefill_chunk_workspace_bytes(ctypes.byref(dims), count, ctypes.byref(lo),
+                                                         ctypes.byref(hi)), "msa_prefill_chunk_workspace_bytes")
+    return lo.value, hi.value
+
+
+def msa_plan_check(op, dims: MsaDims, ws_bytes: int) -> int:
+    """Launches the call would make with a workspace of ws_bytes (host only;
+    raises MsaError when the workspace is too small)."""
+    n = ctypes.c_int32(0)
+    _check(_lib.load().msa_plan_check(op, ctypes.byref(dims), ctypes.c_size_t(ws_bytes), ctypes.byref(n)),
+           "msa_plan_check")
+    return n.value
 
 
 def profile_read():

@@ -1,4 +1,6 @@
-"""The CPU oracle over many query rows at once, in worker processes.
+"""The CPU oracle over many query rows at once, in worker processes --
+TEST INFRASTRUCTURE ONLY (the test suite and the benchmark's CPU-baseline
+leg use it; the library never does).
 
 The oracle is single-threaded by design; full-size parity checks (every row
 of a 32K prefill, 4096 sampled rows of the 128K and 1M prefills) run it over

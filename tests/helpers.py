@@ -119,7 +119,7 @@ def oracle_prefill_rows(inp, w, rows, block_size=None, top_k=None):
 def oracle_prefill_rows_pooled(inp, w, rows, block_size=None, top_k=None):
     """The same for many rows, over worker processes: (summaries, sel,
     bf16-rounded output as float32, stats)."""
-    from tests import oracle_pool
+    from oracle import pool as oracle_pool
     bs = block_size or w.block_size
     k = top_k or w.top_k
     rt = torch.as_tensor(rows, device=inp["q"].device)

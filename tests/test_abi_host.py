@@ -299,10 +299,11 @@ def test_decode_noalloc_validation(lib):
         args = [FAKE] * 6
         args[i] = None
         assert lib.msa_decode_noalloc(ctypes.byref(dims), *args, None, None) == -1
-    # the decode workload's scratch fits; 32768 units x 8 heads do not
+    # the decode workload's scratch fits; that of 524288 units (65536
+    # sequences x 8 groups) does not
     st, lo, _ = _ws(lib, _lib.MSA_OP_DECODE, dims)
     assert st == 0 and lo <= _lib.MSA_DECODE_SCRATCH_BYTES
-    big = D(batch=4096, seq_len=1000)
+    big = D(batch=65536, seq_len=1)
     st, lo, _ = _ws(lib, _lib.MSA_OP_DECODE, big)
     assert st == 0 and lo > _lib.MSA_DECODE_SCRATCH_BYTES
     assert lib.msa_decode_noalloc(ctypes.byref(big), *([FAKE] * 6), None, None) == _lib.MSA_ERR_SCRATCH

@@ -61,11 +61,13 @@ def test_decode_noalloc_two_calls_second_smaller():
 
 
 def test_decode_noalloc_rejects_oversized_shape():
-    w = get_workload("decode_b16_256k", n_q_heads=8, n_kv_heads=8, top_k=4)
-    q = torch.zeros((4096, 8, 128), dtype=torch.bfloat16, device=DEV)
-    qi = torch.zeros((4096, 8, 64), dtype=torch.int8, device=DEV)
-    kc = torch.zeros((4096, 8, 1, 128), dtype=torch.bfloat16, device=DEV)
-    bk = torch.zeros((4096, 8, 1, 64), dtype=torch.int8, device=DEV)
+    """65536 one-token sequences x 8 groups: their selections (33.5 MB) do
+    not fit the fixed scratch; the call is refused before any launch."""
+    w = get_workload("decode_b16_256k", n_q_heads=8, n_kv_heads=8, top_k=16)
+    q = torch.zeros((65536, 8, 128), dtype=torch.bfloat16, device=DEV)
+    qi = torch.zeros((65536, 8, 64), dtype=torch.int8, device=DEV)
+    kc = torch.zeros((65536, 8, 1, 128), dtype=torch.bfloat16, device=DEV)
+    bk = torch.zeros((65536, 8, 1, 64), dtype=torch.int8, device=DEV)
     out = torch.empty_like(q)
     with pytest.raises(msa.MsaError) as e:
         msa.msa_decode_noalloc(q, qi, kc, kc, bk, w.block_size, w.top_k, out)
