@@ -15,12 +15,13 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import MSA_OP_BACKWARD, MSA_OP_DECODE, MSA_OP_INDEX, MSA_OP_POOL, MSA_OP_PREFILL, MsaDims  # noqa: F401
+from ._lib import (MSA_OP_BACKWARD, MSA_OP_DECODE, MSA_OP_INDEX, MSA_OP_POOL, MSA_OP_PREFILL,  # noqa: F401
+                   MSA_OP_PREFILL_VARLEN, MsaDims)
 
 __all__ = [
     "MsaError", "make_dims", "profile_enable", "profile_read", "msa_workspace_bytes", "msa_backward_pass_rows", "msa_prefill_chunk_workspace_bytes", "msa_plan_check",
     "msa_pool_block_keys", "msa_index_select",
-    "msa_prefill", "msa_prefill_lse", "msa_prefill_backward", "msa_prefill_chunk", "msa_decode", "msa_decode_noalloc", "msa_decode_init", "msa_decode_step", "MSA_OP_POOL", "MSA_OP_INDEX", "MSA_OP_PREFILL", "MSA_OP_DECODE", "MSA_OP_BACKWARD",
+    "msa_prefill", "msa_prefill_varlen", "msa_prefill_switched", "msa_prefill_lse", "msa_prefill_backward", "msa_prefill_chunk", "msa_decode", "msa_decode_noalloc", "msa_decode_init", "msa_decode_step", "MSA_OP_POOL", "MSA_OP_INDEX", "MSA_OP_PREFILL", "MSA_OP_DECODE", "MSA_OP_BACKWARD",
 ]
 
 
@@ -188,6 +189,77 @@ def msa_prefill(q, k, v, q_idx, k_idx, block_size: int, top_k: int, softmax_scal
     _check(_lib.load().msa_prefill(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(q_idx), _ptr(k_idx),
                                    _ptr(out), _ptr(sel), _ptr(ws), ws_bytes, _stream(dev)), "msa_prefill")
     return (out, sel) if return_sel else out
+
+
+def msa_prefill_varlen(q, k, v, q_idx, k_idx, cu_seqlens, block_size: int, top_k: int, softmax_scale: float = 0.0,
+                       out=None, sel=None, return_sel: bool = False, workspace=None):
+    """Ragged batch of sequences packed along the token axis -> out [T, Hq, D]
+    bf16 (and sel [G, T, top_k] when return_sel).  q [T, Hq, D]; k, v [G, T, D];
+    q_idx, k_idx [G, T, di]; cu_seqlens: host sequence offsets (list or CPU
+    tensor, n + 1 entries from 0 to T)."""
+    _need(q, "q", torch.bfloat16, 3)
+    dev = q.device
+    _need(k, "k", torch.bfloat16, 3, dev)
+    _need(v, "v", torch.bfloat16, 3, dev)
+    _need(q_idx, "q_idx", torch.int8, 3, dev)
+    _need(k_idx, "k_idx", torch.int8, 3, dev)
+    T, Hq, D = q.shape
+    G = k.shape[0]
+    if k.shape != (G, T, D) or v.shape != k.shape:
+        raise ValueError(f"k/v must be [G, T, D] = {(G, T, D)}")
+    if q_idx.shape[:2] != (G, T) or k_idx.shape != q_idx.shape:
+        raise ValueError("q_idx/k_idx must be [G, T, di]")
+    cu = [int(x) for x in (cu_seqlens.tolist() if isinstance(cu_seqlens, torch.Tensor) else cu_seqlens)]
+    if len(cu) < 2 or cu[-1] != T:
+        raise ValueError("cu_seqlens must have n + 1 entries ending at T")
+    n = len(cu) - 1
+    longest = max(b - a for a, b in zip(cu[:-1], cu[1:]))
+    dims = make_dims(n, max(1, longest), Hq, G, block_size, top_k, head_dim=D, idx_dim=q_idx.shape[2],
+                     softmax_scale=softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16, 3, dev)
+    if sel is None and return_sel:
+        sel = torch.empty((G, T, top_k), dtype=torch.int32, device=dev)
+    if sel is not None:
+        _need(sel, "sel", torch.int32, 3, dev)
+    ws, ws_bytes = _workspace(MSA_OP_PREFILL_VARLEN, dims, dev, workspace)
+    cu_arr = (ctypes.c_int32 * len(cu))(*cu)
+    _check(_lib.load().msa_prefill_varlen(ctypes.byref(dims), cu_arr, _ptr(q), _ptr(k), _ptr(v), _ptr(q_idx),
+                                          _ptr(k_idx), _ptr(out), _ptr(sel), _ptr(ws), ws_bytes, _stream(dev)),
+           "msa_prefill_varlen")
+    return (out, sel) if return_sel else out
+
+
+def msa_prefill_switched(q, k, v, q_idx, k_idx, block_size: int, top_k: int, dense_below: int = 0,
+                         softmax_scale: float = 0.0, out=None, sel=None, workspace=None):
+    """msa_prefill, or -- for sequences shorter than dense_below tokens (0:
+    8192) -- standard causal GQA attention (not MSA; sel filled with -1).
+    Returns (out, took_dense)."""
+    _need(q, "q", torch.bfloat16, 4)
+    dev = q.device
+    _need(k, "k", torch.bfloat16, 4, dev)
+    _need(v, "v", torch.bfloat16, 4, dev)
+    _need(q_idx, "q_idx", torch.int8, 4, dev)
+    _need(k_idx, "k_idx", torch.int8, 4, dev)
+    B, S, Hq, D = q.shape
+    G = k.shape[1]
+    if k.shape != (B, G, S, D) or v.shape != k.shape:
+        raise ValueError(f"k/v must be [B, G, S, D] = {(B, G, S, D)}")
+    dims = make_dims(B, S, Hq, G, block_size, top_k, head_dim=D, idx_dim=q_idx.shape[3],
+                     softmax_scale=softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16, 4, dev)
+    if sel is not None:
+        _need(sel, "sel", torch.int32, 4, dev)
+    below = dense_below if dense_below > 0 else 8192
+    ws, ws_bytes = (None, 0) if S < below else _workspace(MSA_OP_PREFILL, dims, dev, workspace)
+    took = ctypes.c_int32(-1)
+    _check(_lib.load().msa_prefill_switched(ctypes.byref(dims), int(dense_below), _ptr(q), _ptr(k), _ptr(v),
+                                            _ptr(q_idx), _ptr(k_idx), _ptr(out), _ptr(sel), _ptr(ws), ws_bytes,
+                                            _stream(dev), ctypes.byref(took)), "msa_prefill_switched")
+    return out, bool(took.value)
 
 
 def msa_prefill_lse(q, k, v, q_idx, k_idx, block_size: int, top_k: int, softmax_scale: float = 0.0,

@@ -17,6 +17,7 @@ MSA_OP_INDEX = 1
 MSA_OP_PREFILL = 2
 MSA_OP_DECODE = 3
 MSA_OP_BACKWARD = 4
+MSA_OP_PREFILL_VARLEN = 5
 
 
 class MsaDims(ctypes.Structure):
@@ -51,6 +52,10 @@ SIGNATURES = {
     "msa_pool_block_keys": (ctypes.c_int, [_DIMS, _P, _P, _P]),
     "msa_index_select": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "msa_prefill": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "msa_prefill_varlen": (ctypes.c_int, [_DIMS, ctypes.POINTER(ctypes.c_int32), _P, _P, _P, _P, _P, _P, _P, _P,
+                                          ctypes.c_size_t, _P]),
+    "msa_prefill_switched": (ctypes.c_int, [_DIMS, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                                            _P, ctypes.POINTER(ctypes.c_int32)]),
     "msa_decode": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "msa_decode_noalloc": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P]),
     "msa_prefill_lse": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),

@@ -776,14 +776,16 @@ __global__ __launch_bounds__(512 / NCT, 1) void dense_kernel(const uint16_t* __r
   }
 }
 
-// sel of a dense prefill: every block up to the own one, ascending, then -1.
+// sel of a dense prefill: every block up to the own one, ascending, then -1
+// (rows of unit u at sel + u * sel_rows * top_k).
 __global__ __launch_bounds__(256) void dense_sel_kernel(int32_t* __restrict__ sel, int units, int S, int bs_log2,
-                                                        int top_k) {
+                                                        int top_k, int sel_rows) {
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
   if (i >= (long)units * S * top_k) return;
   const int s = (int)(i % top_k);
   const int t = (int)((i / top_k) % S);
-  sel[i] = s <= (t >> bs_log2) ? s : -1;
+  const long u = i / ((long)S * top_k);
+  sel[(u * sel_rows + t) * top_k + s] = s <= (t >> bs_log2) ? s : -1;
 }
 
 }  // namespace
@@ -818,7 +820,7 @@ hipError_t launch_merge(const PrefillShape& sh, const PassInfo& pass, const uint
 
 
 hipError_t launch_dense(const PrefillShape& sh, const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                        uint16_t* out, int32_t* sel, hipStream_t st) {
+                        uint16_t* out, int32_t* sel, int sel_rows, hipStream_t st) {
   int r_log2 = 0;
   while ((1 << r_log2) < sh.r) ++r_log2;
   const int tpt = kItemRows >> r_log2;
@@ -847,7 +849,7 @@ hipError_t launch_dense(const PrefillShape& sh, const uint16_t* q, const uint16_
   if (e != hipSuccess || sel == nullptr) return e;
   const long n = (long)sh.B * sh.G * sh.S * sh.top_k;
   hipLaunchKernelGGL(dense_sel_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, sel, sh.B * sh.G, sh.S,
-                     sh.bs_log2, sh.top_k);
+                     sh.bs_log2, sh.top_k, sel_rows);
   return hipGetLastError();
 }
 

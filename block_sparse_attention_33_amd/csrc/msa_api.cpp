@@ -27,7 +27,11 @@ bool pow2_in(int x, int lo, int hi) { return x >= lo && x <= hi && (x & (x - 1))
 
 static_assert(MSA_DECODE_SCRATCH_BYTES == msa::kDecodeScratchBytes, "msa.h and the decode scratch disagree");
 
-constexpr long kMaxSparseTopK = 32;  // selection slots of the sparse paths (5 bits in a CSR entry)
+constexpr long kMaxSparseTopK = 32;
+// msa_prefill_switched runs standard attention below this many tokens when
+// the caller passes no threshold (the figure one page gives for where the
+// selection stops paying).
+constexpr long kDefaultDenseBelow = 8192;  // selection slots of the sparse paths (5 bits in a CSR entry)
 
 struct Dims {
   long B, S, Hq, G, r, D, di, bs, nb, k, kp, U;
@@ -269,6 +273,34 @@ Dims chunk_dims(const Dims& dc, long n_q) {
   return d;
 }
 
+// Dims of one sequence of length L of a ragged batch (dims.batch sequences,
+// dims.seq_len the longest): a batch of one.
+Dims seq_dims(const Dims& d, long L) {
+  Dims o = d;
+  o.B = 1;
+  o.S = L;
+  o.nb = (L + d.bs - 1) / d.bs;
+  o.U = d.G;
+  return o;
+}
+
+// The sequence lengths of a ragged batch from host cu_seqlens [n + 1]:
+// cu_seqlens[0] = 0, non-decreasing, no length above dims.seq_len, at least
+// one token in all; *total = cu_seqlens[n].
+int check_cu_seqlens(const Dims& d, const int32_t* cu, long* total) {
+  if (cu == nullptr || cu[0] != 0) return MSA_ERR_INVALID_ARG;
+  for (long s = 0; s < d.B; ++s) {
+    const long L = (long)cu[s + 1] - cu[s];
+    if (L < 0 || L > d.S) return MSA_ERR_INVALID_ARG;
+  }
+  *total = cu[d.B];
+  if (*total < 1) return MSA_ERR_INVALID_ARG;
+  // row offsets of the packed tensors stay within int32 arithmetic of the
+  // kernels' per-unit strides
+  if ((long)d.G * *total * d.k >= (1L << 31) || *total >= (1L << 30)) return MSA_ERR_UNSUPPORTED;
+  return MSA_OK;
+}
+
 // A long prefill runs in query chunks.  Up to 128K tokens a chunk holds
 // 16384 queries: its partials (about 280 MB for 64 query heads and top_k 16)
 // then mostly stay in the 256 MB memory-side cache until the merge reads
@@ -289,13 +321,18 @@ long prefill_query_chunk(const Dims& d) {
   return (quarter + kPrefillQueryChunk - 1) / kPrefillQueryChunk * kPrefillQueryChunk;
 }
 
-// Prefill of the queries at positions q0 .. q0 + n_q - 1 of sequences whose
-// keys, values and index keys are rows 0 .. q0 + n_q - 1 of k, v and k_idx
-// (dc.S rows per unit; q0 = 0 and n_q = dc.S for a whole prefill).  q,
-// q_idx, out and sel (when given) hold the n_q query rows, q_stride rows
-// apart per batch / unit.  ext_keys: block summaries that persist across
-// calls (dc.nb rows per unit; blocks before q0 / bs already pooled), or
-// null to pool every block into the workspace.
+// Row strides of the tensors a prefill reads and writes, in rows of D (or
+// di, or top_k) elements: q, out and lse per batch entry; k, v and k_idx per
+// (batch, group) unit; q_idx and sel per unit.  A whole prefill of [B, S]
+// tensors has S everywhere; a chunk against a cache of capacity C has C for
+// the caches; a packed ragged batch has the total token count for k, v and
+// the index tensors.
+struct Strides {
+  long q_rows, kv_rows, qi_rows, sel_rows;
+};
+
+Strides dense_strides(const Dims& d) { return Strides{d.S, d.S, d.S, d.S}; }
+
 // The plan of one query chunk (n_q rows of a prefill of dc) in a workspace
 // of ws_bytes: the inversion's plan, the workspace layout and the (batch,
 // group) units per pass -- as many as the workspace holds partials for.
@@ -325,7 +362,13 @@ int plan_chunk(const Dims& dc, long n_q, size_t ws_bytes, ChunkRun* run) {
   return MSA_OK;
 }
 
-int run_prefill(const Dims& dc, long q0, long n_q, long q_stride, const uint16_t* q, const uint16_t* k,
+// Prefill of the queries at positions q0 .. q0 + n_q - 1 of sequences whose
+// keys, values and index keys are rows 0 .. q0 + n_q - 1 of k, v and k_idx
+// (q0 = 0 and n_q = dc.S for a whole prefill); q, q_idx, out, sel (when
+// given) and lse (when given) hold the n_q query rows.  ext_keys: block
+// summaries that persist across calls (dc.nb rows per unit; blocks before
+// q0 / bs already pooled), or null to pool every block into the workspace.
+int run_prefill(const Dims& dc, long q0, long n_q, const Strides& str, const uint16_t* q, const uint16_t* k,
                 const uint16_t* v, const int8_t* q_idx, const int8_t* k_idx, int8_t* ext_keys, uint16_t* out,
                 int32_t* sel, float* lse, void* ws, size_t ws_bytes, hipStream_t s) {
   const Dims d = chunk_dims(dc, n_q);
@@ -357,19 +400,19 @@ int run_prefill(const Dims& dc, long q0, long n_q, long q_stride, const uint16_t
   cp.tpc = (int)P.tpc;
   cp.n_chunks = (int)P.n_chunks;
   cp.n_ranges = (int)P.n_ranges;
-  const int sel_stride = sel ? (int)q_stride : S;  // the workspace's sel holds the n_q rows only
+  const int sel_stride = sel ? (int)str.sel_rows : S;  // the workspace's sel holds the n_q rows only
   cp.q_stride = sel_stride;
   const int tpi = (int)P.tokens_per_item;
   const int iq0 = (int)q0;
   if (ext_keys != nullptr) {
     // the blocks the new tokens fall in; earlier ones are the caller's
     bkeys = ext_keys;
-    MSA_LAUNCH_NAMED("pool", s, msa::launch_pool_strided(k_idx, bkeys, nullptr, U, (int)(q0 + n_q), dc.S, nb, bs,
-                                                         (int)(q0 / bs), s));
+    MSA_LAUNCH_NAMED("pool", s, msa::launch_pool_strided(k_idx, bkeys, nullptr, U, (int)(q0 + n_q), str.kv_rows,
+                                                         nb, bs, (int)(q0 / bs), s));
   } else {
-    MSA_LAUNCH_NAMED("pool", s, msa::launch_pool(k_idx, bkeys, U, S, bs, s));
+    MSA_LAUNCH_NAMED("pool", s, msa::launch_pool_strided(k_idx, bkeys, nullptr, U, S, str.kv_rows, nb, bs, 0, s));
   }
-  MSA_LAUNCH_NAMED("index_topk", s, msa::launch_index_topk_at(q_idx, bkeys, sel_use, U, S, iq0, (int)q_stride,
+  MSA_LAUNCH_NAMED("index_topk", s, msa::launch_index_topk_at(q_idx, bkeys, sel_use, U, S, iq0, (int)str.qi_rows,
                                                                sel_stride, nb, bs, K, s));
   MSA_LAUNCH_NAMED("chunk_hist", s, msa::launch_chunk_hist(sel_use, hist, U, S, nb, bs, K, cp, iq0, s));
   MSA_LAUNCH_NAMED("chunk_total", s, msa::launch_chunk_total(hist, counts, U, nb, cp, s));
@@ -390,8 +433,8 @@ int run_prefill(const Dims& dc, long q0, long n_q, long q_stride, const uint16_t
   sh.range_tokens = (int)P.T;
   sh.scale_log2 = d.scale * 1.4426950408889634f;
   sh.q0 = iq0;
-  sh.q_stride = (int)q_stride;
-  sh.kv_rows = (int)dc.S;
+  sh.q_stride = (int)str.q_rows;
+  sh.kv_rows = (int)str.kv_rows;
   sh.lse = lse;
   auto run_pass = [&](long u0, long u1) -> int {
     msa::PassInfo ps;
@@ -499,43 +542,51 @@ int check_backward_plans(const Dims& d, long T, const BackwardLayout& L) {
   return MSA_OK;
 }
 
-// Whole prefill (msa_prefill, msa_prefill_lse), arguments checked.
-int prefill_impl(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v, const int8_t* q_idx,
-                 const int8_t* k_idx, uint16_t* out, int32_t* sel, float* lse, void* ws, size_t ws_bytes,
-                 hipStream_t s) {
+// Plain causal GQA attention of every query of d (the dense kernel), and,
+// when sel is given, the selection that keeps every block up to the own one.
+int dense_impl(const Dims& d, const Strides& str, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+               uint16_t* out, int32_t* sel, float* lse, hipStream_t s) {
+  msa::PrefillShape sh{};
+  sh.B = (int)d.B;
+  sh.S = (int)d.S;
+  sh.Hq = (int)d.Hq;
+  sh.G = (int)d.G;
+  sh.r = (int)d.r;
+  sh.bs = (int)d.bs;
+  sh.bs_log2 = bs_log2_of(d.bs);
+  sh.nb = (int)d.nb;
+  sh.top_k = (int)d.k;
+  sh.q0 = 0;
+  sh.q_stride = (int)str.q_rows;
+  sh.kv_rows = (int)str.kv_rows;
+  sh.scale_log2 = d.scale * 1.4426950408889634f;
+  sh.lse = lse;
+  MSA_LAUNCH_NAMED("dense", s, msa::launch_dense(sh, q, k, v, out, sel, (int)str.sel_rows, s));
+  return MSA_OK;
+}
+
+// Whole prefill (msa_prefill, msa_prefill_lse, each sequence of
+// msa_prefill_varlen), arguments checked and every plan checked.
+int prefill_impl(const Dims& d, const Strides& str, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                 const int8_t* q_idx, const int8_t* k_idx, uint16_t* out, int32_t* sel, float* lse, void* ws,
+                 size_t ws_bytes, hipStream_t s) {
   if (d.nb > msa::kMaxInvertBlocks) return MSA_ERR_UNSUPPORTED;
   if (d.k >= d.nb) {
     // top_k covers every block: each query keeps all earlier blocks and its
     // own, which is plain causal attention (no index branch, no partials)
-    msa::PrefillShape sh{};
-    sh.B = (int)d.B;
-    sh.S = (int)d.S;
-    sh.Hq = (int)d.Hq;
-    sh.G = (int)d.G;
-    sh.r = (int)d.r;
-    sh.bs = (int)d.bs;
-    sh.bs_log2 = bs_log2_of(d.bs);
-    sh.nb = (int)d.nb;
-    sh.top_k = (int)d.k;
-    sh.q0 = 0;
-    sh.q_stride = (int)d.S;
-    sh.kv_rows = (int)d.S;
-    sh.scale_log2 = d.scale * 1.4426950408889634f;
-    sh.lse = lse;
-    MSA_LAUNCH_NAMED("dense", s, msa::launch_dense(sh, q, k, v, out, sel, s));
-    return MSA_OK;
+    return dense_impl(d, str, q, k, v, out, sel, lse, s);
   }
   const long T = prefill_query_chunk(d);
   // every chunk is planned and checked before anything is enqueued
   int st = check_prefill_plans(d, ws_bytes, nullptr);
   if (st != MSA_OK) return st;
-  if (T >= d.S) return run_prefill(d, 0, d.S, d.S, q, k, v, q_idx, k_idx, nullptr, out, sel, lse, ws, ws_bytes, s);
+  if (T >= d.S) return run_prefill(d, 0, d.S, str, q, k, v, q_idx, k_idx, nullptr, out, sel, lse, ws, ws_bytes, s);
   // query chunks of T tokens; the summaries persist in the workspace's first
   // region (block_keys, which every layout places at offset 0)
   int8_t* keys = static_cast<int8_t*>(ws);
   for (long q0 = 0; q0 < d.S; q0 += T) {
     const long n = std::min(T, d.S - q0);
-    const int st2 = run_prefill(d, q0, n, d.S, q + q0 * d.Hq * d.D, k, v, q_idx + q0 * d.di, k_idx, keys,
+    const int st2 = run_prefill(d, q0, n, str, q + q0 * d.Hq * d.D, k, v, q_idx + q0 * d.di, k_idx, keys,
                                 out + q0 * d.Hq * d.D, sel ? sel + q0 * d.k : nullptr,
                                 lse ? lse + q0 * d.Hq : nullptr, ws, ws_bytes, s);
     if (st2 != MSA_OK) return st2;
@@ -566,7 +617,7 @@ const char* msa_status_string(int status) {
   }
 }
 
-int msa_version(void) { return 10400; }
+int msa_version(void) { return 10500; }
 
 int msa_backward_pass_rows(const msa_dims* dims, size_t ws_bytes, int32_t* rows) {
   Dims d;
@@ -627,6 +678,18 @@ int msa_workspace_bytes(int op, const msa_dims* dims, size_t* min_bytes, size_t*
       hi = prefill_layout(dq, p, dq.U).total;
       break;
     }
+    case MSA_OP_PREFILL_VARLEN: {
+      // one sequence at a time, the longest (dims.seq_len) sizing the
+      // workspace; a shorter one plans within it
+      if (d.nb > msa::kMaxInvertBlocks) return MSA_ERR_UNSUPPORTED;
+      const Dims d1 = seq_dims(d, d.S);
+      if (d1.k >= d1.nb) break;
+      const Dims dq = chunk_dims(d1, std::min(d1.S, prefill_query_chunk(d1)));
+      const PrefillPlan p = plan_prefill(dq);
+      lo = prefill_layout(dq, p, 1).total;
+      hi = prefill_layout(dq, p, dq.U).total;
+      break;
+    }
     case MSA_OP_BACKWARD: {
       if (d.k > kMaxSparseTopK || d.nb > msa::kMaxInvertBlocks) return MSA_ERR_UNSUPPORTED;
       hi = backward_layout(d, d.S).total;
@@ -681,7 +744,78 @@ int msa_prefill(const msa_dims* dims, const uint16_t* q, const uint16_t* k, cons
   int st = check_dims(dims, &d);
   if (st != MSA_OK) return st;
   if (!q || !k || !v || !q_idx || !k_idx || !out) return MSA_ERR_INVALID_ARG;
-  return prefill_impl(d, q, k, v, q_idx, k_idx, out, sel, nullptr, ws, ws_bytes, (hipStream_t)stream);
+  return prefill_impl(d, dense_strides(d), q, k, v, q_idx, k_idx, out, sel, nullptr, ws, ws_bytes,
+                      (hipStream_t)stream);
+}
+
+int msa_prefill_varlen(const msa_dims* dims, const int32_t* cu_seqlens, const uint16_t* q, const uint16_t* k,
+                       const uint16_t* v, const int8_t* q_idx, const int8_t* k_idx, uint16_t* out, int32_t* sel,
+                       void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  int st = check_dims(dims, &d);
+  if (st != MSA_OK) return st;
+  if (!q || !k || !v || !q_idx || !k_idx || !out) return MSA_ERR_INVALID_ARG;
+  if (d.nb > msa::kMaxInvertBlocks) return MSA_ERR_UNSUPPORTED;
+  long T = 0;
+  st = check_cu_seqlens(d, cu_seqlens, &T);
+  if (st != MSA_OK) return st;
+  // every sequence's plan is checked before the first launch
+  bool sparse = false;
+  for (long b = 0; b < d.B; ++b) {
+    const long L = (long)cu_seqlens[b + 1] - cu_seqlens[b];
+    if (L == 0) continue;
+    const Dims ds = seq_dims(d, L);
+    if (ds.k >= ds.nb) continue;
+    sparse = true;
+    st = check_prefill_plans(ds, ws_bytes, nullptr);
+    if (st != MSA_OK) return st;
+  }
+  if (sparse && (ws == nullptr || ((uintptr_t)ws) % kAlign != 0)) return MSA_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  for (long b = 0; b < d.B; ++b) {
+    const long o = cu_seqlens[b], L = (long)cu_seqlens[b + 1] - o;
+    if (L == 0) continue;
+    const Dims ds = seq_dims(d, L);
+    st = prefill_impl(ds, Strides{L, T, T, T}, q + o * d.Hq * d.D, k + o * d.D, v + o * d.D, q_idx + o * d.di,
+                      k_idx + o * d.di, out + o * d.Hq * d.D, sel ? sel + o * d.k : nullptr, nullptr, ws, ws_bytes,
+                      s);
+    if (st != MSA_OK) return st;
+  }
+  return MSA_OK;
+}
+
+int msa_prefill_switched(const msa_dims* dims, int32_t dense_below, const uint16_t* q, const uint16_t* k,
+                         const uint16_t* v, const int8_t* q_idx, const int8_t* k_idx, uint16_t* out, int32_t* sel,
+                         void* ws, size_t ws_bytes, void* stream, int32_t* took_dense) {
+  if (dims == nullptr) return MSA_ERR_INVALID_ARG;
+  const long below = dense_below > 0 ? dense_below : kDefaultDenseBelow;
+  if (dims->seq_len >= below) {
+    Dims d;
+    int st = check_dims(dims, &d);
+    if (st != MSA_OK) return st;
+    if (!q || !k || !v || !q_idx || !k_idx || !out) return MSA_ERR_INVALID_ARG;
+    if (took_dense) *took_dense = 0;
+    return prefill_impl(d, dense_strides(d), q, k, v, q_idx, k_idx, out, sel, nullptr, ws, ws_bytes,
+                        (hipStream_t)stream);
+  }
+  // standard causal GQA attention: the index branch is skipped, so top_k
+  // plays no part beyond the layout of sel (checked as if it kept every
+  // block)
+  msa_dims dd = *dims;
+  if (dd.block_size > 0 && dd.seq_len > 0)
+    dd.top_k = std::max<int32_t>(dd.top_k, (int32_t)((dd.seq_len + (long)dd.block_size - 1) / dd.block_size));
+  Dims d;
+  int st = check_dims(&dd, &d);
+  if (st != MSA_OK) return st;
+  if (dims->top_k <= 0) return MSA_ERR_INVALID_ARG;
+  if (!q || !k || !v || !out) return MSA_ERR_INVALID_ARG;
+  if (took_dense) *took_dense = 1;
+  hipStream_t s = (hipStream_t)stream;
+  st = dense_impl(d, dense_strides(d), q, k, v, out, nullptr, nullptr, s);
+  if (st != MSA_OK) return st;
+  if (sel != nullptr)
+    MSA_LAUNCH_NAMED("fill", s, msa::launch_fill_i32(sel, -1, (size_t)d.B * d.G * d.S * dims->top_k, s));
+  return MSA_OK;
 }
 
 int msa_prefill_lse(const msa_dims* dims, const uint16_t* q, const uint16_t* k, const uint16_t* v,
@@ -691,7 +825,8 @@ int msa_prefill_lse(const msa_dims* dims, const uint16_t* q, const uint16_t* k, 
   int st = check_dims(dims, &d);
   if (st != MSA_OK) return st;
   if (!q || !k || !v || !q_idx || !k_idx || !out || !lse) return MSA_ERR_INVALID_ARG;
-  return prefill_impl(d, q, k, v, q_idx, k_idx, out, sel, lse, ws, ws_bytes, (hipStream_t)stream);
+  return prefill_impl(d, dense_strides(d), q, k, v, q_idx, k_idx, out, sel, lse, ws, ws_bytes,
+                      (hipStream_t)stream);
 }
 
 int msa_prefill_backward(const msa_dims* dims, const uint16_t* q, const uint16_t* k, const uint16_t* v,
@@ -809,8 +944,8 @@ int msa_prefill_chunk(const msa_dims* dims, int32_t start, int32_t count, const 
   if (!q || !q_idx || !k_cache || !v_cache || !k_idx || !block_keys || !out) return MSA_ERR_INVALID_ARG;
   if (start < 0 || count < 1 || (long)start + count > d.S) return MSA_ERR_INVALID_ARG;
   if (d.nb > msa::kMaxInvertBlocks) return MSA_ERR_UNSUPPORTED;
-  return run_prefill(d, start, count, count, q, k_cache, v_cache, q_idx, k_idx, block_keys, out, sel, nullptr, ws,
-                     ws_bytes, (hipStream_t)stream);
+  return run_prefill(d, start, count, Strides{count, d.S, count, count}, q, k_cache, v_cache, q_idx, k_idx,
+                     block_keys, out, sel, nullptr, ws, ws_bytes, (hipStream_t)stream);
 }
 
 int msa_decode(const msa_dims* dims, const uint16_t* q, const int8_t* q_idx, const uint16_t* k_cache,

@@ -106,10 +106,11 @@ hipError_t launch_attend(const PrefillShape& sh, const PassInfo& pass, const uin
                          const uint32_t* entries, uint16_t* part_o, float2* part_ml, int max_items, hipStream_t st);
 
 // Dense causal attention of every query row (for top_k >= nb, when the
-// selection keeps every block up to the own one) -> out, and that selection
-// -> sel when non-null.
+// selection keeps every block up to the own one, and for the short-sequence
+// switch) -> out, and that selection -> sel [U, sel_rows, top_k] when
+// non-null.
 hipError_t launch_dense(const PrefillShape& sh, const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                        uint16_t* out, int32_t* sel, hipStream_t st);
+                        uint16_t* out, int32_t* sel, int sel_rows, hipStream_t st);
 
 // Merge of every partial of the pass's query rows -> out.
 hipError_t launch_merge(const PrefillShape& sh, const PassInfo& pass, const uint16_t* part_o,

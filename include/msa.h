@@ -89,6 +89,7 @@ extern "C" {
 #define MSA_OP_PREFILL 2
 #define MSA_OP_DECODE 3
 #define MSA_OP_BACKWARD 4
+#define MSA_OP_PREFILL_VARLEN 5  /* msa_prefill_varlen: dims.seq_len = the longest sequence */
 
 typedef struct msa_dims {
   int32_t batch;        /* B */
@@ -159,6 +160,46 @@ int msa_index_select(const msa_dims* dims, const int8_t* q_idx, const int8_t* k_
 int msa_prefill(const msa_dims* dims, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                 const int8_t* q_idx, const int8_t* k_idx, uint16_t* out, int32_t* sel, void* ws,
                 size_t ws_bytes, void* stream);
+
+/* Ragged batch (varlen) prefill: dims->batch sequences of different lengths
+ * packed along the token axis, each an independent MSA prefill (its blocks
+ * start at its own first token; it sees only its own keys).  The pages use
+ * MSA for prompts of up to 1M tokens served side by side ("深度解析
+ * MiniMax-M3：稀疏注意力机制、基准测试与 API 集成指南", section "技术细节"), which
+ * real batches of uneven lengths need.
+ *
+ * cu_seqlens: HOST int32 [batch + 1], cu_seqlens[0] = 0, non-decreasing;
+ * sequence s holds tokens cu_seqlens[s] .. cu_seqlens[s + 1] - 1 of the packed
+ * tensors (a length of 0 is allowed and skipped), T = cu_seqlens[batch] >= 1.
+ * dims->seq_len: the longest sequence (no length may exceed it).
+ *   q, out       [T, Hq, D]     bf16
+ *   k, v         [G, T, D]      bf16
+ *   q_idx, k_idx [G, T, di]     int8
+ *   sel          [G, T, top_k]  int32, when non-NULL
+ * Row t of sequence s gets exactly what msa_prefill gives row t -
+ * cu_seqlens[s] of that sequence on its own.  The sequences run one after
+ * another on `stream`, sharing the workspace: ws/ws_bytes at least the
+ * minimum of msa_workspace_bytes(MSA_OP_PREFILL_VARLEN, dims) (the sizes of
+ * the longest sequence alone).  Every sequence's plan is checked before the
+ * first launch; G * T * top_k < 2^31. */
+int msa_prefill_varlen(const msa_dims* dims, const int32_t* cu_seqlens, const uint16_t* q, const uint16_t* k,
+                       const uint16_t* v, const int8_t* q_idx, const int8_t* k_idx, uint16_t* out, int32_t* sel,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* Prefill with the short-sequence switch one page describes: below a length
+ * the index branch's screening does not pay and standard attention is used
+ * instead (devpress.csdn.net article on MiniMax M3, section "M3的技术局限与改进
+ * 方向", first limitation).  With seq_len >= dense_below (<= 0 selects 8192,
+ * the page's figure) this is msa_prefill, same arguments and results.
+ * Below it the call computes STANDARD causal GQA attention -- every key at a
+ * position <= t, whatever top_k is -- which differs from MSA's result
+ * whenever top_k < nb: the index tensors are not read, sel (when non-NULL,
+ * [B, G, S, top_k]) is filled with -1 (no selection was made) and no
+ * workspace is used (ws may be NULL).  *took_dense (optional, host) is set
+ * to 1 when the standard route ran, else 0. */
+int msa_prefill_switched(const msa_dims* dims, int32_t dense_below, const uint16_t* q, const uint16_t* k,
+                         const uint16_t* v, const int8_t* q_idx, const int8_t* k_idx, uint16_t* out,
+                         int32_t* sel, void* ws, size_t ws_bytes, void* stream, int32_t* took_dense);
 
 /* Whole prefill for training: msa_prefill, plus lse [B, S, Hq] fp32 (required),
  * the natural log-sum-exp of each query row's scaled scores over the keys it

@@ -48,7 +48,7 @@ def test_status_strings(lib):
                          (-3, "MSA_ERR_WORKSPACE"), (-4, "MSA_ERR_HIP"), (-5, "MSA_ERR_SCRATCH")]:
         assert lib.msa_status_string(code).decode().startswith(prefix)
     assert lib.msa_status_string(12345).decode() == "unknown MSA status"
-    assert lib.msa_version() == 10400
+    assert lib.msa_version() == 10500
 
 
 def D(**kw):
@@ -384,3 +384,51 @@ def test_plan_check_arguments(lib):
     assert _plan_check(lib, 99, D(), 1 << 30)[0] == -1
     assert _plan_check(lib, _lib.MSA_OP_PREFILL, D(head_dim=64), 1 << 30)[0] == -2
     assert _plan_check(lib, _lib.MSA_OP_BACKWARD, D(), 0)[0] == -3
+
+
+def _cu(*xs):
+    return (ctypes.c_int32 * len(xs))(*xs)
+
+
+def test_prefill_varlen_validation(lib):
+    """Ragged-batch prefill: the host offsets are checked (start at 0,
+    non-decreasing, no sequence longer than dims.seq_len, at least one token)
+    and every sequence's plan is checked against the workspace before any
+    launch; its workspace is the longest sequence's alone."""
+    dims = D(batch=3, seq_len=5000, n_q_heads=8, n_kv_heads=2)
+    args = [FAKE] * 7  # q, k, v, q_idx, k_idx, out, sel
+    good = _cu(0, 100, 5100, 6000)
+    for bad in (None, _cu(1, 100, 5100, 6000), _cu(0, 100, 50, 6000), _cu(0, 100, 5101, 6000), _cu(0, 0, 0, 0)):
+        assert lib.msa_prefill_varlen(ctypes.byref(dims), bad, *args, FAKE, 1 << 40, None) == -1
+    for i in range(6):
+        a = list(args)
+        a[i] = None
+        assert lib.msa_prefill_varlen(ctypes.byref(dims), good, *a, FAKE, 1 << 40, None) == -1
+    st, lo, hi = _ws(lib, _lib.MSA_OP_PREFILL_VARLEN, dims)
+    one = D(batch=1, seq_len=5000, n_q_heads=8, n_kv_heads=2)
+    assert st == 0 and (lo, hi) == _ws(lib, _lib.MSA_OP_PREFILL, one)[1:]
+    assert lo > 0
+    # below the longest sequence's minimum: refused before anything is enqueued
+    assert lib.msa_prefill_varlen(ctypes.byref(dims), good, *args, FAKE, lo - 256, None) == -3
+    assert lib.msa_prefill_varlen(ctypes.byref(dims), good, *args, None, 1 << 40, None) == -3
+
+
+def test_prefill_switched_validation(lib):
+    """The short-sequence switch: null pointers and unsupported shapes are
+    refused before any launch on both routes; at or above the threshold the
+    call is msa_prefill (top_k 33 < nb is unsupported there), below it any
+    top_k >= 1 is accepted (standard attention does not use it)."""
+    took = ctypes.c_int32(-7)
+    assert lib.msa_prefill_switched(None, 0, *([FAKE] * 7), FAKE, 1 << 40, None, ctypes.byref(took)) == -1
+    long_ = D(seq_len=20000, top_k=33)
+    assert lib.msa_prefill_switched(ctypes.byref(long_), 0, *([FAKE] * 7), FAKE, 1 << 40, None,
+                                    ctypes.byref(took)) == -2
+    short = D(seq_len=4000, top_k=0)
+    assert lib.msa_prefill_switched(ctypes.byref(short), 0, *([FAKE] * 7), FAKE, 1 << 40, None,
+                                    ctypes.byref(took)) == -1
+    short = D(seq_len=4000, top_k=16)
+    a = [FAKE] * 7
+    a[0] = None
+    assert lib.msa_prefill_switched(ctypes.byref(short), 0, *a, None, 0, None, ctypes.byref(took)) == -1
+    assert lib.msa_prefill_switched(ctypes.byref(D(seq_len=4000, head_dim=64)), 0, *([FAKE] * 7), None, 0, None,
+                                    ctypes.byref(took)) == -2

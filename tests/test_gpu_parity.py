@@ -512,3 +512,79 @@ def test_decode_matches_last_prefill_row():
     assert torch.equal(dsel, sel[:, :, S - 1])
     d = (dout.float() - out[:, S - 1].float()).abs()
     assert float(d.max()) <= 1e-2
+
+
+# ------------------------------------------------------------------ ragged batch and the short-sequence switch
+
+VARLEN = [
+    # name, workload overrides, sequence lengths (one longer than a 16384-token query chunk, a 1-token
+    # sequence, an empty one, lengths that are not multiples of the block size)
+    ("mixed_bs64_k6", dict(n_q_heads=8, n_kv_heads=2, block_size=64, top_k=6), [1, 300, 20000, 129, 4096, 0, 64]),
+    ("bs128_r8_k16", dict(n_q_heads=16, n_kv_heads=2, block_size=128, top_k=16), [3000, 777, 5000, 1]),
+]
+
+
+@pytest.mark.parametrize("name,over,lens", VARLEN, ids=[c[0] for c in VARLEN])
+def test_prefill_varlen_all_rows(name, over, lens):
+    """msa_prefill_varlen over sequences packed along the token axis: every
+    row of every sequence against the oracle of that sequence alone, and bit
+    for bit the rows msa_prefill gives each sequence on its own."""
+    w = get_workload("tiny_2k", **over)
+    _say(f"[prefill varlen] {name} lengths={lens}")
+    seqs = [prefill_inputs(w, seed=300 + i, device=DEV, seq_len=L) if L > 0 else None for i, L in enumerate(lens)]
+    cu = [0]
+    for L in lens:
+        cu.append(cu[-1] + L)
+    live = [s for s in seqs if s is not None]
+    q = torch.cat([s["q"][0] for s in live], dim=0).contiguous()
+    k = torch.cat([s["k"][0] for s in live], dim=1).contiguous()
+    v = torch.cat([s["v"][0] for s in live], dim=1).contiguous()
+    qi = torch.cat([s["q_idx"][0] for s in live], dim=1).contiguous()
+    ki = torch.cat([s["k_idx"][0] for s in live], dim=1).contiguous()
+    out, sel = msa.msa_prefill_varlen(q, k, v, qi, ki, cu, w.block_size, w.top_k, return_sel=True)
+    torch.cuda.synchronize()
+    for i, s in enumerate(seqs):
+        if s is None:
+            continue
+        a, b = cu[i], cu[i + 1]
+        o1, s1 = _run_prefill(s, w.block_size, w.top_k)
+        assert torch.equal(out[a:b], o1[0]), f"{name}: sequence {i} output differs from its own msa_prefill"
+        assert torch.equal(sel[:, a:b], s1[0]), f"{name}: sequence {i} selection differs from its own msa_prefill"
+        rows = np.arange(b - a)
+        _, osel, oout, st = oracle_prefill_rows_pooled(s, w, rows)
+        assert np.array_equal(host_i8(sel[:, a:b]).astype(np.int32)[None], osel), f"{name}: sequence {i} selection"
+        compare_rounded(out[a:b][None], oout, f"varlen {name} seq {i} (L={b - a})")
+    del seqs, live, q, k, v, qi, ki, out, sel
+    _free()
+
+
+def test_prefill_switched_short_is_standard_attention():
+    """Below the threshold msa_prefill_switched computes standard causal GQA
+    attention (every earlier key, whatever top_k), which the oracle gives with
+    a selection that keeps every block; sel is all -1.  At or above it, the
+    call is msa_prefill, bit for bit."""
+    w = get_workload("tiny_2k", n_q_heads=16, n_kv_heads=2, block_size=64, top_k=4)
+    S = 3000  # 47 blocks: top_k 4 would select; the switch does not
+    _say(f"[prefill switched] S={S} {w}")
+    inp = prefill_inputs(w, seed=55, device=DEV, seq_len=S)
+    sel = torch.zeros((1, w.n_kv_heads, S, w.top_k), dtype=torch.int32, device=DEV)
+    out, dense = msa.msa_prefill_switched(inp["q"], inp["k"], inp["v"], inp["q_idx"], inp["k_idx"], w.block_size,
+                                          w.top_k, sel=sel)
+    torch.cuda.synchronize()
+    assert dense
+    assert bool((sel == -1).all())
+    nb = -(-S // w.block_size)
+    rows = np.arange(S)
+    _, osel, oout, st = oracle_prefill_rows_pooled(inp, w, rows, top_k=nb)
+    compare_rounded(out, oout, "switched: standard attention, 3000 tokens")
+    # the same data through MSA differs: top_k 4 keeps 4 of up to 47 blocks
+    msa_out, _ = _run_prefill(inp, w.block_size, w.top_k)
+    assert float((msa_out.float() - out.float()).abs().max()) > 0.05
+    # at or above the threshold: msa_prefill exactly
+    out2, dense2 = msa.msa_prefill_switched(inp["q"], inp["k"], inp["v"], inp["q_idx"], inp["k_idx"], w.block_size,
+                                            w.top_k, dense_below=2000)
+    torch.cuda.synchronize()
+    assert not dense2
+    assert torch.equal(out2, msa_out)
+    del inp, out, out2, msa_out, sel
+    _free()
