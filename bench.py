@@ -499,6 +499,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--core-only", action="store_true",
                     help="time the step only (no other workloads, extras or CPU baseline), e.g. under a profiler")
+    ap.add_argument("--prefill-workload", default=HEADLINE,
+                    help="prefill workload of the step (default: the 1M prefill); another one is for profiler runs "
+                         "with --core-only")
     ap.add_argument("--train-only", action="store_true",
                     help="time only the training forward (with log-sum-exp) and backward of the 32K prefill")
     ap.add_argument("--pmc-run", action="store_true",
@@ -528,7 +531,8 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    wp = get_workload(HEADLINE)
+    headline = args.prefill_workload
+    wp = get_workload(headline)
     wd = get_workload(DECODE)
     _say("generating inputs")
     pin = prefill_inputs(wp, seed=0, device=dev)
@@ -606,7 +610,7 @@ def main():
     mrg_ms_step = mrg_ms / args.steps
     mrg_design_bytes = (pairs - (tokens * wp.n_q_heads - rows_merged)) * (2 * D + 8) + rows_merged * 2 * D
     dbytes = _decode_bytes(wd)
-    traffic = _measured_traffic()
+    traffic = _measured_traffic() if headline == HEADLINE else None
 
     rec = {
         "metric": "MSA prefill tokens/s + TFLOP/s (% bf16 MFMA peak); decode tokens/s, HBM GB/s",
@@ -621,12 +625,12 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{HEADLINE} + {DECODE}", "batch": wp.batch, "seq_len": wp.seq_len,
+        "config": {"workload": f"{headline} + {DECODE}", "batch": wp.batch, "seq_len": wp.seq_len,
                    "n_q_heads": wp.n_q_heads, "n_kv_heads": wp.n_kv_heads, "head_dim": D,
                    "block_size": wp.block_size, "top_k": wp.top_k, "decode_batch": wd.batch,
                    "decode_cache_len": wd.seq_len, "parallelism": "none (1 GPU)"},
         "prefill": {
-            "workload": HEADLINE,
+            "workload": headline,
             "ms": round(pre_med, 4),
             "tokens_per_s": round(tokens / (pre_med * 1e-3), 1),
             "tflops_alg": round(flop_alg / (pre_med * 1e-3) / 1e12, 2),
@@ -644,7 +648,7 @@ def main():
         },
         "roofline": {
             "kernel": "attend_kernel<128> (KV-outer block attention, all kept blocks of one query chunk)",
-            "workload": HEADLINE,
+            "workload": headline,
             "bound": "mfma",
             "achieved": round(att_tflops, 2) if att_tflops else None,
             "peak": PEAK_BF16_TFLOPS,
@@ -673,7 +677,9 @@ def main():
         "kernels": {k: {"launches": n, "avg_ms": round(ms / max(1, n), 4)}
                     for k, (n, ms) in sorted(list(kt.items()) + list(dkt.items()))},
     }
-    cpu = not (args.no_cpu_baseline or args.core_only)
+    cpu = not (args.no_cpu_baseline or args.core_only) and headline == HEADLINE
+    if headline != HEADLINE and not args.core_only:
+        raise SystemExit("--prefill-workload other than the 1M prefill is for --core-only profiler runs")
     baselines = {}
     if cpu:
         _say(f"cpu baseline: {HEADLINE} ({CPU_SAMPLE_ROWS} rows), {DECODE}")
