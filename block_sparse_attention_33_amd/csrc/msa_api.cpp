@@ -724,7 +724,7 @@ int msa_pool_block_keys(const msa_dims* dims, const int8_t* k_idx, int8_t* block
 
 int msa_index_select(const msa_dims* dims, const int8_t* q_idx, const int8_t* k_idx, int8_t* block_keys,
                      int32_t* sel, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
+  (void)ws;  // reserved (msa.h): the index branch needs no workspace
   (void)ws_bytes;
   Dims d;
   int st = check_dims(dims, &d);

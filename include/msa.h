@@ -144,8 +144,10 @@ int msa_pool_block_keys(const msa_dims* dims, const int8_t* k_idx, int8_t* block
 /* Index branch: pooling, scores and per-(query, group) top-k.
  * q_idx, k_idx [B, G, S, di] int8 -> block_keys [B, G, nb, di] int8 and
  * sel [B, G, S, top_k] int32 (both outputs required).
- * ws/ws_bytes: workspace of at least msa_workspace_bytes(MSA_OP_INDEX) bytes
- * (may be NULL/0 when that is 0). */
+ * ws/ws_bytes: reserved.  The call uses no workspace
+ * (msa_workspace_bytes(MSA_OP_INDEX) reports 0); pass NULL/0.  The
+ * arguments stay so that a future version may take scratch without an ABI
+ * change; they are not read now. */
 int msa_index_select(const msa_dims* dims, const int8_t* q_idx, const int8_t* k_idx,
                      int8_t* block_keys, int32_t* sel, void* ws, size_t ws_bytes, void* stream);
 
