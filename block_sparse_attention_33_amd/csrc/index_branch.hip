@@ -262,6 +262,10 @@ __global__ __launch_bounds__(256) void index_topk_kernel(const int8_t* __restric
 // in arrival order, before a tile could overflow one and at the end.  A
 // stale (lower) threshold lets more candidates through, never fewer, and
 // the arrival order keeps the tie rule, so the lists are the same.
+//
+// This single-sweep kernel serves what the two-sweep kernel below cannot:
+// queries ranking more than 65536 blocks, and (flagged_only) the waves it
+// flags for a score spread its keys cannot hold.
 // ---------------------------------------------------------------------------
 constexpr int kTopkBufMfma = 24;    // buffered candidates per lane (a tile adds at most 16)
 constexpr int kSumStride = 64 + 8;  // bytes per staged summary (18 dwords: the 8-byte A reads of 16 rows hit 32 banks)
@@ -291,7 +295,19 @@ __global__ __launch_bounds__(256) void index_topk_mfma_kernel(const int8_t* __re
                                                          const int8_t* __restrict__ block_keys,
                                                          int32_t* __restrict__ sel, int S,
                                                          int nb_stride, int bs_log2, int top_k, int pos0,
-                                                         int q_stride, int sel_stride) {
+                                                         int q_stride, int sel_stride, int flagged_only) {
+  // flagged_only: run only where the two-sweep kernel left a wave's rows
+  // flagged (first entry -2), i.e. for workgroups holding such a wave
+  if (flagged_only) {
+    bool any = false;
+#pragma unroll
+    for (int w4 = 0; w4 < 4; ++w4) {
+      const int tw = blockIdx.x * 128 + 32 * w4;
+      if (tw < S) any |= sel[((size_t)blockIdx.y * sel_stride + tw) * top_k] == -2;
+    }
+    __syncthreads();   // every flag is read before any row is rewritten
+    if (!any) return;  // the same for every thread of the workgroup
+  }
   // 128 summaries per LDS chunk and 4-byte buffer entries: 33 KiB of LDS,
   // so four workgroups share a CU (the kernel waits on its MFMA results,
   // LDS reads and wave-wide tests far more than it issues; measured on
@@ -423,6 +439,301 @@ __global__ __launch_bounds__(256) void index_topk_mfma_kernel(const int8_t* __re
   }
 }
 
+// ---------------------------------------------------------------------------
+// Scores + top-k in two sweeps over the candidates.  Layout as above: a
+// workgroup takes 128 consecutive query tokens of one (batch, group) unit, a
+// wave 32 of them, and one tile of 32 candidates x 32 queries comes from two
+// exact integer contractions (v_mfma_i32_32x32x32_i8, 32 index dims each),
+// lane (hf, col) holding query col's scores of candidates
+// 8 (i / 4) + 4 hf + i % 4 of the tile.
+//
+// Sweep 1 keeps, per lane, the maximum of each of its 16 register slots over
+// all tiles: 32 maxima per query over disjoint candidate sets.  Their top_k -
+// 1'th largest, L, is a lower bound on the query's (top_k - 1)'th best score
+// (that many distinct candidates reach it), so no candidate scoring below L
+// can be selected.  Sweep 2 scores the candidates again and buffers, per
+// lane in LDS, the scores of each group of four consecutive candidates
+// (slots 4 g .. 4 g + 3) whose maximum reaches the filter bound; few do, so
+// the per-candidate work happens for few.  The buffered candidates go into a
+// per-lane list of the best KCAP, ranked by the unsigned key
+// ((s - L + 1) << 16) | (65535 - j), which orders by score, then by lower
+// block, and makes an insertion one median per list slot.  The two half
+// lists of a query are joined at the end.  After each drain of the buffer
+// the bound rises to one above the list's last score when the list is full:
+// later candidates have higher block indices and cannot displace an entry
+// they only tie.
+//
+// A query with fewer than top_k - 1 candidates keeps them all (key score
+// part 1).  A wave where some query's best score is 65535 or more above its
+// L cannot use the keys: it writes -2 into the first entry of its rows and
+// index_topk_mfma_kernel, launched after this one with flagged_only set,
+// recomputes the workgroups that hold such a wave.  The host sends queries
+// that rank more than 65536 blocks to index_topk_mfma_kernel directly.
+// ---------------------------------------------------------------------------
+constexpr int kSumStride32 = 80;  // bytes per staged summary (20 dwords: the 16-byte A reads of 16 rows hit distinct banks)
+constexpr int kEntCap = 6;        // buffered candidate groups per lane (LDS: 40 KiB per workgroup, four per CU)
+
+__device__ __forceinline__ uint32_t umed3(uint32_t a, uint32_t b, uint32_t c) {
+  return max(min(a, b), min(max(a, b), c));
+}
+
+// Insertion of a key into a list of distinct keys sorted descending
+// (unsigned): slot i becomes the median of itself, the slot before and the
+// key, i.e. max(slot, min(slot before, key)).
+template <int KCAP>
+__device__ __forceinline__ void key_insert(int (&K)[KCAP], uint32_t x) {
+#pragma unroll
+  for (int i = KCAP - 1; i > 0; --i) K[i] = (int)umed3((uint32_t)K[i], (uint32_t)K[i - 1], x);
+  K[0] = (int)max((uint32_t)K[0], x);
+}
+
+// Ascending sort of a bitonic sequence of N (a power of two) values.
+template <int N>
+__device__ __forceinline__ void bitonic_merge(int (&x)[N]) {
+#pragma unroll
+  for (int j = N >> 1; j > 0; j >>= 1) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int l = i ^ j;
+      if (l > i) {
+        const int a = x[i], b = x[l];
+        x[i] = min(a, b);
+        x[l] = max(a, b);
+      }
+    }
+  }
+}
+
+template <int KCAP>
+__global__ __launch_bounds__(256) void index_topk_bound_kernel(const int8_t* __restrict__ q_idx,
+                                                               const int8_t* __restrict__ block_keys,
+                                                               int32_t* __restrict__ sel, int S, int nb_stride,
+                                                               int bs_log2, int top_k, int pos0, int q_stride,
+                                                               int sel_stride) {
+  constexpr int CH = 128;  // summaries per LDS chunk
+  __shared__ __align__(16) char sk[CH * kSumStride32];
+  __shared__ i32x4_t ent[kEntCap][256];  // the four scores of a buffered group
+  __shared__ int entj[kEntCap][256];     // its first block
+
+  const int u = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int hf = lane >> 5;
+  const int col = lane & 31;
+  const int t0 = blockIdx.x * 128;
+  const int t = t0 + 32 * w + col;  // this lane's query (in both lane halves)
+  const bool live = t < S;
+  const int tc = live ? t : S - 1;
+  const int c = (pos0 + tc) >> bs_log2;                           // own block = number of candidates
+  const int c_lo = (pos0 + min(S - 1, t0 + 32 * w)) >> bs_log2;   // the wave's smallest own block
+  const int c_last = (pos0 + min(S - 1, t0 + 127)) >> bs_log2;    // the workgroup's largest
+  const int kp = top_k - 1;
+
+  // B operand: the query's index bytes 32 ks + 16 hf .. + 15 at k-step ks
+  const int8_t* qrow = q_idx + ((size_t)u * q_stride + tc) * kIdxDim;
+  const i32x4_t qb0 = *reinterpret_cast<const i32x4_t*>(qrow + 16 * hf);
+  const i32x4_t qb1 = *reinterpret_cast<const i32x4_t*>(qrow + 32 + 16 * hf);
+
+  const i32x4_t* kb = reinterpret_cast<const i32x4_t*>(block_keys + (size_t)u * nb_stride * kIdxDim);
+  const int n_cand = kp > 0 ? c_last : 0;
+  // the next chunk's summaries (16 bytes x 2 per thread) load while the
+  // current chunk is scored
+  i32x4_t pre[CH * 4 / 256];
+  auto fetch = [&](int from) {
+    const int n = min(CH, n_cand - from);
+#pragma unroll
+    for (int m = 0; m < CH * 4 / 256; ++m) {
+      const int i = tid + 256 * m;
+      pre[m] = i < n * 4 ? kb[(size_t)from * 4 + i] : i32x4_t{};
+    }
+  };
+  // one sweep: body(j0, acc) for every tile, acc[i] = the score of candidate
+  // j0 + c_row(i, hf), INT_MIN where that is not before the query's block
+  // (rows past a chunk's end hold stale summaries; they are all masked)
+  auto sweep = [&](auto&& body) {
+    if (n_cand > 0) fetch(0);
+    for (int base = 0; base < n_cand; base += CH) {
+      const int n = min(CH, n_cand - base);
+      __syncthreads();
+#pragma unroll
+      for (int m = 0; m < CH * 4 / 256; ++m) {
+        const int i = tid + 256 * m;
+        *reinterpret_cast<i32x4_t*>(sk + (i >> 2) * kSumStride32 + 16 * (i & 3)) = pre[m];
+      }
+      __syncthreads();
+      if (base + CH < n_cand) fetch(base + CH);
+      // tiles in pairs, so that one tile's contractions run while the other
+      // tile's scores are used (a pair past n holds only masked rows)
+      for (int tile = 0; tile < n; tile += 64) {
+        i32x16_t acc[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const char* arow = sk + (tile + 32 * h + col) * kSumStride32 + 16 * hf;
+          acc[h] = __builtin_amdgcn_mfma_i32_32x32x32_i8(*reinterpret_cast<const i32x4_t*>(arow), qb0, i32x16_t{},
+                                                         0, 0, 0);
+          acc[h] = __builtin_amdgcn_mfma_i32_32x32x32_i8(*reinterpret_cast<const i32x4_t*>(arow + 32), qb1, acc[h],
+                                                         0, 0, 0);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int j0 = base + tile + 32 * h;
+          if (j0 + 32 > c_lo) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              if (j0 + c_row(i, hf) >= c) acc[h][i] = INT_MIN;
+          }
+          body(j0, acc[h]);
+        }
+      }
+    }
+  };
+
+  // sweep 1: slot maxima, then L = the kp'th largest of the query's 32
+  int bm[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) bm[i] = INT_MIN;
+  sweep([&](int, const i32x16_t& acc) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) bm[i] = max(bm[i], acc[i]);
+  });
+  bitonic_sort<16>(bm);
+  int m32[32];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    m32[i] = bm[i];
+    m32[16 + i] = __shfl_xor(bm[15 - i], 32);  // the other half's, descending: a bitonic sequence
+  }
+  bitonic_merge<32>(m32);
+  int L = INT_MIN;
+#pragma unroll
+  for (int i = 1; i < 32; ++i)
+    if (i == 32 - kp) L = m32[i];
+  const int U = m32[31];
+  // fewer than kp candidates (L undefined): all are kept, key score part 1
+  const bool all_in = L == INT_MIN;
+  const bool narrow = __all(all_in || U - L < 65535);
+
+  // sweep 2: groups reaching the bound are buffered, the buffer drained into
+  // the list before a tile would overflow it and at the end.  A wave whose
+  // scores do not fit the keys still sweeps (the workgroup's barriers need
+  // it) but buffers nothing, and flags its rows for the single-sweep kernel.
+  int K[KCAP];  // keys, descending (unsigned)
+#pragma unroll
+  for (int i = 0; i < KCAP; ++i) K[i] = 0;
+  int lf = !narrow ? INT_MAX : all_in ? INT_MIN : L;  // filter bound
+  int nbuf = 0;
+  auto drain = [&]() {
+    // no branch per lane: entries past a lane's count give key 0, which
+    // inserts nothing
+    for (int e = 0; __any(e < nbuf); ++e) {
+      const i32x4_t s4 = ent[e][tid];
+      const int jb = entj[e][tid];
+      uint32_t kq[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = jb + r;
+        const int sc = s4[r];
+        const bool ok = (e < nbuf) & (j < c) & (all_in | (sc >= L));
+        kq[r] = ok ? ((uint32_t)(all_in ? 1 : sc - L + 1) << 16) | (uint32_t)(65535 - j) : 0u;
+      }
+      // the group's keys, descending; a group rarely holds more than one
+      // candidate of note, so the later insertions are skipped unless some
+      // lane has one
+      auto cx = [&](int a, int b) {
+        const uint32_t x = kq[a], y = kq[b];
+        kq[a] = max(x, y);
+        kq[b] = min(x, y);
+      };
+      cx(0, 1);
+      cx(2, 3);
+      cx(0, 2);
+      cx(1, 3);
+      cx(1, 2);
+      key_insert<KCAP>(K, kq[0]);
+      if (__any(kq[1] != 0)) {
+        key_insert<KCAP>(K, kq[1]);
+        if (__any(kq[2] != 0)) {
+          key_insert<KCAP>(K, kq[2]);
+          if (__any(kq[3] != 0)) key_insert<KCAP>(K, kq[3]);
+        }
+      }
+    }
+    nbuf = 0;
+    // a full list: later candidates (higher blocks) must beat its last score
+    const uint32_t kl = (uint32_t)K[KCAP - 1];
+    if (kl != 0 && !all_in) lf = max(lf, (int)(kl >> 16) + L);
+  };
+  sweep([&](int j0, const i32x16_t& acc) {
+    int gm[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) gm[g] = max(max(acc[4 * g], acc[4 * g + 1]), max(acc[4 * g + 2], acc[4 * g + 3]));
+    const int npass = (gm[0] >= lf) + (gm[1] >= lf) + (gm[2] >= lf) + (gm[3] >= lf);
+    if (__any(nbuf + npass > kEntCap)) drain();
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      if (gm[g] >= lf) {
+        ent[nbuf][tid] = i32x4_t{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+        entj[nbuf][tid] = j0 + 8 * g + 4 * hf;
+        ++nbuf;
+      }
+    }
+  });
+  drain();
+  if (!narrow) {
+    if (live && hf == 0) sel[((size_t)u * sel_stride + t) * top_k] = -2;
+    return;
+  }
+
+  // the other half's list (lane + 32) joins this lane's: both, extended by
+  // one empty key (KCAP + 1 is a power of two), are descending, so the
+  // slot-wise maxima of one against the other reversed are the best KCAP + 1
+  // of the union as a V-shaped sequence, which a bitonic merge sorts
+  constexpr int N = KCAP + 1;
+  static_assert((N & (N - 1)) == 0, "list length + 1 must be a power of two");
+  uint32_t T[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int oi = N - 1 - i;
+    const uint32_t mine = i < KCAP ? (uint32_t)K[i < KCAP ? i : 0] : 0u;
+    const uint32_t other = (uint32_t)__shfl_xor(oi < KCAP ? K[oi < KCAP ? oi : 0] : 0, 32);
+    T[i] = max(mine, other);
+  }
+#pragma unroll
+  for (int j = N >> 1; j > 0; j >>= 1) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int l = i ^ j;
+      if (l > i) {
+        const uint32_t a = T[i], b = T[l];
+        T[i] = max(a, b);
+        T[l] = min(a, b);
+      }
+    }
+  }
+  int Li[KCAP];  // the selected blocks, best first (-1: none)
+#pragma unroll
+  for (int i = 0; i < KCAP; ++i) Li[i] = T[i] != 0 ? 65535 - (int)(T[i] & 65535u) : -1;
+  if (hf != 0) return;
+
+  // best min(top_k - 1, c) candidates, ascending, then the own block
+  const int n_valid = min(kp, c);
+  constexpr int NP = NextPow2<KCAP>::v;
+  int x[NP];
+#pragma unroll
+  for (int i = 0; i < NP; ++i) x[i] = (i < KCAP && i < n_valid) ? Li[i < KCAP ? i : 0] : INT_MAX;
+  bitonic_sort<NP>(x);
+  if (!live) return;
+  int32_t* out = sel + ((size_t)u * sel_stride + t) * top_k;
+#pragma unroll
+  for (int i = 0; i <= KCAP; ++i) {
+    if (i < top_k) {
+      const int xv = (i < NP) ? x[i < NP ? i : 0] : INT_MAX;
+      out[i] = (i < n_valid) ? xv : (i == n_valid ? c : -1);
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* __restrict__ p, int32_t value, size_t n) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (i < n) p[i] = value;
@@ -459,26 +770,35 @@ hipError_t launch_index_topk_at(const int8_t* q_idx, const int8_t* block_keys, i
   while ((1 << bs_log2) < bs) ++bs_log2;
   const int kp = top_k - 1;
   // the matrix-core scores pay once the queries rank many blocks (measured
-  // on MI355X: 14 % faster at 1024 blocks, 27 % at 8192, 12 % slower at 256)
-  const bool mfma = ((q0 + S - 1) >> bs_log2) >= kIndexMfmaMinBlocks;
+  // on MI355X: 14 % faster at 1024 blocks, 27 % at 8192, 12 % slower at 256);
+  // the two-sweep kernel's keys hold block indices below 65536
+  const int n_blocks = (q0 + S - 1) >> bs_log2;
+  const bool mfma = n_blocks >= kIndexMfmaMinBlocks;
+  const bool two_sweep = mfma && n_blocks <= 65536;
   const dim3 grid(mfma ? (S + 127) / 128 : (S + 255) / 256, units);
 #define MSA_TOPK_LAUNCH(KC)                                                                                        \
-  if (mfma)                                                                                                        \
-    hipLaunchKernelGGL(index_topk_mfma_kernel<KC>, grid, dim3(256), 0, st, q_idx, block_keys, sel, S, nb_stride,   \
+  if (two_sweep) {                                                                                                 \
+    hipLaunchKernelGGL(index_topk_bound_kernel<KC>, grid, dim3(256), 0, st, q_idx, block_keys, sel, S, nb_stride,  \
                        bs_log2, top_k, q0, q_stride, sel_stride);                                                  \
-  else                                                                                                             \
+    hipLaunchKernelGGL(index_topk_mfma_kernel<KC>, grid, dim3(256), 0, st, q_idx, block_keys, sel, S, nb_stride,   \
+                       bs_log2, top_k, q0, q_stride, sel_stride, 1);                                               \
+  } else if (mfma) {                                                                                               \
+    hipLaunchKernelGGL(index_topk_mfma_kernel<KC>, grid, dim3(256), 0, st, q_idx, block_keys, sel, S, nb_stride,   \
+                       bs_log2, top_k, q0, q_stride, sel_stride, 0);                                               \
+  } else {                                                                                                         \
     hipLaunchKernelGGL(index_topk_kernel<KC>, grid, dim3(256), 0, st, q_idx, block_keys, sel, S, nb_stride,        \
-                       bs_log2, top_k, q0, q_stride, sel_stride)
+                       bs_log2, top_k, q0, q_stride, sel_stride);                                                  \
+  }
   if (kp <= 1)
-    MSA_TOPK_LAUNCH(1);
+    MSA_TOPK_LAUNCH(1)
   else if (kp <= 3)
-    MSA_TOPK_LAUNCH(3);
+    MSA_TOPK_LAUNCH(3)
   else if (kp <= 7)
-    MSA_TOPK_LAUNCH(7);
+    MSA_TOPK_LAUNCH(7)
   else if (kp <= 15)
-    MSA_TOPK_LAUNCH(15);
+    MSA_TOPK_LAUNCH(15)
   else
-    MSA_TOPK_LAUNCH(31);
+    MSA_TOPK_LAUNCH(31)
 #undef MSA_TOPK_LAUNCH
   return hipGetLastError();
 }

@@ -245,6 +245,41 @@ def test_index_select_many_blocks_all_rows(S, top_k, B):
         check_all_selections(gsel[b:b + 1], qi[b:b + 1], summ[b:b + 1], S, w.block_size, w.top_k)
 
 
+def test_index_select_wide_scores_all_rows():
+    """Scores spread over more than 16 bits: a few planted blocks whose
+    summaries align with the group's query direction score about 2^18
+    while the rest stay near zero.  Queries before the first planted block
+    keep the narrow rank keys; the later ones take the single-sweep path.
+    Every selection is checked, sampled rows against the oracle."""
+    S, bs, G, top_k, di = 24000, 32, 2, 16, 64
+    rng = np.random.default_rng(2024)
+    u = rng.integers(-64, 64, size=(G, di))
+    qi = np.clip(u[:, None, :] + rng.integers(-16, 16, size=(G, S, di)), -128, 127).astype(np.int8)
+    ki = rng.integers(-64, 64, size=(G, S, di)).astype(np.int8)
+    hot = list(range(400, S // bs, 37))
+    for g in range(G):
+        for j in hot:
+            noise = rng.integers(-4, 4, size=(bs, di))
+            ki[g, j * bs:(j + 1) * bs] = np.clip(np.sign(u[g]) * 127 + noise, -128, 127)
+    _say(f"[index wide scores] S={S} bs={bs} hot blocks={len(hot)}")
+    q_idx = torch.from_numpy(qi[None]).to(DEV)
+    k_idx = torch.from_numpy(ki[None]).to(DEV)
+    bk, sel = msa.msa_index_select(q_idx, k_idx, bs, top_k)
+    torch.cuda.synchronize()
+    summ = O.pool_block_keys(ki[None], bs)
+    assert np.array_equal(host_i8(bk), summ)
+    gsel = host_i8(sel).astype(np.int64)
+    assert gsel.min() >= -1
+    rows = sample_rows(S, 512, 2024)
+    osel = O.select_blocks(qi[None], summ, bs, top_k, rows)
+    assert np.array_equal(gsel[:, :, rows], osel)
+    # the planted blocks are kept by every later query
+    late = np.arange((hot[-1] + 1) * bs, S)
+    for j in hot:
+        assert (gsel[0, :, late] == j).any(-1).all()
+    check_all_selections(gsel, qi[None].astype(np.int64), summ, S, bs, top_k)
+
+
 def test_structured_128k_sampled():
     _full_prefill_case("structured_128k", 4096, seed=31, all_selections=True)
 
