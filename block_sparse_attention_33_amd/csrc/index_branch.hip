@@ -472,6 +472,7 @@ __global__ __launch_bounds__(256) void index_topk_mfma_kernel(const int8_t* __re
 // ---------------------------------------------------------------------------
 constexpr int kSumStride32 = 80;  // bytes per staged summary (20 dwords: the 16-byte A reads of 16 rows hit distinct banks)
 constexpr int kEntCap = 6;        // buffered candidate groups per lane (LDS: 40 KiB per workgroup, four per CU)
+constexpr int kMasked = -(1 << 30);  // score of a non-candidate (every real score is within +-2^20)
 
 __device__ __forceinline__ uint32_t umed3(uint32_t a, uint32_t b, uint32_t c) {
   return max(min(a, b), min(max(a, b), c));
@@ -549,7 +550,7 @@ __global__ __launch_bounds__(256) void index_topk_bound_kernel(const int8_t* __r
     }
   };
   // one sweep: body(j0, acc) for every tile, acc[i] = the score of candidate
-  // j0 + c_row(i, hf), INT_MIN where that is not before the query's block
+  // j0 + c_row(i, hf), kMasked where that is not before the query's block
   // (rows past a chunk's end hold stale summaries; they are all masked)
   auto sweep = [&](auto&& body) {
     if (n_cand > 0) fetch(0);
@@ -581,7 +582,7 @@ __global__ __launch_bounds__(256) void index_topk_bound_kernel(const int8_t* __r
           if (j0 + 32 > c_lo) {
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-              if (j0 + c_row(i, hf) >= c) acc[h][i] = INT_MIN;
+              if (j0 + c_row(i, hf) >= c) acc[h][i] = kMasked;
           }
           body(j0, acc[h]);
         }
@@ -592,7 +593,7 @@ __global__ __launch_bounds__(256) void index_topk_bound_kernel(const int8_t* __r
   // sweep 1: slot maxima, then L = the kp'th largest of the query's 32
   int bm[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) bm[i] = INT_MIN;
+  for (int i = 0; i < 16; ++i) bm[i] = kMasked;
   sweep([&](int, const i32x16_t& acc) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) bm[i] = max(bm[i], acc[i]);
@@ -611,75 +612,92 @@ __global__ __launch_bounds__(256) void index_topk_bound_kernel(const int8_t* __r
     if (i == 32 - kp) L = m32[i];
   const int U = m32[31];
   // fewer than kp candidates (L undefined): all are kept, key score part 1
-  const bool all_in = L == INT_MIN;
+  const bool all_in = L <= kMasked;
   const bool narrow = __all(all_in || U - L < 65535);
 
-  // sweep 2: groups reaching the bound are buffered, the buffer drained into
-  // the list before a tile would overflow it and at the end.  A wave whose
-  // scores do not fit the keys still sweeps (the workgroup's barriers need
-  // it) but buffers nothing, and flags its rows for the single-sweep kernel.
-  int K[KCAP];  // keys, descending (unsigned)
+  // sweep 2: groups reaching the bound are buffered in a per-lane ring; when
+  // a tile would overflow some lane's ring, every lane moves its oldest
+  // entry into its list, as often as needed, and at the end the rings are
+  // emptied.  A wave whose scores do not fit the keys still sweeps (the
+  // workgroup's barriers need it) but buffers nothing, and flags its rows
+  // for the single-sweep kernel.
+  int K[KCAP];  // keys, descending (unsigned); below 65536: no candidate
 #pragma unroll
   for (int i = 0; i < KCAP; ++i) K[i] = 0;
-  int lf = !narrow ? INT_MAX : all_in ? INT_MIN : L;  // filter bound
-  int nbuf = 0;
-  auto drain = [&]() {
-    // no branch per lane: entries past a lane's count give key 0, which
-    // inserts nothing
-    for (int e = 0; __any(e < nbuf); ++e) {
-      const i32x4_t s4 = ent[e][tid];
-      const int jb = entj[e][tid];
-      uint32_t kq[4];
+  int lf = !narrow ? INT_MAX : all_in ? kMasked + 1 : L;  // filter bound
+  // key of score sc: ((clamp(sc - bias, 0, cap)) << 16) + 65535 - j; the
+  // clamp's 0 marks no candidate (below L, or not before the query's block)
+  const int bias = all_in ? kMasked + 1 : L - 1;
+  const int cap = all_in ? 1 : 65535;
+  int head = 0, cnt = 0;  // the ring: entries head .. head + cnt - 1 (mod kEntCap)
+  auto drain_one = [&]() {
+    // a lane with an empty ring reads a stale (or never written) slot: its
+    // clamp bound 0 and block 0 make every key of it below 65536
+    const bool has = cnt > 0;
+    const i32x4_t s4 = ent[head][tid];
+    const int jb = has ? entj[head][tid] : 0;
+    const int cap_e = has ? cap : 0;
+    const uint32_t lo = (uint32_t)(65535 - jb);
+    uint32_t kq[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = jb + r;
-        const int sc = s4[r];
-        const bool ok = (e < nbuf) & (j < c) & (all_in | (sc >= L));
-        kq[r] = ok ? ((uint32_t)(all_in ? 1 : sc - L + 1) << 16) | (uint32_t)(65535 - j) : 0u;
-      }
-      // the group's keys, descending; a group rarely holds more than one
-      // candidate of note, so the later insertions are skipped unless some
-      // lane has one
-      auto cx = [&](int a, int b) {
-        const uint32_t x = kq[a], y = kq[b];
-        kq[a] = max(x, y);
-        kq[b] = min(x, y);
-      };
-      cx(0, 1);
-      cx(2, 3);
-      cx(0, 2);
-      cx(1, 3);
-      cx(1, 2);
-      key_insert<KCAP>(K, kq[0]);
-      if (__any(kq[1] != 0)) {
-        key_insert<KCAP>(K, kq[1]);
-        if (__any(kq[2] != 0)) {
-          key_insert<KCAP>(K, kq[2]);
-          if (__any(kq[3] != 0)) key_insert<KCAP>(K, kq[3]);
-        }
+    for (int r = 0; r < 4; ++r) {
+      const int d = min(max((int)((uint32_t)s4[r] - (uint32_t)bias), 0), cap_e);
+      kq[r] = ((uint32_t)d << 16) + (lo - (uint32_t)r);
+    }
+    // the entry's keys, descending; a group rarely holds more than one
+    // candidate of note, so the later insertions are skipped unless some
+    // lane has one
+    auto cx = [&](int x, int y) {
+      const uint32_t p = kq[x], q = kq[y];
+      kq[x] = max(p, q);
+      kq[y] = min(p, q);
+    };
+    cx(0, 1);
+    cx(2, 3);
+    cx(0, 2);
+    cx(1, 3);
+    cx(1, 2);
+    key_insert<KCAP>(K, kq[0]);
+    if (__any(kq[1] >= 65536u)) {
+      key_insert<KCAP>(K, kq[1]);
+      if (__any(kq[2] >= 65536u)) {
+        key_insert<KCAP>(K, kq[2]);
+        if (__any(kq[3] >= 65536u)) key_insert<KCAP>(K, kq[3]);
       }
     }
-    nbuf = 0;
+    if (has) {
+      head = head == kEntCap - 1 ? 0 : head + 1;
+      --cnt;
+    }
     // a full list: later candidates (higher blocks) must beat its last score
     const uint32_t kl = (uint32_t)K[KCAP - 1];
-    if (kl != 0 && !all_in) lf = max(lf, (int)(kl >> 16) + L);
+    if (kl >= 65536u && !all_in) lf = max(lf, (int)(kl >> 16) + L);
   };
   sweep([&](int j0, const i32x16_t& acc) {
     int gm[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) gm[g] = max(max(acc[4 * g], acc[4 * g + 1]), max(acc[4 * g + 2], acc[4 * g + 3]));
     const int npass = (gm[0] >= lf) + (gm[1] >= lf) + (gm[2] >= lf) + (gm[3] >= lf);
-    if (__any(nbuf + npass > kEntCap)) drain();
+    // (a loop entered only when needed: the list's registers then move
+    // through the loop's join only on tiles that drain)
+    if (__any(cnt + npass > kEntCap)) {
+      do {
+        drain_one();
+      } while (__any(cnt + npass > kEntCap));
+    }
+    int tail = head + cnt;
+    tail = tail >= kEntCap ? tail - kEntCap : tail;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       if (gm[g] >= lf) {
-        ent[nbuf][tid] = i32x4_t{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
-        entj[nbuf][tid] = j0 + 8 * g + 4 * hf;
-        ++nbuf;
+        ent[tail][tid] = i32x4_t{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+        entj[tail][tid] = j0 + 8 * g + 4 * hf;
+        tail = tail == kEntCap - 1 ? 0 : tail + 1;
+        ++cnt;
       }
     }
   });
-  drain();
+  while (__any(cnt > 0)) drain_one();
   if (!narrow) {
     if (live && hf == 0) sel[((size_t)u * sel_stride + t) * top_k] = -2;
     return;
@@ -713,7 +731,7 @@ __global__ __launch_bounds__(256) void index_topk_bound_kernel(const int8_t* __r
   }
   int Li[KCAP];  // the selected blocks, best first (-1: none)
 #pragma unroll
-  for (int i = 0; i < KCAP; ++i) Li[i] = T[i] != 0 ? 65535 - (int)(T[i] & 65535u) : -1;
+  for (int i = 0; i < KCAP; ++i) Li[i] = T[i] >= 65536u ? 65535 - (int)(T[i] & 65535u) : -1;
   if (hf != 0) return;
 
   // best min(top_k - 1, c) candidates, ascending, then the own block
@@ -771,10 +789,12 @@ hipError_t launch_index_topk_at(const int8_t* q_idx, const int8_t* block_keys, i
   const int kp = top_k - 1;
   // the matrix-core scores pay once the queries rank many blocks (measured
   // on MI355X: 14 % faster at 1024 blocks, 27 % at 8192, 12 % slower at 256);
-  // the two-sweep kernel's keys hold block indices below 65536
+  // the two-sweep kernel's keys hold block indices below 65536, including
+  // those of the masked rows of its last chunk (up to 127 past the last
+  // candidate)
   const int n_blocks = (q0 + S - 1) >> bs_log2;
   const bool mfma = n_blocks >= kIndexMfmaMinBlocks;
-  const bool two_sweep = mfma && n_blocks <= 65536;
+  const bool two_sweep = mfma && n_blocks <= 65536 - 128;
   const dim3 grid(mfma ? (S + 127) / 128 : (S + 255) / 256, units);
 #define MSA_TOPK_LAUNCH(KC)                                                                                        \
   if (two_sweep) {                                                                                                 \
