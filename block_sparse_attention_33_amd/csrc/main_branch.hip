@@ -9,7 +9,7 @@
 // node "KV-outer gather Q").
 //
 //   attend_kernel  one work item = one KV block j of one (batch, group) unit
-//                  and up to 4 chunks of 256 query rows (tokens x heads) whose
+//                  and up to 6 chunks of 256 query rows (tokens x heads) whose
 //                  selection holds j, the query's own block included.  The
 //                  kernel is persistent: one workgroup of four waves per CU
 //                  walks its items, K_j and V_j^T go through one of two LDS
@@ -255,17 +255,17 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(
   };
   // this wave's entries of item d: ring position jj = c * epw + i holds
   // the entry of token c * tpc + (64 w >> r_log2) + i (clamped to the item)
-  auto load_ents = [&](const ItemDesc& d, uint32_t (&e)[4]) {
+  auto load_ents = [&](const ItemDesc& d, uint32_t (&e)[kItemChunks]) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
+    for (int m = 0; m < kItemChunks; ++m) {
       const int jj = min(lane + 64 * m, ring - 1);
       const int tk = (jj / epw) * tpc + ((64 * w) >> r_log2) + jj % epw;
       e[m] = entries[d.e0 + min(tk, d.n_ent - 1)];
     }
   };
-  auto store_ents = [&](int slot, const uint32_t (&e)[4]) {
+  auto store_ents = [&](int slot, const uint32_t (&e)[kItemChunks]) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < kItemChunks; ++m)
       if (lane + 64 * m < ring) ering[slot * ring + lane + 64 * m] = e[m];
   };
   auto ent_at = [&](int slot, int c, int ct) -> uint32_t {
@@ -290,7 +290,7 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(
   ItemDesc nxt2 = decode_at(it + 2 * stride);
   int qn = 0;  // sequence number of the current item (entry ring slot qn % 3)
   {
-    uint32_t e0r[4], e1r[4];
+    uint32_t e0r[kItemChunks], e1r[kItemChunks];
     load_ents(cur, e0r);
     load_ents(nxt, e1r);
     store_ents(0, e0r);
@@ -318,7 +318,7 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(
     size_t nxt_off;
     const int nxt_keys = kv_src(nxt, &nxt_off);
     load_kv_regs<BS, 256>(k + nxt_off, v + nxt_off, nxt_keys, kv);
-    uint32_t e2r[4];
+    uint32_t e2r[kItemChunks];
     load_ents(nxt2, e2r);
     const uint16_t* nxt_qb = q_base(nxt.u);
     const int key0 = cur.j * BS;

@@ -259,7 +259,7 @@ def test_prefill_workspace_layout(lib, B, S, Hq, G, bs, k):
     U, r = B * G, Hq // G
     nb = -(-S // bs)
     S = _query_chunk(S)
-    tpi = 4 * 256 // r          # up to 4 chunks of 256 query rows per work item
+    tpi = 6 * 256 // r          # up to 6 chunks of 256 query rows per work item
     n_chunks = _plan(U, S, nb)
     rows = U * nb
     items = U * ((S * k + tpi - 1) // tpi + nb) + 1
