@@ -114,7 +114,7 @@ PrefillPlan plan_prefill(const Dims& d) {
 }
 
 struct PrefillLayout {
-  size_t block_keys, sel, counts, hist, row_ptr, item_ptr, entries, items, part_o, part_ml, total;
+  size_t block_keys, sel, counts, hist, row_ptr, item_ptr, entries, items, sched, part_o, part_ml, total;
 };
 
 // Workspace: fixed part + partials of `units_per_pass` units of pass_tokens.
@@ -135,6 +135,7 @@ PrefillLayout prefill_layout(const Dims& d, const PrefillPlan& p, long units_per
   L.item_ptr = take((size_t)(p.rows + 1) * 4);
   L.entries = take((size_t)d.U * d.S * d.k * 4);
   L.items = take((size_t)(d.U * p.n_ranges * p.max_items_per_range + 1) * 8);
+  L.sched = take(4);  // the attention kernel's run counter
   L.part_o = take((size_t)units_per_pass * pass_tokens * d.k * d.r * d.D * 2);
   L.part_ml = take((size_t)units_per_pass * pass_tokens * d.k * d.r * 8);
   L.total = off;
@@ -390,6 +391,7 @@ int run_prefill(const Dims& dc, long q0, long n_q, const Strides& str, const uin
   int32_t* item_ptr = reinterpret_cast<int32_t*>(base + L.item_ptr);
   uint32_t* entries = reinterpret_cast<uint32_t*>(base + L.entries);
   int2* items = reinterpret_cast<int2*>(base + L.items);
+  int* sched = reinterpret_cast<int*>(base + L.sched);
   uint16_t* part_o = reinterpret_cast<uint16_t*>(base + L.part_o);
   float2* part_ml = reinterpret_cast<float2*>(base + L.part_ml);
 
@@ -448,7 +450,7 @@ int run_prefill(const Dims& dc, long q0, long n_q, const Strides& str, const uin
     ps.row_end = (int)(u1 * nb);
     const long max_items = (u1 - u0) * P.max_items_per_range;
     MSA_LAUNCH_NAMED("attend", s, msa::launch_attend(sh, ps, q, k, v, row_ptr, item_ptr, items, entries, part_o,
-                                                     part_ml, (int)max_items, s));
+                                                     part_ml, sched, (int)max_items, s));
     MSA_LAUNCH_NAMED("merge", s, msa::launch_merge(sh, ps, part_o, part_ml, out, s));
     return MSA_OK;
   };

@@ -106,9 +106,11 @@ hipError_t launch_scatter(const int32_t* sel, const int32_t* H, uint32_t* entrie
 // entry rings (three items' entries per wave) still fit beside the two K/V
 // buffers at one query head per group.
 constexpr int kItemChunks = 6;
+// sched: one int of scratch (the run counter), zeroed by the launch.
 hipError_t launch_attend(const PrefillShape& sh, const PassInfo& pass, const uint16_t* q, const uint16_t* k,
                          const uint16_t* v, const int32_t* row_ptr, const int32_t* item_ptr, const int2* items,
-                         const uint32_t* entries, uint16_t* part_o, float2* part_ml, int max_items, hipStream_t st);
+                         const uint32_t* entries, uint16_t* part_o, float2* part_ml, int* sched, int max_items,
+                         hipStream_t st);
 
 // Dense causal attention of every query row (for top_k >= nb, when the
 // selection keeps every block up to the own one, and for the short-sequence

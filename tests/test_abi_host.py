@@ -264,7 +264,7 @@ def test_prefill_workspace_layout(lib, B, S, Hq, G, bs, k):
     rows = U * nb
     items = U * ((S * k + tpi - 1) // tpi + nb) + 1
     fixed = (_a(U * nb * 64) + _a(U * S * k * 4) + _a(rows * 4) + _a(U * n_chunks * nb * 4)
-             + 2 * _a((rows + 1) * 4) + _a(U * S * k * 4) + _a(items * 8))
+             + 2 * _a((rows + 1) * 4) + _a(U * S * k * 4) + _a(items * 8) + _a(4))
     part = lambda n: _a(n * S * k * r * 128 * 2) + _a(n * S * k * r * 8)  # noqa: E731
     assert lo == fixed + part(1)
     assert hi == fixed + part(U)
