@@ -2,8 +2,8 @@
 
 Selections and block summaries must match bit for bit; outputs must be
 within max-abs 1e-2 and mean-abs 1e-3 of the oracle's fp64 result rounded to
-bf16, and every compared (row, head) within 5 % of its own mean magnitude
-(tests/helpers.py).  Small cases compare every row; at full size the 32K
+bf16, and every compared (row, head) with a mean error within 3 % of its own
+mean magnitude (tests/helpers.py).  Small cases compare every row; at full size the 32K
 prefill compares every row, the structured 128K and the 1M prefills 4096
 seeded rows each (the oracle runs over worker processes), and the 128K
 selections and the last 16384 rows of the 1M index are checked in full.
@@ -245,13 +245,14 @@ def test_index_select_many_blocks_all_rows(S, top_k, B):
         check_all_selections(gsel[b:b + 1], qi[b:b + 1], summ[b:b + 1], S, w.block_size, w.top_k)
 
 
-def test_index_select_wide_scores_all_rows():
+@pytest.mark.parametrize("top_k", [5, 16, 32])
+def test_index_select_wide_scores_all_rows(top_k):
     """Scores spread over more than 16 bits: a few planted blocks whose
     summaries align with the group's query direction score about 2^18
     while the rest stay near zero.  Queries before the first planted block
     keep the narrow rank keys; the later ones take the single-sweep path.
     Every selection is checked, sampled rows against the oracle."""
-    S, bs, G, top_k, di = 24000, 32, 2, 16, 64
+    S, bs, G, di = 24000, 32, 2, 64
     rng = np.random.default_rng(2024)
     u = rng.integers(-64, 64, size=(G, di))
     qi = np.clip(u[:, None, :] + rng.integers(-16, 16, size=(G, S, di)), -128, 127).astype(np.int8)
@@ -261,7 +262,7 @@ def test_index_select_wide_scores_all_rows():
         for j in hot:
             noise = rng.integers(-4, 4, size=(bs, di))
             ki[g, j * bs:(j + 1) * bs] = np.clip(np.sign(u[g]) * 127 + noise, -128, 127)
-    _say(f"[index wide scores] S={S} bs={bs} hot blocks={len(hot)}")
+    _say(f"[index wide scores] S={S} bs={bs} top_k={top_k} hot blocks={len(hot)}")
     q_idx = torch.from_numpy(qi[None]).to(DEV)
     k_idx = torch.from_numpy(ki[None]).to(DEV)
     bk, sel = msa.msa_index_select(q_idx, k_idx, bs, top_k)
@@ -273,10 +274,12 @@ def test_index_select_wide_scores_all_rows():
     rows = sample_rows(S, 512, 2024)
     osel = O.select_blocks(qi[None], summ, bs, top_k, rows)
     assert np.array_equal(gsel[:, :, rows], osel)
-    # the planted blocks are kept by every later query
+    # the planted blocks (9 of them) are kept by every later query that
+    # keeps as many
     late = np.arange((hot[-1] + 1) * bs, S)
-    for j in hot:
-        assert (gsel[0, :, late] == j).any(-1).all()
+    if top_k - 1 >= len(hot):
+        for j in hot:
+            assert (gsel[0, :, late] == j).any(-1).all()
     check_all_selections(gsel, qi[None].astype(np.int64), summ, S, bs, top_k)
 
 
