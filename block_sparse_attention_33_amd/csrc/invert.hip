@@ -77,11 +77,19 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
   const int per = (n + 1023) / 1024;
   const int i0 = min(n, tid * per);
   const int i1 = min(n, i0 + per);
+  // the run's counts are loaded 16 at a time (one memory round trip per 16
+  // instead of one per count)
+  constexpr int kB = 16;
   int a = 0, b = 0;
-  for (int i = i0; i < i1; ++i) {
-    const int c = counts[i];
-    a += c;
-    b += (c + tpi - 1) / tpi;
+  for (int i = i0; i < i1; i += kB) {
+    int c[kB];
+#pragma unroll
+    for (int j = 0; j < kB; ++j) c[j] = i + j < i1 ? counts[i + j] : 0;
+#pragma unroll
+    for (int j = 0; j < kB; ++j) {
+      a += c[j];
+      b += (c[j] + tpi - 1) / tpi;
+    }
   }
   sa[tid] = a;
   sb[tid] = b;
@@ -96,12 +104,19 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
   }
   int ea = sa[tid] - a;
   int eb = sb[tid] - b;
-  for (int i = i0; i < i1; ++i) {
-    const int c = counts[i];
-    row_ptr[i] = ea;
-    item_ptr[i] = eb;
-    ea += c;
-    eb += (c + tpi - 1) / tpi;
+  for (int i = i0; i < i1; i += kB) {
+    int c[kB];
+#pragma unroll
+    for (int j = 0; j < kB; ++j) c[j] = i + j < i1 ? counts[i + j] : 0;
+#pragma unroll
+    for (int j = 0; j < kB; ++j) {
+      if (i + j < i1) {
+        row_ptr[i + j] = ea;
+        item_ptr[i + j] = eb;
+      }
+      ea += c[j];
+      eb += (c[j] + tpi - 1) / tpi;
+    }
   }
   if (tid == 1023) {
     row_ptr[n] = sa[1023];
