@@ -224,7 +224,7 @@ def test_prefill_32k_selection_all_rows():
     check_all_selections(gsel, qi, summ, S, bs, w.top_k)
 
 
-@pytest.mark.parametrize("S,top_k,B", [(40000, 12, 1), (20000, 32, 1), (20000, 2, 2), (17000, 5, 1)])
+@pytest.mark.parametrize("S,top_k,B", [(40000, 12, 1), (20000, 32, 1), (20000, 2, 2), (17000, 5, 1), (9000, 1, 1)])
 def test_index_select_many_blocks_all_rows(S, top_k, B):
     """Thousands of tokens in blocks of 32 (531 to 1250 blocks): the queries
     rank enough blocks for the matrix-core scoring; every selection is
