@@ -264,7 +264,7 @@ __global__ __launch_bounds__(256) void index_topk_kernel(const int8_t* __restric
 // the arrival order keeps the tie rule, so the lists are the same.
 //
 // This single-sweep kernel serves what the two-sweep kernel below cannot:
-// queries ranking more than 65536 blocks, and (flagged_only) the waves it
+// queries ranking more than 65408 blocks, and (flagged_only) the waves it
 // flags for a score spread its keys cannot hold.
 // ---------------------------------------------------------------------------
 constexpr int kTopkBufMfma = 24;    // buffered candidates per lane (a tile adds at most 16)
@@ -451,24 +451,27 @@ __global__ __launch_bounds__(256) void index_topk_mfma_kernel(const int8_t* __re
 // all tiles: 32 maxima per query over disjoint candidate sets.  Their top_k -
 // 1'th largest, L, is a lower bound on the query's (top_k - 1)'th best score
 // (that many distinct candidates reach it), so no candidate scoring below L
-// can be selected.  Sweep 2 scores the candidates again and buffers, per
-// lane in LDS, the scores of each group of four consecutive candidates
-// (slots 4 g .. 4 g + 3) whose maximum reaches the filter bound; few do, so
-// the per-candidate work happens for few.  The buffered candidates go into a
-// per-lane list of the best KCAP, ranked by the unsigned key
-// ((s - L + 1) << 16) | (65535 - j), which orders by score, then by lower
-// block, and makes an insertion one median per list slot.  The two half
-// lists of a query are joined at the end.  After each drain of the buffer
-// the bound rises to one above the list's last score when the list is full:
-// later candidates have higher block indices and cannot displace an entry
-// they only tie.
+// can be selected.  Sweep 2 scores the candidates again and appends to a
+// per-lane ring in LDS the scores of each group of four consecutive
+// candidates (slots 4 g .. 4 g + 3) whose maximum reaches the filter bound;
+// few do, so the per-candidate work happens for few.  When a tile would
+// overflow some lane's ring, every lane moves its oldest entry into a
+// per-lane list of the best KCAP (and the rings are emptied at the end),
+// ranked by the unsigned key ((s - L + 1) << 16) + 65535 - j, which orders
+// by score, then by lower block, and makes an insertion one median per list
+// slot; a key below 65536 stands for no candidate.  The two half lists of a
+// query are joined at the end.  Whenever the list is full, the bound rises
+// to one above its last score: later candidates have higher block indices
+// and cannot displace an entry they only tie.
 //
 // A query with fewer than top_k - 1 candidates keeps them all (key score
 // part 1).  A wave where some query's best score is 65535 or more above its
 // L cannot use the keys: it writes -2 into the first entry of its rows and
 // index_topk_mfma_kernel, launched after this one with flagged_only set,
 // recomputes the workgroups that hold such a wave.  The host sends queries
-// that rank more than 65536 blocks to index_topk_mfma_kernel directly.
+// that rank more than 65408 blocks (so that even the masked rows past the
+// last candidate keep block indices below 65536) to index_topk_mfma_kernel
+// directly.
 // ---------------------------------------------------------------------------
 constexpr int kSumStride32 = 80;  // bytes per staged summary (20 dwords: the 16-byte A reads of 16 rows hit distinct banks)
 constexpr int kEntCap = 4;        // buffered candidate groups per lane (with 256-summary chunks: 40 KiB of
