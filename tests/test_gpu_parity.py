@@ -283,6 +283,33 @@ def test_index_select_wide_scores_all_rows(top_k):
     check_all_selections(gsel, qi[None].astype(np.int64), summ, S, bs, top_k)
 
 
+@pytest.mark.parametrize("nb", [65000, 65625])
+def test_index_select_block_index_limit(nb):
+    """Either side of the two-sweep kernel's block limit (65408 blocks, so
+    that its keys hold every block index below 65536): 65000 blocks of 32
+    tokens rank on the two-sweep kernel, 65625 on the single-sweep one.  One
+    group; the last 2048 rows against the exact top-k rule, 256 of them
+    against the oracle."""
+    S, bs, top_k = nb * 32, 32, 16
+    g = torch.Generator().manual_seed(nb)
+    q_idx = torch.randint(-64, 64, (1, 1, S, 64), generator=g, dtype=torch.int8)
+    k_idx = torch.randint(-64, 64, (1, 1, S, 64), generator=g, dtype=torch.int8)
+    _say(f"[index block limit] S={S} nb={nb}")
+    bk, sel = msa.msa_index_select(q_idx.to(DEV), k_idx.to(DEV), bs, top_k)
+    torch.cuda.synchronize()
+    summ = O.pool_block_keys(k_idx.numpy(), bs)
+    assert np.array_equal(host_i8(bk), summ)
+    gsel = host_i8(sel)
+    qi = q_idx.numpy()
+    rows = np.arange(S - 2048, S)
+    check_all_selections(gsel, qi, summ, S, bs, top_k, row_slice=512, rows=rows)
+    some = sample_rows(2048, 256, nb) + (S - 2048)
+    osel = O.select_blocks(qi, summ, bs, top_k, some)
+    assert np.array_equal(gsel[:, :, some].astype(np.int32), osel)
+    del bk, sel
+    _free()
+
+
 def test_structured_128k_sampled():
     _full_prefill_case("structured_128k", 4096, seed=31, all_selections=True)
 
