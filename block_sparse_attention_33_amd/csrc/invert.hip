@@ -18,8 +18,9 @@ namespace msa {
 namespace {
 
 // Per-chunk histograms: one workgroup per (token chunk, unit) counts, in LDS,
-// how many of the chunk's queries kept each block (the own block included),
-// and stores the counts as H[u][chunk][block].  LDS atomics only.
+// how many of the chunk's queries kept each block (the own block only with
+// with_own: the forward attends it elsewhere, the backward through the
+// lists), and stores the counts as H[u][chunk][block].  LDS atomics only.
 __device__ __forceinline__ void chunk_tokens(const ChunkPlan& cp, int c, int S, int* t0, int* t1) {
   const int rng = c / cp.m;
   const int i = c - rng * cp.m;
@@ -29,7 +30,8 @@ __device__ __forceinline__ void chunk_tokens(const ChunkPlan& cp, int c, int S, 
 
 __global__ __launch_bounds__(256) void chunk_hist_kernel(const int32_t* __restrict__ sel,
                                                          int32_t* __restrict__ H, int S, int nb,
-                                                         int bs_log2, int top_k, ChunkPlan cp, int q0) {
+                                                         int bs_log2, int top_k, ChunkPlan cp, int q0,
+                                                         int with_own) {
   extern __shared__ int32_t hist[];
   const int c = blockIdx.x;
   const int u = blockIdx.y;
@@ -42,7 +44,7 @@ __global__ __launch_bounds__(256) void chunk_hist_kernel(const int32_t* __restri
   for (int t = t0 + (int)threadIdx.x; t < t1; t += 256) {
     const int nv = min(kp, (q0 + t) >> bs_log2);  // slot nv holds the own block
     const int32_t* srow = sel + ((size_t)u * cp.q_stride + t) * top_k;
-    for (int s = 0; s <= nv; ++s) atomicAdd(&hist[srow[s]], 1);
+    for (int s = 0; s < nv + with_own; ++s) atomicAdd(&hist[srow[s]], 1);
   }
   __syncthreads();
   int32_t* dst = H + ((size_t)u * n_chunks + c) * nb;
@@ -157,7 +159,8 @@ __global__ __launch_bounds__(256) void offsets_items_kernel(int32_t* __restrict_
 __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ sel,
                                                       const int32_t* __restrict__ H,
                                                       uint32_t* __restrict__ entries, int S, int nb,
-                                                      int bs_log2, int top_k, ChunkPlan cp, int q0) {
+                                                      int bs_log2, int top_k, ChunkPlan cp, int q0,
+                                                      int with_own) {
   extern __shared__ int32_t cursor[];
   const int c = blockIdx.x;
   const int u = blockIdx.y;
@@ -170,7 +173,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
   for (int t = t0 + (int)threadIdx.x; t < t1; t += 256) {
     const int nv = min(kp, (q0 + t) >> bs_log2);  // slot nv holds the own block
     const int32_t* srow = sel + ((size_t)u * cp.q_stride + t) * top_k;
-    for (int s = 0; s <= nv; ++s) {
+    for (int s = 0; s < nv + with_own; ++s) {
       const int pos = atomicAdd(&cursor[srow[s]], 1);
       entries[pos] = ((uint32_t)t << 5) | (uint32_t)s;
     }
@@ -180,7 +183,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
 }  // namespace
 
 hipError_t launch_chunk_hist(const int32_t* sel, int32_t* H, int units, int S, int nb, int bs, int top_k,
-                             const ChunkPlan& cp, int q0, hipStream_t st) {
+                             const ChunkPlan& cp, int q0, bool with_own, hipStream_t st) {
   int bs_log2 = 0;
   while ((1 << bs_log2) < bs) ++bs_log2;
   const size_t lds = (size_t)nb * 4;
@@ -188,7 +191,7 @@ hipError_t launch_chunk_hist(const int32_t* sel, int32_t* H, int units, int S, i
       ensure_dynamic_lds(reinterpret_cast<const void*>(&chunk_hist_kernel), kMaxInvertBlocks * 4);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(chunk_hist_kernel, dim3(cp.n_chunks, units), dim3(256), lds, st, sel, H, S, nb, bs_log2,
-                     top_k, cp, q0);
+                     top_k, cp, q0, with_own ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -214,14 +217,14 @@ hipError_t launch_offsets_items(int32_t* H, const int32_t* row_ptr, const int32_
 }
 
 hipError_t launch_scatter(const int32_t* sel, const int32_t* H, uint32_t* entries, int units, int S, int nb,
-                          int bs, int top_k, const ChunkPlan& cp, int q0, hipStream_t st) {
+                          int bs, int top_k, const ChunkPlan& cp, int q0, bool with_own, hipStream_t st) {
   int bs_log2 = 0;
   while ((1 << bs_log2) < bs) ++bs_log2;
   const size_t lds = (size_t)nb * 4;
   const hipError_t attr = ensure_dynamic_lds(reinterpret_cast<const void*>(&scatter_kernel), kMaxInvertBlocks * 4);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(scatter_kernel, dim3(cp.n_chunks, units), dim3(256), lds, st, sel, H, entries, S, nb, bs_log2,
-                     top_k, cp, q0);
+                     top_k, cp, q0, with_own ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -10,21 +10,22 @@
 //
 //   attend_kernel  one work item = one KV block j of one (batch, group) unit
 //                  and up to 6 chunks of 256 query rows (tokens x heads) whose
-//                  selection holds j, the query's own block included.  The
-//                  kernel is persistent: one workgroup of four waves per CU
-//                  walks its items, K_j and V_j^T go through one of two LDS
-//                  buffers while the next item's block is staged into the
-//                  other, and each wave loads the 64 gathered query rows of
-//                  its next chunk during the current one.  Every row leaves an
-//                  unnormalised bf16 partial and its (max, sum) in base-2
-//                  units at its selection slot (a row with no other partial,
-//                  own block 0 or top_k = 1, leaves o / l with a sum of 1).
-//                  Chunks holding a query's own block apply the
-//                  causal mask and split P into two bf16 terms, so P.V keeps
-//                  ~16 mantissa bits for the first tokens of a sequence,
-//                  which see only a few keys.
-//   merge_kernel   log-sum-exp merge of a query row's partials -> out.
-//
+//                  selection holds j as one of the blocks before the query's
+//                  own.  The kernel is persistent: one workgroup of four
+//                  waves per CU walks its items, K_j and V_j^T go through one
+//                  of two LDS buffers while the next item's block is staged
+//                  into the other, and each wave loads the 64 gathered query
+//                  rows of its next chunk during the current one.  Every row
+//                  leaves an unnormalised bf16 partial and its (max, sum) in
+//                  base-2 units at its selection slot.  No key of such a
+//                  block is after a query that selected it: no mask.
+//   merge_kernel   the own block (the one kept block holding keys after some
+//                  of its queries): causal attention of 128-row tiles with P
+//                  split into two bf16 terms, so P.V keeps ~16 mantissa bits
+//                  for the first tokens of a block, which see only a few
+//                  keys; the result, in fp32 registers, is merged with the
+//                  row's partials by log-sum-exp -> out.
+
 // Tile shapes (wave64, v_mfma_f32_32x32x16_bf16):
 //   S^T = K Q^T : 32 keys x 32 query rows per tile, K from LDS (A operand),
 //                 Q rows straight from HBM into registers (B operand).
@@ -152,18 +153,6 @@ __device__ __forceinline__ u32x4_t vt_frag(const char* lds, int dt, int kt, int 
 
 // A column tile's results packed for storing: the row's 128 values as bf16,
 // lane-half-major (position 64 * hf + 16 * dt + i), 8 u32x4 per lane.
-__device__ __forceinline__ void pack_tile(const f32x16_t (&o)[4], float scale, u32x4_t (&pv)[8]) {
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
-    pv[2 * dt] = u32x4_t{pack_bf16x2(o[dt][0] * scale, o[dt][1] * scale), pack_bf16x2(o[dt][2] * scale, o[dt][3] * scale),
-                         pack_bf16x2(o[dt][4] * scale, o[dt][5] * scale), pack_bf16x2(o[dt][6] * scale, o[dt][7] * scale)};
-    pv[2 * dt + 1] =
-        u32x4_t{pack_bf16x2(o[dt][8] * scale, o[dt][9] * scale), pack_bf16x2(o[dt][10] * scale, o[dt][11] * scale),
-                pack_bf16x2(o[dt][12] * scale, o[dt][13] * scale), pack_bf16x2(o[dt][14] * scale, o[dt][15] * scale)};
-  }
-}
-
-// Without a scale: plain conversion.
 __device__ __forceinline__ void pack_tile(const f32x16_t (&o)[4], u32x4_t (&pv)[8]) {
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) {
@@ -174,15 +163,19 @@ __device__ __forceinline__ void pack_tile(const f32x16_t (&o)[4], u32x4_t (&pv)[
   }
 }
 
-// Store a packed row of the partials at row pidx, lane half hf, with its
-// (max, sum).  Both lane halves store the (max, sum) pair (the same value),
-// so that every path issues the same memory operations.
-__device__ __forceinline__ void store_row(const u32x4_t (&pv)[8], float2 ml, size_t pidx, int hf,
+// Store a packed row of the partials: (token, slot) row prow, head `head`
+// of r, lane half hf, with its (max, sum).  The 16-byte pieces of the r
+// heads' rows are interleaved, piece-major (piece 2 m + hf of head h at
+// piece (16 prow + 2 m + hf) r + h), so that the lanes holding one token's
+// heads write, and the merge reads, r consecutive pieces.  Both lane halves
+// store the (max, sum) pair (the same value), so that every path issues the
+// same memory operations.
+__device__ __forceinline__ void store_row(const u32x4_t (&pv)[8], float2 ml, size_t prow, int head, int r, int hf,
                                           uint16_t* __restrict__ part_o, float2* __restrict__ part_ml) {
-  uint16_t* dst = part_o + pidx * kHeadDim + 64 * hf;
+  u32x4_t* dst = reinterpret_cast<u32x4_t*>(part_o) + (prow * 16 + hf) * r + head;
 #pragma unroll
-  for (int m = 0; m < 8; ++m) *reinterpret_cast<u32x4_t*>(dst + 8 * m) = pv[m];
-  part_ml[pidx] = ml;
+  for (int m = 0; m < 8; ++m) dst[(size_t)(2 * m) * r] = pv[m];
+  part_ml[prow * r + head] = ml;
 }
 
 // ---------------------------------------------------------------------------
@@ -361,7 +354,6 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(
     uint32_t e2r[kItemChunks];
     load_ents(nxt2, e2r);
     const uint16_t* nxt_qb = q_base(nxt.u);
-    const int key0 = cur.j * BS;
     const size_t row0 = (size_t)(cur.u - pass.u0) * pass.pass_tokens + pass_row0;
     const int n_chunks = n_chunks_of(cur);
     const int slot_cur = qn % 3;
@@ -415,126 +407,57 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(
       }
       load_q(qb_nx, ent_nx, qf);
 
-      size_t pidx[2];
+      size_t prow[2];
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) pidx[ct] = ((row0 + tok[ct]) * K + slot[ct]) * sh.r + head[ct];
-      const bool own[2] = {((sh.q0 + tok[0]) >> sh.bs_log2) == cur.j, ((sh.q0 + tok[1]) >> sh.bs_log2) == cur.j};
-      if (!__any(own[0] || own[1])) {
-        // ---- no query of this chunk owns the block: plain softmax
-        float m2[2], sum[2];
-        u32x4_t ph[KT][2][2];
+      for (int ct = 0; ct < 2; ++ct) prow[ct] = (row0 + tok[ct]) * K + slot[ct];
+      // softmax: the block lies wholly before every query of the chunk (the
+      // own block is attended by the merge), so no key is masked
+      float m2[2], sum[2];
+      u32x4_t ph[KT][2][2];
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          float mx = -__builtin_inff();
+      for (int ct = 0; ct < 2; ++ct) {
+        float mx = -__builtin_inff();
 #pragma unroll
-          for (int kt = 0; kt < KT; ++kt)
+        for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][ct][i]);
-          m2[ct] = wave_max_pair(mx) * c2;
-          sum[ct] = 0.f;
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][ct][i]);
+        m2[ct] = wave_max_pair(mx) * c2;
+        sum[ct] = 0.f;
 #pragma unroll
-          for (int kt = 0; kt < KT; ++kt)
+        for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-              uint32_t d[4];
+          for (int h2 = 0; h2 < 2; ++h2) {
+            uint32_t d[4];
 #pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const float p0 = fast_exp2(fmaf(s[kt][ct][8 * h2 + 2 * e], c2, -m2[ct]));
-                const float p1 = fast_exp2(fmaf(s[kt][ct][8 * h2 + 2 * e + 1], c2, -m2[ct]));
-                sum[ct] += p0 + p1;
-                d[e] = pack_bf16x2(p0, p1);
-              }
-              ph[kt][ct][h2] = u32x4_t{d[0], d[1], d[2], d[3]};
+            for (int e = 0; e < 4; ++e) {
+              const float p0 = fast_exp2(fmaf(s[kt][ct][8 * h2 + 2 * e], c2, -m2[ct]));
+              const float p1 = fast_exp2(fmaf(s[kt][ct][8 * h2 + 2 * e + 1], c2, -m2[ct]));
+              sum[ct] += p0 + p1;
+              d[e] = pack_bf16x2(p0, p1);
             }
-        }
-        // O^T = V^T P^T, one column tile at a time; V^T is read again for
-        // the second tile (kept from the first it would take 128 registers)
+            ph[kt][ct][h2] = u32x4_t{d[0], d[1], d[2], d[3]};
+          }
+      }
+      // O^T = V^T P^T, one column tile at a time; V^T is read again for
+      // the second tile (kept from the first it would take 128 registers)
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          int vo = kvo;
-          __asm__ volatile("" : "+v"(vo));
-          const char* kvt = lds + vo;
-          f32x16_t o[4];
+      for (int ct = 0; ct < 2; ++ct) {
+        int vo = kvo;
+        __asm__ volatile("" : "+v"(vo));
+        const char* kvt = lds + vo;
+        f32x16_t o[4];
 #pragma unroll
-          for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16_t{};
+        for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16_t{};
 #pragma unroll
-          for (int kt = 0; kt < KT; ++kt)
+        for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2)
+          for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-              for (int dt = 0; dt < 4; ++dt)
-                o[dt] = mfma32x32x16(vt_frag<BS>(kvt, dt, kt, h2, lane), ph[kt][ct][h2], o[dt]);
-          u32x4_t pv1[8];
-          pack_tile(o, pv1);
-          store_row(pv1, make_float2(m2[ct], wave_sum_pair(sum[ct])), pidx[ct], hf, part_o, part_ml);
-        }
-      } else {
-        // ---- some query owns the block: causal mask on the own columns,
-        // and P = hi + lo in bf16 there (~16 mantissa bits).  The other
-        // columns take a zero low term and come out bit-identical to the
-        // plain path.
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          // keys 0 .. tok - key0 are not after the query; the lane-half
-          // term of the key index moves to the right-hand side so that
-          // every compare is against a constant
-          const int lim = sh.q0 + tok[ct] - key0 - 4 * hf;
-#pragma unroll
-          for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-              if (32 * kt + c_row(i, 0) > lim) s[kt][ct][i] = -__builtin_inff();
-        }
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          int vo = kvo;
-          __asm__ volatile("" : "+v"(vo));
-          const char* kvt = lds + vo;
-          float mx = -__builtin_inff();
-#pragma unroll
-          for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][ct][i]);
-          const float m2 = wave_max_pair(mx) * c2;
-          const float lo_on = own[ct] ? 1.0f : 0.0f;  // arithmetic select: no divergent branch
-          float sum = 0.f;
-          f32x16_t o[4];
-#pragma unroll
-          for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16_t{};
-#pragma unroll
-          for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-              uint32_t dh[4], dl[4];
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const float p0 = fast_exp2(fmaf(s[kt][ct][8 * h2 + 2 * e], c2, -m2));
-                const float p1 = fast_exp2(fmaf(s[kt][ct][8 * h2 + 2 * e + 1], c2, -m2));
-                sum += p0 + p1;
-                dh[e] = pack_bf16x2(p0, p1);
-                dl[e] = pack_bf16x2((p0 - bf16_lo(dh[e])) * lo_on, (p1 - bf16_hi(dh[e])) * lo_on);
-              }
-              const u32x4_t ph = u32x4_t{dh[0], dh[1], dh[2], dh[3]};
-              const u32x4_t pl = u32x4_t{dl[0], dl[1], dl[2], dl[3]};
-#pragma unroll
-              for (int dt = 0; dt < 4; ++dt) {
-                const u32x4_t a = vt_frag<BS>(kvt, dt, kt, h2, lane);
-                o[dt] = mfma32x32x16(a, ph, o[dt]);
-                o[dt] = mfma32x32x16(a, pl, o[dt]);
-              }
-            }
-          const float l = wave_sum_pair(sum);
-          // a row with no other partial (own block 0, or top_k = 1) stores
-          // o / l with a sum of 1: the merge then reproduces it exactly, so
-          // the row is rounded to bf16 once, as every other row
-          const bool single = ((sh.q0 + tok[ct]) >> sh.bs_log2) == 0 || K == 1;
-          // (its max then carries log2 l, so that the merge's log-sum-exp
-          // is the row's)
-          u32x4_t pv1[8];
-          pack_tile(o, single ? 1.0f / l : 1.0f, pv1);
-          store_row(pv1, make_float2(single ? m2 + fast_log2(l) : m2, single ? 1.0f : l), pidx[ct], hf, part_o,
-                    part_ml);
-        }
+            for (int dt = 0; dt < 4; ++dt)
+              o[dt] = mfma32x32x16(vt_frag<BS>(kvt, dt, kt, h2, lane), ph[kt][ct][h2], o[dt]);
+        u32x4_t pv1[8];
+        pack_tile(o, pv1);
+        store_row(pv1, make_float2(m2[ct], wave_sum_pair(sum[ct])), prow[ct], head[ct], sh.r, hf, part_o, part_ml);
       }
       qb = qb_nx;
     }
@@ -568,83 +491,254 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Merge: 16 threads per query row, 8 stored values (16 bytes) each.  Every
-// partial is read once, with a non-temporal hint (measured on MI355X: the
-// merge 0.97 -> 0.86 ms per 16K-query chunk).
-//   out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,  M = max_s m_s
-// over the row's min(top_k - 1, own) + 1 partials (a row with a single
-// partial holds o / l with a sum of 1, which the merge reproduces exactly).
+// Own block and merge.  A query's own block is the one kept block that
+// holds keys after some of its queries; it is attended here, not in the
+// attention kernel, and its result stays in registers in fp32 while the
+// row's other partials are merged into it:
+//   out = (2^(m_o - M) o_o + sum_s 2^(m_s - M) o_s) / (2^(m_o - M) l_o + sum_s 2^(m_s - M) l_s)
+// with M the largest of the maxima, over the own block (o) and the
+// min(top_k - 1, own) partials s of the row.  One workgroup per tile of 128
+// query rows (128 / r tokens x the r heads of a group), one 32-row column
+// tile per wave.  The own block's keys up to the tile's last token go to
+// LDS (K key-major, V transposed), then S^T = K Q^T with the causal mask, a
+// base-2 softmax and O^T += V^T P^T with P split into two bf16 terms
+// (hi + lo, ~16 mantissa bits, for the first tokens of a block, which see
+// few keys).  A tile whose tokens fall in two blocks takes them in turn,
+// each row attending only its own.  The partials are read once, with a
+// non-temporal hint, each lane reading its row's half (the lanes of one
+// token's heads read consecutive pieces).  Workgroups go to the eight XCDs
+// in turn; tiles are numbered so that each XCD takes runs of eight
+// consecutive tiles, which mostly share their block, whose K and V then
+// come from that XCD's L2 after the first read.  Measured on MI355X against
+// attending the own block in the attention kernel and merging its partial
+// like the others: the 1M prefill 200 -> 172 ms with the interleaved
+// partial layout (the attention kernel 142 -> 113 ms, the merge 48 ms both).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void merge_kernel(const uint16_t* __restrict__ part_o,
-                                                    const float2* __restrict__ part_ml,
-                                                    uint16_t* __restrict__ out, PrefillShape sh, PassInfo pass,
-                                                    int t_first, int r_log2) {
-  const long gid = (long)blockIdx.x * 256 + threadIdx.x;
-  const int c16 = (int)(gid & 15);
-  const long qr = gid >> 4;
-  const int h = (int)(qr & (sh.r - 1));
-  const int t = t_first + (int)(qr >> r_log2);
-  if (t >= pass.t1) return;
+constexpr int kMergeRows = 128;  // query rows per workgroup
+constexpr int kMaxOther = 31;    // partials per row besides the own block
+constexpr int kMergeRowBytes = 2 * kHeadDim + 16;  // a row of O in LDS (padded)
+template <int BS>
+constexpr int merge_lds_bytes() {
+  return Tile<BS>::kLdsBytes > kMergeRows * kMergeRowBytes ? Tile<BS>::kLdsBytes : kMergeRows * kMergeRowBytes;
+}
+
+// Value e (0..7) of a packed u32x4 of bf16 pairs.
+__device__ __forceinline__ float bf16_at(const u32x4_t& v, int e) {
+  const uint32_t x = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
+  return (e & 1) ? bf16_hi(x) : bf16_lo(x);
+}
+
+template <int BS>
+__global__ __launch_bounds__(256, 2) void merge_kernel(const uint16_t* __restrict__ q,
+                                                       const uint16_t* __restrict__ k,
+                                                       const uint16_t* __restrict__ v,
+                                                       const uint16_t* __restrict__ part_o,
+                                                       const float2* __restrict__ part_ml,
+                                                       uint16_t* __restrict__ out, PrefillShape sh, PassInfo pass,
+                                                       int r_log2, int n_tiles) {
+  constexpr int KT = Tile<BS>::KT;
+  extern __shared__ __align__(16) char lds[];  // one K/V buffer
+  // workgroup i runs on XCD i % 8; its 64-tile group gives XCD x the tiles
+  // 8 x .. 8 x + 7
+  const int gi = (int)blockIdx.x;
+  const int tile = (gi & ~63) + 8 * (gi & 7) + ((gi >> 3) & 7);
+  if (tile >= n_tiles) return;
   const int u = pass.u0 + (int)blockIdx.y;
   const int b = u / sh.G;
   const int g = u - b * sh.G;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int hf = lane >> 5;
   const int K = sh.top_k;
-  const int n = min(K - 1, (sh.q0 + t) >> sh.bs_log2) + 1;
-  const size_t base = ((size_t)(u - pass.u0) * pass.pass_tokens + (t - pass.t0)) * K;
+  const float c2 = sh.scale_log2;
+  const int tpt = kMergeRows >> r_log2;         // tokens per tile
+  const int t_a = pass.t0 + tile * tpt;          // the tile's first token
+  const int t_z = min(pass.t1, t_a + tpt) - 1;   // and its last
+  // this wave's tokens tw0 .. tw1 (none if tw1 < tw0)
+  const int tw0 = t_a + ((32 * w) >> r_log2);
+  const int tw1 = min(t_z, t_a + ((32 * w + 31) >> r_log2));
+  const bool wave_live = tw0 <= tw1;
+  const int qr = 32 * w + (lane & 31);
+  const int tok = t_a + (qr >> r_log2);
+  const int head = qr & (sh.r - 1);
+  const bool live = tok <= t_z;
+  const int tc = min(tok, t_z);
+  const int pos = sh.q0 + tc;
+  const int jo = pos >> sh.bs_log2;  // the row's own block
+  const size_t orow = ((size_t)b * sh.q_stride + tc) * sh.Hq + g * sh.r + head;
 
-  float m[32], l[32];
-  float M = -__builtin_inff();
+  u32x4_t qf[8];
+  load_q_frag(q + orow * kHeadDim, hf, qf);
+  float m = -__builtin_inff(), l = 0.f;
+  f32x16_t o[4];
 #pragma unroll
-  for (int s = 0; s < 32; ++s) {
-    const f32x2_t ml = (s < n) ? __builtin_nontemporal_load(reinterpret_cast<const f32x2_t*>(part_ml + (base + s) * sh.r + h))
-                               : f32x2_t{-__builtin_inff(), 0.f};
-    m[s] = ml.x;
-    l[s] = ml.y;
-    M = fmaxf(M, m[s]);
-  }
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float W = 0.f;
+  for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16_t{};
+
+  const int jf = (sh.q0 + t_a) >> sh.bs_log2;
+  const int jl = (sh.q0 + t_z) >> sh.bs_log2;
+  const int jw0 = (sh.q0 + tw0) >> sh.bs_log2;  // own blocks of this wave's rows
+  const int jw1 = (sh.q0 + tw1) >> sh.bs_log2;
+  for (int j = jf; j <= jl; ++j) {
+    // keys of block j up to the tile's last token (rows beyond are zeroed)
+    const int n_keys = min(BS, sh.q0 + t_z + 1 - j * BS);
+    if (j > jf) __syncthreads();  // every wave is done with block j - 1
+    {
+      KvStage<BS, 256> kv;
+      const size_t off = ((size_t)u * sh.kv_rows + (size_t)j * BS) * kHeadDim;
+      load_kv_regs<BS, 256>(k + off, v + off, n_keys, kv);
+      store_kv_lds<BS, 256>(kv, n_keys, lds);
+    }
+    __syncthreads();
+    if (!wave_live || j < jw0 || j > jw1) continue;  // no row of this wave owns block j
+    // key tiles that hold a key not after this wave's last token
+    const int kt_n = j < jw1 ? KT : ((sh.q0 + tw1 - j * BS) >> 5) + 1;
+    int ko = 0;
+    __asm__ volatile("" : "+v"(ko));
+    const char* kvl = lds + ko;
+    f32x16_t sc[KT];
 #pragma unroll
-  for (int s0 = 0; s0 < 32; s0 += 8) {
-    if (s0 >= n) break;
-    u32x4_t val[8];
+    for (int kt = 0; kt < KT; ++kt) {
+      sc[kt] = f32x16_t{};
+      if (kt < kt_n) {
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
-      if (s0 + s < n)
-        val[s] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4_t*>(part_o + ((base + s0 + s) * sh.r + h) * kHeadDim + 8 * c16));
+        for (int ks = 0; ks < 8; ++ks) sc[kt] = mfma32x32x16(k_frag(kvl, kt, ks, lane), qf[ks], sc[kt]);
+      }
+    }
+    // visible: the row's own block, keys not after the query (the lane-half
+    // term of the key index moved to the right-hand side)
+    const int lim = jo == j ? pos - j * BS - 4 * hf : -64;
+    float mx = -__builtin_inff();
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      if (s0 + s < n) {
-        const float wgt = fast_exp2(m[s0 + s] - M);
-        W = fmaf(wgt, l[s0 + s], W);
+    for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc[2 * e] = fmaf(wgt, bf16_lo(val[s][e]), acc[2 * e]);
-          acc[2 * e + 1] = fmaf(wgt, bf16_hi(val[s][e]), acc[2 * e + 1]);
+      for (int i = 0; i < 16; ++i) {
+        if (kt >= kt_n || 32 * kt + c_row(i, 0) > lim) sc[kt][i] = -__builtin_inff();
+        mx = fmaxf(mx, sc[kt][i]);
+      }
+    const float m_new = fmaxf(m, wave_max_pair(mx) * c2);
+    const float m_use = m_new == -__builtin_inff() ? 0.f : m_new;  // a row with no key yet
+    const float alpha = fast_exp2(m - m_use);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+    int vo = 0;
+    __asm__ volatile("" : "+v"(vo));
+    const char* kvt = lds + vo;
+    float sum = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      if (kt < kt_n) {
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          uint32_t dh[4], dl[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float p0 = fast_exp2(fmaf(sc[kt][8 * h2 + 2 * e], c2, -m_use));
+            const float p1 = fast_exp2(fmaf(sc[kt][8 * h2 + 2 * e + 1], c2, -m_use));
+            sum += p0 + p1;
+            dh[e] = pack_bf16x2(p0, p1);
+            dl[e] = pack_bf16x2(p0 - bf16_lo(dh[e]), p1 - bf16_hi(dh[e]));
+          }
+          const u32x4_t ph = u32x4_t{dh[0], dh[1], dh[2], dh[3]};
+          const u32x4_t pl = u32x4_t{dl[0], dl[1], dl[2], dl[3]};
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) {
+            const u32x4_t a = vt_frag<BS>(kvt, dt, kt, h2, lane);
+            o[dt] = mfma32x32x16(a, ph, o[dt]);
+            o[dt] = mfma32x32x16(a, pl, o[dt]);
+          }
         }
       }
     }
+    l = fmaf(l, alpha, wave_sum_pair(sum));
+    m = m_new;
+  }
+
+  // ---- merge: the row's other partials (slots 0 .. nv - 1; the own block
+  // is slot nv), four at a time, each lane reading its row's half (the
+  // values o[dt][i], positions 64 hf + 16 dt + i); the running max M moves
+  // up per batch
+  const int nv = live ? min(K - 1, jo) : 0;
+  const int nvw = wave_live ? min(K - 1, jw1) : 0;  // the most any row of the wave has
+  const size_t pbase = ((size_t)(u - pass.u0) * pass.pass_tokens + (tc - pass.t0)) * K;
+  const u32x4_t* pob = reinterpret_cast<const u32x4_t*>(part_o) + (pbase * 16 + hf) * sh.r + head;
+  const float2* pml = part_ml + pbase * sh.r + head;
+  const size_t slot_pieces = (size_t)16 * sh.r;
+  float M = m;  // finite: key 0 of the own block is visible to every row
+  float W = l;
+  constexpr int kB = 4;
+#pragma unroll
+  for (int s0 = 0; s0 < kMaxOther; s0 += kB) {
+    if (s0 >= nvw) break;
+    u32x4_t val[kB][8];
+    f32x2_t ml[kB];
+#pragma unroll
+    for (int s = 0; s < kB; ++s) {
+      ml[s] = f32x2_t{-__builtin_inff(), 0.f};
+      if (s0 + s < nv) {
+        ml[s] = __builtin_nontemporal_load(reinterpret_cast<const f32x2_t*>(pml + (size_t)(s0 + s) * sh.r));
+        const u32x4_t* src = pob + (size_t)(s0 + s) * slot_pieces;
+#pragma unroll
+        for (int mm = 0; mm < 8; ++mm) val[s][mm] = __builtin_nontemporal_load(src + (size_t)(2 * mm) * sh.r);
+      }
+    }
+    float Mn = M;
+#pragma unroll
+    for (int s = 0; s < kB; ++s) Mn = fmaxf(Mn, ml[s].x);
+    const float a = fast_exp2(M - Mn);
+    W *= a;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[dt][i] *= a;
+#pragma unroll
+    for (int s = 0; s < kB; ++s)
+      if (s0 + s < nv) {
+        const float wgt = fast_exp2(ml[s].x - Mn);
+        W = fmaf(wgt, ml[s].y, W);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[dt][i] = fmaf(wgt, bf16_at(val[s][2 * dt + (i >> 3)], i & 7), o[dt][i]);
+      }
+    M = Mn;
   }
   const float inv = 1.0f / W;
-  if (sh.lse != nullptr && c16 == 0)
-    sh.lse[((size_t)b * sh.q_stride + t) * sh.Hq + g * sh.r + h] = (M + fast_log2(W)) * 0.6931471805599453f;
-  // stored positions 8 * c16 .. + 7 = lane half hf, tile dt, i0 .. i0 + 7
-  const int p0 = 8 * c16;
-  const int hfp = p0 >> 6, dt = (p0 >> 4) & 3, i0 = p0 & 15;
-  const int d0 = 32 * dt + 8 * (i0 >> 2) + 4 * hfp;
-  uint16_t* orow = out + (((size_t)b * sh.q_stride + t) * sh.Hq + g * sh.r + h) * kHeadDim;
-  u32x2_t w0, w1;
-  w0.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-  w0.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
-  w1.x = pack_bf16x2(acc[4] * inv, acc[5] * inv);
-  w1.y = pack_bf16x2(acc[6] * inv, acc[7] * inv);
+  if (live && sh.lse != nullptr && hf == 0) sh.lse[orow] = (M + fast_log2(W)) * 0.6931471805599453f;
+  // O goes out through LDS (every wave is past its last K/V read at the
+  // barrier): each lane writes its 64 values, head dims 32 dt + 8 q4 + 4 hf
+  // + 0..3, into the tile's row-major copy, and the stores then cover whole
+  // rows, a token's r heads being consecutive rows of out.  (Stored straight
+  // from the lanes, every store instruction touched a sliver of 64 rows:
+  // measured on MI355X, the 1M prefill's merge took twice as long.)
+  __syncthreads();
+  char* ob = lds + qr * kMergeRowBytes;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      u32x2_t wv;
+      wv.x = pack_bf16x2(o[dt][4 * q4 + 0] * inv, o[dt][4 * q4 + 1] * inv);
+      wv.y = pack_bf16x2(o[dt][4 * q4 + 2] * inv, o[dt][4 * q4 + 3] * inv);
+      *reinterpret_cast<u32x2_t*>(ob + 2 * (32 * dt + 8 * q4 + 4 * hf)) = wv;
+    }
+  __syncthreads();
   // O is not read again by the prefill: non-temporal stores keep it from
   // lingering dirty in the caches (a decode right after a 32K prefill:
-  // 48.5 -> 46.5 us on MI355X; the same hint on the partials, which the
-  // merge reads back, made the prefill 3x slower)
-  __builtin_nontemporal_store(w0, reinterpret_cast<u32x2_t*>(orow + d0));
-  __builtin_nontemporal_store(w1, reinterpret_cast<u32x2_t*>(orow + d0 + 8));
+  // 48.5 -> 46.5 us on MI355X)
+#pragma unroll
+  for (int it = 0; it < kMergeRows * 16 / 256; ++it) {
+    const int piece = (int)threadIdx.x + 256 * it;
+    const int row = piece >> 4;
+    const int tk = t_a + (row >> r_log2);
+    if (tk <= t_z) {
+      const u32x4_t val = *reinterpret_cast<const u32x4_t*>(lds + row * kMergeRowBytes + 16 * (piece & 15));
+      uint16_t* dst = out + (((size_t)b * sh.q_stride + tk) * sh.Hq + g * sh.r + (row & (sh.r - 1))) * kHeadDim +
+                      8 * (piece & 15);
+      __builtin_nontemporal_store(val, reinterpret_cast<u32x4_t*>(dst));
+    }
+  }
 }
 
 template <int BS>
@@ -878,15 +972,33 @@ hipError_t launch_attend(const PrefillShape& sh, const PassInfo& pass, const uin
   }
 }
 
-hipError_t launch_merge(const PrefillShape& sh, const PassInfo& pass, const uint16_t* part_o,
-                        const float2* part_ml, uint16_t* out, hipStream_t st) {
+hipError_t launch_merge(const PrefillShape& sh, const PassInfo& pass, const uint16_t* q, const uint16_t* k,
+                        const uint16_t* v, const uint16_t* part_o, const float2* part_ml, uint16_t* out,
+                        hipStream_t st) {
   int r_log2 = 0;
   while ((1 << r_log2) < sh.r) ++r_log2;
-  const int t_first = pass.t0;
-  if (t_first >= pass.t1) return hipSuccess;
-  const long threads = (long)(pass.t1 - t_first) * sh.r * 16;
-  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)((threads + 255) / 256), pass.u1 - pass.u0), dim3(256), 0, st,
-                     part_o, part_ml, out, sh, pass, t_first, r_log2);
+  if (pass.t0 >= pass.t1 || pass.u0 >= pass.u1) return hipSuccess;
+  const int tpt = kMergeRows >> r_log2;
+  const int n_tiles = (pass.t1 - pass.t0 + tpt - 1) / tpt;
+  const dim3 grid((unsigned)((n_tiles + 63) / 64 * 64), (unsigned)(pass.u1 - pass.u0));
+  switch (sh.bs) {
+#define MSA_MERGE_LAUNCH(BS_)                                                                                     \
+  {                                                                                                               \
+    const hipError_t attr =                                                                                       \
+        ensure_dynamic_lds(reinterpret_cast<const void*>(&merge_kernel<BS_>), merge_lds_bytes<BS_>());           \
+    if (attr != hipSuccess) return attr;                                                                          \
+    hipLaunchKernelGGL((merge_kernel<BS_>), grid, dim3(256), merge_lds_bytes<BS_>(), st, q, k, v, part_o, part_ml, \
+                       out, sh, pass, r_log2, n_tiles);                                                           \
+    break;                                                                                                        \
+  }
+    case 32:
+      MSA_MERGE_LAUNCH(32)
+    case 64:
+      MSA_MERGE_LAUNCH(64)
+    default:
+      MSA_MERGE_LAUNCH(128)
+#undef MSA_MERGE_LAUNCH
+  }
   return hipGetLastError();
 }
 

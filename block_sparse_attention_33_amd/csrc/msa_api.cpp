@@ -416,11 +416,11 @@ int run_prefill(const Dims& dc, long q0, long n_q, const Strides& str, const uin
   }
   MSA_LAUNCH_NAMED("index_topk", s, msa::launch_index_topk_at(q_idx, bkeys, sel_use, U, S, iq0, (int)str.qi_rows,
                                                                sel_stride, nb, bs, K, s));
-  MSA_LAUNCH_NAMED("chunk_hist", s, msa::launch_chunk_hist(sel_use, hist, U, S, nb, bs, K, cp, iq0, s));
+  MSA_LAUNCH_NAMED("chunk_hist", s, msa::launch_chunk_hist(sel_use, hist, U, S, nb, bs, K, cp, iq0, false, s));
   MSA_LAUNCH_NAMED("chunk_total", s, msa::launch_chunk_total(hist, counts, U, nb, cp, s));
   MSA_LAUNCH_NAMED("scan", s, msa::launch_scan(counts, row_ptr, item_ptr, (int)P.rows, tpi, s));
   MSA_LAUNCH_NAMED("offsets_items", s, msa::launch_offsets_items(hist, row_ptr, item_ptr, items, U, nb, cp, tpi, s));
-  MSA_LAUNCH_NAMED("scatter", s, msa::launch_scatter(sel_use, hist, entries, U, S, nb, bs, K, cp, iq0, s));
+  MSA_LAUNCH_NAMED("scatter", s, msa::launch_scatter(sel_use, hist, entries, U, S, nb, bs, K, cp, iq0, false, s));
   msa::PrefillShape sh;
   sh.B = (int)d.B;
   sh.S = S;
@@ -451,7 +451,7 @@ int run_prefill(const Dims& dc, long q0, long n_q, const Strides& str, const uin
     const long max_items = (u1 - u0) * P.max_items_per_range;
     MSA_LAUNCH_NAMED("attend", s, msa::launch_attend(sh, ps, q, k, v, row_ptr, item_ptr, items, entries, part_o,
                                                      part_ml, sched, (int)max_items, s));
-    MSA_LAUNCH_NAMED("merge", s, msa::launch_merge(sh, ps, part_o, part_ml, out, s));
+    MSA_LAUNCH_NAMED("merge", s, msa::launch_merge(sh, ps, q, k, v, part_o, part_ml, out, s));
     return MSA_OK;
   };
   for (long u0 = 0; u0 < d.U; u0 += upp) {
@@ -903,12 +903,12 @@ int msa_prefill_backward(const msa_dims* dims, const uint16_t* q, const uint16_t
     const int tpi = (int)P.tokens_per_item;
     const int32_t* psel = sel + q0 * K;
     const int iq0 = (int)q0, in_q = (int)n_q;
-    MSA_LAUNCH_NAMED("chunk_hist", s, msa::launch_chunk_hist(psel, hist, U, in_q, nb, bs, K, cp, iq0, s));
+    MSA_LAUNCH_NAMED("chunk_hist", s, msa::launch_chunk_hist(psel, hist, U, in_q, nb, bs, K, cp, iq0, true, s));
     MSA_LAUNCH_NAMED("chunk_total", s, msa::launch_chunk_total(hist, counts, U, nb, cp, s));
     MSA_LAUNCH_NAMED("scan", s, msa::launch_scan(counts, row_ptr, item_ptr, (int)P.rows, tpi, s));
     MSA_LAUNCH_NAMED("offsets_items", s,
                      msa::launch_offsets_items(hist, row_ptr, item_ptr, items, U, nb, cp, tpi, s));
-    MSA_LAUNCH_NAMED("scatter", s, msa::launch_scatter(psel, hist, entries, U, in_q, nb, bs, K, cp, iq0, s));
+    MSA_LAUNCH_NAMED("scatter", s, msa::launch_scatter(psel, hist, entries, U, in_q, nb, bs, K, cp, iq0, true, s));
     sh.q0 = iq0;
     sh.n_q = in_q;
     MSA_LAUNCH_NAMED("bwd_kv", s,

@@ -70,13 +70,15 @@ hipError_t launch_fill_i32(int32_t* p, int32_t value, size_t n, hipStream_t st);
 // tokens is cut into m chunks of tpc tokens (n_chunks = n_ranges * m per
 // unit); H [U, n_chunks, nb] int32 holds per-chunk block counts, then (in
 // place) each chunk's first position in its (unit, range, block) list.
-//   chunk_hist:    sel -> H (counts of kept blocks, the own block included)
+//   chunk_hist:    sel -> H (counts of kept blocks, the own block only if
+//                  with_own)
 //   chunk_total:   H -> counts [U * n_ranges * nb]
 //   scan:          counts -> row_ptr [n + 1], item_ptr [n + 1] (exclusive),
 //                  items of a row = ceil(count / tokens_per_item)
 //   offsets_items: H -> chunk offsets (in place); item list {row id, first entry}
 //   scatter:       entries[...] = (t << 5) | slot for every kept block (the
-//                  own block sits at slot min(top_k - 1, t / block_size))
+//                  own block sits at slot min(top_k - 1, t / block_size) and
+//                  is listed only if with_own)
 constexpr int kMaxInvertBlocks = 36864;  // nb limit: LDS histogram of nb int32
 struct ChunkPlan {
   int T, m, tpc, n_chunks, n_ranges;
@@ -84,7 +86,7 @@ struct ChunkPlan {
 };
 // (query rows are tokens q0 .. q0 + S - 1)
 hipError_t launch_chunk_hist(const int32_t* sel, int32_t* H, int units, int S, int nb, int bs, int top_k,
-                             const ChunkPlan& cp, int q0, hipStream_t st);
+                             const ChunkPlan& cp, int q0, bool with_own, hipStream_t st);
 hipError_t launch_chunk_total(const int32_t* H, int32_t* counts, int units, int nb, const ChunkPlan& cp,
                               hipStream_t st);
 hipError_t launch_scan(const int32_t* counts, int32_t* row_ptr, int32_t* item_ptr, int n,
@@ -92,14 +94,14 @@ hipError_t launch_scan(const int32_t* counts, int32_t* row_ptr, int32_t* item_pt
 hipError_t launch_offsets_items(int32_t* H, const int32_t* row_ptr, const int32_t* item_ptr, int2* items,
                                 int units, int nb, const ChunkPlan& cp, int tokens_per_item, hipStream_t st);
 hipError_t launch_scatter(const int32_t* sel, const int32_t* H, uint32_t* entries, int units, int S, int nb,
-                          int bs, int top_k, const ChunkPlan& cp, int q0, hipStream_t st);
+                          int bs, int top_k, const ChunkPlan& cp, int q0, bool with_own, hipStream_t st);
 
 // Main branch: one work item = one KV block of a (unit, range) row and up to
-// kItemChunks chunks of kItemRows gathered query rows (the query's own block
-// included); writes unnormalised bf16 partials + (running max, sum) in base-2
-// units per (token, selection slot, head).  A row with a single partial
-// stores it normalised with a sum of 1.  Items [item_ptr[row_begin],
-// item_ptr[row_end]).
+// kItemChunks chunks of kItemRows gathered query rows (the lists hold the
+// blocks before each query's own); writes unnormalised bf16 partials +
+// (running max, sum) in base-2 units per (token, selection slot, head), the
+// 16-byte pieces of a (token, slot)'s heads interleaved.  Items
+// [item_ptr[row_begin], item_ptr[row_end]).
 // Chunks per work item: more chunks load a block's K/V for fewer items
 // (measured on MI355X against 4: the 32K prefill 2.3 %, the structured 128K
 // 3.4 %, the 1M 0.8 % faster; 8 was slower at 32K and 128K), and the LDS
@@ -119,9 +121,11 @@ hipError_t launch_attend(const PrefillShape& sh, const PassInfo& pass, const uin
 hipError_t launch_dense(const PrefillShape& sh, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         uint16_t* out, int32_t* sel, int sel_rows, hipStream_t st);
 
-// Merge of every partial of the pass's query rows -> out.
-hipError_t launch_merge(const PrefillShape& sh, const PassInfo& pass, const uint16_t* part_o,
-                        const float2* part_ml, uint16_t* out, hipStream_t st);
+// Attention of the pass's query rows over their own blocks, merged with
+// every other partial of the rows -> out (and lse when sh.lse is set).
+hipError_t launch_merge(const PrefillShape& sh, const PassInfo& pass, const uint16_t* q, const uint16_t* k,
+                        const uint16_t* v, const uint16_t* part_o, const float2* part_ml, uint16_t* out,
+                        hipStream_t st);
 
 // Backward of the main branch (selection fixed).
 struct BwdShape {
