@@ -45,17 +45,19 @@ def _say(*a):
 
 def _prefill_counts(w):
     """Algorithmic work of one prefill: attended keys summed over queries
-    (per query head) and the (query row, kept block) pairs, own block
-    included."""
+    (per query head), the part of them in blocks before each query's own
+    (the attention kernel's share; the own block's keys go to the merge
+    kernel), and the (query row, earlier kept block) pairs."""
     import numpy as np
     t = np.arange(w.seq_len, dtype=np.int64)
     own = t // w.block_size
-    kept = np.minimum(w.top_k - 1, own)
-    keys = kept * w.block_size + (t % w.block_size) + 1
+    kept = np.minimum(w.top_k - 1, own)   # kept blocks before the own one
+    earlier_keys = kept * w.block_size
+    keys = earlier_keys + (t % w.block_size) + 1
     per_head_keys = int(keys.sum()) * w.batch
-    pairs = int((kept + 1).sum()) * w.batch * w.n_q_heads
-    rows_merged = int((own > 0).sum()) * w.batch * w.n_q_heads   # rows with partials to merge
-    return per_head_keys, pairs, rows_merged
+    per_head_earlier = int(earlier_keys.sum()) * w.batch
+    pairs = int(kept.sum()) * w.batch * w.n_q_heads
+    return per_head_keys, per_head_earlier, pairs
 
 
 def _flop_alg(w):
@@ -592,23 +594,28 @@ def main():
     msa.profile_enable(False)
     dkt = msa.profile_read()
 
-    per_head_keys, pairs, rows_merged = _prefill_counts(wp)
+    per_head_keys, per_head_earlier, pairs = _prefill_counts(wp)
     D = wp.head_dim
     flop_alg = 4.0 * D * wp.n_q_heads * per_head_keys
+    flop_att = 4.0 * D * wp.n_q_heads * per_head_earlier   # the attention kernel's share
     tokens = wp.batch * wp.seq_len
+    rows = tokens * wp.n_q_heads
     # dominant kernel: the attention kernel (all kept blocks of every query),
     # one launch per query chunk
     n_att, att_ms = kt.get("attend", (0, 0.0))
     att_ms_step = att_ms / args.steps
     att_launch_ms = att_ms / max(1, n_att)
     launches_per_step = max(1, n_att // args.steps)
-    att_tflops = flop_alg / (att_ms_step * 1e-3) / 1e12 if att_ms_step > 0 else None
-    # bytes the KV-outer design moves: per (query row, kept block) pair a
-    # gathered Q row (256 B) and a bf16 partial + fp32 (max, sum) (264 B)
+    att_tflops = flop_att / (att_ms_step * 1e-3) / 1e12 if att_ms_step > 0 else None
+    # bytes the KV-outer design moves: per (query row, earlier kept block)
+    # pair a gathered Q row (256 B) and a bf16 partial + fp32 (max, sum)
+    # (264 B); the merge reads the partials back and, per row, Q (256 B) for
+    # the own block and writes O (256 B) (the own blocks' K and V, 64 KB per
+    # 1024 rows at the headline's shape, come mostly from L2 and are left out)
     att_design_bytes = pairs * (2 * D + 2 * D + 8)
     n_mrg, mrg_ms = kt.get("merge", (0, 0.0))
     mrg_ms_step = mrg_ms / args.steps
-    mrg_design_bytes = (pairs - (tokens * wp.n_q_heads - rows_merged)) * (2 * D + 8) + rows_merged * 2 * D
+    mrg_design_bytes = pairs * (2 * D + 8) + rows * (2 * D + 2 * D)
     dbytes = _decode_bytes(wd)
     traffic = _measured_traffic() if headline == HEADLINE else None
 
@@ -647,8 +654,8 @@ def main():
             "timing": "right after the 1M prefill in the same stream",
         },
         "roofline": {
-            "kernel": "attend_kernel<128, true> (KV-outer block attention, all kept blocks of one query chunk; "
-                      "the instance taking runs of items from a counter, used at 1M)",
+            "kernel": "attend_kernel<128, true> (KV-outer block attention over the kept blocks before each "
+                      "query's own, one query chunk; the instance taking runs of items from a counter, used at 1M)",
             "workload": headline,
             "bound": "mfma",
             "achieved": round(att_tflops, 2) if att_tflops else None,
@@ -658,7 +665,7 @@ def main():
             "traffic": traffic,
             "avg_launch_ms": round(att_launch_ms, 4),
             "launches_per_step": launches_per_step,
-            "flop_per_launch": flop_alg / launches_per_step,
+            "flop_per_launch": flop_att / launches_per_step,
             "design_bytes_per_step": att_design_bytes,
             "design_hbm_gbs": round(att_design_bytes / (att_ms_step * 1e-3) / 1e9, 1) if att_ms_step else None,
             # the same kernel against the HBM roof, with the bytes the KV-outer
@@ -671,7 +678,9 @@ def main():
             if (traffic and att_launch_ms) else None,
         },
         "merge_kernel": {
+            "what": "own block's causal attention + log-sum-exp merge of every row's partials",
             "ms_per_step": round(mrg_ms_step, 4),
+            "own_block_flop": flop_alg - flop_att,
             "design_bytes": mrg_design_bytes,
             "hbm_gbs": round(mrg_design_bytes / (mrg_ms_step * 1e-3) / 1e9, 1) if mrg_ms_step else None,
         },

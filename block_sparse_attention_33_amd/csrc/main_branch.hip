@@ -799,6 +799,7 @@ __global__ __launch_bounds__(512 / NCT, 1) void dense_kernel(const uint16_t* __r
   // NCT column tiles of 32 rows per wave, 8 / NCT waves per tile of 256 rows
   constexpr int KT = Tile<BS>::KT;
   constexpr int NT = 512 / NCT;
+  static_assert(2 * Tile<BS>::kLdsBytes >= 128 * kMergeRowBytes, "half a tile of O must fit the K/V buffers");
   extern __shared__ __align__(16) char lds[];  // two K/V buffers
   const int tpt = kItemRows >> r_log2;          // tokens per tile
   const int n_tiles = (sh.S + tpt - 1) / tpt;
@@ -920,24 +921,49 @@ __global__ __launch_bounds__(512 / NCT, 1) void dense_kernel(const uint16_t* __r
     __syncthreads();
   }
 
-  // O = o / l, head dims 32 dt + 8 q4 + 4 hf + 0..3 of this lane's row
+  // O = o / l, out through LDS in two halves of 128 rows (the loop's last
+  // barrier freed it): each lane writes its values, head dims 32 dt + 8 q4 +
+  // 4 hf + 0..3, into a row-major copy, and the stores then cover whole rows
+  // (a token's r heads are consecutive rows of out)
+  float inv[NCT];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
-    if (tok[ct] >= sh.S) continue;
-    const float inv = 1.0f / l[ct];
-    if (sh.lse != nullptr && hf == 0)
+    inv[ct] = 1.0f / l[ct];
+    if (sh.lse != nullptr && hf == 0 && tok[ct] < sh.S)
       sh.lse[((size_t)b * sh.q_stride + tok[ct]) * sh.Hq + g * sh.r + head[ct]] =
           (m[ct] + fast_log2(l[ct])) * 0.6931471805599453f;
-    uint16_t* orow = out + (((size_t)b * sh.q_stride + tok[ct]) * sh.Hq + g * sh.r + head[ct]) * kHeadDim;
+  }
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+  for (int half = 0; half < 2; ++half) {
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        u32x2_t wv;
-        wv.x = pack_bf16x2(o[ct][dt][4 * q4 + 0] * inv, o[ct][dt][4 * q4 + 1] * inv);
-        wv.y = pack_bf16x2(o[ct][dt][4 * q4 + 2] * inv, o[ct][dt][4 * q4 + 3] * inv);
-        *reinterpret_cast<u32x2_t*>(orow + 32 * dt + 8 * q4 + 4 * hf) = wv;
+    for (int ct = 0; ct < NCT; ++ct) {
+      const int qr = 32 * (NCT * w + ct) + (lane & 31);
+      if ((qr >> 7) == half) {
+        char* ob = lds + (qr & 127) * kMergeRowBytes;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            u32x2_t wv;
+            wv.x = pack_bf16x2(o[ct][dt][4 * q4 + 0] * inv[ct], o[ct][dt][4 * q4 + 1] * inv[ct]);
+            wv.y = pack_bf16x2(o[ct][dt][4 * q4 + 2] * inv[ct], o[ct][dt][4 * q4 + 3] * inv[ct]);
+            *reinterpret_cast<u32x2_t*>(ob + 2 * (32 * dt + 8 * q4 + 4 * hf)) = wv;
+          }
       }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 128 * 16 / NT; ++it) {
+      const int piece = (int)threadIdx.x + NT * it;
+      const int qr = 128 * half + (piece >> 4);
+      const int tk = t0 + (qr >> r_log2);
+      if (tk < sh.S) {
+        const u32x4_t val = *reinterpret_cast<const u32x4_t*>(lds + (piece >> 4) * kMergeRowBytes + 16 * (piece & 15));
+        *reinterpret_cast<u32x4_t*>(out + (((size_t)b * sh.q_stride + tk) * sh.Hq + g * sh.r + (qr & (sh.r - 1))) *
+                                              kHeadDim + 8 * (piece & 15)) = val;
+      }
+    }
+    __syncthreads();
   }
 }
 
