@@ -21,7 +21,7 @@ from ._lib import (MSA_OP_BACKWARD, MSA_OP_DECODE, MSA_OP_INDEX, MSA_OP_POOL, MS
 __all__ = [
     "MsaError", "make_dims", "profile_enable", "profile_read", "msa_workspace_bytes", "msa_backward_pass_rows", "msa_prefill_chunk_workspace_bytes", "msa_plan_check",
     "msa_pool_block_keys", "msa_index_select",
-    "msa_prefill", "msa_prefill_varlen", "msa_prefill_switched", "msa_prefill_lse", "msa_prefill_backward", "msa_prefill_chunk", "msa_decode", "msa_decode_noalloc", "msa_decode_init", "msa_decode_step", "MSA_OP_POOL", "MSA_OP_INDEX", "MSA_OP_PREFILL", "MSA_OP_DECODE", "MSA_OP_BACKWARD",
+    "msa_prefill", "msa_prefill_varlen", "msa_prefill_switched", "msa_prefill_lse", "msa_prefill_backward", "msa_prefill_chunk", "msa_prefill_chunk_varlen", "msa_decode", "msa_decode_noalloc", "msa_decode_init", "msa_decode_step", "MSA_OP_POOL", "MSA_OP_INDEX", "MSA_OP_PREFILL", "MSA_OP_DECODE", "MSA_OP_BACKWARD",
 ]
 
 
@@ -495,4 +495,53 @@ def msa_prefill_chunk(q, q_idx, k_cache, v_cache, k_idx, block_keys, start: int,
     _check(_lib.load().msa_prefill_chunk(ctypes.byref(dims), int(start), int(T), _ptr(q), _ptr(q_idx),
                                          _ptr(k_cache), _ptr(v_cache), _ptr(k_idx), _ptr(block_keys), _ptr(out),
                                          _ptr(sel), _ptr(ws), ws_bytes, _stream(dev)), "msa_prefill_chunk")
+    return (out, sel) if return_sel else out
+
+
+def msa_prefill_chunk_varlen(q, q_idx, k_cache, v_cache, k_idx, block_keys, starts, counts, block_size: int,
+                             top_k: int, softmax_scale: float = 0.0, out=None, sel=None, return_sel: bool = False,
+                             workspace=None):
+    """Each sequence b of the caches (k_cache/v_cache [B, G, C, D] bf16, k_idx
+    [B, G, C, di] int8, block_keys [B, G, ceil(C/bs), di] int8) adds counts[b]
+    queries at positions starts[b] .. starts[b] + counts[b] - 1; the queries
+    are packed along the token axis in sequence order: q [T, Hq, D], q_idx
+    [G, T, di] with T = sum(counts) -> out [T, Hq, D] bf16 (and sel [G, T,
+    top_k] when return_sel).  starts, counts: host lists or CPU tensors."""
+    _need(q, "q", torch.bfloat16, 3)
+    dev = q.device
+    _need(q_idx, "q_idx", torch.int8, 3, dev)
+    _need(k_cache, "k_cache", torch.bfloat16, 4, dev)
+    _need(v_cache, "v_cache", torch.bfloat16, 4, dev)
+    _need(k_idx, "k_idx", torch.int8, 4, dev)
+    _need(block_keys, "block_keys", torch.int8, 4, dev)
+    T, Hq, D = q.shape
+    B, G, C, _ = k_cache.shape
+    di = q_idx.shape[2]
+    st = [int(x) for x in (starts.tolist() if isinstance(starts, torch.Tensor) else starts)]
+    ct = [int(x) for x in (counts.tolist() if isinstance(counts, torch.Tensor) else counts)]
+    if len(st) != B or len(ct) != B or sum(ct) != T:
+        raise ValueError("starts and counts need one entry per sequence, and the counts must sum to q.shape[0]")
+    if k_cache.shape != (B, G, C, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache/v_cache must be [B, G, C, D]")
+    if q_idx.shape != (G, T, di) or k_idx.shape != (B, G, C, di):
+        raise ValueError("q_idx must be [G, T, di] and k_idx [B, G, C, di]")
+    if block_keys.shape != (B, G, -(-C // block_size), di):
+        raise ValueError("block_keys must be [B, G, ceil(C/bs), di]")
+    dims = make_dims(B, C, Hq, G, block_size, top_k, head_dim=D, idx_dim=di, softmax_scale=softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16, 3, dev)
+    if sel is None and return_sel:
+        sel = torch.empty((G, T, top_k), dtype=torch.int32, device=dev)
+    if sel is not None:
+        _need(sel, "sel", torch.int32, 3, dev)
+    one = make_dims(1, C, Hq, G, block_size, top_k, head_dim=D, idx_dim=di, softmax_scale=softmax_scale)
+    lo, hi = msa_prefill_chunk_workspace_bytes(one, max(1, max(ct)))
+    ws, ws_bytes = _workspace(MSA_OP_PREFILL, dims, dev, workspace, sizes=(lo, hi))
+    st_arr = (ctypes.c_int32 * B)(*st)
+    ct_arr = (ctypes.c_int32 * B)(*ct)
+    _check(_lib.load().msa_prefill_chunk_varlen(ctypes.byref(dims), st_arr, ct_arr, _ptr(q), _ptr(q_idx),
+                                                _ptr(k_cache), _ptr(v_cache), _ptr(k_idx), _ptr(block_keys),
+                                                _ptr(out), _ptr(sel), _ptr(ws), ws_bytes, _stream(dev)),
+           "msa_prefill_chunk_varlen")
     return (out, sel) if return_sel else out

@@ -619,7 +619,7 @@ const char* msa_status_string(int status) {
   }
 }
 
-int msa_version(void) { return 10500; }
+int msa_version(void) { return 10600; }
 
 int msa_backward_pass_rows(const msa_dims* dims, size_t ws_bytes, int32_t* rows) {
   Dims d;
@@ -948,6 +948,53 @@ int msa_prefill_chunk(const msa_dims* dims, int32_t start, int32_t count, const 
   if (d.nb > msa::kMaxInvertBlocks) return MSA_ERR_UNSUPPORTED;
   return run_prefill(d, start, count, Strides{count, d.S, count, count}, q, k_cache, v_cache, q_idx, k_idx,
                      block_keys, out, sel, nullptr, ws, ws_bytes, (hipStream_t)stream);
+}
+
+int msa_prefill_chunk_varlen(const msa_dims* dims, const int32_t* starts, const int32_t* counts, const uint16_t* q,
+                             const int8_t* q_idx, const uint16_t* k_cache, const uint16_t* v_cache,
+                             const int8_t* k_idx, int8_t* block_keys, uint16_t* out, int32_t* sel, void* ws,
+                             size_t ws_bytes, void* stream) {
+  Dims d;
+  int st = check_dims(dims, &d);
+  if (st != MSA_OK) return st;
+  if (d.k > kMaxSparseTopK) return MSA_ERR_UNSUPPORTED;
+  if (!starts || !counts || !q || !q_idx || !k_cache || !v_cache || !k_idx || !block_keys || !out)
+    return MSA_ERR_INVALID_ARG;
+  if (d.nb > msa::kMaxInvertBlocks) return MSA_ERR_UNSUPPORTED;
+  long T = 0;
+  for (long b = 0; b < d.B; ++b) {
+    if (starts[b] < 0 || counts[b] < 0 || (long)starts[b] + counts[b] > d.S) return MSA_ERR_INVALID_ARG;
+    T += counts[b];
+  }
+  if (T < 1) return MSA_ERR_INVALID_ARG;
+  if ((long)d.G * T * d.k >= (1L << 31) || T >= (1L << 30)) return MSA_ERR_UNSUPPORTED;
+  // one sequence at a time: a batch of one against its cache of capacity C
+  Dims d1 = d;
+  d1.B = 1;
+  d1.U = d.G;
+  // every sequence's plan is checked before the first launch
+  for (long b = 0; b < d.B; ++b) {
+    if (counts[b] == 0) continue;
+    st = check_ws(ws, ws_bytes, 1);
+    if (st != MSA_OK) return st;
+    ChunkRun run;
+    st = plan_chunk(d1, counts[b], ws_bytes, &run);
+    if (st != MSA_OK) return st;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  const size_t cache_rows = (size_t)d.G * d.S;  // rows of one sequence's cache
+  long o = 0;                                   // packed row of the sequence's first query
+  for (long b = 0; b < d.B; ++b) {
+    const long n = counts[b];
+    if (n == 0) continue;
+    st = run_prefill(d1, starts[b], n, Strides{n, d.S, T, T}, q + o * d.Hq * d.D, k_cache + b * cache_rows * d.D,
+                     v_cache + b * cache_rows * d.D, q_idx + o * d.di, k_idx + b * cache_rows * d.di,
+                     block_keys + (size_t)b * d.G * d.nb * d.di, out + o * d.Hq * d.D, sel ? sel + o * d.k : nullptr,
+                     nullptr, ws, ws_bytes, s);
+    if (st != MSA_OK) return st;
+    o += n;
+  }
+  return MSA_OK;
 }
 
 int msa_decode(const msa_dims* dims, const uint16_t* q, const int8_t* q_idx, const uint16_t* k_cache,

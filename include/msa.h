@@ -259,6 +259,37 @@ int msa_prefill_chunk(const msa_dims* dims, int32_t start, int32_t count, const 
                       const int8_t* k_idx, int8_t* block_keys, uint16_t* out, int32_t* sel, void* ws,
                       size_t ws_bytes, void* stream);
 
+/* Ragged chunked prefill: each of the dims->batch sequences adds its own
+ * chunk of queries against its own cache, so prompts of uneven lengths that
+ * arrive piece by piece share one call (the pages serve prompts of up to 1M
+ * tokens side by side: "深度解析 MiniMax-M3：稀疏注意力机制、基准测试与 API 集成指南",
+ * section "技术细节").
+ *
+ * starts, counts: HOST int32 [batch].  Sequence b adds the counts[b] queries
+ * at positions starts[b] .. starts[b] + counts[b] - 1 (counts[b] = 0: the
+ * sequence is skipped); 0 <= starts[b], starts[b] + counts[b] <= C =
+ * dims->seq_len (the caches' capacity), T = sum of counts >= 1.  The caches
+ * are laid out as for msa_prefill_chunk, one per sequence: k_cache, v_cache
+ * [B, G, C, D] bf16 and k_idx [B, G, C, di] int8 already hold each
+ * sequence's tokens 0 .. starts[b] + counts[b] - 1; block_keys [B, G,
+ * ceil(C / block_size), di] int8 holds the summaries of its blocks before
+ * starts[b] / block_size and receives those of the blocks its new tokens
+ * fall in.  The queries are packed along the token axis in sequence order
+ * (sequence b's rows start at the sum of the counts before it):
+ *   q, out       [T, Hq, D]     bf16
+ *   q_idx        [G, T, di]     int8
+ *   sel          [G, T, top_k]  int32, when non-NULL
+ * Sequence b's rows are exactly what msa_prefill_chunk gives that sequence
+ * alone (a batch of one) for the same start and count.  The sequences run
+ * one after another on `stream`, sharing the workspace: ws/ws_bytes at least
+ * the minimum of msa_prefill_chunk_workspace_bytes for a batch of one and
+ * the largest count.  Every sequence's plan is checked before the first
+ * launch; G * T * top_k < 2^31. */
+int msa_prefill_chunk_varlen(const msa_dims* dims, const int32_t* starts, const int32_t* counts,
+                             const uint16_t* q, const int8_t* q_idx, const uint16_t* k_cache,
+                             const uint16_t* v_cache, const int8_t* k_idx, int8_t* block_keys, uint16_t* out,
+                             int32_t* sel, void* ws, size_t ws_bytes, void* stream);
+
 /* One decode step per sequence: the query at position L - 1 of each of the B
  * caches.  q [B, Hq, D] bf16, q_idx [B, G, di] int8, k_cache, v_cache
  * [B, G, L, D] bf16, block_keys [B, G, nb, di] int8 (summaries of the cache's

@@ -48,7 +48,7 @@ def test_status_strings(lib):
                          (-3, "MSA_ERR_WORKSPACE"), (-4, "MSA_ERR_HIP"), (-5, "MSA_ERR_SCRATCH")]:
         assert lib.msa_status_string(code).decode().startswith(prefix)
     assert lib.msa_status_string(12345).decode() == "unknown MSA status"
-    assert lib.msa_version() == 10500
+    assert lib.msa_version() == 10600
 
 
 def D(**kw):
@@ -155,6 +155,40 @@ def test_prefill_chunk_validation(lib):
         assert lib.msa_prefill_chunk(ctypes.byref(dims), 0, 1024, *args, None, FAKE, hi.value, None) == -1
     assert lib.msa_prefill_chunk(ctypes.byref(dims), 0, 1024, *([FAKE] * 7), None, FAKE, lo.value - 1,
                                  None) == -3
+
+
+def test_prefill_chunk_varlen_validation(lib):
+    """Ragged chunked prefill: every sequence's start and count must lie
+    inside the capacity (a count of 0 skips the sequence, but some sequence
+    must add a query); null pointers are refused; every sequence's plan is
+    checked against the workspace -- the largest chunk's, for a batch of
+    one -- before any launch."""
+    dims = D(batch=3, seq_len=4096, n_q_heads=8, n_kv_heads=2)
+    args = [FAKE] * 7  # q, q_idx, k_cache, v_cache, k_idx, block_keys, out
+    one = D(batch=1, seq_len=4096, n_q_heads=8, n_kv_heads=2)
+    lo = ctypes.c_size_t(0)
+    assert lib.msa_prefill_chunk_workspace_bytes(ctypes.byref(one), 2000, ctypes.byref(lo), None) == 0
+    starts, counts = _cu(0, 100, 4000), _cu(2000, 0, 96)
+    for bad_s, bad_c in (((-1, 100, 4000), (2000, 0, 96)), ((0, 100, 4001), (2000, 0, 96)),
+                         ((0, 100, 4000), (2000, -1, 96)), ((0, 100, 4000), (4097, 0, 96)),
+                         ((0, 0, 0), (0, 0, 0))):
+        assert lib.msa_prefill_chunk_varlen(ctypes.byref(dims), _cu(*bad_s), _cu(*bad_c), *args, None, FAKE,
+                                            1 << 40, None) == -1
+    assert lib.msa_prefill_chunk_varlen(ctypes.byref(dims), None, counts, *args, None, FAKE, 1 << 40, None) == -1
+    assert lib.msa_prefill_chunk_varlen(ctypes.byref(dims), starts, None, *args, None, FAKE, 1 << 40, None) == -1
+    for i in range(7):
+        a = list(args)
+        a[i] = None
+        assert lib.msa_prefill_chunk_varlen(ctypes.byref(dims), starts, counts, *a, None, FAKE, 1 << 40,
+                                            None) == -1
+    # below the largest chunk's minimum, or no workspace: refused before anything is enqueued
+    assert lib.msa_prefill_chunk_varlen(ctypes.byref(dims), starts, counts, *args, None, FAKE, lo.value - 256,
+                                        None) == -3
+    assert lib.msa_prefill_chunk_varlen(ctypes.byref(dims), starts, counts, *args, None, None, 1 << 40,
+                                        None) == -3
+    assert lib.msa_prefill_chunk_varlen(ctypes.byref(D(batch=3, seq_len=4096, n_q_heads=8, n_kv_heads=2,
+                                                       top_k=40)), starts, counts, *args, None, FAKE, 1 << 40,
+                                        None) == -2
 
 
 def test_backward_validation(lib):

@@ -467,6 +467,71 @@ def test_prefill_chunked_all_rows(name, over, S, bounds, C):
     compare_out(cout, oout, name)
 
 
+CHUNKED_VARLEN = [
+    # name, workload overrides, sequence lengths, per-sequence counts of each call, capacity
+    ("three_seqs_bs64", dict(n_q_heads=8, n_kv_heads=2, block_size=64, top_k=5), [1000, 300, 1],
+     [[300, 1, 699], [0, 300, 0], [1, 0, 0]], 1100),
+    ("bs128_r8_k6", dict(n_q_heads=16, n_kv_heads=2, block_size=128, top_k=6), [1536, 700],
+     [[512, 512, 512], [100, 0, 600]], 1600),
+]
+
+
+@pytest.mark.parametrize("name,over,lens,rounds,C", CHUNKED_VARLEN, ids=[c[0] for c in CHUNKED_VARLEN])
+def test_prefill_chunk_varlen_all_rows(name, over, lens, rounds, C):
+    """msa_prefill_chunk_varlen: sequences of different lengths, each in its
+    own cache, arrive in chunks of different sizes and starts (a sequence may
+    add nothing in a call).  Every row of every sequence is bit-equal to
+    msa_prefill_chunk on that sequence alone with the same chunks, and
+    matches the oracle."""
+    w = get_workload("tiny_2k", **over)
+    _say(f"[prefill chunk varlen] {name} lengths={lens} counts={rounds} C={C}")
+    B, G, bs = len(lens), w.n_kv_heads, w.block_size
+    seqs = [prefill_inputs(w, seed=400 + i, device="cpu", seq_len=L) for i, L in enumerate(lens)]
+    dseqs = [{kk: vv.to(DEV) for kk, vv in sq.items()} for sq in seqs]
+    D, di = seqs[0]["q"].shape[3], seqs[0]["q_idx"].shape[3]
+    kc = torch.zeros((B, G, C, D), dtype=torch.bfloat16, device=DEV)
+    vc = torch.zeros_like(kc)
+    kic = torch.full((B, G, C, di), 77, dtype=torch.int8, device=DEV)
+    bk = torch.zeros((B, G, -(-C // bs), di), dtype=torch.int8, device=DEV)
+    pos = [0] * B
+    outs, sels = [[] for _ in range(B)], [[] for _ in range(B)]
+    for r in range(len(rounds[0])):
+        starts, counts = list(pos), [rounds[b][r] for b in range(B)]
+        for b in range(B):
+            a, e = pos[b], pos[b] + counts[b]
+            # each sequence's new keys, values and index keys enter its cache first
+            kc[b, :, a:e] = dseqs[b]["k"][0, :, a:e]
+            vc[b, :, a:e] = dseqs[b]["v"][0, :, a:e]
+            kic[b, :, a:e] = dseqs[b]["k_idx"][0, :, a:e]
+        q = torch.cat([dseqs[b]["q"][0, pos[b]:pos[b] + counts[b]] for b in range(B)], dim=0).contiguous()
+        qi = torch.cat([dseqs[b]["q_idx"][0, :, pos[b]:pos[b] + counts[b]] for b in range(B)], dim=1).contiguous()
+        out, sel = msa.msa_prefill_chunk_varlen(q, qi, kc, vc, kic, bk, starts, counts, bs, w.top_k,
+                                                return_sel=True)
+        o = 0
+        for b in range(B):
+            n = counts[b]
+            outs[b].append(out[o:o + n])
+            sels[b].append(sel[:, o:o + n])
+            o += n
+            pos[b] += n
+    torch.cuda.synchronize()
+    assert pos == lens
+    for b in range(B):
+        cout, csel = torch.cat(outs[b], dim=0), torch.cat(sels[b], dim=1)
+        bounds = [0]
+        for r in range(len(rounds[b])):
+            if rounds[b][r] > 0:
+                bounds.append(bounds[-1] + rounds[b][r])
+        o1, s1 = _chunked(dseqs[b], bs, w.top_k, bounds, C)
+        assert torch.equal(csel, s1[0]), f"{name}: sequence {b} selection differs from its own chunked prefill"
+        assert torch.equal(cout, o1[0]), f"{name}: sequence {b} output differs from its own chunked prefill"
+        _, osel, oout = oracle_prefill_rows(seqs[b], w, np.arange(lens[b]))
+        assert np.array_equal(host_i8(csel).astype(np.int32)[None], osel), f"{name}: sequence {b} selection"
+        compare_out(cout[None], oout, f"chunk varlen {name} seq {b} (L={lens[b]})")
+    del seqs, dseqs, kc, vc, kic, bk
+    _free()
+
+
 def test_prefill_chunked_32k_equals_whole():
     """The 32K workload in four chunks of 8192 queries: bit-identical to the
     whole prefill."""
