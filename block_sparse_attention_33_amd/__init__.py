@@ -21,7 +21,7 @@ from ._lib import (MSA_OP_BACKWARD, MSA_OP_DECODE, MSA_OP_INDEX, MSA_OP_POOL, MS
 __all__ = [
     "MsaError", "make_dims", "profile_enable", "profile_read", "msa_workspace_bytes", "msa_backward_pass_rows", "msa_prefill_chunk_workspace_bytes", "msa_plan_check",
     "msa_pool_block_keys", "msa_index_select",
-    "msa_prefill", "msa_prefill_varlen", "msa_prefill_switched", "msa_prefill_lse", "msa_prefill_backward", "msa_prefill_chunk", "msa_prefill_chunk_varlen", "msa_decode", "msa_decode_noalloc", "msa_decode_init", "msa_decode_step", "MSA_OP_POOL", "MSA_OP_INDEX", "MSA_OP_PREFILL", "MSA_OP_DECODE", "MSA_OP_BACKWARD",
+    "msa_prefill", "msa_prefill_varlen", "msa_prefill_switched", "msa_prefill_lse", "msa_prefill_backward", "msa_prefill_chunk", "msa_prefill_chunk_varlen", "msa_decode", "msa_decode_noalloc", "msa_decode_init", "msa_decode_step", "msa_decode_varlen", "msa_decode_init_varlen", "msa_decode_step_varlen", "MSA_OP_POOL", "MSA_OP_INDEX", "MSA_OP_PREFILL", "MSA_OP_DECODE", "MSA_OP_BACKWARD",
 ]
 
 
@@ -453,6 +453,112 @@ def msa_decode_step(q, q_idx, k_new, v_new, k_idx_new, k_cache, v_cache, open_su
                                        _ptr(v_new), _ptr(k_idx_new), _ptr(k_cache), _ptr(v_cache),
                                        _ptr(open_sums), _ptr(block_keys), _ptr(out), _ptr(sel), _ptr(ws),
                                        ws_bytes, _stream(dev)), "msa_decode_step")
+    return (out, sel) if return_sel else out
+
+
+def _lengths(lengths, B):
+    vals = [int(x) for x in (lengths.tolist() if isinstance(lengths, torch.Tensor) else lengths)]
+    if len(vals) != B:
+        raise ValueError(f"lengths needs one entry per sequence ({B})")
+    return (ctypes.c_int32 * B)(*vals)
+
+
+def msa_decode_varlen(q, q_idx, k_cache, v_cache, block_keys, lengths, block_size: int, top_k: int,
+                      softmax_scale: float = 0.0, out=None, sel=None, return_sel: bool = False, workspace=None):
+    """Decode of a ragged batch: sequence b's query at position lengths[b] -
+    1 over its first lengths[b] cached tokens (caches [B, G, C, D] of
+    capacity C, block_keys [B, G, ceil(C/bs), di]); lengths: host list or
+    CPU tensor -> out [B, Hq, D] bf16."""
+    _need(q, "q", torch.bfloat16, 3)
+    dev = q.device
+    _need(q_idx, "q_idx", torch.int8, 3, dev)
+    _need(k_cache, "k_cache", torch.bfloat16, 4, dev)
+    _need(v_cache, "v_cache", torch.bfloat16, 4, dev)
+    _need(block_keys, "block_keys", torch.int8, 4, dev)
+    B, Hq, D = q.shape
+    _, G, C, _ = k_cache.shape
+    di = q_idx.shape[2]
+    if k_cache.shape != (B, G, C, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache/v_cache must be [B, G, C, D]")
+    if q_idx.shape != (B, G, di) or block_keys.shape != (B, G, -(-C // block_size), di):
+        raise ValueError("q_idx must be [B, G, di] and block_keys [B, G, ceil(C/bs), di]")
+    dims = _cache_dims(k_cache, block_size, top_k, Hq, di, softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16, 3, dev)
+    if sel is None and return_sel:
+        sel = torch.empty((B, G, top_k), dtype=torch.int32, device=dev)
+    if sel is not None:
+        _need(sel, "sel", torch.int32, 3, dev)
+    ws, ws_bytes = _workspace(MSA_OP_DECODE, dims, dev, workspace)
+    _check(_lib.load().msa_decode_varlen(ctypes.byref(dims), _lengths(lengths, B), _ptr(q), _ptr(q_idx),
+                                         _ptr(k_cache), _ptr(v_cache), _ptr(block_keys), _ptr(out), _ptr(sel),
+                                         _ptr(ws), ws_bytes, _stream(dev)), "msa_decode_varlen")
+    return (out, sel) if return_sel else out
+
+
+def msa_decode_init_varlen(k_idx, lengths, block_size: int, block_keys=None, open_sums=None):
+    """msa_decode_init with each sequence's own cached length (host list or
+    CPU tensor of B values in 0 .. C) -> (block_keys, open_sums)."""
+    _need(k_idx, "k_idx", torch.int8, 4)
+    dev = k_idx.device
+    B, G, C, di = k_idx.shape
+    nbc = -(-C // block_size)
+    if block_keys is None:
+        block_keys = torch.zeros((B, G, nbc, di), dtype=torch.int8, device=dev)
+    if open_sums is None:
+        open_sums = torch.zeros((B, G, di), dtype=torch.int32, device=dev)
+    _need(block_keys, "block_keys", torch.int8, 4, dev)
+    _need(open_sums, "open_sums", torch.int32, 3, dev)
+    if block_keys.shape != (B, G, nbc, di) or open_sums.shape != (B, G, di):
+        raise ValueError("block_keys must be [B, G, ceil(C/bs), di] and open_sums [B, G, di]")
+    dims = make_dims(B, C, G, G, block_size, 1, idx_dim=di)
+    _check(_lib.load().msa_decode_init_varlen(ctypes.byref(dims), _lengths(lengths, B), _ptr(k_idx),
+                                              _ptr(block_keys), _ptr(open_sums), _stream(dev)),
+           "msa_decode_init_varlen")
+    return block_keys, open_sums
+
+
+def msa_decode_step_varlen(q, q_idx, k_new, v_new, k_idx_new, k_cache, v_cache, open_sums, block_keys, lengths,
+                           block_size: int, top_k: int, softmax_scale: float = 0.0, out=None, sel=None,
+                           return_sel: bool = False, workspace=None):
+    """msa_decode_step with each sequence's own length (host list or CPU
+    tensor): sequence b's new token goes to row lengths[b] - 1 of its caches,
+    then its query there is decoded -> out [B, Hq, D] bf16."""
+    _need(q, "q", torch.bfloat16, 3)
+    dev = q.device
+    _need(q_idx, "q_idx", torch.int8, 3, dev)
+    _need(k_new, "k_new", torch.bfloat16, 3, dev)
+    _need(v_new, "v_new", torch.bfloat16, 3, dev)
+    _need(k_idx_new, "k_idx_new", torch.int8, 3, dev)
+    _need(k_cache, "k_cache", torch.bfloat16, 4, dev)
+    _need(v_cache, "v_cache", torch.bfloat16, 4, dev)
+    _need(open_sums, "open_sums", torch.int32, 3, dev)
+    _need(block_keys, "block_keys", torch.int8, 4, dev)
+    B, Hq, D = q.shape
+    _, G, C, _ = k_cache.shape
+    di = q_idx.shape[2]
+    if k_cache.shape != (B, G, C, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache/v_cache must be [B, G, C, D]")
+    if k_new.shape != (B, G, D) or v_new.shape != (B, G, D):
+        raise ValueError("k_new/v_new must be [B, G, D]")
+    if q_idx.shape != (B, G, di) or k_idx_new.shape != (B, G, di) or open_sums.shape != (B, G, di):
+        raise ValueError("q_idx, k_idx_new and open_sums must be [B, G, di]")
+    if block_keys.shape != (B, G, -(-C // block_size), di):
+        raise ValueError("block_keys must be [B, G, ceil(C/bs), di]")
+    dims = _cache_dims(k_cache, block_size, top_k, Hq, di, softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16, 3, dev)
+    if sel is None and return_sel:
+        sel = torch.empty((B, G, top_k), dtype=torch.int32, device=dev)
+    if sel is not None:
+        _need(sel, "sel", torch.int32, 3, dev)
+    ws, ws_bytes = _workspace(MSA_OP_DECODE, dims, dev, workspace)
+    _check(_lib.load().msa_decode_step_varlen(ctypes.byref(dims), _lengths(lengths, B), _ptr(q), _ptr(q_idx),
+                                              _ptr(k_new), _ptr(v_new), _ptr(k_idx_new), _ptr(k_cache),
+                                              _ptr(v_cache), _ptr(open_sums), _ptr(block_keys), _ptr(out),
+                                              _ptr(sel), _ptr(ws), ws_bytes, _stream(dev)), "msa_decode_step_varlen")
     return (out, sel) if return_sel else out
 
 

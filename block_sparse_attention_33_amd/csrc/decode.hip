@@ -135,10 +135,10 @@ struct DecBlock {
 
 // Loads of block j (a valid block index) for group thread gt, wave-in-group wg.
 __device__ __forceinline__ void dec_load_block(const DecodeShape& sh, const uint16_t* __restrict__ k_cache,
-                                               const uint16_t* __restrict__ v_cache, int u, int j, int gt, int wg,
-                                               int lane, DecBlock& blk) {
+                                               const uint16_t* __restrict__ v_cache, int u, int L, int j, int gt,
+                                               int wg, int lane, DecBlock& blk) {
   const int key0 = j * sh.bs;
-  const int nk = min(sh.bs, sh.L - key0);
+  const int nk = min(sh.bs, L - key0);
   const int col = lane & 31, hf = lane >> 5;
   const uint16_t* krow = k_cache + ((size_t)u * sh.Lc + key0 + min(32 * wg + col, nk - 1)) * kHeadDim;
 #pragma unroll
@@ -163,12 +163,13 @@ struct DecState {
 // One slot (block j, or an empty slot when j < 0) added to the group's state.
 // Starts and ends with a workgroup barrier-free region: the caller places
 // the barriers that order the LDS buffers between slots.
-__device__ __forceinline__ void dec_slot(const DecodeShape& sh, const DecBlock& blk, int j, const char* __restrict__ qs,
-                                         char* __restrict__ vt, char* __restrict__ pt, float (*red_m)[32],
-                                         float (*red_l)[32], int gt, int wg, int lane, DecState& st) {
+__device__ __forceinline__ void dec_slot(const DecodeShape& sh, const DecBlock& blk, int L, int j,
+                                         const char* __restrict__ qs, char* __restrict__ vt, char* __restrict__ pt,
+                                         float (*red_m)[32], float (*red_l)[32], int gt, int wg, int lane,
+                                         DecState& st) {
   const int col = lane & 31, hf = lane >> 5;
   const bool qcol = col < sh.r;
-  const int nk = j < 0 ? 0 : min(sh.bs, sh.L - j * sh.bs);  // valid keys (0: empty slot)
+  const int nk = j < 0 ? 0 : min(sh.bs, L - j * sh.bs);  // valid keys (0: empty slot)
   const int kbase = 32 * wg;
   // V^T in LDS: the thread's 8 x 8 tile is transposed in registers and row
   // d = 8 c + e gets keys 8 o .. 8 o + 7 as one 16-byte write, in 16-byte
@@ -285,7 +286,8 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(const uint16_t* __restri
   const int r = sh.r;
   const int K = sh.top_k;
   const int kp = K - 1;
-  const int own = sh.nb - 1;  // candidates are blocks 0 .. own - 1
+  const int L = sh.lens != nullptr ? sh.lens[b] : sh.L;  // the unit's cached tokens
+  const int own = (L - 1) / sh.bs;                     // candidates are blocks 0 .. own - 1
   // the unit's query rows in LDS (rows r .. 31 zero), read per slot
   if (tid < 32 * 16) {
     const int row = tid >> 4, ch = tid & 15;
@@ -385,7 +387,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(const uint16_t* __restri
   };
   auto load_round = [&](int rd, DecBlock& blk) {
     const int j = slot_block(rd);
-    dec_load_block(sh, k_cache, v_cache, u, j >= 0 ? j : own, gt, wg, lane, blk);
+    dec_load_block(sh, k_cache, v_cache, u, L, j >= 0 ? j : own, gt, wg, lane, blk);
   };
   const int per_wg = 2 * n_split;
   const int n_rounds = (K + per_wg - 1) / per_wg;  // the same for both groups (barriers)
@@ -394,11 +396,11 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(const uint16_t* __restri
   for (int rd = 0; rd < n_rounds; rd += 2) {
     load_round(rd + 1, B);
     if (rd > 0) __syncthreads();  // the previous slot's LDS reads are done
-    dec_slot(sh, A, slot_block(rd), qs, vt[gp], pt[gp], red_m[gp], red_l[gp], gt, wg, lane, st);
+    dec_slot(sh, A, L, slot_block(rd), qs, vt[gp], pt[gp], red_m[gp], red_l[gp], gt, wg, lane, st);
     if (rd + 1 >= n_rounds) break;
     load_round(rd + 2, A);
     __syncthreads();
-    dec_slot(sh, B, slot_block(rd + 1), qs, vt[gp], pt[gp], red_m[gp], red_l[gp], gt, wg, lane, st);
+    dec_slot(sh, B, L, slot_block(rd + 1), qs, vt[gp], pt[gp], red_m[gp], red_l[gp], gt, wg, lane, st);
   }
 
   // ---- merge of the two groups' states -> out = o / l
@@ -500,6 +502,7 @@ __global__ __launch_bounds__(64) void append_kernel(const uint16_t* __restrict__
                                                     int8_t* __restrict__ block_keys, DecodeShape sh, int pos) {
   const int u = blockIdx.x;
   const int l = threadIdx.x;
+  if (sh.lens != nullptr) pos = sh.lens[u / sh.G] - 1;  // the unit's own position
   const size_t row = ((size_t)u * sh.Lc + pos) * kHeadDim;
   if (l < 16)
     reinterpret_cast<u32x4_t*>(k_cache + row)[l] = reinterpret_cast<const u32x4_t*>(k_new + (size_t)u * kHeadDim)[l];
@@ -511,6 +514,13 @@ __global__ __launch_bounds__(64) void append_kernel(const uint16_t* __restrict__
   const int s = (n == 1 ? 0 : open_sums[(size_t)u * kIdxDim + l]) + (int)k_idx_new[(size_t)u * kIdxDim + l];
   open_sums[(size_t)u * kIdxDim + l] = s;
   block_keys[((size_t)u * sh.nbc + j) * kIdxDim + l] = (int8_t)floor_div(s, n);
+}
+
+// Per-sequence lengths into device memory: the values travel in the kernel
+// arguments (a launch copies them), so no host memory is read after the
+// launch and no copy waits for the stream.
+__global__ __launch_bounds__(256) void set_lengths_kernel(int32_t* __restrict__ dst, LengthBatch v, int n) {
+  for (int i = threadIdx.x; i < n; i += 256) dst[i] = v.v[i];
 }
 
 // Scratch of the allocation-free decode entry point: one array per device,
@@ -557,6 +567,18 @@ hipError_t launch_decode(const DecodeShape& sh, const uint16_t* q, const int8_t*
     hipLaunchKernelGGL(decode_kernel<16>, grid, block, 0, st, q, q_idx, k_cache, v_cache, block_keys, sel_out, out,
                        state, sh);
   return hipGetLastError();
+}
+
+hipError_t launch_set_lengths(int32_t* dst, const int32_t* lengths, int n, hipStream_t st) {
+  for (int i0 = 0; i0 < n; i0 += kLengthBatch) {
+    LengthBatch v;
+    const int m = n - i0 < kLengthBatch ? n - i0 : kLengthBatch;
+    for (int i = 0; i < m; ++i) v.v[i] = lengths[i0 + i];
+    hipLaunchKernelGGL(set_lengths_kernel, dim3(1), dim3(256), 0, st, dst + i0, v, m);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_append(const DecodeShape& sh, const uint16_t* k_new, const uint16_t* v_new,

@@ -147,11 +147,12 @@ PrefillLayout prefill_layout(const Dims& d, const PrefillPlan& p, long units_per
 int decode_split(const Dims& d) { return d.k >= 4 ? 2 : 1; }
 
 struct DecodeLayout {
-  size_t sel, state, total;
+  size_t sel, state, lens, total;
 };
 
-// Decode workspace: the selection (when the caller passes no sel) and the
-// workgroups' states (max, sum, unnormalised o per head).
+// Decode workspace: the selection (when the caller passes no sel), the
+// workgroups' states (max, sum, unnormalised o per head) and the sequences'
+// lengths of a ragged batch.
 int decode_layout(const Dims& d, DecodeLayout* L) {
   if (d.nb - 1 > msa::kDecodeMaxCandidates) return MSA_ERR_UNSUPPORTED;
   size_t off = 0;
@@ -162,6 +163,7 @@ int decode_layout(const Dims& d, DecodeLayout* L) {
   };
   L->sel = take((size_t)d.U * d.k * 4);
   L->state = take((size_t)d.U * decode_split(d) * d.r * (d.D + 2) * 4);
+  L->lens = take((size_t)d.B * 4);
   L->total = off;
   return MSA_OK;
 }
@@ -242,21 +244,25 @@ msa::DecodeShape decode_shape(const Dims& d, long length) {
   sh.Lc = (int)d.S;
   sh.nbc = (int)d.nb;
   sh.scale_log2 = d.scale * 1.4426950408889634f;
+  sh.lens = nullptr;
   return sh;
 }
 
 // Decode of the query at position length - 1 over caches with room for d.S
-// tokens per unit (arguments already checked).
-int run_decode(const Dims& d, long length, const uint16_t* q, const int8_t* q_idx, const uint16_t* k_cache,
-               const uint16_t* v_cache, const int8_t* block_keys, uint16_t* out, int32_t* sel, void* ws,
-               size_t ws_bytes, hipStream_t s) {
+// tokens per unit (arguments already checked); with lens (device int32 [B],
+// already written) sequence b's query is at lens[b] - 1 and length is the
+// largest of them.
+int run_decode(const Dims& d, long length, const int32_t* lens, const uint16_t* q, const int8_t* q_idx,
+               const uint16_t* k_cache, const uint16_t* v_cache, const int8_t* block_keys, uint16_t* out,
+               int32_t* sel, void* ws, size_t ws_bytes, hipStream_t s) {
   DecodeLayout L;
   int st = decode_layout(d, &L);
   if (st != MSA_OK) return st;
   st = check_ws(ws, ws_bytes, L.total);
   if (st != MSA_OK) return st;
   char* base = static_cast<char*>(ws);
-  const msa::DecodeShape sh = decode_shape(d, length);
+  msa::DecodeShape sh = decode_shape(d, length);
+  sh.lens = lens;
   int32_t* sel_use = sel ? sel : reinterpret_cast<int32_t*>(base + L.sel);
   float* state = reinterpret_cast<float*>(base + L.state);
   const int n_split = decode_split(d);
@@ -596,6 +602,19 @@ int prefill_impl(const Dims& d, const Strides& str, const uint16_t* q, const uin
   return MSA_OK;
 }
 
+// Host lengths of a ragged decode batch: every one in lo .. d.S (the
+// capacity); *longest = the largest (0 when all are 0).
+int check_lengths(const Dims& d, const int32_t* lengths, long lo, long* longest) {
+  if (lengths == nullptr) return MSA_ERR_INVALID_ARG;
+  long m = 0;
+  for (long b = 0; b < d.B; ++b) {
+    if (lengths[b] < lo || lengths[b] > d.S) return MSA_ERR_INVALID_ARG;
+    m = std::max<long>(m, lengths[b]);
+  }
+  *longest = m;
+  return MSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -619,7 +638,7 @@ const char* msa_status_string(int status) {
   }
 }
 
-int msa_version(void) { return 10600; }
+int msa_version(void) { return 10700; }
 
 int msa_backward_pass_rows(const msa_dims* dims, size_t ws_bytes, int32_t* rows) {
   Dims d;
@@ -1005,7 +1024,8 @@ int msa_decode(const msa_dims* dims, const uint16_t* q, const int8_t* q_idx, con
   if (st != MSA_OK) return st;
   if (d.k > kMaxSparseTopK) return MSA_ERR_UNSUPPORTED;
   if (!q || !q_idx || !k_cache || !v_cache || !block_keys || !out) return MSA_ERR_INVALID_ARG;
-  return run_decode(d, d.S, q, q_idx, k_cache, v_cache, block_keys, out, sel, ws, ws_bytes, (hipStream_t)stream);
+  return run_decode(d, d.S, nullptr, q, q_idx, k_cache, v_cache, block_keys, out, sel, ws, ws_bytes,
+                    (hipStream_t)stream);
 }
 
 int msa_decode_noalloc(const msa_dims* dims, const uint16_t* q, const int8_t* q_idx, const uint16_t* k_cache,
@@ -1025,8 +1045,8 @@ int msa_decode_noalloc(const msa_dims* dims, const uint16_t* q, const int8_t* q_
   // of the scratch they later read
   void* scratch = nullptr;
   if (msa::decode_scratch(&scratch) != hipSuccess) return MSA_ERR_HIP;
-  return run_decode(d, d.S, q, q_idx, k_cache, v_cache, block_keys, out, sel, scratch, msa::kDecodeScratchBytes,
-                    (hipStream_t)stream);
+  return run_decode(d, d.S, nullptr, q, q_idx, k_cache, v_cache, block_keys, out, sel, scratch,
+                    msa::kDecodeScratchBytes, (hipStream_t)stream);
 }
 
 int msa_decode_init(const msa_dims* dims, int32_t length, const int8_t* k_idx, int8_t* block_keys,
@@ -1063,7 +1083,79 @@ int msa_decode_step(const msa_dims* dims, int32_t length, const uint16_t* q, con
   const msa::DecodeShape sh = decode_shape(d, length);
   MSA_LAUNCH_NAMED("append", s, msa::launch_append(sh, k_new, v_new, k_idx_new, k_cache, v_cache, open_sums,
                                                    block_keys, (int)length - 1, s));
-  return run_decode(d, length, q, q_idx, k_cache, v_cache, block_keys, out, sel, ws, ws_bytes, s);
+  return run_decode(d, length, nullptr, q, q_idx, k_cache, v_cache, block_keys, out, sel, ws, ws_bytes, s);
+}
+
+int msa_decode_varlen(const msa_dims* dims, const int32_t* lengths, const uint16_t* q, const int8_t* q_idx,
+                      const uint16_t* k_cache, const uint16_t* v_cache, const int8_t* block_keys, uint16_t* out,
+                      int32_t* sel, void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  int st = check_dims(dims, &d);
+  if (st != MSA_OK) return st;
+  if (d.k > kMaxSparseTopK) return MSA_ERR_UNSUPPORTED;
+  if (!q || !q_idx || !k_cache || !v_cache || !block_keys || !out) return MSA_ERR_INVALID_ARG;
+  long longest = 0;
+  st = check_lengths(d, lengths, 1, &longest);
+  if (st != MSA_OK) return st;
+  DecodeLayout L;
+  st = decode_layout(d, &L);
+  if (st != MSA_OK) return st;
+  st = check_ws(ws, ws_bytes, L.total);
+  if (st != MSA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  int32_t* lens = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + L.lens);
+  MSA_LAUNCH_NAMED("lengths", s, msa::launch_set_lengths(lens, lengths, (int)d.B, s));
+  return run_decode(d, longest, lens, q, q_idx, k_cache, v_cache, block_keys, out, sel, ws, ws_bytes, s);
+}
+
+int msa_decode_init_varlen(const msa_dims* dims, const int32_t* lengths, const int8_t* k_idx, int8_t* block_keys,
+                           int32_t* open_sums, void* stream) {
+  Dims d;
+  int st = check_dims(dims, &d);
+  if (st != MSA_OK) return st;
+  if (d.k > kMaxSparseTopK) return MSA_ERR_UNSUPPORTED;
+  if (!k_idx || !block_keys || !open_sums) return MSA_ERR_INVALID_ARG;
+  long longest = 0;
+  st = check_lengths(d, lengths, 0, &longest);
+  if (st != MSA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  // each sequence's caches as a batch of one (a length of 0 enqueues nothing)
+  for (long b = 0; b < d.B; ++b) {
+    if (lengths[b] == 0) continue;
+    MSA_LAUNCH_NAMED("pool", s, msa::launch_pool_strided(k_idx + (size_t)b * d.G * d.S * d.di,
+                                                         block_keys + (size_t)b * d.G * d.nb * d.di,
+                                                         open_sums + (size_t)b * d.G * d.di, (int)d.G,
+                                                         (int)lengths[b], d.S, (int)d.nb, (int)d.bs, 0, s));
+  }
+  return MSA_OK;
+}
+
+int msa_decode_step_varlen(const msa_dims* dims, const int32_t* lengths, const uint16_t* q, const int8_t* q_idx,
+                           const uint16_t* k_new, const uint16_t* v_new, const int8_t* k_idx_new,
+                           uint16_t* k_cache, uint16_t* v_cache, int32_t* open_sums, int8_t* block_keys,
+                           uint16_t* out, int32_t* sel, void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  int st = check_dims(dims, &d);
+  if (st != MSA_OK) return st;
+  if (d.k > kMaxSparseTopK) return MSA_ERR_UNSUPPORTED;
+  if (!q || !q_idx || !k_new || !v_new || !k_idx_new || !k_cache || !v_cache || !open_sums || !block_keys || !out)
+    return MSA_ERR_INVALID_ARG;
+  long longest = 0;
+  st = check_lengths(d, lengths, 1, &longest);
+  if (st != MSA_OK) return st;
+  DecodeLayout L;
+  st = decode_layout(d, &L);
+  if (st != MSA_OK) return st;
+  st = check_ws(ws, ws_bytes, L.total);
+  if (st != MSA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  int32_t* lens = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + L.lens);
+  MSA_LAUNCH_NAMED("lengths", s, msa::launch_set_lengths(lens, lengths, (int)d.B, s));
+  msa::DecodeShape sh = decode_shape(d, longest);
+  sh.lens = lens;
+  MSA_LAUNCH_NAMED("append", s, msa::launch_append(sh, k_new, v_new, k_idx_new, k_cache, v_cache, open_sums,
+                                                   block_keys, (int)longest - 1, s));
+  return run_decode(d, longest, lens, q, q_idx, k_cache, v_cache, block_keys, out, sel, ws, ws_bytes, s);
 }
 
 int msa_profile_enable(int on) {

@@ -154,7 +154,17 @@ struct DecodeShape {
   int B, L, Hq, G, r, bs, nb, top_k;  // L tokens in the caches, nb = ceil(L / bs)
   int Lc, nbc;                        // cache rows and summary rows per unit (capacity)
   float scale_log2;
+  // device int32 [B]: sequence b holds lens[b] tokens (1 .. Lc) and L, nb
+  // are the largest; null: every sequence holds L
+  const int32_t* lens;
 };
+// Up to kLengthBatch host lengths carried by value in one launch's arguments.
+constexpr int kLengthBatch = 512;
+struct LengthBatch {
+  int32_t v[kLengthBatch];
+};
+// dst[0 .. n) = lengths[0 .. n) (host), in launches of kLengthBatch values.
+hipError_t launch_set_lengths(int32_t* dst, const int32_t* lengths, int n, hipStream_t st);
 constexpr int kDecodeMaxCandidates = 16 * 512;  // 512 threads x 16 candidates
 // Selection (-> sel [U, top_k]: ascending, own block last, -1 padding) and
 // attention over the kept blocks.  n_split workgroups share a unit's slots;

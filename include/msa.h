@@ -357,6 +357,40 @@ int msa_decode_step(const msa_dims* dims, int32_t length, const uint16_t* q, con
                     uint16_t* k_cache, uint16_t* v_cache, int32_t* open_sums, int8_t* block_keys,
                     uint16_t* out, int32_t* sel, void* ws, size_t ws_bytes, void* stream);
 
+/* Decode and generation for a ragged batch: sequence b's caches hold its
+ * own number of tokens, lengths[b], out of the common capacity C =
+ * dims->seq_len (a served batch mixes prompts of any length; the pages
+ * decode over resident KV caches up to 1M tokens: wiki.500nian.com digest of
+ * "MiniMax M3 Review: 1M Tokens, 15X Faster AI Agents", paragraph on the
+ * quadratic wall and the KV cache).  lengths: HOST int32 [batch]; the
+ * values are checked on the host and carried to the device in the
+ * arguments of a small kernel (no host memory is read after the call
+ * returns).  Layouts as for msa_decode_step: k_cache, v_cache [B, G, C, D]
+ * bf16, block_keys [B, G, ceil(C / block_size), di] int8, open_sums
+ * [B, G, di] int32.
+ *
+ * msa_decode_varlen: the query of sequence b at position lengths[b] - 1
+ * over its first lengths[b] tokens (1 <= lengths[b] <= C); q [B, Hq, D],
+ * q_idx [B, G, di] -> out [B, Hq, D], sel [B, G, top_k] when non-NULL.
+ * Sequence b's row equals msa_decode on that sequence alone with L =
+ * lengths[b].
+ * msa_decode_init_varlen: msa_decode_init with each sequence's own length
+ * (0 <= lengths[b] <= C; a length of 0 enqueues nothing for it).
+ * msa_decode_step_varlen: msa_decode_step with each sequence's own length
+ * (1 <= lengths[b] <= C): its new token goes to row lengths[b] - 1, then
+ * its query there is decoded.
+ * ws/ws_bytes (decode, step): at least msa_workspace_bytes(MSA_OP_DECODE). */
+int msa_decode_varlen(const msa_dims* dims, const int32_t* lengths, const uint16_t* q, const int8_t* q_idx,
+                      const uint16_t* k_cache, const uint16_t* v_cache, const int8_t* block_keys,
+                      uint16_t* out, int32_t* sel, void* ws, size_t ws_bytes, void* stream);
+int msa_decode_init_varlen(const msa_dims* dims, const int32_t* lengths, const int8_t* k_idx,
+                           int8_t* block_keys, int32_t* open_sums, void* stream);
+int msa_decode_step_varlen(const msa_dims* dims, const int32_t* lengths, const uint16_t* q,
+                           const int8_t* q_idx, const uint16_t* k_new, const uint16_t* v_new,
+                           const int8_t* k_idx_new, uint16_t* k_cache, uint16_t* v_cache,
+                           int32_t* open_sums, int8_t* block_keys, uint16_t* out, int32_t* sel, void* ws,
+                           size_t ws_bytes, void* stream);
+
 /* Optional per-kernel timing.  While enabled (on != 0), every kernel the
  * entry points enqueue is bracketed by two HIP events on the same stream and
  * recorded under its kernel name; disabled by default.  Returns MSA_OK, or

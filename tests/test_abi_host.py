@@ -48,7 +48,7 @@ def test_status_strings(lib):
                          (-3, "MSA_ERR_WORKSPACE"), (-4, "MSA_ERR_HIP"), (-5, "MSA_ERR_SCRATCH")]:
         assert lib.msa_status_string(code).decode().startswith(prefix)
     assert lib.msa_status_string(12345).decode() == "unknown MSA status"
-    assert lib.msa_version() == 10600
+    assert lib.msa_version() == 10700
 
 
 def D(**kw):
@@ -191,6 +191,36 @@ def test_prefill_chunk_varlen_validation(lib):
                                         None) == -2
 
 
+def test_decode_varlen_validation(lib):
+    """Ragged decode, init and step: the host lengths must lie in 1 .. C
+    (0 .. C for init); null pointers and short workspaces are refused before
+    any launch; the workspace is msa_decode's."""
+    dims = D(batch=3, seq_len=5000, n_q_heads=8, n_kv_heads=2)
+    st, lo, hi = _ws(lib, _lib.MSA_OP_DECODE, dims)
+    assert st == 0 and lo > 0
+    good = _cu(1, 4999, 5000)
+    args = [FAKE] * 6  # q, q_idx, k_cache, v_cache, block_keys, out
+    for bad in (None, _cu(0, 10, 20), _cu(1, 5001, 20), _cu(-1, 10, 20)):
+        assert lib.msa_decode_varlen(ctypes.byref(dims), bad, *args, None, FAKE, hi, None) == -1
+        assert lib.msa_decode_step_varlen(ctypes.byref(dims), bad, *([FAKE] * 10), None, FAKE, hi, None) == -1
+    for i in range(6):
+        a = list(args)
+        a[i] = None
+        assert lib.msa_decode_varlen(ctypes.byref(dims), good, *a, None, FAKE, hi, None) == -1
+    for i in range(10):
+        a = [FAKE] * 10
+        a[i] = None
+        assert lib.msa_decode_step_varlen(ctypes.byref(dims), good, *a, None, FAKE, hi, None) == -1
+    assert lib.msa_decode_varlen(ctypes.byref(dims), good, *args, None, FAKE, lo - 1, None) == -3
+    assert lib.msa_decode_varlen(ctypes.byref(dims), good, *args, None, None, hi, None) == -3
+    assert lib.msa_decode_step_varlen(ctypes.byref(dims), good, *([FAKE] * 10), None, FAKE, lo - 1, None) == -3
+    for bad in (None, _cu(0, 10, 5001), _cu(-1, 0, 0)):
+        assert lib.msa_decode_init_varlen(ctypes.byref(dims), bad, FAKE, FAKE, FAKE, None) == -1
+    assert lib.msa_decode_init_varlen(ctypes.byref(dims), _cu(0, 0, 0), None, FAKE, FAKE, None) == -1
+    # all lengths 0: nothing to pool, nothing enqueued
+    assert lib.msa_decode_init_varlen(ctypes.byref(dims), _cu(0, 0, 0), FAKE, FAKE, FAKE, None) == 0
+
+
 def test_backward_validation(lib):
     """Training path: msa_prefill_lse needs its lse output; the backward
     needs every tensor, a workspace of its documented size (one bf16 dq
@@ -315,9 +345,10 @@ def test_decode_workspace_layout(lib):
     dims = D(batch=16, seq_len=262144)
     st, lo, hi = _ws(lib, _lib.MSA_OP_DECODE, dims)
     U, k, r = 16 * 8, 16, 8
-    # the selection (when the caller passes no sel), then two workgroup
-    # states per unit: r x (128 + 2) fp32
-    exp = _a(U * k * 4) + _a(U * 2 * r * 130 * 4)
+    # the selection (when the caller passes no sel), two workgroup states
+    # per unit: r x (128 + 2) fp32, and a ragged batch's lengths (int32 per
+    # sequence)
+    exp = _a(U * k * 4) + _a(U * 2 * r * 130 * 4) + _a(16 * 4)
     assert st == 0 and lo == hi == exp
     # at most 8192 candidate blocks before the own block
     assert _ws(lib, _lib.MSA_OP_DECODE, D(batch=1, seq_len=8193 * 128))[0] == 0

@@ -629,6 +629,92 @@ def test_decode_generation_steps(bs, top_k, L0, steps):
     assert int(kc[:, :, Lend:].abs().sum()) == 0
 
 
+def test_decode_varlen_rows():
+    """msa_decode_varlen over a ragged batch (1 to 70000 cached tokens in
+    caches of 70001, partial and full last blocks): each sequence's
+    selection and output bit-equal to msa_decode on that sequence alone and
+    matching the oracle; msa_decode_init_varlen's summaries and open-block
+    sums equal the pooling of each sequence's own tokens (rows past them are
+    never read)."""
+    w = get_workload("decode_b16_256k", n_q_heads=8, n_kv_heads=2, block_size=64, top_k=8)
+    lens = [1, 100, 128, 4097, 70000]
+    B, C, bs, k = len(lens), max(lens) + 1, w.block_size, w.top_k
+    _say(f"[decode varlen] lengths={lens} C={C} {w}")
+    inp = decode_inputs(w, seed=91, device=DEV, seq_len=C, batch=B)
+    kidx = inp["k_idx_cache"].clone()
+    for b, L in enumerate(lens):
+        kidx[b, :, L:] = 99
+    bk, osum = msa.msa_decode_init_varlen(kidx, lens, bs)
+    out, sel = msa.msa_decode_varlen(inp["q"], inp["q_idx"], inp["k_cache"], inp["v_cache"], bk, lens, bs, k,
+                                     return_sel=True)
+    torch.cuda.synchronize()
+    hki = host_i8(inp["k_idx_cache"])
+    for b, L in enumerate(lens):
+        nb = -(-L // bs)
+        summ = O.pool_block_keys(hki[b:b + 1, :, :L], bs)
+        assert np.array_equal(host_i8(bk)[b:b + 1, :, :nb], summ), f"summaries of sequence {b}"
+        j0 = L // bs
+        assert np.array_equal(host_i8(osum)[b].astype(np.int64),
+                              hki[b, :, j0 * bs:L].astype(np.int64).sum(axis=1)), f"open sums of sequence {b}"
+        o1, s1 = msa.msa_decode(inp["q"][b:b + 1].contiguous(), inp["q_idx"][b:b + 1].contiguous(),
+                                inp["k_cache"][b:b + 1, :, :L].contiguous(), inp["v_cache"][b:b + 1, :, :L].contiguous(),
+                                bk[b:b + 1, :, :nb].contiguous(), bs, k, return_sel=True)
+        torch.cuda.synchronize()
+        assert torch.equal(sel[b:b + 1], s1), f"sequence {b}: selection differs from msa_decode alone"
+        assert torch.equal(out[b:b + 1], o1), f"sequence {b}: output differs from msa_decode alone"
+        osel, oout = O.decode(host_f32(inp["q"][b:b + 1]), host_i8(inp["q_idx"][b:b + 1]),
+                              HostBf16(inp["k_cache"][b:b + 1, :, :L]), HostBf16(inp["v_cache"][b:b + 1, :, :L]),
+                              summ, bs, k)
+        assert np.array_equal(host_i8(sel[b:b + 1]).astype(np.int32), osel), f"selection of sequence {b}"
+        compare_out(out[b:b + 1], oout, f"decode varlen L={L}")
+    del inp, kidx, bk, osum, out, sel
+    _free()
+
+
+def test_decode_step_varlen_generation():
+    """Ragged generation: msa_decode_init_varlen on 1, 63, 64 and 200 cached
+    tokens, then 70 msa_decode_step_varlen steps, each sequence appending at
+    its own position (every one crosses a block boundary).  Every step's
+    selection and output match the oracle's decode of each sequence's prefix
+    with summaries pooled from its index keys so far, the summaries match
+    that pooling after every step, and the caches end as the new tokens."""
+    w = get_workload("decode_b16_256k", n_q_heads=8, n_kv_heads=2, block_size=64, top_k=4)
+    L0s, steps, bs, k = [1, 63, 64, 200], 70, 64, 4
+    B, C = len(L0s), max(L0s) + steps + 5
+    _say(f"[decode generation varlen] L0={L0s} steps={steps} C={C}")
+    truth = decode_inputs(w, seed=171, device=DEV, seq_len=C, batch=B)
+    tk, tv, tki = truth["k_cache"], truth["v_cache"], truth["k_idx_cache"]
+    hk, hv, hki = host_f32(tk), host_f32(tv), host_i8(tki)
+    kc, vc, kidx = tk.clone(), tv.clone(), tki.clone()
+    for b, L0 in enumerate(L0s):
+        kc[b, :, L0:] = 0
+        vc[b, :, L0:] = 0
+        kidx[b, :, L0:] = 99
+    bk, osum = msa.msa_decode_init_varlen(kidx, L0s, bs)
+    for i in range(steps):
+        lens = [L0 + i + 1 for L0 in L0s]
+        pos = torch.tensor([L - 1 for L in lens], device=DEV)
+        ar = torch.arange(B, device=DEV)
+        qs = decode_inputs(w, seed=7000 + i, device=DEV, seq_len=1, batch=B)
+        k_new = tk[ar, :, pos].contiguous()
+        v_new = tv[ar, :, pos].contiguous()
+        ki_new = tki[ar, :, pos].contiguous()
+        out, sel = msa.msa_decode_step_varlen(qs["q"], qs["q_idx"], k_new, v_new, ki_new, kc, vc, osum, bk, lens,
+                                              bs, k, return_sel=True)
+        torch.cuda.synchronize()
+        for b, L in enumerate(lens):
+            summ = O.pool_block_keys(hki[b:b + 1, :, :L], bs)
+            assert np.array_equal(host_i8(bk)[b:b + 1, :, :-(-L // bs)], summ), f"summaries of {b} at L={L}"
+            osel, oout = O.decode(host_f32(qs["q"][b:b + 1]), host_i8(qs["q_idx"][b:b + 1]), hk[b:b + 1, :, :L],
+                                  hv[b:b + 1, :, :L], summ, bs, k)
+            assert np.array_equal(host_i8(sel[b:b + 1]).astype(np.int32), osel), f"selection of {b} at L={L}"
+            compare_out(out[b:b + 1], oout, f"decode step varlen seq {b} L={L}")
+    for b, L0 in enumerate(L0s):
+        Lend = L0 + steps
+        assert torch.equal(kc[b, :, :Lend], tk[b, :, :Lend]) and torch.equal(vc[b, :, :Lend], tv[b, :, :Lend])
+        assert int(kc[b, :, Lend:].abs().sum()) == 0
+
+
 def test_decode_matches_last_prefill_row():
     w = get_workload("prefill_32k")
     S = 5000
