@@ -209,6 +209,56 @@ def pmc_summary(fetch_csv, write_csv, commands):
     print(json.dumps({"written": TRAFFIC_FILE, "attend_bytes_per_launch": rec["bytes_per_launch"]}))
 
 
+def counter_table(stats_csv, pmc_csvs):
+    """Markdown table of per-dispatch SQ counters of the MSA kernels from
+    rocprofv3 --pmc CSV files (one counter pass each) and the average kernel
+    durations of a --kernel-trace --stats run of the same command, with the
+    ratios they give.  MI355X: 1024 SIMDs (256 CUs x 4) at 2.4 GHz."""
+    import csv
+    import re
+
+    def key_of(name):
+        m = re.search(r"msa::\(anonymous namespace\)::(\w+(?:<[\w, ]+>)?)", name)
+        return m.group(1) if m else None
+
+    dur = {}
+    with open(stats_csv, newline="") as f:
+        for row in csv.DictReader(f):
+            k = key_of(row["Name"])
+            if k:
+                dur[k] = float(row["AverageNs"]) * 1e-9
+    cnt = {}
+    for path in pmc_csvs:
+        with open(path, newline="") as f:
+            for row in csv.DictReader(f):
+                k = key_of(row["Kernel_Name"])
+                if k:
+                    cnt.setdefault(k, {}).setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
+    simd_cycles = 1024 * 2.4e9
+    cols = ["kernel", "avg us", "waves", "VALU / wave", "MFMA / wave", "LDS / wave", "MFMA busy per SIMD",
+            "wave cycles waiting on a counter", "waiting for issue", "issuing", "LDS cycles in bank conflicts"]
+    print("| " + " | ".join(cols) + " |")
+    print("|" + "---|" * len(cols))
+    for k in sorted(cnt, key=lambda x: -dur.get(x, 0.0)):
+        c = {n: sum(v) / len(v) for n, v in cnt[k].items()}
+        g = lambda n: c.get(n)  # noqa: E731
+
+        def ratio(a, b, pct=True):
+            if a is None or b is None or b == 0:
+                return ""
+            return f"{100.0 * a / b:.1f} %" if pct else f"{a / b:.0f}"
+
+        d = dur.get(k)
+        mfma_busy = ratio(g("SQ_VALU_MFMA_BUSY_CYCLES"), d * simd_cycles if d else None)
+        cells = [k, f"{d * 1e6:.1f}" if d else "", f"{g('SQ_WAVES'):.0f}" if g("SQ_WAVES") else "",
+                 ratio(g("SQ_INSTS_VALU"), g("SQ_WAVES"), False), ratio(g("SQ_INSTS_MFMA"), g("SQ_WAVES"), False),
+                 ratio(g("SQ_INSTS_LDS"), g("SQ_WAVES"), False), mfma_busy,
+                 ratio(g("SQ_WAIT_ANY"), g("SQ_WAVE_CYCLES")), ratio(g("SQ_WAIT_INST_ANY"), g("SQ_WAVE_CYCLES")),
+                 ratio(g("SQ_ACTIVE_INST_ANY"), g("SQ_WAVE_CYCLES")),
+                 ratio(g("SQ_LDS_BANK_CONFLICT"), g("SQ_LDS_IDX_ACTIVE"))]
+        print("| " + " | ".join(cells) + " |")
+
+
 # ------------------------------------------------------------------ CPU oracle baseline
 
 def _host_info():
@@ -511,9 +561,15 @@ def main():
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic record from the two counter runs' CSV files")
     ap.add_argument("--pmc-commands", nargs="*", default=[], help=argparse.SUPPRESS)
+    ap.add_argument("--counter-table", nargs="+", metavar=("STATS_CSV", "PMC_CSV"),
+                    help="print the SQ counter table of the MSA kernels from a kernel-trace stats CSV and the "
+                         "counter passes' CSV files")
     args = ap.parse_args()
     if args.pmc_summary:
         pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.pmc_commands)
+        return 0
+    if args.counter_table:
+        counter_table(args.counter_table[0], args.counter_table[1:])
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
