@@ -423,8 +423,41 @@ def decode_extras(msa, din, block_keys, wd, dws, dout, steps):
     b2b = _median_ms(decode, steps, 3) * 1e3
     gen = _median_ms(gen_step, steps, 3) * 1e3
     dbytes = _decode_bytes(wd)
+    # the decode captured once in a HIP graph, as a serving loop would run
+    # it, and `n` replays enqueued back to back between two events (the GPU
+    # never waits for the host); the same for `n` eager calls
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        decode()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        decode()
+    graph.replay()
+    torch.cuda.synchronize()
+    n = max(steps, 20)
+
+    def queued_us(fn):
+        a, b = _events(1)[0]
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / n
+
+    graph_us = queued_us(graph.replay)
+    queued = queued_us(decode)
     return {"decode_back_to_back_us": round(b2b, 2), "decode_back_to_back_frac_hbm_peak":
             round(dbytes / (b2b * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "decode_graph_replay_us": round(graph_us, 2),
+            "decode_graph_replay_frac_hbm_peak": round(dbytes / (graph_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "decode_queued_us": round(queued, 2),
+            "decode_graph_what": f"the decode captured in a HIP graph, {n} replays enqueued back to back between "
+                                 "two events (decode_queued_us: the same for eager calls); the kept blocks may "
+                                 "still sit in the memory-side cache",
             "generation_step_us": round(gen, 2),
             "generation_step_what": "append one token per sequence (K/V rows, running index-key sum, block "
                                     "summary) + decode, back to back",

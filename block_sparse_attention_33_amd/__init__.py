@@ -456,6 +456,16 @@ def msa_decode_step(q, q_idx, k_new, v_new, k_idx_new, k_cache, v_cache, open_su
     return (out, sel) if return_sel else out
 
 
+def _on_device(lengths, B, dev):
+    """True for an int32 [B] tensor on the GPU (read by the kernels)."""
+    if isinstance(lengths, torch.Tensor) and lengths.device.type == "cuda":
+        _need(lengths, "lengths", torch.int32, 1, dev)
+        if lengths.shape[0] != B or not lengths.is_contiguous():
+            raise ValueError(f"device lengths must be a contiguous int32 tensor of {B} entries")
+        return True
+    return False
+
+
 def _lengths(lengths, B):
     vals = [int(x) for x in (lengths.tolist() if isinstance(lengths, torch.Tensor) else lengths)]
     if len(vals) != B:
@@ -468,7 +478,9 @@ def msa_decode_varlen(q, q_idx, k_cache, v_cache, block_keys, lengths, block_siz
     """Decode of a ragged batch: sequence b's query at position lengths[b] -
     1 over its first lengths[b] cached tokens (caches [B, G, C, D] of
     capacity C, block_keys [B, G, ceil(C/bs), di]); lengths: host list or
-    CPU tensor -> out [B, Hq, D] bf16."""
+    CPU tensor, or an int32 [B] tensor on the GPU read by the kernels (a
+    length outside 1 .. C then gives a zero row and sel -1) -> out
+    [B, Hq, D] bf16."""
     _need(q, "q", torch.bfloat16, 3)
     dev = q.device
     _need(q_idx, "q_idx", torch.int8, 3, dev)
@@ -491,6 +503,12 @@ def msa_decode_varlen(q, q_idx, k_cache, v_cache, block_keys, lengths, block_siz
     if sel is not None:
         _need(sel, "sel", torch.int32, 3, dev)
     ws, ws_bytes = _workspace(MSA_OP_DECODE, dims, dev, workspace)
+    if _on_device(lengths, B, dev):
+        _check(_lib.load().msa_decode_varlen_device(ctypes.byref(dims), _ptr(lengths), _ptr(q), _ptr(q_idx),
+                                                    _ptr(k_cache), _ptr(v_cache), _ptr(block_keys), _ptr(out),
+                                                    _ptr(sel), _ptr(ws), ws_bytes, _stream(dev)),
+               "msa_decode_varlen_device")
+        return (out, sel) if return_sel else out
     _check(_lib.load().msa_decode_varlen(ctypes.byref(dims), _lengths(lengths, B), _ptr(q), _ptr(q_idx),
                                          _ptr(k_cache), _ptr(v_cache), _ptr(block_keys), _ptr(out), _ptr(sel),
                                          _ptr(ws), ws_bytes, _stream(dev)), "msa_decode_varlen")
@@ -523,8 +541,9 @@ def msa_decode_step_varlen(q, q_idx, k_new, v_new, k_idx_new, k_cache, v_cache, 
                            block_size: int, top_k: int, softmax_scale: float = 0.0, out=None, sel=None,
                            return_sel: bool = False, workspace=None):
     """msa_decode_step with each sequence's own length (host list or CPU
-    tensor): sequence b's new token goes to row lengths[b] - 1 of its caches,
-    then its query there is decoded -> out [B, Hq, D] bf16."""
+    tensor, or an int32 [B] tensor on the GPU read by the kernels):
+    sequence b's new token goes to row lengths[b] - 1 of its caches, then
+    its query there is decoded -> out [B, Hq, D] bf16."""
     _need(q, "q", torch.bfloat16, 3)
     dev = q.device
     _need(q_idx, "q_idx", torch.int8, 3, dev)
@@ -555,6 +574,13 @@ def msa_decode_step_varlen(q, q_idx, k_new, v_new, k_idx_new, k_cache, v_cache, 
     if sel is not None:
         _need(sel, "sel", torch.int32, 3, dev)
     ws, ws_bytes = _workspace(MSA_OP_DECODE, dims, dev, workspace)
+    if _on_device(lengths, B, dev):
+        _check(_lib.load().msa_decode_step_varlen_device(ctypes.byref(dims), _ptr(lengths), _ptr(q), _ptr(q_idx),
+                                                         _ptr(k_new), _ptr(v_new), _ptr(k_idx_new), _ptr(k_cache),
+                                                         _ptr(v_cache), _ptr(open_sums), _ptr(block_keys),
+                                                         _ptr(out), _ptr(sel), _ptr(ws), ws_bytes, _stream(dev)),
+               "msa_decode_step_varlen_device")
+        return (out, sel) if return_sel else out
     _check(_lib.load().msa_decode_step_varlen(ctypes.byref(dims), _lengths(lengths, B), _ptr(q), _ptr(q_idx),
                                               _ptr(k_new), _ptr(v_new), _ptr(k_idx_new), _ptr(k_cache),
                                               _ptr(v_cache), _ptr(open_sums), _ptr(block_keys), _ptr(out),

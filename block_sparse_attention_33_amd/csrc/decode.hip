@@ -287,7 +287,29 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(const uint16_t* __restri
   const int K = sh.top_k;
   const int kp = K - 1;
   const int L = sh.lens != nullptr ? sh.lens[b] : sh.L;  // the unit's cached tokens
-  const int own = (L - 1) / sh.bs;                     // candidates are blocks 0 .. own - 1
+  if (L < 1 || L > sh.Lc) {
+    // a length outside 1 .. capacity (lengths read from device memory are
+    // not checked on the host): no selection (-1), a zero output row, or a
+    // workgroup state with no key (max -inf, sum 0), which the merge turns
+    // into zeros; nothing else is read.  The test is the same for the whole
+    // workgroup.
+    if (part == 0 && tid < K) sel_out[(size_t)u * K + tid] = -1;
+    if (tid < r * 32) {
+      const int h = tid >> 5, d0 = 4 * (tid & 31);
+      if (n_split > 1) {
+        float* srow = state + (((size_t)u * n_split + part) * r + h) * (kHeadDim + 2);
+        *reinterpret_cast<f32x4_t*>(srow + d0) = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (d0 == 0) {
+          srow[kHeadDim] = -__builtin_inff();
+          srow[kHeadDim + 1] = 0.f;
+        }
+      } else {
+        *reinterpret_cast<u32x2_t*>(out + ((size_t)b * sh.Hq + g * r + h) * kHeadDim + d0) = u32x2_t{0u, 0u};
+      }
+    }
+    return;
+  }
+  const int own = (L - 1) / sh.bs;  // candidates are blocks 0 .. own - 1
   // the unit's query rows in LDS (rows r .. 31 zero), read per slot
   if (tid < 32 * 16) {
     const int row = tid >> 4, ch = tid & 15;
@@ -475,13 +497,16 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
     const f32x4_t o0 = *reinterpret_cast<const f32x4_t*>(s0 + d0);
     const f32x4_t o1 = *reinterpret_cast<const f32x4_t*>(s1 + d0);
     // a share with no kept block has m = -inf, weight 0 (M is finite: the
-    // own block is always kept)
+    // own block is always kept, unless the unit's length was out of range
+    // and both states hold no key: then the row is zero)
     const float M = fmaxf(m0, m1);
-    const float w0 = fast_exp2(m0 - M), w1 = fast_exp2(m1 - M);
-    const float inv = 1.0f / fmaf(w0, l0, w1 * l1);
+    const bool none = M == -__builtin_inff();
+    const float Mu = none ? 0.f : M;
+    const float w0 = fast_exp2(m0 - Mu), w1 = fast_exp2(m1 - Mu);
+    const float inv = none ? 0.f : 1.0f / fmaf(w0, l0, w1 * l1);
     float v[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = fmaf(w0, o0[e], w1 * o1[e]) * inv;
+    for (int e = 0; e < 4; ++e) v[e] = none ? 0.f : fmaf(w0, o0[e], w1 * o1[e]) * inv;
     u32x2_t wv;
     wv.x = pack_bf16x2(v[0], v[1]);
     wv.y = pack_bf16x2(v[2], v[3]);
@@ -502,7 +527,10 @@ __global__ __launch_bounds__(64) void append_kernel(const uint16_t* __restrict__
                                                     int8_t* __restrict__ block_keys, DecodeShape sh, int pos) {
   const int u = blockIdx.x;
   const int l = threadIdx.x;
-  if (sh.lens != nullptr) pos = sh.lens[u / sh.G] - 1;  // the unit's own position
+  if (sh.lens != nullptr) {
+    pos = sh.lens[u / sh.G] - 1;  // the unit's own position
+    if (pos < 0 || pos >= sh.Lc) return;  // a length outside 1 .. capacity: nothing appended
+  }
   const size_t row = ((size_t)u * sh.Lc + pos) * kHeadDim;
   if (l < 16)
     reinterpret_cast<u32x4_t*>(k_cache + row)[l] = reinterpret_cast<const u32x4_t*>(k_new + (size_t)u * kHeadDim)[l];

@@ -638,7 +638,7 @@ const char* msa_status_string(int status) {
   }
 }
 
-int msa_version(void) { return 10700; }
+int msa_version(void) { return 10800; }
 
 int msa_backward_pass_rows(const msa_dims* dims, size_t ws_bytes, int32_t* rows) {
   Dims d;
@@ -1156,6 +1156,45 @@ int msa_decode_step_varlen(const msa_dims* dims, const int32_t* lengths, const u
   MSA_LAUNCH_NAMED("append", s, msa::launch_append(sh, k_new, v_new, k_idx_new, k_cache, v_cache, open_sums,
                                                    block_keys, (int)longest - 1, s));
   return run_decode(d, longest, lens, q, q_idx, k_cache, v_cache, block_keys, out, sel, ws, ws_bytes, s);
+}
+
+int msa_decode_varlen_device(const msa_dims* dims, const int32_t* lengths, const uint16_t* q, const int8_t* q_idx,
+                             const uint16_t* k_cache, const uint16_t* v_cache, const int8_t* block_keys,
+                             uint16_t* out, int32_t* sel, void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  int st = check_dims(dims, &d);
+  if (st != MSA_OK) return st;
+  if (d.k > kMaxSparseTopK) return MSA_ERR_UNSUPPORTED;
+  if (!lengths || !q || !q_idx || !k_cache || !v_cache || !block_keys || !out) return MSA_ERR_INVALID_ARG;
+  // the kernels read each sequence's length and treat one outside 1 .. C
+  // as an empty row; the launch is sized for the capacity
+  return run_decode(d, d.S, lengths, q, q_idx, k_cache, v_cache, block_keys, out, sel, ws, ws_bytes,
+                    (hipStream_t)stream);
+}
+
+int msa_decode_step_varlen_device(const msa_dims* dims, const int32_t* lengths, const uint16_t* q,
+                                  const int8_t* q_idx, const uint16_t* k_new, const uint16_t* v_new,
+                                  const int8_t* k_idx_new, uint16_t* k_cache, uint16_t* v_cache, int32_t* open_sums,
+                                  int8_t* block_keys, uint16_t* out, int32_t* sel, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  Dims d;
+  int st = check_dims(dims, &d);
+  if (st != MSA_OK) return st;
+  if (d.k > kMaxSparseTopK) return MSA_ERR_UNSUPPORTED;
+  if (!lengths || !q || !q_idx || !k_new || !v_new || !k_idx_new || !k_cache || !v_cache || !open_sums ||
+      !block_keys || !out)
+    return MSA_ERR_INVALID_ARG;
+  DecodeLayout L;
+  st = decode_layout(d, &L);
+  if (st != MSA_OK) return st;
+  st = check_ws(ws, ws_bytes, L.total);
+  if (st != MSA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  msa::DecodeShape sh = decode_shape(d, d.S);
+  sh.lens = lengths;
+  MSA_LAUNCH_NAMED("append", s, msa::launch_append(sh, k_new, v_new, k_idx_new, k_cache, v_cache, open_sums,
+                                                   block_keys, 0, s));
+  return run_decode(d, d.S, lengths, q, q_idx, k_cache, v_cache, block_keys, out, sel, ws, ws_bytes, s);
 }
 
 int msa_profile_enable(int on) {

@@ -391,6 +391,27 @@ int msa_decode_step_varlen(const msa_dims* dims, const int32_t* lengths, const u
                            int32_t* open_sums, int8_t* block_keys, uint16_t* out, int32_t* sel, void* ws,
                            size_t ws_bytes, void* stream);
 
+/* The same two calls with the lengths in DEVICE memory (int32 [batch]), read
+ * by the kernels when they run: a generation loop captured once in a HIP
+ * graph then replays every step, the caller advancing the lengths on the
+ * device between replays (host lengths travel in the captured kernel
+ * arguments and stay those of the capture).  The values cannot be checked
+ * on the host; a sequence whose length lies outside 1 .. C gets a zero
+ * output row and sel row -1, and its caches, summaries and open sums are
+ * left as they are -- no memory outside the given arrays is touched.  For
+ * lengths in range the results are those of msa_decode_varlen and
+ * msa_decode_step_varlen.  ws/ws_bytes: at least
+ * msa_workspace_bytes(MSA_OP_DECODE). */
+int msa_decode_varlen_device(const msa_dims* dims, const int32_t* lengths, const uint16_t* q,
+                             const int8_t* q_idx, const uint16_t* k_cache, const uint16_t* v_cache,
+                             const int8_t* block_keys, uint16_t* out, int32_t* sel, void* ws, size_t ws_bytes,
+                             void* stream);
+int msa_decode_step_varlen_device(const msa_dims* dims, const int32_t* lengths, const uint16_t* q,
+                                  const int8_t* q_idx, const uint16_t* k_new, const uint16_t* v_new,
+                                  const int8_t* k_idx_new, uint16_t* k_cache, uint16_t* v_cache,
+                                  int32_t* open_sums, int8_t* block_keys, uint16_t* out, int32_t* sel, void* ws,
+                                  size_t ws_bytes, void* stream);
+
 /* Optional per-kernel timing.  While enabled (on != 0), every kernel the
  * entry points enqueue is bracketed by two HIP events on the same stream and
  * recorded under its kernel name; disabled by default.  Returns MSA_OK, or

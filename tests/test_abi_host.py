@@ -48,7 +48,7 @@ def test_status_strings(lib):
                          (-3, "MSA_ERR_WORKSPACE"), (-4, "MSA_ERR_HIP"), (-5, "MSA_ERR_SCRATCH")]:
         assert lib.msa_status_string(code).decode().startswith(prefix)
     assert lib.msa_status_string(12345).decode() == "unknown MSA status"
-    assert lib.msa_version() == 10700
+    assert lib.msa_version() == 10800
 
 
 def D(**kw):
@@ -219,6 +219,26 @@ def test_decode_varlen_validation(lib):
     assert lib.msa_decode_init_varlen(ctypes.byref(dims), _cu(0, 0, 0), None, FAKE, FAKE, None) == -1
     # all lengths 0: nothing to pool, nothing enqueued
     assert lib.msa_decode_init_varlen(ctypes.byref(dims), _cu(0, 0, 0), FAKE, FAKE, FAKE, None) == 0
+
+
+def test_decode_varlen_device_validation(lib):
+    """Device-resident lengths: the pointers (lengths included) must be
+    given and the workspace must hold msa_decode's; the values themselves
+    are checked by the kernels, not here."""
+    dims = D(batch=3, seq_len=5000, n_q_heads=8, n_kv_heads=2)
+    st, lo, hi = _ws(lib, _lib.MSA_OP_DECODE, dims)
+    for i in range(7):  # lengths, q, q_idx, k_cache, v_cache, block_keys, out
+        a = [FAKE] * 7
+        a[i] = None
+        assert lib.msa_decode_varlen_device(ctypes.byref(dims), *a, None, FAKE, hi, None) == -1
+    for i in range(11):
+        a = [FAKE] * 11
+        a[i] = None
+        assert lib.msa_decode_step_varlen_device(ctypes.byref(dims), *a, None, FAKE, hi, None) == -1
+    assert lib.msa_decode_varlen_device(ctypes.byref(dims), *([FAKE] * 7), None, FAKE, lo - 1, None) == -3
+    assert lib.msa_decode_step_varlen_device(ctypes.byref(dims), *([FAKE] * 11), None, None, hi, None) == -3
+    big_k = D(batch=3, seq_len=5000, n_q_heads=8, n_kv_heads=2, top_k=40)
+    assert lib.msa_decode_varlen_device(ctypes.byref(big_k), *([FAKE] * 7), None, FAKE, 1 << 30, None) == -2
 
 
 def test_backward_validation(lib):

@@ -170,3 +170,62 @@ def test_prefill_graph_replays():
     ref = (out.clone(), sel.clone())
     g = _capture(call)
     _check_replays(g, [out, sel], ref)
+
+
+def test_generation_loop_graph_device_lengths():
+    """A ragged generation loop captured once: the step reads its lengths
+    from device memory, so each of 40 replays -- inputs copied into the
+    captured buffers and the lengths advanced on the device before it --
+    decodes the next position.  Every step's output and selection, and the
+    caches, summaries and open sums at the end, are bit-equal to the same
+    steps run eagerly with host lengths on a copy of the state."""
+    w = get_workload("decode_b16_256k", n_q_heads=8, n_kv_heads=2, block_size=64, top_k=6)
+    L0s, steps = [1, 63, 64, 500], 40
+    B, C, bs, k = len(L0s), max(L0s) + steps + 8, w.block_size, w.top_k
+    _say(f"[graph] generation loop L0={L0s} steps={steps}")
+    tr = decode_inputs(w, seed=31, device=DEV, seq_len=C, batch=B)
+    kc, vc = tr["k_cache"].clone(), tr["v_cache"].clone()
+    for b, L0 in enumerate(L0s):
+        kc[b, :, L0:] = 0
+        vc[b, :, L0:] = 0
+    bk, osum = msa.msa_decode_init_varlen(tr["k_idx_cache"], L0s, bs)
+    ekc, evc, ebk, eos = kc.clone(), vc.clone(), bk.clone(), osum.clone()  # the eager copy
+    lens = torch.tensor([L0 + 1 for L0 in L0s], dtype=torch.int32, device=DEV)
+    qb = torch.empty((B, w.n_q_heads, 128), dtype=torch.bfloat16, device=DEV)
+    qib = torch.empty((B, w.n_kv_heads, 64), dtype=torch.int8, device=DEV)
+    knb = torch.empty((B, w.n_kv_heads, 128), dtype=torch.bfloat16, device=DEV)
+    vnb = torch.empty_like(knb)
+    kinb = torch.empty((B, w.n_kv_heads, 64), dtype=torch.int8, device=DEV)
+    dims = msa.make_dims(B, C, w.n_q_heads, w.n_kv_heads, bs, k)
+    ws = _decode_ws(dims)
+    out = torch.empty_like(qb)
+    sel = torch.empty((B, w.n_kv_heads, k), dtype=torch.int32, device=DEV)
+    ar = torch.arange(B, device=DEV)
+
+    def call():
+        msa.msa_decode_step_varlen(qb, qib, knb, vnb, kinb, kc, vc, osum, bk, lens, bs, k, out=out, sel=sel,
+                                   workspace=ws)
+
+    # capture without running a step on the real state: the warm-up runs on
+    # copies
+    state = [kc, vc, osum, bk]
+    saved = [t.clone() for t in state]
+    g = _capture(call)
+    for t, s0 in zip(state, saved):
+        t.copy_(s0)
+    for i in range(steps):
+        hl = [L0 + i + 1 for L0 in L0s]
+        pos = torch.tensor([x - 1 for x in hl], device=DEV)
+        qs = decode_inputs(w, seed=900 + i, device=DEV, seq_len=1, batch=B)
+        qb.copy_(qs["q"])
+        qib.copy_(qs["q_idx"])
+        knb.copy_(tr["k_cache"][ar, :, pos])
+        vnb.copy_(tr["v_cache"][ar, :, pos])
+        kinb.copy_(tr["k_idx_cache"][ar, :, pos])
+        lens.copy_(torch.tensor(hl, dtype=torch.int32))
+        torch.cuda.synchronize()
+        g.replay()
+        eo, es = msa.msa_decode_step_varlen(qb, qib, knb, vnb, kinb, ekc, evc, eos, ebk, hl, bs, k, return_sel=True)
+        torch.cuda.synchronize()
+        assert torch.equal(out, eo) and torch.equal(sel, es), f"step {i}: the replay differs from the eager step"
+    assert torch.equal(kc, ekc) and torch.equal(vc, evc) and torch.equal(bk, ebk) and torch.equal(osum, eos)

@@ -671,6 +671,47 @@ def test_decode_varlen_rows():
     _free()
 
 
+def test_decode_varlen_device_lengths():
+    """Lengths in device memory, read by the kernels: bit-equal to the
+    host-lengths call for lengths in range; a length outside 1 .. C (0,
+    C + 1, -7) gives a zero output row and sel -1, leaves the other
+    sequences' rows unchanged, and an out-of-range step appends nothing."""
+    w = get_workload("decode_b16_256k", n_q_heads=8, n_kv_heads=2, block_size=64, top_k=8)
+    C, bs, k = 9000, w.block_size, w.top_k
+    good = [1, 900, 65, 9000, 4000, 3000]
+    bad = [1, 0, 65, C + 1, -7, 3000]
+    B = len(good)
+    _say(f"[decode varlen device] lengths={good} / {bad} C={C}")
+    inp = decode_inputs(w, seed=93, device=DEV, seq_len=C, batch=B)
+    bk, osum = msa.msa_decode_init_varlen(inp["k_idx_cache"], good, bs)
+    args = (inp["q"], inp["q_idx"], inp["k_cache"], inp["v_cache"], bk)
+    oh, sh = msa.msa_decode_varlen(*args, good, bs, k, return_sel=True)
+    od, sd = msa.msa_decode_varlen(*args, torch.tensor(good, dtype=torch.int32, device=DEV), bs, k, return_sel=True)
+    ob, sb = msa.msa_decode_varlen(*args, torch.tensor(bad, dtype=torch.int32, device=DEV), bs, k, return_sel=True)
+    torch.cuda.synchronize()
+    assert torch.equal(od, oh) and torch.equal(sd, sh), "device lengths differ from host lengths"
+    for b in range(B):
+        if 1 <= bad[b] <= C:
+            assert torch.equal(ob[b], oh[b]) and torch.equal(sb[b], sh[b]), f"sequence {b} changed"
+        else:
+            assert int(ob[b].float().abs().sum()) == 0 and bool((sb[b] == -1).all()), f"sequence {b} not empty"
+    # a step with out-of-range lengths leaves those sequences' state alone
+    kc, vc, bk2, os2 = inp["k_cache"].clone(), inp["v_cache"].clone(), bk.clone(), osum.clone()
+    new = decode_inputs(w, seed=94, device=DEV, seq_len=1, batch=B)
+    lens_next = torch.tensor([x + 1 if 1 <= x < C else x for x in bad], dtype=torch.int32, device=DEV)
+    o, s_ = msa.msa_decode_step_varlen(new["q"], new["q_idx"], new["k_cache"][:, :, 0].contiguous(),
+                                       new["v_cache"][:, :, 0].contiguous(), new["k_idx_cache"][:, :, 0].contiguous(),
+                                       kc, vc, os2, bk2, lens_next, bs, k, return_sel=True)
+    torch.cuda.synchronize()
+    for b in range(B):
+        if not 1 <= bad[b] <= C:
+            assert torch.equal(kc[b], inp["k_cache"][b]) and torch.equal(vc[b], inp["v_cache"][b])
+            assert torch.equal(bk2[b], bk[b]) and torch.equal(os2[b], osum[b])
+            assert int(o[b].float().abs().sum()) == 0 and bool((s_[b] == -1).all())
+    del inp, kc, vc
+    _free()
+
+
 def test_decode_step_varlen_generation():
     """Ragged generation: msa_decode_init_varlen on 1, 63, 64 and 200 cached
     tokens, then 70 msa_decode_step_varlen steps, each sequence appending at
