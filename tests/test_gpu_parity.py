@@ -572,6 +572,9 @@ def _decode_case(w, L, B, seed, n_check_units=None):
     # more than 2048 and more than 4096 candidate blocks (8 and 16 per thread)
     (150000, 1, dict(n_q_heads=8, n_kv_heads=1, block_size=64, top_k=16)),
     (300001, 1, dict(n_q_heads=8, n_kv_heads=1, block_size=64, top_k=20)),
+    # the largest cache the decode supports: 8193 blocks of 128 (over 1M
+    # tokens), 8192 candidates before the own block
+    (8193 * 128, 1, dict(n_q_heads=8, n_kv_heads=2, block_size=128, top_k=16)),
 ])
 def test_decode_small(L, B, over):
     w = get_workload("decode_b16_256k", **over)
