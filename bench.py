@@ -426,18 +426,23 @@ def decode_extras(msa, din, block_keys, wd, dws, dout, steps):
     # the decode captured once in a HIP graph, as a serving loop would run
     # it, and `n` replays enqueued back to back between two events (the GPU
     # never waits for the host); the same for `n` eager calls
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        decode()
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        decode()
-    graph.replay()
-    torch.cuda.synchronize()
     n = max(steps, 20)
+    graph, graph_error = None, None
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            decode()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            decode()
+        graph.replay()
+        torch.cuda.synchronize()
+    except RuntimeError as e:  # the record keeps the other numbers
+        graph_error = str(e)[:200]
+        graph = None
 
     def queued_us(fn):
         a, b = _events(1)[0]
@@ -448,12 +453,13 @@ def decode_extras(msa, din, block_keys, wd, dws, dout, steps):
         torch.cuda.synchronize()
         return a.elapsed_time(b) * 1e3 / n
 
-    graph_us = queued_us(graph.replay)
+    graph_us = queued_us(graph.replay) if graph is not None else None
     queued = queued_us(decode)
     return {"decode_back_to_back_us": round(b2b, 2), "decode_back_to_back_frac_hbm_peak":
             round(dbytes / (b2b * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
-            "decode_graph_replay_us": round(graph_us, 2),
-            "decode_graph_replay_frac_hbm_peak": round(dbytes / (graph_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "decode_graph_replay_us": round(graph_us, 2) if graph_us else None,
+            "decode_graph_replay_frac_hbm_peak":
+                round(dbytes / (graph_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4) if graph_us else graph_error,
             "decode_queued_us": round(queued, 2),
             "decode_graph_what": f"the decode captured in a HIP graph, {n} replays enqueued back to back between "
                                  "two events (decode_queued_us: the same for eager calls); the kept blocks may "
