@@ -67,62 +67,96 @@ __global__ __launch_bounds__(256) void chunk_total_kernel(const int32_t* __restr
   counts[i] = total;
 }
 
-// One workgroup: each thread scans a contiguous run of the counts, the run
-// totals are scanned in LDS, then every thread writes its exclusive offsets.
+// One workgroup scans the counts in batches of 16 rows of 1024 (thread i
+// holds element i of each row, so every load and store of a row is one
+// contiguous stretch, and a batch's loads are issued together): the
+// inclusive sums within each wave come from lane shuffles for the 16 rows
+// at once, one wave scans the batch's 256 (row, wave) totals in order, with
+// the carry of the earlier batches, and every thread adds its wave's
+// prefix.  Also the items: ceil(count / tpi) per row.
 __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ counts,
                                                     int32_t* __restrict__ row_ptr,
                                                     int32_t* __restrict__ item_ptr, int n,
                                                     int tpi) {
-  __shared__ int sa[1024];
-  __shared__ int sb[1024];
+  constexpr int kB = 16;             // rows per batch
+  __shared__ int wt[2][kB * 16];     // (row, wave) totals, then their exclusive prefixes
+  __shared__ int bt[2];              // the batch's totals
   const int tid = threadIdx.x;
-  const int per = (n + 1023) / 1024;
-  const int i0 = min(n, tid * per);
-  const int i1 = min(n, i0 + per);
-  // the run's counts are loaded 16 at a time (one memory round trip per 16
-  // instead of one per count)
-  constexpr int kB = 16;
-  int a = 0, b = 0;
-  for (int i = i0; i < i1; i += kB) {
-    int c[kB];
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  int carry_a = 0, carry_b = 0;  // the same in every thread
+  for (int base = 0; base < n; base += 1024 * kB) {
+    int c[kB], ia[kB], ib[kB];
 #pragma unroll
-    for (int j = 0; j < kB; ++j) c[j] = i + j < i1 ? counts[i + j] : 0;
-#pragma unroll
-    for (int j = 0; j < kB; ++j) {
-      a += c[j];
-      b += (c[j] + tpi - 1) / tpi;
+    for (int r = 0; r < kB; ++r) {
+      const int i = base + 1024 * r + tid;
+      c[r] = i < n ? counts[i] : 0;
     }
-  }
-  sa[tid] = a;
-  sb[tid] = b;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int va = tid >= off ? sa[tid - off] : 0;
-    const int vb = tid >= off ? sb[tid - off] : 0;
-    __syncthreads();
-    sa[tid] += va;
-    sb[tid] += vb;
-    __syncthreads();
-  }
-  int ea = sa[tid] - a;
-  int eb = sb[tid] - b;
-  for (int i = i0; i < i1; i += kB) {
-    int c[kB];
 #pragma unroll
-    for (int j = 0; j < kB; ++j) c[j] = i + j < i1 ? counts[i + j] : 0;
+    for (int r = 0; r < kB; ++r) {
+      ia[r] = c[r];
+      ib[r] = (c[r] + tpi - 1) / tpi;
+    }
 #pragma unroll
-    for (int j = 0; j < kB; ++j) {
-      if (i + j < i1) {
-        row_ptr[i + j] = ea;
-        item_ptr[i + j] = eb;
+    for (int off = 1; off < 64; off <<= 1) {
+#pragma unroll
+      for (int r = 0; r < kB; ++r) {
+        const int ua = __shfl_up(ia[r], off), ub = __shfl_up(ib[r], off);
+        if (lane >= off) {
+          ia[r] += ua;
+          ib[r] += ub;
+        }
       }
-      ea += c[j];
-      eb += (c[j] + tpi - 1) / tpi;
     }
+    if (lane == 63) {
+#pragma unroll
+      for (int r = 0; r < kB; ++r) {
+        wt[0][r * 16 + w] = ia[r];
+        wt[1][r * 16 + w] = ib[r];
+      }
+    }
+    __syncthreads();
+    if (w == 0) {
+      // lane l: totals 4 l .. 4 l + 3 of each kind, in (row, wave) order
+#pragma unroll
+      for (int kind = 0; kind < 2; ++kind) {
+        int v[4], sum = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[e] = wt[kind][4 * lane + e];
+          sum += v[e];
+        }
+        int incl = sum;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int up = __shfl_up(incl, off);
+          if (lane >= off) incl += up;
+        }
+        int run = (kind == 0 ? carry_a : carry_b) + incl - sum;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          wt[kind][4 * lane + e] = run;
+          run += v[e];
+        }
+        if (lane == 63) bt[kind] = incl;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kB; ++r) {
+      const int i = base + 1024 * r + tid;
+      if (i < n) {
+        row_ptr[i] = wt[0][r * 16 + w] + ia[r] - c[r];
+        item_ptr[i] = wt[1][r * 16 + w] + ib[r] - (c[r] + tpi - 1) / tpi;
+      }
+    }
+    carry_a += bt[0];
+    carry_b += bt[1];
+    __syncthreads();  // every thread has read the prefixes before the next batch writes them
   }
-  if (tid == 1023) {
-    row_ptr[n] = sa[1023];
-    item_ptr[n] = sb[1023];
+  if (tid == 0) {
+    row_ptr[n] = carry_a;
+    item_ptr[n] = carry_b;
   }
 }
 
