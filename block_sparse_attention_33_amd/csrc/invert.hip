@@ -194,10 +194,13 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
                                                       const int32_t* __restrict__ H,
                                                       uint32_t* __restrict__ entries, int S, int nb,
                                                       int bs_log2, int top_k, ChunkPlan cp, int q0,
-                                                      int with_own) {
+                                                      int with_own, int units) {
   extern __shared__ int32_t cursor[];
-  const int c = blockIdx.x;
-  const int u = blockIdx.y;
+  // workgroup i runs on XCD i % 8 and takes unit i % units, chunk i / units:
+  // with a multiple of 8 units every chunk of a unit -- whose segments of a
+  // block's list are adjacent and share cache lines -- writes through one L2
+  const int u = (int)(blockIdx.x % (unsigned)units);
+  const int c = (int)(blockIdx.x / (unsigned)units);
   const int32_t* src = H + ((size_t)u * cp.n_chunks + c) * nb;
   for (int j = threadIdx.x; j < nb; j += 256) cursor[j] = src[j];
   __syncthreads();
@@ -257,8 +260,8 @@ hipError_t launch_scatter(const int32_t* sel, const int32_t* H, uint32_t* entrie
   const size_t lds = (size_t)nb * 4;
   const hipError_t attr = ensure_dynamic_lds(reinterpret_cast<const void*>(&scatter_kernel), kMaxInvertBlocks * 4);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(scatter_kernel, dim3(cp.n_chunks, units), dim3(256), lds, st, sel, H, entries, S, nb, bs_log2,
-                     top_k, cp, q0, with_own ? 1 : 0);
+  hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)(cp.n_chunks * units)), dim3(256), lds, st, sel, H, entries, S,
+                     nb, bs_log2, top_k, cp, q0, with_own ? 1 : 0, units);
   return hipGetLastError();
 }
 
