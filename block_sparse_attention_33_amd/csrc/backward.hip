@@ -478,14 +478,17 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const uint16_t* __restrict_
   const int n = min(sh.top_k - 1, (int)((sh.q0 + t) >> sh.bs_log2)) + 1;
   const uint16_t* src = part_dq + (((size_t)u * sh.n_q + t) * sh.top_k * sh.r + h) * kHeadDim + 8 * c16;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < n; s0 += 8) {
-    u32x4_t val[8];
+  // the loads of up to 16 partials are issued together: one memory round
+  // trip for top_k <= 16
+  constexpr int kB = 16;
+  for (int s0 = 0; s0 < n; s0 += kB) {
+    u32x4_t val[kB];
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
+    for (int s = 0; s < kB; ++s)
       if (s0 + s < n)
         val[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src + (size_t)(s0 + s) * sh.r * kHeadDim));
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
+    for (int s = 0; s < kB; ++s)
       if (s0 + s < n)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
