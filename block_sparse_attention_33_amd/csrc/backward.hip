@@ -59,12 +59,14 @@ struct BwdLds {
   static constexpr int kTrStride = Chunk<BS>::kTrStride;
   static constexpr int kKtStride = 2 * BS + 16;  // bytes per head-dim row of K^T
   static constexpr int kDsStride = 2 * BS + 16;  // bytes per query row of dS
-  static constexpr int kQn = 0;
+  // the row info first: its 24 reads per chunk then take immediate offsets
+  // (a ds instruction's offset field reaches 64 KiB)
+  static constexpr int kInfo = 0;  // lse2, delta, lim, entry: kChunkRows each
+  static constexpr int kQn = kInfo + 4 * kChunkRows * 4;
   static constexpr int kDn = kQn + kChunkRows * kNatStride;
   static constexpr int kQt = kDn + kChunkRows * kNatStride;
   static constexpr int kDt = kQt + kHeadDim * kTrStride;
-  static constexpr int kInfo = kDt + kHeadDim * kTrStride;  // lse2, delta, lim, entry: kChunkRows each
-  static constexpr int kDs = kInfo + 4 * kChunkRows * 4;
+  static constexpr int kDs = kDt + kHeadDim * kTrStride;
   static constexpr int kKt = kDs + kChunkRows * kDsStride;
   static constexpr int kDq = kKt + kHeadDim * kKtStride;  // dq tile: rows x head dims (bf16)
   static constexpr int kBytes = kDq + kChunkRows * kNatStride;
@@ -92,6 +94,12 @@ struct RowEnts {
   uint32_t e[RowStage<NT, CR>::kJobs][2];
   uint32_t info;
 };
+
+// The low halves of a and b as one word (a's in the low half), and the high
+// halves: one byte permute each (v_perm_b32 numbers b's bytes 4..7 and a's
+// 0..3).
+__device__ __forceinline__ uint32_t lo_halves(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
+__device__ __forceinline__ uint32_t hi_halves(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
 
 template <int TRS>
 __device__ __forceinline__ u32x4_t tr_frag(const char* base, int d, int rt, int h2, int hf) {
@@ -162,9 +170,9 @@ __global__ __launch_bounds__(2 * BS, 1) void bwd_kv_kernel(
       char* kt = lds + L::kKt;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        *reinterpret_cast<uint32_t*>(kt + (8 * c + 2 * e) * L::kKtStride + 4 * p) = (a[e] & 0xffffu) | (bb[e] << 16);
+        *reinterpret_cast<uint32_t*>(kt + (8 * c + 2 * e) * L::kKtStride + 4 * p) = lo_halves(a[e], bb[e]);
         *reinterpret_cast<uint32_t*>(kt + (8 * c + 2 * e + 1) * L::kKtStride + 4 * p) =
-            (a[e] >> 16) | (bb[e] & 0xffff0000u);
+            hi_halves(a[e], bb[e]);
       }
     }
   }
@@ -177,6 +185,15 @@ __global__ __launch_bounds__(2 * BS, 1) void bwd_kv_kernel(
   }
 
   // entries of chunk cc for this thread's rows
+  // Index arithmetic in 32 bits where it fits: a CSR row holds at most one
+  // entry per query token (< 2^26), b S + t < units S < 2^31, and
+  // (unit, token, slot) numbers stay below units S top_k < 2^31 (both
+  // checked on the host); row numbers of (token, head) take one 32 x 32 ->
+  // 64-bit multiply-add.
+  const uint32_t* ents = entries + e0;
+  auto ent_at = [&](int i) -> uint32_t {
+    return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(ents) + ((uint32_t)i << 2));
+  };
   auto load_ents = [&](int cc, Ents& re) {
 #pragma unroll
     for (int m = 0; m < Stage::kJobs; ++m) {
@@ -184,14 +201,18 @@ __global__ __launch_bounds__(2 * BS, 1) void bwd_kv_kernel(
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
         const int tk = cc * tpc + ((2 * p + x) >> sh.r_log2);
-        re.e[m][x] = entries[e0 + min(tk, n - 1)];
+        re.e[m][x] = ent_at(min(tk, n - 1));
       }
     }
-    re.info = entries[e0 + min(cc * tpc + ((tid & (kChunkRows - 1)) >> sh.r_log2), n - 1)];
+    re.info = ent_at(min(cc * tpc + ((tid & (kChunkRows - 1)) >> sh.r_log2), n - 1));
+  };
+  const uint32_t tok0 = (uint32_t)(b * sh.S + sh.q0);  // row b S + t of token t = q0 + (ent >> 5)
+  const uint32_t head0 = (uint32_t)(g * sh.r);
+  auto qrow = [&](uint32_t ent, int rho) -> uint64_t {
+    return (uint64_t)(tok0 + (ent >> 5)) * (uint32_t)sh.Hq + (head0 + (uint32_t)(rho & (sh.r - 1)));
   };
   auto row_ptr_q = [&](const uint16_t* base, uint32_t ent, int rho) -> const uint16_t* {
-    const int t = sh.q0 + (int)(ent >> 5);
-    return base + (((size_t)b * sh.S + t) * sh.Hq + g * sh.r + (rho & (sh.r - 1))) * kHeadDim;
+    return base + qrow(ent, rho) * kHeadDim;
   };
   auto load_rows = [&](int cc, const Ents& re, Stage& st) {
 #pragma unroll
@@ -209,7 +230,7 @@ __global__ __launch_bounds__(2 * BS, 1) void bwd_kv_kernel(
     const int tk = cc * tpc + (rho >> sh.r_log2);
     const bool valid = tk < n;
     const int t = sh.q0 + (int)(re.info >> 5);
-    const size_t ri = ((size_t)b * sh.S + t) * sh.Hq + g * sh.r + (rho & (sh.r - 1));
+    const uint64_t ri = qrow(re.info, rho);
     const float l2 = lse[ri] * kLog2e;
     st.lse2 = valid ? l2 : __builtin_inff();
     st.delta = delta[ri];
@@ -231,13 +252,13 @@ __global__ __launch_bounds__(2 * BS, 1) void bwd_kv_kernel(
         char* qt = lds + L::kQt;
         char* dt = lds + L::kDt;
         *reinterpret_cast<uint32_t*>(qt + (8 * c + 2 * e) * kTrStride + 4 * p) =
-            (st.qa[m][e] & 0xffffu) | (st.qb[m][e] << 16);
+            lo_halves(st.qa[m][e], st.qb[m][e]);
         *reinterpret_cast<uint32_t*>(qt + (8 * c + 2 * e + 1) * kTrStride + 4 * p) =
-            (st.qa[m][e] >> 16) | (st.qb[m][e] & 0xffff0000u);
+            hi_halves(st.qa[m][e], st.qb[m][e]);
         *reinterpret_cast<uint32_t*>(dt + (8 * c + 2 * e) * kTrStride + 4 * p) =
-            (st.da[m][e] & 0xffffu) | (st.db[m][e] << 16);
+            lo_halves(st.da[m][e], st.db[m][e]);
         *reinterpret_cast<uint32_t*>(dt + (8 * c + 2 * e + 1) * kTrStride + 4 * p) =
-            (st.da[m][e] >> 16) | (st.db[m][e] & 0xffff0000u);
+            hi_halves(st.da[m][e], st.db[m][e]);
       }
     }
     if (tid < kChunkRows) {
@@ -391,7 +412,8 @@ __global__ __launch_bounds__(2 * BS, 1) void bwd_kv_kernel(
       const u32x4_t val = *reinterpret_cast<const u32x4_t*>(lds + L::kDq + rho * kNatStride + 16 * (tid & 15));
       const uint32_t e = copy_ent[m];
       if (e != 0xffffffffu) {
-        const size_t pidx = (((size_t)u * sh.n_q + (e >> 5)) * sh.top_k + (e & 31u)) * sh.r + (rho & (sh.r - 1));
+        const uint32_t slot = ((uint32_t)u * (uint32_t)sh.n_q + (e >> 5)) * (uint32_t)sh.top_k + (e & 31u);
+        const uint64_t pidx = (uint64_t)slot * (uint32_t)sh.r + (uint32_t)(rho & (sh.r - 1));
         __builtin_nontemporal_store(val, reinterpret_cast<u32x4_t*>(part_dq + pidx * kHeadDim + 8 * (tid & 15)));
       }
     }
