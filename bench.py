@@ -582,6 +582,40 @@ def chunked_and_dense(msa, dev):
 
 # ------------------------------------------------------------------ main
 
+def machine_probes(msa, dev):
+    """What the chip sustains under plain load, beside its published peaks
+    (which stay the roofline's `peak`): the library's matrix-core probe, a
+    kernel of bf16 MFMAs on register operands only, and a 2 GiB device copy
+    (torch's copy kernel; bytes read plus bytes written)."""
+    import torch
+    nwg, iters = 2048, 20000  # 8 workgroups of 4 waves per CU; about 9 ms at the published peak
+    buf = torch.empty(nwg * 256, dtype=torch.float32, device=dev)
+    flop = [0.0]
+
+    def probe():
+        flop[0] = msa.msa_probe_mfma_bf16(nwg, iters, buf)
+
+    mfma_ms = _median_ms(probe, 5)
+    finite = bool(torch.isfinite(buf).all())
+    src = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    copy_ms = _median_ms(lambda: dst.copy_(src), 5)
+    del src, dst, buf
+    torch.cuda.empty_cache()
+    mfma_tflops = flop[0] / (mfma_ms * 1e-3) / 1e12
+    copy_gbs = 2 * (1 << 31) / (copy_ms * 1e-3) / 1e9
+    return {
+        "mfma_bf16_probe_tflops": round(mfma_tflops, 1),
+        "mfma_bf16_probe_frac_of_published": round(mfma_tflops / PEAK_BF16_TFLOPS, 4),
+        "mfma_probe_what": f"msa_probe_mfma_bf16: {nwg} workgroups x 4 waves x {iters} rounds of 4 independent "
+                           f"v_mfma_f32_32x32x16_bf16, register operands only, median of 5 launches"
+                           + ("" if finite else " (non-finite output)"),
+        "hbm_copy_gbs": round(copy_gbs, 1),
+        "hbm_copy_frac_of_published": round(copy_gbs / PEAK_HBM_GBS, 4),
+        "hbm_copy_what": "2 GiB device-to-device copy (torch), read + written bytes, median of 5",
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -800,6 +834,11 @@ def main():
         baselines.update(more)
         rec.update(chunked_and_dense(msa, dev))
         rec["training"] = training_extras(msa, dev)
+        rec["machine"] = machine_probes(msa, dev)
+        ach = rec["roofline"].get("achieved")
+        probe = rec["machine"]["mfma_bf16_probe_tflops"]
+        rec["roofline"]["probe_peak"] = probe
+        rec["roofline"]["frac_of_probe"] = round(ach / probe, 4) if (ach and probe) else None
     rec["cpu_baseline"] = baselines.get(HEADLINE)
     rec["cpu_baselines"] = baselines or None
     print(json.dumps(rec), flush=True)

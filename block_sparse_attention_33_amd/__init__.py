@@ -50,6 +50,19 @@ def msa_workspace_bytes(op, dims: MsaDims):
     return lo.value, hi.value
 
 
+def msa_probe_mfma_bf16(n_workgroups: int, iters: int, out: torch.Tensor) -> float:
+    """Enqueue the matrix-core probe (a kernel of bf16 MFMAs only) on the
+    current stream; out: float32 [n_workgroups * 256] on the GPU.  Returns
+    the FLOP the launch performs (time it with events on the stream)."""
+    _need(out, "out", torch.float32, 1)
+    if out.numel() < n_workgroups * 256:
+        raise ValueError("out needs n_workgroups * 256 floats")
+    flop = ctypes.c_double(0.0)
+    _check(_lib.load().msa_probe_mfma_bf16(int(n_workgroups), int(iters), _ptr(out), ctypes.byref(flop),
+                                           _stream(out.device)), "msa_probe_mfma_bf16")
+    return flop.value
+
+
 def profile_enable(on: bool = True):
     """Record every launch of the library's kernels with HIP events."""
     _check(_lib.load().msa_profile_enable(1 if on else 0), "msa_profile_enable")

@@ -76,6 +76,7 @@ SIGNATURES = {
                                               _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "msa_decode_varlen_device": (ctypes.c_int, [_DIMS] + [_P] * 9 + [ctypes.c_size_t, _P]),
     "msa_decode_step_varlen_device": (ctypes.c_int, [_DIMS] + [_P] * 13 + [ctypes.c_size_t, _P]),
+    "msa_probe_mfma_bf16": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, _P, ctypes.POINTER(ctypes.c_double), _P]),
     "msa_profile_enable": (ctypes.c_int, [ctypes.c_int]),
     "msa_profile_read": (ctypes.c_int, [ctypes.POINTER(MsaKernelTime), ctypes.c_int,
                                         ctypes.POINTER(ctypes.c_int)]),

@@ -18,7 +18,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmsa.so")
 ARCH = os.environ.get("MSA_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["index_branch.hip", "invert.hip", "main_branch.hip", "decode.hip", "backward.hip", "msa_api.cpp", "device_state.cpp"]
+SOURCES = ["index_branch.hip", "invert.hip", "main_branch.hip", "decode.hip", "backward.hip", "probe.hip", "msa_api.cpp",
+           "device_state.cpp"]
 
 COMMON = [
     "-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",

@@ -638,7 +638,7 @@ const char* msa_status_string(int status) {
   }
 }
 
-int msa_version(void) { return 10800; }
+int msa_version(void) { return 10900; }
 
 int msa_backward_pass_rows(const msa_dims* dims, size_t ws_bytes, int32_t* rows) {
   Dims d;
@@ -1195,6 +1195,15 @@ int msa_decode_step_varlen_device(const msa_dims* dims, const int32_t* lengths, 
   MSA_LAUNCH_NAMED("append", s, msa::launch_append(sh, k_new, v_new, k_idx_new, k_cache, v_cache, open_sums,
                                                    block_keys, 0, s));
   return run_decode(d, d.S, lengths, q, q_idx, k_cache, v_cache, block_keys, out, sel, ws, ws_bytes, s);
+}
+
+int msa_probe_mfma_bf16(int32_t n_workgroups, int32_t iters, float* out, double* flop, void* stream) {
+  if (n_workgroups < 1 || n_workgroups > (1 << 20) || iters < 1 || iters > (1 << 24) || out == nullptr)
+    return MSA_ERR_INVALID_ARG;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (flop != nullptr) *flop = msa::mfma_probe_flop(n_workgroups, iters);
+  MSA_LAUNCH_NAMED("mfma_probe", s, msa::launch_mfma_probe(out, n_workgroups, iters, s));
+  return MSA_OK;
 }
 
 int msa_profile_enable(int on) {

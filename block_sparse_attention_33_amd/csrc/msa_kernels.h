@@ -66,6 +66,12 @@ hipError_t launch_index_topk_at(const int8_t* q_idx, const int8_t* block_keys, i
 
 hipError_t launch_fill_i32(int32_t* p, int32_t value, size_t n, hipStream_t st);
 
+// Measurement aid: n_workgroups workgroups of 4 waves, each wave iters
+// rounds of 4 independent bf16 MFMAs on register operands; one float per
+// thread to out.  mfma_probe_flop: the FLOP one such launch performs.
+hipError_t launch_mfma_probe(float* out, int n_workgroups, int iters, hipStream_t st);
+double mfma_probe_flop(int n_workgroups, int iters);
+
 // Query -> block inversion (no global atomics).  Each query range of T
 // tokens is cut into m chunks of tpc tokens (n_chunks = n_ranges * m per
 // unit); H [U, n_chunks, nb] int32 holds per-chunk block counts, then (in

@@ -412,6 +412,19 @@ int msa_decode_step_varlen_device(const msa_dims* dims, const int32_t* lengths, 
                                   int32_t* open_sums, int8_t* block_keys, uint16_t* out, int32_t* sel, void* ws,
                                   size_t ws_bytes, void* stream);
 
+/* Measurement aid, not a step of the attention path: enqueues on `stream`
+ * one kernel made only of bf16 matrix-core products
+ * (v_mfma_f32_32x32x16_bf16 on register operands, four independent
+ * accumulators per wave, no memory traffic in its loop), so that the rate the
+ * chip sustains under load can be read beside its published dense peak.
+ * n_workgroups (1 .. 2^20) workgroups of 4 waves each run iters (1 .. 2^24)
+ * rounds of 4 products; out (device, n_workgroups * 256 floats, caller
+ * owned) receives one float per thread (the products' sum, finite).
+ * *flop (host; may be NULL) = the FLOP the launch performs.  Returns
+ * MSA_ERR_INVALID_ARG for arguments outside those ranges or out == NULL,
+ * MSA_ERR_HIP if the launch fails; time it with events on `stream`. */
+int msa_probe_mfma_bf16(int32_t n_workgroups, int32_t iters, float* out, double* flop, void* stream);
+
 /* Optional per-kernel timing.  While enabled (on != 0), every kernel the
  * entry points enqueue is bracketed by two HIP events on the same stream and
  * recorded under its kernel name; disabled by default.  Returns MSA_OK, or

@@ -25,7 +25,7 @@ def lib():
 def _declared():
     text = open(HEADER, encoding="utf-8").read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(msa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(msa_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_boundary():
@@ -48,7 +48,7 @@ def test_status_strings(lib):
                          (-3, "MSA_ERR_WORKSPACE"), (-4, "MSA_ERR_HIP"), (-5, "MSA_ERR_SCRATCH")]:
         assert lib.msa_status_string(code).decode().startswith(prefix)
     assert lib.msa_status_string(12345).decode() == "unknown MSA status"
-    assert lib.msa_version() == 10800
+    assert lib.msa_version() == 10900
 
 
 def D(**kw):
@@ -239,6 +239,16 @@ def test_decode_varlen_device_validation(lib):
     assert lib.msa_decode_step_varlen_device(ctypes.byref(dims), *([FAKE] * 11), None, None, hi, None) == -3
     big_k = D(batch=3, seq_len=5000, n_q_heads=8, n_kv_heads=2, top_k=40)
     assert lib.msa_decode_varlen_device(ctypes.byref(big_k), *([FAKE] * 7), None, FAKE, 1 << 30, None) == -2
+
+
+def test_mfma_probe_validation(lib):
+    """The matrix-core probe checks its arguments before any launch: 1 ..
+    2^20 workgroups, 1 .. 2^24 rounds, an output buffer."""
+    flop = ctypes.c_double(-1.0)
+    for nw, it, out in [(0, 10, FAKE), ((1 << 20) + 1, 10, FAKE), (8, 0, FAKE), (8, (1 << 24) + 1, FAKE),
+                        (8, 10, None)]:
+        assert lib.msa_probe_mfma_bf16(nw, it, out, ctypes.byref(flop), None) == -1
+    assert flop.value == -1.0  # nothing reported for a rejected call
 
 
 def test_backward_validation(lib):
