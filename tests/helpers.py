@@ -127,6 +127,26 @@ def oracle_prefill_rows_pooled(inp, w, rows, block_size=None, top_k=None):
                                     host_i8(inp["q_idx"]), host_i8(inp["k_idx"]), rows, bs, k)
 
 
+def oracle_query_grads_pooled(inp, dout, sel_rows, rows, block_size):
+    """The oracle's dq of query `rows` (float64 [B, R, Hq, D]) over worker
+    processes, from host copies of the device inputs; sel_rows int32
+    [B, G, R, top_k] are the rows' (oracle) selections.  Returns (dq, stats)."""
+    from oracle import pool as oracle_pool
+    rt = torch.as_tensor(rows, device=inp["q"].device)
+    return oracle_pool.query_grad_rows(host_bits(inp["q"][:, rt]), host_bits(dout[:, rt]), host_bits(inp["k"]),
+                                       host_bits(inp["v"]), sel_rows, rows, block_size)
+
+
+def oracle_kv_grads_pooled(inp, dout, sel, pairs, block_size):
+    """The oracle's dk, dv (float64 [B, P, block_size, D]) of key block j in
+    group g for each (j, g) of `pairs`, over worker processes; sel int32
+    [B, G, S, top_k] is every row's (oracle) selection.  Returns (dk, dv,
+    stats)."""
+    from oracle import pool as oracle_pool
+    return oracle_pool.kv_grad_pairs(host_bits(inp["q"]), host_bits(dout), host_bits(inp["k"]), host_bits(inp["v"]),
+                                     sel, pairs, block_size)
+
+
 def check_all_selections(gsel, qi, summ, S, bs, top_k, row_slice=8192, rows=None):
     """Every row of `rows` (default all): with the composite key score * 2^20
     - block (higher is better, ties to the lower block), the kept set is

@@ -25,7 +25,7 @@ import torch
 import block_sparse_attention_33_amd as msa
 from oracle import msa_oracle as O
 from synth import get_workload, grad_output, prefill_inputs, sample_rows
-from tests.helpers import host_f32, host_i8, record
+from tests.helpers import host_f32, host_i8, oracle_kv_grads_pooled, oracle_query_grads_pooled, record
 
 pytestmark = pytest.mark.gpu
 
@@ -65,6 +65,24 @@ def compare_grad(gpu_bf16, oracle_f64, what):
     assert max_rel <= GRAD_MAX_REL and mean_rel <= GRAD_MEAN_REL, (
         f"{what}: max|err|/max|ref| = {max_rel:.3e} (<= {GRAD_MAX_REL}), mean|err|/mean|ref| = {mean_rel:.3e} "
         f"(<= {GRAD_MEAN_REL}), worst at {np.unravel_index(int(d.argmax()), d.shape)}")
+
+
+def _block_pairs(nb, G, fixed, n_random, seed):
+    """(block, group) pairs: the fixed ones, then n_random distinct seeded
+    ones not among them."""
+    rng = np.random.default_rng(seed)
+    pairs = [tuple(p) for p in fixed]
+    while len(pairs) < len(fixed) + n_random:
+        p = (int(rng.integers(nb)), int(rng.integers(G)))
+        if p not in pairs:
+            pairs.append(p)
+    return pairs
+
+
+def _gather_blocks(x, pairs, bs):
+    """Rows of key block j in group g of x [B, G, S, D], stacked per pair:
+    [B, len(pairs), bs, D]."""
+    return torch.stack([x[:, g, j * bs:(j + 1) * bs] for j, g in pairs], dim=1)
 
 
 def _forward_backward(inp, dout, bs, top_k):
@@ -162,7 +180,7 @@ def test_backward_small_all_elements(name, over, S):
 
 def test_backward_32k_sampled_and_sums():
     """Prefill 32K (64 query heads, 8 groups, block 128, top_k 16): dq on
-    sampled rows and dk, dv on sampled blocks against the oracle; over every
+    every row and dk, dv of 48 (block, group) pairs against the oracle; over every
     key, the closed-form sums (dv rows of a group sum to its heads' dout
     rows, dk rows sum to 0)."""
     w = get_workload("prefill_32k")
@@ -185,27 +203,29 @@ def test_backward_32k_sampled_and_sums():
     summ = O.pool_block_keys(host_i8(inp["k_idx"]), bs)
     osel = O.select_blocks(host_i8(inp["q_idx"]), summ, bs, w.top_k)
     assert np.array_equal(gsel, osel), "selection differs"
-    # fp32 host copies (exact): the oracle gathers thousands of key rows per query
-    hq, hk, hv, hd = host_f32(inp["q"]), host_f32(inp["k"]), host_f32(inp["v"]), host_f32(dout)
-    rows = sample_rows(S, 32, 33)
-    _say(f"[backward full] oracle dq on {len(rows)} rows")
-    rq, _, _ = O.backward(hq, hk, hv, hd, osel, bs, rows=rows, kv_blocks=[])
-    compare_grad(dq[:, torch.as_tensor(rows, device=DEV)], rq, "32k dq (sampled rows)")
-    # an early block (kept by ~6000 queries of its group), a middle one and
-    # the last one, each in one group
-    for j, g in ((5, 3), (140, 6), (255, 0)):
-        _say(f"[backward full] oracle dk, dv of block {j}, group {g}")
-        _, rk, rv = O.backward(hq, hk, hv, hd, osel, bs, rows=[], kv_blocks=[j], groups=[g])
-        compare_grad(dk[:, g, j * bs:(j + 1) * bs], rk[:, g, 0], f"32k dk block {j} group {g}")
-        compare_grad(dv[:, g, j * bs:(j + 1) * bs], rv[:, g, 0], f"32k dv block {j} group {g}")
+    rows = np.arange(S)
+    _say(f"[backward full] oracle dq on every row ({S}, worker processes)")
+    rq, st = oracle_query_grads_pooled(inp, dout, osel, rows, bs)
+    _say(f"[backward full] oracle dq: {st}")
+    compare_grad(dq, rq, "32k dq (every row)")
+    del rq
+    # dk, dv of 48 (block, group) pairs: block 0 (kept by the most queries),
+    # an early block (~6000 queries of its group), a middle one, the last
+    # one, and 44 seeded ones
+    pairs = _block_pairs(S // bs, w.n_kv_heads, [(0, 2), (5, 3), (140, 6), (255, 0)], 44, seed=33)
+    _say(f"[backward full] oracle dk, dv of {len(pairs)} (block, group) pairs (worker processes)")
+    rk, rv, st = oracle_kv_grads_pooled(inp, dout, osel, pairs, bs)
+    _say(f"[backward full] oracle dk, dv: {st}")
+    compare_grad(_gather_blocks(dk, pairs, bs), rk, f"32k dk ({len(pairs)} blocks)")
+    compare_grad(_gather_blocks(dv, pairs, bs), rv, f"32k dv ({len(pairs)} blocks)")
     del inp, dout, dq, dk, dv
     _free()
 
 
 def test_backward_structured_128k_sampled_and_sums():
     """The structured 128K workload (hot blocks kept by most queries of their
-    group, so some CSR rows are very long): dq on sampled rows and dk, dv of
-    the last block against the oracle; the closed-form sums over every key."""
+    group, so some CSR rows are very long): dq on 4096 sampled rows and dk, dv
+    of the last block and 8 seeded (block, group) pairs against the oracle; the closed-form sums over every key."""
     w = get_workload("structured_128k")
     S, bs = w.seq_len, w.block_size
     _say(f"[backward full] structured_128k S={S}")
@@ -225,16 +245,17 @@ def test_backward_structured_128k_sampled_and_sums():
     summ = O.pool_block_keys(host_i8(inp["k_idx"]), bs)
     osel = O.select_blocks(host_i8(inp["q_idx"]), summ, bs, w.top_k)
     assert np.array_equal(gsel, osel), "selection differs"
-    hq, hk, hv, hd = host_f32(inp["q"]), host_f32(inp["k"]), host_f32(inp["v"]), host_f32(dout)
-    rows = sample_rows(S, 24, 41)
-    _say(f"[backward full] oracle dq on {len(rows)} rows")
-    rq, _, _ = O.backward(hq, hk, hv, hd, osel, bs, rows=rows, kv_blocks=[])
+    rows = sample_rows(S, 4096, 41)
+    _say(f"[backward full] oracle dq on {len(rows)} rows (worker processes)")
+    rq, st = oracle_query_grads_pooled(inp, dout, osel[:, :, rows], rows, bs)
+    _say(f"[backward full] oracle dq: {st}")
     compare_grad(dq[:, torch.as_tensor(rows, device=DEV)], rq, "128k dq (sampled rows)")
-    j, g = S // bs - 1, 5
-    _say(f"[backward full] oracle dk, dv of block {j}, group {g}")
-    _, rk, rv = O.backward(hq, hk, hv, hd, osel, bs, rows=[], kv_blocks=[j], groups=[g])
-    compare_grad(dk[:, g, j * bs:(j + 1) * bs], rk[:, g, 0], f"128k dk block {j} group {g}")
-    compare_grad(dv[:, g, j * bs:(j + 1) * bs], rv[:, g, 0], f"128k dv block {j} group {g}")
+    pairs = _block_pairs(S // bs, w.n_kv_heads, [(S // bs - 1, 5)], 8, seed=41)
+    _say(f"[backward full] oracle dk, dv of {len(pairs)} (block, group) pairs (worker processes)")
+    rk, rv, st = oracle_kv_grads_pooled(inp, dout, osel, pairs, bs)
+    _say(f"[backward full] oracle dk, dv: {st}")
+    compare_grad(_gather_blocks(dk, pairs, bs), rk, f"128k dk ({len(pairs)} blocks)")
+    compare_grad(_gather_blocks(dv, pairs, bs), rv, f"128k dv ({len(pairs)} blocks)")
     del inp, dout, dq, dk, dv
     _free()
 
@@ -327,7 +348,7 @@ def test_backward_passes_32k():
     _free()
 
 
-def _check_long_backward(w, inp, dout, sel, dq, dk, dv, seed, g, n_rows=16):
+def _check_long_backward(w, inp, dout, sel, dq, dk, dv, seed, g, n_rows=128):
     """Checks of a long backward: the closed-form sums over every key (fp64
     on the GPU), dq of sampled rows and dk, dv of the last block of group g
     against the oracle."""
@@ -360,8 +381,9 @@ def _check_long_backward(w, inp, dout, sel, dq, dk, dv, seed, g, n_rows=16):
     osel = O.select_blocks(qi, summ, bs, K, rows)
     assert np.array_equal(host_i8(sel[:, :, rows_t]).astype(np.int32), osel), "selection differs on sampled rows"
     kk, vv = HostBf16(inp["k"]), HostBf16(inp["v"])
-    _say(f"[backward {S}] oracle dq on {len(rows)} rows")
-    rq = O.query_grad_rows(host_f32(inp["q"][:, rows_t]), kk, vv, host_f32(dout[:, rows_t]), osel, rows, bs)
+    _say(f"[backward {S}] oracle dq on {len(rows)} rows (worker processes)")
+    rq, st = oracle_query_grads_pooled(inp, dout, osel, rows, bs)
+    _say(f"[backward {S}] oracle dq: {st}")
     compare_grad(dq[:, rows_t], rq, f"{S} dq (sampled rows)")
     # the last block: only the queries inside it can keep it (candidates are
     # earlier blocks and the own one), so the oracle's selection of those
