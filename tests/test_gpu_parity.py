@@ -4,9 +4,10 @@ Selections and block summaries must match bit for bit; outputs must be
 within max-abs 1e-2 and mean-abs 1e-3 of the oracle's fp64 result rounded to
 bf16, and every compared (row, head) with a mean error within 3 % of its own
 mean magnitude (tests/helpers.py).  Small cases compare every row; at full size the 32K
-prefill compares every row, the structured 128K and the 1M prefills 4096
+prefill compares every row, the structured 128K and the 1M prefills 32768
 seeded rows each (the oracle runs over worker processes), and the 128K
-selections and the last 16384 rows of the 1M index are checked in full.
+selections and three ranges of 16384 rows of the 1M index (the first, the
+middle and the last) are checked in full.
 """
 import gc
 import sys
@@ -320,11 +321,13 @@ def test_prefill_1m_sampled():
     _full_prefill_case("prefill_1m", 32768, seed=41, ws_cap_gb=70)
 
 
-def test_index_1m_last_16k_rows_all_selections():
-    """The 1M workload's index branch alone (msa_index_select): the last
-    16384 queries, which rank 8064 to 8191 earlier blocks in 64 summary
-    chunks of the matrix-core top-k, every row checked against the exact
-    top-k rule, 512 of them against the oracle."""
+def test_index_1m_16k_ranges_all_selections():
+    """The 1M workload's index branch alone (msa_index_select) on three
+    ranges of 16384 queries: the first (fewer earlier blocks than kept
+    slots up to query 1920, then 15 to 127 candidates), the middle (about
+    4096 candidates in 32 summary chunks of the matrix-core top-k) and the
+    last (8064 to 8191 candidates in 64 chunks).  Every row of them is
+    checked against the exact top-k rule, 512 of each against the oracle."""
     w = get_workload("prefill_1m")
     S = w.seq_len
     _say(f"[index 1M] S={S}")
@@ -336,13 +339,15 @@ def test_index_1m_last_16k_rows_all_selections():
     torch.cuda.synchronize()
     summ = O.pool_block_keys(host_i8(k_idx), w.block_size)
     assert np.array_equal(host_i8(bk), summ)
-    rows = np.arange(S - 16384, S)
     gsel = host_i8(sel)
     qi = host_i8(q_idx)
-    check_all_selections(gsel, qi, summ, S, w.block_size, w.top_k, row_slice=2048, rows=rows)
-    some = sample_rows(16384, 512, 43) + (S - 16384)
-    osel = O.select_blocks(qi, summ, w.block_size, w.top_k, some)
-    assert np.array_equal(gsel[:, :, some].astype(np.int32), osel)
+    for r0 in (0, S // 2 - 8192, S - 16384):
+        _say(f"[index 1M] rows {r0} .. {r0 + 16383}")
+        rows = np.arange(r0, r0 + 16384)
+        check_all_selections(gsel, qi, summ, S, w.block_size, w.top_k, row_slice=2048, rows=rows)
+        some = sample_rows(16384, 512, 43) + r0
+        osel = O.select_blocks(qi, summ, w.block_size, w.top_k, some)
+        assert np.array_equal(gsel[:, :, some].astype(np.int32), osel), f"selection differs in rows {r0}+"
     del q_idx, k_idx, bk, sel
     _free()
 
