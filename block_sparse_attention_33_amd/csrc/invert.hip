@@ -186,10 +186,17 @@ __global__ __launch_bounds__(256) void offsets_items_kernel(int32_t* __restrict_
   for (int m = 0; m < ni; ++m) items[first + m] = make_int2(i, m * tpi);
 }
 
+// An entry holds its slot in 5 bits: at most 32 slots per selection row.
+constexpr int kEntrySlots = 32;
+
 // One workgroup per (token chunk, unit): the chunk's entries go to its
 // reserved stretch of each block's list; positions inside the stretch come
 // from LDS cursors.  The order inside a list does not matter: each entry's
-// result is written to its own (token, slot) place.
+// result is written to its own (token, slot) place.  VEC: selection rows
+// are 16-byte aligned (top_k a multiple of 4, sel aligned), so a token's row
+// is read as 16-byte loads, all issued before its first cursor update
+// (one 4-byte load per slot touches a cache line per lane of the wave).
+template <bool VEC>
 __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ sel,
                                                       const int32_t* __restrict__ H,
                                                       uint32_t* __restrict__ entries, int S, int nb,
@@ -210,9 +217,31 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
   for (int t = t0 + (int)threadIdx.x; t < t1; t += 256) {
     const int nv = min(kp, (q0 + t) >> bs_log2);  // slot nv holds the own block
     const int32_t* srow = sel + ((size_t)u * cp.q_stride + t) * top_k;
-    for (int s = 0; s < nv + with_own; ++s) {
-      const int pos = atomicAdd(&cursor[srow[s]], 1);
-      entries[pos] = ((uint32_t)t << 5) | (uint32_t)s;
+    const int n = nv + with_own;  // n <= top_k
+    if constexpr (VEC) {
+      int32_t blk[kEntrySlots];
+#pragma unroll
+      for (int i = 0; i < kEntrySlots / 4; ++i) {
+        if (4 * i < n) {  // 4 i + 3 < top_k: inside the row
+          const i32x4_t x = reinterpret_cast<const i32x4_t*>(srow)[i];
+          blk[4 * i] = x[0];
+          blk[4 * i + 1] = x[1];
+          blk[4 * i + 2] = x[2];
+          blk[4 * i + 3] = x[3];
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < kEntrySlots; ++s) {
+        if (s < n) {
+          const int pos = atomicAdd(&cursor[blk[s]], 1);
+          entries[pos] = ((uint32_t)t << 5) | (uint32_t)s;
+        }
+      }
+    } else {
+      for (int s = 0; s < n; ++s) {
+        const int pos = atomicAdd(&cursor[srow[s]], 1);
+        entries[pos] = ((uint32_t)t << 5) | (uint32_t)s;
+      }
     }
   }
 }
@@ -258,10 +287,18 @@ hipError_t launch_scatter(const int32_t* sel, const int32_t* H, uint32_t* entrie
   int bs_log2 = 0;
   while ((1 << bs_log2) < bs) ++bs_log2;
   const size_t lds = (size_t)nb * 4;
-  const hipError_t attr = ensure_dynamic_lds(reinterpret_cast<const void*>(&scatter_kernel), kMaxInvertBlocks * 4);
+  if (top_k > kEntrySlots) return hipErrorInvalidValue;
+  const bool vec = top_k % 4 == 0 && reinterpret_cast<uintptr_t>(sel) % 16 == 0;
+  const void* fn = vec ? reinterpret_cast<const void*>(&scatter_kernel<true>)
+                       : reinterpret_cast<const void*>(&scatter_kernel<false>);
+  const hipError_t attr = ensure_dynamic_lds(fn, kMaxInvertBlocks * 4);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)(cp.n_chunks * units)), dim3(256), lds, st, sel, H, entries, S,
-                     nb, bs_log2, top_k, cp, q0, with_own ? 1 : 0, units);
+  if (vec)
+    hipLaunchKernelGGL(scatter_kernel<true>, dim3((unsigned)(cp.n_chunks * units)), dim3(256), lds, st, sel, H,
+                       entries, S, nb, bs_log2, top_k, cp, q0, with_own ? 1 : 0, units);
+  else
+    hipLaunchKernelGGL(scatter_kernel<false>, dim3((unsigned)(cp.n_chunks * units)), dim3(256), lds, st, sel, H,
+                       entries, S, nb, bs_log2, top_k, cp, q0, with_own ? 1 : 0, units);
   return hipGetLastError();
 }
 
