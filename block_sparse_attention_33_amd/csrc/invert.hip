@@ -17,10 +17,7 @@
 namespace msa {
 namespace {
 
-// Per-chunk histograms: one workgroup per (token chunk, unit) counts, in LDS,
-// how many of the chunk's queries kept each block (the own block only with
-// with_own: the forward attends it elsewhere, the backward through the
-// lists), and stores the counts as H[u][chunk][block].  LDS atomics only.
+// Tokens t0 .. t1 - 1 of histogram chunk c.
 __device__ __forceinline__ void chunk_tokens(const ChunkPlan& cp, int c, int S, int* t0, int* t1) {
   const int rng = c / cp.m;
   const int i = c - rng * cp.m;
@@ -28,6 +25,33 @@ __device__ __forceinline__ void chunk_tokens(const ChunkPlan& cp, int c, int S, 
   *t1 = min(min(S, (rng + 1) * cp.T), *t0 + cp.tpc);
 }
 
+// An entry holds its slot in 5 bits: at most 32 slots per selection row.
+constexpr int kEntrySlots = 32;
+
+// Slots 0 .. n - 1 (n <= kEntrySlots) of a 16-byte aligned selection row
+// whose length is a multiple of 4, as 16-byte loads all issued before the
+// first use (one 4-byte load per slot touches a cache line per lane of the
+// wave).  4 i < n implies 4 i + 3 < the row length: every load is inside it.
+__device__ __forceinline__ void load_sel_row(const int32_t* __restrict__ srow, int n,
+                                             int32_t (&blk)[kEntrySlots]) {
+#pragma unroll
+  for (int i = 0; i < kEntrySlots / 4; ++i) {
+    if (4 * i < n) {
+      const i32x4_t x = reinterpret_cast<const i32x4_t*>(srow)[i];
+      blk[4 * i] = x[0];
+      blk[4 * i + 1] = x[1];
+      blk[4 * i + 2] = x[2];
+      blk[4 * i + 3] = x[3];
+    }
+  }
+}
+
+// Per-chunk histograms: one workgroup per (token chunk, unit) counts, in LDS,
+// how many of the chunk's queries kept each block (the own block only with
+// with_own: the forward attends it elsewhere, the backward through the
+// lists), and stores the counts as H[u][chunk][block].  LDS atomics only.
+// VEC: selection rows 16-byte aligned, read by load_sel_row.
+template <bool VEC>
 __global__ __launch_bounds__(256) void chunk_hist_kernel(const int32_t* __restrict__ sel,
                                                          int32_t* __restrict__ H, int S, int nb,
                                                          int bs_log2, int top_k, ChunkPlan cp, int q0,
@@ -44,7 +68,16 @@ __global__ __launch_bounds__(256) void chunk_hist_kernel(const int32_t* __restri
   for (int t = t0 + (int)threadIdx.x; t < t1; t += 256) {
     const int nv = min(kp, (q0 + t) >> bs_log2);  // slot nv holds the own block
     const int32_t* srow = sel + ((size_t)u * cp.q_stride + t) * top_k;
-    for (int s = 0; s < nv + with_own; ++s) atomicAdd(&hist[srow[s]], 1);
+    const int n = nv + with_own;
+    if constexpr (VEC) {
+      int32_t blk[kEntrySlots];
+      load_sel_row(srow, n, blk);
+#pragma unroll
+      for (int s = 0; s < kEntrySlots; ++s)
+        if (s < n) atomicAdd(&hist[blk[s]], 1);
+    } else {
+      for (int s = 0; s < n; ++s) atomicAdd(&hist[srow[s]], 1);
+    }
   }
   __syncthreads();
   int32_t* dst = H + ((size_t)u * n_chunks + c) * nb;
@@ -186,16 +219,12 @@ __global__ __launch_bounds__(256) void offsets_items_kernel(int32_t* __restrict_
   for (int m = 0; m < ni; ++m) items[first + m] = make_int2(i, m * tpi);
 }
 
-// An entry holds its slot in 5 bits: at most 32 slots per selection row.
-constexpr int kEntrySlots = 32;
-
 // One workgroup per (token chunk, unit): the chunk's entries go to its
 // reserved stretch of each block's list; positions inside the stretch come
 // from LDS cursors.  The order inside a list does not matter: each entry's
 // result is written to its own (token, slot) place.  VEC: selection rows
-// are 16-byte aligned (top_k a multiple of 4, sel aligned), so a token's row
-// is read as 16-byte loads, all issued before its first cursor update
-// (one 4-byte load per slot touches a cache line per lane of the wave).
+// are 16-byte aligned (top_k a multiple of 4, sel aligned) and read by
+// load_sel_row.
 template <bool VEC>
 __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ sel,
                                                       const int32_t* __restrict__ H,
@@ -220,16 +249,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
     const int n = nv + with_own;  // n <= top_k
     if constexpr (VEC) {
       int32_t blk[kEntrySlots];
-#pragma unroll
-      for (int i = 0; i < kEntrySlots / 4; ++i) {
-        if (4 * i < n) {  // 4 i + 3 < top_k: inside the row
-          const i32x4_t x = reinterpret_cast<const i32x4_t*>(srow)[i];
-          blk[4 * i] = x[0];
-          blk[4 * i + 1] = x[1];
-          blk[4 * i + 2] = x[2];
-          blk[4 * i + 3] = x[3];
-        }
-      }
+      load_sel_row(srow, n, blk);
 #pragma unroll
       for (int s = 0; s < kEntrySlots; ++s) {
         if (s < n) {
@@ -253,11 +273,18 @@ hipError_t launch_chunk_hist(const int32_t* sel, int32_t* H, int units, int S, i
   int bs_log2 = 0;
   while ((1 << bs_log2) < bs) ++bs_log2;
   const size_t lds = (size_t)nb * 4;
-  const hipError_t attr =
-      ensure_dynamic_lds(reinterpret_cast<const void*>(&chunk_hist_kernel), kMaxInvertBlocks * 4);
+  if (top_k > kEntrySlots) return hipErrorInvalidValue;
+  const bool vec = top_k % 4 == 0 && reinterpret_cast<uintptr_t>(sel) % 16 == 0;
+  const void* fn = vec ? reinterpret_cast<const void*>(&chunk_hist_kernel<true>)
+                       : reinterpret_cast<const void*>(&chunk_hist_kernel<false>);
+  const hipError_t attr = ensure_dynamic_lds(fn, kMaxInvertBlocks * 4);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(chunk_hist_kernel, dim3(cp.n_chunks, units), dim3(256), lds, st, sel, H, S, nb, bs_log2,
-                     top_k, cp, q0, with_own ? 1 : 0);
+  if (vec)
+    hipLaunchKernelGGL(chunk_hist_kernel<true>, dim3(cp.n_chunks, units), dim3(256), lds, st, sel, H, S, nb,
+                       bs_log2, top_k, cp, q0, with_own ? 1 : 0);
+  else
+    hipLaunchKernelGGL(chunk_hist_kernel<false>, dim3(cp.n_chunks, units), dim3(256), lds, st, sel, H, S, nb,
+                       bs_log2, top_k, cp, q0, with_own ? 1 : 0);
   return hipGetLastError();
 }
 
